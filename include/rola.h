@@ -1,0 +1,166 @@
+/*
+ * rola.h -- C ABI of librola: RoLA attention (rotary-positioned low-rank
+ * linear attention plus block-sparse softmax attention) on AMD MI355X (gfx950).
+ *
+ * The operation (pages: "SparkDiffusion: 265x Faster Video Generation on
+ * Consumer GPUs via Sparse Attention & Distillation", section "RoLA:
+ * Preserving Global Context at Extreme Sparsity"; "SparkDiffusion / SparkWan"
+ * news article, section "What's New"): a block-sparse softmax branch keeps the
+ * highest-energy query-key blocks, and a low-rank linear-attention branch with
+ * rotary positions recovers the global context the sparse branch discards.
+ * The keep ratio `topk` (README "AlibabaResearch/SparkDiffusion", inference
+ * section: 0.1, 0.05, 0.03 mean 90%, 95%, 97% sparsity) fixes how many key
+ * blocks each query block keeps.  fp8 and bf16 are the two precisions the
+ * README names (quick-start section).
+ *
+ * Definitions used by every call (B batch, H heads, D head_dim, N = T*Hg*W
+ * tokens of a raster (t,h,w) latent grid, 64-token blocks, nb = ceil(N/64),
+ * n_pad = 64*nb, r the low-rank width):
+ *  - block energy: Qp[c], Kp[c] = mean of block c's valid tokens (fp32, fixed
+ *    binary-tree summation order, times fl32(1/count));
+ *  - score s[i][j] = sequential fp32 fma chain over d of Qp[i][d]*Kp[j][d];
+ *  - kept blocks: kb = max(1, floor(topk*nb)) (or kb_override) largest scores
+ *    per query block i, ties to the lower j, listed in ascending j;
+ *  - sparse branch: softmax(q k^T * scale) v over the valid tokens of the kept
+ *    key blocks; scale defaults to D^-1/2;
+ *  - low-rank branch: a = phi(Wq^T R(q)), b = phi(Wk^T R(k)), phi = elu + 1,
+ *    R the 3-D rotary embedding (dims split t/h/w, interleaved pairs, base
+ *    theta); S = sum_{n<N} b_n v_n^T, z = sum_{n<N} b_n per (batch, head);
+ *    O_lr = (a^T S) / (a^T z);
+ *  - output O = O_sparse + O_lr for rows < N; rows N..n_pad-1 are written 0.
+ *
+ * Memory: every pointer is device memory owned by the caller.  Q, K, V and O
+ * share one layout: element (b, h, n, d) at b*stride_b + h*stride_h +
+ * n*stride_n + d (elements; d contiguous), rows 0..n_pad-1 addressable;
+ * input rows >= N are ignored (may hold anything).  Q/K/V are bf16.  O is
+ * bf16 or fp32 (config.out_dtype).  Wq, Wk are fp32 [D][r], shared by all
+ * heads.  The workspace (size from rola_plan) is scratch owned by the caller;
+ * the library keeps no state in it between calls.
+ *
+ * Behaviour: every call validates all arguments before launching anything;
+ * on error nothing is launched and a status != ROLA_OK is returned.  Launches
+ * are asynchronous on `stream` (a hipStream_t; NULL = default stream).  The
+ * library never allocates, frees or synchronises device memory.  Calls are
+ * thread-safe when they use distinct workspaces.
+ */
+#ifndef ROLA_H_
+#define ROLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ROLA_ABI_VERSION 1
+#define ROLA_BLOCK 64
+#define ROLA_MAX_BLOCKS 4096 /* nb limit: N <= 262144 tokens */
+
+typedef enum rola_status {
+  ROLA_OK = 0,
+  ROLA_ERR_INVALID_ARG = 1, /* null pointer, bad size, topk outside (0,1], ... */
+  ROLA_ERR_UNSUPPORTED = 2, /* D not in {64,128}, r not in {16,32}, nb too large */
+  ROLA_ERR_ALIGNMENT = 3,   /* pointer or row stride not 16-byte aligned */
+  ROLA_ERR_WORKSPACE = 4,   /* workspace null or smaller than rola_plan's size */
+  ROLA_ERR_DEVICE = 5       /* a HIP launch reported an error */
+} rola_status;
+
+enum { ROLA_PREC_BF16 = 0, ROLA_PREC_FP8 = 1 };
+enum { ROLA_OUT_BF16 = 0, ROLA_OUT_F32 = 1 };
+
+typedef struct rola_problem {
+  int32_t batch, heads, head_dim;
+  int32_t grid_t, grid_h, grid_w;    /* latent token grid; N = grid_t*grid_h*grid_w */
+  int64_t stride_b, stride_h, stride_n; /* in elements, shared by Q, K, V, O */
+} rola_problem;
+
+typedef struct rola_config {
+  float topk;          /* keep ratio in (0, 1] */
+  int32_t kb_override; /* > 0: keep exactly this many key blocks (<= nb) */
+  int32_t rank;        /* low-rank width r: 16 or 32 */
+  int32_t rope_split[3]; /* rotary dims for t, h, w (even, summing to D); all 0: D/4, rest halved */
+  float rope_theta;    /* <= 0: 10000 */
+  float softmax_scale; /* <= 0: 1/sqrt(D) */
+  int32_t precision;   /* ROLA_PREC_BF16 or ROLA_PREC_FP8 (e4m3, per-block absmax scales) */
+  int32_t out_dtype;   /* ROLA_OUT_BF16 or ROLA_OUT_F32 */
+} rola_config;
+
+typedef struct rola_plan_info {
+  int64_t n_tokens; /* N */
+  int32_t nb;       /* 64-token blocks */
+  int32_t kb;       /* key blocks kept per query block */
+  int64_t n_pad;    /* 64*nb rows addressed in every token tensor */
+  int64_t workspace_bytes; /* for the largest call (rola_forward) */
+} rola_plan_info;
+
+/* ABI version (ROLA_ABI_VERSION) and a static message for a status. */
+int32_t rola_abi_version(void);
+const char *rola_status_str(int32_t status);
+
+/* Host-only: validate the problem and config and size the workspace.  No device access. */
+int32_t rola_plan(const rola_problem *prob, const rola_config *cfg, rola_plan_info *out);
+
+/*
+ * Block selection (pages: "What's New" -- keep "a tiny fraction of query-key
+ * blocks"; README inference section -- topk as keep ratio).  Pools Q and K per
+ * block, scores every block pair and writes the kept key blocks of every
+ * query block to block_idx (int32 [B][H][nb][kb], ascending).  pooled_scores,
+ * if not NULL, receives the fp32 score matrix [B][H][nb][nb].
+ */
+int32_t rola_select_blocks(const rola_problem *prob, const rola_config *cfg, const void *q,
+                           const void *k, int32_t *block_idx, float *pooled_scores,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Sparse branch only (pages: RoLA section -- "block-sparse branch" that keeps
+ * the high-energy query-key interactions).  O = O_sparse (accumulate = 0) or
+ * O += O_sparse (accumulate = 1), with block_idx as written by
+ * rola_select_blocks (ids must be ascending and < nb).
+ */
+int32_t rola_sparse_attn(const rola_problem *prob, const rola_config *cfg, const void *q,
+                         const void *k, const void *v, const int32_t *block_idx, void *out,
+                         int32_t accumulate, void *workspace, size_t workspace_bytes,
+                         void *stream);
+
+/*
+ * Low-rank branch only (pages: RoLA paper title "Rotary-Positioned Low-Rank
+ * Linear Attention"; RoLA section -- low-rank linear branch with rotary
+ * positions; README sparse-finetune note -- the added proj_q / proj_k).
+ * O = O_lr (accumulate = 0) or O += O_lr (accumulate = 1).
+ */
+int32_t rola_lowrank_attn(const rola_problem *prob, const rola_config *cfg, const void *q,
+                          const void *k, const void *v, const float *wq, const float *wk,
+                          void *out, int32_t accumulate, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+/*
+ * Fused RoLA forward: O = O_sparse + O_lr.  block_idx_out, if not NULL,
+ * receives the block map (int32 [B][H][nb][kb]).
+ */
+int32_t rola_forward(const rola_problem *prob, const rola_config *cfg, const void *q,
+                     const void *k, const void *v, const float *wq, const float *wk,
+                     int32_t *block_idx_out, void *out, void *workspace,
+                     size_t workspace_bytes, void *stream);
+
+/*
+ * Optional kernel timing for measurement.  While enabled, each call records a
+ * hipEvent pair around every kernel it launches (on the call's stream).
+ * rola_timing_read synchronises those events and returns, per kernel name,
+ * the launch count and total milliseconds (at most `max` entries; returns
+ * the number written, or -1 on error).  Process-global; not thread-safe.
+ */
+typedef struct rola_kernel_time {
+  char name[48];
+  int32_t launches;
+  double total_ms;
+} rola_kernel_time;
+
+int32_t rola_timing_enable(int32_t on);
+int32_t rola_timing_read(rola_kernel_time *out, int32_t max);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ROLA_H_ */

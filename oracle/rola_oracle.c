@@ -1,0 +1,437 @@
+/*
+ * rola_oracle.c -- plain, slow CPU definition of RoLA attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file; only the tests, the smoke check and the benchmark's CPU
+ * baseline leg do.  It shares no code, header or table with the HIP library.
+ *
+ * What is computed (pages: "SparkDiffusion: 265x Faster Video Generation on
+ * Consumer GPUs via Sparse Attention & Distillation", section "RoLA:
+ * Preserving Global Context at Extreme Sparsity"; "SparkDiffusion/SparkWan"
+ * news article, section "What's New"):  RoLA attention keeps the high-energy
+ * query-key blocks in a block-sparse softmax branch, and adds a low-rank
+ * linear-attention branch with rotary positions that restores the global
+ * context the sparse branch drops.  The output is the sum of both branches.
+ * The keep ratio ``topk`` (README "AlibabaResearch/SparkDiffusion",
+ * inference section) is the fraction of key blocks each query block keeps.
+ *
+ * Readings taken where the pages are silent (each is listed in the design doc):
+ *  - 64-token blocks in raster (t,h,w) order; block energy is the mean of the
+ *    block's valid tokens (the tail block's padding is excluded);
+ *  - pooling sums in a fixed binary tree (pairs at distance 32,16,...,1) in
+ *    fp32, then multiplies by fp32(1/count); scores are a sequential fp32 fma
+ *    chain over d = 0..D-1 from +0.0, with no 1/sqrt(D) and no softmax (both
+ *    are monotone per row and would only add roundings);
+ *  - per query block, the kb = max(1, floor(topk*nb)) key blocks with the
+ *    largest score are kept, ties going to the lower block index; the map is
+ *    stored in ascending block order;
+ *  - sparse branch: softmax(q k^T * scale) v over the tokens of the kept key
+ *    blocks that lie below N, scale = D^-1/2;
+ *  - 3-D rotary embedding on the head_dim vector before the low-rank
+ *    projection: dims split (d_t, d_h, d_w) over the axes, pairs interleaved
+ *    (x[o+2p], x[o+2p+1]) rotated by pos * theta^(-2p/d_axis);
+ *  - features phi(x) = elu(x) + 1; the linear branch is normalised,
+ *    O_lr = (a^T S)/(a^T z), S = sum_n b_n v_n^T, z = sum_n b_n over all N
+ *    valid keys; one state per (batch, head);
+ *  - output = sparse + low-rank for rows < N, zero for padded rows;
+ *  - fp8 mode: per (batch, head, 64-token block) absmax scale, codes are
+ *    OCP e4m3 (max 448) rounded to nearest even from x * fl32(448/absmax),
+ *    values dequantise as code * fl32(absmax/448).
+ *
+ * Arrays are contiguous: tokens [BH, n_pad, D] (BH = batch*heads), bf16 held
+ * as uint16 bit patterns; pooled [BH, nb, D]; scores [BH, nb, nb]; map
+ * [BH, nb, kb] int32; projections [D, r] fp32.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define RO_BLOCK 64
+
+int ro_version(void) { return 1; }
+
+static float bf16_to_f32(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return f;
+}
+
+/* Token index -> (t, h, w) for a raster-ordered T x Hg x W grid. */
+void ro_position(int64_t n, int grid_h, int grid_w, int32_t *pos3) {
+  pos3[0] = (int32_t)(n / ((int64_t)grid_h * grid_w));
+  pos3[1] = (int32_t)((n / grid_w) % grid_h);
+  pos3[2] = (int32_t)(n % grid_w);
+}
+
+/* ---------------------------------------------------------------- pooling */
+/* out[bh][c][d] = (pinned fp32 tree sum of the block's valid tokens) * fl32(1/count). */
+void ro_pool(const uint16_t *x, int64_t bh_count, int64_t n_pad, int64_t n_valid, int d_model,
+             float *out) {
+  const int64_t nb = n_pad / RO_BLOCK;
+#pragma omp parallel for schedule(static)
+  for (int64_t bh = 0; bh < bh_count; ++bh) {
+    for (int64_t c = 0; c < nb; ++c) {
+      int64_t count = n_valid - c * RO_BLOCK;
+      if (count > RO_BLOCK) count = RO_BLOCK;
+      if (count < 0) count = 0;
+      const float inv = count > 0 ? 1.0f / (float)count : 0.0f;
+      for (int d = 0; d < d_model; ++d) {
+        float v[RO_BLOCK];
+        for (int s = 0; s < RO_BLOCK; ++s) {
+          const int64_t n = c * RO_BLOCK + s;
+          v[s] = n < n_valid ? bf16_to_f32(x[(bh * n_pad + n) * d_model + d]) : 0.0f;
+        }
+        for (int stride = RO_BLOCK / 2; stride >= 1; stride /= 2)
+          for (int i = 0; i < stride; ++i) v[i] = v[i] + v[i + stride];
+        out[(bh * nb + c) * d_model + d] = v[0] * inv;
+      }
+    }
+  }
+}
+
+/* ----------------------------------------------------------------- scores */
+/* s[bh][i][j] = fma chain over d of qp[i][d] * kp[j][d], starting at +0.0. */
+void ro_scores(const float *qp, const float *kp, int64_t bh_count, int nb, int d_model, float *s) {
+#pragma omp parallel for schedule(static)
+  for (int64_t bh = 0; bh < bh_count; ++bh) {
+    for (int i = 0; i < nb; ++i) {
+      const float *qi = qp + (bh * nb + i) * d_model;
+      for (int j = 0; j < nb; ++j) {
+        const float *kj = kp + (bh * nb + j) * d_model;
+        float acc = 0.0f;
+        for (int d = 0; d < d_model; ++d) acc = fmaf(qi[d], kj[d], acc);
+        s[(bh * nb + i) * (int64_t)nb + j] = acc;
+      }
+    }
+  }
+}
+
+/* -------------------------------------------------------------- selection */
+typedef struct {
+  float s;
+  int32_t j;
+} ro_cand;
+
+/* Order: larger score first; equal scores (including -0.0 == +0.0) by lower index. */
+static int cand_cmp(const void *a, const void *b) {
+  const ro_cand *x = (const ro_cand *)a, *y = (const ro_cand *)b;
+  if (x->s > y->s) return -1;
+  if (x->s < y->s) return 1;
+  return (x->j > y->j) - (x->j < y->j);
+}
+
+static int int_cmp(const void *a, const void *b) {
+  const int32_t x = *(const int32_t *)a, y = *(const int32_t *)b;
+  return (x > y) - (x < y);
+}
+
+/* s [BH, nq, nb] -> map [BH, nq, kb] (nq = nb for a full score matrix). */
+void ro_select(const float *s, int64_t bh_count, int nq, int nb, int kb, int32_t *map) {
+#pragma omp parallel for schedule(static)
+  for (int64_t bh = 0; bh < bh_count; ++bh) {
+    ro_cand *row = (ro_cand *)malloc(sizeof(ro_cand) * (size_t)nb);
+    for (int i = 0; i < nq; ++i) {
+      const float *si = s + (bh * nq + i) * (int64_t)nb;
+      for (int j = 0; j < nb; ++j) {
+        row[j].s = si[j];
+        row[j].j = j;
+      }
+      qsort(row, (size_t)nb, sizeof(ro_cand), cand_cmp);
+      int32_t *mi = map + (bh * nq + i) * (int64_t)kb;
+      for (int t = 0; t < kb; ++t) mi[t] = row[t].j;
+      qsort(mi, (size_t)kb, sizeof(int32_t), int_cmp);
+    }
+    free(row);
+  }
+}
+
+/* ---------------------------------------------------------- sparse branch */
+/* One query row: softmax over the valid tokens of the kept key blocks. */
+static void sparse_row(const double *q, const double *k, const double *v, const int32_t *blocks,
+                       int kb, int64_t n_valid, int d_model, double scale, double *out,
+                       double *buf) {
+  int64_t cnt = 0;
+  double m = -INFINITY;
+  for (int t = 0; t < kb; ++t) {
+    for (int s = 0; s < RO_BLOCK; ++s) {
+      const int64_t n = (int64_t)blocks[t] * RO_BLOCK + s;
+      if (n >= n_valid) continue;
+      double dot = 0.0;
+      for (int d = 0; d < d_model; ++d) dot += q[d] * k[n * d_model + d];
+      dot *= scale;
+      buf[cnt++] = dot;
+      if (dot > m) m = dot;
+    }
+  }
+  for (int d = 0; d < d_model; ++d) out[d] = 0.0;
+  double l = 0.0;
+  cnt = 0;
+  for (int t = 0; t < kb; ++t) {
+    for (int s = 0; s < RO_BLOCK; ++s) {
+      const int64_t n = (int64_t)blocks[t] * RO_BLOCK + s;
+      if (n >= n_valid) continue;
+      const double p = exp(buf[cnt++] - m);
+      l += p;
+      for (int d = 0; d < d_model; ++d) out[d] += p * v[n * d_model + d];
+    }
+  }
+  for (int d = 0; d < d_model; ++d) out[d] /= l;
+}
+
+/*
+ * Sparse branch on selected rows.  q, k, v: fp64 [BH, n_pad, D]; rows[r] =
+ * bh * n_pad + n with n < n_valid; out: [nrows, D].
+ */
+void ro_sparse_rows(const double *q, const double *k, const double *v, const int32_t *map,
+                    int64_t n_pad, int64_t n_valid, int d_model, int kb, double scale,
+                    int64_t nrows, const int64_t *rows, double *out) {
+  const int64_t nb = n_pad / RO_BLOCK;
+#pragma omp parallel
+  {
+    double *buf = (double *)malloc(sizeof(double) * (size_t)kb * RO_BLOCK);
+#pragma omp for schedule(dynamic, 16)
+    for (int64_t r = 0; r < nrows; ++r) {
+      const int64_t bh = rows[r] / n_pad, n = rows[r] % n_pad;
+      const int64_t base = bh * n_pad * d_model;
+      sparse_row(q + rows[r] * d_model, k + base, v + base, map + (bh * nb + n / RO_BLOCK) * kb, kb,
+                 n_valid, d_model, scale, out + r * d_model, buf);
+    }
+    free(buf);
+  }
+}
+
+/* ----------------------------------------------------------- 3-D rotary */
+/*
+ * y = R(t,h,w) x.  Axis a owns dims [o_a, o_a + d_a) with o = (0, d_t, d_t+d_h);
+ * pair p of axis a, (x[o_a+2p], x[o_a+2p+1]), turns by pos_a * theta^(-2p/d_a).
+ */
+void ro_rope3d(const double *x, const int32_t *pos3, const int32_t *split, double theta,
+               int d_model, double *y) {
+  int off = 0;
+  for (int d = 0; d < d_model; ++d) y[d] = x[d];
+  for (int a = 0; a < 3; ++a) {
+    const int da = split[a];
+    for (int p = 0; p < da / 2; ++p) {
+      const double ang = (double)pos3[a] * pow(theta, -2.0 * p / (double)da);
+      const double c = cos(ang), s = sin(ang);
+      const double x0 = x[off + 2 * p], x1 = x[off + 2 * p + 1];
+      y[off + 2 * p] = x0 * c - x1 * s;
+      y[off + 2 * p + 1] = x0 * s + x1 * c;
+    }
+    off += da;
+  }
+}
+
+/* feature map phi(u) = elu(u) + 1 */
+static double phi(double u) { return u > 0.0 ? u + 1.0 : exp(u); }
+
+/* f[r] = phi(sum_d RoPE(x)[d] * w[d][r]) for token n of the grid. */
+static void lowrank_feature(const double *x, int64_t n, const int32_t *grid, const int32_t *split,
+                            double theta, const float *w, int d_model, int rank, double *rot,
+                            double *f) {
+  int32_t pos3[3];
+  ro_position(n, grid[1], grid[2], pos3);
+  ro_rope3d(x, pos3, split, theta, d_model, rot);
+  for (int r = 0; r < rank; ++r) {
+    double u = 0.0;
+    for (int d = 0; d < d_model; ++d) u += rot[d] * (double)w[d * rank + r];
+    f[r] = phi(u);
+  }
+}
+
+/* Public for tests: the feature vector of one token. */
+void ro_lowrank_feature(const double *x, int64_t n, const int32_t *grid, const int32_t *split,
+                        double theta, const float *w, int d_model, int rank, double *f) {
+  double rot[512];
+  lowrank_feature(x, n, grid, split, theta, w, d_model, rank, rot, f);
+}
+
+/* S[bh][r][d] = sum_{n<N} b_n[r] v_n[d],  z[bh][r] = sum_{n<N} b_n[r],  b_n = phi(Wk^T RoPE(k_n)). */
+void ro_lowrank_state(const double *k, const double *v, const float *wk, int64_t bh_count,
+                      int64_t n_pad, int64_t n_valid, int d_model, int rank, const int32_t *grid,
+                      const int32_t *split, double theta, double *S, double *z) {
+#pragma omp parallel for schedule(static)
+  for (int64_t bh = 0; bh < bh_count; ++bh) {
+    double rot[512], f[64];
+    double *Sb = S + bh * rank * d_model, *zb = z + bh * rank;
+    for (int64_t i = 0; i < (int64_t)rank * d_model; ++i) Sb[i] = 0.0;
+    for (int r = 0; r < rank; ++r) zb[r] = 0.0;
+    for (int64_t n = 0; n < n_valid; ++n) {
+      const double *kn = k + (bh * n_pad + n) * d_model, *vn = v + (bh * n_pad + n) * d_model;
+      lowrank_feature(kn, n, grid, split, theta, wk, d_model, rank, rot, f);
+      for (int r = 0; r < rank; ++r) {
+        zb[r] += f[r];
+        for (int d = 0; d < d_model; ++d) Sb[r * d_model + d] += f[r] * vn[d];
+      }
+    }
+  }
+}
+
+/* O_lr for selected rows: (a^T S) / (a^T z), a = phi(Wq^T RoPE(q)). */
+void ro_lowrank_rows(const double *q, const float *wq, const double *S, const double *z,
+                     int64_t n_pad, int d_model, int rank, const int32_t *grid,
+                     const int32_t *split, double theta, int64_t nrows, const int64_t *rows,
+                     double *out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < nrows; ++r) {
+    double rot[512], a[64];
+    const int64_t bh = rows[r] / n_pad, n = rows[r] % n_pad;
+    lowrank_feature(q + rows[r] * d_model, n, grid, split, theta, wq, d_model, rank, rot, a);
+    const double *Sb = S + bh * rank * d_model, *zb = z + bh * rank;
+    double den = 0.0;
+    for (int i = 0; i < rank; ++i) den += a[i] * zb[i];
+    for (int d = 0; d < d_model; ++d) {
+      double num = 0.0;
+      for (int i = 0; i < rank; ++i) num += a[i] * Sb[i * d_model + d];
+      out[r * d_model + d] = num / den;
+    }
+  }
+}
+
+/* --------------------------------------------------------------- fp8 e4m3 */
+/* OCP e4m3 value of a code (no infinities; 0x7f/0xff are NaN). */
+double ro_e4m3_value(uint8_t code) {
+  const int sign = code >> 7, e = (code >> 3) & 15, m = code & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    v = ldexp((double)m, -9); /* subnormal: m/8 * 2^-6 */
+  else
+    v = ldexp(1.0 + m / 8.0, e - 7);
+  return sign ? -v : v;
+}
+
+/* Nearest e4m3 code to y (ties to the even code), saturating at +-448. */
+uint8_t ro_e4m3_encode(float y) {
+  const uint8_t sign = signbit(y) ? 0x80 : 0;
+  double a = fabs((double)y);
+  if (a >= 448.0) return sign | 0x7e;
+  /* candidates are the non-negative codes 0..0x7e in increasing value */
+  int lo = 0, hi = 0x7e;
+  while (hi - lo > 1) { /* largest code with value <= a */
+    const int mid = (lo + hi) / 2;
+    if (ro_e4m3_value((uint8_t)mid) <= a) lo = mid; else hi = mid;
+  }
+  const double vlo = ro_e4m3_value((uint8_t)lo), vhi = ro_e4m3_value((uint8_t)hi);
+  int pick;
+  if (a - vlo < vhi - a) pick = lo;
+  else if (a - vlo > vhi - a) pick = hi;
+  else pick = (lo & 1) ? hi : lo;
+  if (vlo == a) pick = lo;
+  return sign | (uint8_t)pick;
+}
+
+/*
+ * Per-(bh, block) quantisation of bf16 tokens.  codes [BH, n_pad, D];
+ * scale [BH, nb] = fl32(absmax/448); deq [BH, n_pad, D] fp64 = value(code) * scale.
+ * Padded rows are excluded from absmax and quantise to 0.
+ */
+void ro_quant_e4m3(const uint16_t *x, int64_t bh_count, int64_t n_pad, int64_t n_valid,
+                   int d_model, uint8_t *codes, float *scale, double *deq) {
+  const int64_t nb = n_pad / RO_BLOCK;
+#pragma omp parallel for schedule(static)
+  for (int64_t bh = 0; bh < bh_count; ++bh) {
+    for (int64_t c = 0; c < nb; ++c) {
+      float amax = 0.0f;
+      for (int s = 0; s < RO_BLOCK; ++s) {
+        const int64_t n = c * RO_BLOCK + s;
+        if (n >= n_valid) break;
+        for (int d = 0; d < d_model; ++d) {
+          const float a = fabsf(bf16_to_f32(x[(bh * n_pad + n) * d_model + d]));
+          if (a > amax) amax = a;
+        }
+      }
+      const float inv = amax > 0.0f ? 448.0f / amax : 1.0f;
+      const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+      scale[bh * nb + c] = sc;
+      for (int s = 0; s < RO_BLOCK; ++s) {
+        const int64_t n = c * RO_BLOCK + s;
+        for (int d = 0; d < d_model; ++d) {
+          const int64_t idx = (bh * n_pad + n) * d_model + d;
+          uint8_t code = 0;
+          if (n < n_valid) code = ro_e4m3_encode(bf16_to_f32(x[idx]) * inv);
+          codes[idx] = code;
+          deq[idx] = ro_e4m3_value(code) * (double)sc;
+        }
+      }
+    }
+  }
+}
+
+/* ------------------------------------------------------------ full forward */
+static void widen(const uint16_t *x, int64_t count, double *y) {
+  for (int64_t i = 0; i < count; ++i) y[i] = (double)bf16_to_f32(x[i]);
+}
+
+/*
+ * The whole RoLA forward for `bh_count` (batch, head) slices of bf16 tokens.
+ * map_out [BH, nb, kb]; out [BH, n_pad, D] fp64.  Threads run over slices.
+ * fp8 != 0 runs the sparse branch on the e4m3-dequantised Q, K, V; selection
+ * and the low-rank branch always use the bf16 values.
+ */
+void ro_forward(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *wq,
+                const float *wk, int64_t bh_count, int64_t n_pad, int64_t n_valid, int d_model,
+                int rank, int kb, const int32_t *grid, const int32_t *split, double theta,
+                double scale, int fp8, int32_t *map_out, double *out) {
+  const int64_t nb = n_pad / RO_BLOCK;
+  const int64_t per = n_pad * d_model;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t bh = 0; bh < bh_count; ++bh) {
+    float *qp = (float *)malloc(sizeof(float) * nb * d_model);
+    float *kp = (float *)malloc(sizeof(float) * nb * d_model);
+    float *sc = (float *)malloc(sizeof(float) * nb * nb);
+    double *qd = (double *)malloc(sizeof(double) * per);
+    double *kd = (double *)malloc(sizeof(double) * per);
+    double *vd = (double *)malloc(sizeof(double) * per);
+    double *S = (double *)malloc(sizeof(double) * rank * d_model);
+    double *z = (double *)malloc(sizeof(double) * rank);
+    double *lr = (double *)malloc(sizeof(double) * d_model);
+    double *buf = (double *)malloc(sizeof(double) * kb * RO_BLOCK);
+    int32_t *map = map_out + bh * nb * kb;
+    const uint16_t *qb = q + bh * per, *kbf = k + bh * per, *vb = v + bh * per;
+
+    ro_pool(qb, 1, n_pad, n_valid, d_model, qp);
+    ro_pool(kbf, 1, n_pad, n_valid, d_model, kp);
+    ro_scores(qp, kp, 1, (int)nb, d_model, sc);
+    ro_select(sc, 1, (int)nb, (int)nb, kb, map);
+
+    widen(qb, per, qd);
+    widen(kbf, per, kd);
+    widen(vb, per, vd);
+    ro_lowrank_state(kd, vd, wk, 1, n_pad, n_valid, d_model, rank, grid, split, theta, S, z);
+
+    double *qs = qd, *ks = kd, *vs = vd;
+    uint8_t *codes = NULL;
+    float *scl = NULL;
+    if (fp8) {
+      codes = (uint8_t *)malloc((size_t)per);
+      scl = (float *)malloc(sizeof(float) * nb);
+      qs = (double *)malloc(sizeof(double) * per);
+      ks = (double *)malloc(sizeof(double) * per);
+      vs = (double *)malloc(sizeof(double) * per);
+      ro_quant_e4m3(qb, 1, n_pad, n_valid, d_model, codes, scl, qs);
+      ro_quant_e4m3(kbf, 1, n_pad, n_valid, d_model, codes, scl, ks);
+      ro_quant_e4m3(vb, 1, n_pad, n_valid, d_model, codes, scl, vs);
+    }
+    double *ob = out + bh * per;
+    for (int64_t n = 0; n < n_pad; ++n) {
+      double *on = ob + n * d_model;
+      if (n >= n_valid) {
+        for (int d = 0; d < d_model; ++d) on[d] = 0.0;
+        continue;
+      }
+      sparse_row(qs + n * d_model, ks, vs, map + (n / RO_BLOCK) * kb, kb, n_valid, d_model, scale,
+                 on, buf);
+      const int64_t row = n; /* rows are relative to this slice */
+      ro_lowrank_rows(qd, wq, S, z, n_pad, d_model, rank, grid, split, theta, 1, &row, lr);
+      for (int d = 0; d < d_model; ++d) on[d] += lr[d];
+    }
+    if (fp8) {
+      free(codes); free(scl); free(qs); free(ks); free(vs);
+    }
+    free(qp); free(kp); free(sc); free(qd); free(kd); free(vd);
+    free(S); free(z); free(lr); free(buf);
+  }
+}
