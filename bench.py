@@ -1,0 +1,209 @@
+"""Benchmark of the RoLA attention forward (librola on one MI355X).
+
+One step = one fused rola_forward over the whole workload (block pooling and
+selection, low-rank state, block-sparse attention with the low-rank apply and
+merge), on seeded synthetic Wan-shaped bf16 Q/K/V already resident in HBM.
+Default workload: Wan2.1-14B-720P attention shape (B=1, 40 heads, head_dim
+128, 21x45x80 latent grid, N=75600 -> 75648), topk 0.03 (35 of 1182 key blocks
+kept), rank 32.
+
+Prints one JSON line: value = kept-block TFLOP/s of the whole forward, plus the
+per-kernel times measured with HIP events on the call's stream inside the
+timed region, the roofline of the dominant kernel and the CPU oracle baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "RoLA fwd ms + kept-block TFLOP/s (% MFMA peak), Wan-14B-720P shape, topk 0.03"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+DOMINANT = "attn_sparse_lowrank"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_sparse_lowrank_wan14b_720p_traffic.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in ("sparse_rank_attention_amd/csrc/rola_kernels.hip", "sparse_rank_attention_amd/csrc/rola_internal.h"):
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="wan14b_720p")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-baseline-child", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--sample-stride", type=int, default=4,
+                    help="CPU baseline: every n-th query block of one head")
+    return ap.parse_args()
+
+
+# --------------------------------------------------------------- CPU baseline
+def cpu_baseline_child(args):
+    """Runs in a child process with OMP_NUM_THREADS=1: the oracle on one head of
+    the workload -- full block selection and low-rank state, and both branches
+    for every `sample_stride`-th query block -- extrapolated linearly to the
+    whole workload."""
+    import numpy as np
+
+    import oracle
+    from sparse_rank_attention_amd import workloads as W
+
+    w = W.WORKLOADS[args.workload]
+    q, k, v = W.make_qkv(w, heads=[0], threads=1)
+    wq, wk = W.make_proj(w)
+    q, k, v = q[0], k[0], v[0]
+    oracle.lib()
+    t0 = time.perf_counter()
+    bmap = oracle.block_map(q, k, w.n_tokens, w.kb)
+    t1 = time.perf_counter()
+    qf, kf, vf = (oracle.widen_bf16(x) for x in (q, k, v))
+    S, z = oracle.lowrank_state(kf, vf, wk, w.n_tokens, w.grid)
+    t2 = time.perf_counter()
+    qbs = list(range(0, w.nb, args.sample_stride))
+    rows = np.array([n for qb in qbs for n in range(qb * 64, min(qb * 64 + 64, w.n_tokens))])
+    sp = oracle.sparse_rows(qf, kf, vf, bmap, w.n_tokens, rows)
+    lr = oracle.lowrank_rows(qf, wq, S, z, w.grid, rows)
+    t3 = time.perf_counter()
+    assert np.isfinite(sp + lr).all()
+    rows_full = w.n_tokens
+    per_head = (t1 - t0) + (t2 - t1) + (t3 - t2) * rows_full / rows.size
+    total_s = per_head * w.batch * w.heads
+    print(json.dumps({"total_s": total_s, "sample_s": t3 - t0, "rows": int(rows.size),
+                      "select_s": t1 - t0, "state_s": t2 - t1, "rows_s": t3 - t2}))
+
+
+def cpu_baseline(args, w):
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    cmd = [sys.executable, os.path.abspath(__file__), "--cpu-baseline-child", "--workload", args.workload,
+           "--sample-stride", str(args.sample_stride)]
+    res = subprocess.run(cmd, env=env, capture_output=True, text=True, timeout=600)
+    if res.returncode != 0:
+        raise RuntimeError("cpu baseline failed: " + res.stderr[-2000:])
+    r = json.loads(res.stdout.strip().splitlines()[-1])
+    ms = r["total_s"] * 1e3
+    return {
+        "value": w.kept_block_flop() / (r["total_s"]) / 1e12,
+        "unit": "TFLOP/s (kept-block)",
+        "ms": ms,
+        "cores": 1,
+        "kind": "oracle",
+        "sample": ("oracle (C, fp64 branches, 1 thread) on head 0 of %s: full block selection (%.2f s) and "
+                   "low-rank state (%.2f s), both branches on every %d-th query block (%d rows, %.2f s); "
+                   "extrapolated linearly to all %d heads and rows"
+                   % (args.workload, r["select_s"], r["state_s"], args.sample_stride, r["rows"], r["rows_s"],
+                      w.batch * w.heads)),
+    }
+
+
+# -------------------------------------------------------------------- main
+def main():
+    args = parse()
+    if args.cpu_baseline_child:
+        cpu_baseline_child(args)
+        return
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the RoLA forward shards by heads with no "
+              "collective, and this build runs on a single MI355X (use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from sparse_rank_attention_amd import rola, workloads as W
+
+    w = W.WORKLOADS[args.workload]
+    print("[bench] generating %s inputs" % w.name, file=sys.stderr, flush=True)
+    q, k, v = W.make_qkv(w)
+    wq, wk = W.make_proj(w)
+    dev = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    del q, k, v
+    wqd, wkd = torch.from_numpy(wq).cuda(), torch.from_numpy(wk).cuda()
+    cfg = rola.Config(topk=w.topk, rank=w.rank)
+    out = torch.empty_like(qd)
+    stream = torch.cuda.current_stream()
+    print("[bench] warmup %d" % args.warmup, file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        rola.rola_forward(qd, kd, vd, wqd, wkd, w.grid, cfg, out=out, stream=stream)
+    torch.cuda.synchronize()
+    rola.timing_read()  # drop anything recorded so far
+
+    print("[bench] timing %d steps" % args.steps, file=sys.stderr, flush=True)
+    rola.timing_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        rola.rola_forward(qd, kd, vd, wqd, wkd, w.grid, cfg, out=out, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    rola.timing_enable(False)
+    ms = e0.elapsed_time(e1) / args.steps
+    kernels = rola.timing_read()
+    kern_ms = {name: tot / n for name, (n, tot) in kernels.items()}
+
+    kept = w.kept_block_flop()
+    dense = w.dense_equiv_flop()
+    t_attn = kern_ms[DOMINANT] * 1e-3
+    achieved = kept / t_attn / 1e12
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_source_hash") == kernel_source_hash() and tr.get("workload") == w.name:
+            traffic = tr["bytes_per_launch"]
+    # algorithmic HBM bytes of the streaming pass: read Q, K, V once
+    n_tok = w.batch * w.heads * w.n_pad
+    pass1_bytes = 3 * n_tok * w.head_dim * 2
+    pass1_ms = kern_ms.get("pass1_pool_state_vt")
+    rec = {
+        "metric": METRIC,
+        "value": round(kept / (ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s (kept-block, whole forward)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Wan-shaped smooth field + noise Q/K, N(0,1) V; no weights)",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim,
+                   "grid": list(w.grid), "n_tokens": w.n_tokens, "topk": w.topk, "kb": w.kb, "nb": w.nb,
+                   "rank": w.rank},
+        "fwd_ms": round(ms, 4),
+        "dense_equiv_tflops": round(dense / (ms * 1e-3) / 1e12, 1),
+        "kept_block_tflops": round(kept / (ms * 1e-3) / 1e12, 1),
+        "kernel_ms": {k_: round(v_, 4) for k_, v_ in sorted(kern_ms.items())},
+        "roofline": {"kernel": DOMINANT, "bound": "mfma", "achieved": round(achieved, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+    }
+    if pass1_ms:
+        gbs = pass1_bytes / (pass1_ms * 1e-3) / 1e9
+        rec["pass1_roofline"] = {"kernel": "pass1_pool_state_vt", "bound": "hbm", "achieved": round(gbs, 1),
+                                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle, 1 thread, sampled)", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(args, w)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,401 @@
+// rola_api.cpp -- host side of librola: argument validation, workspace
+// planning and kernel launch sequences for the four entry points of rola.h.
+//
+// Every entry point validates all of its arguments before it launches
+// anything, so a call either launches nothing (status != ROLA_OK) or
+// enqueues its whole kernel sequence on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/rola.h"
+#include "rola_internal.h"
+
+namespace {
+
+constexpr int64_t kAlign = 256;
+
+int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// ------------------------------------------------------------------ plan
+struct Plan {
+  int B, H, D, r, kb, nb;
+  int64_t N, n_pad, BH;
+  int split[3];
+  double theta;
+  float scale;
+  int grid[3];
+  int tab_total, tab1, tab2;
+  int nchunks, cpc;
+  // workspace offsets (bytes)
+  int64_t off_tab, off_wqT, off_wkT, off_qp, off_kp, off_scores, off_map, off_vt, off_part, off_st,
+      off_z, total;
+};
+
+int32_t make_plan(const rola_problem *p, const rola_config *c, Plan *pl) {
+  if (!p || !c || !pl) return ROLA_ERR_INVALID_ARG;
+  if (p->batch < 1 || p->heads < 1 || p->grid_t < 1 || p->grid_h < 1 || p->grid_w < 1)
+    return ROLA_ERR_INVALID_ARG;
+  if (p->head_dim != 64 && p->head_dim != 128) return ROLA_ERR_UNSUPPORTED;
+  if (c->rank != 16 && c->rank != 32) return ROLA_ERR_UNSUPPORTED;
+  if (c->precision != ROLA_PREC_BF16 && c->precision != ROLA_PREC_FP8) return ROLA_ERR_INVALID_ARG;
+  if (c->precision == ROLA_PREC_FP8) return ROLA_ERR_UNSUPPORTED;
+  if (c->out_dtype != ROLA_OUT_BF16 && c->out_dtype != ROLA_OUT_F32) return ROLA_ERR_INVALID_ARG;
+  const int D = p->head_dim;
+  const int64_t N = (int64_t)p->grid_t * p->grid_h * p->grid_w;
+  const int64_t nb64 = (N + ROLA_BLOCK - 1) / ROLA_BLOCK;
+  if (nb64 > ROLA_MAX_BLOCKS) return ROLA_ERR_UNSUPPORTED;
+  const int nb = (int)nb64;
+  // strides: 16-byte aligned rows, rows at least D long
+  if (p->stride_n < D || p->stride_n % 8 || p->stride_h % 8 || p->stride_b % 8 ||
+      p->stride_h < 0 || p->stride_b < 0)
+    return ROLA_ERR_ALIGNMENT;
+  int kb;
+  if (c->kb_override > 0) {
+    if (c->kb_override > nb) return ROLA_ERR_INVALID_ARG;
+    kb = c->kb_override;
+  } else {
+    if (!(c->topk > 0.0f && c->topk <= 1.0f)) return ROLA_ERR_INVALID_ARG;
+    double kk = std::floor((double)c->topk * nb + 1e-6);
+    kb = (int)std::max(1.0, std::min((double)nb, kk));
+  }
+  if (c->kb_override < 0) return ROLA_ERR_INVALID_ARG;
+  int split[3] = {c->rope_split[0], c->rope_split[1], c->rope_split[2]};
+  if (split[0] == 0 && split[1] == 0 && split[2] == 0) {
+    split[0] = D / 4;
+    split[1] = (D - split[0]) / 2;
+    split[2] = D - split[0] - split[1];
+  }
+  for (int a = 0; a < 3; ++a)
+    if (split[a] < 0 || split[a] % 2) return ROLA_ERR_INVALID_ARG;
+  if (split[0] + split[1] + split[2] != D) return ROLA_ERR_INVALID_ARG;
+  if (std::isnan(c->rope_theta) || std::isnan(c->softmax_scale) || std::isinf(c->softmax_scale) ||
+      std::isinf(c->rope_theta))
+    return ROLA_ERR_INVALID_ARG;
+
+  Plan &P = *pl;
+  P.B = p->batch; P.H = p->heads; P.D = D; P.r = c->rank; P.kb = kb; P.nb = nb;
+  P.N = N; P.n_pad = (int64_t)nb * ROLA_BLOCK; P.BH = (int64_t)P.B * P.H;
+  for (int a = 0; a < 3; ++a) P.split[a] = split[a];
+  P.theta = c->rope_theta > 0.0f ? (double)c->rope_theta : 10000.0;
+  P.scale = c->softmax_scale > 0.0f ? c->softmax_scale : (float)(1.0 / std::sqrt((double)D));
+  P.grid[0] = p->grid_t; P.grid[1] = p->grid_h; P.grid[2] = p->grid_w;
+  P.tab1 = P.grid[0] * (split[0] / 2);
+  P.tab2 = P.tab1 + P.grid[1] * (split[1] / 2);
+  P.tab_total = P.tab2 + P.grid[2] * (split[2] / 2);
+  // pass-1 chunking: about 4096 workgroups in total
+  int nchunks = (int)std::max<int64_t>(1, std::min<int64_t>(nb, (4096 + P.BH - 1) / P.BH));
+  P.cpc = (nb + nchunks - 1) / nchunks;
+  P.nchunks = (nb + P.cpc - 1) / P.cpc;
+
+  int64_t o = 0;
+  P.off_tab = o; o = align_up(o + (int64_t)P.tab_total * 8);
+  P.off_wqT = o; o = align_up(o + 32LL * D * 2);
+  P.off_wkT = o; o = align_up(o + 32LL * D * 2);
+  P.off_qp = o; o = align_up(o + P.BH * nb * D * 4);
+  P.off_kp = o; o = align_up(o + P.BH * nb * D * 4);
+  P.off_scores = o; o = align_up(o + P.BH * nb * (int64_t)nb * 4);
+  P.off_map = o; o = align_up(o + P.BH * nb * (int64_t)kb * 4);
+  P.off_vt = o; o = align_up(o + P.BH * nb * 64LL * D * 2);
+  P.off_part = o; o = align_up(o + P.BH * P.nchunks * (int64_t)(D * 32 + 32) * 4);
+  P.off_st = o; o = align_up(o + P.BH * D * 32LL * 2);
+  P.off_z = o; o = align_up(o + P.BH * 32LL * 4);
+  P.total = o;
+  return ROLA_OK;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// ------------------------------------------------------------- timing
+struct TimedLaunch {
+  std::string name;
+  hipEvent_t start, stop;
+};
+std::mutex g_mu;
+bool g_timing = false;
+std::vector<TimedLaunch> g_launches;
+std::vector<hipEvent_t> g_free_events;
+
+hipEvent_t take_event() {
+  if (!g_free_events.empty()) {
+    hipEvent_t e = g_free_events.back();
+    g_free_events.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Runs `launch` on stream `st`, bracketed by events when timing is on.
+template <typename F>
+int32_t timed(const char *name, hipStream_t st, F &&launch) {
+  hipEvent_t a = nullptr, b = nullptr;
+  if (g_timing) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    a = take_event();
+    b = take_event();
+    if (a) hipEventRecord(a, st);
+  }
+  launch();
+  hipError_t err = hipGetLastError();
+  if (g_timing && a && b) {
+    hipEventRecord(b, st);
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_launches.push_back({name, a, b});
+  }
+  return err == hipSuccess ? ROLA_OK : ROLA_ERR_DEVICE;
+}
+
+rola::RopeArgsHost rope_args(const Plan &P, uint8_t *ws) {
+  rola::RopeArgsHost r;
+  r.tab = (const float2 *)(ws + P.off_tab);
+  r.off1 = P.split[0];
+  r.off2 = P.split[0] + P.split[1];
+  r.half0 = P.split[0] / 2;
+  r.half1 = P.split[1] / 2;
+  r.half2 = P.split[2] / 2;
+  r.tab1 = P.tab1;
+  r.tab2 = P.tab2;
+  r.grid_h = P.grid[1];
+  r.grid_w = P.grid[2];
+  return r;
+}
+
+int32_t run_setup(const Plan &P, const float *wq, const float *wk, uint8_t *ws, hipStream_t st) {
+  rola::SetupArgs a;
+  a.wq = wq; a.wk = wk; a.D = P.D; a.rank = P.r;
+  a.wqT = (uint16_t *)(ws + P.off_wqT);
+  a.wkT = (uint16_t *)(ws + P.off_wkT);
+  a.tab = (float2 *)(ws + P.off_tab);
+  a.tab_total = P.tab_total;
+  a.g0 = P.grid[0]; a.g1 = P.grid[1];
+  a.h0 = P.split[0] / 2; a.h1 = P.split[1] / 2; a.h2 = P.split[2] / 2;
+  a.theta = P.theta;
+  return timed("setup", st, [&] { rola::launch_setup(a, st); });
+}
+
+int32_t run_pass1(const Plan &P, const rola_problem *p, const void *q, const void *k, const void *v,
+                  uint8_t *ws, bool pool, bool state, bool vt, hipStream_t st) {
+  rola::Pass1Args a;
+  a.q = (const uint16_t *)q; a.k = (const uint16_t *)k; a.v = (const uint16_t *)v;
+  a.stride_b = p->stride_b; a.stride_h = p->stride_h; a.stride_n = p->stride_n;
+  a.heads = P.H; a.nb = P.nb; a.n_tokens = P.N; a.cpc = P.cpc; a.rank = P.r;
+  const int64_t tail = P.N - (int64_t)(P.nb - 1) * ROLA_BLOCK;
+  a.inv_tail = 1.0f / (float)tail;
+  a.qp = (float *)(ws + P.off_qp);
+  a.kp = (float *)(ws + P.off_kp);
+  a.vt = (uint16_t *)(ws + P.off_vt);
+  a.wkT = (const uint16_t *)(ws + P.off_wkT);
+  a.state_part = (float *)(ws + P.off_part);
+  a.rope = rope_args(P, ws);
+  const char *name = (pool && state && vt) ? "pass1_pool_state_vt"
+                     : pool                 ? "pass1_pool"
+                     : state                ? "pass1_state"
+                                            : "pass1_vt";
+  return timed(name, st, [&] { rola::launch_pass1(a, P.D, P.nchunks, (int)P.BH, pool, state, vt, st); });
+}
+
+int32_t run_reduce(const Plan &P, uint8_t *ws, hipStream_t st) {
+  return timed("state_reduce", st, [&] {
+    rola::launch_state_reduce((const float *)(ws + P.off_part), P.nchunks, P.D, P.r, (int)P.BH,
+                              (uint16_t *)(ws + P.off_st), (float *)(ws + P.off_z), st);
+  });
+}
+
+int32_t run_select(const Plan &P, uint8_t *ws, float *scores, int32_t *map, hipStream_t st) {
+  int32_t s = timed("scores", st, [&] {
+    rola::launch_scores((const float *)(ws + P.off_qp), (const float *)(ws + P.off_kp), scores, P.nb,
+                        P.D, (int)P.BH, st);
+  });
+  if (s != ROLA_OK) return s;
+  return timed("topk", st, [&] { rola::launch_topk(scores, map, P.nb, P.kb, P.BH * P.nb, st); });
+}
+
+int32_t run_attn(const Plan &P, const rola_problem *p, const rola_config *c, const void *q,
+                 const void *k, const int32_t *map, void *out, uint8_t *ws, bool sparse,
+                 bool lowrank, bool accum, hipStream_t st) {
+  rola::AttnArgs a;
+  a.q = (const uint16_t *)q; a.k = (const uint16_t *)k;
+  a.vt = (const uint16_t *)(ws + P.off_vt);
+  a.map = map; a.out = out;
+  a.stride_b = p->stride_b; a.stride_h = p->stride_h; a.stride_n = p->stride_n;
+  a.heads = P.H; a.nb = P.nb; a.kb = P.kb; a.rank = P.r; a.n_tokens = P.N;
+  a.tiles = P.BH * P.nb;
+  a.tiles_per_xcd = (a.tiles + 7) / 8;
+  a.scale_log2e = (float)((double)P.scale * 1.4426950408889634);
+  a.wqT = (const uint16_t *)(ws + P.off_wqT);
+  a.st = (const uint16_t *)(ws + P.off_st);
+  a.z = (const float *)(ws + P.off_z);
+  a.rope = rope_args(P, ws);
+  const char *name = sparse && lowrank ? "attn_sparse_lowrank" : sparse ? "attn_sparse" : "attn_lowrank";
+  return timed(name, st, [&] {
+    rola::launch_attn(a, P.D, sparse, lowrank, accum != 0, c->out_dtype == ROLA_OUT_F32, st);
+  });
+}
+
+#define ROLA_TRY(x)                  \
+  do {                               \
+    int32_t _s = (x);                \
+    if (_s != ROLA_OK) return _s;    \
+  } while (0)
+
+}  // namespace
+
+// ---------------------------------------------------------------- C ABI
+extern "C" {
+
+int32_t rola_abi_version(void) { return ROLA_ABI_VERSION; }
+
+const char *rola_status_str(int32_t s) {
+  switch (s) {
+    case ROLA_OK: return "ok";
+    case ROLA_ERR_INVALID_ARG: return "invalid argument";
+    case ROLA_ERR_UNSUPPORTED: return "unsupported problem (head_dim, rank, precision or size)";
+    case ROLA_ERR_ALIGNMENT: return "pointer or stride not 16-byte aligned";
+    case ROLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case ROLA_ERR_DEVICE: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int32_t rola_plan(const rola_problem *prob, const rola_config *cfg, rola_plan_info *out) {
+  if (!out) return ROLA_ERR_INVALID_ARG;
+  Plan P;
+  ROLA_TRY(make_plan(prob, cfg, &P));
+  out->n_tokens = P.N;
+  out->nb = P.nb;
+  out->kb = P.kb;
+  out->n_pad = P.n_pad;
+  out->workspace_bytes = P.total;
+  return ROLA_OK;
+}
+
+int32_t rola_select_blocks(const rola_problem *prob, const rola_config *cfg, const void *q,
+                           const void *k, int32_t *block_idx, float *pooled_scores,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+  Plan P;
+  ROLA_TRY(make_plan(prob, cfg, &P));
+  if (!q || !k || !block_idx) return ROLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(block_idx) ||
+      (pooled_scores && !aligned16(pooled_scores)))
+    return ROLA_ERR_ALIGNMENT;
+  if (!workspace || (int64_t)workspace_bytes < P.total) return ROLA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return ROLA_ERR_ALIGNMENT;
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t *ws = (uint8_t *)workspace;
+  ROLA_TRY(run_pass1(P, prob, q, k, nullptr, ws, true, false, false, st));
+  float *scores = pooled_scores ? pooled_scores : (float *)(ws + P.off_scores);
+  return run_select(P, ws, scores, block_idx, st);
+}
+
+int32_t rola_sparse_attn(const rola_problem *prob, const rola_config *cfg, const void *q,
+                         const void *k, const void *v, const int32_t *block_idx, void *out,
+                         int32_t accumulate, void *workspace, size_t workspace_bytes,
+                         void *stream) {
+  Plan P;
+  ROLA_TRY(make_plan(prob, cfg, &P));
+  if (!q || !k || !v || !block_idx || !out) return ROLA_ERR_INVALID_ARG;
+  if (accumulate != 0 && accumulate != 1) return ROLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(block_idx))
+    return ROLA_ERR_ALIGNMENT;
+  if (!workspace || (int64_t)workspace_bytes < P.total) return ROLA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return ROLA_ERR_ALIGNMENT;
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t *ws = (uint8_t *)workspace;
+  ROLA_TRY(run_pass1(P, prob, nullptr, nullptr, v, ws, false, false, true, st));
+  return run_attn(P, prob, cfg, q, k, block_idx, out, ws, true, false, accumulate != 0, st);
+}
+
+int32_t rola_lowrank_attn(const rola_problem *prob, const rola_config *cfg, const void *q,
+                          const void *k, const void *v, const float *wq, const float *wk,
+                          void *out, int32_t accumulate, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+  Plan P;
+  ROLA_TRY(make_plan(prob, cfg, &P));
+  if (!q || !k || !v || !wq || !wk || !out) return ROLA_ERR_INVALID_ARG;
+  if (accumulate != 0 && accumulate != 1) return ROLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ROLA_ERR_ALIGNMENT;
+  if (((uintptr_t)wq & 3u) || ((uintptr_t)wk & 3u)) return ROLA_ERR_ALIGNMENT;
+  if (!workspace || (int64_t)workspace_bytes < P.total) return ROLA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return ROLA_ERR_ALIGNMENT;
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t *ws = (uint8_t *)workspace;
+  ROLA_TRY(run_setup(P, wq, wk, ws, st));
+  ROLA_TRY(run_pass1(P, prob, nullptr, k, v, ws, false, true, false, st));
+  ROLA_TRY(run_reduce(P, ws, st));
+  return run_attn(P, prob, cfg, q, nullptr, nullptr, out, ws, false, true, accumulate != 0, st);
+}
+
+int32_t rola_forward(const rola_problem *prob, const rola_config *cfg, const void *q,
+                     const void *k, const void *v, const float *wq, const float *wk,
+                     int32_t *block_idx_out, void *out, void *workspace,
+                     size_t workspace_bytes, void *stream) {
+  Plan P;
+  ROLA_TRY(make_plan(prob, cfg, &P));
+  if (!q || !k || !v || !wq || !wk || !out) return ROLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+      (block_idx_out && !aligned16(block_idx_out)))
+    return ROLA_ERR_ALIGNMENT;
+  if (((uintptr_t)wq & 3u) || ((uintptr_t)wk & 3u)) return ROLA_ERR_ALIGNMENT;
+  if (!workspace || (int64_t)workspace_bytes < P.total) return ROLA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return ROLA_ERR_ALIGNMENT;
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t *ws = (uint8_t *)workspace;
+  int32_t *map = block_idx_out ? block_idx_out : (int32_t *)(ws + P.off_map);
+  ROLA_TRY(run_setup(P, wq, wk, ws, st));
+  ROLA_TRY(run_pass1(P, prob, q, k, v, ws, true, true, true, st));
+  ROLA_TRY(run_reduce(P, ws, st));
+  ROLA_TRY(run_select(P, ws, (float *)(ws + P.off_scores), map, st));
+  return run_attn(P, prob, cfg, q, k, map, out, ws, true, true, false, st);
+}
+
+int32_t rola_timing_enable(int32_t on) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_timing = on != 0;
+  return ROLA_OK;
+}
+
+int32_t rola_timing_read(rola_kernel_time *out, int32_t max) {
+  if (!out || max < 0) return -1;
+  std::lock_guard<std::mutex> lk(g_mu);
+  std::vector<rola_kernel_time> agg;
+  for (auto &l : g_launches) {
+    float ms = 0.0f;
+    if (hipEventSynchronize(l.stop) != hipSuccess) return -1;
+    if (hipEventElapsedTime(&ms, l.start, l.stop) != hipSuccess) return -1;
+    g_free_events.push_back(l.start);
+    g_free_events.push_back(l.stop);
+    bool found = false;
+    for (auto &a : agg) {
+      if (l.name == a.name) {
+        a.launches += 1;
+        a.total_ms += ms;
+        found = true;
+        break;
+      }
+    }
+    if (!found) {
+      rola_kernel_time t;
+      std::memset(&t, 0, sizeof t);
+      std::strncpy(t.name, l.name.c_str(), sizeof t.name - 1);
+      t.launches = 1;
+      t.total_ms = ms;
+      agg.push_back(t);
+    }
+  }
+  g_launches.clear();
+  int32_t n = 0;
+  for (auto &a : agg) {
+    if (n >= max) break;
+    out[n++] = a;
+  }
+  return n;
+}
+
+}  // extern "C"

@@ -1,0 +1,70 @@
+// rola_internal.h -- argument blocks shared by the librola host code and its kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rola {
+
+struct RopeArgsHost {
+  const float2 *tab;
+  int off1, off2;
+  int half0, half1, half2;
+  int tab1, tab2;
+  int grid_h, grid_w;
+};
+
+struct SetupArgs {
+  const float *wq, *wk;
+  int D, rank;
+  uint16_t *wqT, *wkT;  // bf16 [32][D]
+  float2 *tab;
+  int tab_total;
+  int g0, g1;           // grid_t, grid_h (positions per axis for the first two axes)
+  int h0, h1, h2;       // pairs per axis
+  double theta;
+};
+
+struct Pass1Args {
+  const uint16_t *q, *k, *v;
+  int64_t stride_b, stride_h, stride_n;
+  int heads;
+  int nb;
+  int64_t n_tokens;
+  int cpc;              // 64-token blocks per workgroup
+  int rank;
+  float inv_tail;       // fl32(1/valid) of the tail block
+  float *qp, *kp;       // pooled [BH][nb][D]
+  uint16_t *vt;         // [BH][nb][64*D] transposed V tiles
+  const uint16_t *wkT;  // bf16 [32][D]
+  float *state_part;    // [BH][nchunks][D*32 + 32]
+  RopeArgsHost rope;
+};
+
+struct AttnArgs {
+  const uint16_t *q, *k, *vt;
+  const int32_t *map;
+  void *out;
+  int64_t stride_b, stride_h, stride_n;
+  int heads, nb, kb, rank;
+  int64_t n_tokens;
+  int64_t tiles;        // BH * nb
+  int64_t tiles_per_xcd;
+  float scale_log2e;
+  const uint16_t *wqT;  // bf16 [32][D]
+  const uint16_t *st;   // bf16 [BH][D][32] (rank permuted)
+  const float *z;       // [BH][32]
+  RopeArgsHost rope;
+};
+
+void launch_setup(const SetupArgs &a, hipStream_t st);
+void launch_pass1(const Pass1Args &a, int D, int nchunks, int bh, bool pool, bool state, bool vt,
+                  hipStream_t st);
+void launch_state_reduce(const float *part, int nchunks, int D, int rank, int bh, uint16_t *st_out,
+                         float *z, hipStream_t st);
+void launch_scores(const float *qp, const float *kp, float *s, int nb, int D, int bh,
+                   hipStream_t st);
+void launch_topk(const float *s, int32_t *map, int nb, int kb, int64_t rows, hipStream_t st);
+void launch_attn(const AttnArgs &a, int D, bool sparse, bool lowrank, bool accum, bool outf32,
+                 hipStream_t st);
+
+}  // namespace rola

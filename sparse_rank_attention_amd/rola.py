@@ -1,0 +1,232 @@
+"""Python binding of librola (ctypes).  Argument marshalling only: every step of
+RoLA attention runs in the HIP kernels of ``librola.so``; PyTorch provides the
+device memory and the stream.  There is no CPU or PyTorch fallback: calls fail
+if the library is missing or the tensors are not on a GPU.
+
+Tensors: q, k, v (and out) are ``[B, H, n_pad, D]`` bf16 views on one device
+with the last dim contiguous and identical strides; rows N..n_pad-1 of the
+inputs are ignored and written as zero in the output.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+from . import build as _build
+
+ROLA_OK = 0
+ROLA_PREC_BF16, ROLA_PREC_FP8 = 0, 1
+ROLA_OUT_BF16, ROLA_OUT_F32 = 0, 1
+BLOCK = 64
+
+
+class RolaProblem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("grid_t", ctypes.c_int32), ("grid_h", ctypes.c_int32), ("grid_w", ctypes.c_int32),
+                ("stride_b", ctypes.c_int64), ("stride_h", ctypes.c_int64), ("stride_n", ctypes.c_int64)]
+
+
+class RolaConfig(ctypes.Structure):
+    _fields_ = [("topk", ctypes.c_float), ("kb_override", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("rope_split", ctypes.c_int32 * 3), ("rope_theta", ctypes.c_float),
+                ("softmax_scale", ctypes.c_float), ("precision", ctypes.c_int32),
+                ("out_dtype", ctypes.c_int32)]
+
+
+class RolaPlanInfo(ctypes.Structure):
+    _fields_ = [("n_tokens", ctypes.c_int64), ("nb", ctypes.c_int32), ("kb", ctypes.c_int32),
+                ("n_pad", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64)]
+
+
+class RolaKernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_int32), ("total_ms", ctypes.c_double)]
+
+
+EXPORTS = ["rola_abi_version", "rola_status_str", "rola_plan", "rola_select_blocks",
+           "rola_sparse_attn", "rola_lowrank_attn", "rola_forward", "rola_timing_enable",
+           "rola_timing_read"]
+
+_lib = None
+
+
+def library_path() -> str:
+    return _build.LIB
+
+
+def lib():
+    """Load librola.so (building it in-tree first if it is missing or stale)."""
+    global _lib
+    if _lib is None:
+        _build.ensure_built()
+        L = ctypes.CDLL(_build.LIB)
+        P, I32 = ctypes.c_void_p, ctypes.c_int32
+        L.rola_abi_version.restype = I32
+        L.rola_status_str.restype = ctypes.c_char_p
+        L.rola_status_str.argtypes = [I32]
+        L.rola_plan.restype = I32
+        L.rola_plan.argtypes = [P, P, P]
+        L.rola_select_blocks.restype = I32
+        L.rola_select_blocks.argtypes = [P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.rola_sparse_attn.restype = I32
+        L.rola_sparse_attn.argtypes = [P, P, P, P, P, P, P, I32, P, ctypes.c_size_t, P]
+        L.rola_lowrank_attn.restype = I32
+        L.rola_lowrank_attn.argtypes = [P, P, P, P, P, P, P, P, I32, P, ctypes.c_size_t, P]
+        L.rola_forward.restype = I32
+        L.rola_forward.argtypes = [P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.rola_timing_enable.restype = I32
+        L.rola_timing_enable.argtypes = [I32]
+        L.rola_timing_read.restype = I32
+        L.rola_timing_read.argtypes = [P, I32]
+        _lib = L
+    return _lib
+
+
+class RolaError(RuntimeError):
+    pass
+
+
+def _check(status: int, what: str):
+    if status != ROLA_OK:
+        raise RolaError("%s failed: %s (status %d)" % (what, lib().rola_status_str(status).decode(), status))
+
+
+@dataclass
+class Config:
+    topk: float = 0.1
+    rank: int = 32
+    kb_override: int = 0
+    rope_split: tuple = (0, 0, 0)
+    rope_theta: float = 10000.0
+    softmax_scale: float = 0.0
+    precision: int = ROLA_PREC_BF16
+    out_dtype: int = ROLA_OUT_BF16
+
+    def c(self) -> RolaConfig:
+        return RolaConfig(self.topk, self.kb_override, self.rank, (ctypes.c_int32 * 3)(*self.rope_split),
+                          self.rope_theta, self.softmax_scale, self.precision, self.out_dtype)
+
+
+def problem(q: torch.Tensor, grid) -> RolaProblem:
+    if q.dim() != 4:
+        raise ValueError("expected [B, H, n_pad, D]")
+    B, H, _, D = q.shape
+    sb, sh, sn, sd = q.stride()
+    if sd != 1:
+        raise ValueError("head_dim must be contiguous")
+    return RolaProblem(B, H, D, grid[0], grid[1], grid[2], sb, sh, sn)
+
+
+def plan(prob: RolaProblem, cfg: Config) -> RolaPlanInfo:
+    info = RolaPlanInfo()
+    c = cfg.c()
+    _check(lib().rola_plan(ctypes.byref(prob), ctypes.byref(c), ctypes.byref(info)), "rola_plan")
+    return info
+
+
+_ws_cache = {}
+
+
+def workspace(device, nbytes: int) -> torch.Tensor:
+    """Caller-owned scratch for librola (cached per device; grows on demand)."""
+    key = torch.device(device).index
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _ws_cache[key] = buf
+    return buf
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _check_tokens(q, *others):
+    if not q.is_cuda:
+        raise RolaError("librola needs GPU tensors")
+    for t in (q,) + others:
+        if t.dtype != torch.bfloat16:
+            raise RolaError("q, k, v must be bfloat16")
+        if t.shape != q.shape or t.stride() != q.stride() or t.device != q.device:
+            raise RolaError("q, k, v must share shape, strides and device")
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _new_out(q, cfg: Config):
+    dt = torch.float32 if cfg.out_dtype == ROLA_OUT_F32 else torch.bfloat16
+    return torch.empty_strided(q.shape, q.stride(), dtype=dt, device=q.device)
+
+
+def rola_select_blocks(q, k, grid, cfg: Config, block_idx=None, pooled_scores=None, stream=None):
+    """Kept key blocks per query block: int32 [B, H, nb, kb], ascending."""
+    _check_tokens(q, k)
+    prob = problem(q, grid)
+    info = plan(prob, cfg)
+    B, H = q.shape[:2]
+    if block_idx is None:
+        block_idx = torch.empty((B, H, info.nb, info.kb), dtype=torch.int32, device=q.device)
+    ws = workspace(q.device, info.workspace_bytes)
+    c = cfg.c()
+    _check(lib().rola_select_blocks(ctypes.byref(prob), ctypes.byref(c), _ptr(q), _ptr(k), _ptr(block_idx),
+                                    _ptr(pooled_scores), _ptr(ws), ws.numel(), _stream(stream)),
+           "rola_select_blocks")
+    return block_idx
+
+
+def rola_sparse_attn(q, k, v, block_idx, grid, cfg: Config, out=None, accumulate=False, stream=None):
+    _check_tokens(q, k, v)
+    prob = problem(q, grid)
+    info = plan(prob, cfg)
+    out = _new_out(q, cfg) if out is None else out
+    ws = workspace(q.device, info.workspace_bytes)
+    c = cfg.c()
+    _check(lib().rola_sparse_attn(ctypes.byref(prob), ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v),
+                                  _ptr(block_idx), _ptr(out), int(bool(accumulate)), _ptr(ws), ws.numel(),
+                                  _stream(stream)), "rola_sparse_attn")
+    return out
+
+
+def rola_lowrank_attn(q, k, v, wq, wk, grid, cfg: Config, out=None, accumulate=False, stream=None):
+    _check_tokens(q, k, v)
+    prob = problem(q, grid)
+    info = plan(prob, cfg)
+    out = _new_out(q, cfg) if out is None else out
+    ws = workspace(q.device, info.workspace_bytes)
+    c = cfg.c()
+    _check(lib().rola_lowrank_attn(ctypes.byref(prob), ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(wq),
+                                   _ptr(wk), _ptr(out), int(bool(accumulate)), _ptr(ws), ws.numel(),
+                                   _stream(stream)), "rola_lowrank_attn")
+    return out
+
+
+def rola_forward(q, k, v, wq, wk, grid, cfg: Config, out=None, block_idx_out=None, stream=None):
+    """Fused RoLA forward O = O_sparse + O_lr."""
+    _check_tokens(q, k, v)
+    prob = problem(q, grid)
+    info = plan(prob, cfg)
+    out = _new_out(q, cfg) if out is None else out
+    ws = workspace(q.device, info.workspace_bytes)
+    c = cfg.c()
+    _check(lib().rola_forward(ctypes.byref(prob), ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(wq),
+                              _ptr(wk), _ptr(block_idx_out), _ptr(out), _ptr(ws), ws.numel(),
+                              _stream(stream)), "rola_forward")
+    return out
+
+
+def timing_enable(on: bool):
+    lib().rola_timing_enable(1 if on else 0)
+
+
+def timing_read():
+    """Per-kernel {name: (launches, total_ms)} since the last read (synchronises the events)."""
+    buf = (RolaKernelTime * 32)()
+    n = lib().rola_timing_read(buf, 32)
+    if n < 0:
+        raise RolaError("rola_timing_read failed")
+    return {buf[i].name.decode(): (buf[i].launches, buf[i].total_ms) for i in range(n)}

@@ -1,0 +1,109 @@
+"""The C ABI of librola on the host: it loads, exports every declared call, and
+plans and validates without touching a device (no compute calls here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_rank_attention_amd import rola
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+P = ctypes.byref
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "rola.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(rola_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_four_calls():
+    names = _declared_functions()
+    for n in ("rola_select_blocks", "rola_sparse_attn", "rola_lowrank_attn", "rola_forward", "rola_plan"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = rola.lib()
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+    assert set(rola.EXPORTS) == set(_declared_functions())
+    assert L.rola_abi_version() == 1
+
+
+def _prob(B=1, H=40, D=128, grid=(21, 45, 80), sn=None):
+    sn = D if sn is None else sn
+    n_pad = ((grid[0] * grid[1] * grid[2] + 63) // 64) * 64
+    return rola.RolaProblem(B, H, D, grid[0], grid[1], grid[2], H * n_pad * sn, n_pad * sn, sn)
+
+
+def _plan(prob, cfg):
+    info = rola.RolaPlanInfo()
+    c = cfg.c()
+    st = rola.lib().rola_plan(P(prob), P(c), P(info))
+    return st, info
+
+
+@pytest.mark.parametrize("grid,topk,nb,kb", [((4, 16, 16), 0.25, 16, 4), ((21, 30, 52), 0.10, 512, 51),
+                                              ((21, 30, 52), 0.05, 512, 25), ((21, 45, 80), 0.03, 1182, 35),
+                                              ((21, 45, 80), 0.10, 1182, 118), ((21, 45, 80), 0.05, 1182, 59),
+                                              ((1, 1, 40), 0.5, 1, 1), ((21, 45, 80), 1.0, 1182, 1182)])
+def test_plan_block_counts(grid, topk, nb, kb):
+    st, info = _plan(_prob(grid=grid), rola.Config(topk=topk))
+    assert st == 0
+    assert (info.nb, info.kb) == (nb, kb)
+    assert info.n_pad == 64 * nb and info.n_tokens == grid[0] * grid[1] * grid[2]
+    st2, info2 = _plan(_prob(grid=grid), rola.Config(topk=topk))
+    assert info2.workspace_bytes == info.workspace_bytes > 0
+
+
+def test_plan_rejects_bad_arguments():
+    ok = rola.Config(topk=0.1)
+    cases = [
+        (_prob(D=96), ok, 2),                                     # head_dim unsupported
+        (_prob(), rola.Config(topk=0.1, rank=8), 2),              # rank unsupported
+        (_prob(), rola.Config(topk=0.0), 1),                      # topk outside (0, 1]
+        (_prob(), rola.Config(topk=1.5), 1),
+        (_prob(), rola.Config(topk=float("nan")), 1),
+        (_prob(), rola.Config(topk=0.1, kb_override=5000), 1),    # more blocks than exist
+        (_prob(), rola.Config(topk=0.1, rope_split=(32, 48, 46)), 1),  # split must sum to D
+        (_prob(), rola.Config(topk=0.1, rope_split=(33, 47, 48)), 1),  # and be even
+        (_prob(sn=132), ok, 3),                                   # rows not 16-byte aligned
+        (_prob(sn=64), ok, 3),                                    # row shorter than D
+        (_prob(grid=(1, 1, 64 * 4097)), ok, 2),                   # too many blocks
+        (_prob(grid=(0, 45, 80)), ok, 1),
+        (_prob(), rola.Config(topk=0.1, precision=7), 1),
+        (_prob(), rola.Config(topk=0.1, out_dtype=3), 1),
+    ]
+    for prob, cfg, want in cases:
+        st, _ = _plan(prob, cfg)
+        assert st == want, (prob.head_dim, cfg, st)
+
+
+def test_entry_points_validate_before_launch():
+    """Errors are returned before any device work, so these run without a GPU."""
+    L = rola.lib()
+    prob, cfg = _prob(grid=(4, 16, 16), D=64, H=2), rola.Config(topk=0.25, rank=16).c()
+    st, info = _plan(prob, rola.Config(topk=0.25, rank=16))
+    fake = ctypes.c_void_p(0x10000)   # never dereferenced: validation fails first
+    odd = ctypes.c_void_p(0x10008)    # not 16-byte aligned
+    null = ctypes.c_void_p(0)
+    big = info.workspace_bytes
+    # null pointers
+    assert L.rola_forward(P(prob), P(cfg), null, fake, fake, fake, fake, null, fake, fake, big, null) == 1
+    assert L.rola_select_blocks(P(prob), P(cfg), fake, fake, null, null, fake, big, null) == 1
+    # misaligned tensors
+    assert L.rola_sparse_attn(P(prob), P(cfg), odd, fake, fake, fake, fake, 0, fake, big, null) == 3
+    # workspace too small or missing
+    assert L.rola_forward(P(prob), P(cfg), fake, fake, fake, fake, fake, null, fake, fake, big - 1, null) == 4
+    assert L.rola_lowrank_attn(P(prob), P(cfg), fake, fake, fake, fake, fake, fake, 0, null, big, null) == 4
+    # bad accumulate flag
+    assert L.rola_sparse_attn(P(prob), P(cfg), fake, fake, fake, fake, fake, 2, fake, big, null) == 1
+    # status strings
+    assert L.rola_status_str(4) == b"workspace missing or too small"
+
+
+def test_timing_read_without_launches_is_empty():
+    assert rola.lib().rola_timing_read(None, 4) == -1
+    assert rola.timing_read() == {}
