@@ -33,8 +33,10 @@ struct Plan {
   int tab_total, tab1, tab2;
   int nchunks, cpc;
   // workspace offsets (bytes)
-  int64_t off_tab, off_wqT, off_wkT, off_qp, off_kp, off_scores, off_map, off_vt, off_part, off_st,
-      off_z, total;
+  int G;
+  int64_t ngroups, list_stride;
+  int64_t off_tab, off_wqT, off_wkT, off_qp, off_kp, off_scores, off_map, off_part, off_st,
+      off_z, off_ugroup, off_ucount, off_ulist, total;
 };
 
 int32_t make_plan(const rola_problem *p, const rola_config *c, Plan *pl) {
@@ -101,10 +103,15 @@ int32_t make_plan(const rola_problem *p, const rola_config *c, Plan *pl) {
   P.off_kp = o; o = align_up(o + P.BH * nb * D * 4);
   P.off_scores = o; o = align_up(o + P.BH * nb * (int64_t)nb * 4);
   P.off_map = o; o = align_up(o + P.BH * nb * (int64_t)kb * 4);
-  P.off_vt = o; o = align_up(o + P.BH * nb * 64LL * D * 2);
-  P.off_part = o; o = align_up(o + P.BH * P.nchunks * (int64_t)(D * 32 + 32) * 4);
+  P.off_part = o; o = align_up(o + P.BH * P.nchunks * 2 * (int64_t)(D * 32 + 32) * 4);
   P.off_st = o; o = align_up(o + P.BH * D * 32LL * 2);
   P.off_z = o; o = align_up(o + P.BH * 32LL * 4);
+  P.G = rola::attn_group_size();
+  P.ngroups = (nb + P.G - 1) / P.G;
+  P.list_stride = (int64_t)P.G * kb;
+  P.off_ugroup = o; o = align_up(o + P.BH * P.ngroups * P.G * 4);
+  P.off_ucount = o; o = align_up(o + P.BH * P.ngroups * 4);
+  P.off_ulist = o; o = align_up(o + P.BH * P.ngroups * P.list_stride * 4);
   P.total = o;
   return ROLA_OK;
 }
@@ -140,12 +147,12 @@ int32_t timed(const char *name, hipStream_t st, F &&launch) {
     std::lock_guard<std::mutex> lk(g_mu);
     a = take_event();
     b = take_event();
-    if (a) hipEventRecord(a, st);
+    if (a) (void)hipEventRecord(a, st);
   }
   launch();
   hipError_t err = hipGetLastError();
   if (g_timing && a && b) {
-    hipEventRecord(b, st);
+    (void)hipEventRecord(b, st);
     std::lock_guard<std::mutex> lk(g_mu);
     g_launches.push_back({name, a, b});
   }
@@ -181,7 +188,7 @@ int32_t run_setup(const Plan &P, const float *wq, const float *wk, uint8_t *ws, 
 }
 
 int32_t run_pass1(const Plan &P, const rola_problem *p, const void *q, const void *k, const void *v,
-                  uint8_t *ws, bool pool, bool state, bool vt, hipStream_t st) {
+                  uint8_t *ws, bool pool, bool state, hipStream_t st) {
   rola::Pass1Args a;
   a.q = (const uint16_t *)q; a.k = (const uint16_t *)k; a.v = (const uint16_t *)v;
   a.stride_b = p->stride_b; a.stride_h = p->stride_h; a.stride_n = p->stride_n;
@@ -190,15 +197,11 @@ int32_t run_pass1(const Plan &P, const rola_problem *p, const void *q, const voi
   a.inv_tail = 1.0f / (float)tail;
   a.qp = (float *)(ws + P.off_qp);
   a.kp = (float *)(ws + P.off_kp);
-  a.vt = (uint16_t *)(ws + P.off_vt);
   a.wkT = (const uint16_t *)(ws + P.off_wkT);
   a.state_part = (float *)(ws + P.off_part);
   a.rope = rope_args(P, ws);
-  const char *name = (pool && state && vt) ? "pass1_pool_state_vt"
-                     : pool                 ? "pass1_pool"
-                     : state                ? "pass1_state"
-                                            : "pass1_vt";
-  return timed(name, st, [&] { rola::launch_pass1(a, P.D, P.nchunks, (int)P.BH, pool, state, vt, st); });
+  const char *name = (pool && state) ? "pass1_pool_state" : pool ? "pass1_pool" : "pass1_state";
+  return timed(name, st, [&] { rola::launch_pass1(a, P.D, P.nchunks, (int)P.BH, pool, state, st); });
 }
 
 int32_t run_reduce(const Plan &P, uint8_t *ws, hipStream_t st) {
@@ -218,21 +221,41 @@ int32_t run_select(const Plan &P, uint8_t *ws, float *scores, int32_t *map, hipS
 }
 
 int32_t run_attn(const Plan &P, const rola_problem *p, const rola_config *c, const void *q,
-                 const void *k, const int32_t *map, void *out, uint8_t *ws, bool sparse,
+                 const void *k, const void *v, const int32_t *map, void *out, uint8_t *ws, bool sparse,
                  bool lowrank, bool accum, hipStream_t st) {
   rola::AttnArgs a;
-  a.q = (const uint16_t *)q; a.k = (const uint16_t *)k;
-  a.vt = (const uint16_t *)(ws + P.off_vt);
-  a.map = map; a.out = out;
+  a.q = (const uint16_t *)q; a.k = (const uint16_t *)k; a.v = (const uint16_t *)v;
+  a.out = out;
   a.stride_b = p->stride_b; a.stride_h = p->stride_h; a.stride_n = p->stride_n;
   a.heads = P.H; a.nb = P.nb; a.kb = P.kb; a.rank = P.r; a.n_tokens = P.N;
-  a.tiles = P.BH * P.nb;
-  a.tiles_per_xcd = (a.tiles + 7) / 8;
+  a.bh_count = P.BH;
+  a.ngroups = P.ngroups;
+  a.groups_per_xcd = (P.ngroups + 7) / 8;
+  a.list_stride = P.list_stride;
+  a.ugroup = (const int32_t *)(ws + P.off_ugroup);
+  a.ucount = (const int32_t *)(ws + P.off_ucount);
+  a.ulist = (const int32_t *)(ws + P.off_ulist);
   a.scale_log2e = (float)((double)P.scale * 1.4426950408889634);
   a.wqT = (const uint16_t *)(ws + P.off_wqT);
   a.st = (const uint16_t *)(ws + P.off_st);
   a.z = (const float *)(ws + P.off_z);
   a.rope = rope_args(P, ws);
+  if (sparse) {
+    int32_t s = timed("schedule", st, [&] {
+      rola::launch_schedule(map, P.nb, P.kb, P.G, (int)P.ngroups, (int)P.list_stride, (int)P.BH,
+                            (int32_t *)(ws + P.off_ugroup), (int32_t *)(ws + P.off_ucount),
+                            (int32_t *)(ws + P.off_ulist), st);
+    });
+    if (s != ROLA_OK) return s;
+  } else {
+    // low-rank only: each "group" is one query block per member slot, in order
+    int32_t s = timed("schedule", st, [&] {
+      rola::launch_schedule(nullptr, P.nb, 0, P.G, (int)P.ngroups, 0, (int)P.BH,
+                            (int32_t *)(ws + P.off_ugroup), (int32_t *)(ws + P.off_ucount),
+                            (int32_t *)(ws + P.off_ulist), st);
+    });
+    if (s != ROLA_OK) return s;
+  }
   const char *name = sparse && lowrank ? "attn_sparse_lowrank" : sparse ? "attn_sparse" : "attn_lowrank";
   return timed(name, st, [&] {
     rola::launch_attn(a, P.D, sparse, lowrank, accum != 0, c->out_dtype == ROLA_OUT_F32, st);
@@ -289,7 +312,7 @@ int32_t rola_select_blocks(const rola_problem *prob, const rola_config *cfg, con
   if (!aligned16(workspace)) return ROLA_ERR_ALIGNMENT;
   hipStream_t st = (hipStream_t)stream;
   uint8_t *ws = (uint8_t *)workspace;
-  ROLA_TRY(run_pass1(P, prob, q, k, nullptr, ws, true, false, false, st));
+  ROLA_TRY(run_pass1(P, prob, q, k, nullptr, ws, true, false, st));
   float *scores = pooled_scores ? pooled_scores : (float *)(ws + P.off_scores);
   return run_select(P, ws, scores, block_idx, st);
 }
@@ -308,8 +331,7 @@ int32_t rola_sparse_attn(const rola_problem *prob, const rola_config *cfg, const
   if (!aligned16(workspace)) return ROLA_ERR_ALIGNMENT;
   hipStream_t st = (hipStream_t)stream;
   uint8_t *ws = (uint8_t *)workspace;
-  ROLA_TRY(run_pass1(P, prob, nullptr, nullptr, v, ws, false, false, true, st));
-  return run_attn(P, prob, cfg, q, k, block_idx, out, ws, true, false, accumulate != 0, st);
+  return run_attn(P, prob, cfg, q, k, v, block_idx, out, ws, true, false, accumulate != 0, st);
 }
 
 int32_t rola_lowrank_attn(const rola_problem *prob, const rola_config *cfg, const void *q,
@@ -327,9 +349,9 @@ int32_t rola_lowrank_attn(const rola_problem *prob, const rola_config *cfg, cons
   hipStream_t st = (hipStream_t)stream;
   uint8_t *ws = (uint8_t *)workspace;
   ROLA_TRY(run_setup(P, wq, wk, ws, st));
-  ROLA_TRY(run_pass1(P, prob, nullptr, k, v, ws, false, true, false, st));
+  ROLA_TRY(run_pass1(P, prob, nullptr, k, v, ws, false, true, st));
   ROLA_TRY(run_reduce(P, ws, st));
-  return run_attn(P, prob, cfg, q, nullptr, nullptr, out, ws, false, true, accumulate != 0, st);
+  return run_attn(P, prob, cfg, q, nullptr, nullptr, nullptr, out, ws, false, true, accumulate != 0, st);
 }
 
 int32_t rola_forward(const rola_problem *prob, const rola_config *cfg, const void *q,
@@ -349,10 +371,10 @@ int32_t rola_forward(const rola_problem *prob, const rola_config *cfg, const voi
   uint8_t *ws = (uint8_t *)workspace;
   int32_t *map = block_idx_out ? block_idx_out : (int32_t *)(ws + P.off_map);
   ROLA_TRY(run_setup(P, wq, wk, ws, st));
-  ROLA_TRY(run_pass1(P, prob, q, k, v, ws, true, true, true, st));
+  ROLA_TRY(run_pass1(P, prob, q, k, v, ws, true, true, st));
   ROLA_TRY(run_reduce(P, ws, st));
   ROLA_TRY(run_select(P, ws, (float *)(ws + P.off_scores), map, st));
-  return run_attn(P, prob, cfg, q, k, map, out, ws, true, true, false, st);
+  return run_attn(P, prob, cfg, q, k, v, map, out, ws, true, true, false, st);
 }
 
 int32_t rola_timing_enable(int32_t on) {

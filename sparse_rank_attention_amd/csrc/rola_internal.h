@@ -34,21 +34,33 @@ struct Pass1Args {
   int rank;
   float inv_tail;       // fl32(1/valid) of the tail block
   float *qp, *kp;       // pooled [BH][nb][D]
-  uint16_t *vt;         // [BH][nb][64*D] transposed V tiles
   const uint16_t *wkT;  // bf16 [32][D]
-  float *state_part;    // [BH][nchunks][D*32 + 32]
+  float *state_part;    // [BH][nchunks][2][D*32 + 32]
   RopeArgsHost rope;
 };
 
+// Attention workgroup shape: G query blocks per workgroup (2 waves each),
+// S-slot LDS ring of K/V^T tiles.
+#ifndef ROLA_ATTN_G
+#define ROLA_ATTN_G 4
+#endif
+#ifndef ROLA_ATTN_S
+#define ROLA_ATTN_S 4
+#endif
+
 struct AttnArgs {
-  const uint16_t *q, *k, *vt;
-  const int32_t *map;
+  const uint16_t *q, *k, *v;
   void *out;
   int64_t stride_b, stride_h, stride_n;
   int heads, nb, kb, rank;
   int64_t n_tokens;
-  int64_t tiles;        // BH * nb
-  int64_t tiles_per_xcd;
+  int64_t bh_count;
+  int64_t ngroups;         // groups of G query blocks per (batch, head)
+  int64_t groups_per_xcd;  // ceil(ngroups / 8)
+  int64_t list_stride;     // G * kb
+  const int32_t *ugroup;   // [BH][ngroups][G] member query blocks (-1: none)
+  const int32_t *ucount;   // [BH][ngroups] union length
+  const int32_t *ulist;    // [BH][ngroups][list_stride] key block | member mask << 16
   float scale_log2e;
   const uint16_t *wqT;  // bf16 [32][D]
   const uint16_t *st;   // bf16 [BH][D][32] (rank permuted)
@@ -57,13 +69,15 @@ struct AttnArgs {
 };
 
 void launch_setup(const SetupArgs &a, hipStream_t st);
-void launch_pass1(const Pass1Args &a, int D, int nchunks, int bh, bool pool, bool state, bool vt,
-                  hipStream_t st);
+void launch_pass1(const Pass1Args &a, int D, int nchunks, int bh, bool pool, bool state, hipStream_t st);
 void launch_state_reduce(const float *part, int nchunks, int D, int rank, int bh, uint16_t *st_out,
                          float *z, hipStream_t st);
 void launch_scores(const float *qp, const float *kp, float *s, int nb, int D, int bh,
                    hipStream_t st);
 void launch_topk(const float *s, int32_t *map, int nb, int kb, int64_t rows, hipStream_t st);
+void launch_schedule(const int32_t *map, int nb, int kb, int G, int ngroups, int list_stride,
+                     int bh, int32_t *ugroup, int32_t *ucount, int32_t *ulist, hipStream_t st);
+int attn_group_size();
 void launch_attn(const AttnArgs &a, int D, bool sparse, bool lowrank, bool accum, bool outf32,
                  hipStream_t st);
 

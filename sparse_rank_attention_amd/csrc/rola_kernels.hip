@@ -9,12 +9,13 @@
 // Kernels, in launch order:
 //   k_setup        rotary cos/sin table, bf16 transposed projections
 //   k_pass1        one streaming pass over the token tensors: block pooling
-//                  of Q and K (fixed fp32 tree order), low-rank state partials
-//                  from K and V (MFMA), and the transposed V tiles the sparse
-//                  kernel reads
+//                  of Q and K (fixed fp32 tree order) and low-rank state
+//                  partials from K and V (MFMA)
 //   k_state_reduce fixed-order sum of the state partials
 //   k_scores       pooled block scores, sequential fp32 fma chain (VALU)
 //   k_topk         per-row radix select of the kept key blocks (one wave/row)
+//   k_order        per head: query blocks ordered by similarity of their maps
+//   k_union        per group of query blocks: merged list of kept key blocks
 //   k_attn         block-sparse flash attention on bf16 MFMA with online
 //                  softmax in fp32, fused low-rank apply and merge
 //
@@ -25,12 +26,15 @@
 // Attention is computed transposed (S^T = K Q^T, O^T = V^T P^T) so that one
 // lane owns one query column throughout: its softmax statistics are lane
 // scalars, and the S^T accumulator is directly the B operand of the PV step
-// provided the key order inside every 16-key group is permuted as
-// [0-3, 8-11, 4-7, 12-15] in the transposed V tile.  The same permutation is
-// used for the rank index of the low-rank state and for tokens in the state
-// contraction.
+// provided the V^T operand lists the keys of every 16-key step in the order
+// [0-3, 8-11] (lanes 0-31) and [4-7, 12-15] (lanes 32-63); the transposing
+// LDS read (ds_read_b64_tr_b16) produces exactly that from a row-major V tile.
+// The same order is used for the rank index of the low-rank state and for
+// tokens in the state contraction.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "rola_internal.h"
 
@@ -64,6 +68,10 @@ static __device__ __forceinline__ int perm16_key_of_pos(int p) {
 
 static __device__ __forceinline__ float phi(float u) { return u > 0.0f ? u + 1.0f : __expf(u); }
 
+// 2^x on the transcendental unit (v_exp_f32); results below the normal range
+// flush to zero, which is harmless for softmax weights.
+static __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 static __device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -72,6 +80,55 @@ static __device__ __forceinline__ float shfl_xor32(float v) { return __shfl_xor(
 
 static __device__ __forceinline__ void lds_dma16(const void *gsrc, void *lds_dst) {
   __builtin_amdgcn_global_load_lds((const GLOBAL_AS void *)gsrc, (LDS_AS void *)lds_dst, 16, 0, 0);
+}
+
+// LDS tile layouts: row-major [64 rows][D] bf16 in 16-byte chunks, chunk c
+// of row r stored at c ^ swizzle(r).  K tiles (read as 16-byte MFMA rows)
+// use r & 7; V tiles (read transposed, 8 bytes per lane) use 2*(r & 3).
+static __device__ __forceinline__ int swz_k(int r) { return r & 7; }
+static __device__ __forceinline__ int swz_v(int r) { return 2 * (r & 3); }
+
+static __device__ __forceinline__ void barrier_lds() {
+  // all LDS reads of this wave retired, then a plain workgroup barrier (no
+  // vmcnt wait: prefetches stay in flight across it)
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int N>
+static __device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | (((N >> 4) & 3) << 14));
+}
+
+template <int OPS, int S>
+static __device__ __forceinline__ void wait_tiles_in_flight(int tiles) {
+  // wait until at most `tiles` later tiles (2*OPS DMA ops each) are outstanding
+  if (S >= 4 && tiles >= 2) wait_vmcnt<(S >= 4 ? 4 * OPS : 0)>();
+  else if (S >= 3 && tiles >= 1) wait_vmcnt<(S >= 3 ? 2 * OPS : 0)>();
+  else wait_vmcnt<0>();
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// A operand V^T[d][keys] of a 32x32x16 MFMA step s (keys 16s..16s+15) and
+// d-tile dt, read from a row-major V tile with the transposing LDS load: in
+// each 16-lane group, lane i points at row kbase + i/4, dims dbase + 4*(i%4),
+// and lane l receives rows kbase..kbase+3 of dim dbase + l%16.  Key order per
+// lane group g: 16s + 4g + {0..3}, then 16s + 8 + 4g + {0..3} -- the order of
+// the S^T accumulator rows that form the matching B operand.
+template <int D>
+static __device__ __forceinline__ bf16x8 vt_operand(const uint16_t *sV, int s, int dt, int lane) {
+  const int g = lane >> 5, dhalf = (lane >> 4) & 1, i = lane & 15;
+  const int dstart = 32 * dt + 16 * dhalf + 4 * (i & 3);
+  const int c = dstart >> 3, sub = dstart & 7;
+  const int r0 = 16 * s + 4 * g + (i >> 2), r1 = r0 + 8;
+  const LDS_AS i16x4 *p0 = (const LDS_AS i16x4 *)(const LDS_AS uint16_t *)(sV + r0 * D + ((c ^ swz_v(r0)) << 3) + sub);
+  const LDS_AS i16x4 *p1 = (const LDS_AS i16x4 *)(const LDS_AS uint16_t *)(sV + r1 * D + ((c ^ swz_v(r1)) << 3) + sub);
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)p0);
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)p1);
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 ab = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, ab);
 }
 
 // Rotary tables: tab holds (cos, sin) per axis, position and pair; the t,
@@ -148,20 +205,26 @@ __global__ void k_setup(const float *__restrict__ wq, const float *__restrict__ 
 }
 
 // ---------------------------------------------------------------- k_pass1
-// Grid (nchunks, B*H), 256 threads.  Each workgroup walks `cpc` consecutive
-// 64-token blocks of one (batch, head).
-//   POOL : waves 0 and 1 pool Q and K (fixed tree order) into Qp, Kp.
-//   STATE: waves 2 and 3 form b = phi(Wk^T R(k)) for the block (MFMA) and
-//          accumulate S^T += V^T b (MFMA) and z += b; partials per workgroup.
-//   VT   : the transposed, key-permuted, chunk-swizzled V tile is written to
-//          the workspace in the exact LDS image the attention kernel loads.
-template <int D, bool POOL, bool STATE, bool VT>
+// Grid (nchunks, B*H), 256 threads: each workgroup streams `cpc` consecutive
+// 64-token blocks of one (batch, head) through a 3-slot LDS ring filled by
+// direct global->LDS copies two blocks ahead of the one being consumed.
+//   POOL : wave 0 pools Q, wave 1 pools K (fixed fp32 tree order).
+//   STATE: waves 2 and 3 take tokens 0-31 and 32-63 of the block: b =
+//          phi(Wk^T R(k)) on MFMA, then S^T += V^T b (V^T read transposed
+//          from the row-major V tile) and z += b.  Per-wave partial sums go
+//          to the workspace for a fixed-order reduction.
+// Rows past N are copied from row N-1 (finite values); they are excluded
+// from the pooled means and get b = 0.
+template <int D, bool POOL, bool STATE>
 __global__ __launch_bounds__(256) void k_pass1(Pass1Args args) {
-  constexpr int CH = D / 8;  // 16-byte chunks per token row
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[POOL ? 64 * D : 1];
-  __shared__ __attribute__((aligned(16))) uint16_t sK[(POOL || STATE) ? 64 * D : 1];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[(STATE || VT) ? 64 * D : 1];
-  __shared__ __attribute__((aligned(16))) uint16_t sVt[(STATE || VT) ? 64 * D : 1];
+  constexpr int CH = D / 8;       // 16-byte chunks per token row
+  constexpr int TILE = 64 * D;    // elements per tensor tile
+  constexpr int NTEN = (POOL ? 1 : 0) + 1 + (STATE ? 1 : 0);  // Q?, K, V?
+  constexpr int STAGE = NTEN * TILE;
+  constexpr int NSTAGE = 3;
+  constexpr int OPS = (64 * CH) / 256;  // DMA ops per thread per tensor
+  constexpr int QOFF = 0, KOFF = POOL ? TILE : 0, VOFF = KOFF + TILE;
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[NSTAGE * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
   const int bh = blockIdx.y;
@@ -170,99 +233,74 @@ __global__ __launch_bounds__(256) void k_pass1(Pass1Args args) {
   const uint16_t *Q = args.q + base, *K = args.k + base, *V = args.v + base;
   const int c0 = blockIdx.x * args.cpc;
   const int c1 = min(args.nb, c0 + args.cpc);
-
+  const int nblk = c1 - c0;
   const RopeArgsDev ra = args.rope;
-  // state accumulators: wave 2 owns d-tiles [0, D/64), wave 3 [D/64, D/32)
-  constexpr int DT = D / 64;
+
+  auto issue = [&](int i) {  // copy block c0+i into slot i % NSTAGE
+    uint16_t *slot = ring + (i % NSTAGE) * STAGE;
+    const int64_t c = c0 + i;
+#pragma unroll
+    for (int o = 0; o < OPS; ++o) {
+      const int cidx = o * 256 + tid;
+      const int row = cidx / CH, pc = cidx % CH;
+      const int64_t src = min(c * 64 + row, args.n_tokens - 1) * args.stride_n;
+      uint16_t *dst = slot + (o * 256 + wave * 64) * 8;
+      if (POOL) lds_dma16(Q + src + pc * 8, dst + QOFF);
+      lds_dma16(K + src + ((pc ^ swz_k(row)) * 8), dst + KOFF);
+      if (STATE) lds_dma16(V + src + ((pc ^ swz_v(row)) * 8), dst + VOFF);
+    }
+  };
+
+  // state accumulators of this wave's token half, all d-tiles
+  constexpr int DT = D / 32;
   f32x16 sacc[DT];
 #pragma unroll
   for (int i = 0; i < DT; ++i) sacc[i] = f32x16{};
   float zacc = 0.0f;
   bf16x8 wkreg[D / 16];
+  const int tt = wave - 2;  // token tile of the state waves
   if (STATE && wave >= 2) {
 #pragma unroll
     for (int s = 0; s < D / 16; ++s)
       wkreg[s] = *(const bf16x8 *)(args.wkT + (lane & 31) * D + 16 * s + 8 * g);
   }
 
-  for (int c = c0; c < c1; ++c) {
+  for (int i = 0; i < NSTAGE - 1; ++i)
+    if (i < nblk) issue(i);
+  for (int i = 0; i < nblk; ++i) {
+    // wait for block i; blocks i+1 (3*OPS*NTEN ops) may stay in flight
+    if (i + 1 < nblk) wait_vmcnt<NTEN * OPS>();
+    else wait_vmcnt<0>();
+    barrier_lds();  // block i visible; every wave is done with block i-1
+    if (i + NSTAGE - 1 < nblk) issue(i + NSTAGE - 1);
+    const int c = c0 + i;
     const int valid = min(64, (int)(args.n_tokens - (int64_t)c * 64));
-    // ---- stage tiles in LDS (plain 16-byte loads; rows >= valid are zeroed)
-    for (int cidx = tid; cidx < 64 * CH; cidx += 256) {
-      const int row = cidx / CH, col = cidx % CH;
-      const int64_t goff = ((int64_t)c * 64 + row) * args.stride_n + col * 8;
-      const bool ok = row < valid;
-      if (POOL) {
-        u32x4 x = ok ? *(const u32x4 *)(Q + goff) : u32x4{0, 0, 0, 0};
-        *(u32x4 *)(sQ + row * D + col * 8) = x;
-      }
-      if (POOL || STATE) {
-        u32x4 x = ok ? *(const u32x4 *)(K + goff) : u32x4{0, 0, 0, 0};
-        *(u32x4 *)(sK + row * D + ((col ^ (row & 7)) * 8)) = x;
-      }
-      if (STATE || VT) {
-        u32x4 x = ok ? *(const u32x4 *)(V + goff) : u32x4{0, 0, 0, 0};
-        *(u32x4 *)(sV + row * D + col * 8) = x;
-      }
-    }
-    __syncthreads();
-
-    // ---- transposed V tile: row d, 64 keys permuted per 16-group, chunks swizzled by d&7
-    if (STATE || VT) {
-      // task = (d pair, logical chunk): 8 keys of two dims
-      for (int task = tid; task < (D / 2) * 8; task += 256) {
-        const int dp = task % (D / 2), lc = task / (D / 2);
-        const int d = 2 * dp;
-        uint32_t w[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int key = perm16_key_of_pos(lc * 8 + e);
-          w[e] = *(const uint32_t *)(sV + key * D + d);
-        }
-        u32x4 lo, hi;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          lo[e] = (w[2 * e] & 0xffffu) | (w[2 * e + 1] << 16);
-          hi[e] = (w[2 * e] >> 16) | (w[2 * e + 1] & 0xffff0000u);
-        }
-        *(u32x4 *)(sVt + d * 64 + ((lc ^ (d & 7)) * 8)) = lo;
-        *(u32x4 *)(sVt + (d + 1) * 64 + ((lc ^ ((d + 1) & 7)) * 8)) = hi;
-      }
-      __syncthreads();
-      if (VT) {
-        uint16_t *dst = args.vt + ((int64_t)bh * args.nb + c) * (64 * D);
-        for (int cidx = tid; cidx < 64 * CH; cidx += 256)
-          *(u32x4 *)(dst + cidx * 8) = *(const u32x4 *)(sVt + cidx * 8);
-      }
-    }
+    const uint16_t *slot = ring + (i % NSTAGE) * STAGE;
 
     // ---- pooling: wave 0 -> Q, wave 1 -> K; lane owns dims 2*lane, 2*lane+1
     if (POOL && wave < 2 && lane < D / 2) {
-      const uint16_t *tile = wave == 0 ? sQ : sK;
+      const uint16_t *tile = slot + (wave == 0 ? QOFF : KOFF);
       const int word = lane;
       float lo[32], hi[32];
 #pragma unroll
-      for (int s = 0; s < 32; ++s) {
+      for (int s = 0; s < 64; ++s) {
         const int off = wave == 0 ? s * D + 2 * word
-                                  : s * D + ((((word >> 2) ^ (s & 7)) << 3) | ((word & 3) << 1));
-        const uint32_t x = *(const uint32_t *)(tile + off);
-        lo[s] = bflo(x);
-        hi[s] = bfhi(x);
-      }
-#pragma unroll
-      for (int s = 32; s < 64; ++s) {
-        const int off = wave == 0 ? s * D + 2 * word
-                                  : s * D + ((((word >> 2) ^ (s & 7)) << 3) | ((word & 3) << 1));
-        const uint32_t x = *(const uint32_t *)(tile + off);
-        lo[s - 32] = lo[s - 32] + bflo(x);
-        hi[s - 32] = hi[s - 32] + bfhi(x);
+                                  : s * D + ((((word >> 2) ^ swz_k(s)) << 3) | ((word & 3) << 1));
+        const uint32_t x = s < valid ? *(const uint32_t *)(tile + off) : 0u;
+        if (s < 32) {
+          lo[s] = bflo(x);
+          hi[s] = bfhi(x);
+        } else {
+          lo[s - 32] = lo[s - 32] + bflo(x);
+          hi[s - 32] = hi[s - 32] + bfhi(x);
+        }
       }
 #pragma unroll
       for (int stride = 16; stride >= 1; stride >>= 1) {
 #pragma unroll
-        for (int i = 0; i < stride; ++i) {
-          lo[i] = lo[i] + lo[i + stride];
-          hi[i] = hi[i] + hi[i + stride];
+        for (int k2 = 0; k2 < stride; ++k2) {
+          lo[k2] = lo[k2] + lo[k2 + stride];
+          hi[k2] = hi[k2] + hi[k2 + stride];
         }
       }
       const float inv = valid == 64 ? 0.015625f : args.inv_tail;
@@ -270,98 +308,82 @@ __global__ __launch_bounds__(256) void k_pass1(Pass1Args args) {
       *(float2 *)dst = make_float2(lo[0] * inv, hi[0] * inv);
     }
 
-    // ---- low-rank state: waves 2 and 3
+    // ---- low-rank state: wave 2 tokens 0-31, wave 3 tokens 32-63
     if (STATE && wave >= 2) {
-      // b tile [64 tokens x 32 r]: A = R(K) (rows tokens), B = Wk^T (cols r)
-      f32x16 bacc[2];
+      const uint16_t *sK = slot + KOFF, *sV = slot + VOFF;
+      f32x16 bacc = f32x16{};
+      const int row = 32 * tt + (lane & 31);
+      int pt, ph, pw;  // padded rows take the last valid position (their b is masked)
+      token_pos(min((int64_t)c * 64 + row, args.n_tokens - 1), ra, pt, ph, pw);
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        bacc[tt] = f32x16{};
-        const int row = 32 * tt + (lane & 31);
-        int pt, ph, pw;  // padded rows take the last valid position (their b is masked)
-        token_pos(min((int64_t)c * 64 + row, args.n_tokens - 1), ra, pt, ph, pw);
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-          const int lc = 2 * s + g;
-          bf16x8 kx = *(const bf16x8 *)(sK + row * D + ((lc ^ (row & 7)) * 8));
-          kx = rope8(kx, 16 * s + 8 * g, pt, ph, pw, ra);
-          bacc[tt] = mfma_bf16(kx, wkreg[s], bacc[tt]);
-        }
+      for (int s = 0; s < D / 16; ++s) {
+        const int lc = 2 * s + g;
+        bf16x8 kx = *(const bf16x8 *)(sK + row * D + ((lc ^ swz_k(row)) * 8));
+        kx = rope8(kx, 16 * s + 8 * g, pt, ph, pw, ra);
+        bacc = mfma_bf16(kx, wkreg[s], bacc);
       }
-      // phi, mask invalid tokens and rank padding, accumulate z, pack as B operand
+      // phi, mask invalid tokens and rank padding, z, pack as B operand
       const bool rok = (lane & 31) < args.rank;
-      bf16x8 bop[4];
+      bf16x8 bop[2];
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int tok = 32 * tt + 8 * (i >> 2) + 4 * g + (i & 3);
-          float f = phi(bacc[tt][i]);
-          f = (rok && tok < valid) ? f : 0.0f;
-          zacc += f;
-          bop[2 * tt + (i >> 3)][i & 7] = (__bf16)f;
-        }
+      for (int e = 0; e < 16; ++e) {
+        const int tok = 32 * tt + 8 * (e >> 2) + 4 * g + (e & 3);
+        float f = phi(bacc[e]);
+        f = (rok && tok < valid) ? f : 0.0f;
+        zacc += f;
+        bop[e >> 3][e & 7] = (__bf16)f;
       }
-      // S^T[d][r] += sum_tok Vt[d][tok] * b[tok][r]
+      // S^T[d][r] += sum_tok V^T[d][tok] * b[tok][r] over this wave's 32 tokens
 #pragma unroll
-      for (int t = 0; t < DT; ++t) {
-        const int dt = (wave - 2) * DT + t;
-        const int d = 32 * dt + (lane & 31);
+      for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int lc = 2 * s + g;
-          const bf16x8 va = *(const bf16x8 *)(sVt + d * 64 + ((lc ^ (d & 7)) * 8));
-          sacc[t] = mfma_bf16(va, bop[s], sacc[t]);
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const bf16x8 va = vt_operand<D>(sV, 2 * tt + s2, dt, lane);
+          sacc[dt] = mfma_bf16(va, bop[s2], sacc[dt]);
         }
       }
     }
-    __syncthreads();
   }
 
   if (STATE && wave >= 2) {
-    float *part = args.state_part + ((int64_t)bh * gridDim.x + blockIdx.x) * (D * 32 + 32);
+    float *part = args.state_part + (((int64_t)bh * gridDim.x + blockIdx.x) * 2 + tt) * (D * 32 + 32);
 #pragma unroll
-    for (int t = 0; t < DT; ++t) {
-      const int dt = (wave - 2) * DT + t;
+    for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int d = 32 * dt + 8 * (i >> 2) + 4 * g + (i & 3);
-        part[d * 32 + (lane & 31)] = sacc[t][i];
+      for (int e = 0; e < 16; ++e) {
+        const int d = 32 * dt + 8 * (e >> 2) + 4 * g + (e & 3);
+        part[d * 32 + (lane & 31)] = sacc[dt][e];
       }
     }
     const float zt = zacc + shfl_xor32(zacc);
-    if (wave == 2 && lane < 32) part[D * 32 + lane] = zt;
+    if (lane < 32) part[D * 32 + lane] = zt;
   }
 }
 
 // ------------------------------------------------------------ k_state_reduce
-// One workgroup per (batch, head): fixed-order sum over the chunk partials.
+// Fixed-order sum over the partials (chunk-major, then token half), one thread
+// per state element.
 // Writes St (bf16 [D][32], rank index permuted per 16-group, the A operand
 // layout of the apply step) and z (fp32 [32]).  Rank columns >= rank are 0.
 __global__ __launch_bounds__(256) void k_state_reduce(const float *__restrict__ part, int nchunks,
                                                       int D, int rank, uint16_t *__restrict__ st,
                                                       float *__restrict__ z) {
-  const int bh = blockIdx.x;
+  const int bh = blockIdx.y;
   const int stride = D * 32 + 32;
-  const float *p = part + (int64_t)bh * nchunks * stride;
-  for (int idx = threadIdx.x; idx < stride; idx += blockDim.x) {
-    float acc = 0.0f;
-    for (int c = 0; c < nchunks; ++c) acc += p[(int64_t)c * stride + idx];
-    if (idx < D * 32) {
-      const int d = idx / 32, r = idx % 32;
-      // position of rank r in the permuted row
-      int pos = 0;
-      {
-        const int w = r & 15;
-        const int pw = (w < 4) ? w : (w < 8) ? w + 4 : (w < 12) ? w - 4 : w;
-        pos = (r & ~15) | pw;
-      }
-      const __bf16 v = (__bf16)(r < rank ? acc : 0.0f);
-      st[(int64_t)bh * D * 32 + d * 32 + pos] = __builtin_bit_cast(uint16_t, v);
-    } else {
-      const int r = idx - D * 32;
-      z[(int64_t)bh * 32 + r] = r < rank ? acc : 0.0f;
-    }
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= stride) return;
+  const float *p = part + (int64_t)bh * nchunks * 2 * stride + idx;
+  float acc = 0.0f;
+  for (int c = 0; c < 2 * nchunks; ++c) acc += p[(int64_t)c * stride];
+  if (idx < D * 32) {
+    const int d = idx / 32, r = idx % 32;
+    const int w = r & 15;
+    const int pos = (r & ~15) | ((w < 4) ? w : (w < 8) ? w + 4 : (w < 12) ? w - 4 : w);
+    const __bf16 v = (__bf16)(r < rank ? acc : 0.0f);
+    st[(int64_t)bh * D * 32 + d * 32 + pos] = __builtin_bit_cast(uint16_t, v);
+  } else {
+    const int r = idx - D * 32;
+    z[(int64_t)bh * 32 + r] = r < rank ? acc : 0.0f;
   }
 }
 
@@ -447,29 +469,133 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ s, int32
   }
 }
 
+// ---------------------------------------------------------------- k_order
+// One workgroup per (batch, head): orders the query blocks by the first two
+// entries of their (ascending) block maps, so that query blocks keeping
+// similar key blocks become neighbours, and writes the groups of G members.
+// Without a map (kb == 0, low-rank only) the order is the identity.
+__global__ __launch_bounds__(1024) void k_order(const int32_t *__restrict__ map, int nb, int kb, int G,
+                                                int ngroups, int32_t *__restrict__ ugroup) {
+  extern __shared__ uint32_t key[];  // [nb]
+  const int bh = blockIdx.x;
+  const int32_t *mb = kb > 0 ? map + (int64_t)bh * nb * kb : nullptr;
+  for (int i = threadIdx.x; i < nb; i += blockDim.x) {
+    uint32_t key_i = (uint32_t)i;
+    if (kb > 0) {
+      const uint32_t a = (uint32_t)min(max(mb[(int64_t)i * kb], 0), nb - 1);
+      const uint32_t b = kb > 1 ? (uint32_t)min(max(mb[(int64_t)i * kb + 1], 0), nb - 1) : 0u;
+      key_i = (a << 12) | b;
+    }
+    key[i] = key_i;
+  }
+  __syncthreads();
+  // rank sort: position of i = #{j : (key_j, j) < (key_i, i)}
+  int32_t *ug = ugroup + (int64_t)bh * ngroups * G;
+  for (int i = threadIdx.x; i < nb; i += blockDim.x) {
+    const uint32_t ki = key[i];
+    int rank = 0;
+    for (int j = 0; j < nb; ++j) {
+      const uint32_t kj = key[j];
+      rank += (kj < ki) || (kj == ki && j < i);
+    }
+    ug[rank] = i;
+  }
+  for (int p = nb + threadIdx.x; p < ngroups * G; p += blockDim.x) ug[p] = -1;
+}
+
+// ---------------------------------------------------------------- k_union
+// One wave per group: the members' maps are folded into per-key-block member
+// masks in LDS (4 key blocks per word, one byte each), then compacted in
+// ascending key-block order into the group's list of (key block | mask << 16).
+constexpr int kUnionWaves = 8;
+
+__global__ __launch_bounds__(64 * kUnionWaves) void k_union(const int32_t *__restrict__ map, int nb,
+                                                            int kb, int G, int ngroups, int list_stride,
+                                                            const int32_t *__restrict__ ugroup,
+                                                            int32_t *__restrict__ ucount,
+                                                            int32_t *__restrict__ ulist) {
+  extern __shared__ uint32_t smask[];  // [kUnionWaves][nbw]
+  const int nbw = (nb + 3) / 4;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int bh = blockIdx.y;
+  const int gi = blockIdx.x * kUnionWaves + wave;
+  if (gi >= ngroups) return;  // per wave; no workgroup barrier follows
+  uint32_t *mw = smask + wave * nbw;
+  for (int w = lane; w < nbw; w += 64) mw[w] = 0u;
+  const int64_t gidx = (int64_t)bh * ngroups + gi;
+  const int32_t *mb = map + (int64_t)bh * nb * kb;
+  for (int e = lane; e < G * kb; e += 64) {
+    const int m = e / kb, t = e - m * kb;
+    const int qb = ugroup[gidx * G + m];
+    if (qb < 0) continue;
+    const int j = min(max(mb[(int64_t)qb * kb + t], 0), nb - 1);
+    atomicOr(&mw[j >> 2], 1u << ((j & 3) * 8 + m));
+  }
+  // ascending compaction: lane owns words [lane*per, lane*per + per)
+  const int per = (nbw + 63) / 64;
+  int cnt = 0;
+  for (int w = lane * per; w < min(nbw, lane * per + per); ++w) {
+    const uint32_t x = mw[w];
+    cnt += ((x & 0xffu) != 0) + ((x & 0xff00u) != 0) + ((x & 0xff0000u) != 0) + ((x >> 24) != 0);
+  }
+  int incl = cnt;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
+  }
+  int pos = incl - cnt;
+  int32_t *out = ulist + gidx * list_stride;
+  for (int w = lane * per; w < min(nbw, lane * per + per); ++w) {
+    const uint32_t x = mw[w];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t msk = (x >> (8 * q)) & 0xffu;
+      if (msk) out[pos++] = (4 * w + q) | (int)(msk << 16);
+    }
+  }
+  if (lane == 63) ucount[gidx] = incl;
+}
+
 // ----------------------------------------------------------------- k_attn
-// One workgroup (2 waves) per (batch, head, query block); wave w owns query
-// rows 32w..32w+31 of the block, one query per lane column.  K and V^T tiles
-// of each kept key block are copied global->LDS directly (16 B per lane).
-template <int D, bool SPARSE, bool LOWRANK, bool ACCUM, bool OUTF32>
-__global__ __launch_bounds__(128) void k_attn(AttnArgs args) {
+// One workgroup per group of G query blocks of one (batch, head); waves
+// 2m and 2m+1 own query rows 0-31 and 32-63 of member m, one query per lane
+// column.  The workgroup walks the group's union list; each listed key
+// block's K and V tiles (row-major, chunk-swizzled) are copied global->LDS
+// directly (16 B per lane) into an S-slot ring,
+// S-1 tiles ahead of the one being consumed, and every member that kept
+// the block runs S^T = K Q^T, the online softmax and O^T += V^T P^T on it.
+// Workgroups are mapped so that all XCDs work on the same head at a time and
+// each XCD takes a contiguous run of similar groups (shared L2 lines).
+template <int D, int G, int S, bool SPARSE, bool LOWRANK, bool ACCUM, bool OUTF32>
+__global__ __launch_bounds__(128 * G) void k_attn(AttnArgs args) {
   constexpr int CH = D / 8;
   constexpr int NS = D / 16;  // k-steps over head_dim
   constexpr int DT = D / 32;  // output d-tiles
-  __shared__ __attribute__((aligned(1024))) uint16_t sK[SPARSE ? 64 * D : 8];
-  __shared__ __attribute__((aligned(1024))) uint16_t sV[SPARSE ? 64 * D : 8];
+  constexpr int NT = 128 * G;
+  constexpr int TILE = 64 * D;                // bf16 elements per K (or V^T) tile
+  constexpr int OPS = (64 * CH) / NT;         // DMA ops per thread per tensor per tile
+  static_assert(OPS >= 1 && (64 * CH) % NT == 0, "tile split");
+  static_assert(S >= 2 && S <= 4, "ring depth");
+  constexpr int LMAX = 2048;  // union-list entries staged in LDS (longer lists read the tail from HBM)
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[SPARSE ? S * 2 * TILE : 8];
+  __shared__ int32_t slist[SPARSE ? LMAX : 1];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 5;
-  // XCD-aware order: consecutive workgroups of one XCD take consecutive
-  // query blocks of one head, so their K/V gathers share that XCD's L2.
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, g = lane >> 5;
+  const int member = wave >> 1, half = wave & 1;
   const int64_t L = blockIdx.x;
-  const int64_t tile = (L % 8) * args.tiles_per_xcd + (L / 8);
-  if (tile >= args.tiles || (L / 8) >= args.tiles_per_xcd) return;
-  const int bh = (int)(tile / args.nb);
-  const int qb = (int)(tile % args.nb);
+  const int64_t sidx = L / 8;
+  const int64_t bh64 = sidx / args.groups_per_xcd;
+  const int64_t group = (L % 8) * args.groups_per_xcd + sidx % args.groups_per_xcd;
+  if (bh64 >= args.bh_count || group >= args.ngroups) return;
+  const int bh = (int)bh64;
+  const int64_t gidx = (int64_t)bh * args.ngroups + group;
+  const int qb = args.ugroup[gidx * G + member];
+  const bool active = qb >= 0;
   const int b = bh / args.heads, h = bh % args.heads;
   const int64_t base = (int64_t)b * args.stride_b + (int64_t)h * args.stride_h;
-  const int64_t n = (int64_t)qb * 64 + 32 * wave + (lane & 31);  // this lane's query token
+  const int64_t n = (int64_t)(active ? qb : 0) * 64 + 32 * half + (lane & 31);
 
   bf16x8 qreg[NS];
   {
@@ -484,92 +610,119 @@ __global__ __launch_bounds__(128) void k_attn(AttnArgs args) {
   float m_run = -INFINITY, l_run = 0.0f;
 
   if (SPARSE) {
-    const int32_t *mrow = args.map + ((int64_t)bh * args.nb + qb) * args.kb;
+    const int32_t *list = args.ulist + gidx * args.list_stride;
+    const int U = args.ucount[gidx];
+    // Stage the list in LDS before the first DMA: a global load inside the
+    // loop would need vmcnt(0), which also drains the prefetched tiles.  Lists
+    // longer than LMAX (keep ratios near 1) take a second copy of the loop
+    // that reads the list from HBM.
+    for (int i = tid; i < min(U, LMAX); i += NT) slist[i] = list[i];
+    __syncthreads();
     const uint16_t *Kb = args.k + base;
-    const uint16_t *Vtb = args.vt + (int64_t)bh * args.nb * (64 * D);
+    const uint16_t *Vb = args.v + base;
     const float c = args.scale_log2e;
-    const int tid = threadIdx.x;
-    for (int t = 0; t < args.kb; ++t) {
-      // ids outside [0, nb) (a malformed caller map) are clamped: wrong output, no stray reads
-      const int j = min(max(mrow[t], 0), args.nb - 1);
-      // ---- copy K_j (chunk-swizzled rows) and V^T_j (already in LDS image order)
+    auto main_loop = [&](auto lds_tag) {
+      constexpr bool FROM_LDS = decltype(lds_tag)::value;
+      auto entry = [&](int t) -> int {
+        if constexpr (FROM_LDS) return slist[t];
+        else return list[t];
+      };
+      auto issue = [&](int t) {
+        const int j = entry(t) & 0xffff;
+        uint16_t *slot = ring + (t % S) * (2 * TILE);
 #pragma unroll
-      for (int it = 0; it < (64 * CH) / 128; ++it) {
-        const int cidx = it * 128 + tid;
-        const int row = cidx / CH, pc = cidx % CH;
-        const int lc = pc ^ (row & 7);
-        lds_dma16(Kb + ((int64_t)j * 64 + row) * args.stride_n + lc * 8,
-                  sK + (it * 128 + wave * 64) * 8);
-        lds_dma16(Vtb + (int64_t)j * (64 * D) + cidx * 8, sV + (it * 128 + wave * 64) * 8);
-      }
-      __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0): both tiles landed in LDS
-      __syncthreads();
-
-      // ---- S^T = K Q^T (two 32-key tiles)
-      f32x16 sacc[2];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        sacc[kt] = f32x16{};
-        const int row = 32 * kt + (lane & 31);
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          const int lc = 2 * s + g;
-          const bf16x8 ka = *(const bf16x8 *)(sK + row * D + ((lc ^ (row & 7)) * 8));
-          sacc[kt] = mfma_bf16(ka, qreg[s], sacc[kt]);
+        for (int o = 0; o < OPS; ++o) {
+          const int cidx = o * NT + tid;
+          const int row = cidx / CH, pc = cidx % CH;
+          // rows past N (tail block) are copied from row N-1: finite values,
+          // masked out of the softmax
+          const int64_t src = min((int64_t)j * 64 + row, args.n_tokens - 1) * args.stride_n;
+          lds_dma16(Kb + src + ((pc ^ swz_k(row)) * 8), slot + (o * NT + wave * 64) * 8);
+          lds_dma16(Vb + src + ((pc ^ swz_v(row)) * 8), slot + TILE + (o * NT + wave * 64) * 8);
         }
-      }
-      // ---- online softmax (base 2); keys >= N masked in the tail block
-      const bool tail = (int64_t)(j + 1) * 64 > args.n_tokens;
-      float mx = -INFINITY;
+      };
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
+      for (int t = 0; t < S - 1; ++t)
+        if (t < U) issue(t);
+      for (int t = 0; t < U; ++t) {
+        wait_tiles_in_flight<OPS, S>(min(S - 2, U - 1 - t));
+        barrier_lds();  // tile t visible to all waves; every wave is done with tile t-1
+        if (t + S - 1 < U) issue(t + S - 1);
+        const int ent = entry(t);
+        if (!active || !((ent >> (16 + member)) & 1)) continue;
+        const int j = ent & 0xffff;
+        const uint16_t *sK = ring + (t % S) * (2 * TILE);
+        const uint16_t *sV = sK + TILE;
+        // ---- S^T = K Q^T (two 32-key tiles)
+        f32x16 sacc[2];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float x = sacc[kt][i] * c;
-          if (tail) {
-            const int64_t key = (int64_t)j * 64 + 32 * kt + 8 * (i >> 2) + 4 * g + (i & 3);
-            x = key < args.n_tokens ? x : -INFINITY;
+        for (int kt = 0; kt < 2; ++kt) {
+          sacc[kt] = f32x16{};
+          const int row = 32 * kt + (lane & 31);
+#pragma unroll
+          for (int s = 0; s < NS; ++s) {
+            const int lc = 2 * s + g;
+            const bf16x8 ka = *(const bf16x8 *)(sK + row * D + ((lc ^ swz_k(row)) * 8));
+            sacc[kt] = mfma_bf16(ka, qreg[s], sacc[kt]);
           }
-          sacc[kt][i] = x;
-          mx = fmaxf(mx, x);
+        }
+        // ---- online softmax (base 2); keys >= N masked in the tail block
+        if ((int64_t)(j + 1) * 64 > args.n_tokens) {
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int64_t key = (int64_t)j * 64 + 32 * kt + 8 * (i >> 2) + 4 * g + (i & 3);
+              if (key >= args.n_tokens) sacc[kt][i] = -INFINITY;
+            }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kt][i]);
+        mx = fmaxf(mx, shfl_xor32(mx)) * c;
+        // Exact running max (the largest weight is exp2(0) = 1, exact in
+        // bf16); O is rescaled only when some lane's max moved.
+        const bool grow = mx > m_run;
+        const float m_new = grow ? mx : m_run;
+        const float alpha = fast_exp2(m_run - m_new);
+        m_run = m_new;
+        float psum = 0.0f;
+        bf16x8 pop[4];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float p = fast_exp2(__builtin_fmaf(sacc[kt][i], c, -m_new));
+            psum += p;
+            pop[2 * kt + (i >> 3)][i & 7] = (__bf16)p;
+          }
+        }
+        l_run = l_run * alpha + psum;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+        }
+        // ---- O^T += V^T P^T
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const bf16x8 va = vt_operand<D>(sV, s, dt, lane);
+            oacc[dt] = mfma_bf16(va, pop[s], oacc[dt]);
+          }
         }
       }
-      mx = fmaxf(mx, shfl_xor32(mx));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = exp2f(m_run - m_new);
-      m_run = m_new;
-      float psum = 0.0f;
-      bf16x8 pop[4];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = exp2f(sacc[kt][i] - m_new);
-          psum += p;
-          pop[2 * kt + (i >> 3)][i & 7] = (__bf16)p;
-        }
-      }
-      l_run = l_run * alpha + psum;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
-      // ---- O^T += V^T P^T
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int d = 32 * dt + (lane & 31);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int lc = 2 * s + g;
-          const bf16x8 va = *(const bf16x8 *)(sV + d * 64 + ((lc ^ (d & 7)) * 8));
-          oacc[dt] = mfma_bf16(va, pop[s], oacc[dt]);
-        }
-      }
-      __syncthreads();  // all reads of sK/sV done before the next copy
-    }
+    };
+    if (U <= LMAX) main_loop(std::integral_constant<bool, true>{});
+    else main_loop(std::integral_constant<bool, false>{});
     const float l_tot = l_run + shfl_xor32(l_run);
-    const float inv_l = args.kb > 0 ? 1.0f / l_tot : 0.0f;
+    const float inv_l = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) oacc[dt] *= inv_l;
   }
+  if (!active) return;
 
   if (LOWRANK) {
     // a^T = Wq^T R(q): A = Wq^T (rows r), B = rotated Q (cols query)
@@ -657,28 +810,22 @@ void launch_setup(const SetupArgs &a, hipStream_t st) {
 }
 
 template <int D>
-static void pass1_d(const Pass1Args &a, int nchunks, int bh, bool pool, bool state, bool vt,
-                    hipStream_t st) {
+static void pass1_d(const Pass1Args &a, int nchunks, int bh, bool pool, bool state, hipStream_t st) {
   dim3 grid(nchunks, bh), block(256);
-  if (pool && state && vt)
-    hipLaunchKernelGGL((k_pass1<D, true, true, true>), grid, block, 0, st, a);
-  else if (pool && !state && !vt)
-    hipLaunchKernelGGL((k_pass1<D, true, false, false>), grid, block, 0, st, a);
-  else if (!pool && !state && vt)
-    hipLaunchKernelGGL((k_pass1<D, false, false, true>), grid, block, 0, st, a);
-  else if (!pool && state && !vt)
-    hipLaunchKernelGGL((k_pass1<D, false, true, false>), grid, block, 0, st, a);
+  if (pool && state) hipLaunchKernelGGL((k_pass1<D, true, true>), grid, block, 0, st, a);
+  else if (pool) hipLaunchKernelGGL((k_pass1<D, true, false>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((k_pass1<D, false, true>), grid, block, 0, st, a);
 }
 
-void launch_pass1(const Pass1Args &a, int D, int nchunks, int bh, bool pool, bool state, bool vt,
-                  hipStream_t st) {
-  if (D == 64) pass1_d<64>(a, nchunks, bh, pool, state, vt, st);
-  else pass1_d<128>(a, nchunks, bh, pool, state, vt, st);
+void launch_pass1(const Pass1Args &a, int D, int nchunks, int bh, bool pool, bool state, hipStream_t st) {
+  if (D == 64) pass1_d<64>(a, nchunks, bh, pool, state, st);
+  else pass1_d<128>(a, nchunks, bh, pool, state, st);
 }
 
 void launch_state_reduce(const float *part, int nchunks, int D, int rank, int bh, uint16_t *st_out,
                          float *z, hipStream_t st) {
-  hipLaunchKernelGGL(k_state_reduce, dim3(bh), dim3(256), 0, st, part, nchunks, D, rank, st_out, z);
+  hipLaunchKernelGGL(k_state_reduce, dim3((D * 32 + 32 + 255) / 256, bh), dim3(256), 0, st, part, nchunks, D,
+                     rank, st_out, z);
 }
 
 void launch_scores(const float *qp, const float *kp, float *s, int nb, int D, int bh,
@@ -706,30 +853,42 @@ void launch_topk(const float *s, int32_t *map, int nb, int kb, int64_t rows, hip
 #undef ROLA_TOPK
 }
 
-template <int D, bool SPARSE, bool LOWRANK>
-static void attn_d2(const AttnArgs &a, bool accum, bool outf32, hipStream_t st) {
-  dim3 grid((unsigned)(8 * a.tiles_per_xcd)), block(128);
-  if (accum) {
-    if (outf32) hipLaunchKernelGGL((k_attn<D, SPARSE, LOWRANK, true, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((k_attn<D, SPARSE, LOWRANK, true, false>), grid, block, 0, st, a);
-  } else {
-    if (outf32) hipLaunchKernelGGL((k_attn<D, SPARSE, LOWRANK, false, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((k_attn<D, SPARSE, LOWRANK, false, false>), grid, block, 0, st, a);
+void launch_schedule(const int32_t *map, int nb, int kb, int G, int ngroups, int list_stride,
+                     int bh, int32_t *ugroup, int32_t *ucount, int32_t *ulist, hipStream_t st) {
+  hipLaunchKernelGGL(k_order, dim3(bh), dim3(1024), (size_t)nb * 4, st, map, nb, kb, G, ngroups, ugroup);
+  if (kb > 0) {
+    const size_t lds = (size_t)kUnionWaves * ((nb + 3) / 4) * 4;
+    hipLaunchKernelGGL(k_union, dim3((ngroups + kUnionWaves - 1) / kUnionWaves, bh), dim3(64 * kUnionWaves), lds,
+                       st, map, nb, kb, G, ngroups, list_stride, ugroup, ucount, ulist);
   }
 }
 
-template <int D>
+template <int D, int G, int S, bool SPARSE, bool LOWRANK>
+static void attn_d2(const AttnArgs &a, bool accum, bool outf32, hipStream_t st) {
+  dim3 grid((unsigned)(8 * a.groups_per_xcd * a.bh_count)), block(128 * G);
+  if (accum) {
+    if (outf32) hipLaunchKernelGGL((k_attn<D, G, S, SPARSE, LOWRANK, true, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_attn<D, G, S, SPARSE, LOWRANK, true, false>), grid, block, 0, st, a);
+  } else {
+    if (outf32) hipLaunchKernelGGL((k_attn<D, G, S, SPARSE, LOWRANK, false, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_attn<D, G, S, SPARSE, LOWRANK, false, false>), grid, block, 0, st, a);
+  }
+}
+
+template <int D, int G, int S>
 static void attn_d(const AttnArgs &a, bool sparse, bool lowrank, bool accum, bool outf32,
                    hipStream_t st) {
-  if (sparse && lowrank) attn_d2<D, true, true>(a, accum, outf32, st);
-  else if (sparse) attn_d2<D, true, false>(a, accum, outf32, st);
-  else attn_d2<D, false, true>(a, accum, outf32, st);
+  if (sparse && lowrank) attn_d2<D, G, S, true, true>(a, accum, outf32, st);
+  else if (sparse) attn_d2<D, G, S, true, false>(a, accum, outf32, st);
+  else attn_d2<D, G, S, false, true>(a, accum, outf32, st);
 }
+
+int attn_group_size() { return ROLA_ATTN_G; }
 
 void launch_attn(const AttnArgs &a, int D, bool sparse, bool lowrank, bool accum, bool outf32,
                  hipStream_t st) {
-  if (D == 64) attn_d<64>(a, sparse, lowrank, accum, outf32, st);
-  else attn_d<128>(a, sparse, lowrank, accum, outf32, st);
+  if (D == 64) attn_d<64, ROLA_ATTN_G, ROLA_ATTN_S>(a, sparse, lowrank, accum, outf32, st);
+  else attn_d<128, ROLA_ATTN_G, ROLA_ATTN_S>(a, sparse, lowrank, accum, outf32, st);
 }
 
 }  // namespace rola

@@ -1,7 +1,11 @@
 """GPU parity: librola (through its C ABI) against the CPU oracle on the same seeded inputs.
 
 Bar: block maps and pooled scores bit-exact; outputs within max|O - O_ref| <=
-2e-2 * rms(O_ref) over valid rows (bf16); padded rows exactly zero.
+2e-2 * rms(O_ref) over valid rows; padded rows exactly zero.  When the output
+is stored in bf16, the correctly rounded storage of a result within that bound
+adds up to half a bf16 ulp (2^-9 |O|) per element, so the bound there is
+2e-2 * rms * (1 + 2^-9) + 2^-9 |O_ref| (with max|O|/rms near 10, rounding alone
+reaches 2e-2 * rms).
 """
 import numpy as np
 import pytest
@@ -33,6 +37,15 @@ def host_f64(t):
 def rel_err(got, ref):
     rms = np.sqrt(np.mean(ref ** 2))
     return float(np.max(np.abs(got - ref)) / rms)
+
+
+def bound_ratio(got, ref, bf16_out):
+    """max over elements of |got - ref| / bound (<= 1 passes)."""
+    rms = np.sqrt(np.mean(ref ** 2))
+    bound = TOL_BF16 * rms
+    if bf16_out:
+        bound = bound * (1 + 2.0 ** -9) + 2.0 ** -9 * np.abs(ref)
+    return float(np.max(np.abs(got - ref) / bound))
 
 
 def say(*a):
@@ -93,8 +106,9 @@ def test_forward_matches_oracle(name, w, out_f32):
     got = host_f64(out)[0]
     assert np.all(got[:, w.n_tokens:] == 0)
     err = rel_err(got[:, :w.n_tokens], o_ref[:, :w.n_tokens])
-    say("forward", name, "err/rms", err)
-    assert err <= TOL_BF16
+    ratio = bound_ratio(got[:, :w.n_tokens], o_ref[:, :w.n_tokens], not out_f32)
+    say("forward", name, "err/rms", err, "err/bound", ratio)
+    assert ratio <= 1.0
 
 
 @pytest.mark.parametrize("name,w", SMALL[:3], ids=[s[0] for s in SMALL[:3]])
@@ -239,8 +253,9 @@ def test_full_size_sampled(name):
         lr = oracle.lowrank_rows(qf, wq, S, z, w.grid, rows)
         got = out[0, h, torch.from_numpy(rows).cuda()].float().cpu().numpy().astype(np.float64)
         err = rel_err(got, sp + lr)
+        ratio = bound_ratio(got, sp + lr, True)
         worst = max(worst, err)
-        assert err <= TOL_BF16, (h, err)
+        assert ratio <= 1.0, (h, err, ratio)
         pad = out[0, h, w.n_tokens:].float()
         assert torch.count_nonzero(pad).item() == 0
     say("full size", name, "worst err/rms", worst)
