@@ -30,12 +30,11 @@ struct Plan {
   double theta;
   float scale;
   int grid[3];
-  int tab_total, tab1, tab2;
   int nchunks, cpc;
   // workspace offsets (bytes)
   int G;
   int64_t ngroups, list_stride;
-  int64_t off_tab, off_wqT, off_wkT, off_qp, off_kp, off_scores, off_map, off_part, off_st,
+  int64_t off_wqT, off_wkT, off_qp, off_kp, off_scores, off_map, off_part, off_st,
       off_z, off_ugroup, off_ucount, off_ulist, total;
 };
 
@@ -87,16 +86,12 @@ int32_t make_plan(const rola_problem *p, const rola_config *c, Plan *pl) {
   P.theta = c->rope_theta > 0.0f ? (double)c->rope_theta : 10000.0;
   P.scale = c->softmax_scale > 0.0f ? c->softmax_scale : (float)(1.0 / std::sqrt((double)D));
   P.grid[0] = p->grid_t; P.grid[1] = p->grid_h; P.grid[2] = p->grid_w;
-  P.tab1 = P.grid[0] * (split[0] / 2);
-  P.tab2 = P.tab1 + P.grid[1] * (split[1] / 2);
-  P.tab_total = P.tab2 + P.grid[2] * (split[2] / 2);
   // pass-1 chunking: about 4096 workgroups in total
   int nchunks = (int)std::max<int64_t>(1, std::min<int64_t>(nb, (4096 + P.BH - 1) / P.BH));
   P.cpc = (nb + nchunks - 1) / nchunks;
   P.nchunks = (nb + P.cpc - 1) / P.cpc;
 
   int64_t o = 0;
-  P.off_tab = o; o = align_up(o + (int64_t)P.tab_total * 8);
   P.off_wqT = o; o = align_up(o + 32LL * D * 2);
   P.off_wkT = o; o = align_up(o + 32LL * D * 2);
   P.off_qp = o; o = align_up(o + P.BH * nb * D * 4);
@@ -159,18 +154,16 @@ int32_t timed(const char *name, hipStream_t st, F &&launch) {
   return err == hipSuccess ? ROLA_OK : ROLA_ERR_DEVICE;
 }
 
-rola::RopeArgsHost rope_args(const Plan &P, uint8_t *ws) {
+rola::RopeArgsHost rope_args(const Plan &P, uint8_t *) {
   rola::RopeArgsHost r;
-  r.tab = (const float2 *)(ws + P.off_tab);
   r.off1 = P.split[0];
   r.off2 = P.split[0] + P.split[1];
   r.half0 = P.split[0] / 2;
   r.half1 = P.split[1] / 2;
   r.half2 = P.split[2] / 2;
-  r.tab1 = P.tab1;
-  r.tab2 = P.tab2;
   r.grid_h = P.grid[1];
   r.grid_w = P.grid[2];
+  r.log2_theta = (float)std::log2(P.theta);
   return r;
 }
 
@@ -179,11 +172,6 @@ int32_t run_setup(const Plan &P, const float *wq, const float *wk, uint8_t *ws, 
   a.wq = wq; a.wk = wk; a.D = P.D; a.rank = P.r;
   a.wqT = (uint16_t *)(ws + P.off_wqT);
   a.wkT = (uint16_t *)(ws + P.off_wkT);
-  a.tab = (float2 *)(ws + P.off_tab);
-  a.tab_total = P.tab_total;
-  a.g0 = P.grid[0]; a.g1 = P.grid[1];
-  a.h0 = P.split[0] / 2; a.h1 = P.split[1] / 2; a.h2 = P.split[2] / 2;
-  a.theta = P.theta;
   return timed("setup", st, [&] { rola::launch_setup(a, st); });
 }
 

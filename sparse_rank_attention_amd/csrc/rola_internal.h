@@ -6,22 +6,16 @@
 namespace rola {
 
 struct RopeArgsHost {
-  const float2 *tab;
-  int off1, off2;
-  int half0, half1, half2;
-  int tab1, tab2;
+  int off1, off2;           // first dims of the h and w axes
+  int half0, half1, half2;  // rotary pairs per axis
   int grid_h, grid_w;
+  float log2_theta;
 };
 
 struct SetupArgs {
   const float *wq, *wk;
   int D, rank;
   uint16_t *wqT, *wkT;  // bf16 [32][D]
-  float2 *tab;
-  int tab_total;
-  int g0, g1;           // grid_t, grid_h (positions per axis for the first two axes)
-  int h0, h1, h2;       // pairs per axis
-  double theta;
 };
 
 struct Pass1Args {
@@ -47,6 +41,7 @@ struct Pass1Args {
 #ifndef ROLA_ATTN_S
 #define ROLA_ATTN_S 4
 #endif
+
 
 struct AttnArgs {
   const uint16_t *q, *k, *v;

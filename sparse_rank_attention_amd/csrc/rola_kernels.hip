@@ -78,15 +78,52 @@ static __device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c)
 
 static __device__ __forceinline__ float shfl_xor32(float v) { return __shfl_xor(v, 32, 64); }
 
+// max / sum of a value and its partner lane l^32, on the VALU: the two
+// halves of the wave are exchanged between two registers (v_permlane32_swap)
+// and combined symmetrically, so every lane gets the pair result.
+static __device__ __forceinline__ float pair_max32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+static __device__ __forceinline__ float pair_sum32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Direct global->LDS copy of 16 bytes per lane: lane l of the wave writes
+// lds_dst + 16*l (lds_dst is wave-uniform).  Issued from inline asm so that
+// the compiler does not order every later LDS access after all pending
+// copies (it would insert s_waitcnt vmcnt(0) and drain the prefetch rings);
+// completion is awaited explicitly with s_waitcnt vmcnt before use.  M0 is
+// saved and restored around the copy.
 static __device__ __forceinline__ void lds_dma16(const void *gsrc, void *lds_dst) {
-  __builtin_amdgcn_global_load_lds((const GLOBAL_AS void *)gsrc, (LDS_AS void *)lds_dst, 16, 0, 0);
+  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(LDS_AS void *)lds_dst);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(base), "v"(gsrc)
+      : "memory");
 }
 
 // LDS tile layouts: row-major [64 rows][D] bf16 in 16-byte chunks, chunk c
 // of row r stored at c ^ swizzle(r).  K tiles (read as 16-byte MFMA rows)
 // use r & 7; V tiles (read transposed, 8 bytes per lane) use 2*(r & 3).
-static __device__ __forceinline__ int swz_k(int r) { return r & 7; }
-static __device__ __forceinline__ int swz_v(int r) { return 2 * (r & 3); }
+#ifndef ROLA_SWZ_K
+#define ROLA_SWZ_K 15
+#endif
+#ifndef ROLA_SWZ_V
+#define ROLA_SWZ_V 4
+#endif
+// K: XOR with the row's low bits (16 chunks per row at D=128, 8 at D=64);
+// V: XOR with a multiple of (row & 3), the four rows a transposed read spans.
+template <int D>
+static __device__ __forceinline__ int swz_k(int r) { return r & (ROLA_SWZ_K & (D / 8 - 1)); }
+template <int D>
+static __device__ __forceinline__ int swz_v(int r) { return (ROLA_SWZ_V * (r & 3)) & (D / 8 - 1); }
 
 static __device__ __forceinline__ void barrier_lds() {
   // all LDS reads of this wave retired, then a plain workgroup barrier (no
@@ -122,8 +159,8 @@ static __device__ __forceinline__ bf16x8 vt_operand(const uint16_t *sV, int s, i
   const int dstart = 32 * dt + 16 * dhalf + 4 * (i & 3);
   const int c = dstart >> 3, sub = dstart & 7;
   const int r0 = 16 * s + 4 * g + (i >> 2), r1 = r0 + 8;
-  const LDS_AS i16x4 *p0 = (const LDS_AS i16x4 *)(const LDS_AS uint16_t *)(sV + r0 * D + ((c ^ swz_v(r0)) << 3) + sub);
-  const LDS_AS i16x4 *p1 = (const LDS_AS i16x4 *)(const LDS_AS uint16_t *)(sV + r1 * D + ((c ^ swz_v(r1)) << 3) + sub);
+  const LDS_AS i16x4 *p0 = (const LDS_AS i16x4 *)(const LDS_AS uint16_t *)(sV + r0 * D + ((c ^ swz_v<D>(r0)) << 3) + sub);
+  const LDS_AS i16x4 *p1 = (const LDS_AS i16x4 *)(const LDS_AS uint16_t *)(sV + r1 * D + ((c ^ swz_v<D>(r1)) << 3) + sub);
   const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)p0);
   const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)p1);
   typedef short i16x8 __attribute__((ext_vector_type(8)));
@@ -131,8 +168,21 @@ static __device__ __forceinline__ bf16x8 vt_operand(const uint16_t *sV, int s, i
   return __builtin_bit_cast(bf16x8, ab);
 }
 
-// Rotary tables: tab holds (cos, sin) per axis, position and pair; the t,
-// h and w axes own dims [0, off1), [off1, off2), [off2, D).
+// The same operand from a precomputed lane address p (first four keys) and
+// the element distance `half` to the second four keys (8 rows further).
+static __device__ __forceinline__ bf16x8 vt_operand_at(const uint16_t *p, int half) {
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(const LDS_AS uint16_t *)p);
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(const LDS_AS uint16_t *)(p + half));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 ab = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, ab);
+}
+
+// 3-D rotary embedding: the t, h and w axes own dims [0, off1), [off1,
+// off2), [off2, D); pair p of an axis with d_a dims turns by
+// pos * theta^(-2p/d_a).  Angles are formed in fp32 and taken modulo one
+// turn before the hardware sine/cosine (inputs in revolutions), so no table
+// lookups (global loads) are needed inside the streaming loops.
 using RopeArgsDev = RopeArgsHost;
 
 static __device__ __forceinline__ void token_pos(int64_t n, const RopeArgsDev &ra, int &pt, int &ph,
@@ -144,38 +194,40 @@ static __device__ __forceinline__ void token_pos(int64_t n, const RopeArgsDev &r
   pw = rem - ph * ra.grid_w;
 }
 
-static __device__ __forceinline__ float2 rope_cs(int d, int pt, int ph, int pw, const RopeArgsDev &ra) {
-  int idx;
-  if (d < ra.off1)
-    idx = pt * ra.half0 + (d >> 1);
-  else if (d < ra.off2)
-    idx = ra.tab1 + ph * ra.half1 + ((d - ra.off1) >> 1);
-  else
-    idx = ra.tab2 + pw * ra.half2 + ((d - ra.off2) >> 1);
-  return ra.tab[idx];
+// inverse frequency of the pair starting at even dim d
+static __device__ __forceinline__ float rope_freq(int d, const RopeArgsDev &ra) {
+  int p, da;
+  if (d < ra.off1) { p = d >> 1; da = 2 * ra.half0; }
+  else if (d < ra.off2) { p = (d - ra.off1) >> 1; da = 2 * ra.half1; }
+  else { p = (d - ra.off2) >> 1; da = 2 * ra.half2; }
+  return exp2f(-2.0f * (float)p / (float)da * ra.log2_theta);
 }
 
 // Rotate 8 consecutive dims (4 pairs) starting at d0 and round to bf16.
+// freq[p]: inverse frequency of pair p (rope_freq(d0 + 2p)).
 static __device__ __forceinline__ bf16x8 rope8(bf16x8 x, int d0, int pt, int ph, int pw,
-                                               const RopeArgsDev &ra) {
+                                               const float *freq, const RopeArgsDev &ra) {
   const u32x4 u = as_u32x4(x);
   bf16x8 y;
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
+    const int d = d0 + 2 * p;
+    const int pos = d < ra.off1 ? pt : (d < ra.off2 ? ph : pw);
+    float rev = (float)pos * freq[p] * 0.15915494309189535f;  // angle / (2 pi)
+    rev = rev - floorf(rev);
+    const float cs = __builtin_amdgcn_cosf(rev), sn = __builtin_amdgcn_sinf(rev);
     const float x0 = bflo(u[p]), x1 = bfhi(u[p]);
-    const float2 cs = rope_cs(d0 + 2 * p, pt, ph, pw, ra);
-    y[2 * p] = (__bf16)(x0 * cs.x - x1 * cs.y);
-    y[2 * p + 1] = (__bf16)(x0 * cs.y + x1 * cs.x);
+    y[2 * p] = (__bf16)(x0 * cs - x1 * sn);
+    y[2 * p + 1] = (__bf16)(x0 * sn + x1 * cs);
   }
   return y;
 }
 
 // ---------------------------------------------------------------- k_setup
+// bf16 transposed projections [32][D]; rows >= rank are zero.
 __global__ void k_setup(const float *__restrict__ wq, const float *__restrict__ wk, int D, int rank,
-                        uint16_t *__restrict__ wqT, uint16_t *__restrict__ wkT, float2 *tab,
-                        int tab_total, int g0, int g1, int h0, int h1, int h2, double theta) {
+                        uint16_t *__restrict__ wqT, uint16_t *__restrict__ wkT) {
   const int tid = blockIdx.x * blockDim.x + threadIdx.x;
-  // transposed bf16 projections [32][D], rows >= rank zero
   if (tid < 32 * D) {
     const int r = tid / D, d = tid % D;
     float a = 0.0f, b = 0.0f;
@@ -186,21 +238,6 @@ __global__ void k_setup(const float *__restrict__ wq, const float *__restrict__ 
     const __bf16 ab = (__bf16)a, bb = (__bf16)b;
     wqT[tid] = __builtin_bit_cast(uint16_t, ab);
     wkT[tid] = __builtin_bit_cast(uint16_t, bb);
-  }
-  // rotary table: axis a, position pos, pair p -> (cos, sin) of pos * theta^(-2p/d_a)
-  if (tid < tab_total) {
-    int a, pos, p, da;
-    const int n0 = g0 * h0, n1 = g1 * h1;
-    if (tid < n0) {
-      a = 0; pos = tid / h0; p = tid % h0; da = 2 * h0;
-    } else if (tid < n0 + n1) {
-      a = 1; pos = (tid - n0) / h1; p = (tid - n0) % h1; da = 2 * h1;
-    } else {
-      a = 2; pos = (tid - n0 - n1) / h2; p = (tid - n0 - n1) % h2; da = 2 * h2;
-    }
-    (void)a;
-    const double ang = (double)pos * pow(theta, -2.0 * p / (double)da);
-    tab[tid] = make_float2((float)cos(ang), (float)sin(ang));
   }
 }
 
@@ -246,8 +283,8 @@ __global__ __launch_bounds__(256) void k_pass1(Pass1Args args) {
       const int64_t src = min(c * 64 + row, args.n_tokens - 1) * args.stride_n;
       uint16_t *dst = slot + (o * 256 + wave * 64) * 8;
       if (POOL) lds_dma16(Q + src + pc * 8, dst + QOFF);
-      lds_dma16(K + src + ((pc ^ swz_k(row)) * 8), dst + KOFF);
-      if (STATE) lds_dma16(V + src + ((pc ^ swz_v(row)) * 8), dst + VOFF);
+      lds_dma16(K + src + ((pc ^ swz_k<D>(row)) * 8), dst + KOFF);
+      if (STATE) lds_dma16(V + src + ((pc ^ swz_v<D>(row)) * 8), dst + VOFF);
     }
   };
 
@@ -258,12 +295,17 @@ __global__ __launch_bounds__(256) void k_pass1(Pass1Args args) {
   for (int i = 0; i < DT; ++i) sacc[i] = f32x16{};
   float zacc = 0.0f;
   bf16x8 wkreg[D / 16];
+  float freq[D / 4];  // inverse frequencies of this lane's rotary pairs
   const int tt = wave - 2;  // token tile of the state waves
   if (STATE && wave >= 2) {
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s)
+    for (int s = 0; s < D / 16; ++s) {
       wkreg[s] = *(const bf16x8 *)(args.wkT + (lane & 31) * D + 16 * s + 8 * g);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) freq[4 * s + p] = rope_freq(16 * s + 8 * g + 2 * p, ra);
+    }
   }
+  wait_vmcnt<0>();  // projection rows loaded before the copies start (in-order vmcnt)
 
   for (int i = 0; i < NSTAGE - 1; ++i)
     if (i < nblk) issue(i);
@@ -285,7 +327,7 @@ __global__ __launch_bounds__(256) void k_pass1(Pass1Args args) {
 #pragma unroll
       for (int s = 0; s < 64; ++s) {
         const int off = wave == 0 ? s * D + 2 * word
-                                  : s * D + ((((word >> 2) ^ swz_k(s)) << 3) | ((word & 3) << 1));
+                                  : s * D + ((((word >> 2) ^ swz_k<D>(s)) << 3) | ((word & 3) << 1));
         const uint32_t x = s < valid ? *(const uint32_t *)(tile + off) : 0u;
         if (s < 32) {
           lo[s] = bflo(x);
@@ -318,8 +360,8 @@ __global__ __launch_bounds__(256) void k_pass1(Pass1Args args) {
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) {
         const int lc = 2 * s + g;
-        bf16x8 kx = *(const bf16x8 *)(sK + row * D + ((lc ^ swz_k(row)) * 8));
-        kx = rope8(kx, 16 * s + 8 * g, pt, ph, pw, ra);
+        bf16x8 kx = *(const bf16x8 *)(sK + row * D + ((lc ^ swz_k<D>(row)) * 8));
+        kx = rope8(kx, 16 * s + 8 * g, pt, ph, pw, &freq[4 * s], ra);
         bacc = mfma_bf16(kx, wkreg[s], bacc);
       }
       // phi, mask invalid tokens and rank padding, z, pack as B operand
@@ -603,6 +645,9 @@ __global__ __launch_bounds__(128 * G) void k_attn(AttnArgs args) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) qreg[s] = *(const bf16x8 *)(qrow + 16 * s + 8 * g);
   }
+  // Q must be in registers before the tile copies start: vmcnt completes in
+  // order, so a first wait for Q inside the loop would also drain the ring.
+  wait_vmcnt<0>();
 
   f32x16 oacc[DT];
 #pragma unroll
@@ -621,6 +666,31 @@ __global__ __launch_bounds__(128 * G) void k_attn(AttnArgs args) {
     const uint16_t *Kb = args.k + base;
     const uint16_t *Vb = args.v + base;
     const float c = args.scale_log2e;
+    // per-lane LDS element offsets of the MFMA operands inside a tile:
+    // K rows l%32 (+32 rows for the second key tile) at chunk 2s+g;
+    // V^T transposed-read rows 4g + (l%16)/4 (+16 per k-step, +8 for the
+    // second half), dims 32dt + 16((l/16)%2) + 4(l%4)
+    int koff[NS], voff[DT];
+    int64_t gk[OPS], gv[OPS];  // this lane's global element offsets inside a key block
+#pragma unroll
+    for (int o = 0; o < OPS; ++o) {
+      const int cidx = o * NT + tid;
+      const int row = cidx / CH, pc = cidx % CH;
+      gk[o] = (int64_t)row * args.stride_n + ((pc ^ swz_k<D>(row)) * 8);
+      gv[o] = (int64_t)row * args.stride_n + ((pc ^ swz_v<D>(row)) * 8);
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < NS; ++s2) {
+      const int row = lane & 31;
+      koff[s2] = row * D + (((2 * s2 + g) ^ swz_k<D>(row)) * 8);
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int i = lane & 15, dhalf = (lane >> 4) & 1;
+      const int dstart = 32 * dt + 16 * dhalf + 4 * (i & 3);
+      const int r0 = 4 * g + (i >> 2);
+      voff[dt] = r0 * D + (((dstart >> 3) ^ swz_v<D>(r0)) << 3) + (dstart & 7);
+    }
     auto main_loop = [&](auto lds_tag) {
       constexpr bool FROM_LDS = decltype(lds_tag)::value;
       auto entry = [&](int t) -> int {
@@ -630,94 +700,109 @@ __global__ __launch_bounds__(128 * G) void k_attn(AttnArgs args) {
       auto issue = [&](int t) {
         const int j = entry(t) & 0xffff;
         uint16_t *slot = ring + (t % S) * (2 * TILE);
+        const int64_t jrow = (int64_t)j * 64;
+        if (jrow + 64 <= args.n_tokens) {
+          const uint16_t *kj = Kb + jrow * args.stride_n, *vj = Vb + jrow * args.stride_n;
 #pragma unroll
-        for (int o = 0; o < OPS; ++o) {
-          const int cidx = o * NT + tid;
-          const int row = cidx / CH, pc = cidx % CH;
-          // rows past N (tail block) are copied from row N-1: finite values,
-          // masked out of the softmax
-          const int64_t src = min((int64_t)j * 64 + row, args.n_tokens - 1) * args.stride_n;
-          lds_dma16(Kb + src + ((pc ^ swz_k(row)) * 8), slot + (o * NT + wave * 64) * 8);
-          lds_dma16(Vb + src + ((pc ^ swz_v(row)) * 8), slot + TILE + (o * NT + wave * 64) * 8);
+          for (int o = 0; o < OPS; ++o) {
+            lds_dma16(kj + gk[o], slot + (o * NT + wave * 64) * 8);
+            lds_dma16(vj + gv[o], slot + TILE + (o * NT + wave * 64) * 8);
+          }
+        } else {
+#pragma unroll
+          for (int o = 0; o < OPS; ++o) {
+            const int cidx = o * NT + tid;
+            const int row = cidx / CH, pc = cidx % CH;
+            // rows past N (tail block) are copied from row N-1: finite
+            // values, masked out of the softmax
+            const int64_t src = min(jrow + row, args.n_tokens - 1) * args.stride_n;
+            lds_dma16(Kb + src + ((pc ^ swz_k<D>(row)) * 8), slot + (o * NT + wave * 64) * 8);
+            lds_dma16(Vb + src + ((pc ^ swz_v<D>(row)) * 8), slot + TILE + (o * NT + wave * 64) * 8);
+          }
         }
       };
 #pragma unroll
       for (int t = 0; t < S - 1; ++t)
         if (t < U) issue(t);
       for (int t = 0; t < U; ++t) {
+        const int slot_t = t % S;
         wait_tiles_in_flight<OPS, S>(min(S - 2, U - 1 - t));
         barrier_lds();  // tile t visible to all waves; every wave is done with tile t-1
-        if (t + S - 1 < U) issue(t + S - 1);
         const int ent = entry(t);
-        if (!active || !((ent >> (16 + member)) & 1)) continue;
+        if (!active || !((ent >> (16 + member)) & 1)) {
+          // waves idle on this tile copy their share of tile t+S-1 at once
+          if (t + S - 1 < U) issue(t + S - 1);
+          continue;
+        }
         const int j = ent & 0xffff;
         const uint16_t *sK = ring + (t % S) * (2 * TILE);
         const uint16_t *sV = sK + TILE;
-        // ---- S^T = K Q^T (two 32-key tiles)
-        f32x16 sacc[2];
+        // ---- S^T = K Q^T: two independent 32-key chains
+        f32x16 sacc0 = f32x16{}, sacc1 = f32x16{};
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          sacc[kt] = f32x16{};
-          const int row = 32 * kt + (lane & 31);
+        for (int s = 0; s < NS; ++s)
+          sacc0 = mfma_bf16(*(const bf16x8 *)(sK + koff[s]), qreg[s], sacc0);
 #pragma unroll
-          for (int s = 0; s < NS; ++s) {
-            const int lc = 2 * s + g;
-            const bf16x8 ka = *(const bf16x8 *)(sK + row * D + ((lc ^ swz_k(row)) * 8));
-            sacc[kt] = mfma_bf16(ka, qreg[s], sacc[kt]);
-          }
-        }
-        // ---- online softmax (base 2); keys >= N masked in the tail block
+        for (int s = 0; s < NS; ++s)
+          sacc1 = mfma_bf16(*(const bf16x8 *)(sK + koff[s] + 32 * D), qreg[s], sacc1);
+        // keys >= N masked in the tail block
         if ((int64_t)(j + 1) * 64 > args.n_tokens) {
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int64_t key = (int64_t)j * 64 + 32 * kt + 8 * (i >> 2) + 4 * g + (i & 3);
-              if (key >= args.n_tokens) sacc[kt][i] = -INFINITY;
-            }
-        }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kt][i]);
-        mx = fmaxf(mx, shfl_xor32(mx)) * c;
-        // Exact running max (the largest weight is exp2(0) = 1, exact in
-        // bf16); O is rescaled only when some lane's max moved.
-        const bool grow = mx > m_run;
-        const float m_new = grow ? mx : m_run;
-        const float alpha = fast_exp2(m_run - m_new);
-        m_run = m_new;
-        float psum = 0.0f;
-        bf16x8 pop[4];
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
+          const int64_t nrel = args.n_tokens - (int64_t)j * 64;
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const float p = fast_exp2(__builtin_fmaf(sacc[kt][i], c, -m_new));
-            psum += p;
-            pop[2 * kt + (i >> 3)][i & 7] = (__bf16)p;
+            const int key = 8 * (i >> 2) + 4 * g + (i & 3);
+            if (key >= nrel) sacc0[i] = -INFINITY;
+            if (key + 32 >= nrel) sacc1[i] = -INFINITY;
           }
         }
-        l_run = l_run * alpha + psum;
+        // ---- online softmax, base 2, against a lazy reference: weights
+        // are exp2(s*c - m_ref) with m_ref an integer that moves only when the
+        // tile max exceeds it by more than 64 (or on the first tile), so O is
+        // almost never rescaled and the rescale, when it happens, is by an
+        // exact power of two.  Weights stay below 2^64: no overflow in fp32.
+        // The row sum is taken over the same bf16 weights the PV product uses.
+        float mx0 = -INFINITY, mx1 = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx0 = fmaxf(mx0, sacc0[i]);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx1 = fmaxf(mx1, sacc1[i]);
+        const float mx = pair_max32(fmaxf(mx0, mx1)) * c;
+        const bool grow = mx > m_run + 64.0f;  // always true on the first tile (m_run = -inf)
         if (__builtin_amdgcn_ballot_w64(grow)) {
+          const float m_new = grow ? ceilf(mx) : m_run;
+          const float alpha = fast_exp2(m_run - m_new);
+          m_run = m_new;
+          l_run *= alpha;
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
         }
-        // ---- O^T += V^T P^T
+        const float negm = -m_run;
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+        float psum = 0.0f;
+        // ---- weights for 16 keys at a time, each step feeding 4 PV MFMAs
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
+        for (int s = 0; s < 4; ++s) {
+          const f32x16 &src = (s < 2) ? sacc0 : sacc1;
+          bf16x8 pw;
 #pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const bf16x8 va = vt_operand<D>(sV, s, dt, lane);
-            oacc[dt] = mfma_bf16(va, pop[s], oacc[dt]);
+          for (int e = 0; e < 8; ++e) pw[e] = (__bf16)fast_exp2(__builtin_fmaf(src[8 * (s & 1) + e], c, negm));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bf16x2 pr = {pw[2 * e], pw[2 * e + 1]};
+            psum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, psum, false);
           }
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+            oacc[dt] = mfma_bf16(vt_operand_at(sV + voff[dt] + s * 16 * D, 8 * D), pw, oacc[dt]);
         }
+        l_run += psum;
+        if (t + S - 1 < U) issue(t + S - 1);  // this wave's share, after its compute
       }
     };
     if (U <= LMAX) main_loop(std::integral_constant<bool, true>{});
     else main_loop(std::integral_constant<bool, false>{});
-    const float l_tot = l_run + shfl_xor32(l_run);
+    const float l_tot = pair_sum32(l_run);
     const float inv_l = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) oacc[dt] *= inv_l;
@@ -731,7 +816,10 @@ __global__ __launch_bounds__(128 * G) void k_attn(AttnArgs args) {
     f32x16 aacc = f32x16{};
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const bf16x8 qr = rope8(qreg[s], 16 * s + 8 * g, pt, ph, pw, args.rope);
+      float freq[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) freq[p] = rope_freq(16 * s + 8 * g + 2 * p, args.rope);
+      const bf16x8 qr = rope8(qreg[s], 16 * s + 8 * g, pt, ph, pw, freq, args.rope);
       const bf16x8 wa = *(const bf16x8 *)(args.wqT + (lane & 31) * D + 16 * s + 8 * g);
       aacc = mfma_bf16(wa, qr, aacc);
     }
@@ -804,9 +892,8 @@ __global__ __launch_bounds__(128 * G) void k_attn(AttnArgs args) {
 
 // ---------------------------------------------------------------- launchers
 void launch_setup(const SetupArgs &a, hipStream_t st) {
-  const int total = (32 * a.D > a.tab_total) ? 32 * a.D : a.tab_total;
-  hipLaunchKernelGGL(k_setup, dim3((total + 255) / 256), dim3(256), 0, st, a.wq, a.wk, a.D, a.rank,
-                     a.wqT, a.wkT, a.tab, a.tab_total, a.g0, a.g1, a.h0, a.h1, a.h2, a.theta);
+  hipLaunchKernelGGL(k_setup, dim3((32 * a.D + 255) / 256), dim3(256), 0, st, a.wq, a.wk, a.D, a.rank,
+                     a.wqT, a.wkT);
 }
 
 template <int D>

@@ -53,15 +53,18 @@ _lib = None
 
 
 def library_path() -> str:
-    return _build.LIB
+    """librola.so in the package (ROLA_LIBRARY may name another build of it)."""
+    return os.environ.get("ROLA_LIBRARY") or _build.LIB
 
 
 def lib():
     """Load librola.so (building it in-tree first if it is missing or stale)."""
     global _lib
     if _lib is None:
-        _build.ensure_built()
-        L = ctypes.CDLL(_build.LIB)
+        path = library_path()
+        if path == _build.LIB:
+            _build.ensure_built()
+        L = ctypes.CDLL(path)
         P, I32 = ctypes.c_void_p, ctypes.c_int32
         L.rola_abi_version.restype = I32
         L.rola_status_str.restype = ctypes.c_char_p
