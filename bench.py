@@ -47,7 +47,7 @@ def parse():
     ap.add_argument("--workload", default="wan14b_720p")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-baseline-child", action="store_true", help=argparse.SUPPRESS)
-    ap.add_argument("--sample-stride", type=int, default=4,
+    ap.add_argument("--sample-stride", type=int, default=1,
                     help="CPU baseline: every n-th query block of one head")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before timing, run one plain device copy of this many MiB (a known-size "
@@ -177,7 +177,7 @@ def main():
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
         if tr.get("kernel_source_hash") == kernel_source_hash() and tr.get("workload") == w.name:
-            traffic = tr["bytes_per_launch"]
+            traffic = round(tr["bytes_per_launch"]["total"])
     # algorithmic HBM bytes of the streaming pass: read Q, K, V once
     n_tok = w.batch * w.heads * w.n_pad
     pass1_bytes = 3 * n_tok * w.head_dim * 2
