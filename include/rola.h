@@ -102,8 +102,9 @@ const char *rola_status_str(int32_t status);
 int32_t rola_plan(const rola_problem *prob, const rola_config *cfg, rola_plan_info *out);
 
 /*
- * Block selection (pages: "What's New" -- keep "a tiny fraction of query-key
- * blocks"; README inference section -- topk as keep ratio).  Pools Q and K per
+ * Block selection (pages: news article, section "What's New": only a small
+ * share of the query-key blocks survives; README "AlibabaResearch/
+ * SparkDiffusion", inference section: topk is the keep ratio).  Pools Q and K per
  * block, scores every block pair and writes the kept key blocks of every
  * query block to block_idx (int32 [B][H][nb][kb], ascending).  pooled_scores,
  * if not NULL, receives the fp32 score matrix [B][H][nb][nb].
@@ -113,8 +114,9 @@ int32_t rola_select_blocks(const rola_problem *prob, const rola_config *cfg, con
                            void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Sparse branch only (pages: RoLA section -- "block-sparse branch" that keeps
- * the high-energy query-key interactions).  O = O_sparse (accumulate = 0) or
+ * Sparse branch only (pages: section "RoLA: Preserving Global Context at
+ * Extreme Sparsity": a block-sparse softmax branch keeps the high-energy
+ * query-key interactions).  O = O_sparse (accumulate = 0) or
  * O += O_sparse (accumulate = 1), with block_idx as written by
  * rola_select_blocks (ids must be ascending and < nb).
  */
@@ -124,9 +126,11 @@ int32_t rola_sparse_attn(const rola_problem *prob, const rola_config *cfg, const
                          void *stream);
 
 /*
- * Low-rank branch only (pages: RoLA paper title "Rotary-Positioned Low-Rank
- * Linear Attention"; RoLA section -- low-rank linear branch with rotary
- * positions; README sparse-finetune note -- the added proj_q / proj_k).
+ * Low-rank branch only (pages: section "RoLA: Preserving Global Context at
+ * Extreme Sparsity", which names the RoLA paper, rotary-positioned low-rank
+ * linear attention: a linear branch with rotary positions; README
+ * "AlibabaResearch/SparkDiffusion", sparse-finetune section: the added
+ * query and key projections).
  * O = O_lr (accumulate = 0) or O += O_lr (accumulate = 1).
  */
 int32_t rola_lowrank_attn(const rola_problem *prob, const rola_config *cfg, const void *q,

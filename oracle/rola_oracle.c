@@ -15,7 +15,7 @@
  * The keep ratio ``topk`` (README "AlibabaResearch/SparkDiffusion",
  * inference section) is the fraction of key blocks each query block keeps.
  *
- * Readings taken where the pages are silent (each is listed in the design doc):
+ * Readings taken where the pages are silent:
  *  - 64-token blocks in raster (t,h,w) order; block energy is the mean of the
  *    block's valid tokens (the tail block's padding is excluded);
  *  - pooling sums in a fixed binary tree (pairs at distance 32,16,...,1) in
