@@ -26,9 +26,12 @@ sys.path.insert(0, ROOT)
 
 METRIC = "RoLA fwd ms + kept-block TFLOP/s (% MFMA peak), Wan-14B-720P shape, topk 0.03"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-DOMINANT = "attn_sparse_lowrank"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_sparse_lowrank_wan14b_720p_traffic.json")
+
+
+def traffic_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", "attn_sparse_lowrank_%s_traffic.json" % workload)
 
 
 def kernel_source_hash() -> str:
@@ -45,6 +48,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="wan14b_720p")
+    ap.add_argument("--topk", type=float, default=None, help="override the workload's keep ratio")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-baseline-child", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--sample-stride", type=int, default=1,
@@ -67,6 +71,9 @@ def cpu_baseline_child(args):
     from sparse_rank_attention_amd import workloads as W
 
     w = W.WORKLOADS[args.workload]
+    if args.topk is not None:
+        import dataclasses
+        w = dataclasses.replace(w, topk=args.topk)
     q, k, v = W.make_qkv(w, heads=[0], threads=1)
     wq, wk = W.make_proj(w)
     q, k, v = q[0], k[0], v[0]
@@ -93,7 +100,7 @@ def cpu_baseline_child(args):
 def cpu_baseline(args, w):
     env = dict(os.environ, OMP_NUM_THREADS="1")
     cmd = [sys.executable, os.path.abspath(__file__), "--cpu-baseline-child", "--workload", args.workload,
-           "--sample-stride", str(args.sample_stride)]
+           "--sample-stride", str(args.sample_stride)] + (["--topk", repr(args.topk)] if args.topk else [])
     res = subprocess.run(cmd, env=env, capture_output=True, text=True, timeout=600)
     if res.returncode != 0:
         raise RuntimeError("cpu baseline failed: " + res.stderr[-2000:])
@@ -130,6 +137,10 @@ def main():
     from sparse_rank_attention_amd import rola, workloads as W
 
     w = W.WORKLOADS[args.workload]
+    if args.topk is not None:
+        import dataclasses
+        w = dataclasses.replace(w, topk=args.topk)
+    fp8 = w.precision == "fp8"
     print("[bench] generating %s inputs" % w.name, file=sys.stderr, flush=True)
     q, k, v = W.make_qkv(w)
     wq, wk = W.make_proj(w)
@@ -137,7 +148,9 @@ def main():
     qd, kd, vd = dev(q), dev(k), dev(v)
     del q, k, v
     wqd, wkd = torch.from_numpy(wq).cuda(), torch.from_numpy(wk).cuda()
-    cfg = rola.Config(topk=w.topk, rank=w.rank)
+    cfg = rola.Config(topk=w.topk, rank=w.rank, precision=rola.ROLA_PREC_FP8 if fp8 else rola.ROLA_PREC_BF16)
+    dominant = "attn8_sparse_lowrank" if fp8 else "attn_sparse_lowrank"
+    peak = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
     out = torch.empty_like(qd)
     stream = torch.cuda.current_stream()
     if args.copy_calibration_mib > 0:
@@ -170,11 +183,12 @@ def main():
 
     kept = w.kept_block_flop()
     dense = w.dense_equiv_flop()
-    t_attn = kern_ms[DOMINANT] * 1e-3
+    t_attn = kern_ms[dominant] * 1e-3
     achieved = kept / t_attn / 1e12
     traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as f:
+    tfile = traffic_file(w.name)
+    if os.path.exists(tfile) and args.topk is None:
+        with open(tfile) as f:
             tr = json.load(f)
         if tr.get("kernel_source_hash") == kernel_source_hash() and tr.get("workload") == w.name:
             traffic = round(tr["bytes_per_launch"]["total"])
@@ -193,7 +207,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8e4m3" if fp8 else "bf16",
         "data": "synthetic (seeded Wan-shaped smooth field + noise Q/K, N(0,1) V; no weights)",
         "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim,
                    "grid": list(w.grid), "n_tokens": w.n_tokens, "topk": w.topk, "kb": w.kb, "nb": w.nb,
@@ -202,8 +216,8 @@ def main():
         "dense_equiv_tflops": round(dense / (ms * 1e-3) / 1e12, 1),
         "kept_block_tflops": round(kept / (ms * 1e-3) / 1e12, 1),
         "kernel_ms": {k_: round(v_, 4) for k_, v_ in sorted(kern_ms.items())},
-        "roofline": {"kernel": DOMINANT, "bound": "mfma", "achieved": round(achieved, 1),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 1),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic},
     }
     if pass1_ms:

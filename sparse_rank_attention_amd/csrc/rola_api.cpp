@@ -36,6 +36,8 @@ struct Plan {
   int64_t ngroups, list_stride;
   int64_t off_wqT, off_wkT, off_qp, off_kp, off_scores, off_map, off_part, off_st,
       off_z, off_ugroup, off_ucount, off_ulist, total;
+  bool fp8;
+  int64_t off_qsc, off_ksc, off_vsc, off_kv8;  // fp8 only
 };
 
 int32_t make_plan(const rola_problem *p, const rola_config *c, Plan *pl) {
@@ -45,7 +47,6 @@ int32_t make_plan(const rola_problem *p, const rola_config *c, Plan *pl) {
   if (p->head_dim != 64 && p->head_dim != 128) return ROLA_ERR_UNSUPPORTED;
   if (c->rank != 16 && c->rank != 32) return ROLA_ERR_UNSUPPORTED;
   if (c->precision != ROLA_PREC_BF16 && c->precision != ROLA_PREC_FP8) return ROLA_ERR_INVALID_ARG;
-  if (c->precision == ROLA_PREC_FP8) return ROLA_ERR_UNSUPPORTED;
   if (c->out_dtype != ROLA_OUT_BF16 && c->out_dtype != ROLA_OUT_F32) return ROLA_ERR_INVALID_ARG;
   const int D = p->head_dim;
   const int64_t N = (int64_t)p->grid_t * p->grid_h * p->grid_w;
@@ -107,6 +108,14 @@ int32_t make_plan(const rola_problem *p, const rola_config *c, Plan *pl) {
   P.off_ugroup = o; o = align_up(o + P.BH * P.ngroups * P.G * 4);
   P.off_ucount = o; o = align_up(o + P.BH * P.ngroups * 4);
   P.off_ulist = o; o = align_up(o + P.BH * P.ngroups * P.list_stride * 4);
+  P.fp8 = c->precision == ROLA_PREC_FP8;
+  P.off_qsc = P.off_ksc = P.off_vsc = P.off_kv8 = 0;
+  if (P.fp8) {
+    P.off_qsc = o; o = align_up(o + P.BH * nb * 8);
+    P.off_ksc = o; o = align_up(o + P.BH * nb * 4);
+    P.off_vsc = o; o = align_up(o + P.BH * nb * 4);
+    P.off_kv8 = o; o = align_up(o + P.BH * nb * 128LL * D);
+  }
   P.total = o;
   return ROLA_OK;
 }
@@ -208,6 +217,19 @@ int32_t run_select(const Plan &P, uint8_t *ws, float *scores, int32_t *map, hipS
   return timed("topk", st, [&] { rola::launch_topk(scores, map, P.nb, P.kb, P.BH * P.nb, st); });
 }
 
+int32_t run_quant8(const Plan &P, const rola_problem *p, const void *q, const void *k, const void *v,
+                   uint8_t *ws, hipStream_t st) {
+  rola::Quant8Args a;
+  a.q = (const uint16_t *)q; a.k = (const uint16_t *)k; a.v = (const uint16_t *)v;
+  a.stride_b = p->stride_b; a.stride_h = p->stride_h; a.stride_n = p->stride_n;
+  a.heads = P.H; a.nb = P.nb; a.n_tokens = P.N;
+  a.qsc = (float *)(ws + P.off_qsc);
+  a.ksc = (float *)(ws + P.off_ksc);
+  a.vsc = (float *)(ws + P.off_vsc);
+  a.kv8 = ws + P.off_kv8;
+  return timed("quant8", st, [&] { rola::launch_quant8(a, P.D, (int)P.BH, st); });
+}
+
 int32_t run_attn(const Plan &P, const rola_problem *p, const rola_config *c, const void *q,
                  const void *k, const void *v, const int32_t *map, void *out, uint8_t *ws, bool sparse,
                  bool lowrank, bool accum, hipStream_t st) {
@@ -228,6 +250,10 @@ int32_t run_attn(const Plan &P, const rola_problem *p, const rola_config *c, con
   a.st = (const uint16_t *)(ws + P.off_st);
   a.z = (const float *)(ws + P.off_z);
   a.rope = rope_args(P, ws);
+  a.kv8 = ws + P.off_kv8;
+  a.qsc = (const float *)(ws + P.off_qsc);
+  a.ksc = (const float *)(ws + P.off_ksc);
+  a.vsc = (const float *)(ws + P.off_vsc);
   if (sparse) {
     int32_t s = timed("schedule", st, [&] {
       rola::launch_schedule(map, P.nb, P.kb, P.G, (int)P.ngroups, (int)P.list_stride, (int)P.BH,
@@ -243,6 +269,12 @@ int32_t run_attn(const Plan &P, const rola_problem *p, const rola_config *c, con
                             (int32_t *)(ws + P.off_ulist), st);
     });
     if (s != ROLA_OK) return s;
+  }
+  if (sparse && P.fp8) {
+    const char *name8 = lowrank ? "attn8_sparse_lowrank" : "attn8_sparse";
+    return timed(name8, st, [&] {
+      rola::launch_attn8(a, P.D, lowrank, accum != 0, c->out_dtype == ROLA_OUT_F32, st);
+    });
   }
   const char *name = sparse && lowrank ? "attn_sparse_lowrank" : sparse ? "attn_sparse" : "attn_lowrank";
   return timed(name, st, [&] {
@@ -319,6 +351,7 @@ int32_t rola_sparse_attn(const rola_problem *prob, const rola_config *cfg, const
   if (!aligned16(workspace)) return ROLA_ERR_ALIGNMENT;
   hipStream_t st = (hipStream_t)stream;
   uint8_t *ws = (uint8_t *)workspace;
+  if (P.fp8) ROLA_TRY(run_quant8(P, prob, q, k, v, ws, st));
   return run_attn(P, prob, cfg, q, k, v, block_idx, out, ws, true, false, accumulate != 0, st);
 }
 
@@ -360,6 +393,7 @@ int32_t rola_forward(const rola_problem *prob, const rola_config *cfg, const voi
   int32_t *map = block_idx_out ? block_idx_out : (int32_t *)(ws + P.off_map);
   ROLA_TRY(run_setup(P, wq, wk, ws, st));
   ROLA_TRY(run_pass1(P, prob, q, k, v, ws, true, true, st));
+  if (P.fp8) ROLA_TRY(run_quant8(P, prob, q, k, v, ws, st));
   ROLA_TRY(run_reduce(P, ws, st));
   ROLA_TRY(run_select(P, ws, (float *)(ws + P.off_scores), map, st));
   return run_attn(P, prob, cfg, q, k, v, map, out, ws, true, true, false, st);

@@ -43,6 +43,24 @@ struct Pass1Args {
 #endif
 
 
+// fp8 copies of the token tensors (k_quant8): per (batch, head, block)
+// scales and one tile image of e4m3 K and V^T codes per block.
+struct Quant8Args {
+  const uint16_t *q, *k, *v;
+  int64_t stride_b, stride_h, stride_n;
+  int heads, nb;
+  int64_t n_tokens;
+  float *qsc;     // [BH][nb][2]: fl32(absmax/448), fl32(448/absmax) of Q
+  float *ksc;     // [BH][nb]: fl32(absmax/448) of K
+  float *vsc;     // [BH][nb]: fl32(absmax/448) of V
+  uint8_t *kv8;   // [BH][nb][128*D] tile images (K rows, then V^T rows)
+};
+
+// fp8 attention ring depth (16 KB tiles at D=128)
+#ifndef ROLA_ATTN8_S
+#define ROLA_ATTN8_S 6
+#endif
+
 struct AttnArgs {
   const uint16_t *q, *k, *v;
   void *out;
@@ -61,6 +79,9 @@ struct AttnArgs {
   const uint16_t *st;   // bf16 [BH][D][32] (rank permuted)
   const float *z;       // [BH][32]
   RopeArgsHost rope;
+  // fp8 sparse branch only
+  const uint8_t *kv8;   // tile images, see Quant8Args
+  const float *qsc, *ksc, *vsc;
 };
 
 void launch_setup(const SetupArgs &a, hipStream_t st);
@@ -75,5 +96,7 @@ void launch_schedule(const int32_t *map, int nb, int kb, int G, int ngroups, int
 int attn_group_size();
 void launch_attn(const AttnArgs &a, int D, bool sparse, bool lowrank, bool accum, bool outf32,
                  hipStream_t st);
+void launch_quant8(const Quant8Args &a, int D, int bh, hipStream_t st);
+void launch_attn8(const AttnArgs &a, int D, bool lowrank, bool accum, bool outf32, hipStream_t st);
 
 }  // namespace rola

@@ -43,6 +43,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 #define LDS_AS __attribute__((address_space(3)))
 #define GLOBAL_AS __attribute__((address_space(1)))
@@ -143,6 +144,20 @@ static __device__ __forceinline__ void wait_tiles_in_flight(int tiles) {
   if (S >= 4 && tiles >= 2) wait_vmcnt<(S >= 4 ? 4 * OPS : 0)>();
   else if (S >= 3 && tiles >= 1) wait_vmcnt<(S >= 3 ? 2 * OPS : 0)>();
   else wait_vmcnt<0>();
+}
+
+// wait until at most `tiles` (<= T) later tiles of PER DMA ops each are outstanding
+template <int PER, int T>
+static __device__ __forceinline__ void wait_tiles(int tiles) {
+  if constexpr (T > 0) {
+    if (tiles >= T) {
+      wait_vmcnt<T * PER>();
+      return;
+    }
+    wait_tiles<PER, T - 1>(tiles);
+  } else {
+    wait_vmcnt<0>();
+  }
 }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -599,6 +614,98 @@ __global__ __launch_bounds__(64 * kUnionWaves) void k_union(const int32_t *__res
   if (lane == 63) ucount[gidx] = incl;
 }
 
+// Epilogue shared by the bf16 and fp8 attention kernels: low-rank apply
+// O^T += St a / (a^T z) with a = phi(Wq^T R(q)) (Q in registers as the
+// bf16 B operand), then the write of query row n (bf16 or fp32, optional
+// accumulate; rows >= N written as zero).
+template <int D, bool LOWRANK, bool ACCUM, bool OUTF32>
+static __device__ __forceinline__ void attn_finish(const AttnArgs &args, const bf16x8 *qreg,
+                                                   f32x16 *oacc, int64_t n, int64_t base, int bh,
+                                                   int lane) {
+  constexpr int NS = D / 16;
+  constexpr int DT = D / 32;
+  const int g = lane >> 5;
+  if (LOWRANK) {
+    // a^T = Wq^T R(q): A = Wq^T (rows r), B = rotated Q (cols query)
+    int pt, ph, pw;  // padded rows take the last valid position (they are written as 0)
+    token_pos(n < args.n_tokens ? n : args.n_tokens - 1, args.rope, pt, ph, pw);
+    f32x16 aacc = f32x16{};
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      float freq[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) freq[p] = rope_freq(16 * s + 8 * g + 2 * p, args.rope);
+      const bf16x8 qr = rope8(qreg[s], 16 * s + 8 * g, pt, ph, pw, freq, args.rope);
+      const bf16x8 wa = *(const bf16x8 *)(args.wqT + (lane & 31) * D + 16 * s + 8 * g);
+      aacc = mfma_bf16(wa, qr, aacc);
+    }
+    const float *zb = args.z + (int64_t)bh * 32;
+    float den = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 8 * (i >> 2) + 4 * g + (i & 3);
+      const float a = r < args.rank ? phi(aacc[i]) : 0.0f;
+      aacc[i] = a;
+      den += a * zb[r];
+    }
+    den += shfl_xor32(den);
+    const float inv_den = 1.0f / den;
+    bf16x8 aop[2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) aop[i >> 3][i & 7] = (__bf16)(aacc[i] * inv_den);
+    const uint16_t *stb = args.st + (int64_t)bh * D * 32;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int d = 32 * dt + (lane & 31);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const bf16x8 sa = *(const bf16x8 *)(stb + d * 32 + 16 * s + 8 * g);
+        oacc[dt] = mfma_bf16(sa, aop[s], oacc[dt]);
+      }
+    }
+  }
+
+  // ---- write O row n: lane holds dims 32*dt + 8*q4 + 4*g + 0..3
+  const bool valid = n < args.n_tokens;
+  if (OUTF32) {
+    float *orow = (float *)args.out + base + n * args.stride_n;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        float *p = orow + 32 * dt + 8 * q4 + 4 * g;
+        f32x4 v = {oacc[dt][4 * q4], oacc[dt][4 * q4 + 1], oacc[dt][4 * q4 + 2], oacc[dt][4 * q4 + 3]};
+        if (ACCUM) v += *(const f32x4 *)p;
+        if (!valid) v = f32x4{0.f, 0.f, 0.f, 0.f};
+        *(f32x4 *)p = v;
+      }
+    }
+  } else {
+    uint16_t *orow = (uint16_t *)args.out + base + n * args.stride_n;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        uint16_t *p = orow + 32 * dt + 8 * q4 + 4 * g;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = oacc[dt][4 * q4 + e];
+        if (ACCUM) {
+          const uint2 old = *(const uint2 *)p;
+          v[0] += bflo(old.x); v[1] += bfhi(old.x);
+          v[2] += bflo(old.y); v[3] += bfhi(old.y);
+        }
+        uint2 o;
+        const __bf16 b0 = (__bf16)v[0], b1 = (__bf16)v[1], b2 = (__bf16)v[2], b3 = (__bf16)v[3];
+        o.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+        o.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
+        if (!valid) o = make_uint2(0u, 0u);
+        *(uint2 *)p = o;
+      }
+    }
+  }
+}
+
 // ----------------------------------------------------------------- k_attn
 // One workgroup per group of G query blocks of one (batch, head); waves
 // 2m and 2m+1 own query rows 0-31 and 32-63 of member m, one query per lane
@@ -808,86 +915,376 @@ __global__ __launch_bounds__(128 * G) void k_attn(AttnArgs args) {
     for (int dt = 0; dt < DT; ++dt) oacc[dt] *= inv_l;
   }
   if (!active) return;
+  attn_finish<D, LOWRANK, ACCUM, OUTF32>(args, qreg, oacc, n, base, bh, lane);
+}
 
-  if (LOWRANK) {
-    // a^T = Wq^T R(q): A = Wq^T (rows r), B = rotated Q (cols query)
-    int pt, ph, pw;  // padded rows take the last valid position (they are written as 0)
-    token_pos(n < args.n_tokens ? n : args.n_tokens - 1, args.rope, pt, ph, pw);
-    f32x16 aacc = f32x16{};
+// ---------------------------------------------------------------- fp8 path
+// e4m3 codes: round to nearest even, saturating at +-448
+// (v_cvt_pk_fp8_f32; `hi` selects the upper 16 bits of `old`).
+template <bool HI>
+static __device__ __forceinline__ int cvt_fp8x2(float a, float b, int old) {
+  return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
+}
+
+// v_mfma_f32_32x32x64_f8f6f4 with both operands e4m3 and no block scales.
+// Lane l holds 32 codes (8 dwords) of row (A) / column (B) l%32; A and B
+// bytes with the same lane half and byte index meet at the same k.
+static __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// Tile image of one 64-token block (bytes; 128*D per block):
+//  K part, [64 keys][D]: dim d of a key sits at position
+//    p = 64*(d/64) + 32*((d%16)/8) + 8*((d%64)/16) + d%8,
+//  so that each MFMA lane half reads the 32 dims its Q operand holds (the
+//  bf16 Q registers, 16 dims per 16-dim step, 8 per lane half) as two
+//  contiguous 16-byte chunks; chunk c of key row r is stored at
+//  c ^ ((r / (256/D)) & (D/16 - 1)), conflict-free for 16-lane reads.
+//  V^T part, [D][64 keys]: key k sits at position 32*((k%8)/4) + e with
+//    e = 4*((k%32)/8) + k%4 (+16 for k >= 32),
+//  the order in which a lane half holds S^T accumulator rows (keys), so P^T
+//  needs no shuffles; chunk c of row d is stored at c ^ ((d/4) & 3).
+template <int D>
+static __device__ __forceinline__ int img_k_off(int r, int d) {
+  const int rem = d & 63;
+  const int p = (d & ~63) + 32 * ((rem & 15) >> 3) + 8 * (rem >> 4) + (rem & 7);
+  const int f = (r / (256 / D)) & (D / 16 - 1);
+  return r * D + ((((p >> 4) ^ f)) << 4) + (p & 15);
+}
+static __device__ __forceinline__ int img_v_pos(int k) {
+  const int g = (k & 7) >> 2;
+  const int e = 4 * ((k & 31) >> 3) + (k & 3) + (k >= 32 ? 16 : 0);
+  return 32 * g + e;
+}
+static __device__ __forceinline__ int img_v_off(int d, int p) {
+  return d * 64 + ((((p >> 4) ^ ((d >> 2) & 3))) << 4) + (p & 15);
+}
+
+// ---------------------------------------------------------------- k_quant8
+// Per (batch, head, 64-token block): absmax of Q, K and V over the valid
+// tokens; scale = fl32(absmax/448), inv = fl32(448/absmax) (1 and 1 for an
+// all-zero block); codes = e4m3(fl32(x * inv)), padded rows 0.  Q gets its
+// scales only (the attention kernel quantises the rows it holds); K and V
+// codes are written as the block's tile image.  Grid (nb, B*H), 256
+// threads: thread t holds dims [D/4*(t%4), +D/4) of token t/4.
+template <int D>
+__global__ __launch_bounds__(256) void k_quant8(Quant8Args a) {
+  constexpr int PER = D / 4;
+  __shared__ __attribute__((aligned(16))) uint8_t img[128 * D];
+  __shared__ float red[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = blockIdx.x, bh = blockIdx.y;
+  const int b = bh / a.heads, h = bh % a.heads;
+  const int64_t base = (int64_t)b * a.stride_b + (int64_t)h * a.stride_h;
+  const int r = tid >> 2, part = tid & 3;
+  const int64_t n = (int64_t)c * 64 + r;
+  const bool valid = n < a.n_tokens;
+  const int64_t roff = base + (valid ? n : 0) * a.stride_n + part * PER;
+
+  auto load = [&](const uint16_t *X, float *x) {
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      float freq[4];
+    for (int i = 0; i < PER; i += 8) {
+      const u32x4 w = *(const u32x4 *)(X + roff + i);
 #pragma unroll
-      for (int p = 0; p < 4; ++p) freq[p] = rope_freq(16 * s + 8 * g + 2 * p, args.rope);
-      const bf16x8 qr = rope8(qreg[s], 16 * s + 8 * g, pt, ph, pw, freq, args.rope);
-      const bf16x8 wa = *(const bf16x8 *)(args.wqT + (lane & 31) * D + 16 * s + 8 * g);
-      aacc = mfma_bf16(wa, qr, aacc);
-    }
-    const float *zb = args.z + (int64_t)bh * 32;
-    float den = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = 8 * (i >> 2) + 4 * g + (i & 3);
-      const float a = r < args.rank ? phi(aacc[i]) : 0.0f;
-      aacc[i] = a;
-      den += a * zb[r];
-    }
-    den += shfl_xor32(den);
-    const float inv_den = 1.0f / den;
-    bf16x8 aop[2];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) aop[i >> 3][i & 7] = (__bf16)(aacc[i] * inv_den);
-    const uint16_t *stb = args.st + (int64_t)bh * D * 32;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int d = 32 * dt + (lane & 31);
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const bf16x8 sa = *(const bf16x8 *)(stb + d * 32 + 16 * s + 8 * g);
-        oacc[dt] = mfma_bf16(sa, aop[s], oacc[dt]);
+      for (int e = 0; e < 4; ++e) {
+        x[i + 2 * e] = valid ? bflo(w[e]) : 0.0f;
+        x[i + 2 * e + 1] = valid ? bfhi(w[e]) : 0.0f;
       }
+    }
+  };
+  auto block_absmax = [&](const float *x) -> float {
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) m = fmaxf(m, fabsf(x[i]));
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    if (lane == 0) red[wave] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
+    return m;
+  };
+  const int64_t sidx = (int64_t)bh * a.nb + c;
+  float x[PER];
+
+  load(a.q, x);
+  {
+    const float m = block_absmax(x);
+    if (tid == 0) {
+      a.qsc[2 * sidx] = m > 0.0f ? __fdiv_rn(m, 448.0f) : 1.0f;
+      a.qsc[2 * sidx + 1] = m > 0.0f ? __fdiv_rn(448.0f, m) : 1.0f;
     }
   }
-
-  // ---- write O row n: lane holds dims 32*dt + 8*q4 + 4*g + 0..3
-  const bool valid = n < args.n_tokens;
-  if (OUTF32) {
-    float *orow = (float *)args.out + base + n * args.stride_n;
+  // K: codes of 8 consecutive dims are 8 consecutive image bytes
+  load(a.k, x);
+  {
+    const float m = block_absmax(x);
+    const float inv = m > 0.0f ? __fdiv_rn(448.0f, m) : 1.0f;
+    if (tid == 0) a.ksc[sidx] = m > 0.0f ? __fdiv_rn(m, 448.0f) : 1.0f;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        float *p = orow + 32 * dt + 8 * q4 + 4 * g;
-        f32x4 v = {oacc[dt][4 * q4], oacc[dt][4 * q4 + 1], oacc[dt][4 * q4 + 2], oacc[dt][4 * q4 + 3]};
-        if (ACCUM) v += *(const f32x4 *)p;
-        if (!valid) v = f32x4{0.f, 0.f, 0.f, 0.f};
-        *(f32x4 *)p = v;
-      }
+    for (int i = 0; i < PER; i += 8) {
+      int w0 = cvt_fp8x2<false>(x[i] * inv, x[i + 1] * inv, 0);
+      w0 = cvt_fp8x2<true>(x[i + 2] * inv, x[i + 3] * inv, w0);
+      int w1 = cvt_fp8x2<false>(x[i + 4] * inv, x[i + 5] * inv, 0);
+      w1 = cvt_fp8x2<true>(x[i + 6] * inv, x[i + 7] * inv, w1);
+      *(uint2 *)(img + img_k_off<D>(r, part * PER + i)) = make_uint2((uint32_t)w0, (uint32_t)w1);
     }
-  } else {
-    uint16_t *orow = (uint16_t *)args.out + base + n * args.stride_n;
+  }
+  // V: transposed, one byte per code
+  load(a.v, x);
+  {
+    const float m = block_absmax(x);
+    const float inv = m > 0.0f ? __fdiv_rn(448.0f, m) : 1.0f;
+    if (tid == 0) a.vsc[sidx] = m > 0.0f ? __fdiv_rn(m, 448.0f) : 1.0f;
+    uint8_t *vimg = img + 64 * D;
+    const int p = img_v_pos(r);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
+    for (int i = 0; i < PER; i += 2) {
+      const int w = cvt_fp8x2<false>(x[i] * inv, x[i + 1] * inv, 0);
+      vimg[img_v_off(part * PER + i, p)] = (uint8_t)(w & 0xff);
+      vimg[img_v_off(part * PER + i + 1, p)] = (uint8_t)((w >> 8) & 0xff);
+    }
+  }
+  __syncthreads();
+  u32x4 *dst = (u32x4 *)(a.kv8 + sidx * (128 * D));
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        uint16_t *p = orow + 32 * dt + 8 * q4 + 4 * g;
-        float v[4];
+  for (int i = tid; i < 8 * D; i += 256) dst[i] = *(const u32x4 *)(img + 16 * i);
+}
+
+// ------------------------------------------------------------------ k_attn8
+// The sparse branch with e4m3 operands on v_mfma_f32_32x32x64_f8f6f4: the
+// workgroup shape, group walk, LDS ring and lazy softmax reference follow
+// k_attn; a tile is the block's 128*D-byte image from k_quant8 (one
+// contiguous copy).  Each wave quantises its Q rows in registers with the
+// query block's inv scale.  Per listed key block j (constants staged in LDS
+// with the list):
+//   logits (base 2)  t = acc * (sq * sk_j * scale * log2 e) - m_ref,
+//   weights          P' = 2^(t + u_j) with u_j = 8 + log2(sv_j / sigma),
+// sigma the largest V scale on the group's list, so P' <= 2^8 stays inside
+// e4m3 range while P' * code_v carries the V scale (P' enters the PV product
+// as the sum of two e4m3 parts); the row sum adds 2^-u_j * sum(P').  m_ref is the integer ceiling of the running max (moved,
+// with an exact power-of-two rescale, whenever a tile max exceeds it).
+// Finally O = O' * sigma * 2^-8 / l.
+template <int D, int G, int S, bool LOWRANK, bool ACCUM, bool OUTF32>
+__global__ __launch_bounds__(128 * G) void k_attn8(AttnArgs args) {
+  constexpr int NS = D / 16;
+  constexpr int DT = D / 32;
+  constexpr int K8 = D / 64;            // fp8 k-steps over head_dim
+  constexpr int NT = 128 * G;
+  constexpr int TB = 128 * D;           // bytes per tile image
+  constexpr int OPS = TB / 16 / NT;     // DMA ops per thread per tile
+  static_assert(OPS >= 1 && (TB / 16) % NT == 0, "tile split");
+  static_assert(S >= 2 && S * OPS <= 63, "ring depth");
+  constexpr int LMAX = 2048;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[S * TB];
+  __shared__ int32_t slist[LMAX];
+  __shared__ float sck[LMAX], sku[LMAX], skw[LMAX];
+  __shared__ float sred[2 * G];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, g = lane >> 5;
+  const int member = wave >> 1, half = wave & 1;
+  const int64_t L = blockIdx.x;
+  const int64_t sidx = L / 8;
+  const int64_t bh64 = sidx / args.groups_per_xcd;
+  const int64_t group = (L % 8) * args.groups_per_xcd + sidx % args.groups_per_xcd;
+  if (bh64 >= args.bh_count || group >= args.ngroups) return;
+  const int bh = (int)bh64;
+  const int64_t gidx = (int64_t)bh * args.ngroups + group;
+  const int qb = args.ugroup[gidx * G + member];
+  const bool active = qb >= 0;
+  const int b = bh / args.heads, h = bh % args.heads;
+  const int64_t base = (int64_t)b * args.stride_b + (int64_t)h * args.stride_h;
+  const int64_t n = (int64_t)(active ? qb : 0) * 64 + 32 * half + (lane & 31);
+
+  const uint16_t *qrow = args.q + base + n * args.stride_n;
+  bf16x8 qreg[NS];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = oacc[dt][4 * q4 + e];
-        if (ACCUM) {
-          const uint2 old = *(const uint2 *)p;
-          v[0] += bflo(old.x); v[1] += bfhi(old.x);
-          v[2] += bflo(old.y); v[3] += bfhi(old.y);
+  for (int s = 0; s < NS; ++s) qreg[s] = *(const bf16x8 *)(qrow + 16 * s + 8 * g);
+  const int64_t qs_idx = (int64_t)bh * args.nb + (active ? qb : 0);
+  const float sq = args.qsc[2 * qs_idx], iq = args.qsc[2 * qs_idx + 1];
+  const int32_t *list = args.ulist + gidx * args.list_stride;
+  const int U = args.ucount[gidx];
+  const float *ksc = args.ksc + (int64_t)bh * args.nb;
+  const float *vsc = args.vsc + (int64_t)bh * args.nb;
+  // sigma: the largest V scale on the list
+  float vmax = 0.0f;
+  for (int t = tid; t < U; t += NT) vmax = fmaxf(vmax, vsc[list[t] & 0xffff]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, o, 64));
+  if (lane == 0) sred[wave] = vmax;
+  __syncthreads();
+  float sigma = sred[0];
+#pragma unroll
+  for (int w = 1; w < 2 * G; ++w) sigma = fmaxf(sigma, sred[w]);
+  const float log2_sigma = __log2f(sigma);
+  const float c_scale = args.scale_log2e;
+  auto consts = [&](int j, float &ck, float &ku, float &kw) {
+    ck = ksc[j] * c_scale;
+    // a V block far below sigma (tiny or denormal absmax) keeps a finite
+    // weight 2^-ku; its codes times sigma-relative weights are negligible
+    ku = fmaxf(8.0f + (__log2f(vsc[j]) - log2_sigma), -100.0f);
+    kw = fast_exp2(-ku);
+  };
+  for (int t = tid; t < min(U, LMAX); t += NT) {
+    const int ent = list[t];
+    slist[t] = ent;
+    consts(ent & 0xffff, sck[t], sku[t], skw[t]);
+  }
+  // Q codes: byte e of k-step s holds dim 64s + 16(e/8) + 8g + e%8, i.e.
+  // element e%8 of qreg[4s + e/8]
+  i32x8 q8[K8];
+#pragma unroll
+  for (int s8 = 0; s8 < K8; ++s8) {
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const bf16x8 &src = qreg[4 * s8 + (w >> 1)];
+      const int e0 = 4 * (w & 1);
+      int v = cvt_fp8x2<false>((float)src[e0] * iq, (float)src[e0 + 1] * iq, 0);
+      v = cvt_fp8x2<true>((float)src[e0 + 2] * iq, (float)src[e0 + 3] * iq, v);
+      q8[s8][w] = v;
+    }
+  }
+  wait_vmcnt<0>();  // Q, scales and the list in registers before the tile copies start
+  __syncthreads();
+
+  f32x16 oacc[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i) oacc[i] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  // per-lane LDS byte offsets of the MFMA operands inside a tile image
+  int koff[K8][2], voff[DT][2];
+#pragma unroll
+  for (int s8 = 0; s8 < K8; ++s8) {
+    const int r = lane & 31;
+    const int f = (r / (256 / D)) & (D / 16 - 1);
+    const int c0 = 4 * s8 + 2 * g;
+    koff[s8][0] = r * D + ((c0 ^ f) << 4);
+    koff[s8][1] = r * D + (((c0 + 1) ^ f) << 4);
+  }
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    const int d = 32 * dt + (lane & 31);
+    voff[dt][0] = 64 * D + d * 64 + (((2 * g) ^ ((d >> 2) & 3)) << 4);
+    voff[dt][1] = 64 * D + d * 64 + (((2 * g + 1) ^ ((d >> 2) & 3)) << 4);
+  }
+  auto ld16 = [](const uint8_t *p) -> u32x4 { return *(const u32x4 *)p; };
+  auto cat = [](u32x4 a, u32x4 b) -> i32x8 {
+    return i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+  };
+  const uint8_t *img = args.kv8 + (int64_t)bh * args.nb * TB;
+
+  auto main_loop = [&](auto lds_tag) {
+    constexpr bool FROM_LDS = decltype(lds_tag)::value;
+    auto issue = [&](int t) {
+      int j;
+      if constexpr (FROM_LDS) j = slist[t] & 0xffff;
+      else j = list[t] & 0xffff;
+      const uint8_t *src = img + (int64_t)j * TB;
+      uint8_t *slot = ring + (t % S) * TB;
+#pragma unroll
+      for (int o = 0; o < OPS; ++o) lds_dma16(src + (o * NT + tid) * 16, slot + (o * NT + wave * 64) * 16);
+    };
+#pragma unroll
+    for (int t = 0; t < S - 1; ++t)
+      if (t < U) issue(t);
+    for (int t = 0; t < U; ++t) {
+      wait_tiles<OPS, S - 2>(min(S - 2, U - 1 - t));
+      barrier_lds();
+      int ent;
+      float ck, ku, kw;
+      if constexpr (FROM_LDS) {
+        ent = slist[t];
+        ck = sck[t]; ku = sku[t]; kw = skw[t];
+      } else {
+        ent = list[t];
+        consts(ent & 0xffff, ck, ku, kw);
+      }
+      if (!active || !((ent >> (16 + member)) & 1)) {
+        if (t + S - 1 < U) issue(t + S - 1);
+        continue;
+      }
+      const int j = ent & 0xffff;
+      const uint8_t *tile = ring + (t % S) * TB;
+      f32x16 sacc0 = f32x16{}, sacc1 = f32x16{};
+#pragma unroll
+      for (int s8 = 0; s8 < K8; ++s8) {
+        sacc0 = mfma_fp8(cat(ld16(tile + koff[s8][0]), ld16(tile + koff[s8][1])), q8[s8], sacc0);
+        sacc1 = mfma_fp8(cat(ld16(tile + koff[s8][0] + 32 * D), ld16(tile + koff[s8][1] + 32 * D)),
+                         q8[s8], sacc1);
+      }
+      if ((int64_t)(j + 1) * 64 > args.n_tokens) {
+        const int64_t nrel = args.n_tokens - (int64_t)j * 64;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = 8 * (i >> 2) + 4 * g + (i & 3);
+          if (key >= nrel) sacc0[i] = -INFINITY;
+          if (key + 32 >= nrel) sacc1[i] = -INFINITY;
         }
-        uint2 o;
-        const __bf16 b0 = (__bf16)v[0], b1 = (__bf16)v[1], b2 = (__bf16)v[2], b3 = (__bf16)v[3];
-        o.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
-        o.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
-        if (!valid) o = make_uint2(0u, 0u);
-        *(uint2 *)p = o;
       }
+      const float c = sq * ck;
+      float mx0 = -INFINITY, mx1 = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx0 = fmaxf(mx0, sacc0[i]);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx1 = fmaxf(mx1, sacc1[i]);
+      const float mx = pair_max32(fmaxf(mx0, mx1)) * c;
+      const bool grow = mx > m_run;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float m_new = grow ? ceilf(mx) : m_run;
+        const float alpha = fast_exp2(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+      }
+      // P' in two e4m3 parts, hi = e4m3(P') and lo = e4m3(P' - hi): a single
+      // 3-bit-mantissa rounding of the weights would cost far more than the
+      // output tolerance; hi + lo keeps them to about 2^-8 relative.
+      const float off = ku - m_run;
+      float psum = 0.0f;
+      i32x8 phi8, plo8;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        const f32x16 &src = (w < 4) ? sacc0 : sacc1;
+        const int e = 4 * (w & 3);
+        const float p0 = fast_exp2(__builtin_fmaf(src[e], c, off));
+        const float p1 = fast_exp2(__builtin_fmaf(src[e + 1], c, off));
+        const float p2 = fast_exp2(__builtin_fmaf(src[e + 2], c, off));
+        const float p3 = fast_exp2(__builtin_fmaf(src[e + 3], c, off));
+        psum += (p0 + p1) + (p2 + p3);
+        const int hi = cvt_fp8x2<true>(p2, p3, cvt_fp8x2<false>(p0, p1, 0));
+        const f32x2 h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
+        const f32x2 h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+        phi8[w] = hi;
+        plo8[w] = cvt_fp8x2<true>(p2 - h23[0], p3 - h23[1], cvt_fp8x2<false>(p0 - h01[0], p1 - h01[1], 0));
+      }
+      l_run = __builtin_fmaf(psum, kw, l_run);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const i32x8 va = cat(ld16(tile + voff[dt][0]), ld16(tile + voff[dt][1]));
+        oacc[dt] = mfma_fp8(va, phi8, oacc[dt]);
+        oacc[dt] = mfma_fp8(va, plo8, oacc[dt]);
+      }
+      if (t + S - 1 < U) issue(t + S - 1);
     }
+  };
+  if (U <= LMAX) main_loop(std::integral_constant<bool, true>{});
+  else main_loop(std::integral_constant<bool, false>{});
+  const float l_tot = pair_sum32(l_run);
+  const float fin = l_tot > 0.0f ? sigma * 0.00390625f / l_tot : 0.0f;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) oacc[dt] *= fin;
+  if (!active) return;
+  // the bf16 Q rows are loaded again for the low-rank apply rather than held
+  // in registers through the loop
+  bf16x8 qlr[NS];
+  if (LOWRANK) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) qlr[s] = *(const bf16x8 *)(qrow + 16 * s + 8 * g);
   }
+  attn_finish<D, LOWRANK, ACCUM, OUTF32>(args, qlr, oacc, n, base, bh, lane);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -976,6 +1373,34 @@ void launch_attn(const AttnArgs &a, int D, bool sparse, bool lowrank, bool accum
                  hipStream_t st) {
   if (D == 64) attn_d<64, ROLA_ATTN_G, ROLA_ATTN_S>(a, sparse, lowrank, accum, outf32, st);
   else attn_d<128, ROLA_ATTN_G, ROLA_ATTN_S>(a, sparse, lowrank, accum, outf32, st);
+}
+
+void launch_quant8(const Quant8Args &a, int D, int bh, hipStream_t st) {
+  dim3 grid(a.nb, bh), block(256);
+  if (D == 64) hipLaunchKernelGGL(k_quant8<64>, grid, block, 0, st, a);
+  else hipLaunchKernelGGL(k_quant8<128>, grid, block, 0, st, a);
+}
+
+template <int D, int G, int S, bool LOWRANK>
+static void attn8_d2(const AttnArgs &a, bool accum, bool outf32, hipStream_t st) {
+  dim3 grid((unsigned)(8 * a.groups_per_xcd * a.bh_count)), block(128 * G);
+  if (accum) {
+    if (outf32) hipLaunchKernelGGL((k_attn8<D, G, S, LOWRANK, true, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_attn8<D, G, S, LOWRANK, true, false>), grid, block, 0, st, a);
+  } else {
+    if (outf32) hipLaunchKernelGGL((k_attn8<D, G, S, LOWRANK, false, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_attn8<D, G, S, LOWRANK, false, false>), grid, block, 0, st, a);
+  }
+}
+
+void launch_attn8(const AttnArgs &a, int D, bool lowrank, bool accum, bool outf32, hipStream_t st) {
+  if (D == 64) {
+    if (lowrank) attn8_d2<64, ROLA_ATTN_G, ROLA_ATTN8_S, true>(a, accum, outf32, st);
+    else attn8_d2<64, ROLA_ATTN_G, ROLA_ATTN8_S, false>(a, accum, outf32, st);
+  } else {
+    if (lowrank) attn8_d2<128, ROLA_ATTN_G, ROLA_ATTN8_S, true>(a, accum, outf32, st);
+    else attn8_d2<128, ROLA_ATTN_G, ROLA_ATTN8_S, false>(a, accum, outf32, st);
+  }
 }
 
 }  // namespace rola

@@ -107,3 +107,14 @@ def test_entry_points_validate_before_launch():
 def test_timing_read_without_launches_is_empty():
     assert rola.lib().rola_timing_read(None, 4) == -1
     assert rola.timing_read() == {}
+
+
+def test_plan_fp8_adds_code_images_to_workspace():
+    """fp8 mode keeps one 128*D-byte e4m3 tile image per (batch, head, block) plus three scales."""
+    prob = _prob(grid=(21, 45, 80))
+    st, b = _plan(prob, rola.Config(topk=0.03))
+    st8, f = _plan(prob, rola.Config(topk=0.03, precision=rola.ROLA_PREC_FP8))
+    assert st == st8 == 0
+    bh_nb = prob.batch * prob.heads * f.nb
+    assert f.workspace_bytes - b.workspace_bytes >= bh_nb * (128 * prob.head_dim + 16)
+    assert f.workspace_bytes - b.workspace_bytes <= bh_nb * (128 * prob.head_dim + 16) + 4 * 256
