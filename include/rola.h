@@ -60,7 +60,8 @@ extern "C" {
 typedef enum rola_status {
   ROLA_OK = 0,
   ROLA_ERR_INVALID_ARG = 1, /* null pointer, bad size, topk outside (0,1], ... */
-  ROLA_ERR_UNSUPPORTED = 2, /* D not in {64,128}, r not in {16,32}, nb too large */
+  ROLA_ERR_UNSUPPORTED = 2, /* D not in {64,128}, r not in {16,32}, nb too large,
+                               stride_n above 2^24 elements */
   ROLA_ERR_ALIGNMENT = 3,   /* pointer or row stride not 16-byte aligned */
   ROLA_ERR_WORKSPACE = 4,   /* workspace null or smaller than rola_plan's size */
   ROLA_ERR_DEVICE = 5       /* a HIP launch reported an error */

@@ -57,6 +57,8 @@ int32_t make_plan(const rola_problem *p, const rola_config *c, Plan *pl) {
   if (p->stride_n < D || p->stride_n % 8 || p->stride_h % 8 || p->stride_b % 8 ||
       p->stride_h < 0 || p->stride_b < 0)
     return ROLA_ERR_ALIGNMENT;
+  // byte offsets inside one 64-token block are 32-bit in the tile copies
+  if (p->stride_n > (1LL << 24)) return ROLA_ERR_UNSUPPORTED;
   int kb;
   if (c->kb_override > 0) {
     if (c->kb_override > nb) return ROLA_ERR_INVALID_ARG;

@@ -15,6 +15,7 @@
 //   k_scores       pooled block scores, sequential fp32 fma chain (VALU)
 //   k_topk         per-row radix select of the kept key blocks (one wave/row)
 //   k_order        per head: query blocks ordered by similarity of their maps
+//   k_group        greedy grouping of similar maps inside windows of that order
 //   k_union        per group of query blocks: merged list of kept key blocks
 //   k_attn         block-sparse flash attention on bf16 MFMA with online
 //                  softmax in fp32, fused low-rank apply and merge
@@ -36,6 +37,7 @@
 
 #include <type_traits>
 
+#include "../../include/rola.h"
 #include "rola_internal.h"
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -107,6 +109,27 @@ static __device__ __forceinline__ void lds_dma16(const void *gsrc, void *lds_dst
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "s"(base), "v"(gsrc)
+      : "memory");
+}
+
+// The same copy from a wave-uniform base address (held in an SGPR pair)
+// plus a 32-bit per-lane byte offset (the global_load_lds saddr form): no
+// per-lane 64-bit address arithmetic.
+static __device__ __forceinline__ void lds_dma16_s(const void *base_ptr, uint32_t voff, void *lds_dst) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(LDS_AS void *)lds_dst);
+  const uint64_t b64 = (uint64_t)(uintptr_t)base_ptr;
+  // readfirstlane returns int: widen through uint32_t (no sign extension)
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b64);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b64 >> 32));
+  const void *sbase = (const void *)(uintptr_t)(((uint64_t)hi << 32) | (uint64_t)lo);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(m), "v"(voff), "s"(sbase)
       : "memory");
 }
 
@@ -560,6 +583,121 @@ __global__ __launch_bounds__(1024) void k_order(const int32_t *__restrict__ map,
   for (int p = nb + threadIdx.x; p < ngroups * G; p += blockDim.x) ug[p] = -1;
 }
 
+// ---------------------------------------------------------------- k_group
+// Refines the grouping inside windows of kGroupWin consecutive positions of
+// the k_order sequence (one wave per window, windows independent): groups
+// are formed greedily, seeded by the first unassigned query block in window
+// order, each next member being the unassigned block whose map shares the
+// most key blocks with the group's union so far (ties to the earlier one).
+// Fewer distinct key blocks per group means fewer K/V tiles to stream and
+// fewer waves idle on a tile.  Windows are multiples of G, so group
+// boundaries stay aligned; padding entries (-1) stay at the end.  Used for
+// kb <= kGroupMaxKb (maps cached in LDS as 16-bit ids).
+constexpr int kGroupWin = 64;
+constexpr int kGroupMaxKb = 64;
+
+// One wave per window, window position c = lane.  Scores (key blocks shared
+// with the current group's union) are kept up to date incrementally: an
+// inverted index in LDS gives, per key block, the 64-bit mask of window
+// positions whose map holds it, and each key block a new member brings into
+// the union adds one to the score of every position in its mask.  Liveness
+// is a 64-bit ballot held by every lane.  Dynamic LDS: nb masks (8 B each)
+// and the union bitset.
+__global__ __launch_bounds__(64) void k_group(const int32_t *__restrict__ map, int nb, int kb, int G,
+                                              int ngroups, int32_t *__restrict__ ugroup) {
+  extern __shared__ uint64_t gsm[];
+  uint64_t *inv = gsm;                                  // [nb]
+  uint32_t *inu = (uint32_t *)(gsm + nb);               // [ceil(nb/32)]
+  __shared__ uint16_t cmap[kGroupWin * kGroupMaxKb];    // maps of the window positions
+  const int lane = threadIdx.x;
+  const int bh = blockIdx.y;
+  const int total = ngroups * G;
+  const int w0 = blockIdx.x * kGroupWin;
+  if (w0 >= total) return;
+  const int wn = min(kGroupWin, total - w0);
+  int32_t *ug = ugroup + (int64_t)bh * total + w0;
+  const int32_t *mb = map + (int64_t)bh * nb * kb;
+  const int nwords = (nb + 31) / 32;
+  const int qb = lane < wn ? ug[lane] : -1;
+  for (int j = lane; j < nb; j += 64) inv[j] = 0ull;
+  for (int w = lane; w < nwords; w += 64) inu[w] = 0u;
+  __syncthreads();
+  // index the window: position c sets bit c of inv[j] for each j it keeps
+  // (map entries e = c*kb + t spread over the lanes, four loads in flight)
+  const int nent = wn * kb;
+  for (int e0 = 0; e0 < nent; e0 += 256) {
+    int jv[4], cv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = e0 + 64 * u + lane;
+      const int c = e < nent ? e / kb : 0;
+      const int qc = __shfl(qb, c, 64);
+      cv[u] = (e < nent && qc >= 0) ? c : -1;
+      jv[u] = cv[u] >= 0 ? mb[(int64_t)qc * kb + (e - c * kb)] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (cv[u] >= 0) {
+        const int j = min(max(jv[u], 0), nb - 1);
+        cmap[e0 + 64 * u + lane] = (uint16_t)j;
+        atomicOr((unsigned long long *)&inv[j], 1ull << cv[u]);
+      }
+    }
+  }
+  __syncthreads();
+  uint64_t live = __builtin_amdgcn_ballot_w64(qb >= 0);
+  int sc = 0;  // score of position lane
+  // adds the key blocks of position c that are new to the union
+  auto add_member = [&](int c) {
+    const int j = lane < kb ? (int)cmap[c * kb + lane] : 0;
+    bool fresh = false;
+    if (lane < kb) fresh = !((inu[j >> 5] >> (j & 31)) & 1u);
+    if (fresh) atomicOr(&inu[j >> 5], 1u << (j & 31));
+    uint64_t nm = __builtin_amdgcn_ballot_w64(fresh);
+    while (nm) {
+      int js[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        js[u] = -1;
+        if (nm) {
+          const int t = __builtin_ctzll(nm);
+          nm &= nm - 1;
+          js[u] = __shfl(j, t, 64);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (js[u] >= 0) sc += (int)((inv[js[u]] >> lane) & 1ull);
+    }
+    __syncthreads();  // the union bits are complete before the next reads
+  };
+  int32_t outv = -1;  // regrouped sequence: position p held by lane p
+  int outp = 0;
+  while (live) {
+    const int sd = __builtin_ctzll(live);
+    for (int w = lane; w < nwords; w += 64) inu[w] = 0u;
+    sc = 0;
+    __syncthreads();
+    const int vs = __shfl(qb, sd, 64);  // with every lane active
+    if (lane == outp) outv = vs;
+    live &= ~(1ull << sd);
+    add_member(sd);
+    for (int members = 1; members < G && live; ++members) {
+      // key = score*64 + (63 - position): most shared key blocks, then earliest
+      int best = ((live >> lane) & 1ull) ? sc * 64 + (63 - lane) : -1;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) best = max(best, __shfl_xor(best, o, 64));
+      const int c = 63 - (best & 63);
+      const int v = __shfl(qb, c, 64);
+      if (lane == outp + members) outv = v;
+      live &= ~(1ull << c);
+      if (members + 1 < G) add_member(c);
+    }
+    outp += G;
+  }
+  if (lane < wn) ug[lane] = outv;
+}
+
 // ---------------------------------------------------------------- k_union
 // One wave per group: the members' maps are folded into per-key-block member
 // masks in LDS (4 key blocks per word, one byte each), then compacted in
@@ -778,13 +916,13 @@ __global__ __launch_bounds__(128 * G) void k_attn(AttnArgs args) {
     // V^T transposed-read rows 4g + (l%16)/4 (+16 per k-step, +8 for the
     // second half), dims 32dt + 16((l/16)%2) + 4(l%4)
     int koff[NS], voff[DT];
-    int64_t gk[OPS], gv[OPS];  // this lane's global element offsets inside a key block
+    uint32_t gk[OPS], gv[OPS];  // this lane's byte offsets inside a key block
 #pragma unroll
     for (int o = 0; o < OPS; ++o) {
       const int cidx = o * NT + tid;
       const int row = cidx / CH, pc = cidx % CH;
-      gk[o] = (int64_t)row * args.stride_n + ((pc ^ swz_k<D>(row)) * 8);
-      gv[o] = (int64_t)row * args.stride_n + ((pc ^ swz_v<D>(row)) * 8);
+      gk[o] = (uint32_t)(((int64_t)row * args.stride_n + ((pc ^ swz_k<D>(row)) * 8)) * 2);
+      gv[o] = (uint32_t)(((int64_t)row * args.stride_n + ((pc ^ swz_v<D>(row)) * 8)) * 2);
     }
 #pragma unroll
     for (int s2 = 0; s2 < NS; ++s2) {
@@ -805,15 +943,15 @@ __global__ __launch_bounds__(128 * G) void k_attn(AttnArgs args) {
         else return list[t];
       };
       auto issue = [&](int t) {
-        const int j = entry(t) & 0xffff;
+        const int j = __builtin_amdgcn_readfirstlane(entry(t) & 0xffff);
         uint16_t *slot = ring + (t % S) * (2 * TILE);
         const int64_t jrow = (int64_t)j * 64;
         if (jrow + 64 <= args.n_tokens) {
           const uint16_t *kj = Kb + jrow * args.stride_n, *vj = Vb + jrow * args.stride_n;
 #pragma unroll
           for (int o = 0; o < OPS; ++o) {
-            lds_dma16(kj + gk[o], slot + (o * NT + wave * 64) * 8);
-            lds_dma16(vj + gv[o], slot + TILE + (o * NT + wave * 64) * 8);
+            lds_dma16_s(kj, gk[o], slot + (o * NT + wave * 64) * 8);
+            lds_dma16_s(vj, gv[o], slot + TILE + (o * NT + wave * 64) * 8);
           }
         } else {
 #pragma unroll
@@ -1340,6 +1478,9 @@ void launch_topk(const float *s, int32_t *map, int nb, int kb, int64_t rows, hip
 void launch_schedule(const int32_t *map, int nb, int kb, int G, int ngroups, int list_stride,
                      int bh, int32_t *ugroup, int32_t *ucount, int32_t *ulist, hipStream_t st) {
   hipLaunchKernelGGL(k_order, dim3(bh), dim3(1024), (size_t)nb * 4, st, map, nb, kb, G, ngroups, ugroup);
+  if (kb > 0 && kb <= kGroupMaxKb && kGroupWin % G == 0)
+    hipLaunchKernelGGL(k_group, dim3((ngroups * G + kGroupWin - 1) / kGroupWin, bh), dim3(64),
+                       (size_t)nb * 8 + (size_t)(nb + 31) / 32 * 4, st, map, nb, kb, G, ngroups, ugroup);
   if (kb > 0) {
     const size_t lds = (size_t)kUnionWaves * ((nb + 3) / 4) * 4;
     hipLaunchKernelGGL(k_union, dim3((ngroups + kUnionWaves - 1) / kUnionWaves, bh), dim3(64 * kUnionWaves), lds,

@@ -118,3 +118,10 @@ def test_plan_fp8_adds_code_images_to_workspace():
     bh_nb = prob.batch * prob.heads * f.nb
     assert f.workspace_bytes - b.workspace_bytes >= bh_nb * (128 * prob.head_dim + 16)
     assert f.workspace_bytes - b.workspace_bytes <= bh_nb * (128 * prob.head_dim + 16) + 4 * 256
+
+
+def test_plan_rejects_token_stride_beyond_32bit_tile_offsets():
+    st, _ = _plan(_prob(sn=(1 << 24) + 8), rola.Config(topk=0.1))
+    assert st == 2
+    st, _ = _plan(_prob(sn=1 << 24), rola.Config(topk=0.1))
+    assert st == 0
