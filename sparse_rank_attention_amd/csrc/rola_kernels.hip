@@ -469,30 +469,61 @@ __global__ __launch_bounds__(256) void k_state_reduce(const float *__restrict__ 
 
 // --------------------------------------------------------------- k_scores
 // s[bh][i][j] = sequential fma chain over d of Qp[i][d] * Kp[j][d] from +0.0.
-// Lane = key block j (its Kp row in registers), rows i wave-uniform.
+// One workgroup per 64x64 tile of (i, j); thread t computes rows
+// 4*(t/16)..+3 by keys 4*(t%16)..+3.  Qp and Kp are staged through LDS in
+// 16-dim chunks, transposed ([d][block]), so each d step is two 16-byte LDS
+// reads and 16 FMAs.  Chunks are taken in increasing d, so every element's
+// chain keeps the order d = 0..D-1.
 template <int D>
 __global__ __launch_bounds__(256) void k_scores(const float *__restrict__ qp,
                                                 const float *__restrict__ kp, float *__restrict__ s,
-                                                int nb, int rows_per_wg) {
+                                                int nb) {
 #pragma clang fp contract(off)
+  __shared__ f32x4 qs[16][16];  // [d in chunk][row group]: 4 rows per float4
+  __shared__ f32x4 ks[16][16];  // [d in chunk][key group]
   const int bh = blockIdx.z;
-  const int j = blockIdx.x * 256 + threadIdx.x;
-  const int jl = j < nb ? j : nb - 1;
-  const float *kr = kp + ((int64_t)bh * nb + jl) * D;
-  float kreg[D];
+  const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
+  const int tid = threadIdx.x;
+  const int tr = tid >> 4, tc = tid & 15;
+  const float *qb = qp + (int64_t)bh * nb * D;
+  const float *kb = kp + (int64_t)bh * nb * D;
+  // staging: thread t copies 4 dims (d4 = t%4) of block row t/4
+  const int srow = tid >> 2, sd4 = tid & 3;
+  const int qrow = min(i0 + srow, nb - 1), krow = min(j0 + srow, nb - 1);
+  float acc[4][4];
 #pragma unroll
-  for (int d = 0; d < D; d += 4) {
-    const f32x4 x = *(const f32x4 *)(kr + d);
-    kreg[d] = x[0]; kreg[d + 1] = x[1]; kreg[d + 2] = x[2]; kreg[d + 3] = x[3];
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[r][c] = 0.0f;
+  for (int dc = 0; dc < D; dc += 16) {
+    const f32x4 qv = *(const f32x4 *)(qb + (int64_t)qrow * D + dc + 4 * sd4);
+    const f32x4 kv = *(const f32x4 *)(kb + (int64_t)krow * D + dc + 4 * sd4);
+    __syncthreads();  // previous chunk fully read
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ((float *)&qs[4 * sd4 + e][srow >> 2])[srow & 3] = qv[e];
+      ((float *)&ks[4 * sd4 + e][srow >> 2])[srow & 3] = kv[e];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int d = 0; d < 16; ++d) {
+      const f32x4 a = qs[d][tr], b = ks[d][tc];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[r][c] = __builtin_fmaf(a[r], b[c], acc[r][c]);
+    }
   }
-  const int i0 = blockIdx.y * rows_per_wg;
-  const int i1 = min(nb, i0 + rows_per_wg);
-  for (int i = i0; i < i1; ++i) {
-    const float *qr = qp + ((int64_t)bh * nb + i) * D;
-    float acc = 0.0f;
 #pragma unroll
-    for (int d = 0; d < D; ++d) acc = __builtin_fmaf(qr[d], kreg[d], acc);
-    if (j < nb) s[((int64_t)bh * nb + i) * nb + j] = acc;
+  for (int r = 0; r < 4; ++r) {
+    const int i = i0 + 4 * tr + r;
+    if (i >= nb) break;
+    float *row = s + ((int64_t)bh * nb + i) * nb;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int j = j0 + 4 * tc + c;
+      if (j < nb) row[j] = acc[r][c];
+    }
   }
 }
 
@@ -1452,10 +1483,9 @@ void launch_state_reduce(const float *part, int nchunks, int D, int rank, int bh
 
 void launch_scores(const float *qp, const float *kp, float *s, int nb, int D, int bh,
                    hipStream_t st) {
-  const int rows = 64;
-  dim3 grid((nb + 255) / 256, (nb + rows - 1) / rows, bh);
-  if (D == 64) hipLaunchKernelGGL(k_scores<64>, grid, dim3(256), 0, st, qp, kp, s, nb, rows);
-  else hipLaunchKernelGGL(k_scores<128>, grid, dim3(256), 0, st, qp, kp, s, nb, rows);
+  dim3 grid((nb + 63) / 64, (nb + 63) / 64, bh);
+  if (D == 64) hipLaunchKernelGGL(k_scores<64>, grid, dim3(256), 0, st, qp, kp, s, nb);
+  else hipLaunchKernelGGL(k_scores<128>, grid, dim3(256), 0, st, qp, kp, s, nb);
 }
 
 void launch_topk(const float *s, int32_t *map, int nb, int kb, int64_t rows, hipStream_t st) {
