@@ -281,163 +281,189 @@ __global__ void k_setup(const float *__restrict__ wq, const float *__restrict__ 
 
 // ---------------------------------------------------------------- k_pass1
 // Grid (nchunks, B*H), 256 threads: each workgroup streams `cpc` consecutive
-// 64-token blocks of one (batch, head) through a 3-slot LDS ring filled by
-// direct global->LDS copies two blocks ahead of the one being consumed.
-//   POOL : wave 0 pools Q, wave 1 pools K (fixed fp32 tree order).
-//   STATE: waves 2 and 3 take tokens 0-31 and 32-63 of the block: b =
-//          phi(Wk^T R(k)) on MFMA, then S^T += V^T b (V^T read transposed
-//          from the row-major V tile) and z += b.  Per-wave partial sums go
-//          to the workspace for a fixed-order reduction.
-// Rows past N are copied from row N-1 (finite values); they are excluded
-// from the pooled means and get b = 0.
+// 64-token blocks of one (batch, head).  The four waves work independently
+// (no barriers):
+//   POOL : wave 0 pools Q, wave 1 pools K, straight from global memory.  A
+//          lane holds 8 dims (one 16-byte load) of tokens 4r + lane/16
+//          (r = 0..15 at D = 128), so the fixed fp32 tree -- pairs at token
+//          distance 32, 16, 8, 4 inside the lane, then 2 and 1 across
+//          lanes -- runs in place.
+//   STATE: waves 2 and 3 take tokens 0-31 and 32-63 of each block: K rows
+//          as MFMA operands straight from global memory (one block ahead in
+//          registers), b = phi(Wk^T R(k)) on MFMA, then S^T += V^T b and
+//          z += b with V^T read transposed from LDS.  Each state wave copies
+//          its own 32-token half of V into its own 3-slot LDS ring (two
+//          blocks ahead), so it only waits for its own copies.  Per-wave
+//          partial sums go to the workspace for a fixed-order reduction.
+// Rows past N are read as zero (pooling) or taken from row N-1 (finite
+// values; their b is masked to 0).
 template <int D, bool POOL, bool STATE>
 __global__ __launch_bounds__(256) void k_pass1(Pass1Args args) {
   constexpr int CH = D / 8;       // 16-byte chunks per token row
-  constexpr int TILE = 64 * D;    // elements per tensor tile
-  constexpr int NTEN = (POOL ? 1 : 0) + 1 + (STATE ? 1 : 0);  // Q?, K, V?
-  constexpr int STAGE = NTEN * TILE;
+  constexpr int NS = D / 16;      // MFMA k-steps over head_dim
+  constexpr int DT = D / 32;      // d-tiles of the state
+  constexpr int VT = 32 * D;      // bf16 elements of a 32-token V half tile
   constexpr int NSTAGE = 3;
-  constexpr int OPS = (64 * CH) / 256;  // DMA ops per thread per tensor
-  constexpr int QOFF = 0, KOFF = POOL ? TILE : 0, VOFF = KOFF + TILE;
-  __shared__ __attribute__((aligned(1024))) uint16_t ring[NSTAGE * STAGE];
+  constexpr int VOPS = (32 * CH) / 64;  // DMA ops per lane per half tile
+  __shared__ __attribute__((aligned(1024))) uint16_t vring[STATE ? 2 * NSTAGE * VT : 8];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
   const int bh = blockIdx.y;
   const int b = bh / args.heads, h = bh % args.heads;
   const int64_t base = (int64_t)b * args.stride_b + (int64_t)h * args.stride_h;
-  const uint16_t *Q = args.q + base, *K = args.k + base, *V = args.v + base;
   const int c0 = blockIdx.x * args.cpc;
   const int c1 = min(args.nb, c0 + args.cpc);
   const int nblk = c1 - c0;
   const RopeArgsDev ra = args.rope;
+  // projection rows and rotary frequencies of the state waves, shared
+  __shared__ __attribute__((aligned(16))) uint16_t swk[STATE ? 32 * D : 8];
+  __shared__ float sfreq[STATE ? D / 2 : 1];
+  if (STATE) {
+    for (int e = tid; e < 32 * D / 8; e += 256) ((u32x4 *)swk)[e] = ((const u32x4 *)args.wkT)[e];
+    for (int p2 = tid; p2 < D / 2; p2 += 256) sfreq[p2] = rope_freq(2 * p2, ra);
+    __syncthreads();  // the only barrier: before the waves take their roles
+  }
 
-  auto issue = [&](int i) {  // copy block c0+i into slot i % NSTAGE
-    uint16_t *slot = ring + (i % NSTAGE) * STAGE;
-    const int64_t c = c0 + i;
+  if (wave < 2) {
+    if (!POOL) return;
+    // ---- pooling: LPR lanes per token row, TG token groups per load
+    constexpr int LPR = D / 8, TG = 64 / LPR, R = 64 / TG;
+    const uint16_t *X = (wave == 0 ? args.q : args.k) + base;
+    float *dst = wave == 0 ? args.qp : args.kp;
+    const int dl = lane % LPR, tg = lane / LPR;
+    for (int i = 0; i < nblk; ++i) {
+      const int c = c0 + i;
+      const int valid = min(64, (int)(args.n_tokens - (int64_t)c * 64));
+      auto ld = [&](int t) __attribute__((always_inline)) -> u32x4 {
+        return t < valid ? *(const u32x4 *)(X + ((int64_t)c * 64 + t) * args.stride_n + 8 * dl)
+                         : u32x4{0u, 0u, 0u, 0u};
+      };
+      // token distance 32 as the pairs arrive (registers r and r + R/2)
+      float x[R / 2][8];
 #pragma unroll
-    for (int o = 0; o < OPS; ++o) {
-      const int cidx = o * 256 + tid;
-      const int row = cidx / CH, pc = cidx % CH;
-      const int64_t src = min(c * 64 + row, args.n_tokens - 1) * args.stride_n;
-      uint16_t *dst = slot + (o * 256 + wave * 64) * 8;
-      if (POOL) lds_dma16(Q + src + pc * 8, dst + QOFF);
-      lds_dma16(K + src + ((pc ^ swz_k<D>(row)) * 8), dst + KOFF);
-      if (STATE) lds_dma16(V + src + ((pc ^ swz_v<D>(row)) * 8), dst + VOFF);
+      for (int r = 0; r < R / 2; ++r) {
+        const u32x4 lo = ld(TG * r + tg), hi = ld(TG * (r + R / 2) + tg);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[r][2 * e] = bflo(lo[e]) + bflo(hi[e]);
+          x[r][2 * e + 1] = bfhi(lo[e]) + bfhi(hi[e]);
+        }
+      }
+      // token distances 16 .. TG inside the lane (register r + dist/TG)
+#pragma unroll
+      for (int dist = 16; dist >= TG; dist >>= 1) {
+#pragma unroll
+        for (int r = 0; r < dist / TG; ++r)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[r][e] = x[r][e] + x[r + dist / TG][e];
+      }
+      // distances TG/2 .. 1 across lanes (token group tg + dist = lane + dist*LPR)
+#pragma unroll
+      for (int dist = TG / 2; dist >= 1; dist >>= 1) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float o = __shfl_xor(x[0][e], dist * LPR, 64);
+          x[0][e] = x[0][e] + o;  // meaningful in token group 0 (lanes < LPR)
+        }
+      }
+      if (lane < LPR) {
+        const float inv = valid == 64 ? 0.015625f : args.inv_tail;
+        float *o = dst + ((int64_t)bh * args.nb + c) * D + 8 * dl;
+        *(f32x4 *)o = f32x4{x[0][0] * inv, x[0][1] * inv, x[0][2] * inv, x[0][3] * inv};
+        *(f32x4 *)(o + 4) = f32x4{x[0][4] * inv, x[0][5] * inv, x[0][6] * inv, x[0][7] * inv};
+      }
     }
-  };
+    return;
+  }
+  if (!STATE) return;
 
-  // state accumulators of this wave's token half, all d-tiles
-  constexpr int DT = D / 32;
+  // ---- low-rank state: wave 2 tokens 0-31, wave 3 tokens 32-63
+  const int tt = wave - 2;
+  const uint16_t *Kb = args.k + base, *Vb = args.v + base;
+  uint16_t *myring = vring + tt * NSTAGE * VT;
   f32x16 sacc[DT];
 #pragma unroll
   for (int i = 0; i < DT; ++i) sacc[i] = f32x16{};
   float zacc = 0.0f;
-  bf16x8 wkreg[D / 16];
-  float freq[D / 4];  // inverse frequencies of this lane's rotary pairs
-  const int tt = wave - 2;  // token tile of the state waves
-  if (STATE && wave >= 2) {
+  // V half tile of block i -> slot i % NSTAGE (row-major, chunk-swizzled)
+  auto issue_v = [&](int i) __attribute__((always_inline)) {
+    const int64_t c = c0 + i;
+    uint16_t *slot = myring + (i % NSTAGE) * VT;
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      wkreg[s] = *(const bf16x8 *)(args.wkT + (lane & 31) * D + 16 * s + 8 * g);
-#pragma unroll
-      for (int p = 0; p < 4; ++p) freq[4 * s + p] = rope_freq(16 * s + 8 * g + 2 * p, ra);
+    for (int o = 0; o < VOPS; ++o) {
+      const int cidx = o * 64 + lane;
+      const int row = cidx / CH, pc = cidx % CH;
+      const int64_t src = min(c * 64 + 32 * tt + row, args.n_tokens - 1) * args.stride_n;
+      lds_dma16(Vb + src + ((pc ^ swz_v<D>(row)) * 8), slot + o * 512);
     }
-  }
-  wait_vmcnt<0>();  // projection rows loaded before the copies start (in-order vmcnt)
-
-  for (int i = 0; i < NSTAGE - 1; ++i)
-    if (i < nblk) issue(i);
+  };
+  // K operand rows of block i: token 32*tt + lane%32, dims 16s + 8g .. +8
+  auto load_k = [&](int i, bf16x8 (&kr)[NS]) __attribute__((always_inline)) {
+    const int64_t row = min((int64_t)(c0 + i) * 64 + 32 * tt + (lane & 31), args.n_tokens - 1);
+    const uint16_t *kp = Kb + row * args.stride_n + 8 * g;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) kr[s] = *(const bf16x8 *)(kp + 16 * s);
+  };
+  bf16x8 kcur[NS], knext[NS];
+  if (nblk > 0) issue_v(0);
+  if (nblk > 1) issue_v(1);
+  if (nblk > 0) load_k(0, kcur);
   for (int i = 0; i < nblk; ++i) {
-    // wait for block i; blocks i+1 (3*OPS*NTEN ops) may stay in flight
-    if (i + 1 < nblk) wait_vmcnt<NTEN * OPS>();
+    if (i + 2 < nblk) issue_v(i + 2);
+    if (i + 1 < nblk) load_k(i + 1, knext);
+    // block i: V(i) and K(i) were issued before V(i+2) and K(i+1); vmcnt
+    // completes in order, so allow exactly the ops issued after K(i)
+    if (i + 2 < nblk) wait_vmcnt<VOPS + NS>();
+    else if (i + 1 < nblk) wait_vmcnt<NS>();
     else wait_vmcnt<0>();
-    barrier_lds();  // block i visible; every wave is done with block i-1
-    if (i + NSTAGE - 1 < nblk) issue(i + NSTAGE - 1);
     const int c = c0 + i;
     const int valid = min(64, (int)(args.n_tokens - (int64_t)c * 64));
-    const uint16_t *slot = ring + (i % NSTAGE) * STAGE;
-
-    // ---- pooling: wave 0 -> Q, wave 1 -> K; lane owns dims 2*lane, 2*lane+1
-    if (POOL && wave < 2 && lane < D / 2) {
-      const uint16_t *tile = slot + (wave == 0 ? QOFF : KOFF);
-      const int word = lane;
-      float lo[32], hi[32];
+    const uint16_t *sV = myring + (i % NSTAGE) * VT;
+    f32x16 bacc = f32x16{};
+    int pt, ph, pw;  // padded rows take the last valid position (their b is masked)
+    token_pos(min((int64_t)c * 64 + 32 * tt + (lane & 31), args.n_tokens - 1), ra, pt, ph, pw);
 #pragma unroll
-      for (int s = 0; s < 64; ++s) {
-        const int off = wave == 0 ? s * D + 2 * word
-                                  : s * D + ((((word >> 2) ^ swz_k<D>(s)) << 3) | ((word & 3) << 1));
-        const uint32_t x = s < valid ? *(const uint32_t *)(tile + off) : 0u;
-        if (s < 32) {
-          lo[s] = bflo(x);
-          hi[s] = bfhi(x);
-        } else {
-          lo[s - 32] = lo[s - 32] + bflo(x);
-          hi[s - 32] = hi[s - 32] + bfhi(x);
-        }
-      }
-#pragma unroll
-      for (int stride = 16; stride >= 1; stride >>= 1) {
-#pragma unroll
-        for (int k2 = 0; k2 < stride; ++k2) {
-          lo[k2] = lo[k2] + lo[k2 + stride];
-          hi[k2] = hi[k2] + hi[k2 + stride];
-        }
-      }
-      const float inv = valid == 64 ? 0.015625f : args.inv_tail;
-      float *dst = (wave == 0 ? args.qp : args.kp) + ((int64_t)bh * args.nb + c) * D + 2 * word;
-      *(float2 *)dst = make_float2(lo[0] * inv, hi[0] * inv);
+    for (int s = 0; s < NS; ++s) {
+      const f32x4 fr = *(const f32x4 *)&sfreq[8 * s + 4 * g];  // pairs of dims 16s + 8g .. +8
+      const float freq4[4] = {fr[0], fr[1], fr[2], fr[3]};
+      const bf16x8 kx = rope8(kcur[s], 16 * s + 8 * g, pt, ph, pw, freq4, ra);
+      bacc = mfma_bf16(kx, *(const bf16x8 *)&swk[(lane & 31) * D + 16 * s + 8 * g], bacc);
     }
-
-    // ---- low-rank state: wave 2 tokens 0-31, wave 3 tokens 32-63
-    if (STATE && wave >= 2) {
-      const uint16_t *sK = slot + KOFF, *sV = slot + VOFF;
-      f32x16 bacc = f32x16{};
-      const int row = 32 * tt + (lane & 31);
-      int pt, ph, pw;  // padded rows take the last valid position (their b is masked)
-      token_pos(min((int64_t)c * 64 + row, args.n_tokens - 1), ra, pt, ph, pw);
+    // phi, mask invalid tokens and rank padding, z, pack as B operand
+    const bool rok = (lane & 31) < args.rank;
+    bf16x8 bop[2];
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        const int lc = 2 * s + g;
-        bf16x8 kx = *(const bf16x8 *)(sK + row * D + ((lc ^ swz_k<D>(row)) * 8));
-        kx = rope8(kx, 16 * s + 8 * g, pt, ph, pw, &freq[4 * s], ra);
-        bacc = mfma_bf16(kx, wkreg[s], bacc);
-      }
-      // phi, mask invalid tokens and rank padding, z, pack as B operand
-      const bool rok = (lane & 31) < args.rank;
-      bf16x8 bop[2];
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int tok = 32 * tt + 8 * (e >> 2) + 4 * g + (e & 3);
-        float f = phi(bacc[e]);
-        f = (rok && tok < valid) ? f : 0.0f;
-        zacc += f;
-        bop[e >> 3][e & 7] = (__bf16)f;
-      }
-      // S^T[d][r] += sum_tok V^T[d][tok] * b[tok][r] over this wave's 32 tokens
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const bf16x8 va = vt_operand<D>(sV, 2 * tt + s2, dt, lane);
-          sacc[dt] = mfma_bf16(va, bop[s2], sacc[dt]);
-        }
-      }
+    for (int e = 0; e < 16; ++e) {
+      const int tok = 32 * tt + 8 * (e >> 2) + 4 * g + (e & 3);
+      float f = phi(bacc[e]);
+      f = (rok && tok < valid) ? f : 0.0f;
+      zacc += f;
+      bop[e >> 3][e & 7] = (__bf16)f;
     }
-  }
-
-  if (STATE && wave >= 2) {
-    float *part = args.state_part + (((int64_t)bh * gridDim.x + blockIdx.x) * 2 + tt) * (D * 32 + 32);
+    // S^T[d][r] += sum_tok V^T[d][tok] * b[tok][r] over this wave's 32 tokens
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int d = 32 * dt + 8 * (e >> 2) + 4 * g + (e & 3);
-        part[d * 32 + (lane & 31)] = sacc[dt][e];
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const bf16x8 va = vt_operand<D>(sV, s2, dt, lane);
+        sacc[dt] = mfma_bf16(va, bop[s2], sacc[dt]);
       }
     }
-    const float zt = zacc + shfl_xor32(zacc);
-    if (lane < 32) part[D * 32 + lane] = zt;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) kcur[s] = knext[s];
   }
+
+  float *part = args.state_part + (((int64_t)bh * gridDim.x + blockIdx.x) * 2 + tt) * (D * 32 + 32);
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int d = 32 * dt + 8 * (e >> 2) + 4 * g + (e & 3);
+      part[d * 32 + (lane & 31)] = sacc[dt][e];
+    }
+  }
+  const float zt = zacc + shfl_xor32(zacc);
+  if (lane < 32) part[D * 32 + lane] = zt;
 }
 
 // ------------------------------------------------------------ k_state_reduce
