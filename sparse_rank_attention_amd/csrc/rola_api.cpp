@@ -187,7 +187,7 @@ int32_t run_setup(const Plan &P, const float *wq, const float *wk, uint8_t *ws, 
 }
 
 int32_t run_pass1(const Plan &P, const rola_problem *p, const void *q, const void *k, const void *v,
-                  uint8_t *ws, bool pool, bool state, hipStream_t st) {
+                  uint8_t *ws, bool pool, bool state, hipStream_t st, bool quant = false) {
   rola::Pass1Args a;
   a.q = (const uint16_t *)q; a.k = (const uint16_t *)k; a.v = (const uint16_t *)v;
   a.stride_b = p->stride_b; a.stride_h = p->stride_h; a.stride_n = p->stride_n;
@@ -199,8 +199,14 @@ int32_t run_pass1(const Plan &P, const rola_problem *p, const void *q, const voi
   a.wkT = (const uint16_t *)(ws + P.off_wkT);
   a.state_part = (float *)(ws + P.off_part);
   a.rope = rope_args(P, ws);
-  const char *name = (pool && state) ? "pass1_pool_state" : pool ? "pass1_pool" : "pass1_state";
-  return timed(name, st, [&] { rola::launch_pass1(a, P.D, P.nchunks, (int)P.BH, pool, state, st); });
+  a.qsc = (float *)(ws + P.off_qsc);
+  a.ksc = (float *)(ws + P.off_ksc);
+  a.vsc = (float *)(ws + P.off_vsc);
+  a.kv8 = ws + P.off_kv8;
+  const char *name = (pool && state) ? (quant ? "pass1_pool_state_quant8" : "pass1_pool_state")
+                     : pool          ? "pass1_pool"
+                                     : "pass1_state";
+  return timed(name, st, [&] { rola::launch_pass1(a, P.D, P.nchunks, (int)P.BH, pool, state, quant, st); });
 }
 
 int32_t run_reduce(const Plan &P, uint8_t *ws, hipStream_t st) {
@@ -394,8 +400,8 @@ int32_t rola_forward(const rola_problem *prob, const rola_config *cfg, const voi
   uint8_t *ws = (uint8_t *)workspace;
   int32_t *map = block_idx_out ? block_idx_out : (int32_t *)(ws + P.off_map);
   ROLA_TRY(run_setup(P, wq, wk, ws, st));
-  ROLA_TRY(run_pass1(P, prob, q, k, v, ws, true, true, st));
-  if (P.fp8) ROLA_TRY(run_quant8(P, prob, q, k, v, ws, st));
+  // fp8: the streaming pass also writes the scales and e4m3 tile images
+  ROLA_TRY(run_pass1(P, prob, q, k, v, ws, true, true, st, P.fp8));
   ROLA_TRY(run_reduce(P, ws, st));
   ROLA_TRY(run_select(P, ws, (float *)(ws + P.off_scores), map, st));
   return run_attn(P, prob, cfg, q, k, v, map, out, ws, true, true, false, st);

@@ -31,6 +31,9 @@ struct Pass1Args {
   const uint16_t *wkT;  // bf16 [32][D]
   float *state_part;    // [BH][nchunks][2][D*32 + 32]
   RopeArgsHost rope;
+  // fp8 mode (see Quant8Args): Q scales, K and V^T codes of each block
+  float *qsc, *ksc, *vsc;
+  uint8_t *kv8;
 };
 
 // Attention workgroup shape: G query blocks per workgroup (2 waves each),
@@ -85,7 +88,8 @@ struct AttnArgs {
 };
 
 void launch_setup(const SetupArgs &a, hipStream_t st);
-void launch_pass1(const Pass1Args &a, int D, int nchunks, int bh, bool pool, bool state, hipStream_t st);
+void launch_pass1(const Pass1Args &a, int D, int nchunks, int bh, bool pool, bool state, bool quant,
+                  hipStream_t st);
 void launch_state_reduce(const float *part, int nchunks, int D, int rank, int bh, uint16_t *st_out,
                          float *z, hipStream_t st);
 void launch_scores(const float *qp, const float *kp, float *s, int nb, int D, int bh,

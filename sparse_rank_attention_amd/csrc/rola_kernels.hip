@@ -279,6 +279,48 @@ __global__ void k_setup(const float *__restrict__ wq, const float *__restrict__ 
   }
 }
 
+// ---------------------------------------------------------------- fp8 path
+// e4m3 codes: round to nearest even, saturating at +-448
+// (v_cvt_pk_fp8_f32; `hi` selects the upper 16 bits of `old`).
+template <bool HI>
+static __device__ __forceinline__ int cvt_fp8x2(float a, float b, int old) {
+  return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
+}
+
+// v_mfma_f32_32x32x64_f8f6f4 with both operands e4m3 and no block scales.
+// Lane l holds 32 codes (8 dwords) of row (A) / column (B) l%32; A and B
+// bytes with the same lane half and byte index meet at the same k.
+static __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// Tile image of one 64-token block (bytes; 128*D per block):
+//  K part, [64 keys][D]: dim d of a key sits at position
+//    p = 64*(d/64) + 32*((d%16)/8) + 8*((d%64)/16) + d%8,
+//  so that each MFMA lane half reads the 32 dims its Q operand holds (the
+//  bf16 Q registers, 16 dims per 16-dim step, 8 per lane half) as two
+//  contiguous 16-byte chunks; chunk c of key row r is stored at
+//  c ^ ((r / (256/D)) & (D/16 - 1)), conflict-free for 16-lane reads.
+//  V^T part, [D][64 keys]: key k sits at position 32*((k%8)/4) + e with
+//    e = 4*((k%32)/8) + k%4 (+16 for k >= 32),
+//  the order in which a lane half holds S^T accumulator rows (keys), so P^T
+//  needs no shuffles; chunk c of row d is stored at c ^ ((d/4) & 3).
+template <int D>
+static __device__ __forceinline__ int img_k_off(int r, int d) {
+  const int rem = d & 63;
+  const int p = (d & ~63) + 32 * ((rem & 15) >> 3) + 8 * (rem >> 4) + (rem & 7);
+  const int f = (r / (256 / D)) & (D / 16 - 1);
+  return r * D + ((((p >> 4) ^ f)) << 4) + (p & 15);
+}
+static __device__ __forceinline__ int img_v_pos(int k) {
+  const int g = (k & 7) >> 2;
+  const int e = 4 * ((k & 31) >> 3) + (k & 3) + (k >= 32 ? 16 : 0);
+  return 32 * g + e;
+}
+static __device__ __forceinline__ int img_v_off(int d, int p) {
+  return d * 64 + ((((p >> 4) ^ ((d >> 2) & 3))) << 4) + (p & 15);
+}
+
 // ---------------------------------------------------------------- k_pass1
 // Grid (nchunks, B*H), 256 threads: each workgroup streams `cpc` consecutive
 // 64-token blocks of one (batch, head).  The four waves work independently
@@ -295,10 +337,15 @@ __global__ void k_setup(const float *__restrict__ wq, const float *__restrict__ 
 //          its own 32-token half of V into its own 3-slot LDS ring (two
 //          blocks ahead), so it only waits for its own copies.  Per-wave
 //          partial sums go to the workspace for a fixed-order reduction.
+//   QUANT: (fp8 mode, with POOL) the pooling waves also take the block
+//          absmax of Q (its scales) and of K (scales and the K part of the
+//          block's e4m3 tile image), and a fifth wave reads V the same way
+//          and writes its scales and the V^T part of the image through an
+//          LDS transpose (see k_quant8 for the image layout and rounding).
 // Rows past N are read as zero (pooling) or taken from row N-1 (finite
 // values; their b is masked to 0).
-template <int D, bool POOL, bool STATE>
-__global__ __launch_bounds__(256) void k_pass1(Pass1Args args) {
+template <int D, bool POOL, bool STATE, bool QUANT>
+__global__ __launch_bounds__(QUANT ? 320 : 256) void k_pass1(Pass1Args args) {
   constexpr int CH = D / 8;       // 16-byte chunks per token row
   constexpr int NS = D / 16;      // MFMA k-steps over head_dim
   constexpr int DT = D / 32;      // d-tiles of the state
@@ -306,6 +353,7 @@ __global__ __launch_bounds__(256) void k_pass1(Pass1Args args) {
   constexpr int NSTAGE = 3;
   constexpr int VOPS = (32 * CH) / 64;  // DMA ops per lane per half tile
   __shared__ __attribute__((aligned(1024))) uint16_t vring[STATE ? 2 * NSTAGE * VT : 8];
+  __shared__ __attribute__((aligned(16))) uint8_t vimg8[QUANT ? 64 * D : 16];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
   const int bh = blockIdx.y;
@@ -324,13 +372,68 @@ __global__ __launch_bounds__(256) void k_pass1(Pass1Args args) {
     __syncthreads();  // the only barrier: before the waves take their roles
   }
 
+  // lane layout of the pooling / quantising waves: LPR lanes per token row
+  // (8 dims each), TG token groups per load, R loads per block
+  constexpr int LPR = D / 8, TG = 64 / LPR, R = 64 / TG;
+  const int dl = lane % LPR, tg = lane / LPR;
+  // block absmax over this wave's lanes, scale fl32(absmax/448) and inverse
+  // fl32(448/absmax) (1 and 1 for an all-zero block)
+  auto wave_absmax = [&](float m) __attribute__((always_inline)) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    return m;
+  };
+  auto e4m3x8 = [&](u32x4 x, float inv) __attribute__((always_inline)) -> uint2 {
+    const int w0 = cvt_fp8x2<true>(bflo(x[1]) * inv, bfhi(x[1]) * inv,
+                                   cvt_fp8x2<false>(bflo(x[0]) * inv, bfhi(x[0]) * inv, 0));
+    const int w1 = cvt_fp8x2<true>(bflo(x[3]) * inv, bfhi(x[3]) * inv,
+                                   cvt_fp8x2<false>(bflo(x[2]) * inv, bfhi(x[2]) * inv, 0));
+    return make_uint2((uint32_t)w0, (uint32_t)w1);
+  };
+
+  if (QUANT && wave == 4) {
+    // ---- fp8 codes of V: scales, then V^T image part via an LDS transpose
+    const uint16_t *X = args.v + base;
+    for (int i = 0; i < nblk; ++i) {
+      const int c = c0 + i;
+      const int valid = min(64, (int)(args.n_tokens - (int64_t)c * 64));
+      u32x4 raw[R];
+      float m = 0.0f;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int t = TG * r + tg;
+        raw[r] = t < valid ? *(const u32x4 *)(X + ((int64_t)c * 64 + t) * args.stride_n + 8 * dl)
+                           : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) m = fmaxf(m, fmaxf(fabsf(bflo(raw[r][e])), fabsf(bfhi(raw[r][e]))));
+      }
+      m = wave_absmax(m);
+      const int64_t sidx = (int64_t)bh * args.nb + c;
+      const float inv = m > 0.0f ? __fdiv_rn(448.0f, m) : 1.0f;
+      if (lane == 0) args.vsc[sidx] = m > 0.0f ? __fdiv_rn(m, 448.0f) : 1.0f;
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // previous block's image read out
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int t = TG * r + tg;
+        const uint2 code = e4m3x8(raw[r], inv);
+        const int pos = img_v_pos(t);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          vimg8[img_v_off(8 * dl + e, pos)] = (uint8_t)(((e < 4 ? code.x : code.y) >> (8 * (e & 3))) & 0xffu);
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // image complete before it is read back
+      u32x4 *dstv = (u32x4 *)(args.kv8 + sidx * (128 * D) + 64 * D);
+#pragma unroll
+      for (int o = 0; o < (64 * D) / (16 * 64); ++o) dstv[o * 64 + lane] = ((const u32x4 *)vimg8)[o * 64 + lane];
+    }
+    return;
+  }
+
   if (wave < 2) {
     if (!POOL) return;
-    // ---- pooling: LPR lanes per token row, TG token groups per load
-    constexpr int LPR = D / 8, TG = 64 / LPR, R = 64 / TG;
+    // ---- pooling
     const uint16_t *X = (wave == 0 ? args.q : args.k) + base;
     float *dst = wave == 0 ? args.qp : args.kp;
-    const int dl = lane % LPR, tg = lane / LPR;
     for (int i = 0; i < nblk; ++i) {
       const int c = c0 + i;
       const int valid = min(64, (int)(args.n_tokens - (int64_t)c * 64));
@@ -340,6 +443,8 @@ __global__ __launch_bounds__(256) void k_pass1(Pass1Args args) {
       };
       // token distance 32 as the pairs arrive (registers r and r + R/2)
       float x[R / 2][8];
+      u32x4 keep[QUANT ? R : 1];  // raw K values for the codes (fp8 mode)
+      float amax = 0.0f;
 #pragma unroll
       for (int r = 0; r < R / 2; ++r) {
         const u32x4 lo = ld(TG * r + tg), hi = ld(TG * (r + R / 2) + tg);
@@ -347,6 +452,31 @@ __global__ __launch_bounds__(256) void k_pass1(Pass1Args args) {
         for (int e = 0; e < 4; ++e) {
           x[r][2 * e] = bflo(lo[e]) + bflo(hi[e]);
           x[r][2 * e + 1] = bfhi(lo[e]) + bfhi(hi[e]);
+          if (QUANT)
+            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(bflo(lo[e])), fabsf(bfhi(lo[e]))),
+                                     fmaxf(fabsf(bflo(hi[e])), fabsf(bfhi(hi[e])))));
+        }
+        if constexpr (QUANT) {
+          keep[r] = lo;
+          keep[r + R / 2] = hi;
+        }
+      }
+      if constexpr (QUANT) {
+        amax = wave_absmax(amax);
+        const int64_t sidx = (int64_t)bh * args.nb + c;
+        const float sc = amax > 0.0f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+        const float inv = amax > 0.0f ? __fdiv_rn(448.0f, amax) : 1.0f;
+        if (wave == 0) {
+          if (lane == 0) {
+            args.qsc[2 * sidx] = sc;
+            args.qsc[2 * sidx + 1] = inv;
+          }
+        } else {
+          if (lane == 0) args.ksc[sidx] = sc;
+          uint8_t *kimg = args.kv8 + sidx * (128 * D);
+#pragma unroll
+          for (int r = 0; r < R; ++r)
+            *(uint2 *)(kimg + img_k_off<D>(TG * r + tg, 8 * dl)) = e4m3x8(keep[r], inv);
         }
       }
       // token distances 16 .. TG inside the lane (register r + dist/TG)
@@ -1041,20 +1171,32 @@ __global__ __launch_bounds__(128 * G) void k_attn(AttnArgs args) {
         const uint16_t *sV = sK + TILE;
         // ---- S^T = K Q^T: two independent 32-key chains
         f32x16 sacc0 = f32x16{}, sacc1 = f32x16{};
+        // all K operands of the tile (2*NS 16-byte LDS reads) are issued
+        // before the first MFMA (the scheduler would otherwise wait on each
+        // read just before its MFMA); the two key halves' chains interleave
+        {
+          bf16x8 ka[NS], kb2[NS];
 #pragma unroll
-        for (int s = 0; s < NS; ++s)
-          sacc0 = mfma_bf16(*(const bf16x8 *)(sK + koff[s]), qreg[s], sacc0);
+          for (int s = 0; s < NS; ++s) {
+            ka[s] = *(const bf16x8 *)(sK + koff[s]);
+            kb2[s] = *(const bf16x8 *)(sK + koff[s] + 32 * D);
+          }
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int s = 0; s < NS; ++s)
-          sacc1 = mfma_bf16(*(const bf16x8 *)(sK + koff[s] + 32 * D), qreg[s], sacc1);
-        // keys >= N masked in the tail block
+          for (int s = 0; s < NS; ++s) {
+            sacc0 = mfma_bf16(ka[s], qreg[s], sacc0);
+            sacc1 = mfma_bf16(kb2[s], qreg[s], sacc1);
+          }
+        }
+        // keys >= N masked in the tail block (key 8(i/4) + 4g + i%4 of the
+        // accumulator; compared as immediates against a per-lane limit)
         if ((int64_t)(j + 1) * 64 > args.n_tokens) {
-          const int64_t nrel = args.n_tokens - (int64_t)j * 64;
+          const int lim = (int)(args.n_tokens - (int64_t)j * 64) - 4 * g;
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int key = 8 * (i >> 2) + 4 * g + (i & 3);
-            if (key >= nrel) sacc0[i] = -INFINITY;
-            if (key + 32 >= nrel) sacc1[i] = -INFINITY;
+            const int kc = 8 * (i >> 2) + (i & 3);
+            if (kc >= lim) sacc0[i] = -INFINITY;
+            if (kc + 32 >= lim) sacc1[i] = -INFINITY;
           }
         }
         // ---- online softmax, base 2, against a lazy reference: weights
@@ -1094,9 +1236,13 @@ __global__ __launch_bounds__(128 * G) void k_attn(AttnArgs args) {
             const bf16x2 pr = {pw[2 * e], pw[2 * e + 1]};
             psum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, psum, false);
           }
+          // the step's V^T operands (2*DT transposing reads) before its MFMAs
+          bf16x8 va[DT];
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt)
-            oacc[dt] = mfma_bf16(vt_operand_at(sV + voff[dt] + s * 16 * D, 8 * D), pw, oacc[dt]);
+          for (int dt = 0; dt < DT; ++dt) va[dt] = vt_operand_at(sV + voff[dt] + s * 16 * D, 8 * D);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) oacc[dt] = mfma_bf16(va[dt], pw, oacc[dt]);
         }
         l_run += psum;
         if (t + S - 1 < U) issue(t + S - 1);  // this wave's share, after its compute
@@ -1111,48 +1257,6 @@ __global__ __launch_bounds__(128 * G) void k_attn(AttnArgs args) {
   }
   if (!active) return;
   attn_finish<D, LOWRANK, ACCUM, OUTF32>(args, qreg, oacc, n, base, bh, lane);
-}
-
-// ---------------------------------------------------------------- fp8 path
-// e4m3 codes: round to nearest even, saturating at +-448
-// (v_cvt_pk_fp8_f32; `hi` selects the upper 16 bits of `old`).
-template <bool HI>
-static __device__ __forceinline__ int cvt_fp8x2(float a, float b, int old) {
-  return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
-}
-
-// v_mfma_f32_32x32x64_f8f6f4 with both operands e4m3 and no block scales.
-// Lane l holds 32 codes (8 dwords) of row (A) / column (B) l%32; A and B
-// bytes with the same lane half and byte index meet at the same k.
-static __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
-}
-
-// Tile image of one 64-token block (bytes; 128*D per block):
-//  K part, [64 keys][D]: dim d of a key sits at position
-//    p = 64*(d/64) + 32*((d%16)/8) + 8*((d%64)/16) + d%8,
-//  so that each MFMA lane half reads the 32 dims its Q operand holds (the
-//  bf16 Q registers, 16 dims per 16-dim step, 8 per lane half) as two
-//  contiguous 16-byte chunks; chunk c of key row r is stored at
-//  c ^ ((r / (256/D)) & (D/16 - 1)), conflict-free for 16-lane reads.
-//  V^T part, [D][64 keys]: key k sits at position 32*((k%8)/4) + e with
-//    e = 4*((k%32)/8) + k%4 (+16 for k >= 32),
-//  the order in which a lane half holds S^T accumulator rows (keys), so P^T
-//  needs no shuffles; chunk c of row d is stored at c ^ ((d/4) & 3).
-template <int D>
-static __device__ __forceinline__ int img_k_off(int r, int d) {
-  const int rem = d & 63;
-  const int p = (d & ~63) + 32 * ((rem & 15) >> 3) + 8 * (rem >> 4) + (rem & 7);
-  const int f = (r / (256 / D)) & (D / 16 - 1);
-  return r * D + ((((p >> 4) ^ f)) << 4) + (p & 15);
-}
-static __device__ __forceinline__ int img_v_pos(int k) {
-  const int g = (k & 7) >> 2;
-  const int e = 4 * ((k & 31) >> 3) + (k & 3) + (k >= 32 ? 16 : 0);
-  return 32 * g + e;
-}
-static __device__ __forceinline__ int img_v_off(int d, int p) {
-  return d * 64 + ((((p >> 4) ^ ((d >> 2) & 3))) << 4) + (p & 15);
 }
 
 // ---------------------------------------------------------------- k_quant8
@@ -1410,12 +1514,12 @@ __global__ __launch_bounds__(128 * G) void k_attn8(AttnArgs args) {
                          q8[s8], sacc1);
       }
       if ((int64_t)(j + 1) * 64 > args.n_tokens) {
-        const int64_t nrel = args.n_tokens - (int64_t)j * 64;
+        const int lim = (int)(args.n_tokens - (int64_t)j * 64) - 4 * g;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int key = 8 * (i >> 2) + 4 * g + (i & 3);
-          if (key >= nrel) sacc0[i] = -INFINITY;
-          if (key + 32 >= nrel) sacc1[i] = -INFINITY;
+          const int kc = 8 * (i >> 2) + (i & 3);
+          if (kc >= lim) sacc0[i] = -INFINITY;
+          if (kc + 32 >= lim) sacc1[i] = -INFINITY;
         }
       }
       const float c = sq * ck;
@@ -1489,16 +1593,19 @@ void launch_setup(const SetupArgs &a, hipStream_t st) {
 }
 
 template <int D>
-static void pass1_d(const Pass1Args &a, int nchunks, int bh, bool pool, bool state, hipStream_t st) {
+static void pass1_d(const Pass1Args &a, int nchunks, int bh, bool pool, bool state, bool quant,
+                    hipStream_t st) {
   dim3 grid(nchunks, bh), block(256);
-  if (pool && state) hipLaunchKernelGGL((k_pass1<D, true, true>), grid, block, 0, st, a);
-  else if (pool) hipLaunchKernelGGL((k_pass1<D, true, false>), grid, block, 0, st, a);
-  else hipLaunchKernelGGL((k_pass1<D, false, true>), grid, block, 0, st, a);
+  if (pool && state && quant) hipLaunchKernelGGL((k_pass1<D, true, true, true>), grid, dim3(320), 0, st, a);
+  else if (pool && state) hipLaunchKernelGGL((k_pass1<D, true, true, false>), grid, block, 0, st, a);
+  else if (pool) hipLaunchKernelGGL((k_pass1<D, true, false, false>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((k_pass1<D, false, true, false>), grid, block, 0, st, a);
 }
 
-void launch_pass1(const Pass1Args &a, int D, int nchunks, int bh, bool pool, bool state, hipStream_t st) {
-  if (D == 64) pass1_d<64>(a, nchunks, bh, pool, state, st);
-  else pass1_d<128>(a, nchunks, bh, pool, state, st);
+void launch_pass1(const Pass1Args &a, int D, int nchunks, int bh, bool pool, bool state, bool quant,
+                  hipStream_t st) {
+  if (D == 64) pass1_d<64>(a, nchunks, bh, pool, state, quant, st);
+  else pass1_d<128>(a, nchunks, bh, pool, state, quant, st);
 }
 
 void launch_state_reduce(const float *part, int nchunks, int D, int rank, int bh, uint16_t *st_out,
