@@ -1153,19 +1153,28 @@ __global__ __launch_bounds__(128 * G) void k_attn(AttnArgs args) {
           }
         }
       };
+      // Two tiles per barrier: iteration k consumes tiles 2k and 2k+1 and
+      // copies 2k+2 and 2k+3 into the slots of 2k-2 and 2k-1.  A SIMD loaded
+      // on one tile and idle on the other evens out within the pair.
+      static_assert(S == 4, "two tiles per barrier in a four-slot ring");
 #pragma unroll
-      for (int t = 0; t < S - 1; ++t)
+      for (int t = 0; t < 2; ++t)
         if (t < U) issue(t);
-      for (int t = 0; t < U; ++t) {
-        const int slot_t = t % S;
-        wait_tiles_in_flight<OPS, S>(min(S - 2, U - 1 - t));
-        barrier_lds();  // tile t visible to all waves; every wave is done with tile t-1
-        const int ent = entry(t);
-        if (!active || !((ent >> (16 + member)) & 1)) {
-          // waves idle on this tile copy their share of tile t+S-1 at once
-          if (t + S - 1 < U) issue(t + S - 1);
+      for (int t2 = 0; t2 < U; t2 += 2) {
+        wait_vmcnt<0>();  // this wave's copies of tiles t2, t2+1
+        barrier_lds();    // both visible to all waves; every wave is done with t2-2, t2-1
+        const int e0 = entry(t2), e1 = t2 + 1 < U ? entry(t2 + 1) : 0;
+        const bool m0 = active && ((e0 >> (16 + member)) & 1);
+        const bool m1 = active && ((e1 >> (16 + member)) & 1);
+        if (!m0 && !m1) {
+          // waves idle on both tiles copy their share of the next pair at once
+          if (t2 + 2 < U) issue(t2 + 2);
+          if (t2 + 3 < U) issue(t2 + 3);
           continue;
         }
+        for (int t = t2; t < min(t2 + 2, U); ++t) {
+        const int ent = t == t2 ? e0 : e1;
+        if (!(t == t2 ? m0 : m1)) continue;
         const int j = ent & 0xffff;
         const uint16_t *sK = ring + (t % S) * (2 * TILE);
         const uint16_t *sV = sK + TILE;
@@ -1245,7 +1254,10 @@ __global__ __launch_bounds__(128 * G) void k_attn(AttnArgs args) {
           for (int dt = 0; dt < DT; ++dt) oacc[dt] = mfma_bf16(va[dt], pw, oacc[dt]);
         }
         l_run += psum;
-        if (t + S - 1 < U) issue(t + S - 1);  // this wave's share, after its compute
+        }
+        // this wave's share of the next pair, after its compute
+        if (t2 + 2 < U) issue(t2 + 2);
+        if (t2 + 3 < U) issue(t2 + 3);
       }
     };
     if (U <= LMAX) main_loop(std::integral_constant<bool, true>{});
