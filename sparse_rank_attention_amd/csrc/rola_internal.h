@@ -59,9 +59,16 @@ struct Quant8Args {
   uint8_t *kv8;   // [BH][nb][128*D] tile images (K rows, then V^T rows)
 };
 
-// fp8 attention ring depth (16 KB tiles at D=128)
+// fp8 attention: ring depth (16 KB tiles at D=128), tiles per barrier and
+// union-list entries staged in LDS
 #ifndef ROLA_ATTN8_S
-#define ROLA_ATTN8_S 6
+#define ROLA_ATTN8_S 8
+#endif
+#ifndef ROLA_ATTN8_P
+#define ROLA_ATTN8_P 4
+#endif
+#ifndef ROLA_ATTN8_LMAX
+#define ROLA_ATTN8_LMAX 1024
 #endif
 
 struct AttnArgs {

@@ -1378,6 +1378,7 @@ __global__ __launch_bounds__(256) void k_quant8(Quant8Args a) {
 // Finally O = O' * sigma * 2^-8 / l.
 template <int D, int G, int S, bool LOWRANK, bool ACCUM, bool OUTF32>
 __global__ __launch_bounds__(128 * G) void k_attn8(AttnArgs args) {
+  constexpr int P = ROLA_ATTN8_P;  // tiles per barrier
   constexpr int NS = D / 16;
   constexpr int DT = D / 32;
   constexpr int K8 = D / 64;            // fp8 k-steps over head_dim
@@ -1386,7 +1387,7 @@ __global__ __launch_bounds__(128 * G) void k_attn8(AttnArgs args) {
   constexpr int OPS = TB / 16 / NT;     // DMA ops per thread per tile
   static_assert(OPS >= 1 && (TB / 16) % NT == 0, "tile split");
   static_assert(S >= 2 && S * OPS <= 63, "ring depth");
-  constexpr int LMAX = 2048;
+  constexpr int LMAX = ROLA_ATTN8_LMAX;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[S * TB];
   __shared__ int32_t slist[LMAX];
   __shared__ float sck[LMAX], sku[LMAX], skw[LMAX];
@@ -1497,24 +1498,40 @@ __global__ __launch_bounds__(128 * G) void k_attn8(AttnArgs args) {
 #pragma unroll
       for (int o = 0; o < OPS; ++o) lds_dma16(src + (o * NT + tid) * 16, slot + (o * NT + wave * 64) * 16);
     };
-#pragma unroll
-    for (int t = 0; t < S - 1; ++t)
+    // P tiles per barrier in an S-slot ring (S/P groups of slots): group k
+    // (tiles kP .. kP+P-1) is consumed while the next S/P-2 groups are in
+    // flight, and group k+S/P-1 is copied into the slots of group k-1.
+    constexpr int NGR = S / P;
+    static_assert(S % P == 0 && NGR >= 2, "ring of whole groups");
+    for (int t = 0; t < (NGR - 1) * P; ++t)
       if (t < U) issue(t);
-    for (int t = 0; t < U; ++t) {
-      wait_tiles<OPS, S - 2>(min(S - 2, U - 1 - t));
+    auto entry = [&](int t) __attribute__((always_inline)) -> int {
+      if constexpr (FROM_LDS) return slist[t];
+      else return list[t];
+    };
+    for (int t2 = 0; t2 < U; t2 += P) {
+      // tiles t2 .. t2+P-1 complete; the tiles copied after them (up to
+      // t2 + (NGR-1)*P - 1) may be in flight
+      wait_tiles<OPS, (NGR - 2) * P>(min((NGR - 2) * P, U - (t2 + P)));
       barrier_lds();
-      int ent;
+      uint32_t mm = 0;  // this wave's membership over the group
+#pragma unroll
+      for (int u = 0; u < P; ++u)
+        if (t2 + u < U && active && ((entry(t2 + u) >> (16 + member)) & 1)) mm |= 1u << u;
+      const int tn = t2 + (NGR - 1) * P;  // first tile of the group to copy now
+      if (!mm) {
+        for (int u = 0; u < P; ++u)
+          if (tn + u < U) issue(tn + u);
+        continue;
+      }
+      for (int t = t2; t < min(t2 + P, U); ++t) {
+      if (!((mm >> (t - t2)) & 1)) continue;
+      const int ent = entry(t);
       float ck, ku, kw;
       if constexpr (FROM_LDS) {
-        ent = slist[t];
         ck = sck[t]; ku = sku[t]; kw = skw[t];
       } else {
-        ent = list[t];
         consts(ent & 0xffff, ck, ku, kw);
-      }
-      if (!active || !((ent >> (16 + member)) & 1)) {
-        if (t + S - 1 < U) issue(t + S - 1);
-        continue;
       }
       const int j = ent & 0xffff;
       const uint8_t *tile = ring + (t % S) * TB;
@@ -1578,7 +1595,9 @@ __global__ __launch_bounds__(128 * G) void k_attn8(AttnArgs args) {
         oacc[dt] = mfma_fp8(va, phi8, oacc[dt]);
         oacc[dt] = mfma_fp8(va, plo8, oacc[dt]);
       }
-      if (t + S - 1 < U) issue(t + S - 1);
+      }
+      for (int u = 0; u < P; ++u)
+        if (tn + u < U) issue(tn + u);
     }
   };
   if (U <= LMAX) main_loop(std::integral_constant<bool, true>{});
