@@ -609,8 +609,20 @@ __global__ __launch_bounds__(256) void k_state_reduce(const float *__restrict__ 
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= stride) return;
   const float *p = part + (int64_t)bh * nchunks * 2 * stride + idx;
-  float acc = 0.0f;
-  for (int c = 0; c < 2 * nchunks; ++c) acc += p[(int64_t)c * stride];
+  // fixed order: eight interleaved partial sums (partial i takes partials
+  // i, i+8, ...), then combined pairwise; independent loads keep the
+  // memory pipeline full
+  float acc8[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc8[i] = 0.0f;
+  const int np = 2 * nchunks;
+  int c = 0;
+  for (; c + 8 <= np; c += 8) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc8[i] += p[(int64_t)(c + i) * stride];
+  }
+  for (int i = 0; c + i < np; ++i) acc8[i] += p[(int64_t)(c + i) * stride];
+  const float acc = ((acc8[0] + acc8[1]) + (acc8[2] + acc8[3])) + ((acc8[4] + acc8[5]) + (acc8[6] + acc8[7]));
   if (idx < D * 32) {
     const int d = idx / 32, r = idx % 32;
     const int w = r & 15;
