@@ -50,6 +50,7 @@ def parse():
     ap.add_argument("--workload", default="wan14b_720p")
     ap.add_argument("--topk", type=float, default=None, help="override the workload's keep ratio")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the MFMA-probe and copy measurements")
     ap.add_argument("--cpu-baseline-child", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--sample-stride", type=int, default=1,
                     help="CPU baseline: every n-th query block of one head")
@@ -121,6 +122,44 @@ def cpu_baseline(args, w):
 
 
 # -------------------------------------------------------------------- main
+def measured_peaks(rola, torch, stream, dtype):
+    """Sustained MFMA rate (probe kernel of independent MFMA chains on every
+    SIMD) and device-to-device copy bandwidth, timed with events on `stream`;
+    best of three runs each.  The shader clock comes from the probe's core and
+    reference clock counters (reference clock taken as 100 MHz)."""
+    sink = torch.zeros(2048, dtype=torch.float32, device="cuda")
+    out = {"mfma_tflops": {}}
+    for name, prec, iters in (("bf16", rola.ROLA_PREC_BF16, 20000), ("fp8", rola.ROLA_PREC_FP8, 10000)):
+        best = 0.0
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            flop = rola.mfma_probe(prec, iters, sink, stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            best = max(best, flop / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+        out["mfma_tflops"][name] = round(best, 1)
+        ticks = sink[1024:1026].cpu().tolist()
+        out["clock_ghz_" + name] = round(ticks[0] / ticks[1] * 0.1, 3) if ticks[1] > 0 else None
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    best = 0.0
+    with torch.cuda.stream(stream):
+        for _ in range(4):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            dst.copy_(src)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            best = max(best, 2 * nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    out["copy_gbs"] = round(best, 1)
+    out["copy_bytes"] = 2 * nbytes
+    out["spec"] = {"mfma_tflops": PEAK_FP8_TFLOPS if dtype == "fp8" else PEAK_BF16_TFLOPS, "hbm_gbs": PEAK_HBM_GBS}
+    del src, dst
+    return out
+
+
 def main():
     args = parse()
     if args.cpu_baseline_child:
@@ -192,10 +231,12 @@ def main():
             tr = json.load(f)
         if tr.get("kernel_source_hash") == kernel_source_hash() and tr.get("workload") == w.name:
             traffic = round(tr["bytes_per_launch"]["total"])
-    # algorithmic HBM bytes of the streaming pass: read Q, K, V once
+    # algorithmic HBM bytes of the streaming pass: read Q, K, V once; in fp8 mode
+    # also write the e4m3 codes of K and V (one byte per element)
     n_tok = w.batch * w.heads * w.n_pad
-    pass1_bytes = 3 * n_tok * w.head_dim * 2
-    pass1_ms = kern_ms.get("pass1_pool_state")
+    pass1_name = "pass1_pool_state_quant8" if fp8 else "pass1_pool_state"
+    pass1_bytes = 3 * n_tok * w.head_dim * 2 + (2 * n_tok * w.head_dim if fp8 else 0)
+    pass1_ms = kern_ms.get(pass1_name)
     rec = {
         "metric": METRIC,
         "value": round(kept / (ms * 1e-3) / 1e12, 2),
@@ -222,8 +263,15 @@ def main():
     }
     if pass1_ms:
         gbs = pass1_bytes / (pass1_ms * 1e-3) / 1e9
-        rec["pass1_roofline"] = {"kernel": "pass1_pool_state", "bound": "hbm", "achieved": round(gbs, 1),
+        rec["pass1_roofline"] = {"kernel": pass1_name, "bound": "hbm", "achieved": round(gbs, 1),
                                  "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    if not args.no_peaks:
+        print("[bench] measured peaks (MFMA probe, device copy)", file=sys.stderr, flush=True)
+        rec["measured_peaks"] = measured_peaks(rola, torch, stream, "fp8" if fp8 else "bf16")
+        mp = rec["measured_peaks"]
+        rec["roofline"]["frac_of_measured"] = round(achieved / mp["mfma_tflops"]["fp8" if fp8 else "bf16"], 4)
+        if "pass1_roofline" in rec:
+            rec["pass1_roofline"]["frac_of_measured"] = round(rec["pass1_roofline"]["achieved"] / mp["copy_gbs"], 4)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle, 1 thread, sampled)", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(args, w)

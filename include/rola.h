@@ -164,6 +164,24 @@ typedef struct rola_kernel_time {
 int32_t rola_timing_enable(int32_t on);
 int32_t rola_timing_read(rola_kernel_time *out, int32_t max);
 
+/*
+ * Measurement helper (not part of RoLA): launches, on `stream`, a kernel
+ * that keeps every SIMD's matrix core busy with independent MFMA chains --
+ * precision ROLA_PREC_BF16: v_mfma_f32_32x32x16_bf16, ROLA_PREC_FP8:
+ * v_mfma_f32_32x32x64_f8f6f4 (e4m3) -- for `iters` steps per chain, and
+ * writes the number of floating-point operations it performs to *flop.
+ * The caller times it with events on the same stream to obtain the MFMA
+ * rate the device sustains, next to its datasheet peak.  The only device
+ * memory written is `sink` (device memory of at least 8192 bytes, owned by
+ * the caller): one float per workgroup in sink[0..1023], then the ticks of
+ * the core clock (s_memtime) and of the constant reference clock
+ * (s_memrealtime) that the first wave spent, as floats in sink[1024] and
+ * sink[1025]; their ratio times the reference frequency is the shader clock
+ * during the run.  Returns ROLA_ERR_INVALID_ARG
+ * for a bad precision, iters < 1 or a NULL pointer; launches nothing then.
+ */
+int32_t rola_mfma_probe(int32_t precision, int32_t iters, double *flop, float *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

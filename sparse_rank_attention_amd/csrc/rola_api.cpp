@@ -407,6 +407,16 @@ int32_t rola_forward(const rola_problem *prob, const rola_config *cfg, const voi
   return run_attn(P, prob, cfg, q, k, v, map, out, ws, true, true, false, st);
 }
 
+int32_t rola_mfma_probe(int32_t precision, int32_t iters, double *flop, float *sink, void *stream) {
+  if (!flop || !sink || iters < 1) return ROLA_ERR_INVALID_ARG;
+  if (precision != ROLA_PREC_BF16 && precision != ROLA_PREC_FP8) return ROLA_ERR_INVALID_ARG;
+  const int blocks = 1024;  // 4 waves each: 16 waves per CU on 256 CUs
+  const double per_mfma = precision == ROLA_PREC_FP8 ? 2.0 * 32 * 32 * 64 : 2.0 * 32 * 32 * 16;
+  *flop = per_mfma * 4.0 * (double)iters * 4.0 * blocks;
+  rola::launch_mfma_probe(precision == ROLA_PREC_FP8, iters, blocks, sink, (hipStream_t)stream);
+  return hipGetLastError() == hipSuccess ? ROLA_OK : ROLA_ERR_DEVICE;
+}
+
 int32_t rola_timing_enable(int32_t on) {
   std::lock_guard<std::mutex> lk(g_mu);
   g_timing = on != 0;

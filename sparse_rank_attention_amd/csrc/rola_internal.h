@@ -108,6 +108,7 @@ int attn_group_size();
 void launch_attn(const AttnArgs &a, int D, bool sparse, bool lowrank, bool accum, bool outf32,
                  hipStream_t st);
 void launch_quant8(const Quant8Args &a, int D, int bh, hipStream_t st);
+void launch_mfma_probe(bool fp8, int iters, int blocks, float *sink, hipStream_t st);
 void launch_attn8(const AttnArgs &a, int D, bool lowrank, bool accum, bool outf32, hipStream_t st);
 
 }  // namespace rola

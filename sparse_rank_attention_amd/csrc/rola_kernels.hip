@@ -1629,6 +1629,48 @@ __global__ __launch_bounds__(128 * G) void k_attn8(AttnArgs args) {
   attn_finish<D, LOWRANK, ACCUM, OUTF32>(args, qlr, oacc, n, base, bh, lane);
 }
 
+// ------------------------------------------------------------ k_mfma_probe
+// Four independent MFMA chains per wave on constant operands (measurement of
+// the sustained matrix-core rate); lane 0 of wave 0 keeps one result alive.
+template <bool FP8>
+__global__ __launch_bounds__(256) void k_mfma_probe(int iters, float *__restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t c0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+  f32x16 a0 = f32x16{}, a1 = f32x16{}, a2 = f32x16{}, a3 = f32x16{};
+  if constexpr (FP8) {
+    const i32x8 x = {0x38383838 + lane, 0x30303030, 0x38383838, 0x30303030,
+                     0x38383838, 0x30303030, 0x38383838, 0x30303030};
+    for (int i = 0; i < iters; ++i) {
+      a0 = mfma_fp8(x, x, a0);
+      a1 = mfma_fp8(x, x, a1);
+      a2 = mfma_fp8(x, x, a2);
+      a3 = mfma_fp8(x, x, a3);
+    }
+  } else {
+    bf16x8 x;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = (__bf16)(0.001f * (float)(lane + e));
+    for (int i = 0; i < iters; ++i) {
+      a0 = mfma_bf16(x, x, a0);
+      a1 = mfma_bf16(x, x, a1);
+      a2 = mfma_bf16(x, x, a2);
+      a3 = mfma_bf16(x, x, a3);
+    }
+  }
+  const float r = a0[0] + a1[1] + a2[2] + a3[3];
+  const uint64_t c1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+  if (threadIdx.x == 0) sink[blockIdx.x] = r;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {  // core-clock and reference-clock ticks of this wave
+    sink[1024] = (float)(c1 - c0);
+    sink[1025] = (float)(r1 - r0);
+  }
+}
+
+void launch_mfma_probe(bool fp8, int iters, int blocks, float *sink, hipStream_t st) {
+  if (fp8) hipLaunchKernelGGL(k_mfma_probe<true>, dim3(blocks), dim3(256), 0, st, iters, sink);
+  else hipLaunchKernelGGL(k_mfma_probe<false>, dim3(blocks), dim3(256), 0, st, iters, sink);
+}
+
 // ---------------------------------------------------------------- launchers
 void launch_setup(const SetupArgs &a, hipStream_t st) {
   hipLaunchKernelGGL(k_setup, dim3((32 * a.D + 255) / 256), dim3(256), 0, st, a.wq, a.wk, a.D, a.rank,

@@ -47,7 +47,7 @@ class RolaKernelTime(ctypes.Structure):
 
 EXPORTS = ["rola_abi_version", "rola_status_str", "rola_plan", "rola_select_blocks",
            "rola_sparse_attn", "rola_lowrank_attn", "rola_forward", "rola_timing_enable",
-           "rola_timing_read"]
+           "rola_timing_read", "rola_mfma_probe"]
 
 _lib = None
 
@@ -83,6 +83,8 @@ def lib():
         L.rola_timing_enable.argtypes = [I32]
         L.rola_timing_read.restype = I32
         L.rola_timing_read.argtypes = [P, I32]
+        L.rola_mfma_probe.restype = I32
+        L.rola_mfma_probe.argtypes = [I32, I32, P, P, P]
         _lib = L
     return _lib
 
@@ -220,6 +222,14 @@ def rola_forward(q, k, v, wq, wk, grid, cfg: Config, out=None, block_idx_out=Non
                               _ptr(wk), _ptr(block_idx_out), _ptr(out), _ptr(ws), ws.numel(),
                               _stream(stream)), "rola_forward")
     return out
+
+
+def mfma_probe(precision: int, iters: int, sink, stream=None) -> float:
+    """Launch the MFMA-rate probe on the stream; returns its flop count (time it with events)."""
+    flop = ctypes.c_double(0.0)
+    _check(lib().rola_mfma_probe(precision, iters, ctypes.byref(flop), _ptr(sink), _stream(stream)),
+           "rola_mfma_probe")
+    return flop.value
 
 
 def timing_enable(on: bool):

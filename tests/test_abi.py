@@ -104,6 +104,17 @@ def test_entry_points_validate_before_launch():
     assert L.rola_status_str(4) == b"workspace missing or too small"
 
 
+def test_mfma_probe_validates_before_launch():
+    L = rola.lib()
+    flop = ctypes.c_double(-1.0)
+    fake = ctypes.c_void_p(0x10000)
+    assert L.rola_mfma_probe(rola.ROLA_PREC_BF16, 0, P(flop), fake, None) == 1
+    assert L.rola_mfma_probe(7, 100, P(flop), fake, None) == 1
+    assert L.rola_mfma_probe(rola.ROLA_PREC_FP8, 100, None, fake, None) == 1
+    assert L.rola_mfma_probe(rola.ROLA_PREC_FP8, 100, P(flop), None, None) == 1
+    assert flop.value == -1.0
+
+
 def test_timing_read_without_launches_is_empty():
     assert rola.lib().rola_timing_read(None, 4) == -1
     assert rola.timing_read() == {}
