@@ -1165,9 +1165,11 @@ __global__ __launch_bounds__(128 * G) void k_attn(AttnArgs args) {
           }
         }
       };
-      // Two tiles per barrier: iteration k consumes tiles 2k and 2k+1 and
-      // copies 2k+2 and 2k+3 into the slots of 2k-2 and 2k-1.  A SIMD loaded
-      // on one tile and idle on the other evens out within the pair.
+      // Two tiles per barrier: iteration k consumes tiles 2k and 2k+1 and,
+      // before computing, copies 2k+2 and 2k+3 into the slots of 2k-2 and
+      // 2k-1 (free once every wave has passed the barrier), so each copy has
+      // a whole iteration to land.  A SIMD loaded on one tile and idle on the
+      // other evens out within the pair.
       static_assert(S == 4, "two tiles per barrier in a four-slot ring");
 #pragma unroll
       for (int t = 0; t < 2; ++t)
@@ -1175,15 +1177,12 @@ __global__ __launch_bounds__(128 * G) void k_attn(AttnArgs args) {
       for (int t2 = 0; t2 < U; t2 += 2) {
         wait_vmcnt<0>();  // this wave's copies of tiles t2, t2+1
         barrier_lds();    // both visible to all waves; every wave is done with t2-2, t2-1
+        if (t2 + 2 < U) issue(t2 + 2);
+        if (t2 + 3 < U) issue(t2 + 3);
         const int e0 = entry(t2), e1 = t2 + 1 < U ? entry(t2 + 1) : 0;
         const bool m0 = active && ((e0 >> (16 + member)) & 1);
         const bool m1 = active && ((e1 >> (16 + member)) & 1);
-        if (!m0 && !m1) {
-          // waves idle on both tiles copy their share of the next pair at once
-          if (t2 + 2 < U) issue(t2 + 2);
-          if (t2 + 3 < U) issue(t2 + 3);
-          continue;
-        }
+        if (!m0 && !m1) continue;
         for (int t = t2; t < min(t2 + 2, U); ++t) {
         const int ent = t == t2 ? e0 : e1;
         if (!(t == t2 ? m0 : m1)) continue;
@@ -1267,9 +1266,6 @@ __global__ __launch_bounds__(128 * G) void k_attn(AttnArgs args) {
         }
         l_run += psum;
         }
-        // this wave's share of the next pair, after its compute
-        if (t2 + 2 < U) issue(t2 + 2);
-        if (t2 + 3 < U) issue(t2 + 3);
       }
     };
     if (U <= LMAX) main_loop(std::integral_constant<bool, true>{});
@@ -1511,8 +1507,9 @@ __global__ __launch_bounds__(128 * G) void k_attn8(AttnArgs args) {
       for (int o = 0; o < OPS; ++o) lds_dma16(src + (o * NT + tid) * 16, slot + (o * NT + wave * 64) * 16);
     };
     // P tiles per barrier in an S-slot ring (S/P groups of slots): group k
-    // (tiles kP .. kP+P-1) is consumed while the next S/P-2 groups are in
-    // flight, and group k+S/P-1 is copied into the slots of group k-1.
+    // (tiles kP .. kP+P-1) is consumed while the next S/P-1 groups are in
+    // flight; group k+S/P-1 is copied into the slots of group k-1 right after
+    // the barrier that frees them, before the compute.
     constexpr int NGR = S / P;
     static_assert(S % P == 0 && NGR >= 2, "ring of whole groups");
     for (int t = 0; t < (NGR - 1) * P; ++t)
@@ -1531,11 +1528,9 @@ __global__ __launch_bounds__(128 * G) void k_attn8(AttnArgs args) {
       for (int u = 0; u < P; ++u)
         if (t2 + u < U && active && ((entry(t2 + u) >> (16 + member)) & 1)) mm |= 1u << u;
       const int tn = t2 + (NGR - 1) * P;  // first tile of the group to copy now
-      if (!mm) {
-        for (int u = 0; u < P; ++u)
-          if (tn + u < U) issue(tn + u);
-        continue;
-      }
+      for (int u = 0; u < P; ++u)
+        if (tn + u < U) issue(tn + u);
+      if (!mm) continue;
       for (int t = t2; t < min(t2 + P, U); ++t) {
       if (!((mm >> (t - t2)) & 1)) continue;
       const int ent = entry(t);
@@ -1608,8 +1603,6 @@ __global__ __launch_bounds__(128 * G) void k_attn8(AttnArgs args) {
         oacc[dt] = mfma_fp8(va, plo8, oacc[dt]);
       }
       }
-      for (int u = 0; u < P; ++u)
-        if (tn + u < U) issue(tn + u);
     }
   };
   if (U <= LMAX) main_loop(std::integral_constant<bool, true>{});
