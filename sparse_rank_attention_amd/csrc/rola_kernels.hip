@@ -223,13 +223,16 @@ static __device__ __forceinline__ bf16x8 vt_operand_at(const uint16_t *p, int ha
 // lookups (global loads) are needed inside the streaming loops.
 using RopeArgsDev = RopeArgsHost;
 
+// (t, h, w) of token n; n < 2^31 (the planner caps N far below), so the
+// divisions are 32-bit
 static __device__ __forceinline__ void token_pos(int64_t n, const RopeArgsDev &ra, int &pt, int &ph,
                                                  int &pw) {
-  const int hw = ra.grid_h * ra.grid_w;
-  pt = (int)(n / hw);
-  const int rem = (int)(n - (int64_t)pt * hw);
-  ph = rem / ra.grid_w;
-  pw = rem - ph * ra.grid_w;
+  const uint32_t hw = (uint32_t)(ra.grid_h * ra.grid_w), gw = (uint32_t)ra.grid_w;
+  const uint32_t n32 = (uint32_t)n;
+  const uint32_t t = n32 / hw, rem = n32 - t * hw, hh = rem / gw;
+  pt = (int)t;
+  ph = (int)hh;
+  pw = (int)(rem - hh * gw);
 }
 
 // inverse frequency of the pair starting at even dim d
@@ -958,7 +961,7 @@ __global__ __launch_bounds__(64 * kUnionWaves) void k_union(const int32_t *__res
 template <int D, bool LOWRANK, bool ACCUM, bool OUTF32>
 static __device__ __forceinline__ void attn_finish(const AttnArgs &args, const bf16x8 *qreg,
                                                    f32x16 *oacc, int64_t n, int64_t base, int bh,
-                                                   int lane) {
+                                                   int lane, const float *sfreq) {
   constexpr int NS = D / 16;
   constexpr int DT = D / 32;
   const int g = lane >> 5;
@@ -969,21 +972,24 @@ static __device__ __forceinline__ void attn_finish(const AttnArgs &args, const b
     f32x16 aacc = f32x16{};
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      float freq[4];
-#pragma unroll
-      for (int p = 0; p < 4; ++p) freq[p] = rope_freq(16 * s + 8 * g + 2 * p, args.rope);
+      const f32x4 fr = *(const f32x4 *)&sfreq[8 * s + 4 * g];  // pairs of dims 16s + 8g .. +8
+      const float freq[4] = {fr[0], fr[1], fr[2], fr[3]};
       const bf16x8 qr = rope8(qreg[s], 16 * s + 8 * g, pt, ph, pw, freq, args.rope);
       const bf16x8 wa = *(const bf16x8 *)(args.wqT + (lane & 31) * D + 16 * s + 8 * g);
       aacc = mfma_bf16(wa, qr, aacc);
     }
-    const float *zb = args.z + (int64_t)bh * 32;
+    const f32x4 *zb = (const f32x4 *)(args.z + (int64_t)bh * 32);
     float den = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = 8 * (i >> 2) + 4 * g + (i & 3);
-      const float a = r < args.rank ? phi(aacc[i]) : 0.0f;
-      aacc[i] = a;
-      den += a * zb[r];
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 zq = zb[2 * q + g];  // z[8q + 4g .. +4]
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = 4 * q + j, r = 8 * q + 4 * g + j;
+        const float a = r < args.rank ? phi(aacc[i]) : 0.0f;
+        aacc[i] = a;
+        den += a * zq[j];
+      }
     }
     den += shfl_xor32(den);
     const float inv_den = 1.0f / den;
@@ -1066,6 +1072,7 @@ __global__ __launch_bounds__(128 * G) void k_attn(AttnArgs args) {
   constexpr int LMAX = 2048;  // union-list entries staged in LDS (longer lists read the tail from HBM)
   __shared__ __attribute__((aligned(1024))) uint16_t ring[SPARSE ? S * 2 * TILE : 8];
   __shared__ int32_t slist[SPARSE ? LMAX : 1];
+  __shared__ __attribute__((aligned(16))) float sfreq[D / 2];  // rotary inverse frequency per pair
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, g = lane >> 5;
@@ -1097,6 +1104,8 @@ __global__ __launch_bounds__(128 * G) void k_attn(AttnArgs args) {
 #pragma unroll
   for (int i = 0; i < DT; ++i) oacc[i] = f32x16{};
   float m_run = -INFINITY, l_run = 0.0f;
+  for (int p2 = tid; p2 < D / 2; p2 += NT) sfreq[p2] = rope_freq(2 * p2, args.rope);
+  if (!SPARSE) __syncthreads();  // the sparse path's list staging synchronises
 
   if (SPARSE) {
     const int32_t *list = args.ulist + gidx * args.list_stride;
@@ -1276,7 +1285,7 @@ __global__ __launch_bounds__(128 * G) void k_attn(AttnArgs args) {
     for (int dt = 0; dt < DT; ++dt) oacc[dt] *= inv_l;
   }
   if (!active) return;
-  attn_finish<D, LOWRANK, ACCUM, OUTF32>(args, qreg, oacc, n, base, bh, lane);
+  attn_finish<D, LOWRANK, ACCUM, OUTF32>(args, qreg, oacc, n, base, bh, lane, sfreq);
 }
 
 // ---------------------------------------------------------------- k_quant8
@@ -1400,6 +1409,7 @@ __global__ __launch_bounds__(128 * G) void k_attn8(AttnArgs args) {
   __shared__ int32_t slist[LMAX];
   __shared__ float sck[LMAX], sku[LMAX], skw[LMAX];
   __shared__ float sred[2 * G];
+  __shared__ __attribute__((aligned(16))) float sfreq[D / 2];  // rotary inverse frequency per pair
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, g = lane >> 5;
@@ -1428,6 +1438,7 @@ __global__ __launch_bounds__(128 * G) void k_attn8(AttnArgs args) {
   const float *ksc = args.ksc + (int64_t)bh * args.nb;
   const float *vsc = args.vsc + (int64_t)bh * args.nb;
   // sigma: the largest V scale on the list
+  for (int p2 = tid; p2 < D / 2; p2 += NT) sfreq[p2] = rope_freq(2 * p2, args.rope);
   float vmax = 0.0f;
   for (int t = tid; t < U; t += NT) vmax = fmaxf(vmax, vsc[list[t] & 0xffff]);
 #pragma unroll
@@ -1619,7 +1630,7 @@ __global__ __launch_bounds__(128 * G) void k_attn8(AttnArgs args) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) qlr[s] = *(const bf16x8 *)(qrow + 16 * s + 8 * g);
   }
-  attn_finish<D, LOWRANK, ACCUM, OUTF32>(args, qlr, oacc, n, base, bh, lane);
+  attn_finish<D, LOWRANK, ACCUM, OUTF32>(args, qlr, oacc, n, base, bh, lane, sfreq);
 }
 
 // ------------------------------------------------------------ k_mfma_probe
