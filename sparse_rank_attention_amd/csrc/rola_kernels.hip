@@ -902,8 +902,14 @@ __global__ __launch_bounds__(64) void k_group(const int32_t *__restrict__ map, i
 
 // ---------------------------------------------------------------- k_union
 // One wave per group: the members' maps are folded into per-key-block member
-// masks in LDS (4 key blocks per word, one byte each), then compacted in
-// ascending key-block order into the group's list of (key block | mask << 16).
+// masks in LDS (4 key blocks per word, one byte each), then compacted into
+// the group's list of (key block | mask << 16).  The attention kernels take
+// the list two tiles per barrier, and their SIMDs host members {0, 2} and
+// {1, 3} in pairs, so the list is ordered to give each consecutive pair of
+// tiles an even load on the two SIMD pairs: entries are ranked by
+// d = |mask & {0,2}| - |mask & {1,3}| (stable in key-block order), and the
+// ranked sequence is emitted from both ends alternately (lowest, highest,
+// second lowest, second highest, ...).
 constexpr int kUnionWaves = 8;
 
 __global__ __launch_bounds__(64 * kUnionWaves) void k_union(const int32_t *__restrict__ map, int nb,
@@ -928,30 +934,57 @@ __global__ __launch_bounds__(64 * kUnionWaves) void k_union(const int32_t *__res
     const int j = min(max(mb[(int64_t)qb * kb + t], 0), nb - 1);
     atomicOr(&mw[j >> 2], 1u << ((j & 3) * 8 + m));
   }
-  // ascending compaction: lane owns words [lane*per, lane*per + per)
+  // lane owns words [lane*per, lane*per + per); per-lane counts per rank
+  // class d + 2 in 0..4, then exclusive scans across lanes
+  auto dclass = [](uint32_t msk) -> int {
+    return __builtin_popcount(msk & 5u) - __builtin_popcount(msk & 10u) + 2;
+  };
   const int per = (nbw + 63) / 64;
-  int cnt = 0;
+  int cnt[5] = {0, 0, 0, 0, 0};
   for (int w = lane * per; w < min(nbw, lane * per + per); ++w) {
     const uint32_t x = mw[w];
-    cnt += ((x & 0xffu) != 0) + ((x & 0xff00u) != 0) + ((x & 0xff0000u) != 0) + ((x >> 24) != 0);
-  }
-  int incl = cnt;
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += y;
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t msk = (x >> (8 * q)) & 0xffu;
+      if (msk) {
+        const int dc = dclass(msk);
+#pragma unroll
+        for (int c = 0; c < 5; ++c) cnt[c] += (dc == c);
+      }
+    }
   }
-  int pos = incl - cnt;
+  int rank[5], base = 0, U = 0;
+#pragma unroll
+  for (int c = 0; c < 5; ++c) {
+    int incl = cnt[c];
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
+    }
+    const int total = __shfl(incl, 63, 64);
+    rank[c] = base + incl - cnt[c];  // this lane's first sorted index in class c
+    base += total;
+  }
+  U = base;
   int32_t *out = ulist + gidx * list_stride;
   for (int w = lane * per; w < min(nbw, lane * per + per); ++w) {
     const uint32_t x = mw[w];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const uint32_t msk = (x >> (8 * q)) & 0xffu;
-      if (msk) out[pos++] = (4 * w + q) | (int)(msk << 16);
+      if (msk) {
+        const int dc = dclass(msk);
+        int i = 0;
+#pragma unroll
+        for (int c = 0; c < 5; ++c)
+          if (dc == c) i = rank[c]++;
+        const int pos = i < (U + 1) / 2 ? 2 * i : 2 * (U - 1 - i) + 1;
+        out[pos] = (4 * w + q) | (int)(msk << 16);
+      }
     }
   }
-  if (lane == 63) ucount[gidx] = incl;
+  if (lane == 0) ucount[gidx] = U;
 }
 
 // Epilogue shared by the bf16 and fp8 attention kernels: low-rank apply
