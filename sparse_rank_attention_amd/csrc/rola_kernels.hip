@@ -133,6 +133,28 @@ static __device__ __forceinline__ void lds_dma16_s(const void *base_ptr, uint32_
       : "memory");
 }
 
+// The same copy with the LDS destination given as a byte address in LDS
+// (wave-uniform, formed by scalar arithmetic from the ring's base) and the
+// global base in an SGPR pair.
+static __device__ __forceinline__ void lds_dma16_m0(const void *sbase, uint32_t voff, uint32_t m0) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(m0), "v"(voff), "s"(sbase)
+      : "memory");
+}
+
+// LDS byte address of a shared array element (the array's own address space
+// is LDS, so no null check is generated)
+template <typename T>
+static __device__ __forceinline__ uint32_t lds_addr(const T *p) {
+  return (uint32_t)(uintptr_t)(const LDS_AS void *)p;
+}
+
 // LDS tile layouts: row-major [64 rows][D] bf16 in 16-byte chunks, chunk c
 // of row r stored at c ^ swizzle(r).  K tiles (read as 16-byte MFMA rows)
 // use r & 7; V tiles (read transposed, 8 bytes per lane) use 2*(r & 3).
@@ -1157,6 +1179,8 @@ __global__ __launch_bounds__(128 * G) void k_attn(AttnArgs args) {
     // V^T transposed-read rows 4g + (l%16)/4 (+16 per k-step, +8 for the
     // second half), dims 32dt + 16((l/16)%2) + 4(l%4)
     int koff[NS], voff[DT];
+    const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_addr(ring));
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
     uint32_t gk[OPS], gv[OPS];  // this lane's byte offsets inside a key block
 #pragma unroll
     for (int o = 0; o < OPS; ++o) {
@@ -1189,10 +1213,11 @@ __global__ __launch_bounds__(128 * G) void k_attn(AttnArgs args) {
         const int64_t jrow = (int64_t)j * 64;
         if (jrow + 64 <= args.n_tokens) {
           const uint16_t *kj = Kb + jrow * args.stride_n, *vj = Vb + jrow * args.stride_n;
+          const uint32_t m0 = ring_lds + (uint32_t)((t % S) * (2 * TILE) * 2) + (uint32_t)wave_s * 1024u;
 #pragma unroll
           for (int o = 0; o < OPS; ++o) {
-            lds_dma16_s(kj, gk[o], slot + (o * NT + wave * 64) * 8);
-            lds_dma16_s(vj, gv[o], slot + TILE + (o * NT + wave * 64) * 8);
+            lds_dma16_m0(kj, gk[o], m0 + (uint32_t)(o * NT * 16));
+            lds_dma16_m0(vj, gv[o], m0 + (uint32_t)(TILE * 2 + o * NT * 16));
           }
         } else {
 #pragma unroll
@@ -1538,6 +1563,8 @@ __global__ __launch_bounds__(128 * G) void k_attn8(AttnArgs args) {
     return i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
   };
   const uint8_t *img = args.kv8 + (int64_t)bh * args.nb * TB;
+  const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_addr(ring));
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
 
   auto main_loop = [&](auto lds_tag) {
     constexpr bool FROM_LDS = decltype(lds_tag)::value;
@@ -1545,10 +1572,11 @@ __global__ __launch_bounds__(128 * G) void k_attn8(AttnArgs args) {
       int j;
       if constexpr (FROM_LDS) j = slist[t] & 0xffff;
       else j = list[t] & 0xffff;
+      j = __builtin_amdgcn_readfirstlane(j);
       const uint8_t *src = img + (int64_t)j * TB;
-      uint8_t *slot = ring + (t % S) * TB;
+      const uint32_t m0 = ring_lds + (uint32_t)((t % S) * TB) + (uint32_t)wave_s * 1024u;
 #pragma unroll
-      for (int o = 0; o < OPS; ++o) lds_dma16(src + (o * NT + tid) * 16, slot + (o * NT + wave * 64) * 16);
+      for (int o = 0; o < OPS; ++o) lds_dma16_m0(src, (uint32_t)((o * NT + tid) * 16), m0 + (uint32_t)(o * NT * 16));
     };
     // P tiles per barrier in an S-slot ring (S/P groups of slots): group k
     // (tiles kP .. kP+P-1) is consumed while the next S/P-1 groups are in
