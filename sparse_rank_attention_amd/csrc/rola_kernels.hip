@@ -774,14 +774,18 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ s, int32
 }
 
 // ---------------------------------------------------------------- k_order
-// One workgroup per (batch, head): orders the query blocks by the first two
-// entries of their (ascending) block maps, so that query blocks keeping
-// similar key blocks become neighbours, and writes the groups of G members.
-// Without a map (kb == 0, low-rank only) the order is the identity.
+// Orders each (batch, head)'s query blocks by the first two entries of their
+// (ascending) block maps, so that query blocks keeping similar key blocks
+// become neighbours, and writes the groups of G members.  Without a map
+// (kb == 0, low-rank only) the order is the identity.  Rank sort: the
+// position of block i is #{j : (key_j, j) < (key_i, i)}.  Grid (ceil(nb /
+// kOrderPer), batch*heads); eight lanes share one block i, each counting a
+// strided eighth of the j, and combine their counts with shuffles.
+constexpr int kOrderPer = 128;
 __global__ __launch_bounds__(1024) void k_order(const int32_t *__restrict__ map, int nb, int kb, int G,
                                                 int ngroups, int32_t *__restrict__ ugroup) {
   extern __shared__ uint32_t key[];  // [nb]
-  const int bh = blockIdx.x;
+  const int bh = blockIdx.y;
   const int32_t *mb = kb > 0 ? map + (int64_t)bh * nb * kb : nullptr;
   for (int i = threadIdx.x; i < nb; i += blockDim.x) {
     uint32_t key_i = (uint32_t)i;
@@ -793,18 +797,22 @@ __global__ __launch_bounds__(1024) void k_order(const int32_t *__restrict__ map,
     key[i] = key_i;
   }
   __syncthreads();
-  // rank sort: position of i = #{j : (key_j, j) < (key_i, i)}
   int32_t *ug = ugroup + (int64_t)bh * ngroups * G;
-  for (int i = threadIdx.x; i < nb; i += blockDim.x) {
-    const uint32_t ki = key[i];
-    int rank = 0;
-    for (int j = 0; j < nb; ++j) {
+  const int i = blockIdx.x * kOrderPer + (int)(threadIdx.x >> 3), part = (int)(threadIdx.x & 7);
+  const uint32_t ki = i < nb ? key[i] : 0u;
+  int rank = 0;
+  if (i < nb) {
+    for (int j = part; j < nb; j += 8) {
       const uint32_t kj = key[j];
       rank += (kj < ki) || (kj == ki && j < i);
     }
-    ug[rank] = i;
   }
-  for (int p = nb + threadIdx.x; p < ngroups * G; p += blockDim.x) ug[p] = -1;
+  rank += __shfl_xor(rank, 1, 64);
+  rank += __shfl_xor(rank, 2, 64);
+  rank += __shfl_xor(rank, 4, 64);
+  if (i < nb && part == 0) ug[rank] = i;
+  if (blockIdx.x == 0)
+    for (int p = nb + threadIdx.x; p < ngroups * G; p += blockDim.x) ug[p] = -1;
 }
 
 // ---------------------------------------------------------------- k_group
@@ -820,18 +828,17 @@ __global__ __launch_bounds__(1024) void k_order(const int32_t *__restrict__ map,
 constexpr int kGroupWin = 64;
 constexpr int kGroupMaxKb = 64;
 
-// One wave per window, window position c = lane.  Scores (key blocks shared
-// with the current group's union) are kept up to date incrementally: an
-// inverted index in LDS gives, per key block, the 64-bit mask of window
-// positions whose map holds it, and each key block a new member brings into
-// the union adds one to the score of every position in its mask.  Liveness
-// is a 64-bit ballot held by every lane.  Dynamic LDS: nb masks (8 B each)
-// and the union bitset.
+// One wave per window, window position c = lane.  Each lane keeps its own
+// map (up to kGroupMaxKb key blocks) in registers; the group's union is a
+// bitset in LDS.  At every greedy step each live lane recounts its key
+// blocks present in the union (all bitset reads independent, so one LDS
+// round trip per step), and a max-reduction over the wave picks the next
+// member.  The maps are also staged in LDS so that a new member's key blocks
+// enter the union in one step (one lane per key block).  Dynamic LDS: the
+// union bitset.
 __global__ __launch_bounds__(64) void k_group(const int32_t *__restrict__ map, int nb, int kb, int G,
                                               int ngroups, int32_t *__restrict__ ugroup) {
-  extern __shared__ uint64_t gsm[];
-  uint64_t *inv = gsm;                                  // [nb]
-  uint32_t *inu = (uint32_t *)(gsm + nb);               // [ceil(nb/32)]
+  extern __shared__ uint32_t inu[];                     // [ceil(nb/32)]
   __shared__ uint16_t cmap[kGroupWin * kGroupMaxKb];    // maps of the window positions
   const int lane = threadIdx.x;
   const int bh = blockIdx.y;
@@ -843,11 +850,8 @@ __global__ __launch_bounds__(64) void k_group(const int32_t *__restrict__ map, i
   const int32_t *mb = map + (int64_t)bh * nb * kb;
   const int nwords = (nb + 31) / 32;
   const int qb = lane < wn ? ug[lane] : -1;
-  for (int j = lane; j < nb; j += 64) inv[j] = 0ull;
-  for (int w = lane; w < nwords; w += 64) inu[w] = 0u;
-  __syncthreads();
-  // index the window: position c sets bit c of inv[j] for each j it keeps
-  // (map entries e = c*kb + t spread over the lanes, four loads in flight)
+  // stage the window's maps: entries e = c*kb + t spread over the lanes,
+  // four loads in flight
   const int nent = wn * kb;
   for (int e0 = 0; e0 < nent; e0 += 256) {
     int jv[4], cv[4];
@@ -860,47 +864,39 @@ __global__ __launch_bounds__(64) void k_group(const int32_t *__restrict__ map, i
       jv[u] = cv[u] >= 0 ? mb[(int64_t)qc * kb + (e - c * kb)] : 0;
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (cv[u] >= 0) {
-        const int j = min(max(jv[u], 0), nb - 1);
-        cmap[e0 + 64 * u + lane] = (uint16_t)j;
-        atomicOr((unsigned long long *)&inv[j], 1ull << cv[u]);
-      }
-    }
+    for (int u = 0; u < 4; ++u)
+      if (cv[u] >= 0) cmap[e0 + 64 * u + lane] = (uint16_t)min(max(jv[u], 0), nb - 1);
   }
   __syncthreads();
+  // this lane's map in registers, as (word, bit) of the union bitset
+  uint32_t kw[kGroupMaxKb];
+#pragma unroll
+  for (int t = 0; t < kGroupMaxKb; ++t) {
+    const int j = (t < kb && qb >= 0) ? (int)cmap[lane * kb + t] : 0;
+    kw[t] = ((uint32_t)(j >> 5) << 5) | (uint32_t)(j & 31);
+  }
   uint64_t live = __builtin_amdgcn_ballot_w64(qb >= 0);
-  int sc = 0;  // score of position lane
-  // adds the key blocks of position c that are new to the union
+  // the key blocks of position c join the union (lane t < kb takes entry t)
   auto add_member = [&](int c) {
-    const int j = lane < kb ? (int)cmap[c * kb + lane] : 0;
-    bool fresh = false;
-    if (lane < kb) fresh = !((inu[j >> 5] >> (j & 31)) & 1u);
-    if (fresh) atomicOr(&inu[j >> 5], 1u << (j & 31));
-    uint64_t nm = __builtin_amdgcn_ballot_w64(fresh);
-    while (nm) {
-      int js[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        js[u] = -1;
-        if (nm) {
-          const int t = __builtin_ctzll(nm);
-          nm &= nm - 1;
-          js[u] = __shfl(j, t, 64);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (js[u] >= 0) sc += (int)((inv[js[u]] >> lane) & 1ull);
+    if (lane < kb) {
+      const int j = cmap[c * kb + lane];
+      atomicOr(&inu[j >> 5], 1u << (j & 31));
     }
     __syncthreads();  // the union bits are complete before the next reads
+  };
+  // key blocks of this lane's map present in the union
+  auto score = [&]() -> int {
+    int sc = 0;
+#pragma unroll
+    for (int t = 0; t < kGroupMaxKb; ++t)
+      if (t < kb) sc += (int)((inu[kw[t] >> 5] >> (kw[t] & 31)) & 1u);
+    return sc;
   };
   int32_t outv = -1;  // regrouped sequence: position p held by lane p
   int outp = 0;
   while (live) {
     const int sd = __builtin_ctzll(live);
     for (int w = lane; w < nwords; w += 64) inu[w] = 0u;
-    sc = 0;
     __syncthreads();
     const int vs = __shfl(qb, sd, 64);  // with every lane active
     if (lane == outp) outv = vs;
@@ -908,7 +904,7 @@ __global__ __launch_bounds__(64) void k_group(const int32_t *__restrict__ map, i
     add_member(sd);
     for (int members = 1; members < G && live; ++members) {
       // key = score*64 + (63 - position): most shared key blocks, then earliest
-      int best = ((live >> lane) & 1ull) ? sc * 64 + (63 - lane) : -1;
+      int best = ((live >> lane) & 1ull) ? score() * 64 + (63 - lane) : -1;
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) best = max(best, __shfl_xor(best, o, 64));
       const int c = 63 - (best & 63);
@@ -918,6 +914,7 @@ __global__ __launch_bounds__(64) void k_group(const int32_t *__restrict__ map, i
       if (members + 1 < G) add_member(c);
     }
     outp += G;
+    __syncthreads();  // every lane's score reads are done before the union is cleared
   }
   if (lane < wn) ug[lane] = outv;
 }
@@ -1790,10 +1787,11 @@ void launch_topk(const float *s, int32_t *map, int nb, int kb, int64_t rows, hip
 
 void launch_schedule(const int32_t *map, int nb, int kb, int G, int ngroups, int list_stride,
                      int bh, int32_t *ugroup, int32_t *ucount, int32_t *ulist, hipStream_t st) {
-  hipLaunchKernelGGL(k_order, dim3(bh), dim3(1024), (size_t)nb * 4, st, map, nb, kb, G, ngroups, ugroup);
+  hipLaunchKernelGGL(k_order, dim3((nb + kOrderPer - 1) / kOrderPer, bh), dim3(1024), (size_t)nb * 4, st, map, nb,
+                     kb, G, ngroups, ugroup);
   if (kb > 0 && kb <= kGroupMaxKb && kGroupWin % G == 0)
     hipLaunchKernelGGL(k_group, dim3((ngroups * G + kGroupWin - 1) / kGroupWin, bh), dim3(64),
-                       (size_t)nb * 8 + (size_t)(nb + 31) / 32 * 4, st, map, nb, kb, G, ngroups, ugroup);
+                       (size_t)(nb + 31) / 32 * 4, st, map, nb, kb, G, ngroups, ugroup);
   if (kb > 0) {
     const size_t lds = (size_t)kUnionWaves * ((nb + 3) / 4) * 4;
     hipLaunchKernelGGL(k_union, dim3((ngroups + kUnionWaves - 1) / kUnionWaves, bh), dim3(64 * kUnionWaves), lds,
