@@ -722,19 +722,41 @@ __global__ __launch_bounds__(256) void k_scores(const float *__restrict__ qp,
 
 // ----------------------------------------------------------------- k_topk
 // One wave per score row: order-preserving uint32 keys (-0.0 folded into
-// +0.0), bitwise search for the kb-th largest key T, then emit, in ascending
-// index order, every j with key > T and the lowest-index ties key == T.
+// +0.0), the kb-th largest key T, then emit, in ascending index order, every
+// j with key > T and the lowest-index ties key == T.
+//  - T comes from a bitwise search (from the top bit down, keep a bit when at
+//    least kb keys reach the prefix with it set).
+//  - For kb <= 64 the search first narrows the row: the kb-th largest of the
+//    64 lane maxima, T_sub, is at most T (those maxima are a subset of the
+//    row), so every key >= T is a key >= T_sub.  When at most 128 keys reach
+//    T_sub they are compacted into two per lane through LDS and the search
+//    runs over them alone; otherwise over the whole row.
 static __device__ __forceinline__ uint32_t order_key(float x) {
   uint32_t u = __float_as_uint(x);
   if (u == 0x80000000u) u = 0u;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// the kb-th largest of the wave's keys k[0..N) (all lanes), by bitwise search
+template <int N>
+static __device__ __forceinline__ uint32_t kth_largest(const uint32_t *k, int kb) {
+  uint32_t prefix = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = prefix | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int m = 0; m < N; ++m) cnt += __popcll(__ballot(k[m] >= cand));
+    if (cnt >= kb) prefix = cand;
+  }
+  return prefix;
+}
+
 template <int PER>
 __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ s, int32_t *__restrict__ map,
                                               int nb, int kb, int64_t rows) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  __shared__ uint32_t cand[4][128];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * 4 + w;
   if (row >= rows) return;
   const float *sr = s + row * nb;
   uint32_t key[PER];
@@ -743,15 +765,35 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ s, int32
     const int j = m * 64 + lane;
     key[m] = j < nb ? order_key(sr[j]) : 0u;  // real keys are >= 0x007fffff
   }
-  uint32_t prefix = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = prefix | (1u << bit);
-    int cnt = 0;
+  uint32_t T;
+  bool narrowed = false;
+  if (kb <= 64) {
+    uint32_t mx = 0;
 #pragma unroll
-    for (int m = 0; m < PER; ++m) cnt += __popcll(__ballot(key[m] >= cand));
-    if (cnt >= kb) prefix = cand;
+    for (int m = 0; m < PER; ++m) mx = max(mx, key[m]);
+    const uint32_t tsub = kth_largest<1>(&mx, kb);
+    int total = 0;
+#pragma unroll
+    for (int m = 0; m < PER; ++m) total += __popcll(__ballot(key[m] >= tsub));
+    if (total <= 128) {
+      int base = 0;
+#pragma unroll
+      for (int m = 0; m < PER; ++m) {
+        const bool c = key[m] >= tsub;
+        const uint64_t cm = __ballot(c);
+        const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(cm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)cm, 0u));
+        if (c) cand[w][base + (int)below] = key[m];
+        base += __popcll(cm);
+      }
+      __builtin_amdgcn_wave_barrier();
+      uint32_t ck[2];
+      ck[0] = lane < total ? cand[w][lane] : 0u;
+      ck[1] = 64 + lane < total ? cand[w][64 + lane] : 0u;
+      T = kth_largest<2>(ck, kb);
+      narrowed = true;
+    }
   }
-  const uint32_t T = prefix;
+  if (!narrowed) T = kth_largest<PER>(key, kb);
   int greater = 0;
 #pragma unroll
   for (int m = 0; m < PER; ++m) greater += __popcll(__ballot(key[m] > T));
