@@ -259,10 +259,11 @@ static __device__ __forceinline__ void token_pos(int64_t n, const RopeArgsDev &r
 
 // inverse frequency of the pair starting at even dim d
 static __device__ __forceinline__ float rope_freq(int d, const RopeArgsDev &ra) {
-  int p, da;
-  if (d < ra.off1) { p = d >> 1; da = 2 * ra.half0; }
-  else if (d < ra.off2) { p = (d - ra.off1) >> 1; da = 2 * ra.half1; }
-  else { p = (d - ra.off2) >> 1; da = 2 * ra.half2; }
+  // the fields are read into registers first: a per-lane choice between
+  // struct fields would otherwise become a per-lane load of the arguments
+  const int off1 = ra.off1, off2 = ra.off2, h0 = ra.half0, h1 = ra.half1, h2 = ra.half2;
+  const int p = (d < off1 ? d : d < off2 ? d - off1 : d - off2) >> 1;
+  const int da = 2 * (d < off1 ? h0 : d < off2 ? h1 : h2);
   return exp2f(-2.0f * (float)p / (float)da * ra.log2_theta);
 }
 
@@ -1178,21 +1179,23 @@ __global__ __launch_bounds__(128 * G) void k_attn(AttnArgs args) {
   if (bh64 >= args.bh_count || group >= args.ngroups) return;
   const int bh = (int)bh64;
   const int64_t gidx = (int64_t)bh * args.ngroups + group;
-  const int qb = args.ugroup[gidx * G + member];
+  // wave-uniform values through the scalar cache (the schedule is written by
+  // earlier kernels and only read here)
+  typedef const __attribute__((address_space(4))) int32_t *cint_p;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int qb = ((cint_p)args.ugroup)[gidx * G + (wave_u >> 1)];
   const bool active = qb >= 0;
   const int b = bh / args.heads, h = bh % args.heads;
   const int64_t base = (int64_t)b * args.stride_b + (int64_t)h * args.stride_h;
   const int64_t n = (int64_t)(active ? qb : 0) * 64 + 32 * half + (lane & 31);
 
   bf16x8 qreg[NS];
-  {
-    const uint16_t *qrow = args.q + base + n * args.stride_n;
+  const uint16_t *qrow = args.q + base + n * args.stride_n;
+  if (!SPARSE) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) qreg[s] = *(const bf16x8 *)(qrow + 16 * s + 8 * g);
+    wait_vmcnt<0>();
   }
-  // Q must be in registers before the tile copies start: vmcnt completes in
-  // order, so a first wait for Q inside the loop would also drain the ring.
-  wait_vmcnt<0>();
 
   f32x16 oacc[DT];
 #pragma unroll
@@ -1203,13 +1206,7 @@ __global__ __launch_bounds__(128 * G) void k_attn(AttnArgs args) {
 
   if (SPARSE) {
     const int32_t *list = args.ulist + gidx * args.list_stride;
-    const int U = args.ucount[gidx];
-    // Stage the list in LDS before the first DMA: a global load inside the
-    // loop would need vmcnt(0), which also drains the prefetched tiles.  Lists
-    // longer than LMAX (keep ratios near 1) take a second copy of the loop
-    // that reads the list from HBM.
-    for (int i = tid; i < min(U, LMAX); i += NT) slist[i] = list[i];
-    __syncthreads();
+    const int U = ((cint_p)args.ucount)[gidx];
     const uint16_t *Kb = args.k + base;
     const uint16_t *Vb = args.v + base;
     const float c = args.scale_log2e;
@@ -1240,46 +1237,69 @@ __global__ __launch_bounds__(128 * G) void k_attn(AttnArgs args) {
       const int r0 = 4 * g + (i >> 2);
       voff[dt] = r0 * D + (((dstart >> 3) ^ swz_v<D>(r0)) << 3) + (dstart & 7);
     }
+    auto issue_j = [&](int t, int j) {
+      uint16_t *slot = ring + (t % S) * (2 * TILE);
+      const int64_t jrow = (int64_t)j * 64;
+      if (jrow + 64 <= args.n_tokens) {
+        const uint16_t *kj = Kb + jrow * args.stride_n, *vj = Vb + jrow * args.stride_n;
+        const uint32_t m0 = ring_lds + (uint32_t)((t % S) * (2 * TILE) * 2) + (uint32_t)wave_s * 1024u;
+#pragma unroll
+        for (int o = 0; o < OPS; ++o) {
+          lds_dma16_m0(kj, gk[o], m0 + (uint32_t)(o * NT * 16));
+          lds_dma16_m0(vj, gv[o], m0 + (uint32_t)(TILE * 2 + o * NT * 16));
+        }
+      } else {
+#pragma unroll
+        for (int o = 0; o < OPS; ++o) {
+          const int cidx = o * NT + tid;
+          const int row = cidx / CH, pc = cidx % CH;
+          // rows past N (tail block) are copied from row N-1: finite
+          // values, masked out of the softmax
+          const int64_t src = min(jrow + row, args.n_tokens - 1) * args.stride_n;
+          lds_dma16(Kb + src + ((pc ^ swz_k<D>(row)) * 8), slot + (o * NT + wave * 64) * 8);
+          lds_dma16(Vb + src + ((pc ^ swz_v<D>(row)) * 8), slot + TILE + (o * NT + wave * 64) * 8);
+        }
+      }
+    };
+    // Prologue, one memory round trip: the copies of tiles 0 and 1 (their
+    // key blocks read through the scalar cache), then Q and the list, all in
+    // flight together.  The list is staged in LDS: a global load inside the
+    // loop would need vmcnt(0), which also drains the prefetched tiles.
+    // Lists longer than LMAX (keep ratios near 1) take a second copy of the
+    // loop that reads the list from HBM.
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      if (t < U) issue_j(t, ((cint_p)list)[t] & 0xffff);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) qreg[s] = *(const bf16x8 *)(qrow + 16 * s + 8 * g);
+    {
+      int32_t lv[(LMAX + NT - 1) / NT];
+#pragma unroll
+      for (int r = 0; r < (LMAX + NT - 1) / NT; ++r) {
+        const int i = r * NT + tid;
+        lv[r] = i < min(U, LMAX) ? list[i] : 0;
+      }
+      wait_vmcnt<0>();
+#pragma unroll
+      for (int r = 0; r < (LMAX + NT - 1) / NT; ++r) {
+        const int i = r * NT + tid;
+        if (i < min(U, LMAX)) slist[i] = lv[r];
+      }
+    }
+    __syncthreads();  // tiles 0 and 1 and the list complete for every wave
     auto main_loop = [&](auto lds_tag) {
       constexpr bool FROM_LDS = decltype(lds_tag)::value;
       auto entry = [&](int t) -> int {
         if constexpr (FROM_LDS) return slist[t];
         else return list[t];
       };
-      auto issue = [&](int t) {
-        const int j = __builtin_amdgcn_readfirstlane(entry(t) & 0xffff);
-        uint16_t *slot = ring + (t % S) * (2 * TILE);
-        const int64_t jrow = (int64_t)j * 64;
-        if (jrow + 64 <= args.n_tokens) {
-          const uint16_t *kj = Kb + jrow * args.stride_n, *vj = Vb + jrow * args.stride_n;
-          const uint32_t m0 = ring_lds + (uint32_t)((t % S) * (2 * TILE) * 2) + (uint32_t)wave_s * 1024u;
-#pragma unroll
-          for (int o = 0; o < OPS; ++o) {
-            lds_dma16_m0(kj, gk[o], m0 + (uint32_t)(o * NT * 16));
-            lds_dma16_m0(vj, gv[o], m0 + (uint32_t)(TILE * 2 + o * NT * 16));
-          }
-        } else {
-#pragma unroll
-          for (int o = 0; o < OPS; ++o) {
-            const int cidx = o * NT + tid;
-            const int row = cidx / CH, pc = cidx % CH;
-            // rows past N (tail block) are copied from row N-1: finite
-            // values, masked out of the softmax
-            const int64_t src = min(jrow + row, args.n_tokens - 1) * args.stride_n;
-            lds_dma16(Kb + src + ((pc ^ swz_k<D>(row)) * 8), slot + (o * NT + wave * 64) * 8);
-            lds_dma16(Vb + src + ((pc ^ swz_v<D>(row)) * 8), slot + TILE + (o * NT + wave * 64) * 8);
-          }
-        }
-      };
+      auto issue = [&](int t) { issue_j(t, __builtin_amdgcn_readfirstlane(entry(t) & 0xffff)); };
       // Two tiles per barrier: iteration k consumes tiles 2k and 2k+1 and,
       // before computing, copies 2k+2 and 2k+3 into the slots of 2k-2 and
       // 2k-1 (free once every wave has passed the barrier), so each copy has
       // a whole iteration to land.  A SIMD loaded on one tile and idle on the
       // other evens out within the pair.
       static_assert(S == 4, "two tiles per barrier in a four-slot ring");
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-        if (t < U) issue(t);
       for (int t2 = 0; t2 < U; t2 += 2) {
         wait_vmcnt<0>();  // this wave's copies of tiles t2, t2+1
         barrier_lds();    // both visible to all waves; every wave is done with t2-2, t2-1
