@@ -1166,7 +1166,7 @@ __global__ __launch_bounds__(128 * G) void k_attn(AttnArgs args) {
   static_assert(S >= 2 && S <= 4, "ring depth");
   constexpr int LMAX = 2048;  // union-list entries staged in LDS (longer lists read the tail from HBM)
   __shared__ __attribute__((aligned(1024))) uint16_t ring[SPARSE ? S * 2 * TILE : 8];
-  __shared__ int32_t slist[SPARSE ? LMAX : 1];
+  __shared__ int32_t slist[SPARSE ? LMAX + 8 : 1];  // + room for the reads ahead past the end
   __shared__ __attribute__((aligned(16))) float sfreq[D / 2];  // rotary inverse frequency per pair
 
   const int tid = threadIdx.x;
@@ -1300,12 +1300,32 @@ __global__ __launch_bounds__(128 * G) void k_attn(AttnArgs args) {
       // a whole iteration to land.  A SIMD loaded on one tile and idle on the
       // other evens out within the pair.
       static_assert(S == 4, "two tiles per barrier in a four-slot ring");
+      // the list entries of tiles t2 .. t2+3, read one iteration ahead so
+      // that no LDS read stands between the barrier and the copies (entries
+      // past U are never used)
+      int ea = 0, eb = 0, ec = 0, ed = 0;
+      if constexpr (FROM_LDS) {
+        ea = slist[0]; eb = slist[1]; ec = slist[2]; ed = slist[3];
+      }
       for (int t2 = 0; t2 < U; t2 += 2) {
         wait_vmcnt<0>();  // this wave's copies of tiles t2, t2+1
         barrier_lds();    // both visible to all waves; every wave is done with t2-2, t2-1
-        if (t2 + 2 < U) issue(t2 + 2);
-        if (t2 + 3 < U) issue(t2 + 3);
-        const int e0 = entry(t2), e1 = t2 + 1 < U ? entry(t2 + 1) : 0;
+        int e0, e1;
+        if constexpr (FROM_LDS) {
+          e0 = ea;
+          e1 = eb;
+          if (t2 + 2 < U) issue_j(t2 + 2, __builtin_amdgcn_readfirstlane(ec & 0xffff));
+          if (t2 + 3 < U) issue_j(t2 + 3, __builtin_amdgcn_readfirstlane(ed & 0xffff));
+          ea = ec;
+          eb = ed;
+          ec = slist[t2 + 4];
+          ed = slist[t2 + 5];
+        } else {
+          if (t2 + 2 < U) issue(t2 + 2);
+          if (t2 + 3 < U) issue(t2 + 3);
+          e0 = entry(t2);
+          e1 = t2 + 1 < U ? entry(t2 + 1) : 0;
+        }
         const bool m0 = active && ((e0 >> (16 + member)) & 1);
         const bool m1 = active && ((e1 >> (16 + member)) & 1);
         if (!m0 && !m1) continue;
