@@ -868,6 +868,8 @@ __global__ __launch_bounds__(1024) void k_order(const int32_t *__restrict__ map,
 // fewer waves idle on a tile.  Windows are multiples of G, so group
 // boundaries stay aligned; padding entries (-1) stay at the end.  Used for
 // kb <= kGroupMaxKb (maps cached in LDS as 16-bit ids).
+extern "C" __device__ int __ockl_wfred_max_i32(int);
+
 constexpr int kGroupWin = 64;
 constexpr int kGroupMaxKb = 64;
 
@@ -877,8 +879,10 @@ constexpr int kGroupMaxKb = 64;
 // blocks present in the union (all bitset reads independent, so one LDS
 // round trip per step), and a max-reduction over the wave picks the next
 // member.  The maps are also staged in LDS so that a new member's key blocks
-// enter the union in one step (one lane per key block).  Dynamic LDS: the
-// union bitset.
+// enter the union in one step (one lane per key block).  KBM >= kb bounds the
+// unrolled recount: all KBM reads are issued without branches (entries past
+// kb are masked afterwards), so they overlap.  Dynamic LDS: the union bitset.
+template <int KBM>
 __global__ __launch_bounds__(64) void k_group(const int32_t *__restrict__ map, int nb, int kb, int G,
                                               int ngroups, int32_t *__restrict__ ugroup) {
   extern __shared__ uint32_t inu[];                     // [ceil(nb/32)]
@@ -912,9 +916,9 @@ __global__ __launch_bounds__(64) void k_group(const int32_t *__restrict__ map, i
   }
   __syncthreads();
   // this lane's map in registers, as (word, bit) of the union bitset
-  uint32_t kw[kGroupMaxKb];
+  uint32_t kw[KBM];
 #pragma unroll
-  for (int t = 0; t < kGroupMaxKb; ++t) {
+  for (int t = 0; t < KBM; ++t) {
     const int j = (t < kb && qb >= 0) ? (int)cmap[lane * kb + t] : 0;
     kw[t] = ((uint32_t)(j >> 5) << 5) | (uint32_t)(j & 31);
   }
@@ -929,10 +933,12 @@ __global__ __launch_bounds__(64) void k_group(const int32_t *__restrict__ map, i
   };
   // key blocks of this lane's map present in the union
   auto score = [&]() -> int {
+    uint32_t bits[KBM];
+#pragma unroll
+    for (int t = 0; t < KBM; ++t) bits[t] = inu[kw[t] >> 5];
     int sc = 0;
 #pragma unroll
-    for (int t = 0; t < kGroupMaxKb; ++t)
-      if (t < kb) sc += (int)((inu[kw[t] >> 5] >> (kw[t] & 31)) & 1u);
+    for (int t = 0; t < KBM; ++t) sc += (t < kb) ? (int)((bits[t] >> (kw[t] & 31)) & 1u) : 0;
     return sc;
   };
   int32_t outv = -1;  // regrouped sequence: position p held by lane p
@@ -948,8 +954,7 @@ __global__ __launch_bounds__(64) void k_group(const int32_t *__restrict__ map, i
     for (int members = 1; members < G && live; ++members) {
       // key = score*64 + (63 - position): most shared key blocks, then earliest
       int best = ((live >> lane) & 1ull) ? score() * 64 + (63 - lane) : -1;
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) best = max(best, __shfl_xor(best, o, 64));
+      best = __ockl_wfred_max_i32(best);  // wave-wide max on DPP
       const int c = 63 - (best & 63);
       const int v = __shfl(qb, c, 64);
       if (lane == outp + members) outv = v;
@@ -1871,9 +1876,14 @@ void launch_schedule(const int32_t *map, int nb, int kb, int G, int ngroups, int
                      int bh, int32_t *ugroup, int32_t *ucount, int32_t *ulist, hipStream_t st) {
   hipLaunchKernelGGL(k_order, dim3((nb + kOrderPer - 1) / kOrderPer, bh), dim3(1024), (size_t)nb * 4, st, map, nb,
                      kb, G, ngroups, ugroup);
-  if (kb > 0 && kb <= kGroupMaxKb && kGroupWin % G == 0)
-    hipLaunchKernelGGL(k_group, dim3((ngroups * G + kGroupWin - 1) / kGroupWin, bh), dim3(64),
-                       (size_t)(nb + 31) / 32 * 4, st, map, nb, kb, G, ngroups, ugroup);
+  if (kb > 0 && kb <= kGroupMaxKb && kGroupWin % G == 0) {
+    const dim3 grid((ngroups * G + kGroupWin - 1) / kGroupWin, bh), block(64);
+    const size_t lds = (size_t)(nb + 31) / 32 * 4;
+    if (kb <= 16) hipLaunchKernelGGL(k_group<16>, grid, block, lds, st, map, nb, kb, G, ngroups, ugroup);
+    else if (kb <= 32) hipLaunchKernelGGL(k_group<32>, grid, block, lds, st, map, nb, kb, G, ngroups, ugroup);
+    else if (kb <= 48) hipLaunchKernelGGL(k_group<48>, grid, block, lds, st, map, nb, kb, G, ngroups, ugroup);
+    else hipLaunchKernelGGL(k_group<64>, grid, block, lds, st, map, nb, kb, G, ngroups, ugroup);
+  }
   if (kb > 0) {
     const size_t lds = (size_t)kUnionWaves * ((nb + 3) / 4) * 4;
     hipLaunchKernelGGL(k_union, dim3((ngroups + kUnionWaves - 1) / kUnionWaves, bh), dim3(64 * kUnionWaves), lds,
