@@ -55,7 +55,8 @@ def lib():
             "ro_e4m3_value": ([ctypes.c_uint8], D),
             "ro_e4m3_encode": ([ctypes.c_float], ctypes.c_uint8),
             "ro_quant_e4m3": ([P, I64, I64, I64, I32, P, P, P], None),
-            "ro_forward": ([P, P, P, P, P, I64, I64, I64, I32, I32, I32, P, P, D, D, I32, P, P], None),
+            "ro_gate": ([P, P, I32], D),
+            "ro_forward": ([P, P, P, P, P, P, I64, I64, I64, I32, I32, I32, P, P, D, D, I32, P, P], None),
         }
         for name, (args, res) in sigs.items():
             f = getattr(L, name)
@@ -166,7 +167,15 @@ def lowrank_state(k, v, wk, n_valid: int, grid, split=None, theta=10000.0):
     return S, z
 
 
-def lowrank_rows(q, wq, S, z, grid, rows, split=None, theta=10000.0) -> np.ndarray:
+def gate(q, g) -> float:
+    """Output gate sigmoid(q . w + b) of one token; ``g`` = fp32 [w_0 .. w_{D-1}, b]."""
+    q, g = _c(q, np.float64), _c(g, np.float32)
+    assert g.size == q.size + 1
+    return lib().ro_gate(_p(q), _p(g), q.size)
+
+
+def lowrank_rows(q, wq, S, z, grid, rows, split=None, theta=10000.0, gate_w=None) -> np.ndarray:
+    """Low-rank output of flat rows (bh * n_pad + n); times the output gate when ``gate_w`` is set."""
     q, wq = _c(q, np.float64), _c(wq, np.float32)
     S, z = _c(S, np.float64), _c(z, np.float64)
     rows = _c(rows, np.int64)
@@ -176,6 +185,10 @@ def lowrank_rows(q, wq, S, z, grid, rows, split=None, theta=10000.0) -> np.ndarr
     out = np.zeros((rows.size, d), dtype=np.float64)
     lib().ro_lowrank_rows(_p(q), _p(wq), _p(S), _p(z), n_pad, d, r, _p(_c(grid, np.int32)),
                           _p(_c(split, np.int32)), theta, rows.size, _p(rows), _p(out))
+    if gate_w is not None:
+        qf = q.reshape(-1, d)
+        for i, row in enumerate(rows):
+            out[i] *= gate(qf[row], gate_w)
     return out
 
 
@@ -198,8 +211,10 @@ def quant_e4m3(x_bits, n_valid: int):
 
 
 def forward(q_bits, k_bits, v_bits, wq, wk, n_valid: int, kb: int, grid, split=None,
-            theta=10000.0, scale=None, fp8=False):
-    """Whole RoLA forward.  Returns (block map [BH, nb, kb] int32, out [BH, n_pad, D] float64)."""
+            theta=10000.0, scale=None, fp8=False, gate_w=None):
+    """Whole RoLA forward.  Returns (block map [BH, nb, kb] int32, out [BH, n_pad, D] float64).
+
+    ``gate_w`` (fp32 [D+1], optional): output gate on the low-rank term."""
     q, k, v = _c(q_bits, np.uint16), _c(k_bits, np.uint16), _c(v_bits, np.uint16)
     wq, wk = _c(wq, np.float32), _c(wk, np.float32)
     bh, n_pad, d = q.shape
@@ -208,7 +223,9 @@ def forward(q_bits, k_bits, v_bits, wq, wk, n_valid: int, kb: int, grid, split=N
     scale = d ** -0.5 if scale is None else scale
     bmap = np.zeros((bh, n_pad // BLOCK, kb), dtype=np.int32)
     out = np.zeros((bh, n_pad, d), dtype=np.float64)
-    lib().ro_forward(_p(q), _p(k), _p(v), _p(wq), _p(wk), bh, n_pad, n_valid, d, r, kb,
+    gw = None if gate_w is None else _c(gate_w, np.float32)
+    assert gw is None or gw.shape == (d + 1,)
+    lib().ro_forward(_p(q), _p(k), _p(v), _p(wq), _p(wk), None if gw is None else _p(gw), bh, n_pad, n_valid, d, r, kb,
                      _p(_c(grid, np.int32)), _p(_c(split, np.int32)), theta, scale, int(fp8),
                      _p(bmap), _p(out))
     return bmap, out

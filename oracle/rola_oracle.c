@@ -34,6 +34,12 @@
  *    O_lr = (a^T S)/(a^T z), S = sum_n b_n v_n^T, z = sum_n b_n over all N
  *    valid keys; one state per (batch, head);
  *  - output = sparse + low-rank for rows < N, zero for padded rows;
+ *  - optional learned output gate on the low-rank term (README
+ *    "AlibabaResearch/SparkDiffusion", sparse-finetune section, names the
+ *    trainable gate_proj and gate_bias without giving their form): read here
+ *    as g = sigmoid(q . w + b) per token and head, from the raw (unrotated)
+ *    query, with one gate vector [w_0 .. w_{D-1}, b] shared by all heads like
+ *    the two projections; the output is then sparse + g * low-rank;
  *  - fp8 mode: per (batch, head, 64-token block) absmax scale, codes are
  *    OCP e4m3 (max 448) rounded to nearest even from x * fl32(448/absmax),
  *    values dequantise as code * fl32(absmax/448).
@@ -290,6 +296,13 @@ void ro_lowrank_rows(const double *q, const float *wq, const double *S, const do
   }
 }
 
+/* Output gate of one token: sigmoid(b + sum_d q[d] w[d]), gate = [w_0 .. w_{D-1}, b]. */
+double ro_gate(const double *q, const float *gate, int d_model) {
+  double u = (double)gate[d_model];
+  for (int d = 0; d < d_model; ++d) u += q[d] * (double)gate[d];
+  return 1.0 / (1.0 + exp(-u));
+}
+
 /* --------------------------------------------------------------- fp8 e4m3 */
 /* OCP e4m3 value of a code (no infinities; 0x7f/0xff are NaN). */
 double ro_e4m3_value(uint8_t code) {
@@ -369,12 +382,14 @@ static void widen(const uint16_t *x, int64_t count, double *y) {
  * The whole RoLA forward for `bh_count` (batch, head) slices of bf16 tokens.
  * map_out [BH, nb, kb]; out [BH, n_pad, D] fp64.  Threads run over slices.
  * fp8 != 0 runs the sparse branch on the e4m3-dequantised Q, K, V; selection
- * and the low-rank branch always use the bf16 values.
+ * and the low-rank branch always use the bf16 values.  gate (fp32 [D+1], may
+ * be NULL for no gate) scales the low-rank term by ro_gate of the bf16 query.
  */
 void ro_forward(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *wq,
-                const float *wk, int64_t bh_count, int64_t n_pad, int64_t n_valid, int d_model,
-                int rank, int kb, const int32_t *grid, const int32_t *split, double theta,
-                double scale, int fp8, int32_t *map_out, double *out) {
+                const float *wk, const float *gate, int64_t bh_count, int64_t n_pad,
+                int64_t n_valid, int d_model, int rank, int kb, const int32_t *grid,
+                const int32_t *split, double theta, double scale, int fp8, int32_t *map_out,
+                double *out) {
   const int64_t nb = n_pad / RO_BLOCK;
   const int64_t per = n_pad * d_model;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -426,7 +441,8 @@ void ro_forward(const uint16_t *q, const uint16_t *k, const uint16_t *v, const f
                  on, buf);
       const int64_t row = n; /* rows are relative to this slice */
       ro_lowrank_rows(qd, wq, S, z, n_pad, d_model, rank, grid, split, theta, 1, &row, lr);
-      for (int d = 0; d < d_model; ++d) on[d] += lr[d];
+      const double g = gate ? ro_gate(qd + n * d_model, gate, d_model) : 1.0;
+      for (int d = 0; d < d_model; ++d) on[d] += g * lr[d];
     }
     if (fp8) {
       free(codes); free(scl); free(qs); free(ks); free(vs);

@@ -210,6 +210,68 @@ def test_forward_is_sum_of_pinned_parts(oracle_lib):
     np.testing.assert_allclose(out.reshape(-1, w.head_dim), sp + lr, rtol=1e-12, atol=1e-14)
 
 
+# ------------------------------------------------------------ output gate
+def test_gate_closed_forms(oracle_lib):
+    rng = np.random.default_rng(47)
+    d = 64
+    _, q = _bf16(rng, (d,))
+    zero = np.zeros(d + 1, dtype=np.float32)
+    assert oracle_lib.gate(q, zero) == 0.5
+    g = zero.copy()
+    g[d] = np.float32(np.log(3.0))
+    assert abs(oracle_lib.gate(q, g) - 0.75) < 1e-7  # sigmoid(ln 3) = 3/4 (bias rounded to fp32)
+    # a unit weight picks one query component: sigmoid(1 + ln 3 - 1)
+    q1 = q.copy()
+    q1[17] = 1.0
+    g = zero.copy()
+    g[17], g[d] = 1.0, np.float32(np.log(3.0) - 1.0)
+    assert abs(oracle_lib.gate(q1, g) - 0.75) < 1e-7
+    # sigmoid(-u) = 1 - sigmoid(u), and a random gate against torch's sigmoid of the dot product
+    w = (rng.standard_normal(d + 1) / 4).astype(np.float32)
+    u = torch.tensor(q) @ torch.tensor(w[:d], dtype=torch.float64) + float(w[d])
+    assert abs(oracle_lib.gate(q, w) - torch.sigmoid(u).item()) < 1e-15
+    assert abs(oracle_lib.gate(q, w) + oracle_lib.gate(q, -w) - 1.0) < 1e-15
+
+
+def test_forward_gate_scales_only_the_lowrank_term(oracle_lib):
+    from sparse_rank_attention_amd.workloads import WORKLOADS, make_proj, make_qkv
+    w = WORKLOADS["tiny"]
+    q, k, v = (x[0] for x in make_qkv(w))
+    wq, wk = make_proj(w)
+    d = w.head_dim
+    n_valid = w.n_tokens - 37
+    qd, kd, vd = (oracle_lib.widen_bf16(x) for x in (q, k, v))
+    bmap, plain = oracle_lib.forward(q, k, v, wq, wk, n_valid, w.kb, w.grid)
+    rows = np.arange(q.shape[0] * w.n_pad)
+    sp = oracle_lib.sparse_rows(qd, kd, vd, bmap, n_valid, rows)
+    S, z = oracle_lib.lowrank_state(kd, vd, wk, n_valid, w.grid)
+    lr = oracle_lib.lowrank_rows(qd, wq, S, z, w.grid, rows)
+    valid = (rows % w.n_pad) < n_valid
+    # a saturated gate is exactly the ungated forward; a shut one leaves the sparse branch alone
+    g = np.zeros(d + 1, dtype=np.float32)
+    g[d] = 800.0
+    _, out = oracle_lib.forward(q, k, v, wq, wk, n_valid, w.kb, w.grid, gate_w=g)
+    np.testing.assert_array_equal(out, plain)
+    g[d] = -800.0
+    _, out = oracle_lib.forward(q, k, v, wq, wk, n_valid, w.kb, w.grid, gate_w=g)
+    np.testing.assert_allclose(out.reshape(-1, d)[valid], sp[valid], rtol=1e-12, atol=1e-14)
+    # constant gate 3/4
+    g[d] = np.float32(np.log(3.0))
+    _, out = oracle_lib.forward(q, k, v, wq, wk, n_valid, w.kb, w.grid, gate_w=g)
+    gv = 1.0 / (1.0 + np.exp(-np.float64(g[d])))
+    np.testing.assert_allclose(out.reshape(-1, d)[valid], (sp + gv * lr)[valid], rtol=1e-12, atol=1e-14)
+    # a per-token gate reads the token's own unrotated query: one weight on component 5
+    g = np.zeros(d + 1, dtype=np.float32)
+    g[5], g[d] = 1.5, -0.25
+    _, out = oracle_lib.forward(q, k, v, wq, wk, n_valid, w.kb, w.grid, gate_w=g)
+    qf = qd.reshape(-1, d)
+    gt = torch.sigmoid(torch.tensor(1.5 * qf[:, 5] - 0.25)).numpy()[:, None]
+    np.testing.assert_allclose(out.reshape(-1, d)[valid], (sp + gt * lr)[valid], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(oracle_lib.lowrank_rows(qd, wq, S, z, w.grid, rows, gate_w=g),
+                               gt * lr, rtol=1e-12, atol=1e-14)
+    assert np.all(out.reshape(-1, d)[~valid] == 0)
+
+
 # ------------------------------------------------------------------- fp8
 def test_e4m3_values_match_torch():
     pytest.importorskip("torch")
