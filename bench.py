@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="wan14b_720p")
     ap.add_argument("--topk", type=float, default=None, help="override the workload's keep ratio")
+    ap.add_argument("--gate", action="store_true",
+                    help="apply the learned output gate to the low-rank term (seeded synthetic gate)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true", help="skip the MFMA-probe and copy measurements")
     ap.add_argument("--cpu-baseline-child", action="store_true", help=argparse.SUPPRESS)
@@ -88,7 +90,7 @@ def cpu_baseline_child(args):
     qbs = list(range(0, w.nb, args.sample_stride))
     rows = np.array([n for qb in qbs for n in range(qb * 64, min(qb * 64 + 64, w.n_tokens))])
     sp = oracle.sparse_rows(qf, kf, vf, bmap, w.n_tokens, rows)
-    lr = oracle.lowrank_rows(qf, wq, S, z, w.grid, rows)
+    lr = oracle.lowrank_rows(qf, wq, S, z, w.grid, rows, gate_w=W.make_gate(w) if args.gate else None)
     t3 = time.perf_counter()
     assert np.isfinite(sp + lr).all()
     rows_full = w.n_tokens
@@ -101,7 +103,8 @@ def cpu_baseline_child(args):
 def cpu_baseline(args, w):
     env = dict(os.environ, OMP_NUM_THREADS="1")
     cmd = [sys.executable, os.path.abspath(__file__), "--cpu-baseline-child", "--workload", args.workload,
-           "--sample-stride", str(args.sample_stride)] + (["--topk", repr(args.topk)] if args.topk else [])
+           "--sample-stride", str(args.sample_stride)] + (["--topk", repr(args.topk)] if args.topk else []) \
+        + (["--gate"] if args.gate else [])
     res = subprocess.run(cmd, env=env, capture_output=True, text=True, timeout=600)
     if res.returncode != 0:
         raise RuntimeError("cpu baseline failed: " + res.stderr[-2000:])
@@ -187,6 +190,7 @@ def main():
     qd, kd, vd = dev(q), dev(k), dev(v)
     del q, k, v
     wqd, wkd = torch.from_numpy(wq).cuda(), torch.from_numpy(wk).cuda()
+    gd = torch.from_numpy(W.make_gate(w)).cuda() if args.gate else None
     cfg = rola.Config(topk=w.topk, rank=w.rank, precision=rola.ROLA_PREC_FP8 if fp8 else rola.ROLA_PREC_BF16)
     dominant = "attn8_sparse_lowrank" if fp8 else "attn_sparse_lowrank"
     peak = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
@@ -201,10 +205,12 @@ def main():
         print("[bench] copy calibration: %d bytes read, %d written" % (nbytes, nbytes), file=sys.stderr, flush=True)
         del src, dst
     print("[bench] warmup %d" % args.warmup, file=sys.stderr, flush=True)
+    rola.timing_enable(True)  # warm the per-kernel event pool as well
     for _ in range(args.warmup):
-        rola.rola_forward(qd, kd, vd, wqd, wkd, w.grid, cfg, out=out, stream=stream)
+        rola.rola_forward(qd, kd, vd, wqd, wkd, w.grid, cfg, out=out, stream=stream, gate=gd)
     torch.cuda.synchronize()
-    rola.timing_read()  # drop anything recorded so far
+    rola.timing_enable(False)
+    rola.timing_read()  # drop the warmup records (their events return to the pool)
 
     print("[bench] timing %d steps" % args.steps, file=sys.stderr, flush=True)
     rola.timing_enable(True)
@@ -212,7 +218,7 @@ def main():
     torch.cuda.synchronize()
     e0.record(stream)
     for _ in range(args.steps):
-        rola.rola_forward(qd, kd, vd, wqd, wkd, w.grid, cfg, out=out, stream=stream)
+        rola.rola_forward(qd, kd, vd, wqd, wkd, w.grid, cfg, out=out, stream=stream, gate=gd)
     e1.record(stream)
     torch.cuda.synchronize()
     rola.timing_enable(False)
@@ -226,7 +232,7 @@ def main():
     achieved = kept / t_attn / 1e12
     traffic = None
     tfile = traffic_file(w.name)
-    if os.path.exists(tfile) and args.topk is None:
+    if os.path.exists(tfile) and args.topk is None and not args.gate:
         with open(tfile) as f:
             tr = json.load(f)
         if tr.get("kernel_source_hash") == kernel_source_hash() and tr.get("workload") == w.name:
@@ -252,7 +258,7 @@ def main():
         "data": "synthetic (seeded Wan-shaped smooth field + noise Q/K, N(0,1) V; no weights)",
         "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim,
                    "grid": list(w.grid), "n_tokens": w.n_tokens, "topk": w.topk, "kb": w.kb, "nb": w.nb,
-                   "rank": w.rank},
+                   "rank": w.rank, "output_gate": bool(args.gate)},
         "fwd_ms": round(ms, 4),
         "dense_equiv_tflops": round(dense / (ms * 1e-3) / 1e12, 1),
         "kept_block_tflops": round(kept / (ms * 1e-3) / 1e12, 1),

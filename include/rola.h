@@ -27,15 +27,22 @@
  *    R the 3-D rotary embedding (dims split t/h/w, interleaved pairs, base
  *    theta); S = sum_{n<N} b_n v_n^T, z = sum_{n<N} b_n per (batch, head);
  *    O_lr = (a^T S) / (a^T z);
- *  - output O = O_sparse + O_lr for rows < N; rows N..n_pad-1 are written 0.
+ *  - output O = O_sparse + g * O_lr for rows < N; rows N..n_pad-1 are written 0.
+ *    g is the optional learned output gate (README "AlibabaResearch/
+ *    SparkDiffusion", sparse-finetune section, names the trainable gate_proj
+ *    and gate_bias without their form), read here as g = sigmoid(q . w + b)
+ *    per token and head from the unrotated query, fp32 sum of products;
+ *    without a gate g = 1.
  *
  * Memory: every pointer is device memory owned by the caller.  Q, K, V and O
  * share one layout: element (b, h, n, d) at b*stride_b + h*stride_h +
  * n*stride_n + d (elements; d contiguous), rows 0..n_pad-1 addressable;
  * input rows >= N are ignored (may hold anything).  Q/K/V are bf16.  O is
  * bf16 or fp32 (config.out_dtype).  Wq, Wk are fp32 [D][r], shared by all
- * heads.  The workspace (size from rola_plan) is scratch owned by the caller;
- * the library keeps no state in it between calls.
+ * heads.  The gate, where given, is fp32 [D+1] (w_0 .. w_{D-1}, then b),
+ * shared by all heads, 16-byte aligned.  The workspace (size from rola_plan)
+ * is scratch owned by the caller; the library keeps no state in it between
+ * calls.
  *
  * Behaviour: every call validates all arguments before launching anything;
  * on error nothing is launched and a status != ROLA_OK is returned.  Launches
@@ -53,7 +60,7 @@
 extern "C" {
 #endif
 
-#define ROLA_ABI_VERSION 1
+#define ROLA_ABI_VERSION 2
 #define ROLA_BLOCK 64
 #define ROLA_MAX_BLOCKS 4096 /* nb limit: N <= 262144 tokens */
 
@@ -132,25 +139,28 @@ int32_t rola_sparse_attn(const rola_problem *prob, const rola_config *cfg, const
  * linear attention: a linear branch with rotary positions; README
  * "AlibabaResearch/SparkDiffusion", sparse-finetune section: the added
  * query and key projections).
- * O = O_lr (accumulate = 0) or O += O_lr (accumulate = 1).
+ * O = g * O_lr (accumulate = 0) or O += g * O_lr (accumulate = 1); gate NULL
+ * means g = 1.
  */
 int32_t rola_lowrank_attn(const rola_problem *prob, const rola_config *cfg, const void *q,
                           const void *k, const void *v, const float *wq, const float *wk,
-                          void *out, int32_t accumulate, void *workspace,
+                          const float *gate, void *out, int32_t accumulate, void *workspace,
                           size_t workspace_bytes, void *stream);
 
 /*
- * Fused RoLA forward: O = O_sparse + O_lr.  block_idx_out, if not NULL,
- * receives the block map (int32 [B][H][nb][kb]).
+ * Fused RoLA forward: O = O_sparse + g * O_lr (gate NULL: g = 1).
+ * block_idx_out, if not NULL, receives the block map (int32 [B][H][nb][kb]).
  */
 int32_t rola_forward(const rola_problem *prob, const rola_config *cfg, const void *q,
                      const void *k, const void *v, const float *wq, const float *wk,
-                     int32_t *block_idx_out, void *out, void *workspace,
+                     const float *gate, int32_t *block_idx_out, void *out, void *workspace,
                      size_t workspace_bytes, void *stream);
 
 /*
  * Optional kernel timing for measurement.  While enabled, each call records a
  * hipEvent pair around every kernel it launches (on the call's stream).
+ * Enabling creates a pool of events on the current device first, so that the
+ * timed calls themselves create none while the pool lasts.
  * rola_timing_read synchronises those events and returns, per kernel name,
  * the launch count and total milliseconds (at most `max` entries; returns
  * the number written, or -1 on error).  Process-global; not thread-safe.

@@ -133,6 +133,7 @@ std::mutex g_mu;
 bool g_timing = false;
 std::vector<TimedLaunch> g_launches;
 std::vector<hipEvent_t> g_free_events;
+constexpr size_t kEventPool = 512;  // enough for about 36 timed forward calls
 
 hipEvent_t take_event() {
   if (!g_free_events.empty()) {
@@ -239,8 +240,8 @@ int32_t run_quant8(const Plan &P, const rola_problem *p, const void *q, const vo
 }
 
 int32_t run_attn(const Plan &P, const rola_problem *p, const rola_config *c, const void *q,
-                 const void *k, const void *v, const int32_t *map, void *out, uint8_t *ws, bool sparse,
-                 bool lowrank, bool accum, hipStream_t st) {
+                 const void *k, const void *v, const int32_t *map, const float *gate, void *out,
+                 uint8_t *ws, bool sparse, bool lowrank, bool accum, hipStream_t st) {
   rola::AttnArgs a;
   a.q = (const uint16_t *)q; a.k = (const uint16_t *)k; a.v = (const uint16_t *)v;
   a.out = out;
@@ -257,6 +258,7 @@ int32_t run_attn(const Plan &P, const rola_problem *p, const rola_config *c, con
   a.wqT = (const uint16_t *)(ws + P.off_wqT);
   a.st = (const uint16_t *)(ws + P.off_st);
   a.z = (const float *)(ws + P.off_z);
+  a.gate = lowrank ? gate : nullptr;
   a.rope = rope_args(P, ws);
   a.kv8 = ws + P.off_kv8;
   a.qsc = (const float *)(ws + P.off_qsc);
@@ -360,12 +362,13 @@ int32_t rola_sparse_attn(const rola_problem *prob, const rola_config *cfg, const
   hipStream_t st = (hipStream_t)stream;
   uint8_t *ws = (uint8_t *)workspace;
   if (P.fp8) ROLA_TRY(run_quant8(P, prob, q, k, v, ws, st));
-  return run_attn(P, prob, cfg, q, k, v, block_idx, out, ws, true, false, accumulate != 0, st);
+  return run_attn(P, prob, cfg, q, k, v, block_idx, nullptr, out, ws, true, false, accumulate != 0,
+                  st);
 }
 
 int32_t rola_lowrank_attn(const rola_problem *prob, const rola_config *cfg, const void *q,
                           const void *k, const void *v, const float *wq, const float *wk,
-                          void *out, int32_t accumulate, void *workspace,
+                          const float *gate, void *out, int32_t accumulate, void *workspace,
                           size_t workspace_bytes, void *stream) {
   Plan P;
   ROLA_TRY(make_plan(prob, cfg, &P));
@@ -373,6 +376,7 @@ int32_t rola_lowrank_attn(const rola_problem *prob, const rola_config *cfg, cons
   if (accumulate != 0 && accumulate != 1) return ROLA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ROLA_ERR_ALIGNMENT;
   if (((uintptr_t)wq & 3u) || ((uintptr_t)wk & 3u)) return ROLA_ERR_ALIGNMENT;
+  if (gate && !aligned16(gate)) return ROLA_ERR_ALIGNMENT;
   if (!workspace || (int64_t)workspace_bytes < P.total) return ROLA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return ROLA_ERR_ALIGNMENT;
   hipStream_t st = (hipStream_t)stream;
@@ -380,12 +384,13 @@ int32_t rola_lowrank_attn(const rola_problem *prob, const rola_config *cfg, cons
   ROLA_TRY(run_setup(P, wq, wk, ws, st));
   ROLA_TRY(run_pass1(P, prob, nullptr, k, v, ws, false, true, st));
   ROLA_TRY(run_reduce(P, ws, st));
-  return run_attn(P, prob, cfg, q, nullptr, nullptr, nullptr, out, ws, false, true, accumulate != 0, st);
+  return run_attn(P, prob, cfg, q, nullptr, nullptr, nullptr, gate, out, ws, false, true,
+                  accumulate != 0, st);
 }
 
 int32_t rola_forward(const rola_problem *prob, const rola_config *cfg, const void *q,
                      const void *k, const void *v, const float *wq, const float *wk,
-                     int32_t *block_idx_out, void *out, void *workspace,
+                     const float *gate, int32_t *block_idx_out, void *out, void *workspace,
                      size_t workspace_bytes, void *stream) {
   Plan P;
   ROLA_TRY(make_plan(prob, cfg, &P));
@@ -394,6 +399,7 @@ int32_t rola_forward(const rola_problem *prob, const rola_config *cfg, const voi
       (block_idx_out && !aligned16(block_idx_out)))
     return ROLA_ERR_ALIGNMENT;
   if (((uintptr_t)wq & 3u) || ((uintptr_t)wk & 3u)) return ROLA_ERR_ALIGNMENT;
+  if (gate && !aligned16(gate)) return ROLA_ERR_ALIGNMENT;
   if (!workspace || (int64_t)workspace_bytes < P.total) return ROLA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return ROLA_ERR_ALIGNMENT;
   hipStream_t st = (hipStream_t)stream;
@@ -404,7 +410,7 @@ int32_t rola_forward(const rola_problem *prob, const rola_config *cfg, const voi
   ROLA_TRY(run_pass1(P, prob, q, k, v, ws, true, true, st, P.fp8));
   ROLA_TRY(run_reduce(P, ws, st));
   ROLA_TRY(run_select(P, ws, (float *)(ws + P.off_scores), map, st));
-  return run_attn(P, prob, cfg, q, k, v, map, out, ws, true, true, false, st);
+  return run_attn(P, prob, cfg, q, k, v, map, gate, out, ws, true, true, false, st);
 }
 
 int32_t rola_mfma_probe(int32_t precision, int32_t iters, double *flop, float *sink, void *stream) {
@@ -420,6 +426,12 @@ int32_t rola_mfma_probe(int32_t precision, int32_t iters, double *flop, float *s
 int32_t rola_timing_enable(int32_t on) {
   std::lock_guard<std::mutex> lk(g_mu);
   g_timing = on != 0;
+  // create events now rather than inside the calls being timed
+  while (g_timing && g_free_events.size() < kEventPool) {
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) break;
+    g_free_events.push_back(e);
+  }
   return ROLA_OK;
 }
 

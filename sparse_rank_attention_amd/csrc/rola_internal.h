@@ -88,6 +88,7 @@ struct AttnArgs {
   const uint16_t *wqT;  // bf16 [32][D]
   const uint16_t *st;   // bf16 [BH][D][32] (rank permuted)
   const float *z;       // [BH][32]
+  const float *gate;    // fp32 [D+1] output gate (w, then b) on the low-rank term; NULL: none
   RopeArgsHost rope;
   // fp8 sparse branch only
   const uint8_t *kv8;   // tile images, see Quant8Args

@@ -1055,8 +1055,8 @@ __global__ __launch_bounds__(64 * kUnionWaves) void k_union(const int32_t *__res
 }
 
 // Epilogue shared by the bf16 and fp8 attention kernels: low-rank apply
-// O^T += St a / (a^T z) with a = phi(Wq^T R(q)) (Q in registers as the
-// bf16 B operand), then the write of query row n (bf16 or fp32, optional
+// O^T += g St a / (a^T z) with a = phi(Wq^T R(q)) (Q in registers as the
+// bf16 B operand) and g the optional output gate (1 without one), then the write of query row n (bf16 or fp32, optional
 // accumulate; rows >= N written as zero).
 template <int D, bool LOWRANK, bool ACCUM, bool OUTF32>
 static __device__ __forceinline__ void attn_finish(const AttnArgs &args, const bf16x8 *qreg,
@@ -1092,7 +1092,24 @@ static __device__ __forceinline__ void attn_finish(const AttnArgs &args, const b
       }
     }
     den += shfl_xor32(den);
-    const float inv_den = 1.0f / den;
+    float inv_den = 1.0f / den;
+    if (args.gate) {
+      // learned output gate sigmoid(q . w + b) of this query on the low-rank
+      // term; each half-wave holds half of the query's dims
+      float u = 0.0f;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const f32x4 w0 = *(const f32x4 *)(args.gate + 16 * s + 8 * g);
+        const f32x4 w1 = *(const f32x4 *)(args.gate + 16 * s + 8 * g + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          u += (float)qreg[s][e] * w0[e];
+          u += (float)qreg[s][4 + e] * w1[e];
+        }
+      }
+      u += shfl_xor32(u);
+      inv_den *= 1.0f / (1.0f + __expf(-(u + args.gate[D])));
+    }
     bf16x8 aop[2];
 #pragma unroll
     for (int i = 0; i < 16; ++i) aop[i >> 3][i & 7] = (__bf16)(aacc[i] * inv_den);
@@ -1171,7 +1188,7 @@ __global__ __launch_bounds__(128 * G) void k_attn(AttnArgs args) {
   static_assert(S >= 2 && S <= 4, "ring depth");
   constexpr int LMAX = 2048;  // union-list entries staged in LDS (longer lists read the tail from HBM)
   __shared__ __attribute__((aligned(1024))) uint16_t ring[SPARSE ? S * 2 * TILE : 8];
-  __shared__ int32_t slist[SPARSE ? LMAX + 8 : 1];  // + room for the reads ahead past the end
+  __shared__ int32_t slist[SPARSE ? LMAX + 8 : 4];  // + room for the reads ahead past the end
   __shared__ __attribute__((aligned(16))) float sfreq[D / 2];  // rotary inverse frequency per pair
 
   const int tid = threadIdx.x;

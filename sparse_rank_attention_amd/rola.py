@@ -45,6 +45,8 @@ class RolaKernelTime(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_int32), ("total_ms", ctypes.c_double)]
 
 
+ABI_VERSION = 2  # ROLA_ABI_VERSION of include/rola.h
+
 EXPORTS = ["rola_abi_version", "rola_status_str", "rola_plan", "rola_select_blocks",
            "rola_sparse_attn", "rola_lowrank_attn", "rola_forward", "rola_timing_enable",
            "rola_timing_read", "rola_mfma_probe"]
@@ -76,15 +78,18 @@ def lib():
         L.rola_sparse_attn.restype = I32
         L.rola_sparse_attn.argtypes = [P, P, P, P, P, P, P, I32, P, ctypes.c_size_t, P]
         L.rola_lowrank_attn.restype = I32
-        L.rola_lowrank_attn.argtypes = [P, P, P, P, P, P, P, P, I32, P, ctypes.c_size_t, P]
+        L.rola_lowrank_attn.argtypes = [P, P, P, P, P, P, P, P, P, I32, P, ctypes.c_size_t, P]
         L.rola_forward.restype = I32
-        L.rola_forward.argtypes = [P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.rola_forward.argtypes = [P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.rola_timing_enable.restype = I32
         L.rola_timing_enable.argtypes = [I32]
         L.rola_timing_read.restype = I32
         L.rola_timing_read.argtypes = [P, I32]
         L.rola_mfma_probe.restype = I32
         L.rola_mfma_probe.argtypes = [I32, I32, P, P, P]
+        if L.rola_abi_version() != ABI_VERSION:
+            raise RuntimeError("%s has ABI version %d, the binding expects %d: rebuild it"
+                               % (path, L.rola_abi_version(), ABI_VERSION))
         _lib = L
     return _lib
 
@@ -197,29 +202,44 @@ def rola_sparse_attn(q, k, v, block_idx, grid, cfg: Config, out=None, accumulate
     return out
 
 
-def rola_lowrank_attn(q, k, v, wq, wk, grid, cfg: Config, out=None, accumulate=False, stream=None):
+def _check_gate(gate, q):
+    """The output gate is an fp32 device vector [D+1]: weights over the query, then the bias."""
+    if gate is None:
+        return
+    if gate.dtype != torch.float32 or not gate.is_contiguous() or gate.device != q.device:
+        raise RolaError("gate must be a contiguous float32 tensor on the device of q")
+    if gate.numel() != q.shape[-1] + 1:
+        raise RolaError("gate must hold head_dim + 1 values (weights, then bias)")
+
+
+def rola_lowrank_attn(q, k, v, wq, wk, grid, cfg: Config, out=None, accumulate=False, stream=None,
+                      gate=None):
+    """Low-rank branch g * O_lr (g = sigmoid(q . w + b) with ``gate``, else 1)."""
     _check_tokens(q, k, v)
+    _check_gate(gate, q)
     prob = problem(q, grid)
     info = plan(prob, cfg)
     out = _new_out(q, cfg) if out is None else out
     ws = workspace(q.device, info.workspace_bytes)
     c = cfg.c()
     _check(lib().rola_lowrank_attn(ctypes.byref(prob), ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(wq),
-                                   _ptr(wk), _ptr(out), int(bool(accumulate)), _ptr(ws), ws.numel(),
+                                   _ptr(wk), _ptr(gate), _ptr(out), int(bool(accumulate)), _ptr(ws), ws.numel(),
                                    _stream(stream)), "rola_lowrank_attn")
     return out
 
 
-def rola_forward(q, k, v, wq, wk, grid, cfg: Config, out=None, block_idx_out=None, stream=None):
-    """Fused RoLA forward O = O_sparse + O_lr."""
+def rola_forward(q, k, v, wq, wk, grid, cfg: Config, out=None, block_idx_out=None, stream=None,
+                 gate=None):
+    """Fused RoLA forward O = O_sparse + g * O_lr (g = sigmoid(q . w + b) with ``gate``, else 1)."""
     _check_tokens(q, k, v)
+    _check_gate(gate, q)
     prob = problem(q, grid)
     info = plan(prob, cfg)
     out = _new_out(q, cfg) if out is None else out
     ws = workspace(q.device, info.workspace_bytes)
     c = cfg.c()
     _check(lib().rola_forward(ctypes.byref(prob), ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(wq),
-                              _ptr(wk), _ptr(block_idx_out), _ptr(out), _ptr(ws), ws.numel(),
+                              _ptr(wk), _ptr(gate), _ptr(block_idx_out), _ptr(out), _ptr(ws), ws.numel(),
                               _stream(stream)), "rola_forward")
     return out
 

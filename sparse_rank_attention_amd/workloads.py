@@ -19,10 +19,12 @@ Recipes
   V ~ N(0, 1).  The smooth part makes pooled block energies non-uniform, as
   in real video latents, so the top-k selection has structure to find.
 * Low-rank projections Wq, Wk (fp32, [D, r], shared by all heads) ~ N(0, 1/D).
+* Output gate (fp32 [D+1]: weights ~ N(0, 1/D), then a bias ~ N(0, 1/4)), so
+  that sigmoid(q . w + b) spreads over (0, 1) for unit-variance queries.
 
 Every (batch, head, tensor) draws from ``numpy.random.default_rng([seed, b, h,
 tid])`` (tid 0=Q, 1=K, 2=V) and the projections from ``default_rng([seed, 100+tid])``
-(tid 3=Wq, 4=Wk), so any head can be regenerated on its own.  Tokens are in
+(tid 3=Wq, 4=Wk, 5=gate), so any head can be regenerated on its own.  Tokens are in
 raster (t, h, w) order; rows from N up to the padded length are zero.
 """
 from __future__ import annotations
@@ -154,6 +156,15 @@ def make_proj(w: Workload):
         rng = np.random.default_rng([w.seed, 100 + tid])
         out.append((rng.standard_normal(size=(w.head_dim, w.rank)) / np.sqrt(w.head_dim)).astype(np.float32))
     return out[0], out[1]
+
+
+def make_gate(w: Workload):
+    """Output gate [w_0 .. w_{D-1}, b]: float32 [D+1], weights ~ N(0, 1/D), bias ~ N(0, 1/4)."""
+    rng = np.random.default_rng([w.seed, 105])
+    g = rng.standard_normal(size=w.head_dim + 1)
+    g[:w.head_dim] /= np.sqrt(w.head_dim)
+    g[w.head_dim] *= 0.5
+    return g.astype(np.float32)
 
 
 def bf16_bits_to_f32(x: np.ndarray) -> np.ndarray:

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     for name in _declared_functions():
         assert hasattr(L, name), name
     assert set(rola.EXPORTS) == set(_declared_functions())
-    assert L.rola_abi_version() == 1
+    assert L.rola_abi_version() == rola.ABI_VERSION == 2
 
 
 def _prob(B=1, H=40, D=128, grid=(21, 45, 80), sn=None):
@@ -91,13 +91,19 @@ def test_entry_points_validate_before_launch():
     null = ctypes.c_void_p(0)
     big = info.workspace_bytes
     # null pointers
-    assert L.rola_forward(P(prob), P(cfg), null, fake, fake, fake, fake, null, fake, fake, big, null) == 1
+    assert L.rola_forward(P(prob), P(cfg), null, fake, fake, fake, fake, null, null, fake, fake, big, null) == 1
     assert L.rola_select_blocks(P(prob), P(cfg), fake, fake, null, null, fake, big, null) == 1
     # misaligned tensors
     assert L.rola_sparse_attn(P(prob), P(cfg), odd, fake, fake, fake, fake, 0, fake, big, null) == 3
     # workspace too small or missing
-    assert L.rola_forward(P(prob), P(cfg), fake, fake, fake, fake, fake, null, fake, fake, big - 1, null) == 4
-    assert L.rola_lowrank_attn(P(prob), P(cfg), fake, fake, fake, fake, fake, fake, 0, null, big, null) == 4
+    assert L.rola_forward(P(prob), P(cfg), fake, fake, fake, fake, fake, null, null, fake, fake, big - 1,
+                          null) == 4
+    assert L.rola_lowrank_attn(P(prob), P(cfg), fake, fake, fake, fake, fake, null, fake, 0, null, big,
+                               null) == 4
+    # the output gate is read as 16-byte vectors
+    assert L.rola_forward(P(prob), P(cfg), fake, fake, fake, fake, fake, odd, null, fake, fake, big, null) == 3
+    assert L.rola_lowrank_attn(P(prob), P(cfg), fake, fake, fake, fake, fake, odd, fake, 0, fake, big,
+                               null) == 3
     # bad accumulate flag
     assert L.rola_sparse_attn(P(prob), P(cfg), fake, fake, fake, fake, fake, 2, fake, big, null) == 1
     # status strings
