@@ -56,7 +56,10 @@ def lib():
             "ro_e4m3_encode": ([ctypes.c_float], ctypes.c_uint8),
             "ro_quant_e4m3": ([P, I64, I64, I64, I32, P, P, P], None),
             "ro_gate": ([P, P, I32], D),
-            "ro_forward": ([P, P, P, P, P, P, I64, I64, I64, I32, I32, I32, P, P, D, D, I32, P, P], None),
+            "ro_lowrank_block_states": ([P, P, P, I64, I64, I32, I32, P, P, D, P, P], None),
+            "ro_lowrank_rows_complement": ([P, P, P, P, P, I32, I64, I32, I32, P, P, D, I64, P, P], None),
+            "ro_forward": ([P, P, P, P, P, P, I64, I64, I64, I32, I32, I32, P, P, D, D, I32, I32, P, P],
+                           None),
         }
         for name, (args, res) in sigs.items():
             f = getattr(L, name)
@@ -192,6 +195,41 @@ def lowrank_rows(q, wq, S, z, grid, rows, split=None, theta=10000.0, gate_w=None
     return out
 
 
+def lowrank_block_states(k, v, wk, n_valid: int, grid, split=None, theta=10000.0):
+    """Per-block low-rank states of one (batch, head): (Sb [nb, r, D], zb [nb, r])."""
+    k, v, wk = _c(k, np.float64), _c(v, np.float64), _c(wk, np.float32)
+    n_pad, d = k.shape[-2:]
+    r = wk.shape[1]
+    split = default_split(d) if split is None else split
+    nb = n_pad // BLOCK
+    Sb = np.zeros((nb, r, d), dtype=np.float64)
+    zb = np.zeros((nb, r), dtype=np.float64)
+    lib().ro_lowrank_block_states(_p(k), _p(v), _p(wk), n_pad, n_valid, d, r, _p(_c(grid, np.int32)),
+                                  _p(_c(split, np.int32)), theta, _p(Sb), _p(zb))
+    return Sb, zb
+
+
+def lowrank_rows_complement(q, wq, Sb, zb, bmap, grid, rows, split=None, theta=10000.0,
+                            gate_w=None) -> np.ndarray:
+    """Complement-scope low-rank output of rows n of one (batch, head): the state of
+    query block n // 64 covers the blocks its row of ``bmap`` [nb, kb] does not keep."""
+    q, wq = _c(q, np.float64), _c(wq, np.float32)
+    Sb, zb, bmap = _c(Sb, np.float64), _c(zb, np.float64), _c(bmap, np.int32)
+    rows = _c(rows, np.int64)
+    n_pad, d = q.shape[-2:]
+    r = wq.shape[1]
+    split = default_split(d) if split is None else split
+    out = np.zeros((rows.size, d), dtype=np.float64)
+    lib().ro_lowrank_rows_complement(_p(q), _p(wq), _p(Sb), _p(zb), _p(bmap), bmap.shape[-1], n_pad, d, r,
+                                     _p(_c(grid, np.int32)), _p(_c(split, np.int32)), theta, rows.size,
+                                     _p(rows), _p(out))
+    if gate_w is not None:
+        qf = q.reshape(-1, d)
+        for i, row in enumerate(rows):
+            out[i] *= gate(qf[row], gate_w)
+    return out
+
+
 def e4m3_value(code: int) -> float:
     return lib().ro_e4m3_value(code)
 
@@ -211,10 +249,11 @@ def quant_e4m3(x_bits, n_valid: int):
 
 
 def forward(q_bits, k_bits, v_bits, wq, wk, n_valid: int, kb: int, grid, split=None,
-            theta=10000.0, scale=None, fp8=False, gate_w=None):
+            theta=10000.0, scale=None, fp8=False, gate_w=None, complement=False):
     """Whole RoLA forward.  Returns (block map [BH, nb, kb] int32, out [BH, n_pad, D] float64).
 
-    ``gate_w`` (fp32 [D+1], optional): output gate on the low-rank term."""
+    ``gate_w`` (fp32 [D+1], optional): output gate on the low-rank term.
+    ``complement``: low-rank state over each query block's unkept blocks only."""
     q, k, v = _c(q_bits, np.uint16), _c(k_bits, np.uint16), _c(v_bits, np.uint16)
     wq, wk = _c(wq, np.float32), _c(wk, np.float32)
     bh, n_pad, d = q.shape
@@ -225,7 +264,7 @@ def forward(q_bits, k_bits, v_bits, wq, wk, n_valid: int, kb: int, grid, split=N
     out = np.zeros((bh, n_pad, d), dtype=np.float64)
     gw = None if gate_w is None else _c(gate_w, np.float32)
     assert gw is None or gw.shape == (d + 1,)
-    lib().ro_forward(_p(q), _p(k), _p(v), _p(wq), _p(wk), None if gw is None else _p(gw), bh, n_pad, n_valid, d, r, kb,
-                     _p(_c(grid, np.int32)), _p(_c(split, np.int32)), theta, scale, int(fp8),
-                     _p(bmap), _p(out))
+    lib().ro_forward(_p(q), _p(k), _p(v), _p(wq), _p(wk), None if gw is None else _p(gw), bh, n_pad, n_valid,
+                     d, r, kb, _p(_c(grid, np.int32)), _p(_c(split, np.int32)), theta, scale, int(fp8),
+                     int(bool(complement)), _p(bmap), _p(out))
     return bmap, out

@@ -32,7 +32,9 @@
  *    (x[o+2p], x[o+2p+1]) rotated by pos * theta^(-2p/d_axis);
  *  - features phi(x) = elu(x) + 1; the linear branch is normalised,
  *    O_lr = (a^T S)/(a^T z), S = sum_n b_n v_n^T, z = sum_n b_n over all N
- *    valid keys; one state per (batch, head);
+ *    valid keys; one state per (batch, head) (the global scope; the
+ *    complement scope, where each query block's state covers only the key
+ *    blocks it does not keep, is the alternative reading, selected per call);
  *  - output = sparse + low-rank for rows < N, zero for padded rows;
  *  - optional learned output gate on the low-rank term (README
  *    "AlibabaResearch/SparkDiffusion", sparse-finetune section, names the
@@ -296,6 +298,77 @@ void ro_lowrank_rows(const double *q, const float *wq, const double *S, const do
   }
 }
 
+/*
+ * Complement scope of the low-rank branch (an alternative reading of the
+ * article's statement that the linear branch restores the context that
+ * sparsification drops): the state a query block sees covers only the key
+ * blocks it does NOT keep.  Per-block states of one (batch, head):
+ * Sb[j][r][d] = sum over the valid tokens n of block j of b_n[r] v_n[d],
+ * zb[j][r] = sum of b_n[r] over the same tokens.
+ */
+void ro_lowrank_block_states(const double *k, const double *v, const float *wk, int64_t n_pad,
+                             int64_t n_valid, int d_model, int rank, const int32_t *grid,
+                             const int32_t *split, double theta, double *Sb, double *zb) {
+  const int64_t nb = n_pad / RO_BLOCK;
+#pragma omp parallel for schedule(static)
+  for (int64_t j = 0; j < nb; ++j) {
+    double rot[512], f[64];
+    double *S = Sb + j * rank * d_model, *z = zb + j * rank;
+    for (int64_t i = 0; i < (int64_t)rank * d_model; ++i) S[i] = 0.0;
+    for (int r = 0; r < rank; ++r) z[r] = 0.0;
+    for (int64_t n = j * RO_BLOCK; n < (j + 1) * RO_BLOCK && n < n_valid; ++n) {
+      lowrank_feature(k + n * d_model, n, grid, split, theta, wk, d_model, rank, rot, f);
+      for (int r = 0; r < rank; ++r) {
+        z[r] += f[r];
+        for (int d = 0; d < d_model; ++d) S[r * d_model + d] += f[r] * v[n * d_model + d];
+      }
+    }
+  }
+}
+
+/* Complement-scope low-rank rows of one (batch, head): a row of query block i
+ * uses S_i = sum of Sb[j] over the blocks j not in map[i] (z_i likewise), and
+ * O_lr = (a^T S_i) / (a^T z_i); when i keeps every block the branch is 0. */
+void ro_lowrank_rows_complement(const double *q, const float *wq, const double *Sb,
+                                const double *zb, const int32_t *map, int kb, int64_t n_pad,
+                                int d_model, int rank, const int32_t *grid, const int32_t *split,
+                                double theta, int64_t nrows, const int64_t *rows, double *out) {
+  const int64_t nb = n_pad / RO_BLOCK;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < nrows; ++r) {
+    double rot[512], a[64], z[64];
+    double *S = (double *)malloc(sizeof(double) * rank * d_model);
+    const int64_t n = rows[r], i = n / RO_BLOCK;
+    const int32_t *kept = map + i * kb;
+    for (int64_t e = 0; e < (int64_t)rank * d_model; ++e) S[e] = 0.0;
+    for (int c = 0; c < rank; ++c) z[c] = 0.0;
+    int64_t left = 0;
+    for (int64_t j = 0; j < nb; ++j) {
+      int is_kept = 0;
+      for (int t = 0; t < kb; ++t) is_kept |= kept[t] == j;
+      if (is_kept) continue;
+      ++left;
+      for (int64_t e = 0; e < (int64_t)rank * d_model; ++e) S[e] += Sb[j * rank * d_model + e];
+      for (int c = 0; c < rank; ++c) z[c] += zb[j * rank + c];
+    }
+    double *o = out + r * d_model;
+    if (left == 0) {
+      for (int d = 0; d < d_model; ++d) o[d] = 0.0;
+      free(S);
+      continue;
+    }
+    lowrank_feature(q + n * d_model, n, grid, split, theta, wq, d_model, rank, rot, a);
+    double den = 0.0;
+    for (int c = 0; c < rank; ++c) den += a[c] * z[c];
+    for (int d = 0; d < d_model; ++d) {
+      double num = 0.0;
+      for (int c = 0; c < rank; ++c) num += a[c] * S[c * d_model + d];
+      o[d] = num / den;
+    }
+    free(S);
+  }
+}
+
 /* Output gate of one token: sigmoid(b + sum_d q[d] w[d]), gate = [w_0 .. w_{D-1}, b]. */
 double ro_gate(const double *q, const float *gate, int d_model) {
   double u = (double)gate[d_model];
@@ -384,12 +457,14 @@ static void widen(const uint16_t *x, int64_t count, double *y) {
  * fp8 != 0 runs the sparse branch on the e4m3-dequantised Q, K, V; selection
  * and the low-rank branch always use the bf16 values.  gate (fp32 [D+1], may
  * be NULL for no gate) scales the low-rank term by ro_gate of the bf16 query.
+ * complement != 0 takes the low-rank state over the unkept blocks of each
+ * query block (ro_lowrank_rows_complement) instead of all blocks.
  */
 void ro_forward(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *wq,
                 const float *wk, const float *gate, int64_t bh_count, int64_t n_pad,
                 int64_t n_valid, int d_model, int rank, int kb, const int32_t *grid,
-                const int32_t *split, double theta, double scale, int fp8, int32_t *map_out,
-                double *out) {
+                const int32_t *split, double theta, double scale, int fp8, int complement,
+                int32_t *map_out, double *out) {
   const int64_t nb = n_pad / RO_BLOCK;
   const int64_t per = n_pad * d_model;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -416,6 +491,12 @@ void ro_forward(const uint16_t *q, const uint16_t *k, const uint16_t *v, const f
     widen(kbf, per, kd);
     widen(vb, per, vd);
     ro_lowrank_state(kd, vd, wk, 1, n_pad, n_valid, d_model, rank, grid, split, theta, S, z);
+    double *Sb = NULL, *zb = NULL;
+    if (complement) {
+      Sb = (double *)malloc(sizeof(double) * nb * rank * d_model);
+      zb = (double *)malloc(sizeof(double) * nb * rank);
+      ro_lowrank_block_states(kd, vd, wk, n_pad, n_valid, d_model, rank, grid, split, theta, Sb, zb);
+    }
 
     double *qs = qd, *ks = kd, *vs = vd;
     uint8_t *codes = NULL;
@@ -440,7 +521,11 @@ void ro_forward(const uint16_t *q, const uint16_t *k, const uint16_t *v, const f
       sparse_row(qs + n * d_model, ks, vs, map + (n / RO_BLOCK) * kb, kb, n_valid, d_model, scale,
                  on, buf);
       const int64_t row = n; /* rows are relative to this slice */
-      ro_lowrank_rows(qd, wq, S, z, n_pad, d_model, rank, grid, split, theta, 1, &row, lr);
+      if (complement)
+        ro_lowrank_rows_complement(qd, wq, Sb, zb, map, kb, n_pad, d_model, rank, grid, split,
+                                   theta, 1, &row, lr);
+      else
+        ro_lowrank_rows(qd, wq, S, z, n_pad, d_model, rank, grid, split, theta, 1, &row, lr);
       const double g = gate ? ro_gate(qd + n * d_model, gate, d_model) : 1.0;
       for (int d = 0; d < d_model; ++d) on[d] += g * lr[d];
     }
@@ -448,6 +533,6 @@ void ro_forward(const uint16_t *q, const uint16_t *k, const uint16_t *v, const f
       free(codes); free(scl); free(qs); free(ks); free(vs);
     }
     free(qp); free(kp); free(sc); free(qd); free(kd); free(vd);
-    free(S); free(z); free(lr); free(buf);
+    free(S); free(z); free(lr); free(buf); free(Sb); free(zb);
   }
 }

@@ -315,3 +315,82 @@ def test_quant_round_trip_bound(oracle_lib):
             assert np.all(err <= bound)
             assert np.isclose(np.abs(deq[bh, lo:hi]).max(), 448.0 * scale[bh, c], rtol=1e-6)
     assert np.all(codes[:, n_valid:] == 0)
+
+
+# ------------------------------------------------------- complement scope
+def _tiny_complement_case(rng, n_valid, n_pad, d, r):
+    _, q = _bf16(rng, (n_pad, d))
+    _, k = _bf16(rng, (n_pad, d))
+    _, v = _bf16(rng, (n_pad, d))
+    wq = (rng.standard_normal((d, r)) / 8).astype(np.float32)
+    wk = (rng.standard_normal((d, r)) / 8).astype(np.float32)
+    return q, k, v, wq, wk
+
+
+def test_block_states_partition_the_global_state(oracle_lib):
+    rng = np.random.default_rng(51)
+    grid = (3, 7, 11)  # N = 231: four blocks, the last with 39 tokens
+    n_valid, n_pad, d, r = 231, 256, 64, 16
+    _, k, v, _, wk = _tiny_complement_case(rng, n_valid, n_pad, d, r)
+    Sb, zb = oracle_lib.lowrank_block_states(k, v, wk, n_valid, grid)
+    S, z = oracle_lib.lowrank_state(k[None], v[None], wk, n_valid, grid)
+    np.testing.assert_allclose(Sb.sum(axis=0), S[0], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(zb.sum(axis=0), z[0], rtol=1e-12)
+    # block 3 holds exactly tokens 192..230
+    b = np.stack([oracle_lib.lowrank_feature(k[n], n, grid, wk) for n in range(192, 231)])
+    np.testing.assert_allclose(zb[3], b.sum(axis=0), rtol=1e-12)
+    np.testing.assert_allclose(Sb[3], b.T @ v[192:231], rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("kb", [1, 2, 4])
+def test_complement_matches_token_quadratic_form(oracle_lib, kb):
+    """Row n of query block i: sum over valid tokens m outside i's kept blocks of
+    (a_n . b_m) v_m, over the sum of a_n . b_m (kb = nb leaves nothing: 0)."""
+    rng = np.random.default_rng(53 + kb)
+    grid = (3, 7, 11)
+    n_valid, n_pad, d, r = 231, 256, 64, 16
+    q, k, v, wq, wk = _tiny_complement_case(rng, n_valid, n_pad, d, r)
+    nb = n_pad // 64
+    bmap = np.stack([np.sort(rng.choice(nb, size=kb, replace=False)) for _ in range(nb)]).astype(np.int32)
+    Sb, zb = oracle_lib.lowrank_block_states(k, v, wk, n_valid, grid)
+    rows = np.arange(n_valid)
+    got = oracle_lib.lowrank_rows_complement(q, wq, Sb, zb, bmap, grid, rows)
+    a = np.stack([oracle_lib.lowrank_feature(q[n], n, grid, wq) for n in range(n_valid)])
+    b = np.stack([oracle_lib.lowrank_feature(k[m], m, grid, wk) for m in range(n_valid)])
+    for n in rows:
+        keep = np.isin(np.arange(n_valid) // 64, bmap[n // 64], invert=True)
+        if not keep.any():
+            assert np.all(got[n] == 0)
+            continue
+        wts = b[keep] @ a[n]
+        ref = wts @ v[:n_valid][keep] / wts.sum()
+        np.testing.assert_allclose(got[n], ref, rtol=1e-10, atol=1e-12)
+
+
+def test_forward_complement_scope(oracle_lib):
+    """Whole forward: constant V still gives twice the constant, keeping every
+    block leaves the sparse branch alone, and the output is the sum of the parts."""
+    from sparse_rank_attention_amd.workloads import WORKLOADS, make_proj, make_qkv
+    w = WORKLOADS["tiny"]
+    q, k, v = (x[0] for x in make_qkv(w))
+    wq, wk = make_proj(w)
+    n_valid = w.n_tokens - 37
+    cval = to_bf16_bits(np.array([0.75], dtype=np.float32))[0]
+    _, out = oracle_lib.forward(q, k, np.full_like(v, cval), wq, wk, n_valid, w.kb, w.grid, complement=True)
+    np.testing.assert_allclose(out[:, :n_valid], 1.5, rtol=1e-12)
+    qd, kd, vd = (oracle_lib.widen_bf16(x) for x in (q, k, v))
+    bmap, out = oracle_lib.forward(q, k, v, wq, wk, n_valid, w.nb, w.grid, complement=True)
+    rows = np.arange(q.shape[0] * w.n_pad)
+    valid = (rows % w.n_pad) < n_valid
+    sp = oracle_lib.sparse_rows(qd, kd, vd, bmap, n_valid, rows)
+    np.testing.assert_allclose(out.reshape(-1, w.head_dim)[valid], sp[valid], rtol=1e-12, atol=1e-14)
+    g = (np.arange(w.head_dim + 1) % 5 - 2).astype(np.float32) / 8
+    bmap, out = oracle_lib.forward(q, k, v, wq, wk, n_valid, w.kb, w.grid, complement=True, gate_w=g)
+    sp = oracle_lib.sparse_rows(qd, kd, vd, bmap, n_valid, rows)
+    for bh in range(q.shape[0]):
+        Sb, zb = oracle_lib.lowrank_block_states(kd[bh], vd[bh], wk, n_valid, w.grid)
+        lr = oracle_lib.lowrank_rows_complement(qd[bh], wq, Sb, zb, bmap[bh], w.grid, np.arange(n_valid),
+                                                gate_w=g)
+        np.testing.assert_allclose(out[bh, :n_valid], sp[bh * w.n_pad:bh * w.n_pad + n_valid] + lr,
+                                   rtol=1e-12, atol=1e-14)
+    assert np.all(out[:, n_valid:] == 0)
