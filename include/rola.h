@@ -26,7 +26,10 @@
  *  - low-rank branch: a = phi(Wq^T R(q)), b = phi(Wk^T R(k)), phi = elu + 1,
  *    R the 3-D rotary embedding (dims split t/h/w, interleaved pairs, base
  *    theta); S = sum_{n<N} b_n v_n^T, z = sum_{n<N} b_n per (batch, head);
- *    O_lr = (a^T S) / (a^T z);
+ *    O_lr = (a^T S) / (a^T z).  With config.lowrank_scope =
+ *    ROLA_LR_COMPLEMENT the sums of query block i run only over the valid
+ *    tokens of the key blocks i does NOT keep (the article's "context the
+ *    sparse branch drops" read literally), and O_lr = 0 when i keeps all;
  *  - output O = O_sparse + g * O_lr for rows < N; rows N..n_pad-1 are written 0.
  *    g is the optional learned output gate (README "AlibabaResearch/
  *    SparkDiffusion", sparse-finetune section, names the trainable gate_proj
@@ -60,7 +63,7 @@
 extern "C" {
 #endif
 
-#define ROLA_ABI_VERSION 2
+#define ROLA_ABI_VERSION 3
 #define ROLA_BLOCK 64
 #define ROLA_MAX_BLOCKS 4096 /* nb limit: N <= 262144 tokens */
 
@@ -76,6 +79,7 @@ typedef enum rola_status {
 
 enum { ROLA_PREC_BF16 = 0, ROLA_PREC_FP8 = 1 };
 enum { ROLA_OUT_BF16 = 0, ROLA_OUT_F32 = 1 };
+enum { ROLA_LR_GLOBAL = 0, ROLA_LR_COMPLEMENT = 1 };
 
 typedef struct rola_problem {
   int32_t batch, heads, head_dim;
@@ -92,6 +96,7 @@ typedef struct rola_config {
   float softmax_scale; /* <= 0: 1/sqrt(D) */
   int32_t precision;   /* ROLA_PREC_BF16 or ROLA_PREC_FP8 (e4m3, per-block absmax scales) */
   int32_t out_dtype;   /* ROLA_OUT_BF16 or ROLA_OUT_F32 */
+  int32_t lowrank_scope; /* ROLA_LR_GLOBAL (one state per head) or ROLA_LR_COMPLEMENT */
 } rola_config;
 
 typedef struct rola_plan_info {
@@ -140,7 +145,8 @@ int32_t rola_sparse_attn(const rola_problem *prob, const rola_config *cfg, const
  * "AlibabaResearch/SparkDiffusion", sparse-finetune section: the added
  * query and key projections).
  * O = g * O_lr (accumulate = 0) or O += g * O_lr (accumulate = 1); gate NULL
- * means g = 1.
+ * means g = 1.  In the complement scope this call also selects the blocks
+ * (as rola_select_blocks does) to know what each query block keeps.
  */
 int32_t rola_lowrank_attn(const rola_problem *prob, const rola_config *cfg, const void *q,
                           const void *k, const void *v, const float *wq, const float *wk,

@@ -38,6 +38,8 @@ struct Plan {
       off_z, off_ugroup, off_ucount, off_ulist, total;
   bool fp8;
   int64_t off_qsc, off_ksc, off_vsc, off_kv8;  // fp8 only
+  bool comp;  // complement scope of the low-rank branch
+  int64_t off_blk, off_s32, off_stc, off_zc;  // complement scope only
 };
 
 int32_t make_plan(const rola_problem *p, const rola_config *c, Plan *pl) {
@@ -48,6 +50,8 @@ int32_t make_plan(const rola_problem *p, const rola_config *c, Plan *pl) {
   if (c->rank != 16 && c->rank != 32) return ROLA_ERR_UNSUPPORTED;
   if (c->precision != ROLA_PREC_BF16 && c->precision != ROLA_PREC_FP8) return ROLA_ERR_INVALID_ARG;
   if (c->out_dtype != ROLA_OUT_BF16 && c->out_dtype != ROLA_OUT_F32) return ROLA_ERR_INVALID_ARG;
+  if (c->lowrank_scope != ROLA_LR_GLOBAL && c->lowrank_scope != ROLA_LR_COMPLEMENT)
+    return ROLA_ERR_INVALID_ARG;
   const int D = p->head_dim;
   const int64_t N = (int64_t)p->grid_t * p->grid_h * p->grid_w;
   const int64_t nb64 = (N + ROLA_BLOCK - 1) / ROLA_BLOCK;
@@ -117,6 +121,14 @@ int32_t make_plan(const rola_problem *p, const rola_config *c, Plan *pl) {
     P.off_ksc = o; o = align_up(o + P.BH * nb * 4);
     P.off_vsc = o; o = align_up(o + P.BH * nb * 4);
     P.off_kv8 = o; o = align_up(o + P.BH * nb * 128LL * D);
+  }
+  P.comp = c->lowrank_scope == ROLA_LR_COMPLEMENT;
+  P.off_blk = P.off_s32 = P.off_stc = P.off_zc = 0;
+  if (P.comp) {
+    P.off_blk = o; o = align_up(o + P.BH * nb * (int64_t)(D * 32 + 32) * 4);
+    P.off_s32 = o; o = align_up(o + P.BH * D * 32LL * 4);
+    P.off_stc = o; o = align_up(o + P.BH * nb * (int64_t)D * 32 * 2);
+    P.off_zc = o; o = align_up(o + P.BH * nb * 32LL * 4);
   }
   P.total = o;
   return ROLA_OK;
@@ -199,12 +211,15 @@ int32_t run_pass1(const Plan &P, const rola_problem *p, const void *q, const voi
   a.kp = (float *)(ws + P.off_kp);
   a.wkT = (const uint16_t *)(ws + P.off_wkT);
   a.state_part = (float *)(ws + P.off_part);
+  a.blk_state = (P.comp && pool && state) ? (float *)(ws + P.off_blk) : nullptr;
   a.rope = rope_args(P, ws);
   a.qsc = (float *)(ws + P.off_qsc);
   a.ksc = (float *)(ws + P.off_ksc);
   a.vsc = (float *)(ws + P.off_vsc);
   a.kv8 = ws + P.off_kv8;
-  const char *name = (pool && state) ? (quant ? "pass1_pool_state_quant8" : "pass1_pool_state")
+  const char *name = (pool && state) ? (quant ? (a.blk_state ? "pass1_pool_blkstate_quant8"
+                                                            : "pass1_pool_state_quant8")
+                                              : (a.blk_state ? "pass1_pool_blkstate" : "pass1_pool_state"))
                      : pool          ? "pass1_pool"
                                      : "pass1_state";
   return timed(name, st, [&] { rola::launch_pass1(a, P.D, P.nchunks, (int)P.BH, pool, state, quant, st); });
@@ -212,8 +227,11 @@ int32_t run_pass1(const Plan &P, const rola_problem *p, const void *q, const voi
 
 int32_t run_reduce(const Plan &P, uint8_t *ws, hipStream_t st) {
   return timed("state_reduce", st, [&] {
-    rola::launch_state_reduce((const float *)(ws + P.off_part), P.nchunks, P.D, P.r, (int)P.BH,
-                              (uint16_t *)(ws + P.off_st), (float *)(ws + P.off_z), st);
+    // complement scope: pass 1 wrote per-block states instead of chunk partials
+    rola::launch_state_reduce(P.comp ? (const float *)(ws + P.off_blk) : (const float *)(ws + P.off_part),
+                              P.comp ? P.nb : 2 * P.nchunks, P.D, P.r, (int)P.BH,
+                              (uint16_t *)(ws + P.off_st), (float *)(ws + P.off_z),
+                              P.comp ? (float *)(ws + P.off_s32) : nullptr, st);
   });
 }
 
@@ -259,12 +277,13 @@ int32_t run_attn(const Plan &P, const rola_problem *p, const rola_config *c, con
   a.st = (const uint16_t *)(ws + P.off_st);
   a.z = (const float *)(ws + P.off_z);
   a.gate = lowrank ? gate : nullptr;
+  a.complement = (lowrank && P.comp) ? 1 : 0;
   a.rope = rope_args(P, ws);
   a.kv8 = ws + P.off_kv8;
   a.qsc = (const float *)(ws + P.off_qsc);
   a.ksc = (const float *)(ws + P.off_ksc);
   a.vsc = (const float *)(ws + P.off_vsc);
-  if (sparse) {
+  if (sparse || a.complement) {
     int32_t s = timed("schedule", st, [&] {
       rola::launch_schedule(map, P.nb, P.kb, P.G, (int)P.ngroups, (int)P.list_stride, (int)P.BH,
                             (int32_t *)(ws + P.off_ugroup), (int32_t *)(ws + P.off_ucount),
@@ -279,6 +298,23 @@ int32_t run_attn(const Plan &P, const rola_problem *p, const rola_config *c, con
                             (int32_t *)(ws + P.off_ulist), st);
     });
     if (s != ROLA_OK) return s;
+  }
+  if (a.complement) {
+    // per query block: the global state minus the states of its kept blocks
+    rola::CompArgs ca;
+    ca.blk = (const float *)(ws + P.off_blk);
+    ca.s32 = (const float *)(ws + P.off_s32);
+    ca.z = (const float *)(ws + P.off_z);
+    ca.ugroup = a.ugroup; ca.ucount = a.ucount; ca.ulist = a.ulist;
+    ca.nb = P.nb; ca.kb = P.kb;
+    ca.bh_count = P.BH; ca.ngroups = P.ngroups; ca.groups_per_xcd = a.groups_per_xcd;
+    ca.list_stride = P.list_stride;
+    ca.stc = (uint16_t *)(ws + P.off_stc);
+    ca.zc = (float *)(ws + P.off_zc);
+    int32_t s = timed("complement", st, [&] { rola::launch_complement(ca, P.D, st); });
+    if (s != ROLA_OK) return s;
+    a.st = ca.stc;
+    a.z = ca.zc;
   }
   if (sparse && P.fp8) {
     const char *name8 = lowrank ? "attn8_sparse_lowrank" : "attn8_sparse";
@@ -382,6 +418,15 @@ int32_t rola_lowrank_attn(const rola_problem *prob, const rola_config *cfg, cons
   hipStream_t st = (hipStream_t)stream;
   uint8_t *ws = (uint8_t *)workspace;
   ROLA_TRY(run_setup(P, wq, wk, ws, st));
+  if (P.comp) {
+    // the complement needs the block map: pool Q and K in the same pass
+    ROLA_TRY(run_pass1(P, prob, q, k, v, ws, true, true, st));
+    ROLA_TRY(run_reduce(P, ws, st));
+    int32_t *map = (int32_t *)(ws + P.off_map);
+    ROLA_TRY(run_select(P, ws, (float *)(ws + P.off_scores), map, st));
+    return run_attn(P, prob, cfg, q, nullptr, nullptr, map, gate, out, ws, false, true,
+                    accumulate != 0, st);
+  }
   ROLA_TRY(run_pass1(P, prob, nullptr, k, v, ws, false, true, st));
   ROLA_TRY(run_reduce(P, ws, st));
   return run_attn(P, prob, cfg, q, nullptr, nullptr, nullptr, gate, out, ws, false, true,

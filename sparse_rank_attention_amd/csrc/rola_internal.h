@@ -30,6 +30,7 @@ struct Pass1Args {
   float *qp, *kp;       // pooled [BH][nb][D]
   const uint16_t *wkT;  // bf16 [32][D]
   float *state_part;    // [BH][nchunks][2][D*32 + 32]
+  float *blk_state;     // complement scope: [BH][nb][D*32 + 32] per-block states, else NULL
   RopeArgsHost rope;
   // fp8 mode (see Quant8Args): Q scales, K and V^T codes of each block
   float *qsc, *ksc, *vsc;
@@ -89,6 +90,7 @@ struct AttnArgs {
   const uint16_t *st;   // bf16 [BH][D][32] (rank permuted)
   const float *z;       // [BH][32]
   const float *gate;    // fp32 [D+1] output gate (w, then b) on the low-rank term; NULL: none
+  int complement;       // st and z hold one state per query block ([BH][nb][D][32], [BH][nb][32])
   RopeArgsHost rope;
   // fp8 sparse branch only
   const uint8_t *kv8;   // tile images, see Quant8Args
@@ -97,9 +99,23 @@ struct AttnArgs {
 
 void launch_setup(const SetupArgs &a, hipStream_t st);
 void launch_pass1(const Pass1Args &a, int D, int nchunks, int bh, bool pool, bool state, bool quant,
-                  hipStream_t st);
-void launch_state_reduce(const float *part, int nchunks, int D, int rank, int bh, uint16_t *st_out,
-                         float *z, hipStream_t st);
+                  hipStream_t st);  // per-block states as well when a.blk_state is set
+// part: np partial states per head ([BH][np][D*32 + 32])
+void launch_state_reduce(const float *part, int np, int D, int rank, int bh, uint16_t *st_out,
+                         float *z, float *s32, hipStream_t st);
+
+// Complement scope: per query block, the global state minus the states of its
+// kept key blocks, gathered along the attention schedule's union lists.
+struct CompArgs {
+  const float *blk;        // [BH][nb][D*32 + 32] per-block S (d-major, rank inner) then z
+  const float *s32, *z;    // global S [BH][D*32] and z [BH][32]
+  const int32_t *ugroup, *ucount, *ulist;
+  int nb, kb;
+  int64_t bh_count, ngroups, groups_per_xcd, list_stride;
+  uint16_t *stc;           // out: bf16 [BH][nb][D][32], rank-permuted like st
+  float *zc;               // out: [BH][nb][32]
+};
+void launch_complement(const CompArgs &a, int D, hipStream_t st);
 void launch_scores(const float *qp, const float *kp, float *s, int nb, int D, int bh,
                    hipStream_t st);
 void launch_topk(const float *s, int32_t *map, int nb, int kb, int64_t rows, hipStream_t st);

@@ -12,6 +12,8 @@
 //                  of Q and K (fixed fp32 tree order) and low-rank state
 //                  partials from K and V (MFMA)
 //   k_state_reduce fixed-order sum of the state partials
+//   k_complement   (complement scope) per query block: global state minus
+//                  the states of its kept key blocks
 //   k_scores       pooled block scores, sequential fp32 fma chain (VALU)
 //   k_topk         per-row radix select of the kept key blocks (one wave/row)
 //   k_order        per head: query blocks ordered by similarity of their maps
@@ -370,7 +372,7 @@ static __device__ __forceinline__ int img_v_off(int d, int p) {
 //          LDS transpose (see k_quant8 for the image layout and rounding).
 // Rows past N are read as zero (pooling) or taken from row N-1 (finite
 // values; their b is masked to 0).
-template <int D, bool POOL, bool STATE, bool QUANT>
+template <int D, bool POOL, bool STATE, bool QUANT, bool BLK>
 __global__ __launch_bounds__(QUANT ? 320 : 256) void k_pass1(Pass1Args args) {
   constexpr int CH = D / 8;       // 16-byte chunks per token row
   constexpr int NS = D / 16;      // MFMA k-steps over head_dim
@@ -533,7 +535,12 @@ __global__ __launch_bounds__(QUANT ? 320 : 256) void k_pass1(Pass1Args args) {
   }
   if (!STATE) return;
 
-  // ---- low-rank state: wave 2 tokens 0-31, wave 3 tokens 32-63
+  // ---- low-rank state.  Default: wave 2 takes tokens 0-31 and wave 3
+  // tokens 32-63 of every block and both write chunk partial sums.  BLK
+  // (complement scope): wave 2 takes the even and wave 3 the odd blocks of
+  // the chunk, each block as two 32-token half tiles in turn, so that one
+  // wave holds a whole block's state; it writes every block's state and no
+  // chunk partials (the reduction then sums the block states).
   const int tt = wave - 2;
   const uint16_t *Kb = args.k + base, *Vb = args.v + base;
   uint16_t *myring = vring + tt * NSTAGE * VT;
@@ -541,43 +548,56 @@ __global__ __launch_bounds__(QUANT ? 320 : 256) void k_pass1(Pass1Args args) {
 #pragma unroll
   for (int i = 0; i < DT; ++i) sacc[i] = f32x16{};
   float zacc = 0.0f;
-  // V half tile of block i -> slot i % NSTAGE (row-major, chunk-swizzled)
-  auto issue_v = [&](int i) __attribute__((always_inline)) {
-    const int64_t c = c0 + i;
-    uint16_t *slot = myring + (i % NSTAGE) * VT;
+  // half tile u of this wave: block index (in the chunk) and token half
+  const int nu = BLK ? 2 * max(0, (nblk - tt + 1) / 2) : nblk;
+  auto blk_of = [&](int u) __attribute__((always_inline)) { return BLK ? tt + 2 * (u >> 1) : u; };
+  auto half_of = [&](int u) __attribute__((always_inline)) { return BLK ? (u & 1) : tt; };
+  // V half tile u -> slot u % NSTAGE (row-major, chunk-swizzled)
+  auto issue_v = [&](int u) __attribute__((always_inline)) {
+    const int64_t c = c0 + blk_of(u);
+    uint16_t *slot = myring + (u % NSTAGE) * VT;
 #pragma unroll
     for (int o = 0; o < VOPS; ++o) {
       const int cidx = o * 64 + lane;
       const int row = cidx / CH, pc = cidx % CH;
-      const int64_t src = min(c * 64 + 32 * tt + row, args.n_tokens - 1) * args.stride_n;
+      const int64_t src = min(c * 64 + 32 * half_of(u) + row, args.n_tokens - 1) * args.stride_n;
       lds_dma16(Vb + src + ((pc ^ swz_v<D>(row)) * 8), slot + o * 512);
     }
   };
-  // K operand rows of block i: token 32*tt + lane%32, dims 16s + 8g .. +8
-  auto load_k = [&](int i, bf16x8 (&kr)[NS]) __attribute__((always_inline)) {
-    const int64_t row = min((int64_t)(c0 + i) * 64 + 32 * tt + (lane & 31), args.n_tokens - 1);
+  // K operand rows of half tile u: token 32*half + lane%32, dims 16s + 8g .. +8
+  auto load_k = [&](int u, bf16x8 (&kr)[NS]) __attribute__((always_inline)) {
+    const int64_t row =
+        min((int64_t)(c0 + blk_of(u)) * 64 + 32 * half_of(u) + (lane & 31), args.n_tokens - 1);
     const uint16_t *kp = Kb + row * args.stride_n + 8 * g;
 #pragma unroll
     for (int s = 0; s < NS; ++s) kr[s] = *(const bf16x8 *)(kp + 16 * s);
   };
   bf16x8 kcur[NS], knext[NS];
-  if (nblk > 0) issue_v(0);
-  if (nblk > 1) issue_v(1);
-  if (nblk > 0) load_k(0, kcur);
-  for (int i = 0; i < nblk; ++i) {
-    if (i + 2 < nblk) issue_v(i + 2);
-    if (i + 1 < nblk) load_k(i + 1, knext);
-    // block i: V(i) and K(i) were issued before V(i+2) and K(i+1); vmcnt
-    // completes in order, so allow exactly the ops issued after K(i)
-    if (i + 2 < nblk) wait_vmcnt<VOPS + NS>();
-    else if (i + 1 < nblk) wait_vmcnt<NS>();
+  if (nu > 0) issue_v(0);
+  if (nu > 1) issue_v(1);
+  if (nu > 0) load_k(0, kcur);
+  for (int u = 0; u < nu; ++u) {
+    if (u + 2 < nu) issue_v(u + 2);
+    if (u + 1 < nu) load_k(u + 1, knext);
+    // half tile u: V(u) and K(u) were issued before V(u+2) and K(u+1); vmcnt
+    // completes in order, so allow exactly the ops issued after K(u)
+    if (u + 2 < nu) wait_vmcnt<VOPS + NS>();
+    else if (u + 1 < nu) wait_vmcnt<NS>();
     else wait_vmcnt<0>();
-    const int c = c0 + i;
+    const int c = c0 + blk_of(u);
+    const int hf = half_of(u);
     const int valid = min(64, (int)(args.n_tokens - (int64_t)c * 64));
-    const uint16_t *sV = myring + (i % NSTAGE) * VT;
+    const uint16_t *sV = myring + (u % NSTAGE) * VT;
+    if constexpr (BLK) {
+      if (hf == 0) {  // a new block: its own sums
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) sacc[dt] = f32x16{};
+        zacc = 0.0f;
+      }
+    }
     f32x16 bacc = f32x16{};
     int pt, ph, pw;  // padded rows take the last valid position (their b is masked)
-    token_pos(min((int64_t)c * 64 + 32 * tt + (lane & 31), args.n_tokens - 1), ra, pt, ph, pw);
+    token_pos(min((int64_t)c * 64 + 32 * hf + (lane & 31), args.n_tokens - 1), ra, pt, ph, pw);
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const f32x4 fr = *(const f32x4 *)&sfreq[8 * s + 4 * g];  // pairs of dims 16s + 8g .. +8
@@ -590,13 +610,13 @@ __global__ __launch_bounds__(QUANT ? 320 : 256) void k_pass1(Pass1Args args) {
     bf16x8 bop[2];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int tok = 32 * tt + 8 * (e >> 2) + 4 * g + (e & 3);
+      const int tok = 32 * hf + 8 * (e >> 2) + 4 * g + (e & 3);
       float f = phi(bacc[e]);
       f = (rok && tok < valid) ? f : 0.0f;
       zacc += f;
       bop[e >> 3][e & 7] = (__bf16)f;
     }
-    // S^T[d][r] += sum_tok V^T[d][tok] * b[tok][r] over this wave's 32 tokens
+    // S^T[d][r] += sum_tok V^T[d][tok] * b[tok][r] over these 32 tokens
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
@@ -605,10 +625,26 @@ __global__ __launch_bounds__(QUANT ? 320 : 256) void k_pass1(Pass1Args args) {
         sacc[dt] = mfma_bf16(va, bop[s2], sacc[dt]);
       }
     }
+    if constexpr (BLK) {
+      if (hf == 1) {  // the whole block's state
+        float *bs = args.blk_state + ((int64_t)bh * args.nb + c) * (D * 32 + 32);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int d = 32 * dt + 8 * (e >> 2) + 4 * g + (e & 3);
+            bs[d * 32 + (lane & 31)] = sacc[dt][e];
+          }
+        }
+        const float zb = zacc + shfl_xor32(zacc);
+        if (lane < 32) bs[D * 32 + lane] = zb;
+      }
+    }
 #pragma unroll
     for (int s = 0; s < NS; ++s) kcur[s] = knext[s];
   }
 
+  if (BLK) return;
   float *part = args.state_part + (((int64_t)bh * gridDim.x + blockIdx.x) * 2 + tt) * (D * 32 + 32);
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
@@ -621,27 +657,26 @@ __global__ __launch_bounds__(QUANT ? 320 : 256) void k_pass1(Pass1Args args) {
   const float zt = zacc + shfl_xor32(zacc);
   if (lane < 32) part[D * 32 + lane] = zt;
 }
-
 // ------------------------------------------------------------ k_state_reduce
-// Fixed-order sum over the partials (chunk-major, then token half), one thread
-// per state element.
+// Fixed-order sum over the np partials of each head (chunk-major, then token
+// half; or the per-block states in block order), one thread per state element.
 // Writes St (bf16 [D][32], rank index permuted per 16-group, the A operand
-// layout of the apply step) and z (fp32 [32]).  Rank columns >= rank are 0.
-__global__ __launch_bounds__(256) void k_state_reduce(const float *__restrict__ part, int nchunks,
+// layout of the apply step), z (fp32 [32]) and, if s32 is set, S^T in fp32
+// ([D][32], natural rank order).  Rank columns >= rank are 0.
+__global__ __launch_bounds__(256) void k_state_reduce(const float *__restrict__ part, int np,
                                                       int D, int rank, uint16_t *__restrict__ st,
-                                                      float *__restrict__ z) {
+                                                      float *__restrict__ z, float *__restrict__ s32) {
   const int bh = blockIdx.y;
   const int stride = D * 32 + 32;
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= stride) return;
-  const float *p = part + (int64_t)bh * nchunks * 2 * stride + idx;
+  const float *p = part + (int64_t)bh * np * stride + idx;
   // fixed order: eight interleaved partial sums (partial i takes partials
   // i, i+8, ...), then combined pairwise; independent loads keep the
   // memory pipeline full
   float acc8[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc8[i] = 0.0f;
-  const int np = 2 * nchunks;
   int c = 0;
   for (; c + 8 <= np; c += 8) {
 #pragma unroll
@@ -655,9 +690,95 @@ __global__ __launch_bounds__(256) void k_state_reduce(const float *__restrict__ 
     const int pos = (r & ~15) | ((w < 4) ? w : (w < 8) ? w + 4 : (w < 12) ? w - 4 : w);
     const __bf16 v = (__bf16)(r < rank ? acc : 0.0f);
     st[(int64_t)bh * D * 32 + d * 32 + pos] = __builtin_bit_cast(uint16_t, v);
+    if (s32) s32[(int64_t)bh * D * 32 + idx] = r < rank ? acc : 0.0f;
   } else {
     const int r = idx - D * 32;
     z[(int64_t)bh * 32 + r] = r < rank ? acc : 0.0f;
+  }
+}
+
+// ------------------------------------------------------------ k_complement
+// Complement scope.  One workgroup per group of query blocks, in the same
+// group order and XCD mapping as the attention kernel: it walks the group's
+// union list once, adding each listed key block's fp32 state into the sums
+// of the members that kept it (a block shared by several members is read
+// once), then writes per member query block St_c = S - sum (bf16, the
+// rank-permuted A-operand layout of St) and z_c = z - sum.  A query block
+// that keeps every block gets zeros: nothing is left for its low-rank term.
+template <int D, int G>
+__global__ __launch_bounds__(256) void k_complement(CompArgs a) {
+  constexpr int E = D * 32 + 32;        // floats per block state (S^T then z)
+  constexpr int TC = E / 4;             // 16-byte chunks per block state
+  constexpr int NK = (TC + 255) / 256;  // chunks per thread
+  constexpr int UN = 4;                 // list entries loaded together
+  const int tid = threadIdx.x;
+  const int64_t L = blockIdx.x;
+  const int64_t sidx = L / 8;
+  const int64_t bh64 = sidx / a.groups_per_xcd;
+  const int64_t group = (L % 8) * a.groups_per_xcd + sidx % a.groups_per_xcd;
+  if (bh64 >= a.bh_count || group >= a.ngroups) return;
+  const int bh = (int)bh64;
+  const int64_t gidx = (int64_t)bh * a.ngroups + group;
+  const int32_t *list = a.ulist + gidx * a.list_stride;
+  const int U = a.ucount[gidx];
+  const f32x4 *blk = (const f32x4 *)(a.blk + (int64_t)bh * a.nb * E);
+  f32x4 acc[G][NK];
+#pragma unroll
+  for (int m = 0; m < G; ++m)
+#pragma unroll
+    for (int k = 0; k < NK; ++k) acc[m][k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int u0 = 0; u0 < U; u0 += UN) {
+    f32x4 x[UN][NK];
+    int msk[UN];
+#pragma unroll
+    for (int i = 0; i < UN; ++i) {
+      const bool in = u0 + i < U;
+      const int e = in ? list[u0 + i] : 0;
+      msk[i] = in ? (e >> 16) : 0;  // entries past the list add nothing
+      const f32x4 *src = blk + (int64_t)(e & 0xffff) * TC;
+#pragma unroll
+      for (int k = 0; k < NK; ++k) {
+        const int c = k * 256 + tid;
+        x[i][k] = c < TC ? src[c] : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < UN; ++i)
+#pragma unroll
+      for (int m = 0; m < G; ++m)
+        if ((msk[i] >> m) & 1)
+#pragma unroll
+          for (int k = 0; k < NK; ++k) acc[m][k] += x[i][k];
+  }
+  const float *sg = a.s32 + (int64_t)bh * D * 32;
+  const float *zg = a.z + (int64_t)bh * 32;
+  const bool empty = a.kb >= a.nb;
+#pragma unroll
+  for (int m = 0; m < G; ++m) {
+    const int qb = a.ugroup[gidx * G + m];
+    if (qb < 0) continue;
+    const int64_t qi = (int64_t)bh * a.nb + qb;
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+      const int c = k * 256 + tid;
+      if (c < D * 8) {
+        // S^T elements d, r..r+3 (r a multiple of 4): one 8-byte group of St
+        const int e = 4 * c, d = e >> 5, r = e & 31, w = r & 15;
+        const int pos = (r & ~15) | (w == 4 ? 8 : w == 8 ? 4 : w);
+        f32x4 v = *(const f32x4 *)(sg + e) - acc[m][k];
+        if (empty) v = f32x4{0.f, 0.f, 0.f, 0.f};
+        const __bf16 b0 = (__bf16)v[0], b1 = (__bf16)v[1], b2 = (__bf16)v[2], b3 = (__bf16)v[3];
+        uint2 o;
+        o.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+        o.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
+        *(uint2 *)(a.stc + qi * D * 32 + d * 32 + pos) = o;
+      } else if (c < TC) {
+        const int r = 4 * (c - D * 8);
+        f32x4 v = *(const f32x4 *)(zg + r) - acc[m][k];
+        if (empty) v = f32x4{0.f, 0.f, 0.f, 0.f};
+        *(f32x4 *)(a.zc + qi * 32 + r) = v;
+      }
+    }
   }
 }
 
@@ -1078,7 +1199,9 @@ static __device__ __forceinline__ void attn_finish(const AttnArgs &args, const b
       const bf16x8 wa = *(const bf16x8 *)(args.wqT + (lane & 31) * D + 16 * s + 8 * g);
       aacc = mfma_bf16(wa, qr, aacc);
     }
-    const f32x4 *zb = (const f32x4 *)(args.z + (int64_t)bh * 32);
+    // one state per (batch, head), or per query block in the complement scope
+    const int64_t si = args.complement ? (int64_t)bh * args.nb + n / 64 : (int64_t)bh;
+    const f32x4 *zb = (const f32x4 *)(args.z + si * 32);
     float den = 0.0f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -1092,7 +1215,7 @@ static __device__ __forceinline__ void attn_finish(const AttnArgs &args, const b
       }
     }
     den += shfl_xor32(den);
-    float inv_den = 1.0f / den;
+    float inv_den = den > 0.0f ? 1.0f / den : 0.0f;  // 0: an empty complement
     if (args.gate) {
       // learned output gate sigmoid(q . w + b) of this query on the low-rank
       // term; each half-wave holds half of the query's dims
@@ -1113,7 +1236,7 @@ static __device__ __forceinline__ void attn_finish(const AttnArgs &args, const b
     bf16x8 aop[2];
 #pragma unroll
     for (int i = 0; i < 16; ++i) aop[i >> 3][i & 7] = (__bf16)(aacc[i] * inv_den);
-    const uint16_t *stb = args.st + (int64_t)bh * D * 32;
+    const uint16_t *stb = args.st + si * D * 32;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const int d = 32 * dt + (lane & 31);
@@ -1847,10 +1970,18 @@ template <int D>
 static void pass1_d(const Pass1Args &a, int nchunks, int bh, bool pool, bool state, bool quant,
                     hipStream_t st) {
   dim3 grid(nchunks, bh), block(256);
-  if (pool && state && quant) hipLaunchKernelGGL((k_pass1<D, true, true, true>), grid, dim3(320), 0, st, a);
-  else if (pool && state) hipLaunchKernelGGL((k_pass1<D, true, true, false>), grid, block, 0, st, a);
-  else if (pool) hipLaunchKernelGGL((k_pass1<D, true, false, false>), grid, block, 0, st, a);
-  else hipLaunchKernelGGL((k_pass1<D, false, true, false>), grid, block, 0, st, a);
+  const bool blk = a.blk_state != nullptr;
+  if (pool && state && quant) {
+    if (blk) hipLaunchKernelGGL((k_pass1<D, true, true, true, true>), grid, dim3(320), 0, st, a);
+    else hipLaunchKernelGGL((k_pass1<D, true, true, true, false>), grid, dim3(320), 0, st, a);
+  } else if (pool && state) {
+    if (blk) hipLaunchKernelGGL((k_pass1<D, true, true, false, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_pass1<D, true, true, false, false>), grid, block, 0, st, a);
+  } else if (pool) {
+    hipLaunchKernelGGL((k_pass1<D, true, false, false, false>), grid, block, 0, st, a);
+  } else {
+    hipLaunchKernelGGL((k_pass1<D, false, true, false, false>), grid, block, 0, st, a);
+  }
 }
 
 void launch_pass1(const Pass1Args &a, int D, int nchunks, int bh, bool pool, bool state, bool quant,
@@ -1859,10 +1990,16 @@ void launch_pass1(const Pass1Args &a, int D, int nchunks, int bh, bool pool, boo
   else pass1_d<128>(a, nchunks, bh, pool, state, quant, st);
 }
 
-void launch_state_reduce(const float *part, int nchunks, int D, int rank, int bh, uint16_t *st_out,
-                         float *z, hipStream_t st) {
-  hipLaunchKernelGGL(k_state_reduce, dim3((D * 32 + 32 + 255) / 256, bh), dim3(256), 0, st, part, nchunks, D,
-                     rank, st_out, z);
+void launch_state_reduce(const float *part, int np, int D, int rank, int bh, uint16_t *st_out,
+                         float *z, float *s32, hipStream_t st) {
+  hipLaunchKernelGGL(k_state_reduce, dim3((D * 32 + 32 + 255) / 256, bh), dim3(256), 0, st, part, np, D,
+                     rank, st_out, z, s32);
+}
+
+void launch_complement(const CompArgs &a, int D, hipStream_t st) {
+  const dim3 grid((unsigned)(8 * a.groups_per_xcd * a.bh_count)), block(256);
+  if (D == 64) hipLaunchKernelGGL((k_complement<64, ROLA_ATTN_G>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((k_complement<128, ROLA_ATTN_G>), grid, block, 0, st, a);
 }
 
 void launch_scores(const float *qp, const float *kp, float *s, int nb, int D, int bh,

@@ -20,6 +20,7 @@ from . import build as _build
 ROLA_OK = 0
 ROLA_PREC_BF16, ROLA_PREC_FP8 = 0, 1
 ROLA_OUT_BF16, ROLA_OUT_F32 = 0, 1
+ROLA_LR_GLOBAL, ROLA_LR_COMPLEMENT = 0, 1
 BLOCK = 64
 
 
@@ -33,7 +34,7 @@ class RolaConfig(ctypes.Structure):
     _fields_ = [("topk", ctypes.c_float), ("kb_override", ctypes.c_int32), ("rank", ctypes.c_int32),
                 ("rope_split", ctypes.c_int32 * 3), ("rope_theta", ctypes.c_float),
                 ("softmax_scale", ctypes.c_float), ("precision", ctypes.c_int32),
-                ("out_dtype", ctypes.c_int32)]
+                ("out_dtype", ctypes.c_int32), ("lowrank_scope", ctypes.c_int32)]
 
 
 class RolaPlanInfo(ctypes.Structure):
@@ -45,7 +46,7 @@ class RolaKernelTime(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_int32), ("total_ms", ctypes.c_double)]
 
 
-ABI_VERSION = 2  # ROLA_ABI_VERSION of include/rola.h
+ABI_VERSION = 3  # ROLA_ABI_VERSION of include/rola.h
 
 EXPORTS = ["rola_abi_version", "rola_status_str", "rola_plan", "rola_select_blocks",
            "rola_sparse_attn", "rola_lowrank_attn", "rola_forward", "rola_timing_enable",
@@ -113,10 +114,12 @@ class Config:
     softmax_scale: float = 0.0
     precision: int = ROLA_PREC_BF16
     out_dtype: int = ROLA_OUT_BF16
+    lowrank_scope: int = ROLA_LR_GLOBAL
 
     def c(self) -> RolaConfig:
         return RolaConfig(self.topk, self.kb_override, self.rank, (ctypes.c_int32 * 3)(*self.rope_split),
-                          self.rope_theta, self.softmax_scale, self.precision, self.out_dtype)
+                          self.rope_theta, self.softmax_scale, self.precision, self.out_dtype,
+                          self.lowrank_scope)
 
 
 def problem(q: torch.Tensor, grid) -> RolaProblem:

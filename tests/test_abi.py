@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     for name in _declared_functions():
         assert hasattr(L, name), name
     assert set(rola.EXPORTS) == set(_declared_functions())
-    assert L.rola_abi_version() == rola.ABI_VERSION == 2
+    assert L.rola_abi_version() == rola.ABI_VERSION == 3
 
 
 def _prob(B=1, H=40, D=128, grid=(21, 45, 80), sn=None):
@@ -58,6 +58,18 @@ def test_plan_block_counts(grid, topk, nb, kb):
     assert info2.workspace_bytes == info.workspace_bytes > 0
 
 
+def test_complement_scope_plans_its_block_states():
+    """The complement scope adds per-block states (fp32) and per-query-block complements
+    (bf16 S, fp32 z) to the workspace."""
+    prob = _prob()
+    st, g = _plan(prob, rola.Config(topk=0.03))
+    st2, c = _plan(prob, rola.Config(topk=0.03, lowrank_scope=rola.ROLA_LR_COMPLEMENT))
+    assert st == st2 == 0 and (c.nb, c.kb) == (g.nb, g.kb)
+    bh, nb, D = 40, 1182, 128
+    extra = bh * nb * (D * 32 + 32) * 4 + bh * D * 32 * 4 + bh * nb * D * 32 * 2 + bh * nb * 32 * 4
+    assert extra <= c.workspace_bytes - g.workspace_bytes <= extra + 4 * 256
+
+
 def test_plan_rejects_bad_arguments():
     ok = rola.Config(topk=0.1)
     cases = [
@@ -75,6 +87,7 @@ def test_plan_rejects_bad_arguments():
         (_prob(grid=(0, 45, 80)), ok, 1),
         (_prob(), rola.Config(topk=0.1, precision=7), 1),
         (_prob(), rola.Config(topk=0.1, out_dtype=3), 1),
+        (_prob(), rola.Config(topk=0.1, lowrank_scope=2), 1),
     ]
     for prob, cfg, want in cases:
         st, _ = _plan(prob, cfg)
