@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--topk", type=float, default=None, help="override the workload's keep ratio")
     ap.add_argument("--gate", action="store_true",
                     help="apply the learned output gate to the low-rank term (seeded synthetic gate)")
+    ap.add_argument("--complement", action="store_true",
+                    help="low-rank state over each query block's unkept blocks instead of all blocks")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true", help="skip the MFMA-probe and copy measurements")
     ap.add_argument("--cpu-baseline-child", action="store_true", help=argparse.SUPPRESS)
@@ -85,12 +87,19 @@ def cpu_baseline_child(args):
     bmap = oracle.block_map(q, k, w.n_tokens, w.kb)
     t1 = time.perf_counter()
     qf, kf, vf = (oracle.widen_bf16(x) for x in (q, k, v))
-    S, z = oracle.lowrank_state(kf, vf, wk, w.n_tokens, w.grid)
+    gate_w = W.make_gate(w) if args.gate else None
+    if args.complement:
+        Sb, zb = oracle.lowrank_block_states(kf[0], vf[0], wk, w.n_tokens, w.grid)
+    else:
+        S, z = oracle.lowrank_state(kf, vf, wk, w.n_tokens, w.grid)
     t2 = time.perf_counter()
     qbs = list(range(0, w.nb, args.sample_stride))
     rows = np.array([n for qb in qbs for n in range(qb * 64, min(qb * 64 + 64, w.n_tokens))])
     sp = oracle.sparse_rows(qf, kf, vf, bmap, w.n_tokens, rows)
-    lr = oracle.lowrank_rows(qf, wq, S, z, w.grid, rows, gate_w=W.make_gate(w) if args.gate else None)
+    if args.complement:
+        lr = oracle.lowrank_rows_complement(qf[0], wq, Sb, zb, bmap[0], w.grid, rows, gate_w=gate_w)
+    else:
+        lr = oracle.lowrank_rows(qf, wq, S, z, w.grid, rows, gate_w=gate_w)
     t3 = time.perf_counter()
     assert np.isfinite(sp + lr).all()
     rows_full = w.n_tokens
@@ -102,9 +111,11 @@ def cpu_baseline_child(args):
 
 def cpu_baseline(args, w):
     env = dict(os.environ, OMP_NUM_THREADS="1")
+    # the complement rows sum every unkept block state per row: sample fewer query blocks
+    stride = max(args.sample_stride, 32) if args.complement else args.sample_stride
     cmd = [sys.executable, os.path.abspath(__file__), "--cpu-baseline-child", "--workload", args.workload,
-           "--sample-stride", str(args.sample_stride)] + (["--topk", repr(args.topk)] if args.topk else []) \
-        + (["--gate"] if args.gate else [])
+           "--sample-stride", str(stride)] + (["--topk", repr(args.topk)] if args.topk else []) \
+        + (["--gate"] if args.gate else []) + (["--complement"] if args.complement else [])
     res = subprocess.run(cmd, env=env, capture_output=True, text=True, timeout=600)
     if res.returncode != 0:
         raise RuntimeError("cpu baseline failed: " + res.stderr[-2000:])
@@ -119,7 +130,7 @@ def cpu_baseline(args, w):
         "sample": ("oracle (C, fp64 branches, 1 thread) on head 0 of %s: full block selection (%.2f s) and "
                    "low-rank state (%.2f s), both branches on every %d-th query block (%d rows, %.2f s); "
                    "extrapolated linearly to all %d heads and rows"
-                   % (args.workload, r["select_s"], r["state_s"], args.sample_stride, r["rows"], r["rows_s"],
+                   % (args.workload, r["select_s"], r["state_s"], stride, r["rows"], r["rows_s"],
                       w.batch * w.heads)),
     }
 
@@ -191,7 +202,8 @@ def main():
     del q, k, v
     wqd, wkd = torch.from_numpy(wq).cuda(), torch.from_numpy(wk).cuda()
     gd = torch.from_numpy(W.make_gate(w)).cuda() if args.gate else None
-    cfg = rola.Config(topk=w.topk, rank=w.rank, precision=rola.ROLA_PREC_FP8 if fp8 else rola.ROLA_PREC_BF16)
+    cfg = rola.Config(topk=w.topk, rank=w.rank, precision=rola.ROLA_PREC_FP8 if fp8 else rola.ROLA_PREC_BF16,
+                      lowrank_scope=rola.ROLA_LR_COMPLEMENT if args.complement else rola.ROLA_LR_GLOBAL)
     dominant = "attn8_sparse_lowrank" if fp8 else "attn_sparse_lowrank"
     peak = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
     out = torch.empty_like(qd)
@@ -232,7 +244,7 @@ def main():
     achieved = kept / t_attn / 1e12
     traffic = None
     tfile = traffic_file(w.name)
-    if os.path.exists(tfile) and args.topk is None and not args.gate:
+    if os.path.exists(tfile) and args.topk is None and not args.gate and not args.complement:
         with open(tfile) as f:
             tr = json.load(f)
         if tr.get("kernel_source_hash") == kernel_source_hash() and tr.get("workload") == w.name:
@@ -240,8 +252,10 @@ def main():
     # algorithmic HBM bytes of the streaming pass: read Q, K, V once; in fp8 mode
     # also write the e4m3 codes of K and V (one byte per element)
     n_tok = w.batch * w.heads * w.n_pad
-    pass1_name = "pass1_pool_state_quant8" if fp8 else "pass1_pool_state"
-    pass1_bytes = 3 * n_tok * w.head_dim * 2 + (2 * n_tok * w.head_dim if fp8 else 0)
+    # (complement scope: plus the per-block states it writes, bf16 S and fp32 z)
+    pass1_name = "pass1_pool_%s%s" % ("blkstate" if args.complement else "state", "_quant8" if fp8 else "")
+    pass1_bytes = 3 * n_tok * w.head_dim * 2 + (2 * n_tok * w.head_dim if fp8 else 0) \
+        + (w.batch * w.heads * w.nb * (w.head_dim * 64 + 128) if args.complement else 0)
     pass1_ms = kern_ms.get(pass1_name)
     rec = {
         "metric": METRIC,
@@ -258,7 +272,8 @@ def main():
         "data": "synthetic (seeded Wan-shaped smooth field + noise Q/K, N(0,1) V; no weights)",
         "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim,
                    "grid": list(w.grid), "n_tokens": w.n_tokens, "topk": w.topk, "kb": w.kb, "nb": w.nb,
-                   "rank": w.rank, "output_gate": bool(args.gate)},
+                   "rank": w.rank, "output_gate": bool(args.gate),
+                   "lowrank_scope": "complement" if args.complement else "global"},
         "fwd_ms": round(ms, 4),
         "dense_equiv_tflops": round(dense / (ms * 1e-3) / 1e12, 1),
         "kept_block_tflops": round(kept / (ms * 1e-3) / 1e12, 1),

@@ -19,6 +19,7 @@
 namespace {
 
 constexpr int64_t kAlign = 256;
+constexpr int kBlkParts = 32;  // complement scope: block-range partials of the global state
 
 int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -105,7 +106,10 @@ int32_t make_plan(const rola_problem *p, const rola_config *c, Plan *pl) {
   P.off_kp = o; o = align_up(o + P.BH * nb * D * 4);
   P.off_scores = o; o = align_up(o + P.BH * nb * (int64_t)nb * 4);
   P.off_map = o; o = align_up(o + P.BH * nb * (int64_t)kb * 4);
-  P.off_part = o; o = align_up(o + P.BH * P.nchunks * 2 * (int64_t)(D * 32 + 32) * 4);
+  // state partials: 2 per chunk, or (complement scope) up to kBlkParts block-range sums
+  P.comp = c->lowrank_scope == ROLA_LR_COMPLEMENT;
+  const int64_t nparts = std::max<int64_t>(2LL * P.nchunks, P.comp ? std::min(nb, kBlkParts) : 0);
+  P.off_part = o; o = align_up(o + P.BH * nparts * (int64_t)(D * 32 + 32) * 4);
   P.off_st = o; o = align_up(o + P.BH * D * 32LL * 2);
   P.off_z = o; o = align_up(o + P.BH * 32LL * 4);
   P.G = rola::attn_group_size();
@@ -122,10 +126,9 @@ int32_t make_plan(const rola_problem *p, const rola_config *c, Plan *pl) {
     P.off_vsc = o; o = align_up(o + P.BH * nb * 4);
     P.off_kv8 = o; o = align_up(o + P.BH * nb * 128LL * D);
   }
-  P.comp = c->lowrank_scope == ROLA_LR_COMPLEMENT;
   P.off_blk = P.off_s32 = P.off_stc = P.off_zc = 0;
   if (P.comp) {
-    P.off_blk = o; o = align_up(o + P.BH * nb * (int64_t)(D * 32 + 32) * 4);
+    P.off_blk = o; o = align_up(o + P.BH * nb * (int64_t)(D * 64 + 128));  // bf16 S^T, fp32 z
     P.off_s32 = o; o = align_up(o + P.BH * D * 32LL * 4);
     P.off_stc = o; o = align_up(o + P.BH * nb * (int64_t)D * 32 * 2);
     P.off_zc = o; o = align_up(o + P.BH * nb * 32LL * 4);
@@ -211,7 +214,7 @@ int32_t run_pass1(const Plan &P, const rola_problem *p, const void *q, const voi
   a.kp = (float *)(ws + P.off_kp);
   a.wkT = (const uint16_t *)(ws + P.off_wkT);
   a.state_part = (float *)(ws + P.off_part);
-  a.blk_state = (P.comp && pool && state) ? (float *)(ws + P.off_blk) : nullptr;
+  a.blk_state = (P.comp && pool && state) ? ws + P.off_blk : nullptr;
   a.rope = rope_args(P, ws);
   a.qsc = (float *)(ws + P.off_qsc);
   a.ksc = (float *)(ws + P.off_ksc);
@@ -226,10 +229,19 @@ int32_t run_pass1(const Plan &P, const rola_problem *p, const void *q, const voi
 }
 
 int32_t run_reduce(const Plan &P, uint8_t *ws, hipStream_t st) {
+  int np = 2 * P.nchunks;
+  if (P.comp) {
+    // pass 1 wrote per-block states instead of chunk partials: sum them over
+    // block ranges first (into the chunk-partial space, which holds at least
+    // min(nb, kBlkParts) partials per head)
+    np = std::min<int>(P.nb, kBlkParts);
+    int32_t s = timed("blk_partial", st, [&] {
+      rola::launch_blk_partial(ws + P.off_blk, P.nb, np, P.D, (int)P.BH, (float *)(ws + P.off_part), st);
+    });
+    if (s != ROLA_OK) return s;
+  }
   return timed("state_reduce", st, [&] {
-    // complement scope: pass 1 wrote per-block states instead of chunk partials
-    rola::launch_state_reduce(P.comp ? (const float *)(ws + P.off_blk) : (const float *)(ws + P.off_part),
-                              P.comp ? P.nb : 2 * P.nchunks, P.D, P.r, (int)P.BH,
+    rola::launch_state_reduce((const float *)(ws + P.off_part), np, P.D, P.r, (int)P.BH,
                               (uint16_t *)(ws + P.off_st), (float *)(ws + P.off_z),
                               P.comp ? (float *)(ws + P.off_s32) : nullptr, st);
   });
@@ -302,7 +314,7 @@ int32_t run_attn(const Plan &P, const rola_problem *p, const rola_config *c, con
   if (a.complement) {
     // per query block: the global state minus the states of its kept blocks
     rola::CompArgs ca;
-    ca.blk = (const float *)(ws + P.off_blk);
+    ca.blk = ws + P.off_blk;
     ca.s32 = (const float *)(ws + P.off_s32);
     ca.z = (const float *)(ws + P.off_z);
     ca.ugroup = a.ugroup; ca.ucount = a.ucount; ca.ulist = a.ulist;

@@ -30,7 +30,8 @@ struct Pass1Args {
   float *qp, *kp;       // pooled [BH][nb][D]
   const uint16_t *wkT;  // bf16 [32][D]
   float *state_part;    // [BH][nchunks][2][D*32 + 32]
-  float *blk_state;     // complement scope: [BH][nb][D*32 + 32] per-block states, else NULL
+  uint8_t *blk_state;   // complement scope: [BH][nb] per-block states (bf16 S^T [D][32], fp32 z
+                        // [32]; D*64 + 128 bytes each), else NULL
   RopeArgsHost rope;
   // fp8 mode (see Quant8Args): Q scales, K and V^T codes of each block
   float *qsc, *ksc, *vsc;
@@ -100,14 +101,17 @@ struct AttnArgs {
 void launch_setup(const SetupArgs &a, hipStream_t st);
 void launch_pass1(const Pass1Args &a, int D, int nchunks, int bh, bool pool, bool state, bool quant,
                   hipStream_t st);  // per-block states as well when a.blk_state is set
-// part: np partial states per head ([BH][np][D*32 + 32])
+// part: np fp32 partial states per head, [BH][np][D*32 + 32]
 void launch_state_reduce(const float *part, int np, int D, int rank, int bh, uint16_t *st_out,
                          float *z, float *s32, hipStream_t st);
+// complement scope: `parts` block-range sums of pass 1's per-block states into
+// part ([BH][parts][D*32 + 32]) for launch_state_reduce
+void launch_blk_partial(const uint8_t *blk, int nb, int parts, int D, int bh, float *part, hipStream_t st);
 
 // Complement scope: per query block, the global state minus the states of its
 // kept key blocks, gathered along the attention schedule's union lists.
 struct CompArgs {
-  const float *blk;        // [BH][nb][D*32 + 32] per-block S (d-major, rank inner) then z
+  const uint8_t *blk;      // [BH][nb] per-block states as written by pass 1 (bf16 S^T, fp32 z)
   const float *s32, *z;    // global S [BH][D*32] and z [BH][32]
   const int32_t *ugroup, *ucount, *ulist;
   int nb, kb;

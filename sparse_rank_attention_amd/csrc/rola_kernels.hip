@@ -11,6 +11,7 @@
 //   k_pass1        one streaming pass over the token tensors: block pooling
 //                  of Q and K (fixed fp32 tree order) and low-rank state
 //                  partials from K and V (MFMA)
+//   k_blk_partial  (complement scope) block-range sums of the per-block states
 //   k_state_reduce fixed-order sum of the state partials
 //   k_complement   (complement scope) per query block: global state minus
 //                  the states of its kept key blocks
@@ -372,6 +373,10 @@ static __device__ __forceinline__ int img_v_off(int d, int p) {
 //          LDS transpose (see k_quant8 for the image layout and rounding).
 // Rows past N are read as zero (pooling) or taken from row N-1 (finite
 // values; their b is masked to 0).
+// bytes of one per-block low-rank state (complement scope): bf16 S^T [D][32]
+// (rank in natural order), then fp32 z [32]
+static __host__ __device__ constexpr int blk_state_bytes(int D) { return D * 64 + 128; }
+
 template <int D, bool POOL, bool STATE, bool QUANT, bool BLK>
 __global__ __launch_bounds__(QUANT ? 320 : 256) void k_pass1(Pass1Args args) {
   constexpr int CH = D / 8;       // 16-byte chunks per token row
@@ -626,18 +631,19 @@ __global__ __launch_bounds__(QUANT ? 320 : 256) void k_pass1(Pass1Args args) {
       }
     }
     if constexpr (BLK) {
-      if (hf == 1) {  // the whole block's state
-        float *bs = args.blk_state + ((int64_t)bh * args.nb + c) * (D * 32 + 32);
+      if (hf == 1) {  // the whole block's state: bf16 S^T [D][32], then fp32 z [32]
+        uint8_t *bb = args.blk_state + ((int64_t)bh * args.nb + c) * blk_state_bytes(D);
+        uint16_t *bs = (uint16_t *)bb;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             const int d = 32 * dt + 8 * (e >> 2) + 4 * g + (e & 3);
-            bs[d * 32 + (lane & 31)] = sacc[dt][e];
+            bs[d * 32 + (lane & 31)] = __builtin_bit_cast(uint16_t, (__bf16)sacc[dt][e]);
           }
         }
         const float zb = zacc + shfl_xor32(zacc);
-        if (lane < 32) bs[D * 32 + lane] = zb;
+        if (lane < 32) ((float *)(bb + D * 64))[lane] = zb;
       }
     }
 #pragma unroll
@@ -658,8 +664,9 @@ __global__ __launch_bounds__(QUANT ? 320 : 256) void k_pass1(Pass1Args args) {
   if (lane < 32) part[D * 32 + lane] = zt;
 }
 // ------------------------------------------------------------ k_state_reduce
-// Fixed-order sum over the np partials of each head (chunk-major, then token
-// half; or the per-block states in block order), one thread per state element.
+// Fixed-order sum over the np fp32 partials of each head (chunk-major, then
+// token half; or the block-range partials of k_blk_partial), one thread per
+// state element.
 // Writes St (bf16 [D][32], rank index permuted per 16-group, the A operand
 // layout of the apply step), z (fp32 [32]) and, if s32 is set, S^T in fp32
 // ([D][32], natural rank order).  Rank columns >= rank are 0.
@@ -697,18 +704,66 @@ __global__ __launch_bounds__(256) void k_state_reduce(const float *__restrict__ 
   }
 }
 
+// ------------------------------------------------------------ k_blk_partial
+// Complement scope, first level of the global state: workgroup (p, bh) sums
+// the per-block states (bf16 S^T, fp32 z) of blocks [p*per, (p+1)*per) in
+// block order, in fp32, 16 bytes per thread and load, and writes an fp32
+// partial in the layout k_state_reduce sums ([D*32] S^T, then [32] z).  The
+// global state is thereby the sum of exactly the values the complement
+// subtracts.
+template <int D>
+__global__ __launch_bounds__(256) void k_blk_partial(const uint8_t *__restrict__ blk, int nb, int per,
+                                                     float *__restrict__ part) {
+  constexpr int BB = D * 64 + 128, SC = D * 4, TC = SC + 8, NK = (TC + 255) / 256;
+  const int tid = threadIdx.x, p = blockIdx.x, bh = blockIdx.y;
+  const int j0 = p * per, j1 = min(nb, j0 + per);
+  const uint8_t *base = blk + (int64_t)bh * nb * BB;
+  f32x4 acc[NK][2];
+#pragma unroll
+  for (int k = 0; k < NK; ++k) acc[k][0] = acc[k][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = j0; j < j1; ++j) {
+    const u32x4 *src = (const u32x4 *)(base + (int64_t)j * BB);
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+      const int c = k * 256 + tid;
+      if (c < SC) {
+        const u32x4 w = src[c];
+        acc[k][0] += f32x4{bflo(w[0]), bfhi(w[0]), bflo(w[1]), bfhi(w[1])};
+        acc[k][1] += f32x4{bflo(w[2]), bfhi(w[2]), bflo(w[3]), bfhi(w[3])};
+      } else if (c < TC) {
+        acc[k][0] += __builtin_bit_cast(f32x4, src[c]);
+      }
+    }
+  }
+  float *out = part + ((int64_t)bh * gridDim.x + p) * (D * 32 + 32);
+#pragma unroll
+  for (int k = 0; k < NK; ++k) {
+    const int c = k * 256 + tid;
+    if (c < SC) {
+      *(f32x4 *)(out + 8 * c) = acc[k][0];
+      *(f32x4 *)(out + 8 * c + 4) = acc[k][1];
+    } else if (c < TC) {
+      *(f32x4 *)(out + D * 32 + 4 * (c - SC)) = acc[k][0];
+    }
+  }
+}
+
 // ------------------------------------------------------------ k_complement
 // Complement scope.  One workgroup per group of query blocks, in the same
 // group order and XCD mapping as the attention kernel: it walks the group's
-// union list once, adding each listed key block's fp32 state into the sums
-// of the members that kept it (a block shared by several members is read
-// once), then writes per member query block St_c = S - sum (bf16, the
-// rank-permuted A-operand layout of St) and z_c = z - sum.  A query block
-// that keeps every block gets zeros: nothing is left for its low-rank term.
+// union list once, adding each listed key block's state (bf16 S^T, fp32 z)
+// in fp32 into the sums of the members that kept it (a block shared by
+// several members is read once), then writes per member query block
+// St_c = S - sum (bf16, the rank-permuted A-operand layout of St) and
+// z_c = z - sum.  S and z are the sums of the same block states, so the
+// difference is the sum over the unkept blocks up to fp32 rounding.  A query
+// block that keeps every block gets zeros: nothing is left for its low-rank
+// term.
 template <int D, int G>
 __global__ __launch_bounds__(256) void k_complement(CompArgs a) {
-  constexpr int E = D * 32 + 32;        // floats per block state (S^T then z)
-  constexpr int TC = E / 4;             // 16-byte chunks per block state
+  constexpr int BB = D * 64 + 128;      // bytes per block state
+  constexpr int SC = D * 4;             // 16-byte chunks of S^T (8 bf16 each)
+  constexpr int TC = SC + 8;            // plus the z chunks (4 floats each)
   constexpr int NK = (TC + 255) / 256;  // chunks per thread
   constexpr int UN = 4;                 // list entries loaded together
   const int tid = threadIdx.x;
@@ -721,34 +776,52 @@ __global__ __launch_bounds__(256) void k_complement(CompArgs a) {
   const int64_t gidx = (int64_t)bh * a.ngroups + group;
   const int32_t *list = a.ulist + gidx * a.list_stride;
   const int U = a.ucount[gidx];
-  const f32x4 *blk = (const f32x4 *)(a.blk + (int64_t)bh * a.nb * E);
-  f32x4 acc[G][NK];
+  const uint8_t *blk = a.blk + (int64_t)bh * a.nb * BB;
+  // per member and chunk: ranks r0..r0+3 and r0+4..r0+7 of an S^T row, or
+  // (the z chunk) four z values and zeros
+  f32x4 acc[G][NK][2];
 #pragma unroll
   for (int m = 0; m < G; ++m)
 #pragma unroll
-    for (int k = 0; k < NK; ++k) acc[m][k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < NK; ++k) acc[m][k][0] = acc[m][k][1] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int u0 = 0; u0 < U; u0 += UN) {
-    f32x4 x[UN][NK];
+    u32x4 x[UN][NK];
     int msk[UN];
 #pragma unroll
     for (int i = 0; i < UN; ++i) {
       const bool in = u0 + i < U;
       const int e = in ? list[u0 + i] : 0;
       msk[i] = in ? (e >> 16) : 0;  // entries past the list add nothing
-      const f32x4 *src = blk + (int64_t)(e & 0xffff) * TC;
+      const u32x4 *src = (const u32x4 *)(blk + (int64_t)(e & 0xffff) * BB);
 #pragma unroll
       for (int k = 0; k < NK; ++k) {
         const int c = k * 256 + tid;
-        x[i][k] = c < TC ? src[c] : f32x4{0.f, 0.f, 0.f, 0.f};
+        x[i][k] = c < TC ? src[c] : u32x4{0u, 0u, 0u, 0u};
       }
     }
 #pragma unroll
-    for (int i = 0; i < UN; ++i)
+    for (int i = 0; i < UN; ++i) {
+      f32x4 f[NK][2];
+#pragma unroll
+      for (int k = 0; k < NK; ++k) {
+        const u32x4 w = x[i][k];
+        if (k * 256 + tid < SC) {
+          f[k][0] = f32x4{bflo(w[0]), bfhi(w[0]), bflo(w[1]), bfhi(w[1])};
+          f[k][1] = f32x4{bflo(w[2]), bfhi(w[2]), bflo(w[3]), bfhi(w[3])};
+        } else {
+          f[k][0] = __builtin_bit_cast(f32x4, w);
+          f[k][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
 #pragma unroll
       for (int m = 0; m < G; ++m)
         if ((msk[i] >> m) & 1)
 #pragma unroll
-          for (int k = 0; k < NK; ++k) acc[m][k] += x[i][k];
+          for (int k = 0; k < NK; ++k) {
+            acc[m][k][0] += f[k][0];
+            acc[m][k][1] += f[k][1];
+          }
+    }
   }
   const float *sg = a.s32 + (int64_t)bh * D * 32;
   const float *zg = a.z + (int64_t)bh * 32;
@@ -761,22 +834,31 @@ __global__ __launch_bounds__(256) void k_complement(CompArgs a) {
 #pragma unroll
     for (int k = 0; k < NK; ++k) {
       const int c = k * 256 + tid;
-      if (c < D * 8) {
-        // S^T elements d, r..r+3 (r a multiple of 4): one 8-byte group of St
-        const int e = 4 * c, d = e >> 5, r = e & 31, w = r & 15;
-        const int pos = (r & ~15) | (w == 4 ? 8 : w == 8 ? 4 : w);
-        f32x4 v = *(const f32x4 *)(sg + e) - acc[m][k];
-        if (empty) v = f32x4{0.f, 0.f, 0.f, 0.f};
-        const __bf16 b0 = (__bf16)v[0], b1 = (__bf16)v[1], b2 = (__bf16)v[2], b3 = (__bf16)v[3];
-        uint2 o;
-        o.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
-        o.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
-        *(uint2 *)(a.stc + qi * D * 32 + d * 32 + pos) = o;
+      if (c < SC) {
+        // S^T row d, ranks r0 .. r0+7 -> two 8-byte groups of the permuted St
+        const int d = c >> 2, r0 = 8 * (c & 3);
+        const f32x4 g0 = *(const f32x4 *)(sg + d * 32 + r0);
+        const f32x4 g1 = *(const f32x4 *)(sg + d * 32 + r0 + 4);
+        const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
+        const f32x4 d0 = empty ? zero : g0 - acc[m][k][0], d1 = empty ? zero : g1 - acc[m][k][1];
+        const float v[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+        uint2 o[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const __bf16 b0 = (__bf16)v[4 * h], b1 = (__bf16)v[4 * h + 1], b2 = (__bf16)v[4 * h + 2],
+                       b3 = (__bf16)v[4 * h + 3];
+          o[h].x = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+          o[h].y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
+        }
+        // ranks 4-7 and 8-11 of each 16-group trade places
+        const int pa = (r0 & 8) ? r0 - 4 : r0, pb = (r0 & 8) ? r0 + 4 : r0 + 8;
+        uint16_t *so = a.stc + qi * D * 32 + d * 32;
+        *(uint2 *)(so + pa) = o[0];
+        *(uint2 *)(so + pb) = o[1];
       } else if (c < TC) {
-        const int r = 4 * (c - D * 8);
-        f32x4 v = *(const f32x4 *)(zg + r) - acc[m][k];
-        if (empty) v = f32x4{0.f, 0.f, 0.f, 0.f};
-        *(f32x4 *)(a.zc + qi * 32 + r) = v;
+        const int r = 4 * (c - SC);
+        const f32x4 zz = *(const f32x4 *)(zg + r);
+        *(f32x4 *)(a.zc + qi * 32 + r) = empty ? f32x4{0.f, 0.f, 0.f, 0.f} : zz - acc[m][k][0];
       }
     }
   }
@@ -1994,6 +2076,13 @@ void launch_state_reduce(const float *part, int np, int D, int rank, int bh, uin
                          float *z, float *s32, hipStream_t st) {
   hipLaunchKernelGGL(k_state_reduce, dim3((D * 32 + 32 + 255) / 256, bh), dim3(256), 0, st, part, np, D,
                      rank, st_out, z, s32);
+}
+
+void launch_blk_partial(const uint8_t *blk, int nb, int parts, int D, int bh, float *part, hipStream_t st) {
+  const int per = (nb + parts - 1) / parts;
+  const dim3 grid((unsigned)parts, (unsigned)bh);
+  if (D == 64) hipLaunchKernelGGL(k_blk_partial<64>, grid, dim3(256), 0, st, blk, nb, per, part);
+  else hipLaunchKernelGGL(k_blk_partial<128>, grid, dim3(256), 0, st, blk, nb, per, part);
 }
 
 void launch_complement(const CompArgs &a, int D, hipStream_t st) {

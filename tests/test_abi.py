@@ -59,14 +59,14 @@ def test_plan_block_counts(grid, topk, nb, kb):
 
 
 def test_complement_scope_plans_its_block_states():
-    """The complement scope adds per-block states (fp32) and per-query-block complements
-    (bf16 S, fp32 z) to the workspace."""
+    """The complement scope adds per-block states and per-query-block complements
+    (bf16 S, fp32 z each) and the fp32 global S to the workspace."""
     prob = _prob()
     st, g = _plan(prob, rola.Config(topk=0.03))
     st2, c = _plan(prob, rola.Config(topk=0.03, lowrank_scope=rola.ROLA_LR_COMPLEMENT))
     assert st == st2 == 0 and (c.nb, c.kb) == (g.nb, g.kb)
     bh, nb, D = 40, 1182, 128
-    extra = bh * nb * (D * 32 + 32) * 4 + bh * D * 32 * 4 + bh * nb * D * 32 * 2 + bh * nb * 32 * 4
+    extra = bh * nb * (D * 32 * 2 + 32 * 4) + bh * D * 32 * 4 + bh * nb * D * 32 * 2 + bh * nb * 32 * 4
     assert extra <= c.workspace_bytes - g.workspace_bytes <= extra + 4 * 256
 
 
