@@ -36,7 +36,8 @@ def traffic_file(workload: str) -> str:
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for p in ("sparse_rank_attention_amd/csrc/rola_kernels.hip", "sparse_rank_attention_amd/csrc/rola_internal.h"):
+    for p in ("sparse_rank_attention_amd/csrc/rola_kernels.hip", "sparse_rank_attention_amd/csrc/rola_internal.h",
+              "sparse_rank_attention_amd/csrc/rola_device.h"):
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
