@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define ROLA_ABI_VERSION 3
+#define ROLA_ABI_VERSION 4
 #define ROLA_BLOCK 64
 #define ROLA_MAX_BLOCKS 4096 /* nb limit: N <= 262144 tokens */
 
@@ -104,7 +104,8 @@ typedef struct rola_plan_info {
   int32_t nb;       /* 64-token blocks */
   int32_t kb;       /* key blocks kept per query block */
   int64_t n_pad;    /* 64*nb rows addressed in every token tensor */
-  int64_t workspace_bytes; /* for the largest call (rola_forward) */
+  int64_t workspace_bytes; /* for rola_select_blocks, _sparse_attn, _lowrank_attn, _forward */
+  int64_t workspace_bytes_backward; /* for rola_backward (larger) */
 } rola_plan_info;
 
 /* ABI version (ROLA_ABI_VERSION) and a static message for a status. */
@@ -161,6 +162,30 @@ int32_t rola_forward(const rola_problem *prob, const rola_config *cfg, const voi
                      const void *k, const void *v, const float *wq, const float *wk,
                      const float *gate, int32_t *block_idx_out, void *out, void *workspace,
                      size_t workspace_bytes, void *stream);
+
+/*
+ * Backward of rola_forward (training; the README "AlibabaResearch/
+ * SparkDiffusion" fine-tunes and distils this module, sparse-finetune and
+ * distillation sections).  Given dout = dL/dO (bf16 or fp32 as
+ * config.out_dtype, the layout of O; fp32 values are rounded to bf16, to
+ * nearest even, as they enter the products) and the block map the forward used
+ * (block_idx, as rola_forward or rola_select_blocks wrote it: ascending ids
+ * < nb), writes the gradients of L through O = O_sparse + g * O_lr:
+ *   dq, dk, dv: bf16, the layout of Q (rows >= N written as 0);
+ *   dwq, dwk:   fp32 [D][rank] (overwritten), the gradients of Wq and Wk;
+ *   dgate:      fp32 [D+1] (overwritten), the gate's gradient -- required
+ *               exactly when gate is given.
+ * The block map is a constant of the backward (the top-k selection has no
+ * gradient).  Internally the state S, z, the sparse output and each row's
+ * log-sum-exp are recomputed.  Supported: precision ROLA_PREC_BF16 and
+ * lowrank_scope ROLA_LR_GLOBAL (ROLA_ERR_UNSUPPORTED otherwise).  The
+ * workspace must hold plan.workspace_bytes_backward bytes.
+ */
+int32_t rola_backward(const rola_problem *prob, const rola_config *cfg, const void *q, const void *k,
+                      const void *v, const float *wq, const float *wk, const float *gate,
+                      const int32_t *block_idx, const void *dout, void *dq, void *dk, void *dv,
+                      float *dwq, float *dwk, float *dgate, void *workspace, size_t workspace_bytes,
+                      void *stream);
 
 /*
  * Optional kernel timing for measurement.  While enabled, each call records a

@@ -41,6 +41,9 @@ struct Plan {
   int64_t off_qsc, off_ksc, off_vsc, off_kv8;  // fp8 only
   bool comp;  // complement scope of the low-rank branch
   int64_t off_blk, off_s32, off_stc, off_zc;  // complement scope only
+  // rola_backward: its buffers follow the forward's (offsets from 0)
+  int64_t b_os, b_os_elems, b_lse, b_lse2, b_dob, b_dn, b_dqp, b_dkp, b_dvp, b_ahat, b_duq, b_dwk, b_dy, b_dg,
+      b_wqP, b_wkP, b_sd, b_dsr, b_dst, b_ds32, b_dz, b_s32, b_part, b_tcount, b_tlist, total_bwd;
 };
 
 int32_t make_plan(const rola_problem *p, const rola_config *c, Plan *pl) {
@@ -134,6 +137,44 @@ int32_t make_plan(const rola_problem *p, const rola_config *c, Plan *pl) {
     P.off_zc = o; o = align_up(o + P.BH * nb * 32LL * 4);
   }
   P.total = o;
+
+  // backward buffers
+  const int64_t tok = P.BH * P.n_pad;
+  // the recomputed sparse output uses the problem's strides (the attention
+  // kernel writes O through them): its extent in elements
+  P.b_os_elems = (int64_t)(P.B - 1) * p->stride_b + (int64_t)(P.H - 1) * p->stride_h +
+                 (P.n_pad - 1) * p->stride_n + D;
+  const int64_t pp = rola::bwd_outer_parts(P.BH, nb, 0);
+  auto take = [&](int64_t bytes) {
+    const int64_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  P.b_os = take(P.b_os_elems * 2);
+  P.b_lse = take(tok * 4);
+  P.b_lse2 = take(tok * 4);
+  P.b_dob = take(tok * D * 2);
+  P.b_dn = take(tok * 4);
+  P.b_dqp = take(tok * D * 4);
+  P.b_dkp = take(tok * D * 4);
+  P.b_dvp = take(tok * D * 4);
+  P.b_ahat = take(tok * 32 * 2);
+  P.b_duq = take(tok * 32 * 2);
+  P.b_dwk = take(tok * 32 * 2);
+  P.b_dy = take(tok * 4);
+  P.b_dg = take(tok * 4);
+  P.b_wqP = take(D * 32 * 2);
+  P.b_wkP = take(D * 32 * 2);
+  P.b_sd = take(P.BH * 32 * D * 2 * 2);  // hi, then lo
+  P.b_dsr = take(P.BH * 32 * D * 2);
+  P.b_dst = take(P.BH * D * 32 * 2);
+  P.b_ds32 = take(P.BH * D * 32 * 4);
+  P.b_dz = take(P.BH * 32 * 4);
+  P.b_s32 = take(P.BH * D * 32 * 4);
+  P.b_part = take((P.BH * pp * 4 * (int64_t)D * 32 + P.BH) * 4);
+  P.b_tcount = take(P.BH * nb * 4);
+  P.b_tlist = take(P.BH * nb * (int64_t)nb * 4);
+  P.total_bwd = o;
   return ROLA_OK;
 }
 
@@ -271,7 +312,8 @@ int32_t run_quant8(const Plan &P, const rola_problem *p, const void *q, const vo
 
 int32_t run_attn(const Plan &P, const rola_problem *p, const rola_config *c, const void *q,
                  const void *k, const void *v, const int32_t *map, const float *gate, void *out,
-                 uint8_t *ws, bool sparse, bool lowrank, bool accum, hipStream_t st) {
+                 uint8_t *ws, bool sparse, bool lowrank, bool accum, hipStream_t st,
+                 float *lse = nullptr) {
   rola::AttnArgs a;
   a.q = (const uint16_t *)q; a.k = (const uint16_t *)k; a.v = (const uint16_t *)v;
   a.out = out;
@@ -290,6 +332,7 @@ int32_t run_attn(const Plan &P, const rola_problem *p, const rola_config *c, con
   a.z = (const float *)(ws + P.off_z);
   a.gate = lowrank ? gate : nullptr;
   a.complement = (lowrank && P.comp) ? 1 : 0;
+  a.lse = (sparse && !lowrank) ? lse : nullptr;
   a.rope = rope_args(P, ws);
   a.kv8 = ws + P.off_kv8;
   a.qsc = (const float *)(ws + P.off_qsc);
@@ -374,6 +417,7 @@ int32_t rola_plan(const rola_problem *prob, const rola_config *cfg, rola_plan_in
   out->kb = P.kb;
   out->n_pad = P.n_pad;
   out->workspace_bytes = P.total;
+  out->workspace_bytes_backward = P.total_bwd;
   return ROLA_OK;
 }
 
@@ -468,6 +512,84 @@ int32_t rola_forward(const rola_problem *prob, const rola_config *cfg, const voi
   ROLA_TRY(run_reduce(P, ws, st));
   ROLA_TRY(run_select(P, ws, (float *)(ws + P.off_scores), map, st));
   return run_attn(P, prob, cfg, q, k, v, map, gate, out, ws, true, true, false, st);
+}
+
+int32_t rola_backward(const rola_problem *prob, const rola_config *cfg, const void *q, const void *k,
+                      const void *v, const float *wq, const float *wk, const float *gate,
+                      const int32_t *block_idx, const void *dout, void *dq, void *dk, void *dv,
+                      float *dwq, float *dwk, float *dgate, void *workspace, size_t workspace_bytes,
+                      void *stream) {
+  Plan P;
+  ROLA_TRY(make_plan(prob, cfg, &P));
+  if (P.fp8 || P.comp) return ROLA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !wq || !wk || !block_idx || !dout || !dq || !dk || !dv || !dwq || !dwk)
+    return ROLA_ERR_INVALID_ARG;
+  if ((gate != nullptr) != (dgate != nullptr)) return ROLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv) || !aligned16(block_idx) || (gate && !aligned16(gate)))
+    return ROLA_ERR_ALIGNMENT;
+  if (((uintptr_t)wq & 3u) || ((uintptr_t)wk & 3u) || ((uintptr_t)dwq & 3u) || ((uintptr_t)dwk & 3u) ||
+      ((uintptr_t)dgate & 3u))
+    return ROLA_ERR_ALIGNMENT;
+  if (!workspace || (int64_t)workspace_bytes < P.total_bwd) return ROLA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return ROLA_ERR_ALIGNMENT;
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t *ws = (uint8_t *)workspace;
+  // forward state: bf16 projections, S (bf16 permuted and fp32) and z
+  ROLA_TRY(run_setup(P, wq, wk, ws, st));
+  ROLA_TRY(run_pass1(P, prob, nullptr, k, v, ws, false, true, st));
+  ROLA_TRY(timed("state_reduce", st, [&] {
+    rola::launch_state_reduce((const float *)(ws + P.off_part), 2 * P.nchunks, P.D, P.r, (int)P.BH,
+                              (uint16_t *)(ws + P.off_st), (float *)(ws + P.off_z),
+                              (float *)(ws + P.b_s32), st);
+  }));
+  // the sparse branch alone again, for each row's log-sum-exp (its output O_s
+  // goes to a scratch buffer with the problem's strides and is not used)
+  rola_config c16 = *cfg;
+  c16.out_dtype = ROLA_OUT_BF16;
+  ROLA_TRY(run_attn(P, prob, &c16, q, k, v, block_idx, nullptr, ws + P.b_os, ws, true, false, false, st,
+                    (float *)(ws + P.b_lse)));
+
+  rola::BwdArgs a;
+  a.q = (const uint16_t *)q; a.k = (const uint16_t *)k; a.v = (const uint16_t *)v;
+  a.dout = dout; a.dout_f32 = cfg->out_dtype == ROLA_OUT_F32;
+  a.wq = wq; a.wk = wk; a.gate = gate;
+  a.stride_b = prob->stride_b; a.stride_h = prob->stride_h; a.stride_n = prob->stride_n;
+  a.heads = P.H; a.nb = P.nb; a.kb = P.kb; a.rank = P.r;
+  a.n_tokens = P.N; a.bh_count = P.BH;
+  a.scale = P.scale;
+  a.scale_log2e = (float)((double)P.scale * 1.4426950408889634);
+  a.rope = rope_args(P, ws);
+  a.map = block_idx;
+  a.wqT = (const uint16_t *)(ws + P.off_wqT); a.wkT = (const uint16_t *)(ws + P.off_wkT);
+  a.st = (const uint16_t *)(ws + P.off_st);
+  a.s32 = (const float *)(ws + P.b_s32); a.z = (const float *)(ws + P.off_z);
+  a.lse = (const float *)(ws + P.b_lse);
+  a.lse_out = (float *)(ws + P.b_lse2);
+  a.wqP = (uint16_t *)(ws + P.b_wqP); a.wkP = (uint16_t *)(ws + P.b_wkP);
+  a.sd = (uint16_t *)(ws + P.b_sd); a.dsr = (uint16_t *)(ws + P.b_dsr); a.dst = (uint16_t *)(ws + P.b_dst);
+  a.ds32 = (float *)(ws + P.b_ds32); a.dz = (float *)(ws + P.b_dz);
+  a.dob = (uint16_t *)(ws + P.b_dob); a.dn = (float *)(ws + P.b_dn);
+  a.dqp = (float *)(ws + P.b_dqp); a.dkp = (float *)(ws + P.b_dkp); a.dvp = (float *)(ws + P.b_dvp);
+  a.ahat = (uint16_t *)(ws + P.b_ahat); a.duq = (uint16_t *)(ws + P.b_duq);
+  a.dwk_tok = (uint16_t *)(ws + P.b_dwk);
+  a.dy = (float *)(ws + P.b_dy); a.dg = (float *)(ws + P.b_dg);
+  a.part = (float *)(ws + P.b_part);
+  a.tcount = (int32_t *)(ws + P.b_tcount); a.tlist = (int32_t *)(ws + P.b_tlist);
+  a.dq = (uint16_t *)dq; a.dk = (uint16_t *)dk; a.dv = (uint16_t *)dv;
+  a.dwq = dwq; a.dwk = dwk; a.dgate = dgate;
+  const int D = P.D;
+  ROLA_TRY(timed("bwd_prep", st, [&] { rola::launch_bwd_prep(a, D, st); }));
+  ROLA_TRY(timed("bwd_query", st, [&] { rola::launch_bwd_query(a, D, st); }));
+  ROLA_TRY(timed("bwd_ds", st, [&] { rola::launch_bwd_outer(a, D, rola::kOuterDout, st); }));
+  ROLA_TRY(timed("bwd_dsops", st, [&] { rola::launch_bwd_dsops(a, D, st); }));
+  ROLA_TRY(timed("bwd_key", st, [&] { rola::launch_bwd_key(a, D, st); }));
+  ROLA_TRY(timed("bwd_dwq", st, [&] { rola::launch_bwd_outer(a, D, rola::kOuterRopeQ, st); }));
+  ROLA_TRY(timed("bwd_dwk", st, [&] { rola::launch_bwd_outer(a, D, rola::kOuterRopeK, st); }));
+  if (gate) ROLA_TRY(timed("bwd_dgate", st, [&] { rola::launch_bwd_outer(a, D, rola::kOuterGate, st); }));
+  ROLA_TRY(timed("bwd_dq", st, [&] { rola::launch_bwd_dq(a, D, st); }));
+  ROLA_TRY(timed("bwd_tmap", st, [&] { rola::launch_bwd_tmap(a, st); }));
+  return timed("bwd_dkv", st, [&] { rola::launch_bwd_dkv(a, D, st); });
 }
 
 int32_t rola_mfma_probe(int32_t precision, int32_t iters, double *flop, float *sink, void *stream) {

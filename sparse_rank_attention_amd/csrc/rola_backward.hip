@@ -1,0 +1,899 @@
+// rola_backward.hip -- gfx950 kernels of the RoLA backward (training).
+//
+// Gradients of O = O_sparse + g * O_lr with respect to Q, K, V, the two
+// low-rank projections and the output gate (pages: "SparkDiffusion: 265x
+// Faster Video Generation on Consumer GPUs via Sparse Attention &
+// Distillation", section "RoLA: Preserving Global Context at Extreme
+// Sparsity"; README "AlibabaResearch/SparkDiffusion", sparse-finetune and
+// distillation sections, which train the module and name its trainable
+// projections and gate).  The block map is a constant of the backward: the
+// top-k selection is piecewise constant in Q and K.
+//
+// Per (batch, head), with c = scale and L = O_lr:
+//   sparse:   P = exp2(c log2e q.k - lse2), D_n = sum_m P_nm dP_nm,
+//             dS = P (dO.v - D), dq = c dS k, dk = c dS^T q, dv = P^T dO
+//   low rank: a = phi(u), u = Wq^T R(q); num = S^T a, den = a.z, L = num/den;
+//             with the gate g = sigmoid(y), y = q.w + b:
+//             dg = dO.L, dy = dg g (1-g), dnum = g dO / den, dden = -g dg / den,
+//             da = S dnum + z dden, du = da phi'(u), dq += R^T(Wq du) + dy w,
+//             dWq = sum R(q) du^T, dS = sum a dnum^T, dz = sum a dden,
+//             db = dS v + dz, dv += dS^T b, dw' = db phi'(Wk^T R(k)),
+//             dk += R^T(Wk dw'), dWk = sum R(k) dw'^T, dw = sum dy q, db_gate = sum dy.
+//
+// Kernels, in launch order (after pass 1's state and a sparse-only forward
+// that leaves O_s and the row log-sum-exp):
+//   k_bwd_prep   bf16 operand copies: Wq, Wk rank-permuted, S with d permuted
+//   k_bwd_query  per query token: the low-rank and gate terms of dq, dL/du,
+//                g a / den and dO in bf16 (MFMA on 32-token tiles)
+//   k_bwd_outer  sums X^T Y over tokens on MFMA (dS, dWq, dWk, gate weights)
+//   k_bwd_sum    fixed-order sums of the partials
+//   k_bwd_dz     dz and the gate bias gradient per head
+//   k_bwd_dsops  bf16 operand copies of dS
+//   k_bwd_key    per key token: the low-rank terms of dk, dv and dL/dw'
+//   k_bwd_dq     sparse dq over each query block's kept key blocks
+//   k_bwd_tmap   query blocks that keep each key block
+//   k_bwd_dkv    sparse dk, dv over the query blocks keeping each key block
+#include "rola_device.h"
+
+namespace rola {
+
+// ------------------------------------------------------------ k_bwd_prep
+// y = 0: Wq, Wk as bf16 [D][32] with the rank index permuted per 16-group
+// (the A operand of R^T-side products whose B operand is an accumulator);
+// y = 1: per head, S as a bf16 pair hi + lo, [32][D] each with d permuted
+// per 16-group (the A operand of S dnum).  Ranks >= rank are zero.
+template <int D>
+__global__ __launch_bounds__(256) void k_bwd_prep(BwdArgs a) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (blockIdx.y == 0) {
+    if (t >= D * 32) return;
+    const int d = (int)(t / 32), pos = (int)(t % 32), r = perm16_key_of_pos(pos);
+    const float wq = r < a.rank ? a.wq[d * a.rank + r] : 0.0f;
+    const float wk = r < a.rank ? a.wk[d * a.rank + r] : 0.0f;
+    a.wqP[t] = __builtin_bit_cast(uint16_t, (__bf16)wq);
+    a.wkP[t] = __builtin_bit_cast(uint16_t, (__bf16)wk);
+  } else {
+    if (t >= a.bh_count * 32 * D) return;
+    const int64_t bh = t / (32 * D);
+    const int r = (int)((t / D) % 32), p = (int)(t % D), d = perm16_key_of_pos(p);
+    const float x = a.s32[bh * D * 32 + d * 32 + r];
+    const __bf16 hi = (__bf16)x;
+    a.sd[t] = __builtin_bit_cast(uint16_t, hi);
+    a.sd[a.bh_count * 32 * D + t] = __builtin_bit_cast(uint16_t, (__bf16)(x - (float)hi));
+  }
+}
+
+// inverse rotation (R^T) of the pair (x0, x1) at even dim d of a token at (pt, ph, pw)
+static __device__ __forceinline__ void rope_back(float &x0, float &x1, int d, int pt, int ph, int pw,
+                                                 float freq, const RopeArgsDev &ra) {
+  const int pos = d < ra.off1 ? pt : (d < ra.off2 ? ph : pw);
+  float rev = (float)pos * freq * 0.15915494309189535f;
+  rev = rev - floorf(rev);
+  const float cs = __builtin_amdgcn_cosf(rev), sn = __builtin_amdgcn_sinf(rev);
+  const float y0 = x0 * cs + x1 * sn, y1 = x1 * cs - x0 * sn;
+  x0 = y0;
+  x1 = y1;
+}
+
+// x as hi + lo, both bf16 (hi = RNE(x), lo = RNE(x - hi)), into element e of two operands
+static __device__ __forceinline__ void split_bf16(float x, bf16x8 &hi, bf16x8 &lo, int e) {
+  const __bf16 h = (__bf16)x;
+  hi[e] = h;
+  lo[e] = (__bf16)(x - (float)h);
+}
+
+static __device__ __forceinline__ uint2 pack_bf16x4(float v0, float v1, float v2, float v3) {
+  const __bf16 b0 = (__bf16)v0, b1 = (__bf16)v1, b2 = (__bf16)v2, b3 = (__bf16)v3;
+  uint2 o;
+  o.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+  o.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
+  return o;
+}
+
+// ----------------------------------------------------------- k_bwd_query
+// One wave per 32-token tile of one (batch, head); lane column t = token.
+// MFMA C/D rows are the rank index (u, a, da, du) or the head dim (num, dO,
+// dRq) in the accumulator order 8*(i/4) + 4*g + i%4, so the elementwise
+// steps are lane-local and the bf16 accumulators feed the next product as B
+// operands against the permuted A copies.
+template <int D, bool GATE, bool DF32>
+__global__ __launch_bounds__(256) void k_bwd_query(BwdArgs a) {
+  constexpr int NS = D / 16, DT = D / 32;
+  __shared__ __attribute__((aligned(16))) float sfreq[D / 2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5, col = lane & 31;
+  for (int p2 = tid; p2 < D / 2; p2 += 256) sfreq[p2] = rope_freq(2 * p2, a.rope);
+  __syncthreads();
+  const int bh = blockIdx.y;
+  const int tile = blockIdx.x * 4 + wave;
+  if (tile >= 2 * a.nb) return;
+  const int b = bh / a.heads, h = bh % a.heads;
+  const int64_t base = (int64_t)b * a.stride_b + (int64_t)h * a.stride_h;
+  const int64_t n_pad = (int64_t)a.nb * 64;
+  const int64_t n = (int64_t)tile * 32 + col;
+  const bool valid = n < a.n_tokens;
+  const int64_t nc = valid ? n : a.n_tokens - 1;
+  const int64_t row = (int64_t)bh * n_pad + n;
+
+  bf16x8 qreg[NS];
+  const uint16_t *qrow = a.q + base + nc * a.stride_n;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) qreg[s] = *(const bf16x8 *)(qrow + 16 * s + 8 * g);
+  float y = 0.0f;
+  if (GATE) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const f32x4 w0 = *(const f32x4 *)(a.gate + 16 * s + 8 * g);
+      const f32x4 w1 = *(const f32x4 *)(a.gate + 16 * s + 8 * g + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        y += (float)qreg[s][e] * w0[e];
+        y += (float)qreg[s][4 + e] * w1[e];
+      }
+    }
+    y += shfl_xor32(y);
+    y += a.gate[D];
+  }
+  // u = Wq^T R(q), a = phi(u), den = a . z
+  int pt, ph, pw;
+  token_pos(nc, a.rope, pt, ph, pw);
+  f32x16 uacc = f32x16{};
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const f32x4 fr = *(const f32x4 *)&sfreq[8 * s + 4 * g];
+    const float freq[4] = {fr[0], fr[1], fr[2], fr[3]};
+    const bf16x8 qr = rope8(qreg[s], 16 * s + 8 * g, pt, ph, pw, freq, a.rope);
+    uacc = mfma_bf16(*(const bf16x8 *)(a.wqT + col * D + 16 * s + 8 * g), qr, uacc);
+  }
+  const f32x4 *zb = (const f32x4 *)(a.z + (int64_t)bh * 32);
+  f32x4 zr[4];
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) zr[q4] = zb[2 * q4 + g];  // z[8 q4 + 4 g .. +4]
+  float av[16];
+  float den = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = 8 * (i >> 2) + 4 * g + (i & 3);
+    av[i] = r < a.rank ? phi(uacc[i]) : 0.0f;
+    den += av[i] * zr[i >> 2][i & 3];
+  }
+  den += shfl_xor32(den);
+  const float inv_den = 1.0f / den;
+  bf16x8 aop[2];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) aop[i >> 3][i & 7] = (__bf16)av[i];
+  // num = S^T a (rows d)
+  const uint16_t *stb = a.st + (int64_t)bh * D * 32;
+  f32x16 num[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    num[dt] = f32x16{};
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+      num[dt] = mfma_bf16(*(const bf16x8 *)(stb + (32 * dt + col) * 32 + 16 * s2 + 8 * g), aop[s2], num[dt]);
+  }
+  // dO and O_s at the lane's dims d = 32 dt + 8 q4 + 4 g + j; D_n and dg
+  f32x16 dov[DT];
+  float dg_p = 0.0f;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d0 = 32 * dt + 8 * q4 + 4 * g;
+      float dv4[4];
+      if (DF32) {
+        const f32x4 x = *(const f32x4 *)((const float *)a.dout + base + nc * a.stride_n + d0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dv4[j] = valid ? x[j] : 0.0f;
+      } else {
+        const uint2 u = *(const uint2 *)((const uint16_t *)a.dout + base + nc * a.stride_n + d0);
+        dv4[0] = bflo(u.x); dv4[1] = bfhi(u.x); dv4[2] = bflo(u.y); dv4[3] = bfhi(u.y);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dv4[j] = valid ? dv4[j] : 0.0f;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        dov[dt][4 * q4 + j] = dv4[j];
+        dg_p += dv4[j] * (num[dt][4 * q4 + j] * inv_den);
+      }
+      *(uint2 *)(a.dob + row * D + d0) = pack_bf16x4(dv4[0], dv4[1], dv4[2], dv4[3]);
+    }
+  }
+  const float dg = dg_p + shfl_xor32(dg_p);
+  const float gv = GATE ? 1.0f / (1.0f + __expf(-y)) : 1.0f;
+  const float dy = GATE ? dg * gv * (1.0f - gv) : 0.0f;
+  const float sc = gv * inv_den, dden = -gv * dg * inv_den;
+  // da = S dnum + z dden (rows r).  The two terms largely cancel, so S and
+  // dnum enter as bf16 pairs hi + lo (three products: hi hi, hi lo, lo hi)
+  const uint16_t *sdb = a.sd + (int64_t)bh * 32 * D;
+  const uint16_t *sdl = sdb + a.bh_count * 32 * D;
+  f32x16 da = f32x16{};
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      bf16x8 bh_, bl_;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) split_bf16(dov[dt][8 * s2 + e] * sc, bh_, bl_, e);
+      const int off = col * D + 32 * dt + 16 * s2 + 8 * g;
+      const bf16x8 ah = *(const bf16x8 *)(sdb + off), al = *(const bf16x8 *)(sdl + off);
+      da = mfma_bf16(ah, bh_, da);
+      da = mfma_bf16(ah, bl_, da);
+      da = mfma_bf16(al, bh_, da);
+    }
+  }
+  float du[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = 8 * (i >> 2) + 4 * g + (i & 3);
+    const float dai = da[i] + zr[i >> 2][i & 3] * dden;
+    du[i] = (r < a.rank && valid) ? dai * (uacc[i] > 0.0f ? 1.0f : __expf(uacc[i])) : 0.0f;
+  }
+  bf16x8 duop[2];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) duop[i >> 3][i & 7] = (__bf16)du[i];
+  // dRq = Wq du (rows d), then R^T and the gate term
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    f32x16 dr = f32x16{};
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+      dr = mfma_bf16(*(const bf16x8 *)(a.wqP + (32 * dt + col) * 32 + 16 * s2 + 8 * g), duop[s2], dr);
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d0 = 32 * dt + 8 * q4 + 4 * g;
+      float v4[4] = {dr[4 * q4], dr[4 * q4 + 1], dr[4 * q4 + 2], dr[4 * q4 + 3]};
+      rope_back(v4[0], v4[1], d0, pt, ph, pw, sfreq[d0 / 2], a.rope);
+      rope_back(v4[2], v4[3], d0 + 2, pt, ph, pw, sfreq[d0 / 2 + 1], a.rope);
+      if (GATE) {
+        const f32x4 w4 = *(const f32x4 *)(a.gate + d0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v4[j] += dy * w4[j];
+      }
+      f32x4 o = {v4[0], v4[1], v4[2], v4[3]};
+      if (!valid) o = f32x4{0.f, 0.f, 0.f, 0.f};
+      *(f32x4 *)(a.dqp + row * D + d0) = o;
+    }
+  }
+  // per-token work arrays
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    const int r0 = 8 * q4 + 4 * g;
+    const float s = valid ? sc : 0.0f;
+    *(uint2 *)(a.ahat + row * 32 + r0) =
+        pack_bf16x4(av[4 * q4] * s, av[4 * q4 + 1] * s, av[4 * q4 + 2] * s, av[4 * q4 + 3] * s);
+    *(uint2 *)(a.duq + row * 32 + r0) = pack_bf16x4(du[4 * q4], du[4 * q4 + 1], du[4 * q4 + 2], du[4 * q4 + 3]);
+  }
+  if (lane < 32) {
+    a.dg[row] = valid ? dg : 0.0f;
+    a.dy[row] = valid ? dy : 0.0f;
+  }
+}
+
+// ----------------------------------------------------------- k_bwd_outer
+// C[D][32] += sum over tokens of X[t][d] Y[t][r] on MFMA.  Each wave stages
+// one 32-token tile of X (row-major, V-style swizzle) and of Y ([32][32]) in
+// its own LDS area and reads both with the transposing LDS load, so the
+// token index is the MFMA k index on both sides in the same order.
+//   kOuterRopeQ: X = R(q), Y = dL/du (query)    -> dWq (summed over heads)
+//   kOuterDout:  X = dO,   Y = g a / den        -> dS^T per head
+//   kOuterRopeK: X = R(k), Y = dL/dw' (key)     -> dWk (summed over heads)
+//   kOuterGate:  X = q,    Y = (dy, 0, ..., 0)  -> gate weights (column 0)
+// Workgroup (p, bh) takes tiles p*4 + wave, p*4 + wave + 4*PP, ... of head bh
+// and writes one fp32 partial [D][32] per wave.
+template <int D, int MODE>
+__global__ __launch_bounds__(256) void k_bwd_outer(BwdArgs a, int PP) {
+  constexpr int NS = D / 16, DT = D / 32;
+  __shared__ __attribute__((aligned(1024))) uint16_t sx[4][32 * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sy[4][32 * 32];
+  __shared__ __attribute__((aligned(16))) float sfreq[D / 2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5, col = lane & 31;
+  for (int p2 = tid; p2 < D / 2; p2 += 256) sfreq[p2] = rope_freq(2 * p2, a.rope);
+  __syncthreads();
+  const int bh = blockIdx.y, p = blockIdx.x;
+  const int b = bh / a.heads, h = bh % a.heads;
+  const int64_t base = (int64_t)b * a.stride_b + (int64_t)h * a.stride_h;
+  const int64_t n_pad = (int64_t)a.nb * 64;
+  uint16_t *X = sx[wave], *Y = sy[wave];
+  f32x16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
+  for (int tile = p * 4 + wave; tile < 2 * a.nb; tile += 4 * PP) {
+    const int64_t n = (int64_t)tile * 32 + col;
+    const bool valid = n < a.n_tokens;
+    const int64_t nc = valid ? n : a.n_tokens - 1;
+    const int64_t row = (int64_t)bh * n_pad + n;
+    // X row (8 dims per 16-byte chunk 2s + g), zero on padded tokens
+    bf16x8 xr[NS];
+    if (MODE == kOuterDout) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) xr[s] = *(const bf16x8 *)(a.dob + row * D + 16 * s + 8 * g);
+    } else {
+      const uint16_t *src = (MODE == kOuterRopeK ? a.k : a.q) + base + nc * a.stride_n;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) xr[s] = *(const bf16x8 *)(src + 16 * s + 8 * g);
+      if (MODE == kOuterRopeQ || MODE == kOuterRopeK) {
+        int pt, ph, pw;
+        token_pos(nc, a.rope, pt, ph, pw);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const f32x4 fr = *(const f32x4 *)&sfreq[8 * s + 4 * g];
+          const float freq[4] = {fr[0], fr[1], fr[2], fr[3]};
+          xr[s] = rope8(xr[s], 16 * s + 8 * g, pt, ph, pw, freq, a.rope);
+        }
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int c = 2 * s + g;
+      const u32x4 v = valid ? as_u32x4(xr[s]) : u32x4{0u, 0u, 0u, 0u};
+      *(u32x4 *)(X + col * D + ((c ^ swz_v<D>(col)) << 3)) = v;
+    }
+    // Y row: 32 bf16 in 4 chunks, chunks 2g and 2g+1 from this lane
+    u32x4 y0, y1;
+    if (MODE == kOuterGate) {
+      const float dyv = a.dy[row];
+      y0 = u32x4{g == 0 ? (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)dyv) : 0u, 0u, 0u, 0u};
+      y1 = u32x4{0u, 0u, 0u, 0u};
+    } else {
+      const uint16_t *ysrc = (MODE == kOuterRopeQ ? a.duq : MODE == kOuterDout ? a.ahat : a.dwk_tok) + row * 32;
+      y0 = *(const u32x4 *)(ysrc + 16 * g);
+      y1 = *(const u32x4 *)(ysrc + 16 * g + 8);
+    }
+    *(u32x4 *)(Y + col * 32 + 16 * g) = y0;
+    *(u32x4 *)(Y + col * 32 + 16 * g + 8) = y1;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's tiles written
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const bf16x8 yb = vt_operand<32>(Y, s2, 0, lane);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma_bf16(vt_operand<D>(X, s2, dt, lane), yb, acc[dt]);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next tile's writes
+  }
+  float *out = a.part + (((int64_t)bh * PP + p) * 4 + wave) * (D * 32);
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int d = 32 * dt + 8 * (i >> 2) + 4 * g + (i & 3);
+      out[d * 32 + col] = acc[dt][i];
+    }
+  }
+}
+
+// ------------------------------------------------------------- k_bwd_sum
+// Fixed-order sums of k_bwd_outer's partials.  PER_HEAD: per head over its
+// 4*PP partials (dS^T -> ds32); else over all heads' partials, written as
+// [D][rank] (dWq, dWk) or, for the gate, column 0 as dgate[0..D) plus the
+// per-head bias sums as dgate[D].
+template <int D, bool PER_HEAD, bool GATE>
+__global__ __launch_bounds__(256) void k_bwd_sum(BwdArgs a, int PP, float *dst) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= D * 32) return;
+  const int bh0 = PER_HEAD ? blockIdx.y : 0;
+  const int64_t np = PER_HEAD ? 4LL * PP : 4LL * PP * a.bh_count;
+  const float *p = a.part + (int64_t)bh0 * 4 * PP * (D * 32) + idx;
+  float acc8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  int64_t c = 0;
+  for (; c + 8 <= np; c += 8) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc8[i] += p[(c + i) * (D * 32)];
+  }
+  for (int i = 0; c + i < np; ++i) acc8[i] += p[(c + i) * (D * 32)];
+  const float acc = ((acc8[0] + acc8[1]) + (acc8[2] + acc8[3])) + ((acc8[4] + acc8[5]) + (acc8[6] + acc8[7]));
+  const int d = idx / 32, r = idx % 32;
+  if (PER_HEAD) {
+    dst[(int64_t)bh0 * D * 32 + idx] = acc;
+  } else if (GATE) {
+    if (r == 0) dst[d] = acc;
+    if (idx == 0) {
+      float bsum = 0.0f;
+      for (int64_t i = 0; i < a.bh_count; ++i) bsum += a.part[a.bh_count * 4 * PP * (D * 32) + i];
+      dst[D] = bsum;
+    }
+  } else if (r < a.rank) {
+    dst[d * a.rank + r] = acc;
+  }
+}
+
+// -------------------------------------------------------------- k_bwd_dz
+// Per head: dz[r] = sum_t dden_t a_t[r] = -sum_t dg_t (g a / den)_t[r] and
+// the gate-bias partial sum_t dy_t (into part[bias_at + bh]).
+__global__ __launch_bounds__(256) void k_bwd_dz(BwdArgs a, int64_t bias_at) {
+  __shared__ float red[8][33];
+  const int tid = threadIdx.x, r = tid & 31, lane8 = tid >> 5;
+  const int bh = blockIdx.x;
+  const int64_t n_pad = (int64_t)a.nb * 64, row0 = (int64_t)bh * n_pad;
+  float acc = 0.0f, yb = 0.0f;
+  for (int64_t n = lane8; n < a.n_tokens; n += 8) {
+    acc -= a.dg[row0 + n] * __builtin_bit_cast(float, ((uint32_t)a.ahat[(row0 + n) * 32 + r]) << 16);
+    if (r == 0) yb += a.dy[row0 + n];
+  }
+  red[lane8][r] = acc;
+  red[lane8][32] = 0.0f;
+  __syncthreads();
+  if (r == 0) red[lane8][32] = yb;
+  __syncthreads();
+  if (tid < 32) {
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s += red[i][tid];
+    a.dz[(int64_t)bh * 32 + tid] = tid < a.rank ? s : 0.0f;
+    if (tid == 0) {
+      float t = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) t += red[i][32];
+      a.part[bias_at + bh] = t;
+    }
+  }
+}
+
+// ----------------------------------------------------------- k_bwd_dsops
+// dS as bf16 operands: dsr [32][D] (rows r, natural d) and dst [D][32]
+// (rows d, rank permuted).
+template <int D>
+__global__ __launch_bounds__(256) void k_bwd_dsops(BwdArgs a) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= a.bh_count * D * 32) return;
+  const int64_t bh = t / (D * 32);
+  const int e = (int)(t % (D * 32)), d = e / 32, r = e % 32;
+  const __bf16 v = (__bf16)a.ds32[t];
+  a.dsr[bh * 32 * D + r * D + d] = __builtin_bit_cast(uint16_t, v);
+  a.dst[bh * D * 32 + d * 32 + perm16_key_of_pos(r)] = __builtin_bit_cast(uint16_t, v);
+}
+
+// ------------------------------------------------------------- k_bwd_key
+// One wave per 32-token tile of keys: b = phi(Wk^T R(k)), db = dS v + dz,
+// dw' = db phi'(.), the low-rank parts of dk (R^T(Wk dw')) and dv (dS^T b).
+template <int D>
+__global__ __launch_bounds__(256) void k_bwd_key(BwdArgs a) {
+  constexpr int NS = D / 16, DT = D / 32;
+  __shared__ __attribute__((aligned(16))) float sfreq[D / 2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5, col = lane & 31;
+  for (int p2 = tid; p2 < D / 2; p2 += 256) sfreq[p2] = rope_freq(2 * p2, a.rope);
+  __syncthreads();
+  const int bh = blockIdx.y;
+  const int tile = blockIdx.x * 4 + wave;
+  if (tile >= 2 * a.nb) return;
+  const int b = bh / a.heads, h = bh % a.heads;
+  const int64_t base = (int64_t)b * a.stride_b + (int64_t)h * a.stride_h;
+  const int64_t n_pad = (int64_t)a.nb * 64;
+  const int64_t m = (int64_t)tile * 32 + col;
+  const bool valid = m < a.n_tokens;
+  const int64_t mc = valid ? m : a.n_tokens - 1;
+  const int64_t row = (int64_t)bh * n_pad + m;
+  bf16x8 kreg[NS], vreg[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    kreg[s] = *(const bf16x8 *)(a.k + base + mc * a.stride_n + 16 * s + 8 * g);
+    vreg[s] = *(const bf16x8 *)(a.v + base + mc * a.stride_n + 16 * s + 8 * g);
+  }
+  int pt, ph, pw;
+  token_pos(mc, a.rope, pt, ph, pw);
+  f32x16 wacc = f32x16{}, db = f32x16{};
+  const uint16_t *dsb = a.dsr + (int64_t)bh * 32 * D;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const f32x4 fr = *(const f32x4 *)&sfreq[8 * s + 4 * g];
+    const float freq[4] = {fr[0], fr[1], fr[2], fr[3]};
+    const bf16x8 kr = rope8(kreg[s], 16 * s + 8 * g, pt, ph, pw, freq, a.rope);
+    wacc = mfma_bf16(*(const bf16x8 *)(a.wkT + col * D + 16 * s + 8 * g), kr, wacc);
+    db = mfma_bf16(*(const bf16x8 *)(dsb + col * D + 16 * s + 8 * g), vreg[s], db);
+  }
+  const f32x4 *dzb = (const f32x4 *)(a.dz + (int64_t)bh * 32);
+  float bv[16], dw[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = 8 * (i >> 2) + 4 * g + (i & 3);
+    const bool ok = r < a.rank && valid;
+    const float dzr = dzb[2 * (i >> 2) + g][i & 3];
+    bv[i] = ok ? phi(wacc[i]) : 0.0f;
+    dw[i] = ok ? (db[i] + dzr) * (wacc[i] > 0.0f ? 1.0f : __expf(wacc[i])) : 0.0f;
+  }
+  bf16x8 bop[2], dwop[2];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    bop[i >> 3][i & 7] = (__bf16)bv[i];
+    dwop[i >> 3][i & 7] = (__bf16)dw[i];
+  }
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4)
+    *(uint2 *)(a.dwk_tok + row * 32 + 8 * q4 + 4 * g) =
+        pack_bf16x4(dw[4 * q4], dw[4 * q4 + 1], dw[4 * q4 + 2], dw[4 * q4 + 3]);
+  const uint16_t *dstb = a.dst + (int64_t)bh * D * 32;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    f32x16 dv = f32x16{}, dr = f32x16{};
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      dv = mfma_bf16(*(const bf16x8 *)(dstb + (32 * dt + col) * 32 + 16 * s2 + 8 * g), bop[s2], dv);
+      dr = mfma_bf16(*(const bf16x8 *)(a.wkP + (32 * dt + col) * 32 + 16 * s2 + 8 * g), dwop[s2], dr);
+    }
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d0 = 32 * dt + 8 * q4 + 4 * g;
+      float k4[4] = {dr[4 * q4], dr[4 * q4 + 1], dr[4 * q4 + 2], dr[4 * q4 + 3]};
+      rope_back(k4[0], k4[1], d0, pt, ph, pw, sfreq[d0 / 2], a.rope);
+      rope_back(k4[2], k4[3], d0 + 2, pt, ph, pw, sfreq[d0 / 2 + 1], a.rope);
+      f32x4 ok = {k4[0], k4[1], k4[2], k4[3]};
+      f32x4 ov = {dv[4 * q4], dv[4 * q4 + 1], dv[4 * q4 + 2], dv[4 * q4 + 3]};
+      if (!valid) ok = ov = f32x4{0.f, 0.f, 0.f, 0.f};
+      *(f32x4 *)(a.dkp + row * D + d0) = ok;
+      *(f32x4 *)(a.dvp + row * D + d0) = ov;
+    }
+  }
+}
+
+// ------------------------------------------------------------- tile copies
+// Copy 64 token rows of a bf16 matrix (row stride `stride` elements, rows
+// past `last` taken from row `last`) into an LDS tile, row-major with the
+// V-style chunk swizzle, 16 bytes per lane per op; `ops` ops per thread of a
+// 128-thread workgroup, thread tid taking chunks o*128 + tid.
+template <int D>
+static __device__ __forceinline__ void copy_tile64(const uint16_t *src, int64_t stride, int64_t r0,
+                                                   int64_t last, uint16_t *tile, int tid) {
+  constexpr int CH = D / 8, OPS = 64 * CH / 128;
+  const int wave = tid >> 6;
+#pragma unroll
+  for (int o = 0; o < OPS; ++o) {
+    const int cidx = o * 128 + tid;
+    const int row = cidx / CH, pc = cidx % CH;
+    const int64_t sr = min(r0 + row, last);
+    lds_dma16(src + sr * stride + ((pc ^ swz_v<D>(row)) << 3), tile + (o * 128 + wave * 64) * 8);
+  }
+}
+
+// 16-byte MFMA operand from row `row` of a V-style swizzled tile: dims
+// 16 s + 8 g .. +8 (logical chunk 2 s + g)
+template <int D>
+static __device__ __forceinline__ bf16x8 row_operand(const uint16_t *tile, int row, int s, int g) {
+  return *(const bf16x8 *)(tile + row * D + (((2 * s + g) ^ swz_v<D>(row)) << 3));
+}
+
+// -------------------------------------------------------------- k_bwd_dq
+// One workgroup (2 waves, 32 queries each) per query block, with K and V
+// tiles of its kept key blocks in a two-slot LDS ring, walked twice:
+//  pass 0: S^T = K Q^T and dP^T = V dO^T give, with the forward's log-sum-
+//          exp, the fp32 row sums l = sum P and sum P dP; then lse2 += log2 l
+//          and D = sum P dP / l, so that the weights P used below sum to one
+//          and D = sum P dP exactly for them (the forward normalised with its
+//          bf16 weights; a D from its O would leave sum dS != 0);
+//  pass 1: dS^T = P^T (dP^T - D), dq^T += K^T dS^T on MFMA.
+// Writes the corrected lse2 and D for k_bwd_dkv, adds the low-rank part and
+// writes dq in bf16.
+template <int D>
+__global__ __launch_bounds__(128) void k_bwd_dq(BwdArgs a) {
+  constexpr int NS = D / 16, DT = D / 32, TILE = 64 * D, OPS = 2 * (64 * (D / 8)) / 128;
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[2][2 * TILE];
+  const int tid = threadIdx.x, lane = tid & 63, half = tid >> 6, g = lane >> 5, col = lane & 31;
+  const int qb = blockIdx.x, bh = blockIdx.y;
+  const int b = bh / a.heads, h = bh % a.heads;
+  const int64_t base = (int64_t)b * a.stride_b + (int64_t)h * a.stride_h;
+  const int64_t n_pad = (int64_t)a.nb * 64;
+  const int64_t n = (int64_t)qb * 64 + 32 * half + col;
+  const bool valid = n < a.n_tokens;
+  const int64_t nc = valid ? n : a.n_tokens - 1;
+  const int64_t row = (int64_t)bh * n_pad + n;
+  bf16x8 qreg[NS], doreg[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    qreg[s] = *(const bf16x8 *)(a.q + base + nc * a.stride_n + 16 * s + 8 * g);
+    doreg[s] = *(const bf16x8 *)(a.dob + row * D + 16 * s + 8 * g);
+  }
+  float lse2 = valid ? a.lse[row] : 0.0f;
+  // the block map through the scalar cache (uniform per workgroup)
+  typedef const __attribute__((address_space(4))) int32_t *cint_p;
+  const cint_p mrow = (cint_p)(a.map + ((int64_t)bh * a.nb + qb) * a.kb);
+  const int kb = a.kb, T = 2 * kb;  // tile t walks entry t mod kb, pass t / kb
+  wait_vmcnt<0>();
+  auto issue = [&](int t, int slot) __attribute__((always_inline)) {
+    const int j = __builtin_amdgcn_readfirstlane(mrow[t < kb ? t : t - kb]);
+    copy_tile64<D>(a.k + base, a.stride_n, (int64_t)j * 64, a.n_tokens - 1, ring[slot], tid);
+    copy_tile64<D>(a.v + base, a.stride_n, (int64_t)j * 64, a.n_tokens - 1, ring[slot] + TILE, tid);
+  };
+  issue(0, 0);
+  issue(1, 1);
+  f32x16 dq[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dq[dt] = f32x16{};
+  const float c = a.scale_log2e;
+  float lsum = 0.0f, pdp = 0.0f, dn = 0.0f;
+  for (int t = 0; t < T; ++t) {
+    if (t + 1 < T) wait_vmcnt<OPS>();
+    else wait_vmcnt<0>();
+    __syncthreads();
+    const bool second = t >= kb;
+    if (t == kb) {
+      // pass 0 done: normalise the weights and form D
+      const float l = pair_sum32(lsum);
+      dn = l > 0.0f ? pair_sum32(pdp) / l : 0.0f;
+      lse2 += l > 0.0f ? log2f(l) : 0.0f;
+    }
+    const uint16_t *sK = ring[t & 1], *sV = ring[t & 1] + TILE;
+    const int j = __builtin_amdgcn_readfirstlane(mrow[second ? t - kb : t]);
+    const int lim = (int)min<int64_t>(64, a.n_tokens - (int64_t)j * 64);  // valid keys of the block
+    // dS as a bf16 pair hi + lo (about 16 significant bits): its terms cancel
+    // in the sum over keys
+    bf16x8 dshi[4], dslo[4];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      f32x16 sacc = f32x16{}, dpacc = f32x16{};
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        sacc = mfma_bf16(row_operand<D>(sK, 32 * h2 + col, s, g), qreg[s], sacc);
+        dpacc = mfma_bf16(row_operand<D>(sV, 32 * h2 + col, s, g), doreg[s], dpacc);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = 32 * h2 + 8 * (i >> 2) + 4 * g + (i & 3);
+        const float pv = (valid && key < lim) ? fast_exp2(__builtin_fmaf(sacc[i], c, -lse2)) : 0.0f;
+        if (!second) {
+          lsum += pv;
+          pdp += pv * dpacc[i];
+        } else {
+          split_bf16(pv * (dpacc[i] - dn), dshi[2 * h2 + (i >> 3)], dslo[2 * h2 + (i >> 3)], i & 7);
+        }
+      }
+    }
+    if (second) {
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const bf16x8 kt = vt_operand<D>(sK, s4, dt, lane);
+          dq[dt] = mfma_bf16(kt, dshi[s4], dq[dt]);
+          dq[dt] = mfma_bf16(kt, dslo[s4], dq[dt]);
+        }
+    }
+    __syncthreads();
+    if (t + 2 < T) issue(t + 2, t & 1);
+  }
+  if (lane < 32) {
+    a.lse_out[row] = valid ? lse2 : 0.0f;
+    a.dn[row] = valid ? dn : 0.0f;
+  }
+  uint16_t *orow = a.dq + base + n * a.stride_n;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d0 = 32 * dt + 8 * q4 + 4 * g;
+      const f32x4 lr = *(const f32x4 *)(a.dqp + row * D + d0);
+      float v[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) v[jj] = valid ? a.scale * dq[dt][4 * q4 + jj] + lr[jj] : 0.0f;
+      *(uint2 *)(orow + d0) = pack_bf16x4(v[0], v[1], v[2], v[3]);
+    }
+  }
+}
+
+// ------------------------------------------------------------ k_bwd_tmap
+// For each key block j of a head: the query blocks that kept it, ascending.
+__global__ __launch_bounds__(256) void k_bwd_tmap(BwdArgs a) {
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  const int bh = blockIdx.y;
+  if (j >= a.nb) return;
+  const int32_t *map = a.map + (int64_t)bh * a.nb * a.kb;
+  int32_t *out = a.tlist + ((int64_t)bh * a.nb + j) * a.nb;
+  int cnt = 0;
+  for (int i = 0; i < a.nb; ++i) {
+    const int32_t *mr = map + (int64_t)i * a.kb;
+    int lo = 0, hi = a.kb;  // first entry >= j
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (mr[mid] < j) lo = mid + 1;
+      else hi = mid;
+    }
+    if (lo < a.kb && mr[lo] == j) out[cnt++] = i;
+  }
+  a.tcount[(int64_t)bh * a.nb + j] = cnt;
+}
+
+// ------------------------------------------------------------- k_bwd_dkv
+// One workgroup (2 waves, 32 keys each) per key block: walks the query blocks
+// that kept it with Q, dO, their log-sum-exp and D rows in a two-slot LDS
+// ring, and accumulates dv^T = dO^T P and dk^T = Q^T dS on MFMA, keys as the
+// lane column (S = Q K^T, dP = dO V^T).  Adds the low-rank parts and writes
+// dk, dv in bf16.
+template <int D>
+__global__ __launch_bounds__(128) void k_bwd_dkv(BwdArgs a) {
+  constexpr int NS = D / 16, DT = D / 32, TILE = 64 * D, OPS = 2 * (64 * (D / 8)) / 128 + 1;
+  constexpr int SLOT = 2 * TILE + 256;  // Q, dO, then 64 lse + 64 D floats
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[2][SLOT];
+  const int tid = threadIdx.x, lane = tid & 63, half = tid >> 6, g = lane >> 5, col = lane & 31;
+  const int kbk = blockIdx.x, bh = blockIdx.y;
+  const int b = bh / a.heads, h = bh % a.heads;
+  const int64_t base = (int64_t)b * a.stride_b + (int64_t)h * a.stride_h;
+  const int64_t n_pad = (int64_t)a.nb * 64;
+  const int64_t m = (int64_t)kbk * 64 + 32 * half + col;
+  const bool valid = m < a.n_tokens;
+  const int64_t mc = valid ? m : a.n_tokens - 1;
+  const int64_t row = (int64_t)bh * n_pad + m;
+  bf16x8 kreg[NS], vreg[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    kreg[s] = *(const bf16x8 *)(a.k + base + mc * a.stride_n + 16 * s + 8 * g);
+    vreg[s] = *(const bf16x8 *)(a.v + base + mc * a.stride_n + 16 * s + 8 * g);
+  }
+  typedef const __attribute__((address_space(4))) int32_t *cint_p;
+  const int cnt = ((cint_p)a.tcount)[(int64_t)bh * a.nb + kbk];
+  const cint_p list = (cint_p)(a.tlist + ((int64_t)bh * a.nb + kbk) * a.nb);
+  wait_vmcnt<0>();
+  auto issue = [&](int t, int slot) __attribute__((always_inline)) {
+    const int i = __builtin_amdgcn_readfirstlane(list[t]);
+    copy_tile64<D>(a.q + base, a.stride_n, (int64_t)i * 64, a.n_tokens - 1, ring[slot], tid);
+    copy_tile64<D>(a.dob + (int64_t)bh * n_pad * D, D, (int64_t)i * 64, n_pad - 1, ring[slot] + TILE, tid);
+    // lse (wave 0) and D (wave 1) of the 64 rows: 16 lanes x 16 bytes each
+    const float *src = (half == 0 ? a.lse_out : a.dn) + (int64_t)bh * n_pad + (int64_t)i * 64;
+    uint16_t *dst = ring[slot] + 2 * TILE + half * 128;
+    if (lane < 16) lds_dma16(src + 4 * lane, dst);
+  };
+  if (cnt > 0) issue(0, 0);
+  if (cnt > 1) issue(1, 1);
+  f32x16 dk[DT], dv[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dk[dt] = dv[dt] = f32x16{};
+  const float c = a.scale_log2e;
+  for (int t = 0; t < cnt; ++t) {
+    if (t + 1 < cnt) wait_vmcnt<OPS>();
+    else wait_vmcnt<0>();
+    __syncthreads();
+    const uint16_t *sQ = ring[t & 1], *sO = ring[t & 1] + TILE;
+    const float *slse = (const float *)(ring[t & 1] + 2 * TILE), *sdn = slse + 64;
+    const int i = __builtin_amdgcn_readfirstlane(list[t]);
+    const int lim = (int)min<int64_t>(64, a.n_tokens - (int64_t)i * 64);  // valid query rows
+    // P and dS as bf16 pairs hi + lo (see k_bwd_dq)
+    bf16x8 phi_[4], plo[4], dshi[4], dslo[4];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      f32x16 sacc = f32x16{}, dpacc = f32x16{};
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        sacc = mfma_bf16(row_operand<D>(sQ, 32 * h2 + col, s, g), kreg[s], sacc);
+        dpacc = mfma_bf16(row_operand<D>(sO, 32 * h2 + col, s, g), vreg[s], dpacc);
+      }
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int r0 = 32 * h2 + 8 * q4 + 4 * g;
+        const f32x4 l4 = *(const f32x4 *)(slse + r0);
+        const f32x4 d4 = *(const f32x4 *)(sdn + r0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int e = 4 * q4 + j;
+          const float pv = (r0 + j < lim) ? fast_exp2(__builtin_fmaf(sacc[e], c, -l4[j])) : 0.0f;
+          split_bf16(pv, phi_[2 * h2 + (e >> 3)], plo[2 * h2 + (e >> 3)], e & 7);
+          split_bf16(pv * (dpacc[e] - d4[j]), dshi[2 * h2 + (e >> 3)], dslo[2 * h2 + (e >> 3)], e & 7);
+        }
+      }
+    }
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const bf16x8 ot = vt_operand<D>(sO, s4, dt, lane), qt = vt_operand<D>(sQ, s4, dt, lane);
+        dv[dt] = mfma_bf16(ot, phi_[s4], dv[dt]);
+        dv[dt] = mfma_bf16(ot, plo[s4], dv[dt]);
+        dk[dt] = mfma_bf16(qt, dshi[s4], dk[dt]);
+        dk[dt] = mfma_bf16(qt, dslo[s4], dk[dt]);
+      }
+    }
+    __syncthreads();
+    if (t + 2 < cnt) issue(t + 2, t & 1);
+  }
+  uint16_t *krow = a.dk + base + m * a.stride_n, *vrow = a.dv + base + m * a.stride_n;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d0 = 32 * dt + 8 * q4 + 4 * g;
+      const f32x4 lk = *(const f32x4 *)(a.dkp + row * D + d0);
+      const f32x4 lv = *(const f32x4 *)(a.dvp + row * D + d0);
+      float vk[4], vv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        vk[j] = valid ? a.scale * dk[dt][4 * q4 + j] + lk[j] : 0.0f;
+        vv[j] = valid ? dv[dt][4 * q4 + j] + lv[j] : 0.0f;
+      }
+      *(uint2 *)(krow + d0) = pack_bf16x4(vk[0], vk[1], vk[2], vk[3]);
+      *(uint2 *)(vrow + d0) = pack_bf16x4(vv[0], vv[1], vv[2], vv[3]);
+    }
+  }
+}
+
+// ------------------------------------------------------------- launchers
+static int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+int bwd_outer_parts(int64_t bh_count, int nb, int mode) {
+  // per head about 256 tiles per workgroup pass for the pooled modes; the
+  // per-head dS reduction uses more workgroups per head
+  (void)mode;
+  const int tiles = 2 * nb;
+  const int want = (int)std::max<int64_t>(1, 2048 / std::max<int64_t>(1, bh_count));
+  return std::max(1, std::min(want, cdiv(tiles, 4)));
+}
+
+void launch_bwd_prep(const BwdArgs &a, int D, hipStream_t st) {
+  const dim3 grid(cdiv(std::max<int64_t>(D * 32, a.bh_count * 32 * D), 256), 2);
+  if (D == 64) hipLaunchKernelGGL(k_bwd_prep<64>, grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(k_bwd_prep<128>, grid, dim3(256), 0, st, a);
+}
+
+void launch_bwd_query(const BwdArgs &a, int D, hipStream_t st) {
+  const dim3 grid(cdiv(2 * a.nb, 4), (unsigned)a.bh_count);
+  const bool gate = a.gate != nullptr, f32 = a.dout_f32 != 0;
+#define ROLA_BQ(DD, GG, FF) hipLaunchKernelGGL((k_bwd_query<DD, GG, FF>), grid, dim3(256), 0, st, a)
+  if (D == 64) {
+    if (gate) { if (f32) ROLA_BQ(64, true, true); else ROLA_BQ(64, true, false); }
+    else { if (f32) ROLA_BQ(64, false, true); else ROLA_BQ(64, false, false); }
+  } else {
+    if (gate) { if (f32) ROLA_BQ(128, true, true); else ROLA_BQ(128, true, false); }
+    else { if (f32) ROLA_BQ(128, false, true); else ROLA_BQ(128, false, false); }
+  }
+#undef ROLA_BQ
+}
+
+template <int D>
+static void bwd_outer_d(const BwdArgs &a, int mode, hipStream_t st) {
+  const int PP = bwd_outer_parts(a.bh_count, a.nb, mode);
+  const dim3 grid(PP, (unsigned)a.bh_count), block(256);
+  const int sg = cdiv(D * 32, 256);
+  switch (mode) {
+    case kOuterRopeQ:
+      hipLaunchKernelGGL((k_bwd_outer<D, kOuterRopeQ>), grid, block, 0, st, a, PP);
+      hipLaunchKernelGGL((k_bwd_sum<D, false, false>), dim3(sg), block, 0, st, a, PP, a.dwq);
+      break;
+    case kOuterRopeK:
+      hipLaunchKernelGGL((k_bwd_outer<D, kOuterRopeK>), grid, block, 0, st, a, PP);
+      hipLaunchKernelGGL((k_bwd_sum<D, false, false>), dim3(sg), block, 0, st, a, PP, a.dwk);
+      break;
+    case kOuterDout:
+      hipLaunchKernelGGL((k_bwd_outer<D, kOuterDout>), grid, block, 0, st, a, PP);
+      hipLaunchKernelGGL((k_bwd_sum<D, true, false>), dim3(sg, (unsigned)a.bh_count), block, 0, st, a, PP,
+                         a.ds32);
+      break;
+    default:
+      // the bias partials (k_bwd_dz, run before dS) sit right after the weight partials
+      hipLaunchKernelGGL((k_bwd_outer<D, kOuterGate>), grid, block, 0, st, a, PP);
+      hipLaunchKernelGGL((k_bwd_sum<D, false, true>), dim3(sg), block, 0, st, a, PP, a.dgate);
+      break;
+  }
+}
+
+void launch_bwd_outer(const BwdArgs &a, int D, int mode, hipStream_t st) {
+  if (D == 64) bwd_outer_d<64>(a, mode, st);
+  else bwd_outer_d<128>(a, mode, st);
+}
+
+void launch_bwd_dsops(const BwdArgs &a, int D, hipStream_t st) {
+  // dz and the per-head gate-bias partials, then the dS operands
+  const int PP = bwd_outer_parts(a.bh_count, a.nb, kOuterGate);
+  const int64_t bias_at = a.bh_count * 4LL * PP * (D * 32);
+  hipLaunchKernelGGL(k_bwd_dz, dim3((unsigned)a.bh_count), dim3(256), 0, st, a, bias_at);
+  const dim3 grid(cdiv(a.bh_count * D * 32, 256));
+  if (D == 64) hipLaunchKernelGGL(k_bwd_dsops<64>, grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(k_bwd_dsops<128>, grid, dim3(256), 0, st, a);
+}
+
+void launch_bwd_key(const BwdArgs &a, int D, hipStream_t st) {
+  const dim3 grid(cdiv(2 * a.nb, 4), (unsigned)a.bh_count);
+  if (D == 64) hipLaunchKernelGGL(k_bwd_key<64>, grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(k_bwd_key<128>, grid, dim3(256), 0, st, a);
+}
+
+void launch_bwd_dq(const BwdArgs &a, int D, hipStream_t st) {
+  const dim3 grid((unsigned)a.nb, (unsigned)a.bh_count);
+  if (D == 64) hipLaunchKernelGGL(k_bwd_dq<64>, grid, dim3(128), 0, st, a);
+  else hipLaunchKernelGGL(k_bwd_dq<128>, grid, dim3(128), 0, st, a);
+}
+
+void launch_bwd_tmap(const BwdArgs &a, hipStream_t st) {
+  hipLaunchKernelGGL(k_bwd_tmap, dim3(cdiv(a.nb, 256), (unsigned)a.bh_count), dim3(256), 0, st, a);
+}
+
+void launch_bwd_dkv(const BwdArgs &a, int D, hipStream_t st) {
+  const dim3 grid((unsigned)a.nb, (unsigned)a.bh_count);
+  if (D == 64) hipLaunchKernelGGL(k_bwd_dkv<64>, grid, dim3(128), 0, st, a);
+  else hipLaunchKernelGGL(k_bwd_dkv<128>, grid, dim3(128), 0, st, a);
+}
+
+}  // namespace rola

@@ -92,6 +92,8 @@ struct AttnArgs {
   const float *z;       // [BH][32]
   const float *gate;    // fp32 [D+1] output gate (w, then b) on the low-rank term; NULL: none
   int complement;       // st and z hold one state per query block ([BH][nb][D][32], [BH][nb][32])
+  float *lse;           // sparse branch alone: if set, base-2 log-sum-exp of each row's scaled
+                        // logits (s * scale * log2 e), [BH][n_pad], for the backward
   RopeArgsHost rope;
   // fp8 sparse branch only
   const uint8_t *kv8;   // tile images, see Quant8Args
@@ -131,5 +133,59 @@ void launch_attn(const AttnArgs &a, int D, bool sparse, bool lowrank, bool accum
 void launch_quant8(const Quant8Args &a, int D, int bh, hipStream_t st);
 void launch_mfma_probe(bool fp8, int iters, int blocks, float *sink, hipStream_t st);
 void launch_attn8(const AttnArgs &a, int D, bool lowrank, bool accum, bool outf32, hipStream_t st);
+
+// ---------------------------------------------------------------- backward
+// Buffers of one rola_backward call.  Token-major work arrays are [BH][n_pad]
+// rows; bf16 arrays hold uint16 bit patterns.
+struct BwdArgs {
+  // inputs (caller layout for q, k, v, dout; strides in elements)
+  const uint16_t *q, *k, *v;
+  const void *dout;  // bf16 or fp32 (dout_f32)
+  int dout_f32;
+  const float *wq, *wk, *gate;
+  int64_t stride_b, stride_h, stride_n;
+  int heads, nb, kb, rank;
+  int64_t n_tokens, bh_count;
+  float scale, scale_log2e;
+  RopeArgsHost rope;
+  const int32_t *map;  // [BH][nb][kb], ascending
+  // state of the forward (from pass 1 and the reduction)
+  const uint16_t *wqT, *wkT;  // bf16 [32][D]
+  const uint16_t *st;         // bf16 [BH][D][32], rank-permuted
+  const float *s32, *z;       // S^T fp32 [BH][D][32], z [BH][32]
+  const float *lse;           // [BH][n_pad], base 2, from the forward
+  float *lse_out;             // [BH][n_pad], renormalised in fp32 by k_bwd_dq
+  // operand copies
+  uint16_t *wqP, *wkP;        // bf16 [D][32], rank-permuted
+  uint16_t *sd;               // bf16 [2][BH][32][D], S with d permuted per 16-group (hi, lo)
+  uint16_t *dsr;              // bf16 [BH][32][D], dS (natural)
+  uint16_t *dst;              // bf16 [BH][D][32], dS^T rank-permuted
+  float *ds32;                // fp32 [BH][D][32], dS^T
+  float *dz;                  // [BH][32]
+  // per-token work arrays
+  uint16_t *dob;              // dO in bf16 [BH][n_pad][D] (0 on padded rows)
+  float *dn;                  // D_n = sum_m P_nm dP_nm [BH][n_pad] (k_bwd_dq)
+  float *dqp, *dkp, *dvp;     // low-rank and gate parts of dq, dk, dv, fp32 [BH][n_pad][D]
+  uint16_t *ahat, *duq, *dwk_tok;  // bf16 [BH][n_pad][32]: g a / den, dL/du (query), dL/dw (key)
+  float *dy, *dg;             // gate: dL/d(q.w + b), dL/dg [BH][n_pad]
+  float *part;                // reduction partials
+  int32_t *tcount, *tlist;    // query blocks keeping each key block: [BH][nb], [BH][nb][nb]
+  // outputs
+  uint16_t *dq, *dk, *dv;     // bf16, caller layout
+  float *dwq, *dwk, *dgate;   // [D][rank], [D][rank], [D+1]
+};
+
+// X^T Y reductions over tokens (dWq, dWk, dS, gate weights)
+enum BwdOuterMode { kOuterRopeQ = 0, kOuterDout = 1, kOuterRopeK = 2, kOuterGate = 3 };
+
+void launch_bwd_prep(const BwdArgs &a, int D, hipStream_t st);   // wqP, wkP, sd
+void launch_bwd_query(const BwdArgs &a, int D, hipStream_t st);  // low-rank and gate, per query token
+void launch_bwd_outer(const BwdArgs &a, int D, int mode, hipStream_t st);
+void launch_bwd_dsops(const BwdArgs &a, int D, hipStream_t st);  // dz, then dS operands
+void launch_bwd_key(const BwdArgs &a, int D, hipStream_t st);    // low-rank, per key token
+void launch_bwd_dq(const BwdArgs &a, int D, hipStream_t st);     // sparse dq (+ the low-rank part)
+void launch_bwd_tmap(const BwdArgs &a, hipStream_t st);
+void launch_bwd_dkv(const BwdArgs &a, int D, hipStream_t st);    // sparse dk, dv (+ low-rank parts)
+int bwd_outer_parts(int64_t bh_count, int nb, int mode);        // partials written per mode
 
 }  // namespace rola

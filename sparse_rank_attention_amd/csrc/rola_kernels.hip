@@ -1396,6 +1396,9 @@ __global__ __launch_bounds__(128 * G) void k_attn(AttnArgs args) {
     const float inv_l = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) oacc[dt] *= inv_l;
+    // the sparse branch alone can leave each row's log-sum-exp for the backward
+    if (!LOWRANK && args.lse && active && lane < 32 && n < args.n_tokens)
+      args.lse[(int64_t)bh * args.nb * 64 + n] = m_run + log2f(l_tot);
   }
   if (!active) return;
   attn_finish<D, LOWRANK, ACCUM, OUTF32>(args, qreg, oacc, n, base, bh, lane, sfreq);

@@ -39,17 +39,18 @@ class RolaConfig(ctypes.Structure):
 
 class RolaPlanInfo(ctypes.Structure):
     _fields_ = [("n_tokens", ctypes.c_int64), ("nb", ctypes.c_int32), ("kb", ctypes.c_int32),
-                ("n_pad", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64)]
+                ("n_pad", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
+                ("workspace_bytes_backward", ctypes.c_int64)]
 
 
 class RolaKernelTime(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_int32), ("total_ms", ctypes.c_double)]
 
 
-ABI_VERSION = 3  # ROLA_ABI_VERSION of include/rola.h
+ABI_VERSION = 4  # ROLA_ABI_VERSION of include/rola.h
 
 EXPORTS = ["rola_abi_version", "rola_status_str", "rola_plan", "rola_select_blocks",
-           "rola_sparse_attn", "rola_lowrank_attn", "rola_forward", "rola_timing_enable",
+           "rola_sparse_attn", "rola_lowrank_attn", "rola_forward", "rola_backward", "rola_timing_enable",
            "rola_timing_read", "rola_mfma_probe"]
 
 _lib = None
@@ -82,6 +83,8 @@ def lib():
         L.rola_lowrank_attn.argtypes = [P, P, P, P, P, P, P, P, P, I32, P, ctypes.c_size_t, P]
         L.rola_forward.restype = I32
         L.rola_forward.argtypes = [P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.rola_backward.restype = I32
+        L.rola_backward.argtypes = [P] * 17 + [ctypes.c_size_t, P]
         L.rola_timing_enable.restype = I32
         L.rola_timing_enable.argtypes = [I32]
         L.rola_timing_read.restype = I32
@@ -245,6 +248,36 @@ def rola_forward(q, k, v, wq, wk, grid, cfg: Config, out=None, block_idx_out=Non
                               _ptr(wk), _ptr(gate), _ptr(block_idx_out), _ptr(out), _ptr(ws), ws.numel(),
                               _stream(stream)), "rola_forward")
     return out
+
+
+def rola_backward(q, k, v, wq, wk, grid, cfg: Config, block_idx, dout, gate=None, stream=None):
+    """Gradients of the forward for dL/dO = dout (the block map held constant).
+
+    Returns (dq, dk, dv, dwq, dwk, dgate): bf16 tensors like q, fp32 [D, rank]
+    tensors, and the fp32 [D+1] gate gradient (None without a gate)."""
+    _check_tokens(q, k, v)
+    _check_gate(gate, q)
+    want = torch.float32 if cfg.out_dtype == ROLA_OUT_F32 else torch.bfloat16
+    if dout.dtype != want or dout.shape != q.shape or dout.stride() != q.stride():
+        raise RolaError("dout must have the output dtype and the layout of q")
+    prob = problem(q, grid)
+    info = plan(prob, cfg)
+    B, H, _, D = q.shape
+    if block_idx.dtype != torch.int32 or tuple(block_idx.shape) != (B, H, info.nb, info.kb) \
+            or not block_idx.is_contiguous():
+        raise RolaError("block_idx must be a contiguous int32 [B, H, nb, kb] map")
+    dq, dk, dv = (torch.empty_strided(q.shape, q.stride(), dtype=torch.bfloat16, device=q.device)
+                  for _ in range(3))
+    dwq = torch.empty((D, cfg.rank), dtype=torch.float32, device=q.device)
+    dwk = torch.empty((D, cfg.rank), dtype=torch.float32, device=q.device)
+    dgate = torch.empty(D + 1, dtype=torch.float32, device=q.device) if gate is not None else None
+    ws = workspace(q.device, info.workspace_bytes_backward)
+    c = cfg.c()
+    _check(lib().rola_backward(ctypes.byref(prob), ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(wq),
+                               _ptr(wk), _ptr(gate), _ptr(block_idx), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                               _ptr(dwq), _ptr(dwk), _ptr(dgate), _ptr(ws), ws.numel(), _stream(stream)),
+           "rola_backward")
+    return dq, dk, dv, dwq, dwk, dgate
 
 
 def mfma_probe(precision: int, iters: int, sink, stream=None) -> float:

@@ -23,7 +23,7 @@ Recipes
   that sigmoid(q . w + b) spreads over (0, 1) for unit-variance queries.
 
 Every (batch, head, tensor) draws from ``numpy.random.default_rng([seed, b, h,
-tid])`` (tid 0=Q, 1=K, 2=V) and the projections from ``default_rng([seed, 100+tid])``
+tid])`` (tid 0=Q, 1=K, 2=V, 6=the output gradient of the backward tests) and the projections from ``default_rng([seed, 100+tid])``
 (tid 3=Wq, 4=Wk, 5=gate), so any head can be regenerated on its own.  Tokens are in
 raster (t, h, w) order; rows from N up to the padded length are zero.
 """
@@ -165,6 +165,17 @@ def make_gate(w: Workload):
     g[:w.head_dim] /= np.sqrt(w.head_dim)
     g[w.head_dim] *= 0.5
     return g.astype(np.float32)
+
+
+def make_dout(w: Workload, f32: bool = False):
+    """Output gradient dL/dO ~ N(0, 1) of shape [B, H, N_pad, D] (rows >= N zero):
+    bf16 bit patterns (uint16), or float32 values when ``f32``."""
+    out = np.zeros((w.batch, w.heads, w.n_pad, w.head_dim), dtype=np.float32)
+    for b in range(w.batch):
+        for h in range(w.heads):
+            rng = np.random.default_rng([w.seed, b, h, 6])
+            out[b, h, :w.n_tokens] = rng.standard_normal((w.n_tokens, w.head_dim))
+    return out if f32 else to_bf16_bits(out)
 
 
 def bf16_bits_to_f32(x: np.ndarray) -> np.ndarray:

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     for name in _declared_functions():
         assert hasattr(L, name), name
     assert set(rola.EXPORTS) == set(_declared_functions())
-    assert L.rola_abi_version() == rola.ABI_VERSION == 3
+    assert L.rola_abi_version() == rola.ABI_VERSION == 4
 
 
 def _prob(B=1, H=40, D=128, grid=(21, 45, 80), sn=None):
@@ -121,6 +121,35 @@ def test_entry_points_validate_before_launch():
     assert L.rola_sparse_attn(P(prob), P(cfg), fake, fake, fake, fake, fake, 2, fake, big, null) == 1
     # status strings
     assert L.rola_status_str(4) == b"workspace missing or too small"
+
+
+def test_backward_validates_before_launch():
+    L = rola.lib()
+    prob = _prob(grid=(4, 16, 16), D=64, H=2)
+    cfg = rola.Config(topk=0.25, rank=16)
+    st, info = _plan(prob, cfg)
+    assert st == 0 and info.workspace_bytes_backward > info.workspace_bytes
+    fake = ctypes.c_void_p(0x10000)
+    odd = ctypes.c_void_p(0x10008)
+    null = ctypes.c_void_p(0)
+    big = info.workspace_bytes_backward
+    ok = [fake] * 5 + [null] + [fake] * 7 + [null]  # q, k, v, wq, wk; gate; block_idx .. dwk; dgate
+
+    def call(c, args, ws_bytes=big):
+        return L.rola_backward(P(prob), P(c.c()), *args, fake, ws_bytes, null)
+
+    args = list(ok)
+    args[0] = null
+    assert call(cfg, args) == 1                               # q missing
+    args = list(ok)
+    args[5] = fake
+    assert call(cfg, args) == 1                               # gate without dgate
+    args = list(ok)
+    args[7] = odd
+    assert call(cfg, args) == 3                               # dout misaligned
+    assert call(cfg, ok, big - 1) == 4                        # workspace too small
+    assert call(rola.Config(topk=0.25, rank=16, precision=rola.ROLA_PREC_FP8), ok) == 2
+    assert call(rola.Config(topk=0.25, rank=16, lowrank_scope=rola.ROLA_LR_COMPLEMENT), ok) == 2
 
 
 def test_mfma_probe_validates_before_launch():

@@ -1,0 +1,85 @@
+"""GPU parity of rola_backward (through the C ABI) against the autograd oracle.
+
+The oracle (oracle/backward.py) differentiates a plain torch fp64 forward that
+is pinned to the C oracle and to finite differences.  Both sides use the same
+block map (the selection is a constant of the backward) and the same seeded
+dL/dO.
+
+Bar, per element: |g - g_ref| <= TOL * rms(g_ref) * (1 + 2^-8) + 2^-8 |g_ref|
+for dq, dk, dv (stored in bf16: half an ulp of the stored value, at most
+2^-8 of it, as for the forward's bf16 output) and <= TOL * rms(g_ref) for the
+fp32 dwq, dwk, dgate; padded rows of dq, dk, dv exactly zero.  TOL = 3e-2:
+the forward's 2e-2 widened for the bf16 operands of the low-rank products
+(R(q), dL/du, dS) whose sums over tokens cancel; the sparse weights P and dS
+enter their products as bf16 pairs (hi + lo) and are normalised in fp32, so
+they add little.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import backward as OB
+from sparse_rank_attention_amd import workloads as W
+from tests.conftest import gpu_available
+from tests.test_gpu_parity import SMALL, dev, host_f64, say, small_workload
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+TOL_BWD = 3e-2
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ratio(got, ref, bf16_store):
+    """max over elements of |got - ref| / bound (<= 1 passes)."""
+    rms = np.sqrt(np.mean(ref ** 2))
+    bound = TOL_BWD * rms
+    if bf16_store:
+        bound = bound * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(ref)
+    return float(np.max(np.abs(got - ref) / bound))
+
+
+CASES = SMALL + [("d128_1280", small_workload((5, 16, 16), D=128, H=2, rank=32, topk=0.25, kind="field", seed=2))]
+
+
+@pytest.mark.parametrize("name,w", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("gated", [False, True], ids=["nogate", "gate"])
+@pytest.mark.parametrize("dout_f32", [False, True], ids=["dobf16", "dof32"])
+def test_backward_matches_oracle(name, w, gated, dout_f32):
+    from sparse_rank_attention_amd import rola
+    torch = _torch()
+    say("backward", name, "gate" if gated else "nogate", "f32" if dout_f32 else "bf16")
+    q, k, v = W.make_qkv(w)
+    wq, wk = W.make_proj(w)
+    g = W.make_gate(w) if gated else None
+    do = W.make_dout(w, f32=dout_f32)
+    cfg = rola.Config(topk=w.topk, rank=w.rank, out_dtype=rola.ROLA_OUT_F32 if dout_f32 else rola.ROLA_OUT_BF16)
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    bmap = rola.rola_select_blocks(qd, kd, w.grid, cfg)
+    dod = torch.from_numpy(do).cuda() if dout_f32 else dev(do)
+    gd = torch.from_numpy(g).cuda() if gated else None
+    dq, dk, dv, dwq, dwk, dgate = rola.rola_backward(qd, kd, vd, torch.from_numpy(wq).cuda(),
+                                                     torch.from_numpy(wk).cuda(), w.grid, cfg, bmap, dod, gate=gd)
+    torch.cuda.synchronize()
+    m_ref = oracle.block_map(q[0], k[0], w.n_tokens, w.kb)
+    np.testing.assert_array_equal(bmap.cpu().numpy()[0], m_ref)
+    f64 = oracle.widen_bf16
+    # an fp32 dout is taken at bf16 precision (the header's contract)
+    do_ref = f64(W.to_bf16_bits(do[0])) if dout_f32 else f64(do[0])
+    ref = OB.backward(f64(q[0]), f64(k[0]), f64(v[0]), wq, wk, m_ref, do_ref, w.n_tokens, w.grid, gate=g)
+    n = w.n_tokens
+    ratios = {}
+    for key, got in (("dq", dq), ("dk", dk), ("dv", dv)):
+        gh = host_f64(got)[0]
+        assert np.all(gh[:, n:] == 0), key
+        ratios[key] = _ratio(gh[:, :n], ref[key][:, :n], True)
+    ratios["dwq"] = _ratio(host_f64(dwq), ref["dwq"], False)
+    ratios["dwk"] = _ratio(host_f64(dwk), ref["dwk"], False)
+    if gated:
+        ratios["dgate"] = _ratio(host_f64(dgate), ref["dgate"], False)
+    say("backward", name, "err/bound", {k_: round(v_, 3) for k_, v_ in ratios.items()})
+    for key, r in ratios.items():
+        assert r <= 1.0, (key, r)

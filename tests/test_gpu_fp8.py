@@ -32,7 +32,7 @@ def bound_ratio8(got, ref, bf16_out):
     rms = np.sqrt(np.mean(ref ** 2))
     bound = TOL_FP8 * rms
     if bf16_out:
-        bound = bound * (1 + 2.0 ** -9) + 2.0 ** -9 * np.abs(ref)
+        bound = bound * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(ref)
     return float(np.max(np.abs(got - ref) / bound))
 
 

@@ -3,9 +3,10 @@
 Bar: block maps and pooled scores bit-exact; outputs within max|O - O_ref| <=
 2e-2 * rms(O_ref) over valid rows; padded rows exactly zero.  When the output
 is stored in bf16, the correctly rounded storage of a result within that bound
-adds up to half a bf16 ulp (2^-9 |O|) per element, so the bound there is
-2e-2 * rms * (1 + 2^-9) + 2^-9 |O_ref| (with max|O|/rms near 10, rounding alone
-reaches 2e-2 * rms).
+adds up to half a bf16 ulp per element, which is at most 2^-8 |O| (8
+significant bits: at the bottom of a binade half an ulp is 2^-8 of the
+value), so the bound there is 2e-2 * rms * (1 + 2^-8) + 2^-8 |O_ref| (with
+max|O|/rms near 10, rounding alone can reach 4e-2 * rms).
 """
 import numpy as np
 import pytest
@@ -44,7 +45,7 @@ def bound_ratio(got, ref, bf16_out):
     rms = np.sqrt(np.mean(ref ** 2))
     bound = TOL_BF16 * rms
     if bf16_out:
-        bound = bound * (1 + 2.0 ** -9) + 2.0 ** -9 * np.abs(ref)
+        bound = bound * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(ref)
     return float(np.max(np.abs(got - ref) / bound))
 
 
