@@ -54,6 +54,8 @@ def parse():
                     help="apply the learned output gate to the low-rank term (seeded synthetic gate)")
     ap.add_argument("--complement", action="store_true",
                     help="low-rank state over each query block's unkept blocks instead of all blocks")
+    ap.add_argument("--backward", action="store_true",
+                    help="time rola_backward (bf16, global scope) instead of the forward; its own JSON line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true", help="skip the MFMA-probe and copy measurements")
     ap.add_argument("--cpu-baseline-child", action="store_true", help=argparse.SUPPRESS)
@@ -136,6 +138,66 @@ def cpu_baseline(args, w):
     }
 
 
+# -------------------------------------------------------------- backward
+def backward_bench(args, w, rola, torch, np, W, qd, kd, vd, wqd, wkd, gd, stream):
+    """rola_backward on the workload: W untimed calls, then K timed ones (HIP events on
+    the stream), with the forward's block map and a seeded N(0, 1) dL/dO in bf16."""
+    cfg = rola.Config(topk=w.topk, rank=w.rank)
+    B, H = w.batch, w.heads
+    bmap = torch.empty((B, H, w.nb, w.kb), dtype=torch.int32, device="cuda")
+    rola.rola_forward(qd, kd, vd, wqd, wkd, w.grid, cfg, block_idx_out=bmap, stream=stream, gate=gd)
+    print("[bench] generating dL/dO", file=sys.stderr, flush=True)
+    dod = torch.from_numpy(W.make_dout(w).view(np.int16)).view(torch.bfloat16).cuda()
+    rola.timing_enable(True)
+    for _ in range(args.warmup):
+        rola.rola_backward(qd, kd, vd, wqd, wkd, w.grid, cfg, bmap, dod, gate=gd, stream=stream)
+    torch.cuda.synchronize()
+    rola.timing_enable(False)
+    rola.timing_read()
+    print("[bench] timing %d backward steps" % args.steps, file=sys.stderr, flush=True)
+    rola.timing_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        rola.rola_backward(qd, kd, vd, wqd, wkd, w.grid, cfg, bmap, dod, gate=gd, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    rola.timing_enable(False)
+    ms = e0.elapsed_time(e1) / args.steps
+    kern_ms = {name: tot / n for name, (n, tot) in rola.timing_read().items()}
+    pairs = w.nb * w.kb * B * H
+    unit = 2.0 * 64 * 64 * w.head_dim  # one 64x64xD product
+    total = 5 * unit * pairs            # S, dP, dV, dQ, dK per kept block pair
+    rec = {
+        "metric": "RoLA bwd ms + kept-block TFLOP/s, Wan-14B-720P shape, topk 0.03",
+        "value": round(total / (ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s (kept-block, whole backward: 5 products of 2*64*64*D flop per kept block pair)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded Wan-shaped smooth field + noise Q/K, N(0,1) V and dL/dO; no weights)",
+        "config": {"workload": w.name, "batch": B, "heads": H, "head_dim": w.head_dim, "grid": list(w.grid),
+                   "n_tokens": w.n_tokens, "topk": w.topk, "kb": w.kb, "nb": w.nb, "rank": w.rank,
+                   "output_gate": bool(args.gate), "pass": "backward"},
+        "bwd_ms": round(ms, 4),
+        "kernel_ms": {k_: round(v_, 4) for k_, v_ in sorted(kern_ms.items())},
+        "cpu_baseline": None,
+    }
+    # the two sparse kernels against the bf16 MFMA peak, on their algorithmic
+    # products (dq: S, dP, dQ; dkv: S, dP, dV, dK)
+    roof = {}
+    for name, prods in (("bwd_dq", 3), ("bwd_dkv", 4)):
+        if name in kern_ms:
+            tf = prods * unit * pairs / (kern_ms[name] * 1e-3) / 1e12
+            roof[name] = {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                          "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    dom = max(roof, key=lambda k_: kern_ms[k_]) if roof else None
+    if dom:
+        rec["roofline"] = dict(kernel=dom, **roof[dom])
+        rec["sparse_rooflines"] = roof
+    print(json.dumps(rec), flush=True)
+
+
 # -------------------------------------------------------------------- main
 def measured_peaks(rola, torch, stream, dtype):
     """Sustained MFMA rate (probe kernel of independent MFMA chains on every
@@ -205,6 +267,12 @@ def main():
     gd = torch.from_numpy(W.make_gate(w)).cuda() if args.gate else None
     cfg = rola.Config(topk=w.topk, rank=w.rank, precision=rola.ROLA_PREC_FP8 if fp8 else rola.ROLA_PREC_BF16,
                       lowrank_scope=rola.ROLA_LR_COMPLEMENT if args.complement else rola.ROLA_LR_GLOBAL)
+    if args.backward:
+        if fp8 or args.complement:
+            print("bench.py --backward: the backward is bf16 with the global low-rank scope", file=sys.stderr)
+            sys.exit(2)
+        backward_bench(args, w, rola, torch, np, W, qd, kd, vd, wqd, wkd, gd, torch.cuda.current_stream())
+        return
     dominant = "attn8_sparse_lowrank" if fp8 else "attn_sparse_lowrank"
     peak = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
     out = torch.empty_like(qd)

@@ -31,7 +31,7 @@
 //   k_bwd_dsops  bf16 operand copies of dS
 //   k_bwd_key    per key token: the low-rank terms of dk, dv and dL/dw'
 //   k_bwd_dq     sparse dq over each query block's kept key blocks
-//   k_bwd_tmap   query blocks that keep each key block
+//   k_bwd_mapbits, k_bwd_tmap  query blocks that keep each key block
 //   k_bwd_dkv    sparse dk, dv over the query blocks keeping each key block
 #include "rola_device.h"
 
@@ -398,34 +398,40 @@ __global__ __launch_bounds__(256) void k_bwd_sum(BwdArgs a, int PP, float *dst) 
 
 // -------------------------------------------------------------- k_bwd_dz
 // Per head: dz[r] = sum_t dden_t a_t[r] = -sum_t dg_t (g a / den)_t[r] and
-// the gate-bias partial sum_t dy_t (into part[bias_at + bh]).
-__global__ __launch_bounds__(256) void k_bwd_dz(BwdArgs a, int64_t bias_at) {
+// the gate-bias partial sum_t dy_t.  First level: workgroup (p, bh) sums the
+// tokens p*per .. (p+1)*per into part[(bh*PZ + p)*33 + (r | 32)]; second
+// level (k_bwd_dz2): per head over p in order, into dz and part[bias_at + bh].
+constexpr int kDzParts = 64;
+__global__ __launch_bounds__(256) void k_bwd_dz(BwdArgs a) {
   __shared__ float red[8][33];
   const int tid = threadIdx.x, r = tid & 31, lane8 = tid >> 5;
-  const int bh = blockIdx.x;
+  const int p = blockIdx.x, bh = blockIdx.y;
   const int64_t n_pad = (int64_t)a.nb * 64, row0 = (int64_t)bh * n_pad;
+  const int64_t per = (a.n_tokens + kDzParts - 1) / kDzParts;
+  const int64_t n0 = p * per, n1 = min<int64_t>(a.n_tokens, n0 + per);
   float acc = 0.0f, yb = 0.0f;
-  for (int64_t n = lane8; n < a.n_tokens; n += 8) {
+  for (int64_t n = n0 + lane8; n < n1; n += 8) {
     acc -= a.dg[row0 + n] * __builtin_bit_cast(float, ((uint32_t)a.ahat[(row0 + n) * 32 + r]) << 16);
     if (r == 0) yb += a.dy[row0 + n];
   }
   red[lane8][r] = acc;
-  red[lane8][32] = 0.0f;
-  __syncthreads();
   if (r == 0) red[lane8][32] = yb;
   __syncthreads();
-  if (tid < 32) {
+  if (tid < 33) {
     float s = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) s += red[i][tid];
-    a.dz[(int64_t)bh * 32 + tid] = tid < a.rank ? s : 0.0f;
-    if (tid == 0) {
-      float t = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) t += red[i][32];
-      a.part[bias_at + bh] = t;
-    }
+    a.part[((int64_t)bh * kDzParts + p) * 33 + tid] = s;
   }
+}
+
+__global__ __launch_bounds__(64) void k_bwd_dz2(BwdArgs a, int64_t bias_at) {
+  const int tid = threadIdx.x, bh = blockIdx.x;
+  if (tid >= 33) return;
+  float s = 0.0f;
+  for (int p = 0; p < kDzParts; ++p) s += a.part[((int64_t)bh * kDzParts + p) * 33 + tid];
+  if (tid < 32) a.dz[(int64_t)bh * 32 + tid] = tid < a.rank ? s : 0.0f;
+  else a.part[bias_at + bh] = s;
 }
 
 // ----------------------------------------------------------- k_bwd_dsops
@@ -669,23 +675,45 @@ __global__ __launch_bounds__(128) void k_bwd_dq(BwdArgs a) {
 
 // ------------------------------------------------------------ k_bwd_tmap
 // For each key block j of a head: the query blocks that kept it, ascending.
+// k_bwd_mapbits turns each map row into a bitset over key blocks; k_bwd_tmap
+// then scans, for its key block, bit j of every row in order (independent
+// loads, shared by the 32 key blocks of a word).
+__global__ __launch_bounds__(64) void k_bwd_mapbits(BwdArgs a) {
+  extern __shared__ uint32_t bits[];
+  const int i = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int W = (a.nb + 31) / 32;
+  for (int w = tid; w < W; w += 64) bits[w] = 0u;
+  __syncthreads();
+  const int32_t *mr = a.map + ((int64_t)bh * a.nb + i) * a.kb;
+  for (int t = tid; t < a.kb; t += 64) {
+    const int j = mr[t];
+    atomicOr(&bits[j >> 5], 1u << (j & 31));
+  }
+  __syncthreads();
+  uint32_t *out = (uint32_t *)a.tbits + ((int64_t)bh * a.nb + i) * W;
+  for (int w = tid; w < W; w += 64) out[w] = bits[w];
+}
+
 __global__ __launch_bounds__(256) void k_bwd_tmap(BwdArgs a) {
   const int j = blockIdx.x * 256 + threadIdx.x;
   const int bh = blockIdx.y;
   if (j >= a.nb) return;
-  const int32_t *map = a.map + (int64_t)bh * a.nb * a.kb;
+  const int W = (a.nb + 31) / 32;
+  const uint32_t *col = (const uint32_t *)a.tbits + (int64_t)bh * a.nb * W + (j >> 5);
+  const uint32_t bit = 1u << (j & 31);
   int32_t *out = a.tlist + ((int64_t)bh * a.nb + j) * a.nb;
   int cnt = 0;
-  for (int i = 0; i < a.nb; ++i) {
-    const int32_t *mr = map + (int64_t)i * a.kb;
-    int lo = 0, hi = a.kb;  // first entry >= j
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (mr[mid] < j) lo = mid + 1;
-      else hi = mid;
-    }
-    if (lo < a.kb && mr[lo] == j) out[cnt++] = i;
+  int i = 0;
+  for (; i + 8 <= a.nb; i += 8) {
+    uint32_t w8[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) w8[u] = col[(int64_t)(i + u) * W];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (w8[u] & bit) out[cnt++] = i + u;
   }
+  for (; i < a.nb; ++i)
+    if (col[(int64_t)i * W] & bit) out[cnt++] = i;
   a.tcount[(int64_t)bh * a.nb + j] = cnt;
 }
 
@@ -868,7 +896,8 @@ void launch_bwd_dsops(const BwdArgs &a, int D, hipStream_t st) {
   // dz and the per-head gate-bias partials, then the dS operands
   const int PP = bwd_outer_parts(a.bh_count, a.nb, kOuterGate);
   const int64_t bias_at = a.bh_count * 4LL * PP * (D * 32);
-  hipLaunchKernelGGL(k_bwd_dz, dim3((unsigned)a.bh_count), dim3(256), 0, st, a, bias_at);
+  hipLaunchKernelGGL(k_bwd_dz, dim3(kDzParts, (unsigned)a.bh_count), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_bwd_dz2, dim3((unsigned)a.bh_count), dim3(64), 0, st, a, bias_at);
   const dim3 grid(cdiv(a.bh_count * D * 32, 256));
   if (D == 64) hipLaunchKernelGGL(k_bwd_dsops<64>, grid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL(k_bwd_dsops<128>, grid, dim3(256), 0, st, a);
@@ -887,6 +916,8 @@ void launch_bwd_dq(const BwdArgs &a, int D, hipStream_t st) {
 }
 
 void launch_bwd_tmap(const BwdArgs &a, hipStream_t st) {
+  const size_t lds = (size_t)((a.nb + 31) / 32) * 4;
+  hipLaunchKernelGGL(k_bwd_mapbits, dim3((unsigned)a.nb, (unsigned)a.bh_count), dim3(64), lds, st, a);
   hipLaunchKernelGGL(k_bwd_tmap, dim3(cdiv(a.nb, 256), (unsigned)a.bh_count), dim3(256), 0, st, a);
 }
 

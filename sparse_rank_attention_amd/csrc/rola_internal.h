@@ -170,6 +170,7 @@ struct BwdArgs {
   float *dy, *dg;             // gate: dL/d(q.w + b), dL/dg [BH][n_pad]
   float *part;                // reduction partials
   int32_t *tcount, *tlist;    // query blocks keeping each key block: [BH][nb], [BH][nb][nb]
+  int32_t *tbits;             // the map as bitsets over key blocks [BH][nb][ceil(nb/32)]
   // outputs
   uint16_t *dq, *dk, *dv;     // bf16, caller layout
   float *dwq, *dwk, *dgate;   // [D][rank], [D][rank], [D+1]
