@@ -36,9 +36,10 @@ def _default_split(d: int):
     return (dt, dh, d - dt - dh)
 
 
-def _rope(x: torch.Tensor, grid, split, theta: float) -> torch.Tensor:
+def _rope(x: torch.Tensor, grid, split, theta: float, inverse: bool = False) -> torch.Tensor:
     """3-D rotary embedding of x [..., n, D]: axis a owns a contiguous run of
-    split[a] dims; its pair p, (x[o+2p], x[o+2p+1]), turns by pos_a * theta^(-2p/split[a])."""
+    split[a] dims; its pair p, (x[o+2p], x[o+2p+1]), turns by pos_a * theta^(-2p/split[a])
+    (by minus that angle, the transpose, when ``inverse``)."""
     n = x.shape[-2]
     idx = torch.arange(n)
     hw = grid[1] * grid[2]
@@ -47,6 +48,8 @@ def _rope(x: torch.Tensor, grid, split, theta: float) -> torch.Tensor:
     for p_axis, dax in zip(pos, split):
         pair = torch.arange(dax // 2, dtype=torch.float64)
         ang = p_axis.double()[:, None] * theta ** (-2.0 * pair / dax)[None, :]
+        if inverse:
+            ang = -ang
         c, s = torch.cos(ang), torch.sin(ang)
         x0, x1 = x[..., o:o + dax:2], x[..., o + 1:o + dax:2]
         parts.append(torch.stack([x0 * c - x1 * s, x0 * s + x1 * c], dim=-1).reshape(*x.shape[:-1], dax))
@@ -111,3 +114,92 @@ def backward(q, k, v, wq, wk, bmap, dout, n_valid: int, grid, split=None, theta=
     grads = torch.autograd.grad(loss, leaves)
     names = ["dq", "dk", "dv", "dwq", "dwk"] + (["dgate"] if tg is not None else [])
     return {n: g.numpy() for n, g in zip(names, grads)}
+
+
+def backward_sampled(q_bits, k_bits, v_bits, wq, wk, bmap, dout_bits, n_valid: int, grid, q_rows, k_rows,
+                     split=None, theta=10000.0, scale=None, gate=None):
+    """The same gradients at full size, for sampled rows, from the gradient
+    formulas written out (no autograd), one head at a time.
+
+    q_bits, k_bits, v_bits, dout_bits: bf16 bit patterns [BH, n_pad, D];
+    q_rows, k_rows: {head: row indices} of the dq and of the dk, dv rows wanted.
+    Returns ({head: dq rows}, {head: dk rows}, {head: dv rows}, dwq, dwk, dgate or None).
+
+    Per head, with the low-rank sums over all N valid tokens:
+      a = phi(R(q) Wq), b = phi(R(k) Wk), S = b^T v, z = sum b, L = a S / (a . z);
+      g = sigmoid(q . w + beta) (1 without a gate); dg = dO . L; dy = dg g (1 - g);
+      dnum = g dO / den, dden = -g dg / den, da = S dnum + z dden, du = da phi'(u);
+      dq_lr = R^T(Wq du) + dy w, dWq = sum R(q) du^T, dS = sum a dnum^T,
+      dz = sum a dden, db = dS v + dz, dv_lr = dS^T b, dw' = db phi'(.),
+      dk_lr = R^T(Wk dw'), dWk = sum R(k) dw'^T;
+    and for the sparse branch of each sampled query row n (its kept keys M):
+      P = softmax(scale q_n . k_M), dP = dO_n . v_M, D = P . dP,
+      dq_n = scale sum (P (dP - D)) k_M;
+    of each sampled key m: the same rows' P and dS for every query row whose
+    block kept m's block, dk_m = scale sum_n dS_nm q_n, dv_m = sum_n P_nm dO_n."""
+    w16 = lambda x: torch.from_numpy((np.asarray(x, dtype=np.uint32) << 16).view(np.float32).astype(np.float64))
+    bh_count, n_pad, d = q_bits.shape
+    split = _default_split(d) if split is None else split
+    scale = d ** -0.5 if scale is None else scale
+    n = n_valid
+    Wq, Wk = torch.tensor(np.asarray(wq, np.float64)), torch.tensor(np.asarray(wk, np.float64))
+    G = None if gate is None else torch.tensor(np.asarray(gate, np.float64))
+    dwq, dwk = torch.zeros_like(Wq), torch.zeros_like(Wk)
+    dgate = torch.zeros(d + 1, dtype=torch.float64) if gate is not None else None
+    dq_out, dk_out, dv_out = {}, {}, {}
+    dphi = lambda u: torch.where(u > 0, torch.ones_like(u), torch.exp(u))
+    for h in range(bh_count):
+        Q, K, V, DO = w16(q_bits[h])[:n], w16(k_bits[h])[:n], w16(v_bits[h])[:n], w16(dout_bits[h])[:n]
+        Rq, Rk = _rope(Q, grid, split, theta), _rope(K, grid, split, theta)
+        u, wv = Rq @ Wq, Rk @ Wk
+        a, b = _phi(u), _phi(wv)
+        S, z = b.T @ V, b.sum(dim=0)
+        den = a @ z
+        L = (a @ S) / den[:, None]
+        g = torch.sigmoid(Q @ G[:d] + G[d]) if G is not None else torch.ones(n, dtype=torch.float64)
+        dg = (DO * L).sum(dim=1)
+        dy = dg * g * (1 - g) if G is not None else torch.zeros(n, dtype=torch.float64)
+        dnum = g[:, None] * DO / den[:, None]
+        dden = -g * dg / den
+        du = (dnum @ S.T + dden[:, None] * z[None, :]) * dphi(u)
+        dq_lr = _rope(du @ Wq.T, grid, split, theta, inverse=True) + dy[:, None] * (G[:d][None, :] if G is not None else 0)
+        dwq += Rq.T @ du
+        dS, dz = a.T @ dnum, (a * dden[:, None]).sum(dim=0)
+        dw_ = (V @ dS.T + dz[None, :]) * dphi(wv)
+        dv_lr, dk_lr = b @ dS, _rope(dw_ @ Wk.T, grid, split, theta, inverse=True)
+        dwk += Rk.T @ dw_
+        if G is not None:
+            dgate[:d] += Q.T @ dy
+            dgate[d] += dy.sum()
+        kept = np.asarray(bmap[h])
+        keys_of = lambda i: torch.cat([torch.arange(j * BLOCK, min(j * BLOCK + BLOCK, n)) for j in sorted(kept[i])])
+
+        def block_rows(i):  # P, dS of query block i over its kept keys
+            rows = torch.arange(i * BLOCK, min(i * BLOCK + BLOCK, n))
+            idx = keys_of(i)
+            P = torch.softmax((Q[rows] @ K[idx].T) * scale, dim=1)
+            dP = DO[rows] @ V[idx].T
+            dS_ = P * (dP - (P * dP).sum(dim=1, keepdim=True))
+            return rows, idx, P, dS_
+
+        out = []
+        for r in q_rows.get(h, []):
+            rows, idx, P, dS_ = block_rows(r // BLOCK)
+            out.append(scale * dS_[r - r // BLOCK * BLOCK] @ K[idx] + dq_lr[r])
+        dq_out[h] = torch.stack(out).numpy() if out else np.zeros((0, d))
+        want = list(k_rows.get(h, []))
+        dk_acc = {m: torch.zeros(d, dtype=torch.float64) for m in want}
+        dv_acc = {m: torch.zeros(d, dtype=torch.float64) for m in want}
+        for i in range(kept.shape[0]):
+            hit = [m for m in want if (m // BLOCK) in set(kept[i].tolist())]
+            if not hit or i * BLOCK >= n:
+                continue
+            rows, idx, P, dS_ = block_rows(i)
+            pos = {int(t): c for c, t in enumerate(idx)}
+            for m in hit:
+                cidx = pos[m]
+                dk_acc[m] += scale * dS_[:, cidx] @ Q[rows]
+                dv_acc[m] += P[:, cidx] @ DO[rows]
+        dk_out[h] = np.stack([(dk_acc[m] + dk_lr[m]).numpy() for m in want]) if want else np.zeros((0, d))
+        dv_out[h] = np.stack([(dv_acc[m] + dv_lr[m]).numpy() for m in want]) if want else np.zeros((0, d))
+    return dq_out, dk_out, dv_out, dwq.numpy(), dwk.numpy(), (dgate.numpy() if dgate is not None else None)

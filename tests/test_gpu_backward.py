@@ -83,3 +83,45 @@ def test_backward_matches_oracle(name, w, gated, dout_f32):
     say("backward", name, "err/bound", {k_: round(v_, 3) for k_, v_ in ratios.items()})
     for key, r in ratios.items():
         assert r <= 1.0, (key, r)
+
+
+def test_backward_full_size_sampled():
+    """The benchmarked backward launch (Wan 14B 720P: 40 heads, N = 75600, 35
+    kept blocks of 1182, bf16 dL/dO) against the written-out gradient formulas
+    (oracle.backward.backward_sampled, pinned to autograd): dq rows of sampled
+    query blocks and dk, dv rows of sampled key blocks in two heads, and the
+    projection gradients, which sum over all heads and tokens."""
+    from sparse_rank_attention_amd import rola
+    from tests.test_gpu_parity import _full_inputs
+    torch = _torch()
+    name = "wan14b_720p"
+    say("backward full size", name)
+    w, (q, k, v), (wq, wk) = _full_inputs(name)
+    do = W.make_dout(w)
+    cfg = rola.Config(topk=w.topk, rank=w.rank)
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    bmap = rola.rola_select_blocks(qd, kd, w.grid, cfg)
+    dq, dk, dv, dwq, dwk, _ = rola.rola_backward(qd, kd, vd, torch.from_numpy(wq).cuda(), torch.from_numpy(wk).cuda(),
+                                                 w.grid, cfg, bmap, dev(do))
+    torch.cuda.synchronize()
+    m_ref = oracle.block_map(q[0], k[0], w.n_tokens, w.kb)
+    np.testing.assert_array_equal(bmap.cpu().numpy()[0], m_ref)
+    rng = np.random.default_rng(17)
+    heads = (1, w.heads - 2)
+    pick = lambda: sorted({n for b in {0, w.nb // 2, w.nb - 1, *rng.integers(0, w.nb, 3).tolist()}
+                           for n in (b * 64, b * 64 + 33, b * 64 + 63) if n < w.n_tokens})
+    q_rows = {h: pick() for h in heads}
+    k_rows = {h: pick() for h in heads}
+    rq, rk, rv, dwq_ref, dwk_ref, _ = OB.backward_sampled(q[0], k[0], v[0], wq, wk, m_ref, do[0], w.n_tokens, w.grid,
+                                                          q_rows, k_rows)
+    ratios = {}
+    for h in heads:
+        for key, got, rows, ref in (("dq", dq, q_rows[h], rq[h]), ("dk", dk, k_rows[h], rk[h]),
+                                    ("dv", dv, k_rows[h], rv[h])):
+            g = got[0, h, torch.tensor(rows, device="cuda")].float().cpu().numpy().astype(np.float64)
+            ratios["%s_h%d" % (key, h)] = _ratio(g, ref, True)
+    ratios["dwq"] = _ratio(host_f64(dwq), dwq_ref, False)
+    ratios["dwk"] = _ratio(host_f64(dwk), dwk_ref, False)
+    say("backward full size", name, "err/bound", {k_: round(v_, 3) for k_, v_ in ratios.items()})
+    for key, r in ratios.items():
+        assert r <= 1.0, (key, r)

@@ -4,6 +4,8 @@ Its torch forward is checked against the C oracle (same outputs), and its
 gradients against central finite differences of the C oracle's own fp64
 branch functions: a directional derivative for Q, K, V and coordinate steps
 for the fp32 projections and gate, in each scope and with and without a gate.
+The written-out gradient formulas used at full size on sampled rows are
+checked against the autograd gradients on every row of a small case.
 """
 import numpy as np
 import pytest
@@ -95,3 +97,25 @@ def test_gradients_match_finite_differences(complement, gated):
         fd = (L(**{name: hi}) - L(**{name: lo})) / (float(hi[idx]) - float(lo[idx]))
         an = grads["dgate" if name == "gate" else "d" + name][idx]
         assert abs(fd - an) <= 1e-5 * max(1.0, abs(an)), (name, idx, fd, an)
+
+
+@pytest.mark.parametrize("gated", [False, True], ids=["nogate", "gate"])
+def test_sampled_formulas_equal_autograd(gated):
+    """The written-out gradient formulas (used at full size on sampled rows)
+    reproduce the autograd gradients on every row of a small case."""
+    c = _case(71 + gated, grid=(3, 7, 11), n_pad=256, d=64, r=16, bh=2, kb=2)
+    g = c["g"] if gated else None
+    dout_bits = to_bf16_bits(c["dout"].astype(np.float32))
+    dout = oracle.widen_bf16(dout_bits)
+    ref = B.backward(c["q"], c["k"], c["v"], c["wq"], c["wk"], c["bmap"], dout, c["n_valid"], c["grid"], gate=g)
+    rows = {h: list(range(c["n_valid"])) for h in range(2)}
+    dq, dk, dv, dwq, dwk, dgate = B.backward_sampled(c["qb"], c["kb"], c["vb"], c["wq"], c["wk"], c["bmap"],
+                                                     dout_bits, c["n_valid"], c["grid"], rows, rows, gate=g)
+    for h in range(2):
+        np.testing.assert_allclose(dq[h], ref["dq"][h, :c["n_valid"]], rtol=1e-9, atol=1e-12)
+        np.testing.assert_allclose(dk[h], ref["dk"][h, :c["n_valid"]], rtol=1e-9, atol=1e-12)
+        np.testing.assert_allclose(dv[h], ref["dv"][h, :c["n_valid"]], rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(dwq, ref["dwq"], rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(dwk, ref["dwk"], rtol=1e-9, atol=1e-12)
+    if gated:
+        np.testing.assert_allclose(dgate, ref["dgate"], rtol=1e-9, atol=1e-12)
