@@ -43,7 +43,7 @@ struct Plan {
   int64_t off_blk, off_s32, off_stc, off_zc;  // complement scope only
   // rola_backward: its buffers follow the forward's (offsets from 0)
   int64_t b_os, b_os_elems, b_lse, b_lse2, b_dob, b_dn, b_dqp, b_dkp, b_dvp, b_ahat, b_duq, b_dwk, b_dy, b_dg,
-      b_wqP, b_wkP, b_sd, b_dsr, b_dst, b_ds32, b_dz, b_s32, b_part, b_tcount, b_tlist, b_tbits, total_bwd;
+      b_wqP, b_wkP, b_sd, b_dsr, b_dst, b_ds32, b_dz, b_s32, b_part, b_tcount, b_tlist, b_tbits, b_sumtmp, total_bwd;
 };
 
 int32_t make_plan(const rola_problem *p, const rola_config *c, Plan *pl) {
@@ -175,6 +175,7 @@ int32_t make_plan(const rola_problem *p, const rola_config *c, Plan *pl) {
   P.b_tcount = take(P.BH * nb * 4);
   P.b_tlist = take(P.BH * nb * (int64_t)nb * 4);
   P.b_tbits = take(P.BH * nb * (int64_t)((nb + 31) / 32) * 4);
+  P.b_sumtmp = take(P.BH * D * 32LL * 4);
   P.total_bwd = o;
   return ROLA_OK;
 }
@@ -578,6 +579,7 @@ int32_t rola_backward(const rola_problem *prob, const rola_config *cfg, const vo
   a.part = (float *)(ws + P.b_part);
   a.tcount = (int32_t *)(ws + P.b_tcount); a.tlist = (int32_t *)(ws + P.b_tlist);
   a.tbits = (int32_t *)(ws + P.b_tbits);
+  a.sumtmp = (float *)(ws + P.b_sumtmp);
   a.dq = (uint16_t *)dq; a.dk = (uint16_t *)dk; a.dv = (uint16_t *)dv;
   a.dwq = dwq; a.dwk = dwk; a.dgate = dgate;
   const int D = P.D;

@@ -26,7 +26,7 @@
 //   k_bwd_query  per query token: the low-rank and gate terms of dq, dL/du,
 //                g a / den and dO in bf16 (MFMA on 32-token tiles)
 //   k_bwd_outer  sums X^T Y over tokens on MFMA (dS, dWq, dWk, gate weights)
-//   k_bwd_sum    fixed-order sums of the partials
+//   k_bwd_sum, k_bwd_sum_heads  fixed-order sums of the partials
 //   k_bwd_dz     dz and the gate bias gradient per head
 //   k_bwd_dsops  bf16 operand copies of dS
 //   k_bwd_key    per key token: the low-rank terms of dk, dv and dL/dw'
@@ -362,17 +362,16 @@ __global__ __launch_bounds__(256) void k_bwd_outer(BwdArgs a, int PP) {
 }
 
 // ------------------------------------------------------------- k_bwd_sum
-// Fixed-order sums of k_bwd_outer's partials.  PER_HEAD: per head over its
-// 4*PP partials (dS^T -> ds32); else over all heads' partials, written as
-// [D][rank] (dWq, dWk) or, for the gate, column 0 as dgate[0..D) plus the
-// per-head bias sums as dgate[D].
-template <int D, bool PER_HEAD, bool GATE>
+// Fixed-order sums of k_bwd_outer's partials, per head over its 4*PP
+// partials, into dst [BH][D*32] (dS^T, or the per-head parts of the pooled
+// gradients).
+template <int D>
 __global__ __launch_bounds__(256) void k_bwd_sum(BwdArgs a, int PP, float *dst) {
   const int idx = blockIdx.x * 256 + threadIdx.x;
   if (idx >= D * 32) return;
-  const int bh0 = PER_HEAD ? blockIdx.y : 0;
-  const int64_t np = PER_HEAD ? 4LL * PP : 4LL * PP * a.bh_count;
-  const float *p = a.part + (int64_t)bh0 * 4 * PP * (D * 32) + idx;
+  const int bh = blockIdx.y;
+  const int64_t np = 4LL * PP;
+  const float *p = a.part + (int64_t)bh * np * (D * 32) + idx;
   float acc8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   int64_t c = 0;
   for (; c + 8 <= np; c += 8) {
@@ -380,15 +379,26 @@ __global__ __launch_bounds__(256) void k_bwd_sum(BwdArgs a, int PP, float *dst) 
     for (int i = 0; i < 8; ++i) acc8[i] += p[(c + i) * (D * 32)];
   }
   for (int i = 0; c + i < np; ++i) acc8[i] += p[(c + i) * (D * 32)];
-  const float acc = ((acc8[0] + acc8[1]) + (acc8[2] + acc8[3])) + ((acc8[4] + acc8[5]) + (acc8[6] + acc8[7]));
+  dst[(int64_t)bh * D * 32 + idx] =
+      ((acc8[0] + acc8[1]) + (acc8[2] + acc8[3])) + ((acc8[4] + acc8[5]) + (acc8[6] + acc8[7]));
+}
+
+// The pooled gradients: the per-head sums of k_bwd_sum added over heads in
+// order, written as [D][rank] (dWq, dWk) or, for the gate, column 0 as
+// dgate[0..D) plus the per-head bias sums (at part[bias_at ...]) as dgate[D].
+template <int D, bool GATE>
+__global__ __launch_bounds__(256) void k_bwd_sum_heads(BwdArgs a, const float *heads, int64_t bias_at,
+                                                       float *dst) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= D * 32) return;
+  float acc = 0.0f;
+  for (int64_t h = 0; h < a.bh_count; ++h) acc += heads[h * D * 32 + idx];
   const int d = idx / 32, r = idx % 32;
-  if (PER_HEAD) {
-    dst[(int64_t)bh0 * D * 32 + idx] = acc;
-  } else if (GATE) {
+  if (GATE) {
     if (r == 0) dst[d] = acc;
     if (idx == 0) {
       float bsum = 0.0f;
-      for (int64_t i = 0; i < a.bh_count; ++i) bsum += a.part[a.bh_count * 4 * PP * (D * 32) + i];
+      for (int64_t i = 0; i < a.bh_count; ++i) bsum += a.part[bias_at + i];
       dst[D] = bsum;
     }
   } else if (r < a.rank) {
@@ -864,25 +874,28 @@ template <int D>
 static void bwd_outer_d(const BwdArgs &a, int mode, hipStream_t st) {
   const int PP = bwd_outer_parts(a.bh_count, a.nb, mode);
   const dim3 grid(PP, (unsigned)a.bh_count), block(256);
-  const int sg = cdiv(D * 32, 256);
+  const dim3 gsum(cdiv(D * 32, 256), (unsigned)a.bh_count), gfin(cdiv(D * 32, 256));
+  // the gate-bias partials (k_bwd_dz, run before dS) sit right after the weight partials
+  const int64_t bias_at = a.bh_count * 4LL * PP * (D * 32);
   switch (mode) {
     case kOuterRopeQ:
       hipLaunchKernelGGL((k_bwd_outer<D, kOuterRopeQ>), grid, block, 0, st, a, PP);
-      hipLaunchKernelGGL((k_bwd_sum<D, false, false>), dim3(sg), block, 0, st, a, PP, a.dwq);
+      hipLaunchKernelGGL((k_bwd_sum<D>), gsum, block, 0, st, a, PP, a.sumtmp);
+      hipLaunchKernelGGL((k_bwd_sum_heads<D, false>), gfin, block, 0, st, a, a.sumtmp, bias_at, a.dwq);
       break;
     case kOuterRopeK:
       hipLaunchKernelGGL((k_bwd_outer<D, kOuterRopeK>), grid, block, 0, st, a, PP);
-      hipLaunchKernelGGL((k_bwd_sum<D, false, false>), dim3(sg), block, 0, st, a, PP, a.dwk);
+      hipLaunchKernelGGL((k_bwd_sum<D>), gsum, block, 0, st, a, PP, a.sumtmp);
+      hipLaunchKernelGGL((k_bwd_sum_heads<D, false>), gfin, block, 0, st, a, a.sumtmp, bias_at, a.dwk);
       break;
     case kOuterDout:
       hipLaunchKernelGGL((k_bwd_outer<D, kOuterDout>), grid, block, 0, st, a, PP);
-      hipLaunchKernelGGL((k_bwd_sum<D, true, false>), dim3(sg, (unsigned)a.bh_count), block, 0, st, a, PP,
-                         a.ds32);
+      hipLaunchKernelGGL((k_bwd_sum<D>), gsum, block, 0, st, a, PP, a.ds32);
       break;
     default:
-      // the bias partials (k_bwd_dz, run before dS) sit right after the weight partials
       hipLaunchKernelGGL((k_bwd_outer<D, kOuterGate>), grid, block, 0, st, a, PP);
-      hipLaunchKernelGGL((k_bwd_sum<D, false, true>), dim3(sg), block, 0, st, a, PP, a.dgate);
+      hipLaunchKernelGGL((k_bwd_sum<D>), gsum, block, 0, st, a, PP, a.sumtmp);
+      hipLaunchKernelGGL((k_bwd_sum_heads<D, true>), gfin, block, 0, st, a, a.sumtmp, bias_at, a.dgate);
       break;
   }
 }

@@ -169,6 +169,7 @@ struct BwdArgs {
   uint16_t *ahat, *duq, *dwk_tok;  // bf16 [BH][n_pad][32]: g a / den, dL/du (query), dL/dw (key)
   float *dy, *dg;             // gate: dL/d(q.w + b), dL/dg [BH][n_pad]
   float *part;                // reduction partials
+  float *sumtmp;              // per-head sums of the pooled gradients [BH][D][32]
   int32_t *tcount, *tlist;    // query blocks keeping each key block: [BH][nb], [BH][nb][nb]
   int32_t *tbits;             // the map as bitsets over key blocks [BH][nb][ceil(nb/32)]
   // outputs
