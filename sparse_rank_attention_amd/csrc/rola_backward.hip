@@ -780,8 +780,9 @@ __global__ __launch_bounds__(128) void k_bwd_dkv(BwdArgs a) {
     const float *slse = (const float *)(ring[t & 1] + 2 * TILE), *sdn = slse + 64;
     const int i = __builtin_amdgcn_readfirstlane(list[t]);
     const int lim = (int)min<int64_t>(64, a.n_tokens - (int64_t)i * 64);  // valid query rows
-    // P and dS as bf16 pairs hi + lo (see k_bwd_dq)
-    bf16x8 phi_[4], plo[4], dshi[4], dslo[4];
+    // P and dS in bf16: the sums over query rows here do not cancel the way
+    // dS does over keys (k_bwd_dq), so one rounding suffices
+    bf16x8 pop[4], dsop[4];
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
       f32x16 sacc = f32x16{}, dpacc = f32x16{};
@@ -799,8 +800,8 @@ __global__ __launch_bounds__(128) void k_bwd_dkv(BwdArgs a) {
         for (int j = 0; j < 4; ++j) {
           const int e = 4 * q4 + j;
           const float pv = (r0 + j < lim) ? fast_exp2(__builtin_fmaf(sacc[e], c, -l4[j])) : 0.0f;
-          split_bf16(pv, phi_[2 * h2 + (e >> 3)], plo[2 * h2 + (e >> 3)], e & 7);
-          split_bf16(pv * (dpacc[e] - d4[j]), dshi[2 * h2 + (e >> 3)], dslo[2 * h2 + (e >> 3)], e & 7);
+          pop[2 * h2 + (e >> 3)][e & 7] = (__bf16)pv;
+          dsop[2 * h2 + (e >> 3)][e & 7] = (__bf16)(pv * (dpacc[e] - d4[j]));
         }
       }
     }
@@ -809,10 +810,8 @@ __global__ __launch_bounds__(128) void k_bwd_dkv(BwdArgs a) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const bf16x8 ot = vt_operand<D>(sO, s4, dt, lane), qt = vt_operand<D>(sQ, s4, dt, lane);
-        dv[dt] = mfma_bf16(ot, phi_[s4], dv[dt]);
-        dv[dt] = mfma_bf16(ot, plo[s4], dv[dt]);
-        dk[dt] = mfma_bf16(qt, dshi[s4], dk[dt]);
-        dk[dt] = mfma_bf16(qt, dslo[s4], dk[dt]);
+        dv[dt] = mfma_bf16(ot, pop[s4], dv[dt]);
+        dk[dt] = mfma_bf16(qt, dsop[s4], dk[dt]);
       }
     }
     __syncthreads();

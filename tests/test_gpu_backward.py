@@ -9,10 +9,10 @@ Bar, per element: |g - g_ref| <= TOL * rms(g_ref) * (1 + 2^-8) + 2^-8 |g_ref|
 for dq, dk, dv (stored in bf16: half an ulp of the stored value, at most
 2^-8 of it, as for the forward's bf16 output) and <= TOL * rms(g_ref) for the
 fp32 dwq, dwk, dgate; padded rows of dq, dk, dv exactly zero.  TOL = 3e-2:
-the forward's 2e-2 widened for the bf16 operands of the low-rank products
-(R(q), dL/du, dS) whose sums over tokens cancel; the sparse weights P and dS
-enter their products as bf16 pairs (hi + lo) and are normalised in fp32, so
-they add little.
+the forward's 2e-2 widened for the bf16 operands of the backward's products
+(the weights P and dS in the dk, dv products; R(q), dL/du and dS in the
+low-rank sums over tokens); in dq, whose dS terms cancel over the keys, dS
+enters as a bf16 pair (hi + lo), and the weights are renormalised in fp32.
 """
 import numpy as np
 import pytest
