@@ -42,7 +42,7 @@ struct Plan {
   bool comp;  // complement scope of the low-rank branch
   int64_t off_blk, off_s32, off_stc, off_zc;  // complement scope only
   // rola_backward: its buffers follow the forward's (offsets from 0)
-  int64_t b_os, b_os_elems, b_lse, b_lse2, b_dob, b_dn, b_dqp, b_dkp, b_dvp, b_ahat, b_duq, b_dwk, b_dy, b_dg,
+  int64_t b_os, b_os_elems, b_lse, b_dob, b_dn, b_dqp, b_dkp, b_dvp, b_ahat, b_duq, b_dwk, b_dy, b_dg,
       b_wqP, b_wkP, b_sd, b_dsr, b_dst, b_ds32, b_dz, b_s32, b_part, b_tcount, b_tlist, b_tbits, b_sumtmp, total_bwd;
 };
 
@@ -150,9 +150,8 @@ int32_t make_plan(const rola_problem *p, const rola_config *c, Plan *pl) {
     o = align_up(o + bytes);
     return at;
   };
-  P.b_os = take(P.b_os_elems * 2);
+  P.b_os = take(P.b_os_elems * 4);
   P.b_lse = take(tok * 4);
-  P.b_lse2 = take(tok * 4);
   P.b_dob = take(tok * D * 2);
   P.b_dn = take(tok * 4);
   P.b_dqp = take(tok * D * 4);
@@ -545,11 +544,11 @@ int32_t rola_backward(const rola_problem *prob, const rola_config *cfg, const vo
                               (uint16_t *)(ws + P.off_st), (float *)(ws + P.off_z),
                               (float *)(ws + P.b_s32), st);
   }));
-  // the sparse branch alone again, for each row's log-sum-exp (its output O_s
-  // goes to a scratch buffer with the problem's strides and is not used)
-  rola_config c16 = *cfg;
-  c16.out_dtype = ROLA_OUT_BF16;
-  ROLA_TRY(run_attn(P, prob, &c16, q, k, v, block_idx, nullptr, ws + P.b_os, ws, true, false, false, st,
+  // the sparse branch alone again with fp32 weights: O_s (fp32, the
+  // problem's strides) and each row's log-sum-exp
+  rola_config c32 = *cfg;
+  c32.out_dtype = ROLA_OUT_F32;
+  ROLA_TRY(run_attn(P, prob, &c32, q, k, v, block_idx, nullptr, ws + P.b_os, ws, true, false, false, st,
                     (float *)(ws + P.b_lse)));
 
   rola::BwdArgs a;
@@ -566,8 +565,7 @@ int32_t rola_backward(const rola_problem *prob, const rola_config *cfg, const vo
   a.wqT = (const uint16_t *)(ws + P.off_wqT); a.wkT = (const uint16_t *)(ws + P.off_wkT);
   a.st = (const uint16_t *)(ws + P.off_st);
   a.s32 = (const float *)(ws + P.b_s32); a.z = (const float *)(ws + P.off_z);
-  a.lse = (const float *)(ws + P.b_lse);
-  a.lse_out = (float *)(ws + P.b_lse2);
+  a.os = (const float *)(ws + P.b_os); a.lse = (const float *)(ws + P.b_lse);
   a.wqP = (uint16_t *)(ws + P.b_wqP); a.wkP = (uint16_t *)(ws + P.b_wkP);
   a.sd = (uint16_t *)(ws + P.b_sd); a.dsr = (uint16_t *)(ws + P.b_dsr); a.dst = (uint16_t *)(ws + P.b_dst);
   a.ds32 = (float *)(ws + P.b_ds32); a.dz = (float *)(ws + P.b_dz);

@@ -10,7 +10,7 @@
 // top-k selection is piecewise constant in Q and K.
 //
 // Per (batch, head), with c = scale and L = O_lr:
-//   sparse:   P = exp2(c log2e q.k - lse2), D_n = sum_m P_nm dP_nm,
+//   sparse:   P = exp2(c log2e q.k - lse2), D_n = dO_n . O_s,n,
 //             dS = P (dO.v - D), dq = c dS k, dk = c dS^T q, dv = P^T dO
 //   low rank: a = phi(u), u = Wq^T R(q); num = S^T a, den = a.z, L = num/den;
 //             with the gate g = sigmoid(y), y = q.w + b:
@@ -21,10 +21,13 @@
 //             dk += R^T(Wk dw'), dWk = sum R(k) dw'^T, dw = sum dy q, db_gate = sum dy.
 //
 // Kernels, in launch order (after pass 1's state and a sparse-only forward
-// that leaves O_s and the row log-sum-exp):
+// with fp32 weights that leaves O_s and the row log-sum-exp, consistent with
+// each other to about 16 bits, so that the P of the backward sums to one and
+// D = dO . O_s = sum P dP -- with bf16 weights the sum of dS over a row's keys
+// would not vanish and the error would show in dq):
 //   k_bwd_prep   bf16 operand copies: Wq, Wk rank-permuted, S with d permuted
 //   k_bwd_query  per query token: the low-rank and gate terms of dq, dL/du,
-//                g a / den and dO in bf16 (MFMA on 32-token tiles)
+//                g a / den, dO in bf16 and D_n = dO . O_s (MFMA on 32-token tiles)
 //   k_bwd_outer  sums X^T Y over tokens on MFMA (dS, dWq, dWk, gate weights)
 //   k_bwd_sum, k_bwd_sum_heads  fixed-order sums of the partials
 //   k_bwd_dz     dz and the gate bias gradient per head
@@ -173,7 +176,7 @@ __global__ __launch_bounds__(256) void k_bwd_query(BwdArgs a) {
   }
   // dO and O_s at the lane's dims d = 32 dt + 8 q4 + 4 g + j; D_n and dg
   f32x16 dov[DT];
-  float dg_p = 0.0f;
+  float dn_p = 0.0f, dg_p = 0.0f;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
@@ -190,14 +193,17 @@ __global__ __launch_bounds__(256) void k_bwd_query(BwdArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) dv4[j] = valid ? dv4[j] : 0.0f;
       }
+      const f32x4 o4 = *(const f32x4 *)(a.os + base + n * a.stride_n + d0);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         dov[dt][4 * q4 + j] = dv4[j];
+        dn_p += dv4[j] * o4[j];
         dg_p += dv4[j] * (num[dt][4 * q4 + j] * inv_den);
       }
       *(uint2 *)(a.dob + row * D + d0) = pack_bf16x4(dv4[0], dv4[1], dv4[2], dv4[3]);
     }
   }
+  const float dn = dn_p + shfl_xor32(dn_p);
   const float dg = dg_p + shfl_xor32(dg_p);
   const float gv = GATE ? 1.0f / (1.0f + __expf(-y)) : 1.0f;
   const float dy = GATE ? dg * gv * (1.0f - gv) : 0.0f;
@@ -264,6 +270,7 @@ __global__ __launch_bounds__(256) void k_bwd_query(BwdArgs a) {
     *(uint2 *)(a.duq + row * 32 + r0) = pack_bf16x4(du[4 * q4], du[4 * q4 + 1], du[4 * q4 + 2], du[4 * q4 + 3]);
   }
   if (lane < 32) {
+    a.dn[row] = valid ? dn : 0.0f;
     a.dg[row] = valid ? dg : 0.0f;
     a.dy[row] = valid ? dy : 0.0f;
   }
@@ -568,15 +575,11 @@ static __device__ __forceinline__ bf16x8 row_operand(const uint16_t *tile, int r
 
 // -------------------------------------------------------------- k_bwd_dq
 // One workgroup (2 waves, 32 queries each) per query block, with K and V
-// tiles of its kept key blocks in a two-slot LDS ring, walked twice:
-//  pass 0: S^T = K Q^T and dP^T = V dO^T give, with the forward's log-sum-
-//          exp, the fp32 row sums l = sum P and sum P dP; then lse2 += log2 l
-//          and D = sum P dP / l, so that the weights P used below sum to one
-//          and D = sum P dP exactly for them (the forward normalised with its
-//          bf16 weights; a D from its O would leave sum dS != 0);
-//  pass 1: dS^T = P^T (dP^T - D), dq^T += K^T dS^T on MFMA.
-// Writes the corrected lse2 and D for k_bwd_dkv, adds the low-rank part and
-// writes dq in bf16.
+// tiles of its kept key blocks in a two-slot LDS ring: S^T = K Q^T and
+// dP^T = V dO^T as in the forward's transposed form, dS^T = P^T (dP^T - D),
+// dq^T += K^T dS^T on MFMA.  dS enters as a bf16 pair hi + lo (about 16
+// significant bits): its terms cancel in the sum over keys.  Adds the
+// low-rank part and writes dq in bf16.
 template <int D>
 __global__ __launch_bounds__(128) void k_bwd_dq(BwdArgs a) {
   constexpr int NS = D / 16, DT = D / 32, TILE = 64 * D, OPS = 2 * (64 * (D / 8)) / 128;
@@ -596,40 +599,31 @@ __global__ __launch_bounds__(128) void k_bwd_dq(BwdArgs a) {
     qreg[s] = *(const bf16x8 *)(a.q + base + nc * a.stride_n + 16 * s + 8 * g);
     doreg[s] = *(const bf16x8 *)(a.dob + row * D + 16 * s + 8 * g);
   }
-  float lse2 = valid ? a.lse[row] : 0.0f;
+  const float lse2 = valid ? a.lse[row] : 0.0f;
+  const float dn = a.dn[row];
   // the block map through the scalar cache (uniform per workgroup)
   typedef const __attribute__((address_space(4))) int32_t *cint_p;
   const cint_p mrow = (cint_p)(a.map + ((int64_t)bh * a.nb + qb) * a.kb);
-  const int kb = a.kb, T = 2 * kb;  // tile t walks entry t mod kb, pass t / kb
+  const int kb = a.kb;
   wait_vmcnt<0>();
   auto issue = [&](int t, int slot) __attribute__((always_inline)) {
-    const int j = __builtin_amdgcn_readfirstlane(mrow[t < kb ? t : t - kb]);
+    const int j = __builtin_amdgcn_readfirstlane(mrow[t]);
     copy_tile64<D>(a.k + base, a.stride_n, (int64_t)j * 64, a.n_tokens - 1, ring[slot], tid);
     copy_tile64<D>(a.v + base, a.stride_n, (int64_t)j * 64, a.n_tokens - 1, ring[slot] + TILE, tid);
   };
   issue(0, 0);
-  issue(1, 1);
+  if (kb > 1) issue(1, 1);
   f32x16 dq[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) dq[dt] = f32x16{};
   const float c = a.scale_log2e;
-  float lsum = 0.0f, pdp = 0.0f, dn = 0.0f;
-  for (int t = 0; t < T; ++t) {
-    if (t + 1 < T) wait_vmcnt<OPS>();
+  for (int t = 0; t < kb; ++t) {
+    if (t + 1 < kb) wait_vmcnt<OPS>();
     else wait_vmcnt<0>();
     __syncthreads();
-    const bool second = t >= kb;
-    if (t == kb) {
-      // pass 0 done: normalise the weights and form D
-      const float l = pair_sum32(lsum);
-      dn = l > 0.0f ? pair_sum32(pdp) / l : 0.0f;
-      lse2 += l > 0.0f ? log2f(l) : 0.0f;
-    }
     const uint16_t *sK = ring[t & 1], *sV = ring[t & 1] + TILE;
-    const int j = __builtin_amdgcn_readfirstlane(mrow[second ? t - kb : t]);
+    const int j = __builtin_amdgcn_readfirstlane(mrow[t]);
     const int lim = (int)min<int64_t>(64, a.n_tokens - (int64_t)j * 64);  // valid keys of the block
-    // dS as a bf16 pair hi + lo (about 16 significant bits): its terms cancel
-    // in the sum over keys
     bf16x8 dshi[4], dslo[4];
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
@@ -643,30 +637,19 @@ __global__ __launch_bounds__(128) void k_bwd_dq(BwdArgs a) {
       for (int i = 0; i < 16; ++i) {
         const int key = 32 * h2 + 8 * (i >> 2) + 4 * g + (i & 3);
         const float pv = (valid && key < lim) ? fast_exp2(__builtin_fmaf(sacc[i], c, -lse2)) : 0.0f;
-        if (!second) {
-          lsum += pv;
-          pdp += pv * dpacc[i];
-        } else {
-          split_bf16(pv * (dpacc[i] - dn), dshi[2 * h2 + (i >> 3)], dslo[2 * h2 + (i >> 3)], i & 7);
-        }
+        split_bf16(pv * (dpacc[i] - dn), dshi[2 * h2 + (i >> 3)], dslo[2 * h2 + (i >> 3)], i & 7);
       }
     }
-    if (second) {
 #pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4)
+    for (int s4 = 0; s4 < 4; ++s4)
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const bf16x8 kt = vt_operand<D>(sK, s4, dt, lane);
-          dq[dt] = mfma_bf16(kt, dshi[s4], dq[dt]);
-          dq[dt] = mfma_bf16(kt, dslo[s4], dq[dt]);
-        }
-    }
+      for (int dt = 0; dt < DT; ++dt) {
+        const bf16x8 kt = vt_operand<D>(sK, s4, dt, lane);
+        dq[dt] = mfma_bf16(kt, dshi[s4], dq[dt]);
+        dq[dt] = mfma_bf16(kt, dslo[s4], dq[dt]);
+      }
     __syncthreads();
-    if (t + 2 < T) issue(t + 2, t & 1);
-  }
-  if (lane < 32) {
-    a.lse_out[row] = valid ? lse2 : 0.0f;
-    a.dn[row] = valid ? dn : 0.0f;
+    if (t + 2 < kb) issue(t + 2, t & 1);
   }
   uint16_t *orow = a.dq + base + n * a.stride_n;
 #pragma unroll
@@ -762,7 +745,7 @@ __global__ __launch_bounds__(128) void k_bwd_dkv(BwdArgs a) {
     copy_tile64<D>(a.q + base, a.stride_n, (int64_t)i * 64, a.n_tokens - 1, ring[slot], tid);
     copy_tile64<D>(a.dob + (int64_t)bh * n_pad * D, D, (int64_t)i * 64, n_pad - 1, ring[slot] + TILE, tid);
     // lse (wave 0) and D (wave 1) of the 64 rows: 16 lanes x 16 bytes each
-    const float *src = (half == 0 ? a.lse_out : a.dn) + (int64_t)bh * n_pad + (int64_t)i * 64;
+    const float *src = (half == 0 ? a.lse : a.dn) + (int64_t)bh * n_pad + (int64_t)i * 64;
     uint16_t *dst = ring[slot] + 2 * TILE + half * 128;
     if (lane < 16) lds_dma16(src + 4 * lane, dst);
   };

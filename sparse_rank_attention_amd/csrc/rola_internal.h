@@ -92,8 +92,9 @@ struct AttnArgs {
   const float *z;       // [BH][32]
   const float *gate;    // fp32 [D+1] output gate (w, then b) on the low-rank term; NULL: none
   int complement;       // st and z hold one state per query block ([BH][nb][D][32], [BH][nb][32])
-  float *lse;           // sparse branch alone: if set, base-2 log-sum-exp of each row's scaled
-                        // logits (s * scale * log2 e), [BH][n_pad], for the backward
+  float *lse;           // sparse branch alone with fp32 output: if set, the backward's
+                        // recompute -- fp32 weights, and the base-2 log-sum-exp of each
+                        // row's scaled logits (s * scale * log2 e), [BH][n_pad]
   RopeArgsHost rope;
   // fp8 sparse branch only
   const uint8_t *kv8;   // tile images, see Quant8Args
@@ -153,8 +154,8 @@ struct BwdArgs {
   const uint16_t *wqT, *wkT;  // bf16 [32][D]
   const uint16_t *st;         // bf16 [BH][D][32], rank-permuted
   const float *s32, *z;       // S^T fp32 [BH][D][32], z [BH][32]
-  const float *lse;           // [BH][n_pad], base 2, from the forward
-  float *lse_out;             // [BH][n_pad], renormalised in fp32 by k_bwd_dq
+  const float *os;            // recomputed sparse output, fp32, the problem's strides
+  const float *lse;           // [BH][n_pad], base 2, from the recompute
   // operand copies
   uint16_t *wqP, *wkP;        // bf16 [D][32], rank-permuted
   uint16_t *sd;               // bf16 [2][BH][32][D], S with d permuted per 16-group (hi, lo)
@@ -164,7 +165,7 @@ struct BwdArgs {
   float *dz;                  // [BH][32]
   // per-token work arrays
   uint16_t *dob;              // dO in bf16 [BH][n_pad][D] (0 on padded rows)
-  float *dn;                  // D_n = sum_m P_nm dP_nm [BH][n_pad] (k_bwd_dq)
+  float *dn;                  // D_n = dO_n . O_s,n [BH][n_pad]
   float *dqp, *dkp, *dvp;     // low-rank and gate parts of dq, dk, dv, fp32 [BH][n_pad][D]
   uint16_t *ahat, *duq, *dwk_tok;  // bf16 [BH][n_pad][32]: g a / den, dL/du (query), dL/dw (key)
   float *dy, *dg;             // gate: dL/d(q.w + b), dL/dg [BH][n_pad]

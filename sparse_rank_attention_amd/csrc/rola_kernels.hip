@@ -1130,7 +1130,10 @@ static __device__ __forceinline__ void attn_finish(const AttnArgs &args, const b
 // the block runs S^T = K Q^T, the online softmax and O^T += V^T P^T on it.
 // Workgroups are mapped so that all XCDs work on the same head at a time and
 // each XCD takes a contiguous run of similar groups (shared L2 lines).
-template <int D, int G, int S, bool SPARSE, bool LOWRANK, bool ACCUM, bool OUTF32>
+// EXACT (the backward's recompute of the sparse branch): the row sums add the
+// fp32 weights and each weight enters the PV product as a bf16 pair hi + lo,
+// so that O and the log-sum-exp agree with fp32 weights to about 16 bits.
+template <int D, int G, int S, bool SPARSE, bool LOWRANK, bool ACCUM, bool OUTF32, bool EXACT = false>
 __global__ __launch_bounds__(128 * G) void k_attn(AttnArgs args) {
   constexpr int CH = D / 8;
   constexpr int NS = D / 16;  // k-steps over head_dim
@@ -1370,13 +1373,23 @@ __global__ __launch_bounds__(128 * G) void k_attn(AttnArgs args) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           const f32x16 &src = (s < 2) ? sacc0 : sacc1;
-          bf16x8 pw;
+          bf16x8 pw, plo;
+          if constexpr (EXACT) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) pw[e] = (__bf16)fast_exp2(__builtin_fmaf(src[8 * (s & 1) + e], c, negm));
+            for (int e = 0; e < 8; ++e) {
+              const float wv = fast_exp2(__builtin_fmaf(src[8 * (s & 1) + e], c, negm));
+              pw[e] = (__bf16)wv;
+              plo[e] = (__bf16)(wv - (float)pw[e]);
+              psum += wv;
+            }
+          } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const bf16x2 pr = {pw[2 * e], pw[2 * e + 1]};
-            psum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, psum, false);
+            for (int e = 0; e < 8; ++e) pw[e] = (__bf16)fast_exp2(__builtin_fmaf(src[8 * (s & 1) + e], c, negm));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const bf16x2 pr = {pw[2 * e], pw[2 * e + 1]};
+              psum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, psum, false);
+            }
           }
           // the step's V^T operands (2*DT transposing reads) before its MFMAs
           bf16x8 va[DT];
@@ -1384,7 +1397,10 @@ __global__ __launch_bounds__(128 * G) void k_attn(AttnArgs args) {
           for (int dt = 0; dt < DT; ++dt) va[dt] = vt_operand_at(sV + voff[dt] + s * 16 * D, 8 * D);
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt) oacc[dt] = mfma_bf16(va[dt], pw, oacc[dt]);
+          for (int dt = 0; dt < DT; ++dt) {
+            oacc[dt] = mfma_bf16(va[dt], pw, oacc[dt]);
+            if constexpr (EXACT) oacc[dt] = mfma_bf16(va[dt], plo, oacc[dt]);
+          }
         }
         l_run += psum;
         }
@@ -1910,6 +1926,15 @@ int attn_group_size() { return ROLA_ATTN_G; }
 
 void launch_attn(const AttnArgs &a, int D, bool sparse, bool lowrank, bool accum, bool outf32,
                  hipStream_t st) {
+  if (a.lse && sparse && !lowrank && !accum && outf32) {
+    // the backward's recompute: fp32 weights (see k_attn, EXACT)
+    const dim3 grid((unsigned)(8 * a.groups_per_xcd * a.bh_count)), block(128 * ROLA_ATTN_G);
+    if (D == 64)
+      hipLaunchKernelGGL((k_attn<64, ROLA_ATTN_G, ROLA_ATTN_S, true, false, false, true, true>), grid, block, 0, st, a);
+    else
+      hipLaunchKernelGGL((k_attn<128, ROLA_ATTN_G, ROLA_ATTN_S, true, false, false, true, true>), grid, block, 0, st, a);
+    return;
+  }
   if (D == 64) attn_d<64, ROLA_ATTN_G, ROLA_ATTN_S>(a, sparse, lowrank, accum, outf32, st);
   else attn_d<128, ROLA_ATTN_G, ROLA_ATTN_S>(a, sparse, lowrank, accum, outf32, st);
 }
