@@ -56,6 +56,8 @@ def lib():
             "ro_e4m3_encode": ([ctypes.c_float], ctypes.c_uint8),
             "ro_quant_e4m3": ([P, I64, I64, I64, I32, P, P, P], None),
             "ro_gate": ([P, P, I32], D),
+            "ro_quant_rows_e4m3": ([P, I64, I64, I64, P, P, P], None),
+            "ro_gemm_w8a8": ([P, P, P, P, P, I64, I64, I64, P, P], None),
             "ro_lowrank_block_states": ([P, P, P, I64, I64, I32, I32, P, P, D, P, P], None),
             "ro_lowrank_rows_complement": ([P, P, P, P, P, I32, I64, I32, I32, P, P, D, I64, P, P], None),
             "ro_forward": ([P, P, P, P, P, P, I64, I64, I64, I32, I32, I32, P, P, D, D, I32, I32, P, P],
@@ -246,6 +248,42 @@ def quant_e4m3(x_bits, n_valid: int):
     deq = np.zeros(x.shape, dtype=np.float64)
     lib().ro_quant_e4m3(_p(x), bh, n_pad, n_valid, d, _p(codes), _p(scale), _p(deq))
     return codes, scale, deq
+
+
+def quant_rows_e4m3(x_bits):
+    """Per-row e4m3 quantisation of a bf16 matrix [rows, cols] (uint16 bits).
+    Returns (codes uint8 [rows, cols], scale float32 [rows], deq float64)."""
+    x = _c(x_bits, np.uint16)
+    rows, cols = x.shape
+    codes = np.zeros(x.shape, dtype=np.uint8)
+    scale = np.zeros(rows, dtype=np.float32)
+    deq = np.zeros(x.shape, dtype=np.float64)
+    lib().ro_quant_rows_e4m3(_p(x), rows, cols, cols, _p(codes), _p(scale), _p(deq))
+    return codes, scale, deq
+
+
+def gemm_w8a8(a_codes, sa, w_codes, sw, bias=None, with_abs=False):
+    """y[m, n] = sa[m] sw[n] sum_k value(a[m,k]) value(w[n,k]) + bias[n], fp64.
+    With ``with_abs`` also returns sa sw sum_k |products| + |bias| (error scale)."""
+    a, w = _c(a_codes, np.uint8), _c(w_codes, np.uint8)
+    sa, sw = _c(sa, np.float32), _c(sw, np.float32)
+    M, K = a.shape
+    N = w.shape[0]
+    assert w.shape[1] == K and sa.shape == (M,) and sw.shape == (N,)
+    b = None if bias is None else _c(bias, np.float32)
+    y = np.zeros((M, N), dtype=np.float64)
+    yabs = np.zeros((M, N), dtype=np.float64) if with_abs else None
+    lib().ro_gemm_w8a8(_p(a), _p(sa), _p(w), _p(sw), None if b is None else _p(b), M, N, K, _p(y),
+                       None if yabs is None else _p(yabs))
+    return (y, yabs) if with_abs else y
+
+
+def linear_w8a8(x_bits, w_bits, bias=None, with_abs=False):
+    """The whole w8a8 linear layer: x [M, K] and W [N, K] (bf16 bits) each
+    quantised per row, then the scaled fp8 product plus bias."""
+    ca, sa, _ = quant_rows_e4m3(x_bits)
+    cw, sw, _ = quant_rows_e4m3(w_bits)
+    return gemm_w8a8(ca, sa, cw, sw, bias, with_abs)
 
 
 def forward(q_bits, k_bits, v_bits, wq, wk, n_valid: int, kb: int, grid, split=None,

@@ -446,6 +446,71 @@ void ro_quant_e4m3(const uint16_t *x, int64_t bh_count, int64_t n_pad, int64_t n
   }
 }
 
+/* ------------------------------------------- w8a8 linear layers (fp8 GEMM) */
+/*
+ * The projections either side of attention in the fp8 pipeline (README
+ * "AlibabaResearch/SparkDiffusion", highlights: optional weight-activation
+ * quantisation, w8a8; project page, section "FP8 Quantization & Fused
+ * Kernels").  Reading taken: activations are quantised per token (row of
+ * x [M, K]) and weights per output channel (row of W [N, K]), both with the
+ * e4m3 absmax rule used for attention inputs, and the layer computes
+ *   y[m, n] = sa[m] * sw[n] * sum_k value(a[m, k]) * value(w[n, k]) + bias[n].
+ */
+
+/* Per-row quantisation of a bf16 matrix x [rows, cols] with row stride ld.
+ * codes [rows, cols]; scale [rows] = fl32(absmax/448) (1 for a zero row);
+ * deq [rows, cols] fp64 = value(code) * scale. */
+void ro_quant_rows_e4m3(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld,
+                        uint8_t *codes, float *scale, double *deq) {
+#pragma omp parallel for schedule(static)
+  for (int64_t m = 0; m < rows; ++m) {
+    float amax = 0.0f;
+    for (int64_t c = 0; c < cols; ++c) {
+      const float a = fabsf(bf16_to_f32(x[m * ld + c]));
+      if (a > amax) amax = a;
+    }
+    const float inv = amax > 0.0f ? 448.0f / amax : 1.0f;
+    const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+    scale[m] = sc;
+    for (int64_t c = 0; c < cols; ++c) {
+      const uint8_t code = ro_e4m3_encode(bf16_to_f32(x[m * ld + c]) * inv);
+      codes[m * cols + c] = code;
+      deq[m * cols + c] = ro_e4m3_value(code) * (double)sc;
+    }
+  }
+}
+
+/* y [M, N] fp64 from codes a [M, K], w [N, K], scales sa [M], sw [N] and an
+ * optional fp32 bias [N] (NULL: none).  Each product of two e4m3 values is
+ * a multiple of 2^-18 below 2^18, so for K <= 65536 every partial sum is a
+ * multiple of 2^-18 below 2^34, held exactly in fp64: the dot product is
+ * exact in any order.  It is then scaled and the bias added.
+ * yabs [M, N] (optional) receives sa*sw*sum_k |value*value| + |bias|, the
+ * magnitude that bounds the rounding of any fp32 evaluation. */
+void ro_gemm_w8a8(const uint8_t *a, const float *sa, const uint8_t *w, const float *sw,
+                  const float *bias, int64_t M, int64_t N, int64_t K, double *y, double *yabs) {
+  double *wv = (double *)malloc(sizeof(double) * (size_t)(N * K));
+  for (int64_t i = 0; i < N * K; ++i) wv[i] = ro_e4m3_value(w[i]);
+#pragma omp parallel for schedule(static)
+  for (int64_t m = 0; m < M; ++m) {
+    double *av = (double *)malloc(sizeof(double) * (size_t)K);
+    for (int64_t k = 0; k < K; ++k) av[k] = ro_e4m3_value(a[m * K + k]);
+    for (int64_t n = 0; n < N; ++n) {
+      double dot = 0.0, mag = 0.0;
+      for (int64_t k = 0; k < K; ++k) {
+        dot += av[k] * wv[n * K + k];
+        mag += fabs(av[k] * wv[n * K + k]);
+      }
+      const double s = (double)sa[m] * (double)sw[n];
+      const double b = bias ? (double)bias[n] : 0.0;
+      y[m * N + n] = s * dot + b;
+      if (yabs) yabs[m * N + n] = s * mag + fabs(b);
+    }
+    free(av);
+  }
+  free(wv);
+}
+
 /* ------------------------------------------------------------ full forward */
 static void widen(const uint16_t *x, int64_t count, double *y) {
   for (int64_t i = 0; i < count; ++i) y[i] = (double)bf16_to_f32(x[i]);
