@@ -56,6 +56,8 @@ def parse():
                     help="low-rank state over each query block's unkept blocks instead of all blocks")
     ap.add_argument("--backward", action="store_true",
                     help="time rola_backward (bf16, global scope) instead of the forward; its own JSON line")
+    ap.add_argument("--linear", default=None,
+                    help="time a w8a8 linear layer instead (wan14b_720p_qkv, wan14b_720p_out, ...)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true", help="skip the MFMA-probe and copy measurements")
     ap.add_argument("--cpu-baseline-child", action="store_true", help=argparse.SUPPRESS)
@@ -198,6 +200,87 @@ def backward_bench(args, w, rola, torch, np, W, qd, kd, vd, wqd, wkd, gd, stream
     print(json.dumps(rec), flush=True)
 
 
+def linear_bench(args, rola, torch, np, W):
+    """One w8a8 linear layer per step on the resident bf16 activations: per-token
+    quantisation (rola_quant_rows) then the scaled fp8 GEMM (rola_gemm_w8a8),
+    with the weights quantised per output channel beforehand (untimed)."""
+    lw = W.LINEAR[args.linear]
+    print("[bench] generating %s inputs" % lw.name, file=sys.stderr, flush=True)
+    xb = W.make_linear_x(lw)
+    wb, bias = W.make_linear_w(lw)
+    dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    xd, wd, bd = dev(xb), dev(wb), torch.from_numpy(bias).cuda()
+    del xb
+    stream = torch.cuda.Stream()
+    wc, sw = rola.rola_quant_rows(wd, stream=stream)
+    xc = torch.empty((lw.tokens, lw.d_in), dtype=torch.uint8, device="cuda")
+    sx = torch.empty(lw.tokens, dtype=torch.float32, device="cuda")
+    y = torch.empty((lw.tokens, lw.d_out), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        rola.rola_quant_rows(xd, xc, sx, stream=stream)
+        rola.rola_gemm_w8a8(xc, sx, wc, sw, bd, out=y, stream=stream)
+
+    rola.timing_enable(True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    rola.timing_enable(False)
+    rola.timing_read()
+    print("[bench] timing %d layer steps" % args.steps, file=sys.stderr, flush=True)
+    rola.timing_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    rola.timing_enable(False)
+    ms = e0.elapsed_time(e1) / args.steps
+    kern_ms = {name: tot / n for name, (n, tot) in rola.timing_read().items()}
+    gemm_tf = lw.flop / (kern_ms["gemm_w8a8"] * 1e-3) / 1e12
+    qbytes = lw.tokens * (lw.d_in * 3 + 4)  # bf16 in, e4m3 out, fp32 scale
+    rec = {
+        "metric": "w8a8 linear layer TFLOP/s (per-token e4m3 quantisation + fp8 GEMM)",
+        "value": round(lw.flop / (ms * 1e-3) / 1e12, 1),
+        "unit": "TFLOP/s (2*tokens*d_in*d_out per layer call)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8 (e4m3), fp32 accumulate",
+        "data": "synthetic (seeded N(0,1) activations with 1% outlier channels x8, N(0,1/d_in) weights; no checkpoint)",
+        "config": {"workload": lw.name, "tokens": lw.tokens, "d_in": lw.d_in, "d_out": lw.d_out,
+                   "out_dtype": "bf16", "bias": True},
+        "kernel_ms": {k_: round(v_, 4) for k_, v_ in sorted(kern_ms.items())},
+        "roofline": {"kernel": "gemm_w8a8", "bound": "mfma", "achieved": round(gemm_tf, 1),
+                     "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(gemm_tf / PEAK_FP8_TFLOPS, 4),
+                     "traffic": None},
+        "quant_roofline": {"kernel": "quant_rows", "bound": "hbm",
+                           "achieved": round(qbytes / (kern_ms["quant_rows"] * 1e-3) / 1e9, 1),
+                           "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                           "frac": round(qbytes / (kern_ms["quant_rows"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                           "traffic": None},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        rows = np.arange(0, lw.tokens, max(1, lw.tokens // 512))[:512]
+        xs = W.make_linear_x(lw, rows)
+        t0 = time.perf_counter()
+        oracle.linear_w8a8(xs, wb, bias)
+        dt = time.perf_counter() - t0
+        sample_flop = 2.0 * len(rows) * lw.d_in * lw.d_out
+        rec["cpu_baseline"] = {"value": round(sample_flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": _omp_threads(),
+                               "kind": "oracle",
+                               "sample": "%d of %d token rows (whole layer incl. weight quantisation), %.1f s"
+                                         % (len(rows), lw.tokens, dt)}
+    print(json.dumps(rec), flush=True)
+
+
+def _omp_threads() -> int:
+    n = os.environ.get("OMP_NUM_THREADS")
+    return int(n) if n and n.isdigit() else (os.cpu_count() or 1)
+
+
 # -------------------------------------------------------------------- main
 def measured_peaks(rola, torch, stream, dtype):
     """Sustained MFMA rate (probe kernel of independent MFMA chains on every
@@ -252,6 +335,9 @@ def main():
 
     from sparse_rank_attention_amd import rola, workloads as W
 
+    if args.linear:
+        linear_bench(args, rola, torch, np, W)
+        return
     w = W.WORKLOADS[args.workload]
     if args.topk is not None:
         import dataclasses

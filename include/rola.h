@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define ROLA_ABI_VERSION 4
+#define ROLA_ABI_VERSION 5
 #define ROLA_BLOCK 64
 #define ROLA_MAX_BLOCKS 4096 /* nb limit: N <= 262144 tokens */
 
@@ -204,6 +204,41 @@ typedef struct rola_kernel_time {
 
 int32_t rola_timing_enable(int32_t on);
 int32_t rola_timing_read(rola_kernel_time *out, int32_t max);
+
+/*
+ * w8a8 linear layers: the projections either side of attention in the fp8
+ * pipeline (README "AlibabaResearch/SparkDiffusion", highlights: optional
+ * weight-activation quantisation; project page, section "FP8 Quantization &
+ * Fused Kernels").  Activations are quantised per token (row), weights per
+ * output channel (row of W [N, K]), both with the e4m3 absmax rule of the
+ * fp8 attention inputs.
+ *
+ * rola_quant_rows: x bf16 [rows, cols] with row stride ld_x (elements) ->
+ * codes e4m3 [rows, cols] with row stride ld_codes (bytes), scale fp32
+ * [rows] = fl32(absmax/448) (1 for an all-zero row); code = RNE-saturating
+ * e4m3 of fl32(x * fl32(448/absmax)).  Requires cols > 0 and a multiple of
+ * 8, ld_x >= cols and ld_codes >= cols both multiples of 8, x and codes
+ * 16-byte aligned, scale 4-byte aligned (ROLA_ERR_INVALID_ARG /
+ * ROLA_ERR_ALIGNMENT; rows == 0 launches nothing).  No workspace; all
+ * buffers are the caller's.
+ *
+ * rola_gemm_w8a8: out[m, n] = sx[m] * sw[n] * sum_k value(x[m, k]) *
+ * value(w[n, k]) + bias[n] for m < M, n < N, accumulated in fp32 on the
+ * matrix cores and stored as bf16 (RNE) or fp32 (out_dtype ROLA_OUT_BF16 /
+ * ROLA_OUT_F32) with row stride ld_out (elements), so the output may be a
+ * column slice of a wider buffer (for example the Q, K or V part of a
+ * token-major [T, 3*H*D] tensor).  x e4m3 [M, K] (row stride ld_x bytes),
+ * w e4m3 [N, K] (row stride ld_w), sx fp32 [M], sw fp32 [N], bias fp32 [N]
+ * or NULL.  Requires M >= 1, N >= 4 and a multiple of 4, K >= 64 and a
+ * multiple of 64, ld_x, ld_w in [K, 2^24) and multiples of 16, ld_out >= N
+ * and a multiple of 4; x, w, out, sw and bias 16-byte aligned, sx 4-byte
+ * aligned.  Other columns of out are not touched.  No workspace.
+ */
+int32_t rola_quant_rows(const void *x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t *codes,
+                        int64_t ld_codes, float *scale, void *stream);
+int32_t rola_gemm_w8a8(const uint8_t *x, int64_t ld_x, const float *sx, const uint8_t *w,
+                       int64_t ld_w, const float *sw, const float *bias, int64_t M, int32_t N,
+                       int32_t K, void *out, int64_t ld_out, int32_t out_dtype, void *stream);
 
 /*
  * Measurement helper (not part of RoLA): launches, on `stream`, a kernel

@@ -594,6 +594,58 @@ int32_t rola_backward(const rola_problem *prob, const rola_config *cfg, const vo
   return timed("bwd_dkv", st, [&] { rola::launch_bwd_dkv(a, D, st); });
 }
 
+int32_t rola_quant_rows(const void *x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t *codes,
+                        int64_t ld_codes, float *scale, void *stream) {
+  if (!x || !codes || !scale || rows < 0 || cols <= 0 || cols % 8 || ld_x < cols || ld_x % 8 ||
+      ld_codes < cols || ld_codes % 8)
+    return ROLA_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(codes) || ((uintptr_t)scale & 3)) return ROLA_ERR_ALIGNMENT;
+  if (rows == 0) return ROLA_OK;
+  if ((rows + 3) / 4 > INT32_MAX) return ROLA_ERR_UNSUPPORTED;
+  rola::QuantRowsArgs a;
+  a.x = (const uint16_t *)x;
+  a.rows = rows;
+  a.cols = cols;
+  a.ldx = ld_x;
+  a.codes = codes;
+  a.ldc = ld_codes;
+  a.scale = scale;
+  return timed("quant_rows", (hipStream_t)stream, [&] { rola::launch_quant_rows(a, (hipStream_t)stream); });
+}
+
+int32_t rola_gemm_w8a8(const uint8_t *x, int64_t ld_x, const float *sx, const uint8_t *w,
+                       int64_t ld_w, const float *sw, const float *bias, int64_t M, int32_t N,
+                       int32_t K, void *out, int64_t ld_out, int32_t out_dtype, void *stream) {
+  if (!x || !sx || !w || !sw || !out) return ROLA_ERR_INVALID_ARG;
+  if (M < 1 || N < 4 || N % 4 || K < 64 || K % 64) return ROLA_ERR_INVALID_ARG;
+  if (ld_x < K || ld_x % 16 || ld_x >= (int64_t(1) << 24) || ld_w < K || ld_w % 16 ||
+      ld_w >= (int64_t(1) << 24) || ld_out < N || ld_out % 4)
+    return ROLA_ERR_INVALID_ARG;
+  if (out_dtype != ROLA_OUT_BF16 && out_dtype != ROLA_OUT_F32) return ROLA_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(out) || !aligned16(sw) ||
+      (bias && !aligned16(bias)) || ((uintptr_t)sx & 3))
+    return ROLA_ERR_ALIGNMENT;
+  const int64_t tiles_t = (M + 255) / 256, tiles_c = (N + 255) / 256;
+  if (tiles_t * tiles_c > INT32_MAX) return ROLA_ERR_UNSUPPORTED;
+  rola::GemmArgs a;
+  a.x = x;
+  a.sx = sx;
+  a.w = w;
+  a.sw = sw;
+  a.bias = bias;
+  a.out = out;
+  a.M = M;
+  a.ldx = ld_x;
+  a.ldw = ld_w;
+  a.ldo = ld_out;
+  a.N = N;
+  a.K = K;
+  a.out_f32 = out_dtype == ROLA_OUT_F32;
+  a.tiles_t = (int)tiles_t;
+  a.tiles_c = (int)tiles_c;
+  return timed("gemm_w8a8", (hipStream_t)stream, [&] { rola::launch_gemm_w8a8(a, (hipStream_t)stream); });
+}
+
 int32_t rola_mfma_probe(int32_t precision, int32_t iters, double *flop, float *sink, void *stream) {
   if (!flop || !sink || iters < 1) return ROLA_ERR_INVALID_ARG;
   if (precision != ROLA_PREC_BF16 && precision != ROLA_PREC_FP8) return ROLA_ERR_INVALID_ARG;

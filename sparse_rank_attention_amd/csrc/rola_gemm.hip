@@ -1,0 +1,247 @@
+// rola_gemm.hip -- the w8a8 linear layers either side of attention in the
+// fp8 pipeline (README "AlibabaResearch/SparkDiffusion", highlights: optional
+// weight-activation quantisation; project page, section "FP8 Quantization &
+// Fused Kernels"): per-row e4m3 quantisation of activations (per token) and
+// weights (per output channel), and the scaled fp8 product
+//   y[m, n] = sx[m] * sw[n] * sum_k value(x[m, k]) * value(w[n, k]) + bias[n]
+// on v_mfma_f32_32x32x64_f8f6f4 with fp32 accumulation.
+#include "rola_device.h"
+
+namespace rola {
+
+// ------------------------------------------------------ row quantisation
+// One wave per row, four rows per 256-thread block.  Row absmax in fp32,
+// scale fl32(absmax/448) and inverse fl32(448/absmax) (1 and 1 for a zero
+// row), codes RNE-saturated from fl32(x * inverse), eight per lane per step.
+__global__ __launch_bounds__(256) void k_quant_rows(QuantRowsArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= a.rows) return;
+  const uint16_t *xr = a.x + row * a.ldx;
+  float m = 0.0f;
+  for (int64_t c = (int64_t)lane * 8; c < a.cols; c += 512) {
+    const u32x4 w = *(const u32x4 *)(xr + c);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m = fmaxf(m, fmaxf(fabsf(bflo(w[j])), fabsf(bfhi(w[j]))));
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  const float inv = m > 0.0f ? __fdiv_rn(448.0f, m) : 1.0f;
+  if (lane == 0) a.scale[row] = m > 0.0f ? __fdiv_rn(m, 448.0f) : 1.0f;
+  uint8_t *cr = a.codes + row * a.ldc;
+  for (int64_t c = (int64_t)lane * 8; c < a.cols; c += 512) {
+    const u32x4 w = *(const u32x4 *)(xr + c);
+    int lo = cvt_fp8x2<false>(bflo(w[0]) * inv, bfhi(w[0]) * inv, 0);
+    lo = cvt_fp8x2<true>(bflo(w[1]) * inv, bfhi(w[1]) * inv, lo);
+    int hi = cvt_fp8x2<false>(bflo(w[2]) * inv, bfhi(w[2]) * inv, 0);
+    hi = cvt_fp8x2<true>(bflo(w[3]) * inv, bfhi(w[3]) * inv, hi);
+    *(uint2 *)(cr + c) = make_uint2((uint32_t)lo, (uint32_t)hi);
+  }
+}
+
+void launch_quant_rows(const QuantRowsArgs &a, hipStream_t st) {
+  const int64_t blocks = (a.rows + 3) / 4;
+  hipLaunchKernelGGL(k_quant_rows, dim3((unsigned)blocks), dim3(256), 0, st, a);
+}
+
+// ------------------------------------------------------------ fp8 GEMM
+// Workgroup tile: 256 output channels x 256 tokens, four waves in a 2 x 2
+// grid of 128 x 128.  The MFMA's A operand is the weight tile (rows =
+// channels) and its B operand the activation tile (columns = tokens), so a
+// lane's accumulator holds four consecutive channels of one token per
+// register quad and stores 8 (bf16) or 16 (fp32) contiguous bytes.
+//
+// K is staged 64 bytes at a time through a four-slot LDS ring (32 KB per
+// slot: 256 weight rows then 256 token rows of 64 bytes) filled by direct
+// global->LDS copies issued three stages ahead.  A row's 16-byte chunk c sits at
+// chunk position c ^ gemm_swz(row), which makes the operand reads (lane l:
+// row l%32, chunks 2g and 2g+1 for lane half g) free of bank conflicts for
+// 8-lane (32-bank) and 16-lane (64-bank) service groups alike.
+constexpr int kGemmTileT = 256;
+constexpr int kGemmTileC = 256;
+constexpr int kGemmK = 64;
+constexpr int kGemmSlots = 4;
+constexpr int kGemmSlotBytes = (kGemmTileT + kGemmTileC) * kGemmK;
+constexpr int kGemmGroupM = 4;  // token tiles per group of the tile order
+
+static __device__ __forceinline__ int gemm_swz(int r) { return (((r >> 1) ^ (r >> 3)) & 1) | ((r >> 1) & 2); }
+
+// Per-thread copies of a stage: 4 of weight rows and 4 of token rows.
+constexpr int kGemmCopies = 8;
+
+template <int N>
+static __device__ __forceinline__ void wait_gemm_stages() {
+  wait_vmcnt<N * kGemmCopies>();
+}
+static __device__ __forceinline__ void wait_gemm_later(int later) {
+  if (later >= 2) wait_gemm_stages<2>();
+  else if (later == 1) wait_gemm_stages<1>();
+  else wait_gemm_stages<0>();
+}
+
+// workgroup barrier without waiting for this wave's LDS reads (their
+// results are awaited where the MFMAs use them)
+static __device__ __forceinline__ void barrier_plain() { asm volatile("s_barrier" ::: "memory"); }
+
+static __device__ __forceinline__ i32x8 cat8(u32x4 a, u32x4 b) {
+  const u32x4 lo = a, hi = b;
+  return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+struct GemmRegs {
+  i32x8 w[4], x[4];
+};
+
+template <bool F32OUT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_w8a8(GemmArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kGemmSlots * kGemmSlotBytes];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5;
+
+  // tile order: each XCD (workgroups b = x mod 8) takes a contiguous range of
+  // tiles; within it, groups of kGemmGroupM token tiles sweep all channel
+  // tiles with the token tile fastest, so the tiles resident on one XCD share
+  // their activation and weight panels in its L2
+  const int ntiles = a.tiles_t * a.tiles_c;
+  const int b = blockIdx.x;
+  const int per = ntiles / 8, rem = ntiles % 8, xcd = b % 8, idx = b / 8;
+  const int t = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + idx;
+  const int group = t / (kGemmGroupM * a.tiles_c);
+  const int first = group * kGemmGroupM;
+  const int gm = min(kGemmGroupM, a.tiles_t - first);
+  const int within = t - group * kGemmGroupM * a.tiles_c;
+  const int64_t tok0 = (int64_t)(first + within % gm) * kGemmTileT;
+  const int ch0 = (within / gm) * kGemmTileC;
+
+  // copy offsets: op o covers LDS rows 16*(4o+wave) .. +16 of each part;
+  // rows past the matrix end repeat its last row (never stored)
+  uint32_t vw[4], vx[4];
+#pragma unroll
+  for (int o = 0; o < 4; ++o) {
+    const int r = 16 * (4 * o + wave) + (lane >> 2);
+    const int c = (lane & 3) ^ gemm_swz(r);
+    const int64_t rw = min((int64_t)ch0 + r, (int64_t)a.N - 1) - ch0;
+    const int64_t rx = min(tok0 + r, a.M - 1) - tok0;
+    vw[o] = (uint32_t)(rw * a.ldw + 16 * c);
+    vx[o] = (uint32_t)(rx * a.ldx + 16 * c);
+  }
+  const uint8_t *wbase = a.w + (int64_t)ch0 * a.ldw;
+  const uint8_t *xbase = a.x + tok0 * a.ldx;
+  const uint32_t lds0 = lds_addr(smem);
+  const int KT = a.K / kGemmK;
+
+  auto issue = [&](int kt) {
+    const uint32_t sb = lds0 + (uint32_t)(kt % kGemmSlots) * kGemmSlotBytes;
+    const uint8_t *wb = wbase + (int64_t)kt * kGemmK;
+    const uint8_t *xb = xbase + (int64_t)kt * kGemmK;
+#pragma unroll
+    for (int o = 0; o < 4; ++o) lds_dma16_m0(wb, vw[o], sb + (uint32_t)(4 * o + wave) * 1024);
+#pragma unroll
+    for (int o = 0; o < 4; ++o)
+      lds_dma16_m0(xb, vx[o], sb + (uint32_t)(kGemmTileC * kGemmK) + (uint32_t)(4 * o + wave) * 1024);
+  };
+
+  // operand reads: the swizzle depends on row bits 1..3 only, i.e. on lane
+  const int wc = wave & 1, wt = wave >> 1;
+  const int rl = lane & 31;
+  const uint32_t off0 = (uint32_t)(rl * kGemmK + 16 * ((2 * g) ^ gemm_swz(rl)));
+  const uint32_t off1 = (uint32_t)(rl * kGemmK + 16 * ((2 * g + 1) ^ gemm_swz(rl)));
+  auto read_w = [&](int slot, int i) -> i32x8 {
+    const LDS_AS uint8_t *p = (const LDS_AS uint8_t *)(LDS_AS void *)smem + slot * kGemmSlotBytes +
+                              (128 * wc + 32 * i) * kGemmK;
+    return cat8(*(const LDS_AS u32x4 *)(p + off0), *(const LDS_AS u32x4 *)(p + off1));
+  };
+  auto read_x = [&](int slot, int j) -> i32x8 {
+    const LDS_AS uint8_t *p = (const LDS_AS uint8_t *)(LDS_AS void *)smem + slot * kGemmSlotBytes +
+                              kGemmTileC * kGemmK + (128 * wt + 32 * j) * kGemmK;
+    return cat8(*(const LDS_AS u32x4 *)(p + off0), *(const LDS_AS u32x4 *)(p + off1));
+  };
+  auto read = [&](int slot, GemmRegs &R) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) R.w[i] = read_w(slot, i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) R.x[j] = read_x(slot, j);
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+
+  // stage s is copied into slot s % 4 during step s - 3, read into
+  // registers during step s - 1 and multiplied in step s, so the slot a
+  // step overwrites was read two steps earlier: its reads are complete
+  // (their MFMAs have issued) once every wave has reached the barrier
+  const int pre = min(3, KT);
+  for (int s = 0; s < pre; ++s) issue(s);
+  wait_gemm_later(pre - 1);
+  barrier_plain();
+
+  GemmRegs R;
+  read(0, R);
+
+  // one stage of MFMAs; with MORE, each operand register is refilled with
+  // the next stage (slot sn) right after its last MFMA of this one
+  auto stage = [&](auto more_c, int sn) {
+    constexpr bool MORE = decltype(more_c)::value;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[i][j] = mfma_fp8(R.w[i], R.x[j], acc[i][j]);
+        if (MORE && i == 3) R.x[j] = read_x(sn, j);
+      }
+      if (MORE) R.w[i] = read_w(sn, i);
+    }
+  };
+  for (int kt = 0; kt + 1 < KT; ++kt) {
+    wait_gemm_later(min(KT - 1, kt + 2) - (kt + 1));
+    barrier_plain();
+    if (kt + 3 < KT) issue(kt + 3);
+    stage(std::true_type{}, (kt + 1) % kGemmSlots);
+  }
+  stage(std::false_type{}, 0);
+
+  // epilogue: y = acc * (sx[token] * sw[channel]) + bias[channel]
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t token = tok0 + 128 * wt + 32 * j + rl;
+    if (token >= a.M) continue;
+    const float sxt = a.sx[token];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int ch = ch0 + 128 * wc + 32 * i + 8 * q + 4 * g;
+        if (ch >= a.N) continue;
+        const f32x4 swv = *(const f32x4 *)(a.sw + ch);
+        const f32x4 bv = a.bias ? *(const f32x4 *)(a.bias + ch) : f32x4{};
+        f32x4 y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = fmaf(acc[i][j][4 * q + e], sxt * swv[e], bv[e]);
+        if constexpr (F32OUT) {
+          *(f32x4 *)((float *)a.out + token * a.ldo + ch) = y;
+        } else {
+          const __bf16 b0 = (__bf16)y[0], b1 = (__bf16)y[1], b2 = (__bf16)y[2], b3 = (__bf16)y[3];
+          const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, b0) |
+                              ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+          const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, b2) |
+                              ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
+          *(uint2 *)((uint16_t *)a.out + token * a.ldo + ch) = make_uint2(lo, hi);
+        }
+      }
+    }
+  }
+}
+
+void launch_gemm_w8a8(const GemmArgs &a, hipStream_t st) {
+  const int ntiles = a.tiles_t * a.tiles_c;
+  if (a.out_f32)
+    hipLaunchKernelGGL(k_gemm_w8a8<true>, dim3((unsigned)ntiles), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_gemm_w8a8<false>, dim3((unsigned)ntiles), dim3(256), 0, st, a);
+}
+
+}  // namespace rola

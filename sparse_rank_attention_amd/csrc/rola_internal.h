@@ -191,4 +191,26 @@ void launch_bwd_tmap(const BwdArgs &a, hipStream_t st);
 void launch_bwd_dkv(const BwdArgs &a, int D, hipStream_t st);    // sparse dk, dv (+ low-rank parts)
 int bwd_outer_parts(int64_t bh_count, int nb, int mode);        // partials written per mode
 
+// w8a8 linear layers
+struct QuantRowsArgs {
+  const uint16_t *x;  // bf16 [rows, cols], row stride ldx (elements)
+  int64_t rows, cols, ldx;
+  uint8_t *codes;     // e4m3 [rows, cols], row stride ldc (bytes)
+  int64_t ldc;
+  float *scale;       // [rows]
+};
+struct GemmArgs {
+  const uint8_t *x;   // e4m3 activations [M, K], row stride ldx
+  const float *sx;    // [M]
+  const uint8_t *w;   // e4m3 weights [N, K], row stride ldw
+  const float *sw;    // [N]
+  const float *bias;  // [N] or null
+  void *out;          // [M, N] bf16 or fp32, row stride ldo (elements)
+  int64_t M, ldx, ldw, ldo;
+  int N, K, out_f32;
+  int tiles_t, tiles_c;
+};
+void launch_quant_rows(const QuantRowsArgs &a, hipStream_t st);
+void launch_gemm_w8a8(const GemmArgs &a, hipStream_t st);
+
 }  // namespace rola

@@ -58,19 +58,6 @@ __global__ void k_setup(const float *__restrict__ wq, const float *__restrict__ 
 }
 
 // ---------------------------------------------------------------- fp8 path
-// e4m3 codes: round to nearest even, saturating at +-448
-// (v_cvt_pk_fp8_f32; `hi` selects the upper 16 bits of `old`).
-template <bool HI>
-static __device__ __forceinline__ int cvt_fp8x2(float a, float b, int old) {
-  return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
-}
-
-// v_mfma_f32_32x32x64_f8f6f4 with both operands e4m3 and no block scales.
-// Lane l holds 32 codes (8 dwords) of row (A) / column (B) l%32; A and B
-// bytes with the same lane half and byte index meet at the same k.
-static __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
-}
 
 // Tile image of one 64-token block (bytes; 128*D per block):
 //  K part, [64 keys][D]: dim d of a key sits at position

@@ -47,11 +47,11 @@ class RolaKernelTime(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_int32), ("total_ms", ctypes.c_double)]
 
 
-ABI_VERSION = 4  # ROLA_ABI_VERSION of include/rola.h
+ABI_VERSION = 5  # ROLA_ABI_VERSION of include/rola.h
 
 EXPORTS = ["rola_abi_version", "rola_status_str", "rola_plan", "rola_select_blocks",
            "rola_sparse_attn", "rola_lowrank_attn", "rola_forward", "rola_backward", "rola_timing_enable",
-           "rola_timing_read", "rola_mfma_probe"]
+           "rola_timing_read", "rola_mfma_probe", "rola_quant_rows", "rola_gemm_w8a8"]
 
 _lib = None
 
@@ -91,6 +91,11 @@ def lib():
         L.rola_timing_read.argtypes = [P, I32]
         L.rola_mfma_probe.restype = I32
         L.rola_mfma_probe.argtypes = [I32, I32, P, P, P]
+        I64 = ctypes.c_int64
+        L.rola_quant_rows.restype = I32
+        L.rola_quant_rows.argtypes = [P, I64, I64, I64, P, I64, P, P]
+        L.rola_gemm_w8a8.restype = I32
+        L.rola_gemm_w8a8.argtypes = [P, I64, P, P, I64, P, P, I64, I32, I32, P, I64, I32, P]
         if L.rola_abi_version() != ABI_VERSION:
             raise RuntimeError("%s has ABI version %d, the binding expects %d: rebuild it"
                                % (path, L.rola_abi_version(), ABI_VERSION))
@@ -299,3 +304,67 @@ def timing_read():
     if n < 0:
         raise RolaError("rola_timing_read failed")
     return {buf[i].name.decode(): (buf[i].launches, buf[i].total_ms) for i in range(n)}
+
+
+# ------------------------------------------------------------ w8a8 layers
+def _on_device(*ts):
+    dev = ts[0].device
+    for t in ts:
+        if t is not None and (not t.is_cuda or t.device != dev):
+            raise RolaError("librola needs all tensors on one GPU")
+
+
+def _row_stride(t):
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise RolaError("expected a 2-D tensor with unit column stride")
+    return t.stride(0)
+
+
+def rola_quant_rows(x, codes=None, scale=None, stream=None):
+    """Per-row e4m3 quantisation of a bf16 matrix [rows, cols] (row slices of
+    a wider buffer allowed).  Returns (codes uint8 [rows, cols], scale fp32 [rows])."""
+    _on_device(x, codes, scale)
+    if x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise RolaError("x must be a 2-D bfloat16 tensor")
+    rows, cols = x.shape
+    if codes is None:
+        codes = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty(rows, dtype=torch.float32, device=x.device)
+    if codes.dtype != torch.uint8 or codes.shape != (rows, cols) or scale.dtype != torch.float32 \
+            or scale.numel() != rows or not scale.is_contiguous():
+        raise RolaError("codes must be uint8 [rows, cols] and scale float32 [rows]")
+    _check(lib().rola_quant_rows(_ptr(x), rows, cols, _row_stride(x), _ptr(codes), _row_stride(codes),
+                                 _ptr(scale), _stream(stream)), "rola_quant_rows")
+    return codes, scale
+
+
+def rola_gemm_w8a8(x_codes, sx, w_codes, sw, bias=None, out=None, out_dtype=ROLA_OUT_BF16, stream=None):
+    """out[m, n] = sx[m] sw[n] sum_k value(x[m, k]) value(w[n, k]) + bias[n].
+    x_codes uint8 [M, K], w_codes uint8 [N, K]; ``out`` may be a column slice
+    of a wider [M, *] buffer (unit column stride)."""
+    _on_device(x_codes, sx, w_codes, sw, bias, out)
+    M, K = x_codes.shape
+    N = w_codes.shape[0]
+    if x_codes.dtype != torch.uint8 or w_codes.dtype != torch.uint8 or w_codes.shape[1] != K:
+        raise RolaError("x_codes and w_codes must be uint8 [M, K] and [N, K]")
+    for t, n in ((sx, M), (sw, N)) + (((bias, N),) if bias is not None else ()):
+        if t.dtype != torch.float32 or t.numel() != n or not t.is_contiguous():
+            raise RolaError("scales and bias must be contiguous float32 vectors of the matching length")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32 if out_dtype == ROLA_OUT_F32 else torch.bfloat16,
+                          device=x_codes.device)
+    want = torch.float32 if out_dtype == ROLA_OUT_F32 else torch.bfloat16
+    if out.dtype != want or tuple(out.shape) != (M, N):
+        raise RolaError("out must be [M, N] of the dtype out_dtype names")
+    _check(lib().rola_gemm_w8a8(_ptr(x_codes), _row_stride(x_codes), _ptr(sx), _ptr(w_codes), _row_stride(w_codes),
+                                _ptr(sw), _ptr(bias), M, N, K, _ptr(out), _row_stride(out), out_dtype,
+                                _stream(stream)), "rola_gemm_w8a8")
+    return out
+
+
+def rola_linear_w8a8(x, w_codes, sw, bias=None, out=None, out_dtype=ROLA_OUT_BF16, stream=None):
+    """The whole w8a8 layer on bf16 activations: quantise x per row, then the
+    scaled fp8 product (weights quantised beforehand with rola_quant_rows)."""
+    xc, sx = rola_quant_rows(x, stream=stream)
+    return rola_gemm_w8a8(xc, sx, w_codes, sw, bias, out, out_dtype, stream)

@@ -22,6 +22,15 @@ Recipes
 * Output gate (fp32 [D+1]: weights ~ N(0, 1/D), then a bias ~ N(0, 1/4)), so
   that sigmoid(q . w + b) spreads over (0, 1) for unit-variance queries.
 
+* w8a8 linear layers (the QKV and output projections of the same DiT blocks,
+  hidden size H*D): activations x [T, H*D] ~ N(0, 1) with 1% of the input
+  channels (a fixed seeded set) scaled by 8, as a stand-in for the outlier
+  channels of real DiT activations; weights W [d_out, H*D] ~ N(0, 1/(H*D));
+  bias ~ N(0, 0.02^2); all rounded to bf16 except the fp32 bias.  Rows of x
+  draw from ``default_rng([seed, 200, row // 4096])`` in 4096-row chunks (so
+  sampled rows regenerate cheaply), the outlier set from ``[seed, 201]``, W
+  from ``[seed, 202]`` and the bias from ``[seed, 203]``.
+
 Every (batch, head, tensor) draws from ``numpy.random.default_rng([seed, b, h,
 tid])`` (tid 0=Q, 1=K, 2=V, 6=the output gradient of the backward tests) and the projections from ``default_rng([seed, 100+tid])``
 (tid 3=Wq, 4=Wk, 5=gate), so any head can be regenerated on its own.  Tokens are in
@@ -180,3 +189,61 @@ def make_dout(w: Workload, f32: bool = False):
 
 def bf16_bits_to_f32(x: np.ndarray) -> np.ndarray:
     return (x.astype(np.uint32) << 16).view(np.float32)
+
+
+@dataclasses.dataclass(frozen=True)
+class LinearWorkload:
+    """A w8a8 linear layer: y [tokens, d_out] = x [tokens, d_in] W^T + bias."""
+    name: str
+    tokens: int
+    d_in: int
+    d_out: int
+    seed: int = 0
+
+    @property
+    def flop(self) -> float:
+        return 2.0 * self.tokens * self.d_in * self.d_out
+
+
+# Wan 2.1 14B (40 heads x 128 = 5120 hidden) at 720P (21 x 45 x 80 = 75600
+# latent tokens): the fused Q/K/V projection and the output projection.
+LINEAR = {
+    "wan14b_720p_qkv": LinearWorkload("wan14b_720p_qkv", 75600, 5120, 15360),
+    "wan14b_720p_out": LinearWorkload("wan14b_720p_out", 75600, 5120, 5120),
+    "wan13b_480p_qkv": LinearWorkload("wan13b_480p_qkv", 32760, 1536, 4608),
+}
+
+_LIN_CHUNK = 4096
+
+
+def _outlier_channels(lw: LinearWorkload) -> np.ndarray:
+    rng = np.random.default_rng([lw.seed, 201])
+    return rng.choice(lw.d_in, size=max(1, lw.d_in // 100), replace=False)
+
+
+def make_linear_x(lw: LinearWorkload, rows=None) -> np.ndarray:
+    """Activations as bf16 bits [len(rows), d_in] (all rows when rows is None)."""
+    rows = np.arange(lw.tokens) if rows is None else np.asarray(rows)
+    out = np.empty((len(rows), lw.d_in), dtype=np.uint16)
+    hot = _outlier_channels(lw)
+    chunks = np.unique(rows // _LIN_CHUNK)
+
+    def run(c):
+        rng = np.random.default_rng([lw.seed, 200, int(c)])
+        n = min(_LIN_CHUNK, lw.tokens - c * _LIN_CHUNK)
+        x = rng.standard_normal((n, lw.d_in), dtype=np.float32)
+        x[:, hot] *= 8.0
+        sel = np.nonzero(rows // _LIN_CHUNK == c)[0]
+        out[sel] = to_bf16_bits(x[rows[sel] - c * _LIN_CHUNK])
+
+    with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        list(ex.map(run, chunks))
+    return out
+
+
+def make_linear_w(lw: LinearWorkload):
+    """Weights as bf16 bits [d_out, d_in] and the fp32 bias [d_out]."""
+    rng = np.random.default_rng([lw.seed, 202])
+    w = rng.standard_normal((lw.d_out, lw.d_in), dtype=np.float32) / np.float32(np.sqrt(lw.d_in))
+    bias = (np.random.default_rng([lw.seed, 203]).standard_normal(lw.d_out) * 0.02).astype(np.float32)
+    return to_bf16_bits(w), bias

@@ -15,7 +15,7 @@ P = ctypes.byref
 def _declared_functions():
     src = open(os.path.join(ROOT, "include", "rola.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(rola_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(rola_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_header_declares_the_four_calls():
@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     for name in _declared_functions():
         assert hasattr(L, name), name
     assert set(rola.EXPORTS) == set(_declared_functions())
-    assert L.rola_abi_version() == rola.ABI_VERSION == 4
+    assert L.rola_abi_version() == rola.ABI_VERSION == 5
 
 
 def _prob(B=1, H=40, D=128, grid=(21, 45, 80), sn=None):
@@ -184,3 +184,37 @@ def test_plan_rejects_token_stride_beyond_32bit_tile_offsets():
     assert st == 2
     st, _ = _plan(_prob(sn=1 << 24), rola.Config(topk=0.1))
     assert st == 0
+
+
+def test_w8a8_entries_validate_before_launch():
+    """The row quantisation and the fp8 GEMM reject bad shapes, strides and
+    alignment before any device work."""
+    L = rola.lib()
+    fake = ctypes.c_void_p(0x10000)
+    odd = ctypes.c_void_p(0x10008)
+    odd4 = ctypes.c_void_p(0x10002)
+    null = ctypes.c_void_p(0)
+    q = L.rola_quant_rows
+    assert q(null, 10, 64, 64, fake, 64, fake, null) == 1
+    assert q(fake, 10, 60, 64, fake, 64, fake, null) == 1        # cols not a multiple of 8
+    assert q(fake, 10, 64, 32, fake, 64, fake, null) == 1        # ld_x < cols
+    assert q(fake, 10, 64, 64, fake, 60, fake, null) == 1        # ld_codes not a multiple of 8
+    assert q(odd, 10, 64, 64, fake, 64, fake, null) == 3
+    assert q(fake, 10, 64, 64, fake, 64, odd4, null) == 3       # scale not 4-byte aligned
+    assert q(fake, 0, 64, 64, fake, 64, fake, null) == 0         # no rows: nothing to do
+    g = L.rola_gemm_w8a8
+    ok = dict(x=fake, ldx=128, sx=fake, w=fake, ldw=128, sw=fake, bias=null, M=100, N=64, K=128, out=fake,
+              ldo=64, dt=0)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return g(a["x"], a["ldx"], a["sx"], a["w"], a["ldw"], a["sw"], a["bias"], a["M"], a["N"], a["K"],
+                 a["out"], a["ldo"], a["dt"], null)
+    assert call(x=null) == 1 and call(sw=null) == 1 and call(out=null) == 1
+    assert call(K=96) == 1 and call(K=0) == 1                    # K a positive multiple of 64
+    assert call(N=66) == 1 and call(M=0) == 1
+    assert call(ldx=64) == 1 and call(ldw=136) == 1 and call(ldo=60) == 1 and call(ldo=66) == 1
+    assert call(ldx=1 << 24) == 1
+    assert call(dt=2) == 1
+    assert call(x=odd) == 3 and call(out=odd) == 3 and call(sw=odd) == 3 and call(bias=odd) == 3
+    assert call(sx=odd4) == 3
