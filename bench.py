@@ -34,10 +34,19 @@ def traffic_file(workload: str) -> str:
     return os.path.join(ROOT, "profiles", "attn_sparse_lowrank_%s_traffic.json" % workload)
 
 
-def kernel_source_hash() -> str:
+def linear_traffic_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", "gemm_w8a8_%s_traffic.json" % workload)
+
+
+ATTN_SOURCES = ("sparse_rank_attention_amd/csrc/rola_kernels.hip", "sparse_rank_attention_amd/csrc/rola_internal.h",
+                "sparse_rank_attention_amd/csrc/rola_device.h")
+GEMM_SOURCES = ("sparse_rank_attention_amd/csrc/rola_gemm.hip", "sparse_rank_attention_amd/csrc/rola_internal.h",
+                "sparse_rank_attention_amd/csrc/rola_device.h")
+
+
+def kernel_source_hash(sources=ATTN_SOURCES) -> str:
     h = hashlib.sha256()
-    for p in ("sparse_rank_attention_amd/csrc/rola_kernels.hip", "sparse_rank_attention_amd/csrc/rola_internal.h",
-              "sparse_rank_attention_amd/csrc/rola_device.h"):
+    for p in sources:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -221,6 +230,15 @@ def linear_bench(args, rola, torch, np, W):
         rola.rola_quant_rows(xd, xc, sx, stream=stream)
         rola.rola_gemm_w8a8(xc, sx, wc, sw, bd, out=y, stream=stream)
 
+    if args.copy_calibration_mib > 0:
+        nbytes = args.copy_calibration_mib << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print("[bench] copy calibration: %d bytes read, %d written" % (nbytes, nbytes), file=sys.stderr, flush=True)
+        del src, dst
+
     rola.timing_enable(True)
     for _ in range(args.warmup):
         step()
@@ -241,6 +259,13 @@ def linear_bench(args, rola, torch, np, W):
     kern_ms = {name: tot / n for name, (n, tot) in rola.timing_read().items()}
     gemm_tf = lw.flop / (kern_ms["gemm_w8a8"] * 1e-3) / 1e12
     qbytes = lw.tokens * (lw.d_in * 3 + 4)  # bf16 in, e4m3 out, fp32 scale
+    traffic = {"gemm_w8a8": None, "quant_rows": None}
+    tfile = linear_traffic_file(lw.name)
+    if os.path.exists(tfile):
+        with open(tfile) as f:
+            tr = json.load(f)
+        if tr.get("kernel_source_hash") == kernel_source_hash(GEMM_SOURCES) and tr.get("workload") == lw.name:
+            traffic = {k_: round(v_["total"]) for k_, v_ in tr["bytes_per_launch"].items()}
     rec = {
         "metric": "w8a8 linear layer TFLOP/s (per-token e4m3 quantisation + fp8 GEMM)",
         "value": round(lw.flop / (ms * 1e-3) / 1e12, 1),
@@ -253,17 +278,17 @@ def linear_bench(args, rola, torch, np, W):
         "kernel_ms": {k_: round(v_, 4) for k_, v_ in sorted(kern_ms.items())},
         "roofline": {"kernel": "gemm_w8a8", "bound": "mfma", "achieved": round(gemm_tf, 1),
                      "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(gemm_tf / PEAK_FP8_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": traffic["gemm_w8a8"]},
         "quant_roofline": {"kernel": "quant_rows", "bound": "hbm",
                            "achieved": round(qbytes / (kern_ms["quant_rows"] * 1e-3) / 1e9, 1),
                            "peak": PEAK_HBM_GBS, "unit": "GB/s",
                            "frac": round(qbytes / (kern_ms["quant_rows"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                           "traffic": None},
+                           "traffic": traffic["quant_rows"]},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
         import oracle
-        rows = np.arange(0, lw.tokens, max(1, lw.tokens // 512))[:512]
+        rows = np.arange(0, lw.tokens, max(1, lw.tokens // 2048))[:2048]
         xs = W.make_linear_x(lw, rows)
         t0 = time.perf_counter()
         oracle.linear_w8a8(xs, wb, bias)

@@ -13,40 +13,76 @@ namespace rola {
 // One wave per row, four rows per 256-thread block.  Row absmax in fp32,
 // scale fl32(absmax/448) and inverse fl32(448/absmax) (1 and 1 for a zero
 // row), codes RNE-saturated from fl32(x * inverse), eight per lane per step.
+// Rows of up to kQuantRegCols columns are read once and held in registers;
+// longer rows are read twice (the second pass mostly from cache).
+constexpr int kQuantRegChunks = 16;
+constexpr int64_t kQuantRegCols = 512 * kQuantRegChunks;
+
+static __device__ __forceinline__ uint2 quant8(u32x4 w, float inv) {
+  int lo = cvt_fp8x2<false>(bflo(w[0]) * inv, bfhi(w[0]) * inv, 0);
+  lo = cvt_fp8x2<true>(bflo(w[1]) * inv, bfhi(w[1]) * inv, lo);
+  int hi = cvt_fp8x2<false>(bflo(w[2]) * inv, bfhi(w[2]) * inv, 0);
+  hi = cvt_fp8x2<true>(bflo(w[3]) * inv, bfhi(w[3]) * inv, hi);
+  return make_uint2((uint32_t)lo, (uint32_t)hi);
+}
+
+static __device__ __forceinline__ float absmax8(u32x4 w, float m) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) m = fmaxf(m, fmaxf(fabsf(bflo(w[j])), fabsf(bfhi(w[j]))));
+  return m;
+}
+
+static __device__ __forceinline__ float wave_max(float m) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  return m;
+}
+
+template <bool REG>
 __global__ __launch_bounds__(256) void k_quant_rows(QuantRowsArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= a.rows) return;
   const uint16_t *xr = a.x + row * a.ldx;
-  float m = 0.0f;
-  for (int64_t c = (int64_t)lane * 8; c < a.cols; c += 512) {
-    const u32x4 w = *(const u32x4 *)(xr + c);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) m = fmaxf(m, fmaxf(fabsf(bflo(w[j])), fabsf(bfhi(w[j]))));
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-  const float inv = m > 0.0f ? __fdiv_rn(448.0f, m) : 1.0f;
-  if (lane == 0) a.scale[row] = m > 0.0f ? __fdiv_rn(m, 448.0f) : 1.0f;
   uint8_t *cr = a.codes + row * a.ldc;
-  for (int64_t c = (int64_t)lane * 8; c < a.cols; c += 512) {
-    const u32x4 w = *(const u32x4 *)(xr + c);
-    int lo = cvt_fp8x2<false>(bflo(w[0]) * inv, bfhi(w[0]) * inv, 0);
-    lo = cvt_fp8x2<true>(bflo(w[1]) * inv, bfhi(w[1]) * inv, lo);
-    int hi = cvt_fp8x2<false>(bflo(w[2]) * inv, bfhi(w[2]) * inv, 0);
-    hi = cvt_fp8x2<true>(bflo(w[3]) * inv, bfhi(w[3]) * inv, hi);
-    *(uint2 *)(cr + c) = make_uint2((uint32_t)lo, (uint32_t)hi);
+  float m = 0.0f;
+  if constexpr (REG) {
+    u32x4 w[kQuantRegChunks];
+#pragma unroll
+    for (int t = 0; t < kQuantRegChunks; ++t) {
+      const int64_t c = (int64_t)lane * 8 + 512 * t;
+      w[t] = c < a.cols ? *(const u32x4 *)(xr + c) : u32x4{};
+      m = absmax8(w[t], m);
+    }
+    m = wave_max(m);
+    const float inv = m > 0.0f ? __fdiv_rn(448.0f, m) : 1.0f;
+    if (lane == 0) a.scale[row] = m > 0.0f ? __fdiv_rn(m, 448.0f) : 1.0f;
+#pragma unroll
+    for (int t = 0; t < kQuantRegChunks; ++t) {
+      const int64_t c = (int64_t)lane * 8 + 512 * t;
+      if (c < a.cols) *(uint2 *)(cr + c) = quant8(w[t], inv);
+    }
+  } else {
+    for (int64_t c = (int64_t)lane * 8; c < a.cols; c += 512) m = absmax8(*(const u32x4 *)(xr + c), m);
+    m = wave_max(m);
+    const float inv = m > 0.0f ? __fdiv_rn(448.0f, m) : 1.0f;
+    if (lane == 0) a.scale[row] = m > 0.0f ? __fdiv_rn(m, 448.0f) : 1.0f;
+    for (int64_t c = (int64_t)lane * 8; c < a.cols; c += 512) *(uint2 *)(cr + c) = quant8(*(const u32x4 *)(xr + c), inv);
   }
 }
 
 void launch_quant_rows(const QuantRowsArgs &a, hipStream_t st) {
   const int64_t blocks = (a.rows + 3) / 4;
-  hipLaunchKernelGGL(k_quant_rows, dim3((unsigned)blocks), dim3(256), 0, st, a);
+  if (a.cols <= kQuantRegCols)
+    hipLaunchKernelGGL(k_quant_rows<true>, dim3((unsigned)blocks), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_quant_rows<false>, dim3((unsigned)blocks), dim3(256), 0, st, a);
 }
 
 // ------------------------------------------------------------ fp8 GEMM
-// Workgroup tile: 256 output channels x 256 tokens, four waves in a 2 x 2
-// grid of 128 x 128.  The MFMA's A operand is the weight tile (rows =
+// Workgroup tile: 256 output channels x 256 tokens, eight waves (two per
+// SIMD, so one wave's MFMAs cover the other's LDS reads and barrier) in a
+// 2 x 4 grid of 128 channels x 64 tokens.  The MFMA's A operand is the weight tile (rows =
 // channels) and its B operand the activation tile (columns = tokens), so a
 // lane's accumulator holds four consecutive channels of one token per
 // register quad and stores 8 (bf16) or 16 (fp32) contiguous bytes.
@@ -60,21 +96,34 @@ void launch_quant_rows(const QuantRowsArgs &a, hipStream_t st) {
 constexpr int kGemmTileT = 256;
 constexpr int kGemmTileC = 256;
 constexpr int kGemmK = 64;
-constexpr int kGemmSlots = 4;
+#ifndef ROLA_GEMM_SLOTS
+#define ROLA_GEMM_SLOTS 4
+#endif
+#ifndef ROLA_GEMM_GROUP
+#define ROLA_GEMM_GROUP 4
+#endif
+constexpr int kGemmSlots = ROLA_GEMM_SLOTS;
 constexpr int kGemmSlotBytes = (kGemmTileT + kGemmTileC) * kGemmK;
-constexpr int kGemmGroupM = 4;  // token tiles per group of the tile order
+constexpr int kGemmGroupM = ROLA_GEMM_GROUP;  // token tiles per group of the tile order
 
 static __device__ __forceinline__ int gemm_swz(int r) { return (((r >> 1) ^ (r >> 3)) & 1) | ((r >> 1) & 2); }
 
-// Per-thread copies of a stage: 4 of weight rows and 4 of token rows.
-constexpr int kGemmCopies = 8;
+#ifndef ROLA_GEMM_WC
+#define ROLA_GEMM_WC 2
+#endif
+#ifndef ROLA_GEMM_WT
+#define ROLA_GEMM_WT 4
+#endif
+// Per-thread copies of a stage: 16 of 1 KB for each part, spread over the waves.
+constexpr int kGemmCopies = 32 / (ROLA_GEMM_WC * ROLA_GEMM_WT);
 
 template <int N>
 static __device__ __forceinline__ void wait_gemm_stages() {
   wait_vmcnt<N * kGemmCopies>();
 }
 static __device__ __forceinline__ void wait_gemm_later(int later) {
-  if (later >= 2) wait_gemm_stages<2>();
+  if (later >= 3) wait_gemm_stages<3>();
+  else if (later == 2) wait_gemm_stages<2>();
   else if (later == 1) wait_gemm_stages<1>();
   else wait_gemm_stages<0>();
 }
@@ -88,12 +137,21 @@ static __device__ __forceinline__ i32x8 cat8(u32x4 a, u32x4 b) {
   return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// waves along channels x waves along tokens; each wave owns TI x TJ MFMA
+// tiles of 32 x 32
+constexpr int kGemmWC = ROLA_GEMM_WC, kGemmWT = ROLA_GEMM_WT;
+constexpr int kGemmWaves = kGemmWC * kGemmWT;
+constexpr int kGemmTI = kGemmTileC / 32 / kGemmWC, kGemmTJ = kGemmTileT / 32 / kGemmWT;
+constexpr int kGemmOps = 16 / kGemmWaves;  // 1 KB copies per wave per part per stage
+static_assert(kGemmWaves == 4 || kGemmWaves == 8, "4 or 8 waves");
+
 struct GemmRegs {
-  i32x8 w[4], x[4];
+  i32x8 w[kGemmTI], x[kGemmTJ];
 };
 
 template <bool F32OUT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_w8a8(GemmArgs a) {
+__global__ __launch_bounds__(64 * kGemmWaves) __attribute__((amdgpu_waves_per_eu(kGemmWaves / 4, kGemmWaves / 4)))
+void k_gemm_w8a8(GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kGemmSlots * kGemmSlotBytes];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -114,12 +172,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int64_t tok0 = (int64_t)(first + within % gm) * kGemmTileT;
   const int ch0 = (within / gm) * kGemmTileC;
 
-  // copy offsets: op o covers LDS rows 16*(4o+wave) .. +16 of each part;
-  // rows past the matrix end repeat its last row (never stored)
-  uint32_t vw[4], vx[4];
+  // copy offsets: op o covers LDS rows 16*(waves*o+wave) .. +16 of each
+  // part; rows past the matrix end repeat its last row (never stored)
+  uint32_t vw[kGemmOps], vx[kGemmOps];
 #pragma unroll
-  for (int o = 0; o < 4; ++o) {
-    const int r = 16 * (4 * o + wave) + (lane >> 2);
+  for (int o = 0; o < kGemmOps; ++o) {
+    const int r = 16 * (kGemmWaves * o + wave) + (lane >> 2);
     const int c = (lane & 3) ^ gemm_swz(r);
     const int64_t rw = min((int64_t)ch0 + r, (int64_t)a.N - 1) - ch0;
     const int64_t rx = min(tok0 + r, a.M - 1) - tok0;
@@ -136,45 +194,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const uint8_t *wb = wbase + (int64_t)kt * kGemmK;
     const uint8_t *xb = xbase + (int64_t)kt * kGemmK;
 #pragma unroll
-    for (int o = 0; o < 4; ++o) lds_dma16_m0(wb, vw[o], sb + (uint32_t)(4 * o + wave) * 1024);
+    for (int o = 0; o < kGemmOps; ++o) lds_dma16_m0(wb, vw[o], sb + (uint32_t)(kGemmWaves * o + wave) * 1024);
 #pragma unroll
-    for (int o = 0; o < 4; ++o)
-      lds_dma16_m0(xb, vx[o], sb + (uint32_t)(kGemmTileC * kGemmK) + (uint32_t)(4 * o + wave) * 1024);
+    for (int o = 0; o < kGemmOps; ++o)
+      lds_dma16_m0(xb, vx[o], sb + (uint32_t)(kGemmTileC * kGemmK) + (uint32_t)(kGemmWaves * o + wave) * 1024);
   };
 
   // operand reads: the swizzle depends on row bits 1..3 only, i.e. on lane
-  const int wc = wave & 1, wt = wave >> 1;
+  const int wc = wave % kGemmWC, wt = wave / kGemmWC;
   const int rl = lane & 31;
   const uint32_t off0 = (uint32_t)(rl * kGemmK + 16 * ((2 * g) ^ gemm_swz(rl)));
   const uint32_t off1 = (uint32_t)(rl * kGemmK + 16 * ((2 * g + 1) ^ gemm_swz(rl)));
   auto read_w = [&](int slot, int i) -> i32x8 {
     const LDS_AS uint8_t *p = (const LDS_AS uint8_t *)(LDS_AS void *)smem + slot * kGemmSlotBytes +
-                              (128 * wc + 32 * i) * kGemmK;
+                              (32 * kGemmTI * wc + 32 * i) * kGemmK;
     return cat8(*(const LDS_AS u32x4 *)(p + off0), *(const LDS_AS u32x4 *)(p + off1));
   };
   auto read_x = [&](int slot, int j) -> i32x8 {
     const LDS_AS uint8_t *p = (const LDS_AS uint8_t *)(LDS_AS void *)smem + slot * kGemmSlotBytes +
-                              kGemmTileC * kGemmK + (128 * wt + 32 * j) * kGemmK;
+                              kGemmTileC * kGemmK + (32 * kGemmTJ * wt + 32 * j) * kGemmK;
     return cat8(*(const LDS_AS u32x4 *)(p + off0), *(const LDS_AS u32x4 *)(p + off1));
   };
   auto read = [&](int slot, GemmRegs &R) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) R.w[i] = read_w(slot, i);
+    for (int i = 0; i < kGemmTI; ++i) R.w[i] = read_w(slot, i);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) R.x[j] = read_x(slot, j);
+    for (int j = 0; j < kGemmTJ; ++j) R.x[j] = read_x(slot, j);
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[kGemmTI][kGemmTJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kGemmTI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < kGemmTJ; ++j) acc[i][j] = f32x16{};
 
-  // stage s is copied into slot s % 4 during step s - 3, read into
-  // registers during step s - 1 and multiplied in step s, so the slot a
-  // step overwrites was read two steps earlier: its reads are complete
-  // (their MFMAs have issued) once every wave has reached the barrier
-  const int pre = min(3, KT);
+  // stage s is copied into slot s % S during step s - (S-1), read into
+  // registers during step s - 1 and multiplied in step s, so the slot a step
+  // overwrites was read two steps earlier: its reads are complete (their
+  // MFMAs have issued) once every wave has reached the barrier
+  constexpr int S = kGemmSlots;
+  static_assert(S >= 3 && S <= 5, "LDS ring of 3 to 5 slots");
+  const int pre = min(S - 1, KT);
   for (int s = 0; s < pre; ++s) issue(s);
   wait_gemm_later(pre - 1);
   barrier_plain();
@@ -187,34 +247,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   auto stage = [&](auto more_c, int sn) {
     constexpr bool MORE = decltype(more_c)::value;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kGemmTI; ++i) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < kGemmTJ; ++j) {
         acc[i][j] = mfma_fp8(R.w[i], R.x[j], acc[i][j]);
-        if (MORE && i == 3) R.x[j] = read_x(sn, j);
+        if (MORE && i == kGemmTI - 1) R.x[j] = read_x(sn, j);
       }
       if (MORE) R.w[i] = read_w(sn, i);
     }
+    // let each operand read issue between two MFMAs
+    if (MORE) {
+#pragma unroll
+      for (int u = 0; u < kGemmTI * kGemmTJ; ++u) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
   };
   for (int kt = 0; kt + 1 < KT; ++kt) {
-    wait_gemm_later(min(KT - 1, kt + 2) - (kt + 1));
+    wait_gemm_later(min(KT - 1, kt + S - 2) - (kt + 1));
     barrier_plain();
-    if (kt + 3 < KT) issue(kt + 3);
+    if (kt + S - 1 < KT) issue(kt + S - 1);
     stage(std::true_type{}, (kt + 1) % kGemmSlots);
   }
   stage(std::false_type{}, 0);
 
   // epilogue: y = acc * (sx[token] * sw[channel]) + bias[channel]
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t token = tok0 + 128 * wt + 32 * j + rl;
+  for (int j = 0; j < kGemmTJ; ++j) {
+    const int64_t token = tok0 + 32 * kGemmTJ * wt + 32 * j + rl;
     if (token >= a.M) continue;
     const float sxt = a.sx[token];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kGemmTI; ++i) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int ch = ch0 + 128 * wc + 32 * i + 8 * q + 4 * g;
+        const int ch = ch0 + 32 * kGemmTI * wc + 32 * i + 8 * q + 4 * g;
         if (ch >= a.N) continue;
         const f32x4 swv = *(const f32x4 *)(a.sw + ch);
         const f32x4 bv = a.bias ? *(const f32x4 *)(a.bias + ch) : f32x4{};
@@ -239,9 +307,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 void launch_gemm_w8a8(const GemmArgs &a, hipStream_t st) {
   const int ntiles = a.tiles_t * a.tiles_c;
   if (a.out_f32)
-    hipLaunchKernelGGL(k_gemm_w8a8<true>, dim3((unsigned)ntiles), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(k_gemm_w8a8<true>, dim3((unsigned)ntiles), dim3(64 * kGemmWaves), 0, st, a);
   else
-    hipLaunchKernelGGL(k_gemm_w8a8<false>, dim3((unsigned)ntiles), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(k_gemm_w8a8<false>, dim3((unsigned)ntiles), dim3(64 * kGemmWaves), 0, st, a);
 }
 
 }  // namespace rola

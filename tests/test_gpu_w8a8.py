@@ -47,7 +47,7 @@ def _mixed_rows(rng, rows, cols):
     return W.to_bf16_bits(x)
 
 
-@pytest.mark.parametrize("rows,cols,pad", [(1, 8, 0), (37, 200, 0), (300, 1536, 24), (5, 5120, 8)])
+@pytest.mark.parametrize("rows,cols,pad", [(1, 8, 0), (37, 200, 0), (300, 1536, 24), (5, 5120, 8), (3, 8200, 16)])
 def test_quant_rows_bit_exact(rows, cols, pad):
     """Codes and scales equal the oracle's, also from a row slice of a wider
     buffer (pad extra columns per row)."""
