@@ -271,7 +271,7 @@ def linear_bench(args, rola, torch, np, W):
         "value": round(lw.flop / (ms * 1e-3) / 1e12, 1),
         "unit": "TFLOP/s (2*tokens*d_in*d_out per layer call)",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8 (e4m3), fp32 accumulate",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8",
         "data": "synthetic (seeded N(0,1) activations with 1% outlier channels x8, N(0,1/d_in) weights; no checkpoint)",
         "config": {"workload": lw.name, "tokens": lw.tokens, "d_in": lw.d_in, "d_out": lw.d_out,
                    "out_dtype": "bf16", "bias": True},

@@ -229,7 +229,7 @@ int32_t rola_timing_read(rola_kernel_time *out, int32_t max);
  * column slice of a wider buffer (for example the Q, K or V part of a
  * token-major [T, 3*H*D] tensor).  x e4m3 [M, K] (row stride ld_x bytes),
  * w e4m3 [N, K] (row stride ld_w), sx fp32 [M], sw fp32 [N], bias fp32 [N]
- * or NULL.  Requires M >= 1, N >= 4 and a multiple of 4, K >= 64 and a
+ * or NULL.  Requires M >= 0 (0 launches nothing), N >= 4 and a multiple of 4, K >= 64 and a
  * multiple of 64, ld_x, ld_w in [K, 2^24) and multiples of 16, ld_out >= N
  * and a multiple of 4; x, w, out, sw and bias 16-byte aligned, sx 4-byte
  * aligned.  Other columns of out are not touched.  No workspace.

@@ -617,7 +617,7 @@ int32_t rola_gemm_w8a8(const uint8_t *x, int64_t ld_x, const float *sx, const ui
                        int64_t ld_w, const float *sw, const float *bias, int64_t M, int32_t N,
                        int32_t K, void *out, int64_t ld_out, int32_t out_dtype, void *stream) {
   if (!x || !sx || !w || !sw || !out) return ROLA_ERR_INVALID_ARG;
-  if (M < 1 || N < 4 || N % 4 || K < 64 || K % 64) return ROLA_ERR_INVALID_ARG;
+  if (M < 0 || N < 4 || N % 4 || K < 64 || K % 64) return ROLA_ERR_INVALID_ARG;
   if (ld_x < K || ld_x % 16 || ld_x >= (int64_t(1) << 24) || ld_w < K || ld_w % 16 ||
       ld_w >= (int64_t(1) << 24) || ld_out < N || ld_out % 4)
     return ROLA_ERR_INVALID_ARG;
@@ -625,6 +625,7 @@ int32_t rola_gemm_w8a8(const uint8_t *x, int64_t ld_x, const float *sx, const ui
   if (!aligned16(x) || !aligned16(w) || !aligned16(out) || !aligned16(sw) ||
       (bias && !aligned16(bias)) || ((uintptr_t)sx & 3))
     return ROLA_ERR_ALIGNMENT;
+  if (M == 0) return ROLA_OK;
   const int64_t tiles_t = (M + 255) / 256, tiles_c = (N + 255) / 256;
   if (tiles_t * tiles_c > INT32_MAX) return ROLA_ERR_UNSUPPORTED;
   rola::GemmArgs a;

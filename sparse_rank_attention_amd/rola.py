@@ -357,6 +357,8 @@ def rola_gemm_w8a8(x_codes, sx, w_codes, sw, bias=None, out=None, out_dtype=ROLA
     want = torch.float32 if out_dtype == ROLA_OUT_F32 else torch.bfloat16
     if out.dtype != want or tuple(out.shape) != (M, N):
         raise RolaError("out must be [M, N] of the dtype out_dtype names")
+    if M == 0:
+        return out
     _check(lib().rola_gemm_w8a8(_ptr(x_codes), _row_stride(x_codes), _ptr(sx), _ptr(w_codes), _row_stride(w_codes),
                                 _ptr(sw), _ptr(bias), M, N, K, _ptr(out), _row_stride(out), out_dtype,
                                 _stream(stream)), "rola_gemm_w8a8")

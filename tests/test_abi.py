@@ -212,7 +212,8 @@ def test_w8a8_entries_validate_before_launch():
                  a["out"], a["ldo"], a["dt"], null)
     assert call(x=null) == 1 and call(sw=null) == 1 and call(out=null) == 1
     assert call(K=96) == 1 and call(K=0) == 1                    # K a positive multiple of 64
-    assert call(N=66) == 1 and call(M=0) == 1
+    assert call(N=66) == 1 and call(M=-1) == 1
+    assert call(M=0) == 0                                        # no tokens: nothing to do
     assert call(ldx=64) == 1 and call(ldw=136) == 1 and call(ldo=60) == 1 and call(ldo=66) == 1
     assert call(ldx=1 << 24) == 1
     assert call(dt=2) == 1
