@@ -103,6 +103,28 @@ def test_gemm_matches_oracle(M, N, K, out_f32, with_bias):
     assert rel <= (4e-3 if not out_f32 else 1e-4)
 
 
+def test_gemm_operands_from_wider_buffers():
+    """x and w as column slices of wider code buffers (ld_x, ld_w > K): only
+    their first K columns take part."""
+    from sparse_rank_attention_amd import rola
+    torch = _torch()
+    say("gemm strided operands")
+    M, N, K = 333, 196, 256
+    rng = np.random.default_rng(12)
+    ca, sa, _ = oracle.quant_rows_e4m3(_mixed_rows(rng, M, K))
+    cw, sw, _ = oracle.quant_rows_e4m3(W.to_bf16_bits((rng.standard_normal((N, K)) / 16).astype(np.float32)))
+    xw = np.full((M, K + 48), 0x7E, dtype=np.uint8)  # the extra columns hold the largest code
+    ww = np.full((N, K + 32), 0x7E, dtype=np.uint8)
+    xw[:, :K], ww[:, :K] = ca, cw
+    xd = torch.from_numpy(xw).cuda()[:, :K]
+    wd = torch.from_numpy(ww).cuda()[:, :K]
+    y = rola.rola_gemm_w8a8(xd, torch.from_numpy(sa).cuda(), wd, torch.from_numpy(sw).cuda(),
+                            out_dtype=rola.ROLA_OUT_F32)
+    torch.cuda.synchronize()
+    ref, yabs = oracle.gemm_w8a8(ca, sa, cw, sw, with_abs=True)
+    assert _bound_ratio(y.cpu().numpy().astype(np.float64), ref, yabs, K, False) <= 1.0
+
+
 def test_linear_layer_and_quantised_weights_on_device():
     """Weights quantised on the device, then the whole layer (activation
     quantisation + GEMM) against the oracle's linear_w8a8."""
@@ -153,11 +175,12 @@ def test_qkv_projection_feeds_attention_through_strides():
     assert _bound_ratio(got, ref, yabs, lw.d_in, True) <= 1.0
 
 
-@pytest.mark.parametrize("name", ["wan14b_720p_qkv", "wan14b_720p_out"])
+@pytest.mark.parametrize("name", ["wan14b_720p_qkv", "wan14b_720p_out", "wan13b_480p_qkv"])
 def test_full_size_layer_sampled(name):
     """Wan 14B 720P projections (75600 tokens x 5120 -> 15360 or 5120) in the
-    launch configuration the benchmark times, checked on sampled rows: codes
-    and scales bit-exact, outputs within the bound."""
+    launch configuration the benchmark times, and the Wan 1.3B 480P QKV
+    projection (32760 x 1536 -> 4608), checked on sampled rows: codes and
+    scales bit-exact, outputs within the bound."""
     from sparse_rank_attention_amd import rola
     torch = _torch()
     say("full size", name)
