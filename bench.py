@@ -351,8 +351,8 @@ def main():
         cpu_baseline_child(args)
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU only: the RoLA forward shards by heads with no "
-              "collective, and this build runs on a single MI355X (use --gpus 1).", file=sys.stderr)
+        print("bench.py measures one GPU only (use --gpus 1): the RoLA forward shards by heads "
+              "with no collective, so N GPUs each run H/N heads of the same kernels.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
