@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define ROLA_ABI_VERSION 5
+#define ROLA_ABI_VERSION 6
 #define ROLA_BLOCK 64
 #define ROLA_MAX_BLOCKS 4096 /* nb limit: N <= 262144 tokens */
 
@@ -162,6 +162,31 @@ int32_t rola_forward(const rola_problem *prob, const rola_config *cfg, const voi
                      const void *k, const void *v, const float *wq, const float *wk,
                      const float *gate, int32_t *block_idx_out, void *out, void *workspace,
                      size_t workspace_bytes, void *stream);
+
+/*
+ * rola_forward with pre-quantised fp8 operands for the sparse branch (the
+ * fp8 pipeline of the project page, section "FP8 Quantization & Fused
+ * Kernels", with the quantisation done by the caller, e.g. fused into the
+ * kernel that produces Q, K and V).  cfg->precision must be ROLA_PREC_FP8.
+ * As in the fp8 mode of rola_forward, block selection and the low-rank
+ * branch read the bf16 q, k, v, and the sparse branch reads e4m3 codes; here
+ * the codes and scales are the caller's and the library quantises nothing:
+ *   q8, k8, v8: e4m3 codes [B, H, n_pad, D] with the strides of prob (in
+ *     elements, one byte each), 16-byte aligned; rows at or past N are
+ *     ignored;
+ *   qs, ks, vs: fp32 [B, H, nb] (contiguous), the value of a code being
+ *     e4m3(code) * scale of its (batch, head, 64-token block); scales must be
+ *     positive and finite.
+ * Codes and scales from the library's own rule (scale = fl32(absmax/448),
+ * code = RNE-saturating e4m3 of fl32(x * fl32(448/absmax))) give exactly the
+ * output of rola_forward in fp8 mode.  Workspace as for rola_forward;
+ * errors as for rola_forward, and ROLA_ERR_INVALID_ARG for a bf16 precision.
+ */
+int32_t rola_forward_e4m3(const rola_problem *prob, const rola_config *cfg, const void *q,
+                          const void *k, const void *v, const uint8_t *q8, const uint8_t *k8,
+                          const uint8_t *v8, const float *qs, const float *ks, const float *vs,
+                          const float *wq, const float *wk, const float *gate, int32_t *block_idx_out,
+                          void *out, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Backward of rola_forward (training; the README "AlibabaResearch/

@@ -298,24 +298,31 @@ int32_t run_select(const Plan &P, uint8_t *ws, float *scores, int32_t *map, hipS
   return timed("topk", st, [&] { rola::launch_topk(scores, map, P.nb, P.kb, P.BH * P.nb, st); });
 }
 
+// fp8 operands of the sparse branch: quantised from bf16 q, k, v, or (when
+// k8 is set) the caller's codes q8, k8, v8 and scales qs, ks, vs laid out
 int32_t run_quant8(const Plan &P, const rola_problem *p, const void *q, const void *k, const void *v,
-                   uint8_t *ws, hipStream_t st) {
+                   uint8_t *ws, hipStream_t st, const uint8_t *q8 = nullptr, const uint8_t *k8 = nullptr,
+                   const uint8_t *v8 = nullptr, const float *qs = nullptr, const float *ks = nullptr,
+                   const float *vs = nullptr) {
   rola::Quant8Args a;
   a.q = (const uint16_t *)q; a.k = (const uint16_t *)k; a.v = (const uint16_t *)v;
+  a.q8 = q8; a.k8 = k8; a.v8 = v8;
+  a.qs_in = qs; a.ks_in = ks; a.vs_in = vs;
   a.stride_b = p->stride_b; a.stride_h = p->stride_h; a.stride_n = p->stride_n;
   a.heads = P.H; a.nb = P.nb; a.n_tokens = P.N;
   a.qsc = (float *)(ws + P.off_qsc);
   a.ksc = (float *)(ws + P.off_ksc);
   a.vsc = (float *)(ws + P.off_vsc);
   a.kv8 = ws + P.off_kv8;
-  return timed("quant8", st, [&] { rola::launch_quant8(a, P.D, (int)P.BH, st); });
+  return timed(k8 ? "image8" : "quant8", st, [&] { rola::launch_quant8(a, P.D, (int)P.BH, st); });
 }
 
 int32_t run_attn(const Plan &P, const rola_problem *p, const rola_config *c, const void *q,
                  const void *k, const void *v, const int32_t *map, const float *gate, void *out,
                  uint8_t *ws, bool sparse, bool lowrank, bool accum, hipStream_t st,
-                 float *lse = nullptr) {
+                 float *lse = nullptr, const uint8_t *q8 = nullptr) {
   rola::AttnArgs a;
+  a.q8 = q8;
   a.q = (const uint16_t *)q; a.k = (const uint16_t *)k; a.v = (const uint16_t *)v;
   a.out = out;
   a.stride_b = p->stride_b; a.stride_h = p->stride_h; a.stride_n = p->stride_n;
@@ -513,6 +520,38 @@ int32_t rola_forward(const rola_problem *prob, const rola_config *cfg, const voi
   ROLA_TRY(run_reduce(P, ws, st));
   ROLA_TRY(run_select(P, ws, (float *)(ws + P.off_scores), map, st));
   return run_attn(P, prob, cfg, q, k, v, map, gate, out, ws, true, true, false, st);
+}
+
+int32_t rola_forward_e4m3(const rola_problem *prob, const rola_config *cfg, const void *q,
+                          const void *k, const void *v, const uint8_t *q8, const uint8_t *k8,
+                          const uint8_t *v8, const float *qs, const float *ks, const float *vs,
+                          const float *wq, const float *wk, const float *gate, int32_t *block_idx_out,
+                          void *out, void *workspace, size_t workspace_bytes, void *stream) {
+  Plan P;
+  ROLA_TRY(make_plan(prob, cfg, &P));
+  if (!P.fp8) return ROLA_ERR_INVALID_ARG;
+  if (!q || !k || !v || !q8 || !k8 || !v8 || !qs || !ks || !vs || !wq || !wk || !out)
+    return ROLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(q8) || !aligned16(k8) ||
+      !aligned16(v8) || !aligned16(out) || (block_idx_out && !aligned16(block_idx_out)))
+    return ROLA_ERR_ALIGNMENT;
+  if (((uintptr_t)wq & 3u) || ((uintptr_t)wk & 3u) || ((uintptr_t)qs & 3u) || ((uintptr_t)ks & 3u) ||
+      ((uintptr_t)vs & 3u))
+    return ROLA_ERR_ALIGNMENT;
+  if (gate && !aligned16(gate)) return ROLA_ERR_ALIGNMENT;
+  if (!workspace || (int64_t)workspace_bytes < P.total) return ROLA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return ROLA_ERR_ALIGNMENT;
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t *ws = (uint8_t *)workspace;
+  int32_t *map = block_idx_out ? block_idx_out : (int32_t *)(ws + P.off_map);
+  ROLA_TRY(run_setup(P, wq, wk, ws, st));
+  // the streaming pass in its bf16 form (pooling and low-rank state only),
+  // then the caller's codes laid out as tile images
+  ROLA_TRY(run_pass1(P, prob, q, k, v, ws, true, true, st, false));
+  ROLA_TRY(run_quant8(P, prob, q, k, v, ws, st, q8, k8, v8, qs, ks, vs));
+  ROLA_TRY(run_reduce(P, ws, st));
+  ROLA_TRY(run_select(P, ws, (float *)(ws + P.off_scores), map, st));
+  return run_attn(P, prob, cfg, q, k, v, map, gate, out, ws, true, true, false, st, nullptr, q8);
 }
 
 int32_t rola_backward(const rola_problem *prob, const rola_config *cfg, const void *q, const void *k,

@@ -55,6 +55,11 @@ struct Quant8Args {
   int64_t stride_b, stride_h, stride_n;
   int heads, nb;
   int64_t n_tokens;
+  // pre-quantised input (else NULL): e4m3 codes with the strides of q, k, v
+  // (in elements) and their per-block scales [BH][nb]; the kernel then only
+  // lays the codes out as tile images and copies the scales
+  const uint8_t *q8, *k8, *v8;
+  const float *qs_in, *ks_in, *vs_in;
   float *qsc;     // [BH][nb][2]: fl32(absmax/448), fl32(448/absmax) of Q
   float *ksc;     // [BH][nb]: fl32(absmax/448) of K
   float *vsc;     // [BH][nb]: fl32(absmax/448) of V
@@ -99,6 +104,7 @@ struct AttnArgs {
   // fp8 sparse branch only
   const uint8_t *kv8;   // tile images, see Quant8Args
   const float *qsc, *ksc, *vsc;
+  const uint8_t *q8;    // fp8 with pre-quantised input: Q codes (strides of q), else NULL
 };
 
 void launch_setup(const SetupArgs &a, hipStream_t st);

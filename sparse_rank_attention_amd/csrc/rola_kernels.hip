@@ -1584,15 +1584,29 @@ __global__ __launch_bounds__(128 * G) void k_attn8(AttnArgs args) {
   // Q codes: byte e of k-step s holds dim 64s + 16(e/8) + 8g + e%8, i.e.
   // element e%8 of qreg[4s + e/8]
   i32x8 q8[K8];
+  if (args.q8) {
+    // pre-quantised input: the caller's codes, in the same byte order
+    const uint8_t *qc = args.q8 + base + n * args.stride_n;
 #pragma unroll
-  for (int s8 = 0; s8 < K8; ++s8) {
+    for (int s8 = 0; s8 < K8; ++s8) {
 #pragma unroll
-    for (int w = 0; w < 8; ++w) {
-      const bf16x8 &src = qreg[4 * s8 + (w >> 1)];
-      const int e0 = 4 * (w & 1);
-      int v = cvt_fp8x2<false>((float)src[e0] * iq, (float)src[e0 + 1] * iq, 0);
-      v = cvt_fp8x2<true>((float)src[e0 + 2] * iq, (float)src[e0 + 3] * iq, v);
-      q8[s8][w] = v;
+      for (int pr = 0; pr < 4; ++pr) {
+        const uint2 u = *(const uint2 *)(qc + 64 * s8 + 16 * pr + 8 * g);
+        q8[s8][2 * pr] = (int)u.x;
+        q8[s8][2 * pr + 1] = (int)u.y;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int s8 = 0; s8 < K8; ++s8) {
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        const bf16x8 &src = qreg[4 * s8 + (w >> 1)];
+        const int e0 = 4 * (w & 1);
+        int v = cvt_fp8x2<false>((float)src[e0] * iq, (float)src[e0 + 1] * iq, 0);
+        v = cvt_fp8x2<true>((float)src[e0 + 2] * iq, (float)src[e0 + 3] * iq, v);
+        q8[s8][w] = v;
+      }
     }
   }
   wait_vmcnt<0>();  // Q, scales and the list in registers before the tile copies start
@@ -1926,8 +1940,58 @@ void launch_attn(const AttnArgs &a, int D, bool sparse, bool lowrank, bool accum
   else attn_d<128, ROLA_ATTN_G, ROLA_ATTN_S>(a, sparse, lowrank, accum, outf32, st);
 }
 
+// Pre-quantised input: the caller's e4m3 codes of K and V laid out as the
+// block's tile image (rows at or past N as code 0) and the caller's scales
+// copied; Q keeps its scale only (the attention kernel loads its Q codes).
+// Same grid and thread mapping as k_quant8.
+template <int D>
+__global__ __launch_bounds__(256) void k_image8(Quant8Args a) {
+  constexpr int PER = D / 4;
+  __shared__ __attribute__((aligned(16))) uint8_t img[128 * D];
+  const int tid = threadIdx.x;
+  const int c = blockIdx.x, bh = blockIdx.y;
+  const int b = bh / a.heads, h = bh % a.heads;
+  const int64_t base = (int64_t)b * a.stride_b + (int64_t)h * a.stride_h;
+  const int r = tid >> 2, part = tid & 3;
+  const int64_t n = (int64_t)c * 64 + r;
+  const bool valid = n < a.n_tokens;
+  const int64_t roff = base + (valid ? n : 0) * a.stride_n + part * PER;
+  const int64_t sidx = (int64_t)bh * a.nb + c;
+  if (tid == 0) {
+    a.qsc[2 * sidx] = a.qs_in[sidx];
+    a.qsc[2 * sidx + 1] = 1.0f;  // no Q quantisation on this path
+    a.ksc[sidx] = a.ks_in[sidx];
+    a.vsc[sidx] = a.vs_in[sidx];
+  }
+  // K: 8 consecutive dims are 8 consecutive image bytes
+#pragma unroll
+  for (int i = 0; i < PER; i += 8) {
+    const uint2 w = valid ? *(const uint2 *)(a.k8 + roff + i) : make_uint2(0u, 0u);
+    *(uint2 *)(img + img_k_off<D>(r, part * PER + i)) = w;
+  }
+  // V: transposed, one byte per code
+  uint8_t *vimg = img + 64 * D;
+  const int p = img_v_pos(r);
+#pragma unroll
+  for (int i = 0; i < PER; i += 8) {
+    const uint2 w = valid ? *(const uint2 *)(a.v8 + roff + i) : make_uint2(0u, 0u);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      vimg[img_v_off(part * PER + i + e, p)] = (uint8_t)(((e < 4 ? w.x : w.y) >> (8 * (e & 3))) & 0xffu);
+  }
+  __syncthreads();
+  u32x4 *dst = (u32x4 *)(a.kv8 + sidx * (128 * D));
+#pragma unroll
+  for (int i = tid; i < 8 * D; i += 256) dst[i] = *(const u32x4 *)(img + 16 * i);
+}
+
 void launch_quant8(const Quant8Args &a, int D, int bh, hipStream_t st) {
   dim3 grid(a.nb, bh), block(256);
+  if (a.k8) {
+    if (D == 64) hipLaunchKernelGGL(k_image8<64>, grid, block, 0, st, a);
+    else hipLaunchKernelGGL(k_image8<128>, grid, block, 0, st, a);
+    return;
+  }
   if (D == 64) hipLaunchKernelGGL(k_quant8<64>, grid, block, 0, st, a);
   else hipLaunchKernelGGL(k_quant8<128>, grid, block, 0, st, a);
 }

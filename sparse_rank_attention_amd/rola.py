@@ -47,11 +47,12 @@ class RolaKernelTime(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_int32), ("total_ms", ctypes.c_double)]
 
 
-ABI_VERSION = 5  # ROLA_ABI_VERSION of include/rola.h
+ABI_VERSION = 6  # ROLA_ABI_VERSION of include/rola.h
 
 EXPORTS = ["rola_abi_version", "rola_status_str", "rola_plan", "rola_select_blocks",
            "rola_sparse_attn", "rola_lowrank_attn", "rola_forward", "rola_backward", "rola_timing_enable",
-           "rola_timing_read", "rola_mfma_probe", "rola_quant_rows", "rola_gemm_w8a8"]
+           "rola_timing_read", "rola_mfma_probe", "rola_quant_rows", "rola_gemm_w8a8",
+           "rola_forward_e4m3"]
 
 _lib = None
 
@@ -96,6 +97,8 @@ def lib():
         L.rola_quant_rows.argtypes = [P, I64, I64, I64, P, I64, P, P]
         L.rola_gemm_w8a8.restype = I32
         L.rola_gemm_w8a8.argtypes = [P, I64, P, P, I64, P, P, I64, I32, I32, P, I64, I32, P]
+        L.rola_forward_e4m3.restype = I32
+        L.rola_forward_e4m3.argtypes = [P] * 17 + [ctypes.c_size_t, P]
         if L.rola_abi_version() != ABI_VERSION:
             raise RuntimeError("%s has ABI version %d, the binding expects %d: rebuild it"
                                % (path, L.rola_abi_version(), ABI_VERSION))
@@ -252,6 +255,35 @@ def rola_forward(q, k, v, wq, wk, grid, cfg: Config, out=None, block_idx_out=Non
     _check(lib().rola_forward(ctypes.byref(prob), ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(wq),
                               _ptr(wk), _ptr(gate), _ptr(block_idx_out), _ptr(out), _ptr(ws), ws.numel(),
                               _stream(stream)), "rola_forward")
+    return out
+
+
+def rola_forward_e4m3(q, k, v, q8, k8, v8, qs, ks, vs, wq, wk, grid, cfg: Config, out=None,
+                      block_idx_out=None, stream=None, gate=None):
+    """rola_forward in fp8 mode with the caller's e4m3 codes (uint8, the
+    shape and strides of q) and per-block scales (float32 [B, H, nb]) for the
+    sparse branch; selection and the low-rank branch read the bf16 q, k, v."""
+    _check_tokens(q, k, v)
+    _check_gate(gate, q)
+    if cfg.precision != ROLA_PREC_FP8:
+        raise RolaError("rola_forward_e4m3 needs precision ROLA_PREC_FP8")
+    for t in (q8, k8, v8):
+        if t.dtype != torch.uint8 or t.shape != q.shape or t.stride() != q.stride() or t.device != q.device:
+            raise RolaError("q8, k8, v8 must be uint8 codes with the shape and strides of q")
+    prob = problem(q, grid)
+    info = plan(prob, cfg)
+    B, H = q.shape[:2]
+    for t in (qs, ks, vs):
+        if t.dtype != torch.float32 or tuple(t.shape) != (B, H, info.nb) or not t.is_contiguous() \
+                or t.device != q.device:
+            raise RolaError("qs, ks, vs must be contiguous float32 [B, H, nb] on the device of q")
+    out = _new_out(q, cfg) if out is None else out
+    ws = workspace(q.device, info.workspace_bytes)
+    c = cfg.c()
+    _check(lib().rola_forward_e4m3(ctypes.byref(prob), ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(q8),
+                                   _ptr(k8), _ptr(v8), _ptr(qs), _ptr(ks), _ptr(vs), _ptr(wq), _ptr(wk),
+                                   _ptr(gate), _ptr(block_idx_out), _ptr(out), _ptr(ws), ws.numel(),
+                                   _stream(stream)), "rola_forward_e4m3")
     return out
 
 

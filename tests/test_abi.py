@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     for name in _declared_functions():
         assert hasattr(L, name), name
     assert set(rola.EXPORTS) == set(_declared_functions())
-    assert L.rola_abi_version() == rola.ABI_VERSION == 5
+    assert L.rola_abi_version() == rola.ABI_VERSION == 6
 
 
 def _prob(B=1, H=40, D=128, grid=(21, 45, 80), sn=None):
@@ -219,3 +219,27 @@ def test_w8a8_entries_validate_before_launch():
     assert call(dt=2) == 1
     assert call(x=odd) == 3 and call(out=odd) == 3 and call(sw=odd) == 3 and call(bias=odd) == 3
     assert call(sx=odd4) == 3
+
+
+def test_forward_e4m3_validates_before_launch():
+    L = rola.lib()
+    prob = _prob(grid=(4, 16, 16), D=64, H=2)
+    fp8 = rola.Config(topk=0.25, rank=16, precision=rola.ROLA_PREC_FP8)
+    st, info = _plan(prob, fp8)
+    fake = ctypes.c_void_p(0x10000)
+    odd = ctypes.c_void_p(0x10008)
+    odd4 = ctypes.c_void_p(0x10002)
+    null = ctypes.c_void_p(0)
+    big = info.workspace_bytes
+
+    def call(cfg, **kw):
+        a = dict(q=fake, k=fake, v=fake, q8=fake, k8=fake, v8=fake, qs=fake, ks=fake, vs=fake, wq=fake, wk=fake,
+                 gate=null, map=null, out=fake)
+        a.update(kw)
+        return L.rola_forward_e4m3(P(prob), P(cfg.c()), a["q"], a["k"], a["v"], a["q8"], a["k8"], a["v8"],
+                                   a["qs"], a["ks"], a["vs"], a["wq"], a["wk"], a["gate"], a["map"], a["out"],
+                                   fake, kw.get("ws", big), null)
+    assert call(rola.Config(topk=0.25, rank=16)) == 1          # bf16 precision
+    assert call(fp8, k8=null) == 1 and call(fp8, vs=null) == 1
+    assert call(fp8, q8=odd) == 3 and call(fp8, qs=odd4) == 3
+    assert call(fp8, ws=big - 1) == 4
