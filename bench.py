@@ -65,6 +65,8 @@ def parse():
                     help="low-rank state over each query block's unkept blocks instead of all blocks")
     ap.add_argument("--backward", action="store_true",
                     help="time rola_backward (bf16, global scope) instead of the forward; its own JSON line")
+    ap.add_argument("--e4m3-input", action="store_true",
+                    help="fp8 workloads: time rola_forward_e4m3 on pre-quantised Q/K/V codes")
     ap.add_argument("--linear", default=None,
                     help="time a w8a8 linear layer instead (wan14b_720p_qkv, wan14b_720p_out, ...)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -384,6 +386,34 @@ def main():
             sys.exit(2)
         backward_bench(args, w, rola, torch, np, W, qd, kd, vd, wqd, wkd, gd, torch.cuda.current_stream())
         return
+    e4m3 = args.e4m3_input
+    if e4m3 and not fp8:
+        print("bench.py --e4m3-input needs an fp8 workload (e.g. --workload wan14b_720p_fp8)", file=sys.stderr)
+        sys.exit(2)
+    codes = scales = None
+    if e4m3:
+        # the caller's side: per-(head, 64-token block) e4m3 codes and scales by
+        # the absmax rule, made with torch ops before the timed region
+        codes, scales = [], []
+        valid = (torch.arange(w.n_pad, device="cuda") < w.n_tokens).view(1, 1, w.nb, 64, 1)
+        for x in (qd, kd, vd):
+            xf = x.float().view(w.batch, w.heads, w.nb, 64, w.head_dim) * valid
+            amax = xf.abs().amax(dim=(3, 4))
+            inv = torch.where(amax > 0, 448.0 / torch.where(amax > 0, amax, torch.ones_like(amax)),
+                              torch.ones_like(amax))
+            scales.append(torch.where(amax > 0, amax / 448.0, torch.ones_like(amax)).contiguous())
+            codes.append((xf * inv[..., None, None]).to(torch.float8_e4m3fn).view(torch.uint8)
+                         .view(w.batch, w.heads, w.n_pad, w.head_dim).contiguous())
+            del xf
+        torch.cuda.synchronize()
+
+    def fwd():
+        if e4m3:
+            rola.rola_forward_e4m3(qd, kd, vd, *codes, *scales, wqd, wkd, w.grid, cfg, out=out, stream=stream,
+                                   gate=gd)
+        else:
+            rola.rola_forward(qd, kd, vd, wqd, wkd, w.grid, cfg, out=out, stream=stream, gate=gd)
+
     dominant = "attn8_sparse_lowrank" if fp8 else "attn_sparse_lowrank"
     peak = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
     out = torch.empty_like(qd)
@@ -399,7 +429,7 @@ def main():
     print("[bench] warmup %d" % args.warmup, file=sys.stderr, flush=True)
     rola.timing_enable(True)  # warm the per-kernel event pool as well
     for _ in range(args.warmup):
-        rola.rola_forward(qd, kd, vd, wqd, wkd, w.grid, cfg, out=out, stream=stream, gate=gd)
+        fwd()
     torch.cuda.synchronize()
     rola.timing_enable(False)
     rola.timing_read()  # drop the warmup records (their events return to the pool)
@@ -410,7 +440,7 @@ def main():
     torch.cuda.synchronize()
     e0.record(stream)
     for _ in range(args.steps):
-        rola.rola_forward(qd, kd, vd, wqd, wkd, w.grid, cfg, out=out, stream=stream, gate=gd)
+        fwd()
     e1.record(stream)
     torch.cuda.synchronize()
     rola.timing_enable(False)
@@ -424,7 +454,7 @@ def main():
     achieved = kept / t_attn / 1e12
     traffic = None
     tfile = traffic_file(w.name)
-    if os.path.exists(tfile) and args.topk is None and not args.gate and not args.complement:
+    if os.path.exists(tfile) and args.topk is None and not args.gate and not args.complement and not e4m3:
         with open(tfile) as f:
             tr = json.load(f)
         if tr.get("kernel_source_hash") == kernel_source_hash() and tr.get("workload") == w.name:
@@ -433,8 +463,9 @@ def main():
     # also write the e4m3 codes of K and V (one byte per element)
     n_tok = w.batch * w.heads * w.n_pad
     # (complement scope: plus the per-block states it writes, bf16 S and fp32 z)
-    pass1_name = "pass1_pool_%s%s" % ("blkstate" if args.complement else "state", "_quant8" if fp8 else "")
-    pass1_bytes = 3 * n_tok * w.head_dim * 2 + (2 * n_tok * w.head_dim if fp8 else 0) \
+    quant_in_pass1 = fp8 and not e4m3
+    pass1_name = "pass1_pool_%s%s" % ("blkstate" if args.complement else "state", "_quant8" if quant_in_pass1 else "")
+    pass1_bytes = 3 * n_tok * w.head_dim * 2 + (2 * n_tok * w.head_dim if quant_in_pass1 else 0) \
         + (w.batch * w.heads * w.nb * (w.head_dim * 64 + 128) if args.complement else 0)
     pass1_ms = kern_ms.get(pass1_name)
     rec = {
@@ -453,7 +484,8 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim,
                    "grid": list(w.grid), "n_tokens": w.n_tokens, "topk": w.topk, "kb": w.kb, "nb": w.nb,
                    "rank": w.rank, "output_gate": bool(args.gate),
-                   "lowrank_scope": "complement" if args.complement else "global"},
+                   "lowrank_scope": "complement" if args.complement else "global",
+                   **({"input": "pre-quantised e4m3 Q/K/V codes and block scales"} if e4m3 else {})},
         "fwd_ms": round(ms, 4),
         "dense_equiv_tflops": round(dense / (ms * 1e-3) / 1e12, 1),
         "kept_block_tflops": round(kept / (ms * 1e-3) / 1e12, 1),
@@ -462,6 +494,11 @@ def main():
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic},
     }
+    if e4m3 and "image8" in kern_ms:
+        ibytes = 4 * n_tok * w.head_dim  # read K, V codes; write their tile images
+        gbs = ibytes / (kern_ms["image8"] * 1e-3) / 1e9
+        rec["image8_roofline"] = {"kernel": "image8", "bound": "hbm", "achieved": round(gbs, 1),
+                                  "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}
     if pass1_ms:
         gbs = pass1_bytes / (pass1_ms * 1e-3) / 1e9
         rec["pass1_roofline"] = {"kernel": pass1_name, "bound": "hbm", "achieved": round(gbs, 1),
