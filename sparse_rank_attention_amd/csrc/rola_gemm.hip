@@ -149,6 +149,58 @@ struct GemmRegs {
   i32x8 w[kGemmTI], x[kGemmTJ];
 };
 
+// y = acc * (sx[token] * sw[channel]) + bias[channel] for a wave's TI x TJ
+// tiles, stored 4 consecutive channels per lane and register quad
+template <bool F32OUT>
+static __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, const f32x16 (&acc)[kGemmTI][kGemmTJ],
+                                                     int64_t tok0, int ch0, int wc, int wt, int rl, int g) {
+#pragma unroll
+  for (int j = 0; j < kGemmTJ; ++j) {
+    const int64_t token = tok0 + 32 * kGemmTJ * wt + 32 * j + rl;
+    if (token >= a.M) continue;
+    const float sxt = a.sx[token];
+#pragma unroll
+    for (int i = 0; i < kGemmTI; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int ch = ch0 + 32 * kGemmTI * wc + 32 * i + 8 * q + 4 * g;
+        if (ch >= a.N) continue;
+        const f32x4 swv = *(const f32x4 *)(a.sw + ch);
+        const f32x4 bv = a.bias ? *(const f32x4 *)(a.bias + ch) : f32x4{};
+        f32x4 y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = fmaf(acc[i][j][4 * q + e], sxt * swv[e], bv[e]);
+        if constexpr (F32OUT) {
+          *(f32x4 *)((float *)a.out + token * a.ldo + ch) = y;
+        } else {
+          const __bf16 b0 = (__bf16)y[0], b1 = (__bf16)y[1], b2 = (__bf16)y[2], b3 = (__bf16)y[3];
+          const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, b0) |
+                              ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+          const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, b2) |
+                              ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
+          *(uint2 *)((uint16_t *)a.out + token * a.ldo + ch) = make_uint2(lo, hi);
+        }
+      }
+    }
+  }
+}
+
+// tile origin of workgroup b: each XCD (workgroups b = x mod 8) takes a
+// contiguous range of tiles; within it, groups of kGemmGroupM token tiles
+// sweep all channel tiles with the token tile fastest, so the tiles resident
+// on one XCD share their activation and weight panels in its L2
+static __device__ __forceinline__ void gemm_tile_origin(const GemmArgs &a, int b, int64_t &tok0, int &ch0) {
+  const int ntiles = a.tiles_t * a.tiles_c;
+  const int per = ntiles / 8, rem = ntiles % 8, xcd = b % 8, idx = b / 8;
+  const int t = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + idx;
+  const int group = t / (kGemmGroupM * a.tiles_c);
+  const int first = group * kGemmGroupM;
+  const int gm = min(kGemmGroupM, a.tiles_t - first);
+  const int within = t - group * kGemmGroupM * a.tiles_c;
+  tok0 = (int64_t)(first + within % gm) * kGemmTileT;
+  ch0 = (within / gm) * kGemmTileC;
+}
+
 template <bool F32OUT>
 __global__ __launch_bounds__(64 * kGemmWaves) __attribute__((amdgpu_waves_per_eu(kGemmWaves / 4, kGemmWaves / 4)))
 void k_gemm_w8a8(GemmArgs a) {
@@ -157,20 +209,9 @@ void k_gemm_w8a8(GemmArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5;
 
-  // tile order: each XCD (workgroups b = x mod 8) takes a contiguous range of
-  // tiles; within it, groups of kGemmGroupM token tiles sweep all channel
-  // tiles with the token tile fastest, so the tiles resident on one XCD share
-  // their activation and weight panels in its L2
-  const int ntiles = a.tiles_t * a.tiles_c;
-  const int b = blockIdx.x;
-  const int per = ntiles / 8, rem = ntiles % 8, xcd = b % 8, idx = b / 8;
-  const int t = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + idx;
-  const int group = t / (kGemmGroupM * a.tiles_c);
-  const int first = group * kGemmGroupM;
-  const int gm = min(kGemmGroupM, a.tiles_t - first);
-  const int within = t - group * kGemmGroupM * a.tiles_c;
-  const int64_t tok0 = (int64_t)(first + within % gm) * kGemmTileT;
-  const int ch0 = (within / gm) * kGemmTileC;
+  int64_t tok0;
+  int ch0;
+  gemm_tile_origin(a, blockIdx.x, tok0, ch0);
 
   // copy offsets: op o covers LDS rows 16*(waves*o+wave) .. +16 of each
   // part; rows past the matrix end repeat its last row (never stored)
@@ -272,40 +313,126 @@ void k_gemm_w8a8(GemmArgs a) {
   }
   stage(std::false_type{}, 0);
 
-  // epilogue: y = acc * (sx[token] * sw[channel]) + bias[channel]
+  gemm_epilogue<F32OUT>(a, acc, tok0, ch0, wc, wt, rl, g);
+}
+
+// The same tile with K staged 128 bytes at a time: two 64 KB slots (256
+// weight rows, then 256 token rows, of 128 bytes), each row copied as one
+// full 128-byte line by 8 lanes.  Stage kt+1 is copied while stage kt is
+// multiplied; a stage's operands are read within its own step (the other
+// wave on the SIMD covers the first reads).  Chunk c of row r sits at
+// c ^ gemm_swz128(r): free of bank conflicts for rows read 8 or 16 at a time.
+constexpr int kGemmK2 = 128;
+constexpr int kGemmSlotBytes2 = (kGemmTileT + kGemmTileC) * kGemmK2;
+constexpr int kGemmOps2 = 32 / kGemmWaves;  // 1 KB copies per wave per part per stage
+
+static __device__ __forceinline__ int gemm_swz128(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+template <bool F32OUT>
+__global__ __launch_bounds__(64 * kGemmWaves) __attribute__((amdgpu_waves_per_eu(kGemmWaves / 4, kGemmWaves / 4)))
+void k_gemm_w8a8_k128(GemmArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kGemmSlotBytes2];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5;
+  int64_t tok0;
+  int ch0;
+  gemm_tile_origin(a, blockIdx.x, tok0, ch0);
+
+  // copy offsets: op o covers LDS rows 8*(waves*o+wave) .. +8 of each part
+  uint32_t vw[kGemmOps2], vx[kGemmOps2];
 #pragma unroll
-  for (int j = 0; j < kGemmTJ; ++j) {
-    const int64_t token = tok0 + 32 * kGemmTJ * wt + 32 * j + rl;
-    if (token >= a.M) continue;
-    const float sxt = a.sx[token];
+  for (int o = 0; o < kGemmOps2; ++o) {
+    const int r = 8 * (kGemmWaves * o + wave) + (lane >> 3);
+    const int c = (lane & 7) ^ gemm_swz128(r);
+    const int64_t rw = min((int64_t)ch0 + r, (int64_t)a.N - 1) - ch0;
+    const int64_t rx = min(tok0 + r, a.M - 1) - tok0;
+    vw[o] = (uint32_t)(rw * a.ldw + 16 * c);
+    vx[o] = (uint32_t)(rx * a.ldx + 16 * c);
+  }
+  const uint8_t *wbase = a.w + (int64_t)ch0 * a.ldw;
+  const uint8_t *xbase = a.x + tok0 * a.ldx;
+  const uint32_t lds0 = lds_addr(smem);
+  const int KT = a.K / kGemmK2;
+  auto issue = [&](int kt) {
+    const uint32_t sb = lds0 + (uint32_t)(kt & 1) * kGemmSlotBytes2;
+    const uint8_t *wb = wbase + (int64_t)kt * kGemmK2;
+    const uint8_t *xb = xbase + (int64_t)kt * kGemmK2;
+#pragma unroll
+    for (int o = 0; o < kGemmOps2; ++o) lds_dma16_m0(wb, vw[o], sb + (uint32_t)(kGemmWaves * o + wave) * 1024);
+#pragma unroll
+    for (int o = 0; o < kGemmOps2; ++o)
+      lds_dma16_m0(xb, vx[o], sb + (uint32_t)(kGemmTileC * kGemmK2) + (uint32_t)(kGemmWaves * o + wave) * 1024);
+  };
+
+  const int wc = wave % kGemmWC, wt = wave / kGemmWC;
+  const int rl = lane & 31;
+  // operand of k-step ks (0, 1) of a stage: chunks 4ks + 2g and 4ks + 2g + 1
+  auto rd = [&](int slot, int row0, int ks) -> i32x8 {
+    const LDS_AS uint8_t *p = (const LDS_AS uint8_t *)(LDS_AS void *)smem + slot * kGemmSlotBytes2 +
+                              (row0 + rl) * kGemmK2;
+    const int sw = gemm_swz128(rl);
+    return cat8(*(const LDS_AS u32x4 *)(p + 16 * ((4 * ks + 2 * g) ^ sw)),
+                *(const LDS_AS u32x4 *)(p + 16 * ((4 * ks + 2 * g + 1) ^ sw)));
+  };
+  auto read_w = [&](int slot, int i, int ks) { return rd(slot, 32 * kGemmTI * wc + 32 * i, ks); };
+  auto read_x = [&](int slot, int j, int ks) { return rd(slot, kGemmTileC + 32 * kGemmTJ * wt + 32 * j, ks); };
+
+  f32x16 acc[kGemmTI][kGemmTJ];
+#pragma unroll
+  for (int i = 0; i < kGemmTI; ++i)
+#pragma unroll
+    for (int j = 0; j < kGemmTJ; ++j) acc[i][j] = f32x16{};
+
+  issue(0);
+  GemmRegs R;
+  for (int kt = 0; kt < KT; ++kt) {
+    wait_vmcnt<0>();  // this wave's copies of stage kt
+    barrier_plain();  // every wave's copies landed; slot (kt+1)&1 (stage kt-1) fully read
+    if (kt + 1 < KT) issue(kt + 1);
+    const int sl = kt & 1;
+#pragma unroll
+    for (int i = 0; i < kGemmTI; ++i) R.w[i] = read_w(sl, i, 0);
+#pragma unroll
+    for (int j = 0; j < kGemmTJ; ++j) R.x[j] = read_x(sl, j, 0);
+    // k-step 0, refilling each operand with k-step 1 after its last MFMA
 #pragma unroll
     for (int i = 0; i < kGemmTI; ++i) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int ch = ch0 + 32 * kGemmTI * wc + 32 * i + 8 * q + 4 * g;
-        if (ch >= a.N) continue;
-        const f32x4 swv = *(const f32x4 *)(a.sw + ch);
-        const f32x4 bv = a.bias ? *(const f32x4 *)(a.bias + ch) : f32x4{};
-        f32x4 y;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = fmaf(acc[i][j][4 * q + e], sxt * swv[e], bv[e]);
-        if constexpr (F32OUT) {
-          *(f32x4 *)((float *)a.out + token * a.ldo + ch) = y;
-        } else {
-          const __bf16 b0 = (__bf16)y[0], b1 = (__bf16)y[1], b2 = (__bf16)y[2], b3 = (__bf16)y[3];
-          const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, b0) |
-                              ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
-          const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, b2) |
-                              ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
-          *(uint2 *)((uint16_t *)a.out + token * a.ldo + ch) = make_uint2(lo, hi);
-        }
+      for (int j = 0; j < kGemmTJ; ++j) {
+        acc[i][j] = mfma_fp8(R.w[i], R.x[j], acc[i][j]);
+        if (i == kGemmTI - 1) R.x[j] = read_x(sl, j, 1);
       }
+      R.w[i] = read_w(sl, i, 1);
     }
+#pragma unroll
+    for (int u = 0; u < kGemmTI * kGemmTJ; ++u) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < kGemmTI; ++i)
+#pragma unroll
+      for (int j = 0; j < kGemmTJ; ++j) acc[i][j] = mfma_fp8(R.w[i], R.x[j], acc[i][j]);
   }
+  gemm_epilogue<F32OUT>(a, acc, tok0, ch0, wc, wt, rl, g);
 }
+
+// K a multiple of 128 takes the 128-byte stages (4 % faster at 75600 x 5120
+// x 15360 than 64-byte stages), otherwise the 64-byte ring
+#ifndef ROLA_GEMM_K128
+#define ROLA_GEMM_K128 1
+#endif
 
 void launch_gemm_w8a8(const GemmArgs &a, hipStream_t st) {
   const int ntiles = a.tiles_t * a.tiles_c;
+  if (ROLA_GEMM_K128 && a.K % kGemmK2 == 0) {
+    if (a.out_f32)
+      hipLaunchKernelGGL(k_gemm_w8a8_k128<true>, dim3((unsigned)ntiles), dim3(64 * kGemmWaves), 0, st, a);
+    else
+      hipLaunchKernelGGL(k_gemm_w8a8_k128<false>, dim3((unsigned)ntiles), dim3(64 * kGemmWaves), 0, st, a);
+    return;
+  }
   if (a.out_f32)
     hipLaunchKernelGGL(k_gemm_w8a8<true>, dim3((unsigned)ntiles), dim3(64 * kGemmWaves), 0, st, a);
   else
