@@ -166,3 +166,23 @@ def test_full_size_library_rule_reproduces_the_fp8_forward():
     ref = rola.rola_forward(qd, kd, vd, wqd, wkd, w.grid, cfg)
     torch.cuda.synchronize()
     assert torch.equal(got, ref)
+
+
+@pytest.mark.parametrize("scope", ["global", "complement"])
+def test_library_rule_codes_with_gate_and_scope(scope):
+    """The output gate and the complement scope work unchanged on this path:
+    library-rule codes give exactly rola_forward's fp8 output."""
+    from sparse_rank_attention_amd import rola
+    torch = _torch()
+    say("e4m3 input, gate", scope)
+    w = SMALL[2][1]
+    q, k, v = W.make_qkv(w)
+    wq, wk = W.make_proj(w)
+    gate = torch.from_numpy(W.make_gate(w)).cuda()
+    (cq, sq), (ck, sk), (cv, sv) = (_rule_codes(w, x) for x in (q, k, v))
+    cfg = fp8_cfg(w, lowrank_scope=rola.ROLA_LR_COMPLEMENT if scope == "complement" else rola.ROLA_LR_GLOBAL)
+    got = _call(w, q, k, v, (cq, ck, cv), (sq, sk, sv), cfg, gate=gate)
+    ref = rola.rola_forward(dev(q), dev(k), dev(v), torch.from_numpy(wq).cuda(), torch.from_numpy(wk).cuda(),
+                            w.grid, cfg, gate=gate)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
