@@ -391,10 +391,12 @@ void k_gemm_w8a8_k128(GemmArgs a) {
     barrier_plain();  // every wave's copies landed; slot (kt+1)&1 (stage kt-1) fully read
     if (kt + 1 < KT) issue(kt + 1);
     const int sl = kt & 1;
-#pragma unroll
-    for (int i = 0; i < kGemmTI; ++i) R.w[i] = read_w(sl, i, 0);
+    // in the order the first MFMAs need them: the first one waits for two reads
+    R.w[0] = read_w(sl, 0, 0);
 #pragma unroll
     for (int j = 0; j < kGemmTJ; ++j) R.x[j] = read_x(sl, j, 0);
+#pragma unroll
+    for (int i = 1; i < kGemmTI; ++i) R.w[i] = read_w(sl, i, 0);
     // k-step 0, refilling each operand with k-step 1 after its last MFMA
 #pragma unroll
     for (int i = 0; i < kGemmTI; ++i) {
