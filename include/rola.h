@@ -241,7 +241,8 @@ int32_t rola_timing_read(rola_kernel_time *out, int32_t max);
  * rola_quant_rows: x bf16 [rows, cols] with row stride ld_x (elements) ->
  * codes e4m3 [rows, cols] with row stride ld_codes (bytes), scale fp32
  * [rows] = fl32(absmax/448) (1 for an all-zero row); code = RNE-saturating
- * e4m3 of fl32(x * fl32(448/absmax)).  Requires cols > 0 and a multiple of
+ * e4m3 of fl32(x * fl32(448/absmax)); x must be finite (a row holding an
+ * infinity or NaN gets unspecified codes).  Requires cols > 0 and a multiple of
  * 8, ld_x >= cols and ld_codes >= cols both multiples of 8, x and codes
  * 16-byte aligned, scale 4-byte aligned (ROLA_ERR_INVALID_ARG /
  * ROLA_ERR_ALIGNMENT; rows == 0 launches nothing).  No workspace; all
