@@ -13,10 +13,9 @@ namespace rola {
 // One wave per row, four rows per 256-thread block.  Row absmax in fp32,
 // scale fl32(absmax/448) and inverse fl32(448/absmax) (1 and 1 for a zero
 // row), codes RNE-saturated from fl32(x * inverse), eight per lane per step.
-// Rows of up to kQuantRegCols columns are read once and held in registers;
-// longer rows are read twice (the second pass mostly from cache).
+// Rows of up to 8192 columns are read once and held in registers; longer
+// rows are read twice (the second pass mostly from cache).
 constexpr int kQuantRegChunks = 16;
-constexpr int64_t kQuantRegCols = 512 * kQuantRegChunks;
 
 static __device__ __forceinline__ uint2 quant8(u32x4 w, float inv) {
   int lo = cvt_fp8x2<false>(bflo(w[0]) * inv, bfhi(w[0]) * inv, 0);
@@ -38,7 +37,9 @@ static __device__ __forceinline__ float wave_max(float m) {
   return m;
 }
 
-template <bool REG>
+// NCH > 0: the row (at most 512 * NCH columns) is held in NCH chunk
+// registers per lane; NCH = 0: two passes over the row
+template <int NCH>
 __global__ __launch_bounds__(256) void k_quant_rows(QuantRowsArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -46,10 +47,10 @@ __global__ __launch_bounds__(256) void k_quant_rows(QuantRowsArgs a) {
   const uint16_t *xr = a.x + row * a.ldx;
   uint8_t *cr = a.codes + row * a.ldc;
   float m = 0.0f;
-  if constexpr (REG) {
-    u32x4 w[kQuantRegChunks];
+  if constexpr (NCH > 0) {
+    u32x4 w[NCH];
 #pragma unroll
-    for (int t = 0; t < kQuantRegChunks; ++t) {
+    for (int t = 0; t < NCH; ++t) {
       const int64_t c = (int64_t)lane * 8 + 512 * t;
       w[t] = c < a.cols ? *(const u32x4 *)(xr + c) : u32x4{};
       m = absmax8(w[t], m);
@@ -58,7 +59,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(QuantRowsArgs a) {
     const float inv = m > 0.0f ? __fdiv_rn(448.0f, m) : 1.0f;
     if (lane == 0) a.scale[row] = m > 0.0f ? __fdiv_rn(m, 448.0f) : 1.0f;
 #pragma unroll
-    for (int t = 0; t < kQuantRegChunks; ++t) {
+    for (int t = 0; t < NCH; ++t) {
       const int64_t c = (int64_t)lane * 8 + 512 * t;
       if (c < a.cols) *(uint2 *)(cr + c) = quant8(w[t], inv);
     }
@@ -72,11 +73,18 @@ __global__ __launch_bounds__(256) void k_quant_rows(QuantRowsArgs a) {
 }
 
 void launch_quant_rows(const QuantRowsArgs &a, hipStream_t st) {
-  const int64_t blocks = (a.rows + 3) / 4;
-  if (a.cols <= kQuantRegCols)
-    hipLaunchKernelGGL(k_quant_rows<true>, dim3((unsigned)blocks), dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL(k_quant_rows<false>, dim3((unsigned)blocks), dim3(256), 0, st, a);
+  const dim3 grid((unsigned)((a.rows + 3) / 4)), block(256);
+  // the fewest chunk registers that hold the row (fewer registers, more
+  // waves in flight)
+  const int64_t nch = (a.cols + 511) / 512;
+  if (nch <= 2) hipLaunchKernelGGL(k_quant_rows<2>, grid, block, 0, st, a);
+  else if (nch <= 4) hipLaunchKernelGGL(k_quant_rows<4>, grid, block, 0, st, a);
+  else if (nch <= 6) hipLaunchKernelGGL(k_quant_rows<6>, grid, block, 0, st, a);
+  else if (nch <= 8) hipLaunchKernelGGL(k_quant_rows<8>, grid, block, 0, st, a);
+  else if (nch <= 10) hipLaunchKernelGGL(k_quant_rows<10>, grid, block, 0, st, a);
+  else if (nch <= 12) hipLaunchKernelGGL(k_quant_rows<12>, grid, block, 0, st, a);
+  else if (nch <= kQuantRegChunks) hipLaunchKernelGGL(k_quant_rows<kQuantRegChunks>, grid, block, 0, st, a);
+  else hipLaunchKernelGGL(k_quant_rows<0>, grid, block, 0, st, a);
 }
 
 // ------------------------------------------------------------ fp8 GEMM
