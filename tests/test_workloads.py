@@ -38,3 +38,22 @@ def test_keep_blocks_table():
     assert W.WORKLOADS["wan13b_480p"].kb == 51
     assert W.WORKLOADS["wan14b_480p"].kb == 25
     assert W.WORKLOADS["wan14b_720p"].kb == 35 and W.WORKLOADS["wan14b_720p"].nb == 1182
+
+
+def test_linear_inputs_regenerate_by_rows():
+    """Sampled rows of the w8a8 activations equal the same rows of the whole
+    matrix (chunked seeding), and the weights are reproducible."""
+    lw = W.LinearWorkload("t", 9000, 64, 32, seed=4)
+    full = W.make_linear_x(lw)
+    rows = np.array([0, 1, 4095, 4096, 8191, 8999])
+    np.testing.assert_array_equal(W.make_linear_x(lw, rows), full[rows])
+    w1, b1 = W.make_linear_w(lw)
+    w2, b2 = W.make_linear_w(lw)
+    np.testing.assert_array_equal(w1, w2)
+    np.testing.assert_array_equal(b1, b2)
+    # the outlier channels carry about 8x the scale of the others
+    x = W.bf16_bits_to_f32(full)
+    hot = W._outlier_channels(lw)
+    cold = np.setdiff1d(np.arange(lw.d_in), hot)
+    ratio = x[:, hot].std() / x[:, cold].std()
+    assert 7.0 < ratio < 9.0
