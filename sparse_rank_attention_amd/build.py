@@ -37,7 +37,9 @@ def source_hash() -> str:
     for p in SOURCES + HEADERS:
         with open(p, "rb") as f:
             h.update(f.read())
-    h.update(" ".join(HIPCC_FLAGS).encode())
+    # the flags without the include path, which names this checkout's
+    # location: a copy of the tree elsewhere hashes the same
+    h.update(" ".join(f for f in HIPCC_FLAGS if not f.startswith("-I")).encode())
     return h.hexdigest()
 
 
