@@ -100,7 +100,8 @@ def cpu_baseline_child(args):
     q, k, v = q[0], k[0], v[0]
     oracle.lib()
     t0 = time.perf_counter()
-    bmap = oracle.block_map(q, k, w.n_tokens, w.kb)
+    kb = oracle.keep_blocks(w.topk, w.nb)
+    bmap = oracle.block_map(q, k, w.n_tokens, kb)
     t1 = time.perf_counter()
     qf, kf, vf = (oracle.widen_bf16(x) for x in (q, k, v))
     gate_w = W.make_gate(w) if args.gate else None
@@ -125,7 +126,7 @@ def cpu_baseline_child(args):
                       "select_s": t1 - t0, "state_s": t2 - t1, "rows_s": t3 - t2}))
 
 
-def cpu_baseline(args, w):
+def cpu_baseline(args, w, kb):
     env = dict(os.environ, OMP_NUM_THREADS="1")
     # the complement rows sum every unkept block state per row: sample fewer query blocks
     stride = max(args.sample_stride, 32) if args.complement else args.sample_stride
@@ -138,7 +139,7 @@ def cpu_baseline(args, w):
     r = json.loads(res.stdout.strip().splitlines()[-1])
     ms = r["total_s"] * 1e3
     return {
-        "value": w.kept_block_flop() / (r["total_s"]) / 1e12,
+        "value": w.kept_block_flop(kb) / (r["total_s"]) / 1e12,
         "unit": "TFLOP/s (kept-block)",
         "ms": ms,
         "cores": 1,
@@ -157,7 +158,8 @@ def backward_bench(args, w, rola, torch, np, W, qd, kd, vd, wqd, wkd, gd, stream
     the stream), with the forward's block map and a seeded N(0, 1) dL/dO in bf16."""
     cfg = rola.Config(topk=w.topk, rank=w.rank)
     B, H = w.batch, w.heads
-    bmap = torch.empty((B, H, w.nb, w.kb), dtype=torch.int32, device="cuda")
+    kb = rola.plan(rola.problem(qd, w.grid), cfg).kb
+    bmap = torch.empty((B, H, w.nb, kb), dtype=torch.int32, device="cuda")
     rola.rola_forward(qd, kd, vd, wqd, wkd, w.grid, cfg, block_idx_out=bmap, stream=stream, gate=gd)
     print("[bench] generating dL/dO", file=sys.stderr, flush=True)
     dod = torch.from_numpy(W.make_dout(w).view(np.int16)).view(torch.bfloat16).cuda()
@@ -179,7 +181,7 @@ def backward_bench(args, w, rola, torch, np, W, qd, kd, vd, wqd, wkd, gd, stream
     rola.timing_enable(False)
     ms = e0.elapsed_time(e1) / args.steps
     kern_ms = {name: tot / n for name, (n, tot) in rola.timing_read().items()}
-    pairs = w.nb * w.kb * B * H
+    pairs = w.nb * kb * B * H
     unit = 2.0 * 64 * 64 * w.head_dim  # one 64x64xD product
     total = 5 * unit * pairs            # S, dP, dV, dQ, dK per kept block pair
     rec = {
@@ -190,7 +192,7 @@ def backward_bench(args, w, rola, torch, np, W, qd, kd, vd, wqd, wkd, gd, stream
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded Wan-shaped smooth field + noise Q/K, N(0,1) V and dL/dO; no weights)",
         "config": {"workload": w.name, "batch": B, "heads": H, "head_dim": w.head_dim, "grid": list(w.grid),
-                   "n_tokens": w.n_tokens, "topk": w.topk, "kb": w.kb, "nb": w.nb, "rank": w.rank,
+                   "n_tokens": w.n_tokens, "topk": w.topk, "kb": kb, "nb": w.nb, "rank": w.rank,
                    "output_gate": bool(args.gate), "pass": "backward"},
         "bwd_ms": round(ms, 4),
         "kernel_ms": {k_: round(v_, 4) for k_, v_ in sorted(kern_ms.items())},
@@ -448,7 +450,8 @@ def main():
     kernels = rola.timing_read()
     kern_ms = {name: tot / n for name, (n, tot) in kernels.items()}
 
-    kept = w.kept_block_flop()
+    kb = rola.plan(rola.problem(qd, w.grid), cfg).kb
+    kept = w.kept_block_flop(kb)
     dense = w.dense_equiv_flop()
     t_attn = kern_ms[dominant] * 1e-3
     achieved = kept / t_attn / 1e12
@@ -482,7 +485,7 @@ def main():
         "dtype": "fp8e4m3" if fp8 else "bf16",
         "data": "synthetic (seeded Wan-shaped smooth field + noise Q/K, N(0,1) V; no weights)",
         "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim,
-                   "grid": list(w.grid), "n_tokens": w.n_tokens, "topk": w.topk, "kb": w.kb, "nb": w.nb,
+                   "grid": list(w.grid), "n_tokens": w.n_tokens, "topk": w.topk, "kb": kb, "nb": w.nb,
                    "rank": w.rank, "output_gate": bool(args.gate),
                    "lowrank_scope": "complement" if args.complement else "global",
                    **({"input": "pre-quantised e4m3 Q/K/V codes and block scales"} if e4m3 else {})},
@@ -512,7 +515,7 @@ def main():
             rec["pass1_roofline"]["frac_of_measured"] = round(rec["pass1_roofline"]["achieved"] / mp["copy_gbs"], 4)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle, 1 thread, sampled)", file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(args, w)
+        rec["cpu_baseline"] = cpu_baseline(args, w, kb)
     print(json.dumps(rec), flush=True)
 
 

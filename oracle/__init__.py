@@ -47,6 +47,7 @@ def lib():
             "ro_pool": ([P, I64, I64, I64, I32, P], None),
             "ro_scores": ([P, P, I64, I32, I32, P], None),
             "ro_select": ([P, I64, I32, I32, I32, P], None),
+            "ro_keep_blocks": ([ctypes.c_float, I32], ctypes.c_int),
             "ro_sparse_rows": ([P, P, P, P, I64, I64, I32, I32, D, I64, P, P], None),
             "ro_rope3d": ([P, P, P, D, I32, P], None),
             "ro_lowrank_feature": ([P, I64, P, P, D, P, I32, I32, P], None),
@@ -120,6 +121,11 @@ def select(s: np.ndarray, kb: int) -> np.ndarray:
     out = np.zeros((bh, nq, kb), dtype=np.int32)
     lib().ro_select(_p(s), bh, nq, nb, kb, _p(out))
     return out
+
+
+def keep_blocks(topk: float, nb: int) -> int:
+    """Key blocks kept per query block for the keep ratio ``topk`` (taken as float32)."""
+    return int(lib().ro_keep_blocks(float(topk), int(nb)))
 
 
 def block_map(q_bits, k_bits, n_valid: int, kb: int) -> np.ndarray:

@@ -117,6 +117,22 @@ void ro_scores(const float *qp, const float *kp, int64_t bh_count, int nb, int d
 }
 
 /* -------------------------------------------------------------- selection */
+/*
+ * Key blocks kept per query block for the keep ratio topk (README
+ * "AlibabaResearch/SparkDiffusion", inference section: 0.1, 0.05 and 0.03
+ * keep 10%, 5% and 3% of the blocks): floor(topk * nb), at least 1 and at
+ * most nb.  topk arrives as a float32, so a decimal ratio is off by up to
+ * 2^-24 of itself; the product is taken with a relative allowance of 2^-22
+ * so that, e.g., 0.7 of 4000 blocks keeps 2800, as the decimal ratio does.
+ */
+int ro_keep_blocks(float topk, int nb) {
+  const double prod = (double)topk * (double)nb;
+  double k = floor(prod + prod * ldexp(1.0, -22));
+  if (k < 1.0) k = 1.0;
+  if (k > (double)nb) k = (double)nb;
+  return (int)k;
+}
+
 typedef struct {
   float s;
   int32_t j;

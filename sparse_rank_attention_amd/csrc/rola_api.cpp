@@ -73,7 +73,10 @@ int32_t make_plan(const rola_problem *p, const rola_config *c, Plan *pl) {
     kb = c->kb_override;
   } else {
     if (!(c->topk > 0.0f && c->topk <= 1.0f)) return ROLA_ERR_INVALID_ARG;
-    double kk = std::floor((double)c->topk * nb + 1e-6);
+    // floor(topk * nb) with a relative allowance of 2^-22 for the float32
+    // rounding of a decimal keep ratio (at most 2^-24 of it)
+    const double prod = (double)c->topk * nb;
+    const double kk = std::floor(prod + std::ldexp(prod, -22));
     kb = (int)std::max(1.0, std::min((double)nb, kk));
   }
   if (c->kb_override < 0) return ROLA_ERR_INVALID_ARG;

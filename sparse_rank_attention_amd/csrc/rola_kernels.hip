@@ -1129,7 +1129,7 @@ __global__ __launch_bounds__(128 * G) void k_attn(AttnArgs args) {
   constexpr int TILE = 64 * D;                // bf16 elements per K (or V^T) tile
   constexpr int OPS = (64 * CH) / NT;         // DMA ops per thread per tensor per tile
   static_assert(OPS >= 1 && (64 * CH) % NT == 0, "tile split");
-  static_assert(S >= 2 && S <= 4, "ring depth");
+  static_assert(S == 2 || S == 4, "ring depth");
   constexpr int LMAX = 2048;  // union-list entries staged in LDS (longer lists read the tail from HBM)
   __shared__ __attribute__((aligned(1024))) uint16_t ring[SPARSE ? S * 2 * TILE : 8];
   __shared__ int32_t slist[SPARSE ? LMAX + 8 : 4];  // + room for the reads ahead past the end
@@ -1260,44 +1260,8 @@ __global__ __launch_bounds__(128 * G) void k_attn(AttnArgs args) {
         else return list[t];
       };
       auto issue = [&](int t) { issue_j(t, __builtin_amdgcn_readfirstlane(entry(t) & 0xffff)); };
-      // Two tiles per barrier: iteration k consumes tiles 2k and 2k+1 and,
-      // before computing, copies 2k+2 and 2k+3 into the slots of 2k-2 and
-      // 2k-1 (free once every wave has passed the barrier), so each copy has
-      // a whole iteration to land.  A SIMD loaded on one tile and idle on the
-      // other evens out within the pair.
-      static_assert(S == 4, "two tiles per barrier in a four-slot ring");
-      // the list entries of tiles t2 .. t2+3, read one iteration ahead so
-      // that no LDS read stands between the barrier and the copies (entries
-      // past U are never used)
-      int ea = 0, eb = 0, ec = 0, ed = 0;
-      if constexpr (FROM_LDS) {
-        ea = slist[0]; eb = slist[1]; ec = slist[2]; ed = slist[3];
-      }
-      for (int t2 = 0; t2 < U; t2 += 2) {
-        wait_vmcnt<0>();  // this wave's copies of tiles t2, t2+1
-        barrier_lds();    // both visible to all waves; every wave is done with t2-2, t2-1
-        int e0, e1;
-        if constexpr (FROM_LDS) {
-          e0 = ea;
-          e1 = eb;
-          if (t2 + 2 < U) issue_j(t2 + 2, __builtin_amdgcn_readfirstlane(ec & 0xffff));
-          if (t2 + 3 < U) issue_j(t2 + 3, __builtin_amdgcn_readfirstlane(ed & 0xffff));
-          ea = ec;
-          eb = ed;
-          ec = slist[t2 + 4];
-          ed = slist[t2 + 5];
-        } else {
-          if (t2 + 2 < U) issue(t2 + 2);
-          if (t2 + 3 < U) issue(t2 + 3);
-          e0 = entry(t2);
-          e1 = t2 + 1 < U ? entry(t2 + 1) : 0;
-        }
-        const bool m0 = active && ((e0 >> (16 + member)) & 1);
-        const bool m1 = active && ((e1 >> (16 + member)) & 1);
-        if (!m0 && !m1) continue;
-        for (int t = t2; t < min(t2 + 2, U); ++t) {
-        const int ent = t == t2 ? e0 : e1;
-        if (!(t == t2 ? m0 : m1)) continue;
+      // one listed tile t (list entry ent) for this wave's 32 query rows
+      auto tile = [&](int t, int ent) __attribute__((always_inline)) {
         const int j = ent & 0xffff;
         const uint16_t *sK = ring + (t % S) * (2 * TILE);
         const uint16_t *sV = sK + TILE;
@@ -1390,7 +1354,70 @@ __global__ __launch_bounds__(128 * G) void k_attn(AttnArgs args) {
           }
         }
         l_run += psum;
+      };
+      if constexpr (S == 4) {
+      // Two tiles per barrier: iteration k consumes tiles 2k and 2k+1 and,
+      // before computing, copies 2k+2 and 2k+3 into the slots of 2k-2 and
+      // 2k-1 (free once every wave has passed the barrier), so each copy has
+      // a whole iteration to land.  A SIMD loaded on one tile and idle on the
+      // other evens out within the pair.
+      // the list entries of tiles t2 .. t2+3, read one iteration ahead so
+      // that no LDS read stands between the barrier and the copies (entries
+      // past U are never used)
+      int ea = 0, eb = 0, ec = 0, ed = 0;
+      if constexpr (FROM_LDS) {
+        ea = slist[0]; eb = slist[1]; ec = slist[2]; ed = slist[3];
+      }
+      for (int t2 = 0; t2 < U; t2 += 2) {
+        wait_vmcnt<0>();  // this wave's copies of tiles t2, t2+1
+        barrier_lds();    // both visible to all waves; every wave is done with t2-2, t2-1
+        int e0, e1;
+        if constexpr (FROM_LDS) {
+          e0 = ea;
+          e1 = eb;
+          if (t2 + 2 < U) issue_j(t2 + 2, __builtin_amdgcn_readfirstlane(ec & 0xffff));
+          if (t2 + 3 < U) issue_j(t2 + 3, __builtin_amdgcn_readfirstlane(ed & 0xffff));
+          ea = ec;
+          eb = ed;
+          ec = slist[t2 + 4];
+          ed = slist[t2 + 5];
+        } else {
+          if (t2 + 2 < U) issue(t2 + 2);
+          if (t2 + 3 < U) issue(t2 + 3);
+          e0 = entry(t2);
+          e1 = t2 + 1 < U ? entry(t2 + 1) : 0;
         }
+        const bool m0 = active && ((e0 >> (16 + member)) & 1);
+        const bool m1 = active && t2 + 1 < U && ((e1 >> (16 + member)) & 1);
+        if (m0) tile(t2, e0);
+        if (m1) tile(t2 + 1, e1);
+      }
+      } else {
+      // One tile per barrier in a two-slot ring (half the LDS, so two
+      // workgroups share a CU): iteration t consumes tile t and, right after
+      // the barrier that frees the slot of tile t-1, copies tile t+1 into
+      // it.  Tiles 0 and 1 come from the prologue.  Entries are read two
+      // iterations ahead (entries past U are never used).
+      static_assert(S == 2, "ring of two or four slots");
+      int ecur = 0, enext = 0;
+      if constexpr (FROM_LDS) {
+        ecur = slist[0]; enext = slist[1];
+      }
+      for (int t = 0; t < U; ++t) {
+        wait_vmcnt<0>();  // this wave's copies of tile t
+        barrier_lds();    // visible to all waves; every wave is done with tile t-1
+        int e;
+        if constexpr (FROM_LDS) {
+          e = ecur;
+          if (t >= 1 && t + 1 < U) issue_j(t + 1, __builtin_amdgcn_readfirstlane(enext & 0xffff));
+          ecur = enext;
+          enext = slist[t + 2];
+        } else {
+          if (t >= 1 && t + 1 < U) issue(t + 1);
+          e = entry(t);
+        }
+        if (active && ((e >> (16 + member)) & 1)) tile(t, e);
+      }
       }
     };
     if (U <= LMAX) main_loop(std::integral_constant<bool, true>{});

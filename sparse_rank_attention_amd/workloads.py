@@ -73,21 +73,13 @@ class Workload:
     def n_pad(self) -> int:
         return self.nb * BLOCK
 
-    @property
-    def kb(self) -> int:
-        return keep_blocks(self.topk, self.nb)
-
     def dense_equiv_flop(self) -> float:
         n = self.n_tokens
         return 4.0 * n * n * self.head_dim * self.batch * self.heads
 
-    def kept_block_flop(self) -> float:
-        return 4.0 * self.nb * self.kb * BLOCK * BLOCK * self.head_dim * self.batch * self.heads
-
-
-def keep_blocks(topk: float, nb: int) -> int:
-    """Number of key blocks kept per query block: floor(topk * nb), at least 1."""
-    return max(1, min(nb, int(np.floor(topk * nb + 1e-6))))
+    def kept_block_flop(self, kb: int) -> float:
+        """Work of the kept 64x64 block pairs when each query block keeps kb key blocks."""
+        return 4.0 * self.nb * kb * BLOCK * BLOCK * self.head_dim * self.batch * self.heads
 
 
 WORKLOADS = {

@@ -64,7 +64,7 @@ def test_backward_matches_oracle(name, w, gated, dout_f32):
     dq, dk, dv, dwq, dwk, dgate = rola.rola_backward(qd, kd, vd, torch.from_numpy(wq).cuda(),
                                                      torch.from_numpy(wk).cuda(), w.grid, cfg, bmap, dod, gate=gd)
     torch.cuda.synchronize()
-    m_ref = oracle.block_map(q[0], k[0], w.n_tokens, w.kb)
+    m_ref = oracle.block_map(q[0], k[0], w.n_tokens, oracle.keep_blocks(w.topk, w.nb))
     np.testing.assert_array_equal(bmap.cpu().numpy()[0], m_ref)
     f64 = oracle.widen_bf16
     # an fp32 dout is taken at bf16 precision (the header's contract)
@@ -104,7 +104,7 @@ def test_backward_full_size_sampled():
     dq, dk, dv, dwq, dwk, _ = rola.rola_backward(qd, kd, vd, torch.from_numpy(wq).cuda(), torch.from_numpy(wk).cuda(),
                                                  w.grid, cfg, bmap, dev(do))
     torch.cuda.synchronize()
-    m_ref = oracle.block_map(q[0], k[0], w.n_tokens, w.kb)
+    m_ref = oracle.block_map(q[0], k[0], w.n_tokens, oracle.keep_blocks(w.topk, w.nb))
     np.testing.assert_array_equal(bmap.cpu().numpy()[0], m_ref)
     rng = np.random.default_rng(17)
     heads = (1, w.heads - 2)

@@ -47,13 +47,13 @@ def test_complement_forward_matches_oracle(name, w, prec, out_f32):
     say("complement forward", name, prec, "f32out" if out_f32 else "bf16out")
     q, k, v = W.make_qkv(w)
     wq, wk = W.make_proj(w)
-    bmap = torch.empty((w.batch, w.heads, w.nb, w.kb), dtype=torch.int32, device="cuda")
+    bmap = torch.empty((w.batch, w.heads, w.nb, oracle.keep_blocks(w.topk, w.nb)), dtype=torch.int32, device="cuda")
     cfg = ccfg(w, out_dtype=rola.ROLA_OUT_F32 if out_f32 else rola.ROLA_OUT_BF16,
                precision=rola.ROLA_PREC_FP8 if fp8 else rola.ROLA_PREC_BF16)
     out = rola.rola_forward(dev(q), dev(k), dev(v), torch.from_numpy(wq).cuda(), torch.from_numpy(wk).cuda(),
                             w.grid, cfg, block_idx_out=bmap)
     torch.cuda.synchronize()
-    m_ref, o_ref = oracle.forward(_flat(w, q), _flat(w, k), _flat(w, v), wq, wk, w.n_tokens, w.kb, w.grid,
+    m_ref, o_ref = oracle.forward(_flat(w, q), _flat(w, k), _flat(w, v), wq, wk, w.n_tokens, oracle.keep_blocks(w.topk, w.nb), w.grid,
                                   fp8=fp8, complement=True)
     np.testing.assert_array_equal(bmap.cpu().numpy().reshape(m_ref.shape), m_ref)
     got = host_f64(out).reshape(o_ref.shape)
@@ -78,8 +78,8 @@ def test_complement_lowrank_alone_and_accumulated(name, w):
     qd, kd, vd = dev(q), dev(k), dev(v)
     wqd, wkd, gd = torch.from_numpy(wq).cuda(), torch.from_numpy(wk).cuda(), torch.from_numpy(g).cuda()
     cfg = ccfg(w, out_dtype=rola.ROLA_OUT_F32)
-    m_ref = oracle.block_map(q[0], k[0], w.n_tokens, w.kb)
-    bmap = torch.from_numpy(m_ref).cuda().reshape(w.batch, w.heads, w.nb, w.kb)
+    m_ref = oracle.block_map(q[0], k[0], w.n_tokens, oracle.keep_blocks(w.topk, w.nb))
+    bmap = torch.from_numpy(m_ref).cuda().reshape(w.batch, w.heads, w.nb, oracle.keep_blocks(w.topk, w.nb))
     o_lr = rola.rola_lowrank_attn(qd, kd, vd, wqd, wkd, w.grid, cfg)
     o_lrg = rola.rola_lowrank_attn(qd, kd, vd, wqd, wkd, w.grid, cfg, gate=gd)
     o_sum = rola.rola_sparse_attn(qd, kd, vd, bmap, w.grid, cfg)
@@ -112,7 +112,7 @@ def test_complement_keep_all_is_the_sparse_branch(prec):
     wq, wk = (torch.from_numpy(x).cuda() for x in W.make_proj(w))
     cfg = ccfg(w, out_dtype=rola.ROLA_OUT_F32,
                precision=rola.ROLA_PREC_FP8 if prec == "fp8" else rola.ROLA_PREC_BF16)
-    bmap = torch.empty((w.batch, w.heads, w.nb, w.kb), dtype=torch.int32, device="cuda")
+    bmap = torch.empty((w.batch, w.heads, w.nb, oracle.keep_blocks(w.topk, w.nb)), dtype=torch.int32, device="cuda")
     out = rola.rola_forward(q, k, v, wq, wk, w.grid, cfg, block_idx_out=bmap)
     lr = rola.rola_lowrank_attn(q, k, v, wq, wk, w.grid, cfg)
     sparse = rola.rola_sparse_attn(q, k, v, bmap, w.grid, cfg)
@@ -129,7 +129,7 @@ def test_complement_full_size_sampled():
     name = "wan14b_720p"
     say("complement full size", name)
     w, (q, k, v), (wq, wk) = _full_inputs(name)
-    bmap = torch.empty((w.batch, w.heads, w.nb, w.kb), dtype=torch.int32, device="cuda")
+    bmap = torch.empty((w.batch, w.heads, w.nb, oracle.keep_blocks(w.topk, w.nb)), dtype=torch.int32, device="cuda")
     out = rola.rola_forward(dev(q), dev(k), dev(v), torch.from_numpy(wq).cuda(), torch.from_numpy(wk).cuda(),
                             w.grid, ccfg(w), block_idx_out=bmap)
     torch.cuda.synchronize()
@@ -137,7 +137,7 @@ def test_complement_full_size_sampled():
     rng = np.random.default_rng(11)
     worst = 0.0
     for h in (2, w.heads - 3):
-        m_ref = oracle.block_map(q[0, h:h + 1], k[0, h:h + 1], w.n_tokens, w.kb)
+        m_ref = oracle.block_map(q[0, h:h + 1], k[0, h:h + 1], w.n_tokens, oracle.keep_blocks(w.topk, w.nb))
         np.testing.assert_array_equal(bmap[0, h], m_ref[0])
         qbs = sorted({0, w.nb // 3, w.nb - 1, *rng.integers(0, w.nb, 3).tolist()})
         rows = np.array(sorted({n for qb in qbs for n in (qb * 64, qb * 64 + 33, qb * 64 + 63)

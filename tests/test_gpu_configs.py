@@ -29,14 +29,14 @@ def test_two_batches(fp8):
     say("two batches", "fp8" if fp8 else "bf16")
     q, k, v = W.make_qkv(w)
     wq, wk = W.make_proj(w)
-    bmap = torch.empty((w.batch, w.heads, w.nb, w.kb), dtype=torch.int32, device="cuda")
+    bmap = torch.empty((w.batch, w.heads, w.nb, oracle.keep_blocks(w.topk, w.nb)), dtype=torch.int32, device="cuda")
     cfg = rola.Config(topk=w.topk, rank=w.rank, out_dtype=rola.ROLA_OUT_F32,
                       precision=rola.ROLA_PREC_FP8 if fp8 else rola.ROLA_PREC_BF16)
     out = rola.rola_forward(dev(q), dev(k), dev(v), torch.from_numpy(wq).cuda(), torch.from_numpy(wk).cuda(),
                             w.grid, cfg, block_idx_out=bmap)
     torch.cuda.synchronize()
     flat = lambda x: x.reshape(w.batch * w.heads, w.n_pad, w.head_dim)
-    m_ref, o_ref = oracle.forward(flat(q), flat(k), flat(v), wq, wk, w.n_tokens, w.kb, w.grid, fp8=fp8)
+    m_ref, o_ref = oracle.forward(flat(q), flat(k), flat(v), wq, wk, w.n_tokens, oracle.keep_blocks(w.topk, w.nb), w.grid, fp8=fp8)
     np.testing.assert_array_equal(bmap.cpu().numpy().reshape(m_ref.shape), m_ref)
     got = host_f64(out).reshape(o_ref.shape)[:, :w.n_tokens]
     ref = o_ref[:, :w.n_tokens]
@@ -80,7 +80,7 @@ def test_full_keep_with_list_beyond_lds(fp8):
     say("full keep, list beyond LDS", "fp8" if fp8 else "bf16", "nb", w.nb)
     q, k, v = W.make_qkv(w)
     wq, wk = W.make_proj(w)
-    bmap = torch.empty((1, 1, w.nb, w.kb), dtype=torch.int32, device="cuda")
+    bmap = torch.empty((1, 1, w.nb, oracle.keep_blocks(w.topk, w.nb)), dtype=torch.int32, device="cuda")
     cfg = rola.Config(topk=1.0, rank=w.rank, out_dtype=rola.ROLA_OUT_F32,
                       precision=rola.ROLA_PREC_FP8 if fp8 else rola.ROLA_PREC_BF16)
     out = rola.rola_forward(dev(q), dev(k), dev(v), torch.from_numpy(wq).cuda(), torch.from_numpy(wk).cuda(),

@@ -74,12 +74,12 @@ def test_library_rule_codes_reproduce_the_fp8_forward(name, w):
     wq, wk = W.make_proj(w)
     (cq, sq), (ck, sk), (cv, sv) = (_rule_codes(w, x) for x in (q, k, v))
     cfg = fp8_cfg(w)
-    bmap = torch.empty((w.batch, w.heads, w.nb, w.kb), dtype=torch.int32, device="cuda")
+    bmap = torch.empty((w.batch, w.heads, w.nb, oracle.keep_blocks(w.topk, w.nb)), dtype=torch.int32, device="cuda")
     got = _call(w, q, k, v, (cq, ck, cv), (sq, sk, sv), cfg, bmap)
     ref = rola.rola_forward(dev(q), dev(k), dev(v), torch.from_numpy(wq).cuda(), torch.from_numpy(wk).cuda(),
                             w.grid, cfg)
     torch.cuda.synchronize()
-    m_ref = oracle.block_map(_flat(w, q), _flat(w, k), w.n_tokens, w.kb)
+    m_ref = oracle.block_map(_flat(w, q), _flat(w, k), w.n_tokens, oracle.keep_blocks(w.topk, w.nb))
     np.testing.assert_array_equal(bmap.cpu().numpy().reshape(m_ref.shape), m_ref)
     assert torch.equal(got, ref)
 
@@ -95,7 +95,7 @@ def test_other_rule_codes_match_oracle(name, w, out_f32):
     cfg = fp8_cfg(w, out_dtype=rola.ROLA_OUT_F32 if out_f32 else rola.ROLA_OUT_BF16)
     out = _call(w, q, k, v, (cq, ck, cv), (sq, sk, sv), cfg)
     got = host_f64(out).reshape(w.batch * w.heads, w.n_pad, w.head_dim)
-    bmap = oracle.block_map(_flat(w, q), _flat(w, k), w.n_tokens, w.kb)
+    bmap = oracle.block_map(_flat(w, q), _flat(w, k), w.n_tokens, oracle.keep_blocks(w.topk, w.nb))
     qf, kf, vf = (oracle.widen_bf16(_flat(w, x)) for x in (q, k, v))
     ref = np.zeros_like(got)
     for h in range(w.batch * w.heads):

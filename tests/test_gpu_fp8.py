@@ -49,13 +49,13 @@ def test_fp8_forward_matches_oracle(name, w, out_f32):
     say("fp8 forward", name, "f32out" if out_f32 else "bf16out")
     q, k, v = W.make_qkv(w)
     wq, wk = W.make_proj(w)
-    bmap = torch.empty((w.batch, w.heads, w.nb, w.kb), dtype=torch.int32, device="cuda")
+    bmap = torch.empty((w.batch, w.heads, w.nb, oracle.keep_blocks(w.topk, w.nb)), dtype=torch.int32, device="cuda")
     cfg = fp8_cfg(w, out_dtype=rola.ROLA_OUT_F32 if out_f32 else rola.ROLA_OUT_BF16)
     out = rola.rola_forward(dev(q), dev(k), dev(v), torch.from_numpy(wq).cuda(), torch.from_numpy(wk).cuda(),
                             w.grid, cfg, block_idx_out=bmap)
     torch.cuda.synchronize()
-    m8, o8 = oracle.forward(q[0], k[0], v[0], wq, wk, w.n_tokens, w.kb, w.grid, fp8=True)
-    m16, o16 = oracle.forward(q[0], k[0], v[0], wq, wk, w.n_tokens, w.kb, w.grid)
+    m8, o8 = oracle.forward(q[0], k[0], v[0], wq, wk, w.n_tokens, oracle.keep_blocks(w.topk, w.nb), w.grid, fp8=True)
+    m16, o16 = oracle.forward(q[0], k[0], v[0], wq, wk, w.n_tokens, oracle.keep_blocks(w.topk, w.nb), w.grid)
     np.testing.assert_array_equal(bmap.cpu().numpy()[0], m8)
     np.testing.assert_array_equal(m8, m16)
     got = host_f64(out[0])
@@ -106,7 +106,7 @@ def test_fp8_full_size_sampled(topk):
     from sparse_rank_attention_amd import rola
     torch = _torch()
     w, (q, k, v), (wq, wk) = _inputs720()
-    kb = W.keep_blocks(topk, w.nb)
+    kb = oracle.keep_blocks(topk, w.nb)
     say("fp8 full size 720p topk", topk, "kb", kb)
     bmap = torch.empty((w.batch, w.heads, w.nb, kb), dtype=torch.int32, device="cuda")
     cfg = rola.Config(topk=topk, rank=w.rank, precision=rola.ROLA_PREC_FP8)

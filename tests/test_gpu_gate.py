@@ -42,13 +42,13 @@ def test_gated_forward_matches_oracle(name, w, prec, out_f32):
     q, k, v = W.make_qkv(w)
     wq, wk = W.make_proj(w)
     g = W.make_gate(w)
-    bmap = torch.empty((w.batch, w.heads, w.nb, w.kb), dtype=torch.int32, device="cuda")
+    bmap = torch.empty((w.batch, w.heads, w.nb, oracle.keep_blocks(w.topk, w.nb)), dtype=torch.int32, device="cuda")
     cfg = cfg_of(w, out_dtype=rola.ROLA_OUT_F32 if out_f32 else rola.ROLA_OUT_BF16,
                  precision=rola.ROLA_PREC_FP8 if fp8 else rola.ROLA_PREC_BF16)
     out = rola.rola_forward(dev(q), dev(k), dev(v), torch.from_numpy(wq).cuda(), torch.from_numpy(wk).cuda(),
                             w.grid, cfg, block_idx_out=bmap, gate=_gate_dev(g))
     torch.cuda.synchronize()
-    m_ref, o_ref = oracle.forward(q[0], k[0], v[0], wq, wk, w.n_tokens, w.kb, w.grid, fp8=fp8, gate_w=g)
+    m_ref, o_ref = oracle.forward(q[0], k[0], v[0], wq, wk, w.n_tokens, oracle.keep_blocks(w.topk, w.nb), w.grid, fp8=fp8, gate_w=g)
     np.testing.assert_array_equal(bmap.cpu().numpy()[0], m_ref)
     got = host_f64(out)[0]
     assert np.all(got[:, w.n_tokens:] == 0)
@@ -69,8 +69,8 @@ def test_gated_lowrank_alone_and_accumulated(name, w):
     qd, kd, vd = dev(q), dev(k), dev(v)
     wqd, wkd, gd = torch.from_numpy(wq).cuda(), torch.from_numpy(wk).cuda(), _gate_dev(g)
     cfg = cfg_of(w, out_dtype=rola.ROLA_OUT_F32)
-    m_ref = oracle.block_map(q[0], k[0], w.n_tokens, w.kb)
-    bmap = torch.from_numpy(m_ref).cuda().reshape(w.batch, w.heads, w.nb, w.kb)
+    m_ref = oracle.block_map(q[0], k[0], w.n_tokens, oracle.keep_blocks(w.topk, w.nb))
+    bmap = torch.from_numpy(m_ref).cuda().reshape(w.batch, w.heads, w.nb, oracle.keep_blocks(w.topk, w.nb))
     o_lr = rola.rola_lowrank_attn(qd, kd, vd, wqd, wkd, w.grid, cfg, gate=gd)
     o_sum = rola.rola_sparse_attn(qd, kd, vd, bmap, w.grid, cfg)
     rola.rola_lowrank_attn(qd, kd, vd, wqd, wkd, w.grid, cfg, out=o_sum, accumulate=True, gate=gd)
@@ -103,7 +103,7 @@ def test_saturated_gates_are_exact(prec):
                  precision=rola.ROLA_PREC_FP8 if prec == "fp8" else rola.ROLA_PREC_BF16)
     g = np.zeros(w.head_dim + 1, dtype=np.float32)
     g[w.head_dim] = 800.0
-    bmap = torch.empty((w.batch, w.heads, w.nb, w.kb), dtype=torch.int32, device="cuda")
+    bmap = torch.empty((w.batch, w.heads, w.nb, oracle.keep_blocks(w.topk, w.nb)), dtype=torch.int32, device="cuda")
     plain = rola.rola_forward(q, k, v, wq, wk, w.grid, cfg, block_idx_out=bmap)
     open_ = rola.rola_forward(q, k, v, wq, wk, w.grid, cfg, gate=_gate_dev(g))
     g[w.head_dim] = -800.0
@@ -145,7 +145,7 @@ def test_gated_full_size_sampled():
     rng = np.random.default_rng(7)
     worst = 0.0
     for h in (1, w.heads - 2):
-        m_ref = oracle.block_map(q[0, h:h + 1], k[0, h:h + 1], w.n_tokens, w.kb)
+        m_ref = oracle.block_map(q[0, h:h + 1], k[0, h:h + 1], w.n_tokens, oracle.keep_blocks(w.topk, w.nb))
         qbs = sorted({0, w.nb - 1, *rng.integers(0, w.nb, 4).tolist()})
         rows = np.array(sorted({n for qb in qbs for n in (qb * 64, qb * 64 + 31, qb * 64 + 63)
                                 if n < w.n_tokens} | {w.n_tokens - 1}))

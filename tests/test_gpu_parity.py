@@ -83,7 +83,7 @@ def test_select_blocks_bit_exact(name, w):
     qp = oracle.pool(q.reshape(-1, w.n_pad, w.head_dim), w.n_tokens)
     kp = oracle.pool(k.reshape(-1, w.n_pad, w.head_dim), w.n_tokens)
     s_ref = oracle.scores(qp, kp)
-    m_ref = oracle.select(s_ref, w.kb)
+    m_ref = oracle.select(s_ref, oracle.keep_blocks(w.topk, w.nb))
     got_s = scores.cpu().numpy().reshape(s_ref.shape)
     assert np.array_equal(got_s.view(np.uint32), s_ref.view(np.uint32)), "pooled scores differ bitwise"
     np.testing.assert_array_equal(bmap.cpu().numpy().reshape(m_ref.shape), m_ref)
@@ -97,12 +97,12 @@ def test_forward_matches_oracle(name, w, out_f32):
     say("forward", name, "f32" if out_f32 else "bf16")
     q, k, v = W.make_qkv(w)
     wq, wk = W.make_proj(w)
-    bmap = torch.full((w.batch, w.heads, w.nb, w.kb), -1, dtype=torch.int32, device="cuda")
+    bmap = torch.full((w.batch, w.heads, w.nb, oracle.keep_blocks(w.topk, w.nb)), -1, dtype=torch.int32, device="cuda")
     cfg = cfg_of(w, out_dtype=rola.ROLA_OUT_F32 if out_f32 else rola.ROLA_OUT_BF16)
     out = rola.rola_forward(dev(q), dev(k), dev(v), torch.from_numpy(wq).cuda(), torch.from_numpy(wk).cuda(),
                             w.grid, cfg, block_idx_out=bmap)
     torch.cuda.synchronize()
-    m_ref, o_ref = oracle.forward(q[0], k[0], v[0], wq, wk, w.n_tokens, w.kb, w.grid)
+    m_ref, o_ref = oracle.forward(q[0], k[0], v[0], wq, wk, w.n_tokens, oracle.keep_blocks(w.topk, w.nb), w.grid)
     np.testing.assert_array_equal(bmap.cpu().numpy()[0], m_ref)
     got = host_f64(out)[0]
     assert np.all(got[:, w.n_tokens:] == 0)
@@ -122,8 +122,8 @@ def test_branches_alone_and_composed(name, w):
     qd, kd, vd = dev(q), dev(k), dev(v)
     wqd, wkd = torch.from_numpy(wq).cuda(), torch.from_numpy(wk).cuda()
     cfg = cfg_of(w, out_dtype=rola.ROLA_OUT_F32)
-    m_ref = oracle.block_map(q[0], k[0], w.n_tokens, w.kb)
-    bmap = torch.from_numpy(m_ref).cuda().reshape(w.batch, w.heads, w.nb, w.kb)
+    m_ref = oracle.block_map(q[0], k[0], w.n_tokens, oracle.keep_blocks(w.topk, w.nb))
+    bmap = torch.from_numpy(m_ref).cuda().reshape(w.batch, w.heads, w.nb, oracle.keep_blocks(w.topk, w.nb))
     o_sp = rola.rola_sparse_attn(qd, kd, vd, bmap, w.grid, cfg)
     o_lr = rola.rola_lowrank_attn(qd, kd, vd, wqd, wkd, w.grid, cfg)
     o_sum = rola.rola_sparse_attn(qd, kd, vd, bmap, w.grid, cfg)
@@ -231,7 +231,7 @@ def test_full_size_sampled(name):
     torch = _torch()
     say("full size", name)
     w, (q, k, v), (wq, wk) = _full_inputs(name)
-    bmap = torch.empty((w.batch, w.heads, w.nb, w.kb), dtype=torch.int32, device="cuda")
+    bmap = torch.empty((w.batch, w.heads, w.nb, oracle.keep_blocks(w.topk, w.nb)), dtype=torch.int32, device="cuda")
     out = rola.rola_forward(dev(q), dev(k), dev(v), torch.from_numpy(wq).cuda(), torch.from_numpy(wk).cuda(),
                             w.grid, cfg_of(w), block_idx_out=bmap)
     torch.cuda.synchronize()
@@ -240,7 +240,7 @@ def test_full_size_sampled(name):
     heads = sorted({0, w.heads // 2, w.heads - 1})
     worst = 0.0
     for h in heads:
-        m_ref = oracle.block_map(q[0, h:h + 1], k[0, h:h + 1], w.n_tokens, w.kb)
+        m_ref = oracle.block_map(q[0, h:h + 1], k[0, h:h + 1], w.n_tokens, oracle.keep_blocks(w.topk, w.nb))
         np.testing.assert_array_equal(bmap[0, h], m_ref[0], err_msg="head %d" % h)
         qbs = sorted({0, 1, w.nb // 2, w.nb - 1, *rng.integers(0, w.nb, 4).tolist()})
         rows = []

@@ -49,9 +49,9 @@ CASES = [("equal_scores", 100, 0.25), ("equal_scores", 150, 0.25), ("equal_score
 def test_select_blocks_with_ties(kind, nb, topk):
     from sparse_rank_attention_amd import rola
     w, q, k = _case(kind, nb, topk, seed=nb)
-    say("ties", kind, "nb", w.nb, "kb", w.kb)
+    say("ties", kind, "nb", w.nb, "kb", oracle.keep_blocks(w.topk, w.nb))
     bmap = rola.rola_select_blocks(dev(q), dev(k), w.grid, rola.Config(topk=w.topk, rank=w.rank))
     qp = oracle.pool(q.reshape(-1, w.n_pad, w.head_dim), w.n_tokens)
     kp = oracle.pool(k.reshape(-1, w.n_pad, w.head_dim), w.n_tokens)
-    m_ref = oracle.select(oracle.scores(qp, kp), w.kb)
+    m_ref = oracle.select(oracle.scores(qp, kp), oracle.keep_blocks(w.topk, w.nb))
     np.testing.assert_array_equal(bmap.cpu().numpy().reshape(m_ref.shape), m_ref)

@@ -9,6 +9,8 @@ import json
 import os
 
 import numpy as np
+
+import oracle
 import pytest
 import torch
 
@@ -190,7 +192,7 @@ def test_forward_constant_v_gives_twice_constant(oracle_lib):
     wq, wk = make_proj(w)
     n_valid = w.n_tokens - 37  # exercise a ragged tail with padding
     v = np.full(q.shape, to_bf16_bits(np.array([-1.25], dtype=np.float32))[0], dtype=np.uint16)
-    bmap, out = oracle_lib.forward(q[0], k[0], v[0], wq, wk, n_valid, w.kb, w.grid)
+    bmap, out = oracle_lib.forward(q[0], k[0], v[0], wq, wk, n_valid, oracle.keep_blocks(w.topk, w.nb), w.grid)
     np.testing.assert_allclose(out[:, :n_valid], -2.5, rtol=1e-12)
     assert np.all(out[:, n_valid:] == 0)
 
@@ -200,8 +202,8 @@ def test_forward_is_sum_of_pinned_parts(oracle_lib):
     w = WORKLOADS["tiny"]
     q, k, v = (x[0] for x in make_qkv(w))
     wq, wk = make_proj(w)
-    bmap, out = oracle_lib.forward(q, k, v, wq, wk, w.n_tokens, w.kb, w.grid)
-    np.testing.assert_array_equal(bmap, oracle_lib.block_map(q, k, w.n_tokens, w.kb))
+    bmap, out = oracle_lib.forward(q, k, v, wq, wk, w.n_tokens, oracle.keep_blocks(w.topk, w.nb), w.grid)
+    np.testing.assert_array_equal(bmap, oracle_lib.block_map(q, k, w.n_tokens, oracle.keep_blocks(w.topk, w.nb)))
     qd, kd, vd = (oracle_lib.widen_bf16(x) for x in (q, k, v))
     rows = np.arange(q.shape[0] * w.n_pad)
     sp = oracle_lib.sparse_rows(qd, kd, vd, bmap, w.n_tokens, rows)
@@ -241,7 +243,7 @@ def test_forward_gate_scales_only_the_lowrank_term(oracle_lib):
     d = w.head_dim
     n_valid = w.n_tokens - 37
     qd, kd, vd = (oracle_lib.widen_bf16(x) for x in (q, k, v))
-    bmap, plain = oracle_lib.forward(q, k, v, wq, wk, n_valid, w.kb, w.grid)
+    bmap, plain = oracle_lib.forward(q, k, v, wq, wk, n_valid, oracle.keep_blocks(w.topk, w.nb), w.grid)
     rows = np.arange(q.shape[0] * w.n_pad)
     sp = oracle_lib.sparse_rows(qd, kd, vd, bmap, n_valid, rows)
     S, z = oracle_lib.lowrank_state(kd, vd, wk, n_valid, w.grid)
@@ -250,20 +252,20 @@ def test_forward_gate_scales_only_the_lowrank_term(oracle_lib):
     # a saturated gate is exactly the ungated forward; a shut one leaves the sparse branch alone
     g = np.zeros(d + 1, dtype=np.float32)
     g[d] = 800.0
-    _, out = oracle_lib.forward(q, k, v, wq, wk, n_valid, w.kb, w.grid, gate_w=g)
+    _, out = oracle_lib.forward(q, k, v, wq, wk, n_valid, oracle.keep_blocks(w.topk, w.nb), w.grid, gate_w=g)
     np.testing.assert_array_equal(out, plain)
     g[d] = -800.0
-    _, out = oracle_lib.forward(q, k, v, wq, wk, n_valid, w.kb, w.grid, gate_w=g)
+    _, out = oracle_lib.forward(q, k, v, wq, wk, n_valid, oracle.keep_blocks(w.topk, w.nb), w.grid, gate_w=g)
     np.testing.assert_allclose(out.reshape(-1, d)[valid], sp[valid], rtol=1e-12, atol=1e-14)
     # constant gate 3/4
     g[d] = np.float32(np.log(3.0))
-    _, out = oracle_lib.forward(q, k, v, wq, wk, n_valid, w.kb, w.grid, gate_w=g)
+    _, out = oracle_lib.forward(q, k, v, wq, wk, n_valid, oracle.keep_blocks(w.topk, w.nb), w.grid, gate_w=g)
     gv = 1.0 / (1.0 + np.exp(-np.float64(g[d])))
     np.testing.assert_allclose(out.reshape(-1, d)[valid], (sp + gv * lr)[valid], rtol=1e-12, atol=1e-14)
     # a per-token gate reads the token's own unrotated query: one weight on component 5
     g = np.zeros(d + 1, dtype=np.float32)
     g[5], g[d] = 1.5, -0.25
-    _, out = oracle_lib.forward(q, k, v, wq, wk, n_valid, w.kb, w.grid, gate_w=g)
+    _, out = oracle_lib.forward(q, k, v, wq, wk, n_valid, oracle.keep_blocks(w.topk, w.nb), w.grid, gate_w=g)
     qf = qd.reshape(-1, d)
     gt = torch.sigmoid(torch.tensor(1.5 * qf[:, 5] - 0.25)).numpy()[:, None]
     np.testing.assert_allclose(out.reshape(-1, d)[valid], (sp + gt * lr)[valid], rtol=1e-12, atol=1e-14)
@@ -376,7 +378,7 @@ def test_forward_complement_scope(oracle_lib):
     wq, wk = make_proj(w)
     n_valid = w.n_tokens - 37
     cval = to_bf16_bits(np.array([0.75], dtype=np.float32))[0]
-    _, out = oracle_lib.forward(q, k, np.full_like(v, cval), wq, wk, n_valid, w.kb, w.grid, complement=True)
+    _, out = oracle_lib.forward(q, k, np.full_like(v, cval), wq, wk, n_valid, oracle.keep_blocks(w.topk, w.nb), w.grid, complement=True)
     np.testing.assert_allclose(out[:, :n_valid], 1.5, rtol=1e-12)
     qd, kd, vd = (oracle_lib.widen_bf16(x) for x in (q, k, v))
     bmap, out = oracle_lib.forward(q, k, v, wq, wk, n_valid, w.nb, w.grid, complement=True)
@@ -385,7 +387,7 @@ def test_forward_complement_scope(oracle_lib):
     sp = oracle_lib.sparse_rows(qd, kd, vd, bmap, n_valid, rows)
     np.testing.assert_allclose(out.reshape(-1, w.head_dim)[valid], sp[valid], rtol=1e-12, atol=1e-14)
     g = (np.arange(w.head_dim + 1) % 5 - 2).astype(np.float32) / 8
-    bmap, out = oracle_lib.forward(q, k, v, wq, wk, n_valid, w.kb, w.grid, complement=True, gate_w=g)
+    bmap, out = oracle_lib.forward(q, k, v, wq, wk, n_valid, oracle.keep_blocks(w.topk, w.nb), w.grid, complement=True, gate_w=g)
     sp = oracle_lib.sparse_rows(qd, kd, vd, bmap, n_valid, rows)
     for bh in range(q.shape[0]):
         Sb, zb = oracle_lib.lowrank_block_states(kd[bh], vd[bh], wk, n_valid, w.grid)

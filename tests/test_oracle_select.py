@@ -9,6 +9,8 @@ import json
 import os
 
 import numpy as np
+
+import oracle
 import pytest
 
 from sparse_rank_attention_amd.workloads import to_bf16_bits
@@ -151,7 +153,7 @@ def test_block_map_invariant_to_power_of_two_scaling(oracle_lib):
     w = WORKLOADS["tiny"]
     q, k, _ = make_qkv(w)
     q, k = q[0], k[0]
-    m = oracle_lib.block_map(q, k, w.n_tokens, w.kb)
+    m = oracle_lib.block_map(q, k, w.n_tokens, oracle.keep_blocks(w.topk, w.nb))
     qf = (q.astype(np.uint32) << 16).view(np.float32)
-    m2 = oracle_lib.block_map(to_bf16_bits(qf * 4), k, w.n_tokens, w.kb)
+    m2 = oracle_lib.block_map(to_bf16_bits(qf * 4), k, w.n_tokens, oracle.keep_blocks(w.topk, w.nb))
     np.testing.assert_array_equal(m, m2)

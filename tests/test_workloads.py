@@ -33,13 +33,6 @@ def test_bf16_rounding_ties_to_even():
     np.testing.assert_array_equal(b, np.array([1.0, 1.0 + 2.0 ** -6, 1.0], dtype=np.float32))
 
 
-def test_keep_blocks_table():
-    assert W.WORKLOADS["tiny"].kb == 4
-    assert W.WORKLOADS["wan13b_480p"].kb == 51
-    assert W.WORKLOADS["wan14b_480p"].kb == 25
-    assert W.WORKLOADS["wan14b_720p"].kb == 35 and W.WORKLOADS["wan14b_720p"].nb == 1182
-
-
 def test_linear_inputs_regenerate_by_rows():
     """Sampled rows of the w8a8 activations equal the same rows of the whole
     matrix (chunked seeding), and the weights are reproducible."""
