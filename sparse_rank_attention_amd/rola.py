@@ -153,12 +153,19 @@ def plan(prob: RolaProblem, cfg: Config) -> RolaPlanInfo:
 _ws_cache = {}
 
 
-def workspace(device, nbytes: int) -> torch.Tensor:
-    """Caller-owned scratch for librola (cached per device; grows on demand)."""
-    key = torch.device(device).index
+def workspace(device, nbytes: int, stream=None) -> torch.Tensor:
+    """Caller-owned scratch for librola, cached per (device, stream) and grown on
+    demand.  It is allocated on the stream the calls run on, so PyTorch's caching
+    allocator reuses a replaced buffer only after that stream's queued kernels,
+    and calls on different streams never share one."""
+    dev = torch.device(device)
+    s = torch.cuda.current_stream(dev) if stream is None else stream
+    key = (dev.index, s.cuda_stream)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
-        buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _ws_cache.pop(key, None)
+        with torch.cuda.stream(s):
+            buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
         _ws_cache[key] = buf
     return buf
 
@@ -168,13 +175,51 @@ def _ptr(t):
 
 
 def _check_tokens(q, *others):
-    if not q.is_cuda:
-        raise RolaError("librola needs GPU tensors")
     for t in (q,) + others:
+        if t.dim() != 4:
+            raise RolaError("q, k, v must be [B, H, n_pad, D] views")
         if t.dtype != torch.bfloat16:
             raise RolaError("q, k, v must be bfloat16")
         if t.shape != q.shape or t.stride() != q.stride() or t.device != q.device:
             raise RolaError("q, k, v must share shape, strides and device")
+
+
+def _require_gpu(q):
+    """Checked after every argument, before the workspace and the call."""
+    if not q.is_cuda:
+        raise RolaError("librola needs GPU tensors")
+
+
+def _check_planned(q, info: RolaPlanInfo):
+    """The library addresses rows 0..n_pad-1 of every token tensor."""
+    if q.shape[2] != info.n_pad:
+        raise RolaError("q, k, v hold %d rows; the grid needs n_pad = %d (64 * ceil(N / 64)), "
+                        "rows N..n_pad-1 being padding" % (q.shape[2], info.n_pad))
+
+
+def _check_out(out, q, cfg: Config):
+    want = torch.float32 if cfg.out_dtype == ROLA_OUT_F32 else torch.bfloat16
+    if out.dtype != want:
+        raise RolaError("out must be %s for this out_dtype" % want)
+    if out.shape != q.shape or out.stride() != q.stride() or out.device != q.device:
+        raise RolaError("out must have the shape, strides and device of q")
+
+
+def _check_proj(q, cfg: Config, *ws):
+    D = q.shape[-1]
+    for w in ws:
+        if w.dtype != torch.float32 or tuple(w.shape) != (D, cfg.rank) or not w.is_contiguous() \
+                or w.device != q.device:
+            raise RolaError("wq and wk must be contiguous float32 [head_dim, rank] = [%d, %d] tensors "
+                            "on the device of q" % (D, cfg.rank))
+
+
+def _check_map(block_idx, q, info: RolaPlanInfo, name="block_idx"):
+    B, H = q.shape[:2]
+    if block_idx.dtype != torch.int32 or tuple(block_idx.shape) != (B, H, info.nb, info.kb) \
+            or not block_idx.is_contiguous() or block_idx.device != q.device:
+        raise RolaError("%s must be a contiguous int32 [B, H, nb, kb] = [%d, %d, %d, %d] tensor on the "
+                        "device of q" % (name, B, H, info.nb, info.kb))
 
 
 def _stream(stream):
@@ -192,10 +237,17 @@ def rola_select_blocks(q, k, grid, cfg: Config, block_idx=None, pooled_scores=No
     _check_tokens(q, k)
     prob = problem(q, grid)
     info = plan(prob, cfg)
+    _check_planned(q, info)
     B, H = q.shape[:2]
     if block_idx is None:
         block_idx = torch.empty((B, H, info.nb, info.kb), dtype=torch.int32, device=q.device)
-    ws = workspace(q.device, info.workspace_bytes)
+    _check_map(block_idx, q, info)
+    if pooled_scores is not None and (pooled_scores.dtype != torch.float32 or not pooled_scores.is_contiguous()
+                                      or tuple(pooled_scores.shape) != (B, H, info.nb, info.nb)
+                                      or pooled_scores.device != q.device):
+        raise RolaError("pooled_scores must be a contiguous float32 [B, H, nb, nb] tensor on the device of q")
+    _require_gpu(q)
+    ws = workspace(q.device, info.workspace_bytes, stream)
     c = cfg.c()
     _check(lib().rola_select_blocks(ctypes.byref(prob), ctypes.byref(c), _ptr(q), _ptr(k), _ptr(block_idx),
                                     _ptr(pooled_scores), _ptr(ws), ws.numel(), _stream(stream)),
@@ -207,8 +259,12 @@ def rola_sparse_attn(q, k, v, block_idx, grid, cfg: Config, out=None, accumulate
     _check_tokens(q, k, v)
     prob = problem(q, grid)
     info = plan(prob, cfg)
+    _check_planned(q, info)
+    _check_map(block_idx, q, info)
     out = _new_out(q, cfg) if out is None else out
-    ws = workspace(q.device, info.workspace_bytes)
+    _check_out(out, q, cfg)
+    _require_gpu(q)
+    ws = workspace(q.device, info.workspace_bytes, stream)
     c = cfg.c()
     _check(lib().rola_sparse_attn(ctypes.byref(prob), ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v),
                                   _ptr(block_idx), _ptr(out), int(bool(accumulate)), _ptr(ws), ws.numel(),
@@ -233,8 +289,12 @@ def rola_lowrank_attn(q, k, v, wq, wk, grid, cfg: Config, out=None, accumulate=F
     _check_gate(gate, q)
     prob = problem(q, grid)
     info = plan(prob, cfg)
+    _check_planned(q, info)
+    _check_proj(q, cfg, wq, wk)
     out = _new_out(q, cfg) if out is None else out
-    ws = workspace(q.device, info.workspace_bytes)
+    _check_out(out, q, cfg)
+    _require_gpu(q)
+    ws = workspace(q.device, info.workspace_bytes, stream)
     c = cfg.c()
     _check(lib().rola_lowrank_attn(ctypes.byref(prob), ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(wq),
                                    _ptr(wk), _ptr(gate), _ptr(out), int(bool(accumulate)), _ptr(ws), ws.numel(),
@@ -249,8 +309,14 @@ def rola_forward(q, k, v, wq, wk, grid, cfg: Config, out=None, block_idx_out=Non
     _check_gate(gate, q)
     prob = problem(q, grid)
     info = plan(prob, cfg)
+    _check_planned(q, info)
+    _check_proj(q, cfg, wq, wk)
+    if block_idx_out is not None:
+        _check_map(block_idx_out, q, info, "block_idx_out")
     out = _new_out(q, cfg) if out is None else out
-    ws = workspace(q.device, info.workspace_bytes)
+    _check_out(out, q, cfg)
+    _require_gpu(q)
+    ws = workspace(q.device, info.workspace_bytes, stream)
     c = cfg.c()
     _check(lib().rola_forward(ctypes.byref(prob), ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(wq),
                               _ptr(wk), _ptr(gate), _ptr(block_idx_out), _ptr(out), _ptr(ws), ws.numel(),
@@ -272,13 +338,19 @@ def rola_forward_e4m3(q, k, v, q8, k8, v8, qs, ks, vs, wq, wk, grid, cfg: Config
             raise RolaError("q8, k8, v8 must be uint8 codes with the shape and strides of q")
     prob = problem(q, grid)
     info = plan(prob, cfg)
+    _check_planned(q, info)
+    _check_proj(q, cfg, wq, wk)
     B, H = q.shape[:2]
     for t in (qs, ks, vs):
         if t.dtype != torch.float32 or tuple(t.shape) != (B, H, info.nb) or not t.is_contiguous() \
                 or t.device != q.device:
             raise RolaError("qs, ks, vs must be contiguous float32 [B, H, nb] on the device of q")
+    if block_idx_out is not None:
+        _check_map(block_idx_out, q, info, "block_idx_out")
     out = _new_out(q, cfg) if out is None else out
-    ws = workspace(q.device, info.workspace_bytes)
+    _check_out(out, q, cfg)
+    _require_gpu(q)
+    ws = workspace(q.device, info.workspace_bytes, stream)
     c = cfg.c()
     _check(lib().rola_forward_e4m3(ctypes.byref(prob), ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(q8),
                                    _ptr(k8), _ptr(v8), _ptr(qs), _ptr(ks), _ptr(vs), _ptr(wq), _ptr(wk),
@@ -295,20 +367,21 @@ def rola_backward(q, k, v, wq, wk, grid, cfg: Config, block_idx, dout, gate=None
     _check_tokens(q, k, v)
     _check_gate(gate, q)
     want = torch.float32 if cfg.out_dtype == ROLA_OUT_F32 else torch.bfloat16
-    if dout.dtype != want or dout.shape != q.shape or dout.stride() != q.stride():
+    if dout.dtype != want or dout.shape != q.shape or dout.stride() != q.stride() or dout.device != q.device:
         raise RolaError("dout must have the output dtype and the layout of q")
     prob = problem(q, grid)
     info = plan(prob, cfg)
+    _check_planned(q, info)
+    _check_proj(q, cfg, wq, wk)
+    _check_map(block_idx, q, info)
     B, H, _, D = q.shape
-    if block_idx.dtype != torch.int32 or tuple(block_idx.shape) != (B, H, info.nb, info.kb) \
-            or not block_idx.is_contiguous():
-        raise RolaError("block_idx must be a contiguous int32 [B, H, nb, kb] map")
     dq, dk, dv = (torch.empty_strided(q.shape, q.stride(), dtype=torch.bfloat16, device=q.device)
                   for _ in range(3))
     dwq = torch.empty((D, cfg.rank), dtype=torch.float32, device=q.device)
     dwk = torch.empty((D, cfg.rank), dtype=torch.float32, device=q.device)
     dgate = torch.empty(D + 1, dtype=torch.float32, device=q.device) if gate is not None else None
-    ws = workspace(q.device, info.workspace_bytes_backward)
+    _require_gpu(q)
+    ws = workspace(q.device, info.workspace_bytes_backward, stream)
     c = cfg.c()
     _check(lib().rola_backward(ctypes.byref(prob), ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(wq),
                                _ptr(wk), _ptr(gate), _ptr(block_idx), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
