@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define ROLA_ABI_VERSION 6
+#define ROLA_ABI_VERSION 7
 #define ROLA_BLOCK 64
 #define ROLA_MAX_BLOCKS 4096 /* nb limit: N <= 262144 tokens */
 
@@ -187,6 +187,23 @@ int32_t rola_forward_e4m3(const rola_problem *prob, const rola_config *cfg, cons
                           const uint8_t *v8, const float *qs, const float *ks, const float *vs,
                           const float *wq, const float *wk, const float *gate, int32_t *block_idx_out,
                           void *out, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * rola_forward without a caller workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops and
+ * harnesses that forbid hipMalloc.  The library keeps one scratch array of
+ * ROLA_NOALLOC_SCRATCH_BYTES (128 MiB) per GPU, held from the first call on
+ * that GPU until the process ends; the call allocates and frees nothing.
+ * Arguments and behaviour are those of rola_forward; problems whose
+ * workspace (rola_plan's workspace_bytes) exceeds the scratch return
+ * ROLA_ERR_WORKSPACE and launch nothing.  The scratch belongs to the GPU of
+ * `stream`; all calls on one GPU share it, so calls that overlap on one GPU
+ * (two streams, two threads) race and must be serialised by the caller.
+ */
+#define ROLA_NOALLOC_SCRATCH_BYTES (128u << 20)
+int32_t rola_forward_noalloc(const rola_problem *prob, const rola_config *cfg, const void *q,
+                             const void *k, const void *v, const float *wq, const float *wk,
+                             const float *gate, int32_t *block_idx_out, void *out, void *stream);
 
 /*
  * Backward of rola_forward (training; the README "AlibabaResearch/

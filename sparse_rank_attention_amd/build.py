@@ -9,7 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "librola.so")
 SOURCES = [os.path.join(CSRC, "rola_kernels.hip"), os.path.join(CSRC, "rola_backward.hip"),
-           os.path.join(CSRC, "rola_gemm.hip"),
+           os.path.join(CSRC, "rola_gemm.hip"), os.path.join(CSRC, "rola_noalloc.hip"),
            os.path.join(CSRC, "rola_api.cpp")]
 HEADERS = [os.path.join(CSRC, "rola_internal.h"), os.path.join(CSRC, "rola_device.h"),
            os.path.join(os.path.dirname(PKG), "include", "rola.h")]

@@ -47,12 +47,13 @@ class RolaKernelTime(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_int32), ("total_ms", ctypes.c_double)]
 
 
-ABI_VERSION = 6  # ROLA_ABI_VERSION of include/rola.h
+ABI_VERSION = 7  # ROLA_ABI_VERSION of include/rola.h
+NOALLOC_SCRATCH_BYTES = 128 << 20  # ROLA_NOALLOC_SCRATCH_BYTES
 
 EXPORTS = ["rola_abi_version", "rola_status_str", "rola_plan", "rola_select_blocks",
            "rola_sparse_attn", "rola_lowrank_attn", "rola_forward", "rola_backward", "rola_timing_enable",
            "rola_timing_read", "rola_mfma_probe", "rola_quant_rows", "rola_gemm_w8a8",
-           "rola_forward_e4m3"]
+           "rola_forward_e4m3", "rola_forward_noalloc"]
 
 _lib = None
 
@@ -97,6 +98,8 @@ def lib():
         L.rola_quant_rows.argtypes = [P, I64, I64, I64, P, I64, P, P]
         L.rola_gemm_w8a8.restype = I32
         L.rola_gemm_w8a8.argtypes = [P, I64, P, P, I64, P, P, I64, I32, I32, P, I64, I32, P]
+        L.rola_forward_noalloc.restype = I32
+        L.rola_forward_noalloc.argtypes = [P] * 11
         L.rola_forward_e4m3.restype = I32
         L.rola_forward_e4m3.argtypes = [P] * 17 + [ctypes.c_size_t, P]
         if L.rola_abi_version() != ABI_VERSION:
@@ -321,6 +324,30 @@ def rola_forward(q, k, v, wq, wk, grid, cfg: Config, out=None, block_idx_out=Non
     _check(lib().rola_forward(ctypes.byref(prob), ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(wq),
                               _ptr(wk), _ptr(gate), _ptr(block_idx_out), _ptr(out), _ptr(ws), ws.numel(),
                               _stream(stream)), "rola_forward")
+    return out
+
+
+def rola_forward_noalloc(q, k, v, wq, wk, grid, cfg: Config, out, block_idx_out=None, stream=None, gate=None):
+    """rola_forward on the library's own per-GPU scratch (no workspace): ``out``
+    is required, so the call itself allocates nothing.  Problems whose
+    workspace exceeds the scratch (NOALLOC_SCRATCH_BYTES) raise RolaError."""
+    _check_tokens(q, k, v)
+    _check_gate(gate, q)
+    prob = problem(q, grid)
+    info = plan(prob, cfg)
+    _check_planned(q, info)
+    _check_proj(q, cfg, wq, wk)
+    if block_idx_out is not None:
+        _check_map(block_idx_out, q, info, "block_idx_out")
+    _check_out(out, q, cfg)
+    if info.workspace_bytes > NOALLOC_SCRATCH_BYTES:
+        raise RolaError("rola_forward_noalloc: this problem needs %d workspace bytes, above the %d-byte "
+                        "scratch" % (info.workspace_bytes, NOALLOC_SCRATCH_BYTES))
+    _require_gpu(q)
+    c = cfg.c()
+    _check(lib().rola_forward_noalloc(ctypes.byref(prob), ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(wq),
+                                      _ptr(wk), _ptr(gate), _ptr(block_idx_out), _ptr(out), _stream(stream)),
+           "rola_forward_noalloc")
     return out
 
 

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     for name in _declared_functions():
         assert hasattr(L, name), name
     assert set(rola.EXPORTS) == set(_declared_functions())
-    assert L.rola_abi_version() == rola.ABI_VERSION == 6
+    assert L.rola_abi_version() == rola.ABI_VERSION == 7
 
 
 def _prob(B=1, H=40, D=128, grid=(21, 45, 80), sn=None):
