@@ -1121,7 +1121,7 @@ static __device__ __forceinline__ void attn_finish(const AttnArgs &args, const b
 // fp32 weights and each weight enters the PV product as a bf16 pair hi + lo,
 // so that O and the log-sum-exp agree with fp32 weights to about 16 bits.
 template <int D, int G, int S, bool SPARSE, bool LOWRANK, bool ACCUM, bool OUTF32, bool EXACT = false>
-__global__ __launch_bounds__(128 * G) void k_attn(AttnArgs args) {
+__global__ __launch_bounds__(128 * G, 2) void k_attn(AttnArgs args) {
   constexpr int CH = D / 8;
   constexpr int NS = D / 16;  // k-steps over head_dim
   constexpr int DT = D / 32;  // output d-tiles
@@ -1131,6 +1131,10 @@ __global__ __launch_bounds__(128 * G) void k_attn(AttnArgs args) {
   static_assert(OPS >= 1 && (64 * CH) % NT == 0, "tile split");
   static_assert(S == 2 || S == 4, "ring depth");
   constexpr int LMAX = 2048;  // union-list entries staged in LDS (longer lists read the tail from HBM)
+#ifndef ROLA_ATTN_HALVES
+#define ROLA_ATTN_HALVES 0
+#endif
+  constexpr bool HALVES = ROLA_ATTN_HALVES != 0;
   __shared__ __attribute__((aligned(1024))) uint16_t ring[SPARSE ? S * 2 * TILE : 8];
   __shared__ int32_t slist[SPARSE ? LMAX + 8 : 4];  // + room for the reads ahead past the end
   __shared__ __attribute__((aligned(16))) float sfreq[D / 2];  // rotary inverse frequency per pair
@@ -1355,6 +1359,114 @@ __global__ __launch_bounds__(128 * G) void k_attn(AttnArgs args) {
         }
         l_run += psum;
       };
+      // The same tile with its two 32-key halves pipelined inside the wave:
+      // S of half B is issued under the softmax of half A, and the PV product
+      // of half A under the softmax of half B, so the wave has independent
+      // MFMA and VALU work side by side.  The weights of a half are formed
+      // speculatively with the current reference; when the half's max grows
+      // the reference (rare after the first tile), O and l are rescaled and
+      // the half's weights formed again.
+      auto tile_h = [&](int t, int ent) __attribute__((always_inline)) {
+        const int j = ent & 0xffff;
+        const uint16_t *sK = ring + (t % S) * (2 * TILE);
+        const uint16_t *sV = sK + TILE;
+        const bool tail = (int64_t)(j + 1) * 64 > args.n_tokens;
+        const int lim = (int)(args.n_tokens - (int64_t)j * 64) - 4 * g;
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+        // weights of one half (16 accumulator values -> two 8-key steps) and their sum
+        auto weights = [&](const f32x16 &src, bf16x8 (&pw)[2]) __attribute__((always_inline)) -> float {
+          const float negm = -m_run;
+          float ps = 0.0f;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pw[h][e] = (__bf16)fast_exp2(__builtin_fmaf(src[8 * h + e], c, negm));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const bf16x2 pr = {pw[h][2 * e], pw[h][2 * e + 1]};
+              ps = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ps, false);
+            }
+          }
+          return ps;
+        };
+        auto half_max = [&](const f32x16 &src) __attribute__((always_inline)) -> float {
+          float a = fmaxf(src[0], src[1]), b = fmaxf(src[2], src[3]);
+#pragma unroll
+          for (int i = 4; i < 16; i += 4) {
+            a = fmaxf(a, fmaxf(src[i], src[i + 1]));
+            b = fmaxf(b, fmaxf(src[i + 2], src[i + 3]));
+          }
+          return pair_max32(fmaxf(a, b)) * c;
+        };
+        // the reference moves when the half's max exceeds it by more than 64;
+        // returns true when it moved (O and l rescaled)
+        auto settle = [&](float mx) __attribute__((always_inline)) -> bool {
+          const bool grow = mx > m_run + 64.0f;
+          if (__builtin_amdgcn_ballot_w64(grow)) {
+            const float m_new = grow ? ceilf(mx) : m_run;
+            const float alpha = fast_exp2(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+            return true;
+          }
+          return false;
+        };
+        auto pv_step = [&](int s, const bf16x8 &pw) __attribute__((always_inline)) {
+          bf16x8 va[DT];
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) va[dt] = vt_operand_at(sV + voff[dt] + s * 16 * D, 8 * D);
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) oacc[dt] = mfma_bf16(va[dt], pw, oacc[dt]);
+        };
+        // ---- S of half A (keys 0-31)
+        f32x16 sa = f32x16{}, sb = f32x16{};
+        {
+          bf16x8 ka[NS];
+#pragma unroll
+          for (int s2 = 0; s2 < NS; ++s2) ka[s2] = *(const bf16x8 *)(sK + koff[s2]);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int s2 = 0; s2 < NS; ++s2) sa = mfma_bf16(ka[s2], qreg[s2], sa);
+        }
+        bf16x8 kb2[NS];
+#pragma unroll
+        for (int s2 = 0; s2 < NS; ++s2) kb2[s2] = *(const bf16x8 *)(sK + koff[s2] + 32 * D);
+        if (tail) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (8 * (i >> 2) + (i & 3) >= lim) sa[i] = -INFINITY;
+        }
+        // ---- S of half B under the softmax of half A
+#pragma unroll
+        for (int s2 = 0; s2 < NS; ++s2) sb = mfma_bf16(kb2[s2], qreg[s2], sb);
+        bf16x8 pa[2];
+        const float mxa = half_max(sa);
+        float psa = weights(sa, pa);
+        // the speculative weights are formed here, under the S MFMAs of half B,
+        // even though the rare growth path below forms them again
+        asm volatile("" ::"v"(pa[0]), "v"(pa[1]), "v"(psa));
+        if (settle(mxa)) psa = weights(sa, pa);
+        l_run += psa;
+        if (tail) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (8 * (i >> 2) + (i & 3) + 32 >= lim) sb[i] = -INFINITY;
+        }
+        // ---- PV of half A under the softmax of half B
+        pv_step(0, pa[0]);
+        pv_step(1, pa[1]);
+        bf16x8 pb[2];
+        const float mxb = half_max(sb);
+        float psb = weights(sb, pb);
+        asm volatile("" ::"v"(pb[0]), "v"(pb[1]), "v"(psb));
+        if (settle(mxb)) psb = weights(sb, pb);
+        l_run += psb;
+        pv_step(2, pb[0]);
+        pv_step(3, pb[1]);
+      };
       if constexpr (S == 4) {
       // Two tiles per barrier: iteration k consumes tiles 2k and 2k+1 and,
       // before computing, copies 2k+2 and 2k+3 into the slots of 2k-2 and
@@ -1389,8 +1501,13 @@ __global__ __launch_bounds__(128 * G) void k_attn(AttnArgs args) {
         }
         const bool m0 = active && ((e0 >> (16 + member)) & 1);
         const bool m1 = active && t2 + 1 < U && ((e1 >> (16 + member)) & 1);
-        if (m0) tile(t2, e0);
-        if (m1) tile(t2 + 1, e1);
+        if constexpr (HALVES && !EXACT) {
+          if (m0) tile_h(t2, e0);
+          if (m1) tile_h(t2 + 1, e1);
+        } else {
+          if (m0) tile(t2, e0);
+          if (m1) tile(t2 + 1, e1);
+        }
       }
       } else {
       // One tile per barrier in a two-slot ring (half the LDS, so two
@@ -1416,7 +1533,10 @@ __global__ __launch_bounds__(128 * G) void k_attn(AttnArgs args) {
           if (t >= 1 && t + 1 < U) issue(t + 1);
           e = entry(t);
         }
-        if (active && ((e >> (16 + member)) & 1)) tile(t, e);
+        if (active && ((e >> (16 + member)) & 1)) {
+          if constexpr (HALVES && !EXACT) tile_h(t, e);
+          else tile(t, e);
+        }
       }
       }
     };
