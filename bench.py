@@ -28,6 +28,9 @@ METRIC = "RoLA fwd ms + kept-block TFLOP/s (% MFMA peak), Wan-14B-720P shape, to
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+# fp32 FMA on the vector ALU without packed math: 256 CUs x 4 SIMDs x 16 lanes x 2 flop x 2.4 GHz
+# (the datasheet's 157.3 TFLOP/s fp32 vector figure counts the packed two-wide form)
+PEAK_FP32_FMA_TFLOPS = 78.6
 
 
 def traffic_file(workload: str) -> str:
@@ -72,8 +75,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true", help="skip the MFMA-probe and copy measurements")
     ap.add_argument("--cpu-baseline-child", action="store_true", help=argparse.SUPPRESS)
-    ap.add_argument("--sample-stride", type=int, default=1,
-                    help="CPU baseline: every n-th query block of one head")
+    ap.add_argument("--sample-stride", type=int, default=32,
+                    help="CPU baseline with --complement: every n-th query block of head 0")
+    ap.add_argument("--cpu-heads", type=int, default=1, help=argparse.SUPPRESS)
+    ap.add_argument("--cpu-threads", type=int, default=1, help=argparse.SUPPRESS)
+    ap.add_argument("--gpu-out", default=None, help=argparse.SUPPRESS)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before timing, run one plain device copy of this many MiB (a known-size "
                          "kernel for scaling profiler byte counters)")
@@ -81,11 +87,27 @@ def parse():
 
 
 # --------------------------------------------------------------- CPU baseline
+def host_cores() -> int:
+    """CPU threads the oracle may use: the affinity mask, capped by OMP_NUM_THREADS when set."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS")
+    return max(1, min(n, int(env))) if env and env.isdigit() else n
+
+
 def cpu_baseline_child(args):
-    """Runs in a child process with OMP_NUM_THREADS=1: the oracle on one head of
-    the workload -- full block selection and low-rank state, and both branches
-    for every `sample_stride`-th query block -- extrapolated linearly to the
-    whole workload."""
+    """The oracle on the host cores, in a child process with OMP_NUM_THREADS set.
+
+    Default: the whole forward (selection, both branches, every row) of the first
+    ``--cpu-heads`` heads, one head per thread, timed; the time scales linearly to
+    all heads (heads are independent and of equal size).  The GPU output of the same
+    heads (``--gpu-out``, written by the parent) is compared with it: block map bit
+    for bit, and max |error| / RMS of the output; for an fp8 workload also against
+    the bf16 oracle (untimed).  With ``--complement`` (whose rows sum every unkept
+    block state) only every ``--sample-stride``-th query block of head 0 is run,
+    with OpenMP over rows, and scaled to the whole workload."""
     import numpy as np
 
     import oracle
@@ -95,61 +117,111 @@ def cpu_baseline_child(args):
     if args.topk is not None:
         import dataclasses
         w = dataclasses.replace(w, topk=args.topk)
-    q, k, v = W.make_qkv(w, heads=[0], threads=1)
-    wq, wk = W.make_proj(w)
-    q, k, v = q[0], k[0], v[0]
-    oracle.lib()
-    t0 = time.perf_counter()
+    fp8 = w.precision == "fp8"
     kb = oracle.keep_blocks(w.topk, w.nb)
-    bmap = oracle.block_map(q, k, w.n_tokens, kb)
-    t1 = time.perf_counter()
-    qf, kf, vf = (oracle.widen_bf16(x) for x in (q, k, v))
+    wq, wk = W.make_proj(w)
     gate_w = W.make_gate(w) if args.gate else None
+    oracle.lib()
     if args.complement:
+        q, k, v = W.make_qkv(w, heads=[0], threads=args.cpu_threads)
+        q, k, v = q[0], k[0], v[0]
+        t0 = time.perf_counter()
+        bmap = oracle.block_map(q, k, w.n_tokens, kb)
+        t1 = time.perf_counter()
+        qf, kf, vf = (oracle.widen_bf16(x) for x in (q, k, v))
         Sb, zb = oracle.lowrank_block_states(kf[0], vf[0], wk, w.n_tokens, w.grid)
-    else:
-        S, z = oracle.lowrank_state(kf, vf, wk, w.n_tokens, w.grid)
-    t2 = time.perf_counter()
-    qbs = list(range(0, w.nb, args.sample_stride))
-    rows = np.array([n for qb in qbs for n in range(qb * 64, min(qb * 64 + 64, w.n_tokens))])
-    sp = oracle.sparse_rows(qf, kf, vf, bmap, w.n_tokens, rows)
-    if args.complement:
+        t2 = time.perf_counter()
+        qbs = list(range(0, w.nb, args.sample_stride))
+        rows = np.array([n for qb in qbs for n in range(qb * 64, min(qb * 64 + 64, w.n_tokens))])
+        sp = oracle.sparse_rows(qf, kf, vf, bmap, w.n_tokens, rows)
         lr = oracle.lowrank_rows_complement(qf[0], wq, Sb, zb, bmap[0], w.grid, rows, gate_w=gate_w)
-    else:
-        lr = oracle.lowrank_rows(qf, wq, S, z, w.grid, rows, gate_w=gate_w)
-    t3 = time.perf_counter()
-    assert np.isfinite(sp + lr).all()
-    rows_full = w.n_tokens
-    per_head = (t1 - t0) + (t2 - t1) + (t3 - t2) * rows_full / rows.size
-    total_s = per_head * w.batch * w.heads
-    print(json.dumps({"total_s": total_s, "sample_s": t3 - t0, "rows": int(rows.size),
-                      "select_s": t1 - t0, "state_s": t2 - t1, "rows_s": t3 - t2}))
+        t3 = time.perf_counter()
+        assert np.isfinite(sp + lr).all()
+        per_head = (t1 - t0) + (t2 - t1) + (t3 - t2) * w.n_tokens / rows.size
+        print(json.dumps({"total_s": per_head * w.batch * w.heads, "heads": 1, "rows": int(rows.size),
+                          "detail": "head 0: selection %.2f s, block states %.2f s, both branches on every %d-th "
+                                    "query block (%d rows) %.2f s" % (t1 - t0, t2 - t1, args.sample_stride, rows.size,
+                                                                      t3 - t2)}))
+        return
+    hs = args.cpu_heads
+    q, k, v = W.make_qkv(w, heads=list(range(hs)), threads=args.cpu_threads)
+    t0 = time.perf_counter()
+    bmap, o_ref = oracle.forward(q[0], k[0], v[0], wq, wk, w.n_tokens, kb, w.grid, fp8=fp8, gate_w=gate_w)
+    t1 = time.perf_counter()
+    rec = {"total_s": (t1 - t0) * w.batch * w.heads / hs, "heads": hs, "sample_s": t1 - t0,
+           "detail": "heads 0-%d of %d, every row, %.2f s" % (hs - 1, w.batch * w.heads, t1 - t0)}
+    if args.gpu_out:
+        g = np.load(args.gpu_out)
+        got = ((g["out"].astype(np.uint32) << 16).view(np.float32)).astype(np.float64)[:, :w.n_tokens]
+        rec["map_exact"] = bool(np.array_equal(g["map"], bmap))
+
+        def err(ref):
+            ref = ref[:, :w.n_tokens]
+            return float(np.abs(got - ref).max() / np.sqrt((ref ** 2).mean()))
+
+        def bound_ratio(ref, tol):
+            # the per-element bar for a bf16-stored output: tol * rms * (1 + 2^-8)
+            # plus half a bf16 ulp of the element (at most 2^-8 |ref|)
+            ref = ref[:, :w.n_tokens]
+            rms = np.sqrt((ref ** 2).mean())
+            return float((np.abs(got - ref) / (tol * rms * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(ref))).max())
+        rec["err_rms"] = err(o_ref)
+        rec["bar"] = 6e-2 if fp8 else 2e-2
+        rec["err_over_bound"] = bound_ratio(o_ref, rec["bar"])
+        if fp8:
+            _, o16 = oracle.forward(q[0], k[0], v[0], wq, wk, w.n_tokens, kb, w.grid, gate_w=gate_w)
+            rec["err_rms_vs_bf16_oracle"] = err(o16)
+    print(json.dumps(rec))
 
 
-def cpu_baseline(args, w, kb):
-    env = dict(os.environ, OMP_NUM_THREADS="1")
-    # the complement rows sum every unkept block state per row: sample fewer query blocks
-    stride = max(args.sample_stride, 32) if args.complement else args.sample_stride
+def cpu_baseline(args, w, kb, out, bmap):
+    """Runs cpu_baseline_child on the host cores; ``out``/``bmap`` are the GPU results
+    (bf16 output and block map) whose first heads the child checks."""
+    import numpy as np
+    import tempfile
+    cores = host_cores()
+    stride = max(args.sample_stride, 32)
     cmd = [sys.executable, os.path.abspath(__file__), "--cpu-baseline-child", "--workload", args.workload,
-           "--sample-stride", str(stride)] + (["--topk", repr(args.topk)] if args.topk else []) \
-        + (["--gate"] if args.gate else []) + (["--complement"] if args.complement else [])
-    res = subprocess.run(cmd, env=env, capture_output=True, text=True, timeout=600)
+           "--cpu-threads", str(cores)] + (["--topk", repr(args.topk)] if args.topk else []) \
+        + (["--gate"] if args.gate else [])
+    tmp = None
+    if args.complement:
+        cmd += ["--complement", "--sample-stride", str(stride)]
+    else:
+        hs = min(cores, w.batch * w.heads)
+        tmp = tempfile.NamedTemporaryFile(suffix=".npz", delete=False)
+        tmp.close()
+        np.savez(tmp.name, out=out[0, :hs].view(torch_int16()).cpu().numpy().view(np.uint16),
+                 map=bmap[0, :hs].cpu().numpy())
+        cmd += ["--cpu-heads", str(hs), "--gpu-out", tmp.name]
+    env = dict(os.environ, OMP_NUM_THREADS=str(cores))
+    try:
+        res = subprocess.run(cmd, env=env, capture_output=True, text=True, timeout=900)
+    finally:
+        if tmp is not None:
+            os.unlink(tmp.name)
     if res.returncode != 0:
         raise RuntimeError("cpu baseline failed: " + res.stderr[-2000:])
     r = json.loads(res.stdout.strip().splitlines()[-1])
-    ms = r["total_s"] * 1e3
-    return {
-        "value": w.kept_block_flop(kb) / (r["total_s"]) / 1e12,
+    base = {
+        "value": w.kept_block_flop(kb) / r["total_s"] / 1e12,
         "unit": "TFLOP/s (kept-block)",
-        "ms": ms,
-        "cores": 1,
+        "ms": r["total_s"] * 1e3,
+        "cores": cores,
         "kind": "oracle",
-        "sample": ("oracle (C, fp64 branches, 1 thread) on head 0 of %s: full block selection (%.2f s) and "
-                   "low-rank state (%.2f s), both branches on every %d-th query block (%d rows, %.2f s); "
-                   "extrapolated linearly to all %d heads and rows"
-                   % (args.workload, r["select_s"], r["state_s"], stride, r["rows"], r["rows_s"],
-                      w.batch * w.heads)),
+        "sample": ("oracle (C, fp64 branches, OpenMP on %d host threads) on %s: %s; scaled linearly to all %d heads"
+                   % (cores, args.workload, r["detail"], w.batch * w.heads)),
     }
+    check = {k_: r[k_] for k_ in ("map_exact", "err_rms", "bar", "err_over_bound", "err_rms_vs_bf16_oracle")
+             if k_ in r}
+    if check:
+        check["heads"] = r["heads"]
+    return base, check
+
+
+def torch_int16():
+    import torch
+    return torch.int16
 
 
 # -------------------------------------------------------------- backward
@@ -429,15 +501,12 @@ def main():
         print("[bench] copy calibration: %d bytes read, %d written" % (nbytes, nbytes), file=sys.stderr, flush=True)
         del src, dst
     print("[bench] warmup %d" % args.warmup, file=sys.stderr, flush=True)
-    rola.timing_enable(True)  # warm the per-kernel event pool as well
     for _ in range(args.warmup):
         fwd()
     torch.cuda.synchronize()
-    rola.timing_enable(False)
-    rola.timing_read()  # drop the warmup records (their events return to the pool)
 
+    # the timed region: plain forwards between two stream events (no per-kernel events)
     print("[bench] timing %d steps" % args.steps, file=sys.stderr, flush=True)
-    rola.timing_enable(True)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
@@ -445,8 +514,23 @@ def main():
         fwd()
     e1.record(stream)
     torch.cuda.synchronize()
-    rola.timing_enable(False)
     ms = e0.elapsed_time(e1) / args.steps
+
+    # per-kernel breakdown: the same number of forwards again, with the library's
+    # HIP events around each kernel on the call's stream (event pool made beforehand)
+    print("[bench] per-kernel breakdown, %d steps" % args.steps, file=sys.stderr, flush=True)
+    rola.timing_enable(True)
+    fwd()
+    torch.cuda.synchronize()
+    rola.timing_read()
+    e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e2.record(stream)
+    for _ in range(args.steps):
+        fwd()
+    e3.record(stream)
+    torch.cuda.synchronize()
+    rola.timing_enable(False)
+    ms_breakdown = e2.elapsed_time(e3) / args.steps
     kernels = rola.timing_read()
     kern_ms = {name: tot / n for name, (n, tot) in kernels.items()}
 
@@ -493,6 +577,8 @@ def main():
         "dense_equiv_tflops": round(dense / (ms * 1e-3) / 1e12, 1),
         "kept_block_tflops": round(kept / (ms * 1e-3) / 1e12, 1),
         "kernel_ms": {k_: round(v_, 4) for k_, v_ in sorted(kern_ms.items())},
+        "kernel_ms_pass": {"steps": args.steps, "fwd_ms": round(ms_breakdown, 4),
+                           "how": "second pass with HIP events around every kernel; the headline ms has none"},
         "roofline": {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 1),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic},
@@ -506,6 +592,14 @@ def main():
         gbs = pass1_bytes / (pass1_ms * 1e-3) / 1e9
         rec["pass1_roofline"] = {"kernel": pass1_name, "bound": "hbm", "achieved": round(gbs, 1),
                                  "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    if "scores" in kern_ms:
+        # pooled block scores: one fp32 FMA per (query block, key block, dim), a
+        # pinned sequential chain, so plain (unpacked) v_fma_f32 on the VALU
+        sflop = 2.0 * w.batch * w.heads * w.nb * w.nb * w.head_dim
+        tf = sflop / (kern_ms["scores"] * 1e-3) / 1e12
+        rec["scores_roofline"] = {"kernel": "scores", "bound": "alu", "achieved": round(tf, 1),
+                                  "peak": PEAK_FP32_FMA_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": round(tf / PEAK_FP32_FMA_TFLOPS, 4)}
     if not args.no_peaks:
         print("[bench] measured peaks (MFMA probe, device copy)", file=sys.stderr, flush=True)
         rec["measured_peaks"] = measured_peaks(rola, torch, stream, "fp8" if fp8 else "bf16")
@@ -514,8 +608,17 @@ def main():
         if "pass1_roofline" in rec:
             rec["pass1_roofline"]["frac_of_measured"] = round(rec["pass1_roofline"]["achieved"] / mp["copy_gbs"], 4)
     if not args.no_cpu_baseline:
-        print("[bench] cpu baseline (oracle, 1 thread, sampled)", file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(args, w, kb)
+        print("[bench] cpu baseline (oracle on %d host threads)" % host_cores(), file=sys.stderr, flush=True)
+        bmap = torch.empty((w.batch, w.heads, w.nb, kb), dtype=torch.int32, device="cuda")
+        if e4m3:
+            rola.rola_forward_e4m3(qd, kd, vd, *codes, *scales, wqd, wkd, w.grid, cfg, out=out, stream=stream,
+                                   gate=gd, block_idx_out=bmap)
+        else:
+            rola.rola_forward(qd, kd, vd, wqd, wkd, w.grid, cfg, out=out, stream=stream, gate=gd, block_idx_out=bmap)
+        torch.cuda.synchronize()
+        rec["cpu_baseline"], check = cpu_baseline(args, w, kb, out, bmap)
+        if check:
+            rec["oracle_check"] = check
     print(json.dumps(rec), flush=True)
 
 

@@ -284,7 +284,8 @@ int32_t rola_gemm_w8a8(const uint8_t *x, int64_t ld_x, const float *sx, const ui
                        int32_t K, void *out, int64_t ld_out, int32_t out_dtype, void *stream);
 
 /*
- * Measurement helper (not part of RoLA): launches, on `stream`, a kernel
+ * ---- Diagnostics (not part of RoLA) ----
+ * Measurement helper: launches, on `stream`, a kernel
  * that keeps every SIMD's matrix core busy with independent MFMA chains --
  * precision ROLA_PREC_BF16: v_mfma_f32_32x32x16_bf16, ROLA_PREC_FP8:
  * v_mfma_f32_32x32x64_f8f6f4 (e4m3) -- for `iters` steps per chain, and

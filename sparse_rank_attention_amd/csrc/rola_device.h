@@ -145,19 +145,14 @@ static __device__ __forceinline__ uint32_t lds_addr(const T *p) {
 
 // LDS tile layouts: row-major [64 rows][D] bf16 in 16-byte chunks, chunk c
 // of row r stored at c ^ swizzle(r).  K tiles (read as 16-byte MFMA rows)
-// use r & 7; V tiles (read transposed, 8 bytes per lane) use 2*(r & 3).
-#ifndef ROLA_SWZ_K
-#define ROLA_SWZ_K 15
-#endif
-#ifndef ROLA_SWZ_V
-#define ROLA_SWZ_V 4
-#endif
-// K: XOR with the row's low bits (16 chunks per row at D=128, 8 at D=64);
-// V: XOR with a multiple of (row & 3), the four rows a transposed read spans.
+// XOR with the row's low four bits (16 chunks per row at D=128, 8 at D=64);
+// V tiles (read transposed, 8 bytes per lane) XOR with 4 * (row & 3), the
+// four rows a transposed read spans.  Both were measured free of bank
+// conflicts (SQ_LDS_BANK_CONFLICT = 0).
 template <int D>
-static __device__ __forceinline__ int swz_k(int r) { return r & (ROLA_SWZ_K & (D / 8 - 1)); }
+static __device__ __forceinline__ int swz_k(int r) { return r & (15 & (D / 8 - 1)); }
 template <int D>
-static __device__ __forceinline__ int swz_v(int r) { return (ROLA_SWZ_V * (r & 3)) & (D / 8 - 1); }
+static __device__ __forceinline__ int swz_v(int r) { return (4 * (r & 3)) & (D / 8 - 1); }
 
 static __device__ __forceinline__ void barrier_lds() {
   // all LDS reads of this wave retired, then a plain workgroup barrier (no

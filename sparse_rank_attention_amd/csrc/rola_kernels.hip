@@ -1117,10 +1117,13 @@ static __device__ __forceinline__ void attn_finish(const AttnArgs &args, const b
 // the block runs S^T = K Q^T, the online softmax and O^T += V^T P^T on it.
 // Workgroups are mapped so that all XCDs work on the same head at a time and
 // each XCD takes a contiguous run of similar groups (shared L2 lines).
-// EXACT (the backward's recompute of the sparse branch): the row sums add the
-// fp32 weights and each weight enters the PV product as a bf16 pair hi + lo,
-// so that O and the log-sum-exp agree with fp32 weights to about 16 bits.
-template <int D, int G, int S, bool SPARSE, bool LOWRANK, bool ACCUM, bool OUTF32, bool EXACT = false>
+// EXACT (fp32 output, and the backward's recompute of the sparse branch):
+// the row sums add the fp32 weights and each weight enters the PV product as
+// a bf16 pair hi + lo, so that O and the log-sum-exp agree with fp32 weights
+// to about 16 bits.  With bf16 output a single bf16 weight is used: its
+// rounding (half a bf16 ulp, relative) is of the size of the output's own
+// bf16 storage rounding.
+template <int D, int G, int S, bool SPARSE, bool LOWRANK, bool ACCUM, bool OUTF32, bool EXACT = OUTF32>
 __global__ __launch_bounds__(128 * G, 2) void k_attn(AttnArgs args) {
   constexpr int CH = D / 8;
   constexpr int NS = D / 16;  // k-steps over head_dim
@@ -2074,15 +2077,8 @@ int attn_group_size() { return ROLA_ATTN_G; }
 
 void launch_attn(const AttnArgs &a, int D, bool sparse, bool lowrank, bool accum, bool outf32,
                  hipStream_t st) {
-  if (a.lse && sparse && !lowrank && !accum && outf32) {
-    // the backward's recompute: fp32 weights (see k_attn, EXACT)
-    const dim3 grid((unsigned)(8 * a.groups_per_xcd * a.bh_count)), block(128 * ROLA_ATTN_G);
-    if (D == 64)
-      hipLaunchKernelGGL((k_attn<64, ROLA_ATTN_G, ROLA_ATTN_S, true, false, false, true, true>), grid, block, 0, st, a);
-    else
-      hipLaunchKernelGGL((k_attn<128, ROLA_ATTN_G, ROLA_ATTN_S, true, false, false, true, true>), grid, block, 0, st, a);
-    return;
-  }
+  // fp32 output (and the backward's recompute, which asks for fp32 output and
+  // the log-sum-exp) takes the split-weight form of the kernel (EXACT = OUTF32)
   if (D == 64) attn_d<64, ROLA_ATTN_G, ROLA_ATTN_S>(a, sparse, lowrank, accum, outf32, st);
   else attn_d<128, ROLA_ATTN_G, ROLA_ATTN_S>(a, sparse, lowrank, accum, outf32, st);
 }

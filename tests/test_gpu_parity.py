@@ -260,3 +260,49 @@ def test_full_size_sampled(name):
         pad = out[0, h, w.n_tokens:].float()
         assert torch.count_nonzero(pad).item() == 0
     say("full size", name, "worst err/rms", worst)
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_every_block_map(name):
+    """The block map of every head of the benchmarked launch, bit for bit."""
+    from sparse_rank_attention_amd import rola
+    torch = _torch()
+    say("full size, every head's map", name)
+    w, (q, k, v), (wq, wk) = _full_inputs(name)
+    kb = oracle.keep_blocks(w.topk, w.nb)
+    bmap = torch.empty((w.batch, w.heads, w.nb, kb), dtype=torch.int32, device="cuda")
+    rola.rola_forward(dev(q), dev(k), dev(v), torch.from_numpy(wq).cuda(), torch.from_numpy(wk).cuda(),
+                      w.grid, cfg_of(w), block_idx_out=bmap)
+    torch.cuda.synchronize()
+    m_ref = oracle.block_map(q[0], k[0], w.n_tokens, kb)  # all heads, threads over heads
+    got = bmap.cpu().numpy()[0]
+    bad = [h for h in range(w.heads) if not np.array_equal(got[h], m_ref[h])]
+    assert not bad, "heads with a differing map: %s" % bad
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_every_row_fp32(name):
+    """Every valid row of the first, middle and last head of the benchmarked launch,
+    with fp32 output, against the plain bar max|O - O_ref| <= 2e-2 * rms(O_ref)
+    (no storage term: nothing is rounded to bf16 on the way out)."""
+    from sparse_rank_attention_amd import rola
+    torch = _torch()
+    w, (q, k, v), (wq, wk) = _full_inputs(name)
+    kb = oracle.keep_blocks(w.topk, w.nb)
+    cfg = cfg_of(w, out_dtype=rola.ROLA_OUT_F32)
+    out = rola.rola_forward(dev(q), dev(k), dev(v), torch.from_numpy(wq).cuda(), torch.from_numpy(wk).cuda(),
+                            w.grid, cfg)
+    torch.cuda.synchronize()
+    rows = np.arange(w.n_tokens)
+    errs = {}
+    for h in sorted({0, w.heads // 2, w.heads - 1}):
+        say("full size fp32 rows", name, "head", h)
+        m_ref = oracle.block_map(q[0, h:h + 1], k[0, h:h + 1], w.n_tokens, kb)
+        qf, kf, vf = (oracle.widen_bf16(x[0, h:h + 1]) for x in (q, k, v))
+        S, z = oracle.lowrank_state(kf, vf, wk, w.n_tokens, w.grid)
+        ref = oracle.sparse_rows(qf, kf, vf, m_ref, w.n_tokens, rows) + oracle.lowrank_rows(qf, wq, S, z, w.grid, rows)
+        got = out[0, h, :w.n_tokens].cpu().numpy().astype(np.float64)
+        errs[h] = rel_err(got, ref)
+        assert errs[h] <= TOL_BF16, (h, errs[h])
+        assert torch.count_nonzero(out[0, h, w.n_tokens:]).item() == 0
+    say("full size fp32 rows", name, "err/rms per head", {h: round(e, 5) for h, e in errs.items()})
