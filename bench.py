@@ -547,12 +547,14 @@ def main():
         if tr.get("kernel_source_hash") == kernel_source_hash() and tr.get("workload") == w.name:
             traffic = round(tr["bytes_per_launch"]["total"])
     # algorithmic HBM bytes of the streaming pass: read Q, K, V once; in fp8 mode
-    # also write the e4m3 codes of K and V (one byte per element)
-    n_tok = w.batch * w.heads * w.n_pad
+    # also write the e4m3 codes of K and V (one byte per element), with bf16
+    # operands (and the bf16 output used here) the fp16 copy of V (two bytes)
+    n_tok = w.batch * w.heads * w.n_tokens
     # (complement scope: plus the per-block states it writes, bf16 S and fp32 z)
     quant_in_pass1 = fp8 and not e4m3
     pass1_name = "pass1_pool_%s%s" % ("blkstate" if args.complement else "state", "_quant8" if quant_in_pass1 else "")
     pass1_bytes = 3 * n_tok * w.head_dim * 2 + (2 * n_tok * w.head_dim if quant_in_pass1 else 0) \
+        + (n_tok * w.head_dim * 2 if not fp8 else 0) \
         + (w.batch * w.heads * w.nb * (w.head_dim * 64 + 128) if args.complement else 0)
     pass1_ms = kern_ms.get(pass1_name)
     rec = {

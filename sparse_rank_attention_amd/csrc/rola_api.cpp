@@ -39,6 +39,8 @@ struct Plan {
       off_z, off_ugroup, off_ucount, off_ulist, total;
   bool fp8;
   int64_t off_qsc, off_ksc, off_vsc, off_kv8;  // fp8 only
+  bool vh;  // bf16 output, bf16 operands: the fp16 copy of V and its range flags
+  int64_t off_vh, off_vovf;
   bool comp;  // complement scope of the low-rank branch
   int64_t off_blk, off_s32, off_stc, off_zc;  // complement scope only
   // rola_backward: its buffers follow the forward's (offsets from 0)
@@ -131,6 +133,12 @@ int32_t make_plan(const rola_problem *p, const rola_config *c, Plan *pl) {
     P.off_ksc = o; o = align_up(o + P.BH * nb * 4);
     P.off_vsc = o; o = align_up(o + P.BH * nb * 4);
     P.off_kv8 = o; o = align_up(o + P.BH * nb * 128LL * D);
+  }
+  P.vh = !P.fp8 && c->out_dtype == ROLA_OUT_BF16;
+  P.off_vh = P.off_vovf = 0;
+  if (P.vh) {
+    P.off_vh = o; o = align_up(o + P.BH * P.n_pad * D * 2);
+    P.off_vovf = o; o = align_up(o + P.BH * 2 * P.nchunks * 4);
   }
   P.off_blk = P.off_s32 = P.off_stc = P.off_zc = 0;
   if (P.comp) {
@@ -247,8 +255,10 @@ int32_t run_setup(const Plan &P, const float *wq, const float *wk, uint8_t *ws, 
   return timed("setup", st, [&] { rola::launch_setup(a, st); });
 }
 
+// vh: also the fp16 copy of V with its range flags (bf16 output); with
+// neither pool nor state, the copy alone
 int32_t run_pass1(const Plan &P, const rola_problem *p, const void *q, const void *k, const void *v,
-                  uint8_t *ws, bool pool, bool state, hipStream_t st, bool quant = false) {
+                  uint8_t *ws, bool pool, bool state, hipStream_t st, bool quant = false, bool vh = false) {
   rola::Pass1Args a;
   a.q = (const uint16_t *)q; a.k = (const uint16_t *)k; a.v = (const uint16_t *)v;
   a.stride_b = p->stride_b; a.stride_h = p->stride_h; a.stride_n = p->stride_n;
@@ -265,6 +275,10 @@ int32_t run_pass1(const Plan &P, const rola_problem *p, const void *q, const voi
   a.ksc = (float *)(ws + P.off_ksc);
   a.vsc = (float *)(ws + P.off_vsc);
   a.kv8 = ws + P.off_kv8;
+  a.vh = vh ? (uint16_t *)(ws + P.off_vh) : nullptr;
+  a.vovf = vh ? (int32_t *)(ws + P.off_vovf) : nullptr;
+  if (!pool && !state)
+    return timed("v_fp16", st, [&] { rola::launch_pass1(a, P.D, P.nchunks, (int)P.BH, false, false, false, st); });
   const char *name = (pool && state) ? (quant ? (a.blk_state ? "pass1_pool_blkstate_quant8"
                                                             : "pass1_pool_state_quant8")
                                               : (a.blk_state ? "pass1_pool_blkstate" : "pass1_pool_state"))
@@ -343,6 +357,13 @@ int32_t run_attn(const Plan &P, const rola_problem *p, const rola_config *c, con
   a.z = (const float *)(ws + P.off_z);
   a.gate = lowrank ? gate : nullptr;
   a.complement = (lowrank && P.comp) ? 1 : 0;
+  // bf16 output of the sparse branch: PV on the fp16 copy of V (written by
+  // pass 1 or the copy pass beforehand), the EXACT form for flagged heads
+  const bool f16v = sparse && !P.fp8 && c->out_dtype == ROLA_OUT_BF16;
+  if (f16v && !P.vh) return ROLA_ERR_INVALID_ARG;  // (the plan of the same config holds the copy)
+  a.vh = f16v ? (const uint16_t *)(ws + P.off_vh) : nullptr;
+  a.vovf = f16v ? (const int32_t *)(ws + P.off_vovf) : nullptr;
+  a.nflags = 2 * P.nchunks;
   a.lse = (sparse && !lowrank) ? lse : nullptr;
   a.rope = rope_args(P, ws);
   a.kv8 = ws + P.off_kv8;
@@ -465,6 +486,7 @@ int32_t rola_sparse_attn(const rola_problem *prob, const rola_config *cfg, const
   hipStream_t st = (hipStream_t)stream;
   uint8_t *ws = (uint8_t *)workspace;
   if (P.fp8) ROLA_TRY(run_quant8(P, prob, q, k, v, ws, st));
+  if (P.vh) ROLA_TRY(run_pass1(P, prob, nullptr, nullptr, v, ws, false, false, st, false, true));
   return run_attn(P, prob, cfg, q, k, v, block_idx, nullptr, out, ws, true, false, accumulate != 0,
                   st);
 }
@@ -519,7 +541,7 @@ int32_t rola_forward(const rola_problem *prob, const rola_config *cfg, const voi
   int32_t *map = block_idx_out ? block_idx_out : (int32_t *)(ws + P.off_map);
   ROLA_TRY(run_setup(P, wq, wk, ws, st));
   // fp8: the streaming pass also writes the scales and e4m3 tile images
-  ROLA_TRY(run_pass1(P, prob, q, k, v, ws, true, true, st, P.fp8));
+  ROLA_TRY(run_pass1(P, prob, q, k, v, ws, true, true, st, P.fp8, P.vh));
   ROLA_TRY(run_reduce(P, ws, st));
   ROLA_TRY(run_select(P, ws, (float *)(ws + P.off_scores), map, st));
   return run_attn(P, prob, cfg, q, k, v, map, gate, out, ws, true, true, false, st);

@@ -14,6 +14,8 @@
 #include "rola_internal.h"
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __fp16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __fp16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -51,6 +53,9 @@ static __device__ __forceinline__ float fast_exp2(float x) { return __builtin_am
 
 static __device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+static __device__ __forceinline__ f32x16 mfma_f16(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
 // e4m3 codes: round to nearest even, saturating at +-448

@@ -36,6 +36,12 @@ struct Pass1Args {
   // fp8 mode (see Quant8Args): Q scales, K and V^T codes of each block
   float *qsc, *ksc, *vsc;
   uint8_t *kv8;
+  // fp16 copy of V (bf16 output), written by the pooling waves: [BH][n_pad][D]
+  // (rows past N not written), and two range flags per (batch*head, chunk),
+  // [BH][2 * gridDim.x]: 1 if a valid |v| of the chunk's half is >= 2^16 (or
+  // inf), beyond fp16, else 0 -- all written on every pass, so never cleared
+  uint16_t *vh;
+  int32_t *vovf;
 };
 
 // Attention workgroup shape: G query blocks per workgroup (2 waves each),
@@ -95,6 +101,9 @@ struct AttnArgs {
   const uint16_t *wqT;  // bf16 [32][D]
   const uint16_t *st;   // bf16 [BH][D][32] (rank permuted)
   const float *z;       // [BH][32]
+  const uint16_t *vh;   // fp16 V copy and its range flags (see Pass1Args), bf16 output
+  const int32_t *vovf;  // with the sparse branch; nflags flags per (batch, head)
+  int nflags;
   const float *gate;    // fp32 [D+1] output gate (w, then b) on the low-rank term; NULL: none
   int complement;       // st and z hold one state per query block ([BH][nb][D][32], [BH][nb][32])
   float *lse;           // sparse branch alone with fp32 output: if set, the backward's
@@ -108,8 +117,10 @@ struct AttnArgs {
 };
 
 void launch_setup(const SetupArgs &a, hipStream_t st);
+// per-block states as well when a.blk_state is set; the fp16 V copy when
+// a.vh is set (not with quant; with neither pool nor state: the copy alone)
 void launch_pass1(const Pass1Args &a, int D, int nchunks, int bh, bool pool, bool state, bool quant,
-                  hipStream_t st);  // per-block states as well when a.blk_state is set
+                  hipStream_t st);
 // part: np fp32 partial states per head, [BH][np][D*32 + 32]
 void launch_state_reduce(const float *part, int np, int D, int rank, int bh, uint16_t *st_out,
                          float *z, float *s32, hipStream_t st);

@@ -107,14 +107,21 @@ static __device__ __forceinline__ int img_v_off(int d, int p) {
 //          block's e4m3 tile image), and a fifth wave reads V the same way
 //          and writes its scales and the V^T part of the image through an
 //          LDS transpose (see k_quant8 for the image layout and rounding).
+//   VH:    (bf16 output) the two pooling waves also read V, 32 tokens of
+//          each block each, and write its fp16 copy for the attention
+//          kernel's PV product, with a range flag per wave (some valid
+//          |v| >= 2^16, beyond fp16, or inf).  bf16 values below 2^16 are
+//          fp16 values (8 significant bits within 11), so the copy is exact
+//          there, down to fp16's subnormal range.  Without POOL: the copy
+//          alone.
 // Rows past N are read as zero (pooling) or taken from row N-1 (finite
 // values; their b is masked to 0).
 // bytes of one per-block low-rank state (complement scope): bf16 S^T [D][32]
 // (rank in natural order), then fp32 z [32]
 static __host__ __device__ constexpr int blk_state_bytes(int D) { return D * 64 + 128; }
 
-template <int D, bool POOL, bool STATE, bool QUANT, bool BLK>
-__global__ __launch_bounds__(QUANT ? 320 : 256) void k_pass1(Pass1Args args) {
+template <int D, bool POOL, bool STATE, bool QUANT, bool BLK, bool VH = false>
+__global__ __launch_bounds__(QUANT ? 320 : 256, QUANT ? 1 : 2) void k_pass1(Pass1Args args) {
   constexpr int CH = D / 8;       // 16-byte chunks per token row
   constexpr int NS = D / 16;      // MFMA k-steps over head_dim
   constexpr int DT = D / 32;      // d-tiles of the state
@@ -197,80 +204,114 @@ __global__ __launch_bounds__(QUANT ? 320 : 256) void k_pass1(Pass1Args args) {
     }
     return;
   }
-
   if (wave < 2) {
-    if (!POOL) return;
-    // ---- pooling
+    if (!POOL && !VH) return;
+    // ---- pooling (wave 0: Q, wave 1: K) and, with VH, the fp16 copy of
+    // this wave's 32 tokens of each V block (wave 0 tokens 0-31, wave 1
+    // tokens 32-63), loaded with the block's Q/K rows
     const uint16_t *X = (wave == 0 ? args.q : args.k) + base;
+    const uint16_t *XV = args.v + base;
+    uint16_t *YV = VH ? args.vh + (int64_t)bh * args.nb * 64 * D : nullptr;
     float *dst = wave == 0 ? args.qp : args.kp;
+    float vmax = 0.0f;  // largest |v| copied (VH)
     for (int i = 0; i < nblk; ++i) {
       const int c = c0 + i;
       const int valid = min(64, (int)(args.n_tokens - (int64_t)c * 64));
-      auto ld = [&](int t) __attribute__((always_inline)) -> u32x4 {
-        return t < valid ? *(const u32x4 *)(X + ((int64_t)c * 64 + t) * args.stride_n + 8 * dl)
-                         : u32x4{0u, 0u, 0u, 0u};
-      };
-      // token distance 32 as the pairs arrive (registers r and r + R/2)
-      float x[R / 2][8];
-      u32x4 keep[QUANT ? R : 1];  // raw K values for the codes (fp8 mode)
-      float amax = 0.0f;
+      u32x4 vraw[VH ? R / 2 : 1];
+      if constexpr (VH) {
 #pragma unroll
-      for (int r = 0; r < R / 2; ++r) {
-        const u32x4 lo = ld(TG * r + tg), hi = ld(TG * (r + R / 2) + tg);
+        for (int r = 0; r < R / 2; ++r) {
+          const int t = 32 * wave + TG * r + tg;
+          vraw[r] = t < valid ? *(const u32x4 *)(XV + ((int64_t)c * 64 + t) * args.stride_n + 8 * dl)
+                              : u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+      if constexpr (POOL) {
+        auto ld = [&](int t) __attribute__((always_inline)) -> u32x4 {
+          return t < valid ? *(const u32x4 *)(X + ((int64_t)c * 64 + t) * args.stride_n + 8 * dl)
+                           : u32x4{0u, 0u, 0u, 0u};
+        };
+        // token distance 32 as the pairs arrive (registers r and r + R/2)
+        float x[R / 2][8];
+        u32x4 keep[QUANT ? R : 1];  // raw K values for the codes (fp8 mode)
+        float amax = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x[r][2 * e] = bflo(lo[e]) + bflo(hi[e]);
-          x[r][2 * e + 1] = bfhi(lo[e]) + bfhi(hi[e]);
-          if (QUANT)
-            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(bflo(lo[e])), fabsf(bfhi(lo[e]))),
-                                     fmaxf(fabsf(bflo(hi[e])), fabsf(bfhi(hi[e])))));
+        for (int r = 0; r < R / 2; ++r) {
+          const u32x4 lo = ld(TG * r + tg), hi = ld(TG * (r + R / 2) + tg);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x[r][2 * e] = bflo(lo[e]) + bflo(hi[e]);
+            x[r][2 * e + 1] = bfhi(lo[e]) + bfhi(hi[e]);
+            if (QUANT)
+              amax = fmaxf(amax, fmaxf(fmaxf(fabsf(bflo(lo[e])), fabsf(bfhi(lo[e]))),
+                                       fmaxf(fabsf(bflo(hi[e])), fabsf(bfhi(hi[e])))));
+          }
+          if constexpr (QUANT) {
+            keep[r] = lo;
+            keep[r + R / 2] = hi;
+          }
         }
         if constexpr (QUANT) {
-          keep[r] = lo;
-          keep[r + R / 2] = hi;
-        }
-      }
-      if constexpr (QUANT) {
-        amax = wave_absmax(amax);
-        const int64_t sidx = (int64_t)bh * args.nb + c;
-        const float sc = amax > 0.0f ? __fdiv_rn(amax, 448.0f) : 1.0f;
-        const float inv = amax > 0.0f ? __fdiv_rn(448.0f, amax) : 1.0f;
-        if (wave == 0) {
-          if (lane == 0) {
-            args.qsc[2 * sidx] = sc;
-            args.qsc[2 * sidx + 1] = inv;
+          amax = wave_absmax(amax);
+          const int64_t sidx = (int64_t)bh * args.nb + c;
+          const float sc = amax > 0.0f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+          const float inv = amax > 0.0f ? __fdiv_rn(448.0f, amax) : 1.0f;
+          if (wave == 0) {
+            if (lane == 0) {
+              args.qsc[2 * sidx] = sc;
+              args.qsc[2 * sidx + 1] = inv;
+            }
+          } else {
+            if (lane == 0) args.ksc[sidx] = sc;
+            uint8_t *kimg = args.kv8 + sidx * (128 * D);
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+              *(uint2 *)(kimg + img_k_off<D>(TG * r + tg, 8 * dl)) = e4m3x8(keep[r], inv);
           }
-        } else {
-          if (lane == 0) args.ksc[sidx] = sc;
-          uint8_t *kimg = args.kv8 + sidx * (128 * D);
+        }
+        // token distances 16 .. TG inside the lane (register r + dist/TG)
 #pragma unroll
-          for (int r = 0; r < R; ++r)
-            *(uint2 *)(kimg + img_k_off<D>(TG * r + tg, 8 * dl)) = e4m3x8(keep[r], inv);
+        for (int dist = 16; dist >= TG; dist >>= 1) {
+#pragma unroll
+          for (int r = 0; r < dist / TG; ++r)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[r][e] = x[r][e] + x[r + dist / TG][e];
+        }
+        // distances TG/2 .. 1 across lanes (token group tg + dist = lane + dist*LPR)
+#pragma unroll
+        for (int dist = TG / 2; dist >= 1; dist >>= 1) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float o = __shfl_xor(x[0][e], dist * LPR, 64);
+            x[0][e] = x[0][e] + o;  // meaningful in token group 0 (lanes < LPR)
+          }
+        }
+        if (lane < LPR) {
+          const float inv = valid == 64 ? 0.015625f : args.inv_tail;
+          float *o = dst + ((int64_t)bh * args.nb + c) * D + 8 * dl;
+          *(f32x4 *)o = f32x4{x[0][0] * inv, x[0][1] * inv, x[0][2] * inv, x[0][3] * inv};
+          *(f32x4 *)(o + 4) = f32x4{x[0][4] * inv, x[0][5] * inv, x[0][6] * inv, x[0][7] * inv};
         }
       }
-      // token distances 16 .. TG inside the lane (register r + dist/TG)
+      if constexpr (VH) {
 #pragma unroll
-      for (int dist = 16; dist >= TG; dist >>= 1) {
+        for (int r = 0; r < R / 2; ++r) {
+          const int t = 32 * wave + TG * r + tg;
+          u32x4 hv;
 #pragma unroll
-        for (int r = 0; r < dist / TG; ++r)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) x[r][e] = x[r][e] + x[r + dist / TG][e];
-      }
-      // distances TG/2 .. 1 across lanes (token group tg + dist = lane + dist*LPR)
-#pragma unroll
-      for (int dist = TG / 2; dist >= 1; dist >>= 1) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float o = __shfl_xor(x[0][e], dist * LPR, 64);
-          x[0][e] = x[0][e] + o;  // meaningful in token group 0 (lanes < LPR)
+          for (int e = 0; e < 4; ++e) {
+            const float lo = bflo(vraw[r][e]), hi = bfhi(vraw[r][e]);
+            vmax = fmaxf(vmax, fmaxf(fabsf(lo), fabsf(hi)));
+            hv[e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+          }
+          if (t < valid) *(u32x4 *)(YV + ((int64_t)c * 64 + t) * D + 8 * dl) = hv;
         }
       }
-      if (lane < LPR) {
-        const float inv = valid == 64 ? 0.015625f : args.inv_tail;
-        float *o = dst + ((int64_t)bh * args.nb + c) * D + 8 * dl;
-        *(f32x4 *)o = f32x4{x[0][0] * inv, x[0][1] * inv, x[0][2] * inv, x[0][3] * inv};
-        *(f32x4 *)(o + 4) = f32x4{x[0][4] * inv, x[0][5] * inv, x[0][6] * inv, x[0][7] * inv};
-      }
+    }
+    // the range flag of this wave's half of the chunk
+    if constexpr (VH) {
+      const bool ovf = __builtin_amdgcn_ballot_w64(!(vmax < 65536.0f)) != 0;
+      if (lane == 0) args.vovf[((int64_t)bh * gridDim.x + blockIdx.x) * 2 + wave] = ovf ? 1 : 0;
     }
     return;
   }
@@ -1117,12 +1158,18 @@ static __device__ __forceinline__ void attn_finish(const AttnArgs &args, const b
 // the block runs S^T = K Q^T, the online softmax and O^T += V^T P^T on it.
 // Workgroups are mapped so that all XCDs work on the same head at a time and
 // each XCD takes a contiguous run of similar groups (shared L2 lines).
-// EXACT (fp32 output, and the backward's recompute of the sparse branch):
-// the row sums add the fp32 weights and each weight enters the PV product as
-// a bf16 pair hi + lo, so that O and the log-sum-exp agree with fp32 weights
-// to about 16 bits.  With bf16 output a single bf16 weight is used: its
-// rounding (half a bf16 ulp, relative) is of the size of the output's own
-// bf16 storage rounding.
+// Two forms of the PV product:
+//   EXACT (fp32 output, and the backward's recompute of the sparse branch):
+//     V is the caller's bf16 tensor; the row sums add the fp32 weights and
+//     each weight enters the PV product as a bf16 pair hi + lo, so that O and
+//     the log-sum-exp agree with fp32 weights to about 16 bits.
+//   otherwise (bf16 output): V is pass 1's fp16 copy (exact for |v| < 2^16)
+//     and each weight is one fp16 value (11 significant bits, against 8 for
+//     a bf16 weight, whose rounding alone would cost up to about 2e-2 of the
+//     output RMS on these shapes), on the f16 MFMA at the bf16 rate.  Heads
+//     whose copy would overflow (a |v| >= 2^16, flagged per pass-1 chunk) are
+//     skipped here and computed by the EXACT form launched after it with the
+//     same flags, which then runs those heads only.
 template <int D, int G, int S, bool SPARSE, bool LOWRANK, bool ACCUM, bool OUTF32, bool EXACT = OUTF32>
 __global__ __launch_bounds__(128 * G, 2) void k_attn(AttnArgs args) {
   constexpr int CH = D / 8;
@@ -1134,10 +1181,6 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn(AttnArgs args) {
   static_assert(OPS >= 1 && (64 * CH) % NT == 0, "tile split");
   static_assert(S == 2 || S == 4, "ring depth");
   constexpr int LMAX = 2048;  // union-list entries staged in LDS (longer lists read the tail from HBM)
-#ifndef ROLA_ATTN_HALVES
-#define ROLA_ATTN_HALVES 0
-#endif
-  constexpr bool HALVES = ROLA_ATTN_HALVES != 0;
   __shared__ __attribute__((aligned(1024))) uint16_t ring[SPARSE ? S * 2 * TILE : 8];
   __shared__ int32_t slist[SPARSE ? LMAX + 8 : 4];  // + room for the reads ahead past the end
   __shared__ __attribute__((aligned(16))) float sfreq[D / 2];  // rotary inverse frequency per pair
@@ -1152,6 +1195,14 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn(AttnArgs args) {
   if (bh64 >= args.bh_count || group >= args.ngroups) return;
   const int bh = (int)bh64;
   const int64_t gidx = (int64_t)bh * args.ngroups + group;
+  // any range flag of this head's fp16 V copy set
+  auto v_overflow = [&]() __attribute__((always_inline)) -> bool {
+    int f = 0;
+    for (int i = lane; i < args.nflags; i += 64) f |= args.vovf[(int64_t)bh * args.nflags + i];
+    return __builtin_amdgcn_ballot_w64(f != 0) != 0;
+  };
+  // the bf16 form as the fallback of the fp16 one: only the flagged heads
+  if (SPARSE && EXACT && args.vovf && !v_overflow()) return;
   // wave-uniform values through the scalar cache (the schedule is written by
   // earlier kernels and only read here)
   typedef const __attribute__((address_space(4))) int32_t *cint_p;
@@ -1181,7 +1232,9 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn(AttnArgs args) {
     const int32_t *list = args.ulist + gidx * args.list_stride;
     const int U = ((cint_p)args.ucount)[gidx];
     const uint16_t *Kb = args.k + base;
-    const uint16_t *Vb = args.v + base;
+    // V: the caller's bf16 tensor, or its fp16 copy [BH][n_pad][D]
+    const uint16_t *Vb = EXACT ? args.v + base : args.vh + (int64_t)bh * args.nb * 64 * D;
+    const int64_t vstride = EXACT ? args.stride_n : D;
     const float c = args.scale_log2e;
     // per-lane LDS element offsets of the MFMA operands inside a tile:
     // K rows l%32 (+32 rows for the second key tile) at chunk 2s+g;
@@ -1196,7 +1249,7 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn(AttnArgs args) {
       const int cidx = o * NT + tid;
       const int row = cidx / CH, pc = cidx % CH;
       gk[o] = (uint32_t)(((int64_t)row * args.stride_n + ((pc ^ swz_k<D>(row)) * 8)) * 2);
-      gv[o] = (uint32_t)(((int64_t)row * args.stride_n + ((pc ^ swz_v<D>(row)) * 8)) * 2);
+      gv[o] = (uint32_t)(((int64_t)row * vstride + ((pc ^ swz_v<D>(row)) * 8)) * 2);
     }
 #pragma unroll
     for (int s2 = 0; s2 < NS; ++s2) {
@@ -1214,7 +1267,7 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn(AttnArgs args) {
       uint16_t *slot = ring + (t % S) * (2 * TILE);
       const int64_t jrow = (int64_t)j * 64;
       if (jrow + 64 <= args.n_tokens) {
-        const uint16_t *kj = Kb + jrow * args.stride_n, *vj = Vb + jrow * args.stride_n;
+        const uint16_t *kj = Kb + jrow * args.stride_n, *vj = Vb + jrow * vstride;
         const uint32_t m0 = ring_lds + (uint32_t)((t % S) * (2 * TILE) * 2) + (uint32_t)wave_s * 1024u;
 #pragma unroll
         for (int o = 0; o < OPS; ++o) {
@@ -1228,9 +1281,9 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn(AttnArgs args) {
           const int row = cidx / CH, pc = cidx % CH;
           // rows past N (tail block) are copied from row N-1: finite
           // values, masked out of the softmax
-          const int64_t src = min(jrow + row, args.n_tokens - 1) * args.stride_n;
-          lds_dma16(Kb + src + ((pc ^ swz_k<D>(row)) * 8), slot + (o * NT + wave * 64) * 8);
-          lds_dma16(Vb + src + ((pc ^ swz_v<D>(row)) * 8), slot + TILE + (o * NT + wave * 64) * 8);
+          const int64_t src = min(jrow + row, args.n_tokens - 1);
+          lds_dma16(Kb + src * args.stride_n + ((pc ^ swz_k<D>(row)) * 8), slot + (o * NT + wave * 64) * 8);
+          lds_dma16(Vb + src * vstride + ((pc ^ swz_v<D>(row)) * 8), slot + TILE + (o * NT + wave * 64) * 8);
         }
       }
     };
@@ -1252,7 +1305,11 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn(AttnArgs args) {
         const int i = r * NT + tid;
         lv[r] = i < min(U, LMAX) ? list[i] : 0;
       }
+      // the fp16 form leaves flagged heads to the bf16 form (checked here,
+      // under the prologue's copies, which are complete before the return)
+      const bool skip = !EXACT && args.vovf && v_overflow();
       wait_vmcnt<0>();
+      if (skip) return;
 #pragma unroll
       for (int r = 0; r < (LMAX + NT - 1) / NT; ++r) {
         const int i = r * NT + tid;
@@ -1304,17 +1361,20 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn(AttnArgs args) {
         }
         // ---- online softmax, base 2, against a lazy reference: weights
         // are exp2(s*c - m_ref) with m_ref an integer that moves only when the
-        // tile max exceeds it by more than 64 (or on the first tile), so O is
-        // almost never rescaled and the rescale, when it happens, is by an
-        // exact power of two.  Weights stay below 2^64: no overflow in fp32.
-        // The row sum is taken over the same bf16 weights the PV product uses.
+        // tile max exceeds it by more than W (or on the first tile), so O is
+        // rarely rescaled and the rescale, when it happens, is by an exact
+        // power of two.  Weights stay below 2^W: W = 64 for the fp32 weights
+        // of the EXACT form, W = 15 for fp16 weights (largest finite 65504).
+        // fp16 weights below 2^-24 vanish; relative to the row sum (at least
+        // 1/2) they are negligible.
+        constexpr float W = EXACT ? 64.0f : 15.0f;
         float mx0 = -INFINITY, mx1 = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx0 = fmaxf(mx0, sacc0[i]);
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx1 = fmaxf(mx1, sacc1[i]);
         const float mx = pair_max32(fmaxf(mx0, mx1)) * c;
-        const bool grow = mx > m_run + 64.0f;  // always true on the first tile (m_run = -inf)
+        const bool grow = mx > m_run + W;  // always true on the first tile (m_run = -inf)
         if (__builtin_amdgcn_ballot_w64(grow)) {
           const float m_new = grow ? ceilf(mx) : m_run;
           const float alpha = fast_exp2(m_run - m_new);
@@ -1324,14 +1384,14 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn(AttnArgs args) {
           for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
         }
         const float negm = -m_run;
-        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+        const f16x2 ones = {(__fp16)1.0f, (__fp16)1.0f};
         float psum = 0.0f;
         // ---- weights for 16 keys at a time, each step feeding 4 PV MFMAs
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           const f32x16 &src = (s < 2) ? sacc0 : sacc1;
           bf16x8 pw, plo;
+          f16x8 ph;
           if constexpr (EXACT) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -1341,12 +1401,17 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn(AttnArgs args) {
               psum += wv;
             }
           } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) pw[e] = (__bf16)fast_exp2(__builtin_fmaf(src[8 * (s & 1) + e], c, negm));
+            // fp16 weights rounded toward zero (one packed conversion per
+            // pair); the row sum adds the same rounded values, so the
+            // rounding's common bias cancels in PV / l
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const bf16x2 pr = {pw[2 * e], pw[2 * e + 1]};
-              psum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, psum, false);
+              const int i = 8 * (s & 1) + 2 * e;
+              const f16x2 pr = __builtin_amdgcn_cvt_pkrtz(fast_exp2(__builtin_fmaf(src[i], c, negm)),
+                                                          fast_exp2(__builtin_fmaf(src[i + 1], c, negm)));
+              ph[2 * e] = pr[0];
+              ph[2 * e + 1] = pr[1];
+              psum = __builtin_amdgcn_fdot2(pr, ones, psum, false);
             }
           }
           // the step's V^T operands (2*DT transposing reads) before its MFMAs
@@ -1356,119 +1421,15 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn(AttnArgs args) {
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) {
-            oacc[dt] = mfma_bf16(va[dt], pw, oacc[dt]);
-            if constexpr (EXACT) oacc[dt] = mfma_bf16(va[dt], plo, oacc[dt]);
+            if constexpr (EXACT) {
+              oacc[dt] = mfma_bf16(va[dt], pw, oacc[dt]);
+              oacc[dt] = mfma_bf16(va[dt], plo, oacc[dt]);
+            } else {
+              oacc[dt] = mfma_f16(__builtin_bit_cast(f16x8, va[dt]), ph, oacc[dt]);
+            }
           }
         }
         l_run += psum;
-      };
-      // The same tile with its two 32-key halves pipelined inside the wave:
-      // S of half B is issued under the softmax of half A, and the PV product
-      // of half A under the softmax of half B, so the wave has independent
-      // MFMA and VALU work side by side.  The weights of a half are formed
-      // speculatively with the current reference; when the half's max grows
-      // the reference (rare after the first tile), O and l are rescaled and
-      // the half's weights formed again.
-      auto tile_h = [&](int t, int ent) __attribute__((always_inline)) {
-        const int j = ent & 0xffff;
-        const uint16_t *sK = ring + (t % S) * (2 * TILE);
-        const uint16_t *sV = sK + TILE;
-        const bool tail = (int64_t)(j + 1) * 64 > args.n_tokens;
-        const int lim = (int)(args.n_tokens - (int64_t)j * 64) - 4 * g;
-        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-        // weights of one half (16 accumulator values -> two 8-key steps) and their sum
-        auto weights = [&](const f32x16 &src, bf16x8 (&pw)[2]) __attribute__((always_inline)) -> float {
-          const float negm = -m_run;
-          float ps = 0.0f;
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) pw[h][e] = (__bf16)fast_exp2(__builtin_fmaf(src[8 * h + e], c, negm));
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const bf16x2 pr = {pw[h][2 * e], pw[h][2 * e + 1]};
-              ps = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ps, false);
-            }
-          }
-          return ps;
-        };
-        auto half_max = [&](const f32x16 &src) __attribute__((always_inline)) -> float {
-          float a = fmaxf(src[0], src[1]), b = fmaxf(src[2], src[3]);
-#pragma unroll
-          for (int i = 4; i < 16; i += 4) {
-            a = fmaxf(a, fmaxf(src[i], src[i + 1]));
-            b = fmaxf(b, fmaxf(src[i + 2], src[i + 3]));
-          }
-          return pair_max32(fmaxf(a, b)) * c;
-        };
-        // the reference moves when the half's max exceeds it by more than 64;
-        // returns true when it moved (O and l rescaled)
-        auto settle = [&](float mx) __attribute__((always_inline)) -> bool {
-          const bool grow = mx > m_run + 64.0f;
-          if (__builtin_amdgcn_ballot_w64(grow)) {
-            const float m_new = grow ? ceilf(mx) : m_run;
-            const float alpha = fast_exp2(m_run - m_new);
-            m_run = m_new;
-            l_run *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
-            return true;
-          }
-          return false;
-        };
-        auto pv_step = [&](int s, const bf16x8 &pw) __attribute__((always_inline)) {
-          bf16x8 va[DT];
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) va[dt] = vt_operand_at(sV + voff[dt] + s * 16 * D, 8 * D);
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) oacc[dt] = mfma_bf16(va[dt], pw, oacc[dt]);
-        };
-        // ---- S of half A (keys 0-31)
-        f32x16 sa = f32x16{}, sb = f32x16{};
-        {
-          bf16x8 ka[NS];
-#pragma unroll
-          for (int s2 = 0; s2 < NS; ++s2) ka[s2] = *(const bf16x8 *)(sK + koff[s2]);
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int s2 = 0; s2 < NS; ++s2) sa = mfma_bf16(ka[s2], qreg[s2], sa);
-        }
-        bf16x8 kb2[NS];
-#pragma unroll
-        for (int s2 = 0; s2 < NS; ++s2) kb2[s2] = *(const bf16x8 *)(sK + koff[s2] + 32 * D);
-        if (tail) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (8 * (i >> 2) + (i & 3) >= lim) sa[i] = -INFINITY;
-        }
-        // ---- S of half B under the softmax of half A
-#pragma unroll
-        for (int s2 = 0; s2 < NS; ++s2) sb = mfma_bf16(kb2[s2], qreg[s2], sb);
-        bf16x8 pa[2];
-        const float mxa = half_max(sa);
-        float psa = weights(sa, pa);
-        // the speculative weights are formed here, under the S MFMAs of half B,
-        // even though the rare growth path below forms them again
-        asm volatile("" ::"v"(pa[0]), "v"(pa[1]), "v"(psa));
-        if (settle(mxa)) psa = weights(sa, pa);
-        l_run += psa;
-        if (tail) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (8 * (i >> 2) + (i & 3) + 32 >= lim) sb[i] = -INFINITY;
-        }
-        // ---- PV of half A under the softmax of half B
-        pv_step(0, pa[0]);
-        pv_step(1, pa[1]);
-        bf16x8 pb[2];
-        const float mxb = half_max(sb);
-        float psb = weights(sb, pb);
-        asm volatile("" ::"v"(pb[0]), "v"(pb[1]), "v"(psb));
-        if (settle(mxb)) psb = weights(sb, pb);
-        l_run += psb;
-        pv_step(2, pb[0]);
-        pv_step(3, pb[1]);
       };
       if constexpr (S == 4) {
       // Two tiles per barrier: iteration k consumes tiles 2k and 2k+1 and,
@@ -1504,13 +1465,8 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn(AttnArgs args) {
         }
         const bool m0 = active && ((e0 >> (16 + member)) & 1);
         const bool m1 = active && t2 + 1 < U && ((e1 >> (16 + member)) & 1);
-        if constexpr (HALVES && !EXACT) {
-          if (m0) tile_h(t2, e0);
-          if (m1) tile_h(t2 + 1, e1);
-        } else {
-          if (m0) tile(t2, e0);
-          if (m1) tile(t2 + 1, e1);
-        }
+        if (m0) tile(t2, e0);
+        if (m1) tile(t2 + 1, e1);
       }
       } else {
       // One tile per barrier in a two-slot ring (half the LDS, so two
@@ -1536,10 +1492,7 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn(AttnArgs args) {
           if (t >= 1 && t + 1 < U) issue(t + 1);
           e = entry(t);
         }
-        if (active && ((e >> (16 + member)) & 1)) {
-          if constexpr (HALVES && !EXACT) tile_h(t, e);
-          else tile(t, e);
-        }
+        if (active && ((e >> (16 + member)) & 1)) tile(t, e);
       }
       }
     };
@@ -1970,14 +1923,20 @@ void launch_setup(const SetupArgs &a, hipStream_t st) {
 template <int D>
 static void pass1_d(const Pass1Args &a, int nchunks, int bh, bool pool, bool state, bool quant,
                     hipStream_t st) {
-  dim3 grid(nchunks, bh), block(256);
+  dim3 grid(nchunks, bh), block(256), block5(320);
   const bool blk = a.blk_state != nullptr;
+  const bool vh = a.vh != nullptr && !quant;
   if (pool && state && quant) {
-    if (blk) hipLaunchKernelGGL((k_pass1<D, true, true, true, true>), grid, dim3(320), 0, st, a);
-    else hipLaunchKernelGGL((k_pass1<D, true, true, true, false>), grid, dim3(320), 0, st, a);
+    if (blk) hipLaunchKernelGGL((k_pass1<D, true, true, true, true>), grid, block5, 0, st, a);
+    else hipLaunchKernelGGL((k_pass1<D, true, true, true, false>), grid, block5, 0, st, a);
+  } else if (pool && state && vh) {
+    if (blk) hipLaunchKernelGGL((k_pass1<D, true, true, false, true, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_pass1<D, true, true, false, false, true>), grid, block, 0, st, a);
   } else if (pool && state) {
     if (blk) hipLaunchKernelGGL((k_pass1<D, true, true, false, true>), grid, block, 0, st, a);
     else hipLaunchKernelGGL((k_pass1<D, true, true, false, false>), grid, block, 0, st, a);
+  } else if (!pool && !state && vh) {
+    hipLaunchKernelGGL((k_pass1<D, false, false, false, false, true>), grid, dim3(128), 0, st, a);
   } else if (pool) {
     hipLaunchKernelGGL((k_pass1<D, true, false, false, false>), grid, block, 0, st, a);
   } else {
@@ -2053,16 +2012,26 @@ void launch_schedule(const int32_t *map, int nb, int kb, int G, int ngroups, int
   }
 }
 
+// fp32 output: the EXACT form.  bf16 output with the sparse branch: the fp16
+// form, then the EXACT form for the heads whose fp16 V copy is flagged (an
+// empty pass, each workgroup reading its head's flags, when none is).
+template <int D, int G, int S, bool SPARSE, bool LOWRANK, bool ACCUM>
+static void attn_d3(const AttnArgs &a, bool outf32, hipStream_t st) {
+  dim3 grid((unsigned)(8 * a.groups_per_xcd * a.bh_count)), block(128 * G);
+  if (outf32) {
+    hipLaunchKernelGGL((k_attn<D, G, S, SPARSE, LOWRANK, ACCUM, true, true>), grid, block, 0, st, a);
+  } else if (!SPARSE) {
+    hipLaunchKernelGGL((k_attn<D, G, S, SPARSE, LOWRANK, ACCUM, false, false>), grid, block, 0, st, a);
+  } else {
+    hipLaunchKernelGGL((k_attn<D, G, S, SPARSE, LOWRANK, ACCUM, false, false>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((k_attn<D, G, S, SPARSE, LOWRANK, ACCUM, false, true>), grid, block, 0, st, a);
+  }
+}
+
 template <int D, int G, int S, bool SPARSE, bool LOWRANK>
 static void attn_d2(const AttnArgs &a, bool accum, bool outf32, hipStream_t st) {
-  dim3 grid((unsigned)(8 * a.groups_per_xcd * a.bh_count)), block(128 * G);
-  if (accum) {
-    if (outf32) hipLaunchKernelGGL((k_attn<D, G, S, SPARSE, LOWRANK, true, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((k_attn<D, G, S, SPARSE, LOWRANK, true, false>), grid, block, 0, st, a);
-  } else {
-    if (outf32) hipLaunchKernelGGL((k_attn<D, G, S, SPARSE, LOWRANK, false, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((k_attn<D, G, S, SPARSE, LOWRANK, false, false>), grid, block, 0, st, a);
-  }
+  if (accum) attn_d3<D, G, S, SPARSE, LOWRANK, true>(a, outf32, st);
+  else attn_d3<D, G, S, SPARSE, LOWRANK, false>(a, outf32, st);
 }
 
 template <int D, int G, int S>
@@ -2077,8 +2046,6 @@ int attn_group_size() { return ROLA_ATTN_G; }
 
 void launch_attn(const AttnArgs &a, int D, bool sparse, bool lowrank, bool accum, bool outf32,
                  hipStream_t st) {
-  // fp32 output (and the backward's recompute, which asks for fp32 output and
-  // the log-sum-exp) takes the split-weight form of the kernel (EXACT = OUTF32)
   if (D == 64) attn_d<64, ROLA_ATTN_G, ROLA_ATTN_S>(a, sparse, lowrank, accum, outf32, st);
   else attn_d<128, ROLA_ATTN_G, ROLA_ATTN_S>(a, sparse, lowrank, accum, outf32, st);
 }

@@ -209,6 +209,61 @@ def test_invalid_rows_of_inputs_are_ignored():
     assert torch.equal(a, b)
 
 
+def test_standalone_sparse_bf16_output():
+    """rola_sparse_attn with bf16 output (its own fp16 copy of V) against the oracle's sparse rows."""
+    from sparse_rank_attention_amd import rola
+    torch = _torch()
+    say("standalone sparse, bf16 out")
+    w = small_workload((5, 9, 13), D=128, H=2, rank=32, topk=0.3, kind="field")
+    q, k, v = W.make_qkv(w)
+    kb = oracle.keep_blocks(w.topk, w.nb)
+    m_ref = oracle.block_map(q[0], k[0], w.n_tokens, kb)
+    bmap = torch.from_numpy(m_ref).cuda().reshape(w.batch, w.heads, w.nb, kb)
+    out = rola.rola_sparse_attn(dev(q), dev(k), dev(v), bmap, w.grid, cfg_of(w))
+    torch.cuda.synchronize()
+    qf, kf, vf = (oracle.widen_bf16(x[0]) for x in (q, k, v))
+    rows = np.arange(w.n_tokens)
+    for h in range(w.heads):
+        ref = oracle.sparse_rows(qf[h:h + 1], kf[h:h + 1], vf[h:h + 1], m_ref[h:h + 1], w.n_tokens, rows)
+        assert bound_ratio(host_f64(out)[0, h, :w.n_tokens], ref, True) <= 1.0, h
+
+
+def test_v_beyond_fp16_range_takes_bf16_form():
+    """A head whose V holds a value at or beyond 2^16 (outside fp16) is computed by the
+    bf16 form: its bf16 output is the fp32 output rounded to bf16, bit for bit, and
+    every head still meets the bar; the fused and the standalone calls alike."""
+    from sparse_rank_attention_amd import rola
+    torch = _torch()
+    say("V beyond fp16 range")
+    w = small_workload((5, 9, 13), D=128, H=3, rank=32, topk=0.3, kind="field")
+    q, k, v = W.make_qkv(w)
+    v = v.copy()
+    big = np.array([1.0e5, -7.0e4], dtype=np.float32).view(np.uint32) >> 16  # bf16 99840, -70144
+    v[0, 1, 100, 3] = big[0]
+    v[0, 2, w.n_tokens - 1, 77] = big[1]
+    wq, wk = W.make_proj(w)
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    wqd, wkd = torch.from_numpy(wq).cuda(), torch.from_numpy(wk).cuda()
+    kb = oracle.keep_blocks(w.topk, w.nb)
+    o16 = rola.rola_forward(qd, kd, vd, wqd, wkd, w.grid, cfg_of(w))
+    o32 = rola.rola_forward(qd, kd, vd, wqd, wkd, w.grid, cfg_of(w, out_dtype=rola.ROLA_OUT_F32))
+    m_ref = oracle.block_map(q[0], k[0], w.n_tokens, kb)
+    bmap = torch.from_numpy(m_ref).cuda().reshape(w.batch, w.heads, w.nb, kb)
+    s16 = rola.rola_sparse_attn(qd, kd, vd, bmap, w.grid, cfg_of(w))
+    s32 = rola.rola_sparse_attn(qd, kd, vd, bmap, w.grid, cfg_of(w, out_dtype=rola.ROLA_OUT_F32))
+    torch.cuda.synchronize()
+    for a, b in ((o16, o32), (s16, s32)):
+        for h in (1, 2):
+            assert torch.equal(a[0, h], b[0, h].to(torch.bfloat16)), h
+    _, o_ref = oracle.forward(q[0], k[0], v[0], wq, wk, w.n_tokens, kb, w.grid)
+    qf, kf, vf = (oracle.widen_bf16(x[0]) for x in (q, k, v))
+    rows = np.arange(w.n_tokens)
+    for h in range(w.heads):
+        assert bound_ratio(host_f64(o16)[0, h, :w.n_tokens], o_ref[h, :w.n_tokens], True) <= 1.0, h
+        sp = oracle.sparse_rows(qf[h:h + 1], kf[h:h + 1], vf[h:h + 1], m_ref[h:h + 1], w.n_tokens, rows)
+        assert bound_ratio(host_f64(s16)[0, h, :w.n_tokens], sp, True) <= 1.0, h
+
+
 # --------------------------------------------------------------- full sizes
 FULL = ["wan13b_480p", "wan14b_480p", "wan14b_720p"]
 _cache = {}
@@ -278,6 +333,31 @@ def test_full_size_every_block_map(name):
     got = bmap.cpu().numpy()[0]
     bad = [h for h in range(w.heads) if not np.array_equal(got[h], m_ref[h])]
     assert not bad, "heads with a differing map: %s" % bad
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_every_row_bf16(name):
+    """Every valid row of the first, middle and last head of the benchmarked launch (bf16
+    output) against the bf16 bound, 2e-2 * rms * (1 + 2^-8) + 2^-8 |O_ref|."""
+    from sparse_rank_attention_amd import rola
+    torch = _torch()
+    w, (q, k, v), (wq, wk) = _full_inputs(name)
+    kb = oracle.keep_blocks(w.topk, w.nb)
+    out = rola.rola_forward(dev(q), dev(k), dev(v), torch.from_numpy(wq).cuda(), torch.from_numpy(wk).cuda(),
+                            w.grid, cfg_of(w))
+    torch.cuda.synchronize()
+    rows = np.arange(w.n_tokens)
+    res = {}
+    for h in sorted({0, w.heads // 2, w.heads - 1}):
+        say("full size bf16 rows", name, "head", h)
+        m_ref = oracle.block_map(q[0, h:h + 1], k[0, h:h + 1], w.n_tokens, kb)
+        qf, kf, vf = (oracle.widen_bf16(x[0, h:h + 1]) for x in (q, k, v))
+        S, z = oracle.lowrank_state(kf, vf, wk, w.n_tokens, w.grid)
+        ref = oracle.sparse_rows(qf, kf, vf, m_ref, w.n_tokens, rows) + oracle.lowrank_rows(qf, wq, S, z, w.grid, rows)
+        got = out[0, h, :w.n_tokens].float().cpu().numpy().astype(np.float64)
+        res[h] = (round(rel_err(got, ref), 5), round(bound_ratio(got, ref, True), 4))
+        assert res[h][1] <= 1.0, (h, res[h])
+    say("full size bf16 rows", name, "(err/rms, err/bound) per head", res)
 
 
 @pytest.mark.parametrize("name", FULL)
