@@ -626,6 +626,13 @@ int32_t rola_backward(const rola_problem *prob, const rola_config *cfg, const vo
   a.scale_log2e = (float)((double)P.scale * 1.4426950408889634);
   a.rope = rope_args(P, ws);
   a.map = block_idx;
+  // the recompute above left the group schedule of this map in the workspace
+  a.ugroup = (const int32_t *)(ws + P.off_ugroup);
+  a.ucount = (const int32_t *)(ws + P.off_ucount);
+  a.ulist = (const int32_t *)(ws + P.off_ulist);
+  a.ngroups = P.ngroups;
+  a.groups_per_xcd = (P.ngroups + 7) / 8;
+  a.list_stride = P.list_stride;
   a.wqT = (const uint16_t *)(ws + P.off_wqT); a.wkT = (const uint16_t *)(ws + P.off_wkT);
   a.st = (const uint16_t *)(ws + P.off_st);
   a.s32 = (const float *)(ws + P.b_s32); a.z = (const float *)(ws + P.off_z);

@@ -666,6 +666,180 @@ __global__ __launch_bounds__(128) void k_bwd_dq(BwdArgs a) {
   }
 }
 
+// ------------------------------------------------------------- k_bwd_dqg
+// Sparse dq on the forward's group schedule (k_order, k_group, k_union of the
+// recompute): one workgroup per group of G query blocks, waves 2m and 2m+1
+// owning rows 0-31 and 32-63 of member m, walks the group's union list two
+// tiles per barrier through a four-slot ring of K and V tiles, as k_attn
+// does, so that each key block is copied once for every member that kept it
+// and two waves share each SIMD.  Per listed block and 32-key half, a member
+// wave forms S^T = K Q^T and dP^T = V dO^T (K and V rows), dS^T = P^T
+// (dP^T - D) as a bf16 pair hi + lo, and dq^T += K^T dS^T (K read
+// transposed).  Unions that can be longer than the LDS copy (kDqgLmax
+// entries) take k_bwd_dq.
+constexpr int kDqgLmax = 2048;
+
+template <int D, int G>
+__global__ __launch_bounds__(128 * G, 2) void k_bwd_dqg(BwdArgs a) {
+  constexpr int NS = D / 16, DT = D / 32, TILE = 64 * D, CH = D / 8;
+  constexpr int NT = 128 * G;
+  constexpr int OPS = (64 * CH) / NT;  // copies per thread per tensor per tile
+  static_assert(OPS >= 1 && (64 * CH) % NT == 0, "tile split");
+  constexpr int S = 4;
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[S * 2 * TILE];
+  __shared__ int32_t slist[kDqgLmax + 8];  // + room for the reads ahead past the end
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5, col = lane & 31;
+  const int member = wave >> 1, half = wave & 1;
+  const int64_t L = blockIdx.x;
+  const int64_t sidx = L / 8;
+  const int64_t bh64 = sidx / a.groups_per_xcd;
+  const int64_t group = (L % 8) * a.groups_per_xcd + sidx % a.groups_per_xcd;
+  if (bh64 >= a.bh_count || group >= a.ngroups) return;
+  const int bh = (int)bh64;
+  const int64_t gidx = (int64_t)bh * a.ngroups + group;
+  typedef const __attribute__((address_space(4))) int32_t *cint_p;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int qb = ((cint_p)a.ugroup)[gidx * G + (wave_u >> 1)];
+  const bool active = qb >= 0;
+  const int b = bh / a.heads, h = bh % a.heads;
+  const int64_t base = (int64_t)b * a.stride_b + (int64_t)h * a.stride_h;
+  const int64_t n_pad = (int64_t)a.nb * 64;
+  const int64_t n = (int64_t)(active ? qb : 0) * 64 + 32 * half + col;
+  const bool valid = active && n < a.n_tokens;
+  const int64_t nc = n < a.n_tokens ? n : a.n_tokens - 1;
+  const int64_t row = (int64_t)bh * n_pad + n;
+  const int32_t *list = a.ulist + gidx * a.list_stride;
+  const int U = ((cint_p)a.ucount)[gidx];
+  const uint16_t *Kb = a.k + base, *Vb = a.v + base;
+  // this thread's byte offsets inside a key block (V-style swizzle, the
+  // layout row_operand and vt_operand read)
+  uint32_t goff[OPS];
+#pragma unroll
+  for (int o = 0; o < OPS; ++o) {
+    const int cidx = o * NT + tid;
+    const int r = cidx / CH, pc = cidx % CH;
+    goff[o] = (uint32_t)(((int64_t)r * a.stride_n + ((pc ^ swz_v<D>(r)) * 8)) * 2);
+  }
+  const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_addr(ring));
+  auto issue_j = [&](int t, int j) __attribute__((always_inline)) {
+    uint16_t *slot = ring + (t % S) * (2 * TILE);
+    const int64_t jrow = (int64_t)j * 64;
+    if (jrow + 64 <= a.n_tokens) {
+      const uint16_t *kj = Kb + jrow * a.stride_n, *vj = Vb + jrow * a.stride_n;
+      const uint32_t m0 = ring_lds + (uint32_t)((t % S) * (2 * TILE) * 2) + (uint32_t)wave_u * 1024u;
+#pragma unroll
+      for (int o = 0; o < OPS; ++o) {
+        lds_dma16_m0(kj, goff[o], m0 + (uint32_t)(o * NT * 16));
+        lds_dma16_m0(vj, goff[o], m0 + (uint32_t)(TILE * 2 + o * NT * 16));
+      }
+    } else {
+#pragma unroll
+      for (int o = 0; o < OPS; ++o) {
+        const int cidx = o * NT + tid;
+        const int r = cidx / CH, pc = cidx % CH;
+        // rows past N (tail block) are copied from row N-1: finite values,
+        // masked out of P
+        const int64_t src = min(jrow + r, a.n_tokens - 1) * a.stride_n + ((pc ^ swz_v<D>(r)) * 8);
+        lds_dma16(Kb + src, slot + (o * NT + wave * 64) * 8);
+        lds_dma16(Vb + src, slot + TILE + (o * NT + wave * 64) * 8);
+      }
+    }
+  };
+  // prologue: tiles 0 and 1, this wave's Q and dO rows and the list in flight together
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+    if (t < U) issue_j(t, ((cint_p)list)[t] & 0xffff);
+  bf16x8 qreg[NS], doreg[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    qreg[s] = *(const bf16x8 *)(a.q + base + nc * a.stride_n + 16 * s + 8 * g);
+    doreg[s] = *(const bf16x8 *)(a.dob + row * D + 16 * s + 8 * g);
+  }
+  const float lse2 = valid ? a.lse[row] : 0.0f;
+  const float dn = a.dn[row];
+  {
+    int32_t lv[(kDqgLmax + NT - 1) / NT];
+#pragma unroll
+    for (int r = 0; r < (kDqgLmax + NT - 1) / NT; ++r) {
+      const int i = r * NT + tid;
+      lv[r] = i < U ? list[i] : 0;
+    }
+    wait_vmcnt<0>();
+#pragma unroll
+    for (int r = 0; r < (kDqgLmax + NT - 1) / NT; ++r) {
+      const int i = r * NT + tid;
+      if (i < U) slist[i] = lv[r];
+    }
+  }
+  __syncthreads();  // tiles 0 and 1 and the list complete for every wave
+  f32x16 dq[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dq[dt] = f32x16{};
+  const float c = a.scale_log2e;
+  auto tile = [&](int t, int ent) __attribute__((always_inline)) {
+    const int j = ent & 0xffff;
+    const uint16_t *sK = ring + (t % S) * (2 * TILE), *sV = sK + TILE;
+    const int lim = (int)min<int64_t>(64, a.n_tokens - (int64_t)j * 64);  // valid keys of the block
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      f32x16 sacc = f32x16{}, dpacc = f32x16{};
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        sacc = mfma_bf16(row_operand<D>(sK, 32 * h2 + col, s, g), qreg[s], sacc);
+        dpacc = mfma_bf16(row_operand<D>(sV, 32 * h2 + col, s, g), doreg[s], dpacc);
+      }
+      bf16x8 dshi[2], dslo[2];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = 32 * h2 + 8 * (i >> 2) + 4 * g + (i & 3);
+        const float pv = (valid && key < lim) ? fast_exp2(__builtin_fmaf(sacc[i], c, -lse2)) : 0.0f;
+        split_bf16(pv * (dpacc[i] - dn), dshi[i >> 3], dslo[i >> 3], i & 7);
+      }
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const bf16x8 kt = vt_operand<D>(sK, 2 * h2 + s2, dt, lane);
+          dq[dt] = mfma_bf16(kt, dshi[s2], dq[dt]);
+          dq[dt] = mfma_bf16(kt, dslo[s2], dq[dt]);
+        }
+    }
+  };
+  // two tiles per barrier: iteration k consumes tiles 2k and 2k+1 and first
+  // copies 2k+2 and 2k+3 into the slots of 2k-2 and 2k-1 (free once every
+  // wave has passed the barrier); list entries are read one iteration ahead
+  int ea = slist[0], eb = slist[1], ec = slist[2], ed = slist[3];
+  for (int t2 = 0; t2 < U; t2 += 2) {
+    wait_vmcnt<0>();  // this wave's copies of tiles t2, t2+1
+    barrier_lds();    // both visible to all waves; every wave is done with t2-2, t2-1
+    const int e0 = ea, e1 = eb;
+    if (t2 + 2 < U) issue_j(t2 + 2, __builtin_amdgcn_readfirstlane(ec & 0xffff));
+    if (t2 + 3 < U) issue_j(t2 + 3, __builtin_amdgcn_readfirstlane(ed & 0xffff));
+    ea = ec;
+    eb = ed;
+    ec = slist[t2 + 4];
+    ed = slist[t2 + 5];
+    const bool m0 = active && ((e0 >> (16 + member)) & 1);
+    const bool m1 = active && t2 + 1 < U && ((e1 >> (16 + member)) & 1);
+    if (m0) tile(t2, e0);
+    if (m1) tile(t2 + 1, e1);
+  }
+  if (!active) return;
+  uint16_t *orow = a.dq + base + n * a.stride_n;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d0 = 32 * dt + 8 * q4 + 4 * g;
+      const f32x4 lr = *(const f32x4 *)(a.dqp + row * D + d0);
+      float v[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) v[jj] = valid ? a.scale * dq[dt][4 * q4 + jj] + lr[jj] : 0.0f;
+      *(uint2 *)(orow + d0) = pack_bf16x4(v[0], v[1], v[2], v[3]);
+    }
+  }
+}
+
 // ------------------------------------------------------------ k_bwd_tmap
 // For each key block j of a head: the query blocks that kept it, ascending.
 // k_bwd_mapbits turns each map row into a bitset over key blocks; k_bwd_tmap
@@ -905,6 +1079,14 @@ void launch_bwd_key(const BwdArgs &a, int D, hipStream_t st) {
 }
 
 void launch_bwd_dq(const BwdArgs &a, int D, hipStream_t st) {
+  // a group's union has at most min(G * kb, nb) entries
+  if (a.ugroup && (a.list_stride < a.nb ? a.list_stride : (int64_t)a.nb) <= kDqgLmax && attn_group_size() == 4) {
+    // the forward's group schedule: one workgroup of 8 waves per group
+    const dim3 grid((unsigned)(8 * a.groups_per_xcd * a.bh_count));
+    if (D == 64) hipLaunchKernelGGL((k_bwd_dqg<64, 4>), grid, dim3(512), 0, st, a);
+    else hipLaunchKernelGGL((k_bwd_dqg<128, 4>), grid, dim3(512), 0, st, a);
+    return;
+  }
   const dim3 grid((unsigned)a.nb, (unsigned)a.bh_count);
   if (D == 64) hipLaunchKernelGGL(k_bwd_dq<64>, grid, dim3(128), 0, st, a);
   else hipLaunchKernelGGL(k_bwd_dq<128>, grid, dim3(128), 0, st, a);

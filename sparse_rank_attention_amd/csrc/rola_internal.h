@@ -167,6 +167,9 @@ struct BwdArgs {
   float scale, scale_log2e;
   RopeArgsHost rope;
   const int32_t *map;  // [BH][nb][kb], ascending
+  // the forward's group schedule of the same map (see AttnArgs), or NULL
+  const int32_t *ugroup, *ucount, *ulist;
+  int64_t ngroups, groups_per_xcd, list_stride;
   // state of the forward (from pass 1 and the reduction)
   const uint16_t *wqT, *wkT;  // bf16 [32][D]
   const uint16_t *st;         // bf16 [BH][D][32], rank-permuted

@@ -21,7 +21,7 @@ import oracle
 from oracle import backward as OB
 from sparse_rank_attention_amd import workloads as W
 from tests.conftest import gpu_available
-from tests.test_gpu_parity import SMALL, dev, host_f64, say, small_workload
+from tests.test_gpu_parity import SMALL, bound_ratio, dev, host_f64, say, small_workload
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
 
@@ -123,5 +123,47 @@ def test_backward_full_size_sampled():
     ratios["dwq"] = _ratio(host_f64(dwq), dwq_ref, False)
     ratios["dwk"] = _ratio(host_f64(dwk), dwk_ref, False)
     say("backward full size", name, "err/bound", {k_: round(v_, 3) for k_, v_ in ratios.items()})
+    for key, r in ratios.items():
+        assert r <= 1.0, (key, r)
+
+
+def test_long_union_lists():
+    """Union lists longer than the 2048 entries the kernels stage in LDS: 2051 key blocks
+    (N = 131241) with 2000 kept per query block, so that group unions pass 2048 entries.
+    The forward's attention kernel then reads the list tail from HBM, and the backward's dq
+    takes the per-query-block kernel.  Forward rows and dq rows of sampled query blocks, and
+    the projection gradients, against the oracle (dk, dv need every query row's softmax
+    at this size and are covered by the other cases)."""
+    from sparse_rank_attention_amd import rola
+    torch = _torch()
+    w = small_workload((3, 41, 1067), D=64, H=1, rank=16, topk=1.0, kind="field", seed=5)
+    kb = 2000
+    say("long union lists", w.nb, "blocks,", kb, "kept")
+    q, k, v = W.make_qkv(w)
+    wq, wk = W.make_proj(w)
+    do = W.make_dout(w)
+    cfg = rola.Config(topk=1.0, rank=w.rank, kb_override=kb)
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    wqd, wkd = torch.from_numpy(wq).cuda(), torch.from_numpy(wk).cuda()
+    bmap = rola.rola_select_blocks(qd, kd, w.grid, cfg)
+    out = rola.rola_forward(qd, kd, vd, wqd, wkd, w.grid, cfg)
+    dq, dk, dv, dwq, dwk, _ = rola.rola_backward(qd, kd, vd, wqd, wkd, w.grid, cfg, bmap, dev(do))
+    torch.cuda.synchronize()
+    m_ref = oracle.block_map(q[0], k[0], w.n_tokens, kb)
+    np.testing.assert_array_equal(bmap.cpu().numpy()[0], m_ref)
+    rows = sorted({n for b in (0, 977, w.nb - 1) for n in (b * 64, b * 64 + 40) if n < w.n_tokens})
+    rows_a = np.array(rows)
+    qf, kf, vf = (oracle.widen_bf16(x[0]) for x in (q, k, v))
+    S, z = oracle.lowrank_state(kf, vf, wk, w.n_tokens, w.grid)
+    o_ref = oracle.sparse_rows(qf, kf, vf, m_ref, w.n_tokens, rows_a) + oracle.lowrank_rows(qf, wq, S, z, w.grid,
+                                                                                            rows_a)
+    got = out[0, 0, torch.tensor(rows, device="cuda")].float().cpu().numpy().astype(np.float64)
+    r_fwd = bound_ratio(got, o_ref, True)  # the forward's bar, 2e-2
+    rq, _, _, dwq_ref, dwk_ref, _ = OB.backward_sampled(q[0], k[0], v[0], wq, wk, m_ref, do[0], w.n_tokens,
+                                                       w.grid, {0: rows}, {0: []})
+    g = dq[0, 0, torch.tensor(rows, device="cuda")].float().cpu().numpy().astype(np.float64)
+    ratios = {"fwd": r_fwd, "dq": _ratio(g, rq[0], True), "dwq": _ratio(host_f64(dwq), dwq_ref, False),
+              "dwk": _ratio(host_f64(dwk), dwk_ref, False)}
+    say("long union lists err/bound", {k_: round(v_, 3) for k_, v_ in ratios.items()})
     for key, r in ratios.items():
         assert r <= 1.0, (key, r)
