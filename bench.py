@@ -28,9 +28,10 @@ METRIC = "RoLA fwd ms + kept-block TFLOP/s (% MFMA peak), Wan-14B-720P shape, to
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-# fp32 FMA on the vector ALU without packed math: 256 CUs x 4 SIMDs x 16 lanes x 2 flop x 2.4 GHz
-# (the datasheet's 157.3 TFLOP/s fp32 vector figure counts the packed two-wide form)
-PEAK_FP32_FMA_TFLOPS = 78.6
+# fp32 vector FMA: the datasheet's 157.3 TFLOP/s (256 CUs x 4 SIMDs x 32 lanes x 2 flop x 2.4 GHz).
+# Plain (unpacked) v_fma_f32 reaches it: with two waves per SIMD a probe of independent FMA chains
+# issues one wave64 FMA per about 2.3 cycles per SIMD (one wave alone, one per about 4.6).
+PEAK_FP32_FMA_TFLOPS = 157.3
 
 
 def traffic_file(workload: str) -> str:
@@ -596,7 +597,7 @@ def main():
                                  "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}
     if "scores" in kern_ms:
         # pooled block scores: one fp32 FMA per (query block, key block, dim), a
-        # pinned sequential chain, so plain (unpacked) v_fma_f32 on the VALU
+        # pinned sequential chain per element, on plain v_fma_f32
         sflop = 2.0 * w.batch * w.heads * w.nb * w.nb * w.head_dim
         tf = sflop / (kern_ms["scores"] * 1e-3) / 1e12
         rec["scores_roofline"] = {"kernel": "scores", "bound": "alu", "achieved": round(tf, 1),
