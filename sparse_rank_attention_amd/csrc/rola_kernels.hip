@@ -669,14 +669,20 @@ __global__ __launch_bounds__(256) void k_scores(const float *__restrict__ qp,
   for (int r = 0; r < 4; ++r)
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[r][c] = 0.0f;
+  // the chunk being staged is loaded one chunk ahead (its latency under the
+  // FMAs of the previous chunk)
+  f32x4 qv = *(const f32x4 *)(qb + (int64_t)qrow * D + 4 * sd4);
+  f32x4 kv = *(const f32x4 *)(kb + (int64_t)krow * D + 4 * sd4);
   for (int dc = 0; dc < D; dc += 16) {
-    const f32x4 qv = *(const f32x4 *)(qb + (int64_t)qrow * D + dc + 4 * sd4);
-    const f32x4 kv = *(const f32x4 *)(kb + (int64_t)krow * D + dc + 4 * sd4);
     __syncthreads();  // previous chunk fully read
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       ((float *)&qs[4 * sd4 + e][srow >> 2])[srow & 3] = qv[e];
       ((float *)&ks[4 * sd4 + e][srow >> 2])[srow & 3] = kv[e];
+    }
+    if (dc + 16 < D) {
+      qv = *(const f32x4 *)(qb + (int64_t)qrow * D + dc + 16 + 4 * sd4);
+      kv = *(const f32x4 *)(kb + (int64_t)krow * D + dc + 16 + 4 * sd4);
     }
     __syncthreads();
 #pragma unroll
