@@ -236,7 +236,11 @@ int32_t rola_backward(const rola_problem *prob, const rola_config *cfg, const vo
  * timed calls themselves create none while the pool lasts.
  * rola_timing_read synchronises those events and returns, per kernel name,
  * the launch count and total milliseconds (at most `max` entries; returns
- * the number written, or -1 on error).  Process-global; not thread-safe.
+ * the number written, or -1 on error).  This is the library's only
+ * process-wide state: off by default, and while off a call only reads its
+ * flag.  Enabling, reading and the recording are serialised by a lock; the
+ * measurement itself is meant for one timing thread (events of concurrent
+ * calls on several streams are recorded but interleave in the totals).
  */
 typedef struct rola_kernel_time {
   char name[48];

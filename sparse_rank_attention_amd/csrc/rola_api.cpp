@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <atomic>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -197,8 +198,10 @@ struct TimedLaunch {
   std::string name;
   hipEvent_t start, stop;
 };
+// The only process-wide state of the library: the measurement aid below.
+// While it is off (the default), a call reads this one flag and nothing else.
 std::mutex g_mu;
-bool g_timing = false;
+std::atomic<bool> g_timing{false};
 std::vector<TimedLaunch> g_launches;
 std::vector<hipEvent_t> g_free_events;
 constexpr size_t kEventPool = 512;  // enough for about 36 timed forward calls
@@ -218,7 +221,8 @@ hipEvent_t take_event() {
 template <typename F>
 int32_t timed(const char *name, hipStream_t st, F &&launch) {
   hipEvent_t a = nullptr, b = nullptr;
-  if (g_timing) {
+  const bool on = g_timing.load(std::memory_order_relaxed);
+  if (on) {
     std::lock_guard<std::mutex> lk(g_mu);
     a = take_event();
     b = take_event();
@@ -226,7 +230,7 @@ int32_t timed(const char *name, hipStream_t st, F &&launch) {
   }
   launch();
   hipError_t err = hipGetLastError();
-  if (g_timing && a && b) {
+  if (on && a && b) {
     (void)hipEventRecord(b, st);
     std::lock_guard<std::mutex> lk(g_mu);
     g_launches.push_back({name, a, b});
@@ -730,9 +734,9 @@ int32_t rola_mfma_probe(int32_t precision, int32_t iters, double *flop, float *s
 
 int32_t rola_timing_enable(int32_t on) {
   std::lock_guard<std::mutex> lk(g_mu);
-  g_timing = on != 0;
+  g_timing.store(on != 0);
   // create events now rather than inside the calls being timed
-  while (g_timing && g_free_events.size() < kEventPool) {
+  while (on && g_free_events.size() < kEventPool) {
     hipEvent_t e = nullptr;
     if (hipEventCreate(&e) != hipSuccess) break;
     g_free_events.push_back(e);
