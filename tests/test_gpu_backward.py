@@ -42,7 +42,8 @@ def _ratio(got, ref, bf16_store):
     return float(np.max(np.abs(got - ref) / bound))
 
 
-CASES = SMALL + [("d128_1280", small_workload((5, 16, 16), D=128, H=2, rank=32, topk=0.25, kind="field", seed=2))]
+CASES = SMALL + [("d128_1280", small_workload((5, 16, 16), D=128, H=2, rank=32, topk=0.25, kind="field", seed=2)),
+                 ("two_batches", W.Workload("b2", 2, 2, 64, (3, 7, 11), 0.25, 16, "iid", seed=3))]
 
 
 @pytest.mark.parametrize("name,w", CASES, ids=[c[0] for c in CASES])
@@ -64,16 +65,19 @@ def test_backward_matches_oracle(name, w, gated, dout_f32):
     dq, dk, dv, dwq, dwk, dgate = rola.rola_backward(qd, kd, vd, torch.from_numpy(wq).cuda(),
                                                      torch.from_numpy(wk).cuda(), w.grid, cfg, bmap, dod, gate=gd)
     torch.cuda.synchronize()
-    m_ref = oracle.block_map(q[0], k[0], w.n_tokens, oracle.keep_blocks(w.topk, w.nb))
-    np.testing.assert_array_equal(bmap.cpu().numpy()[0], m_ref)
+    # batches and heads flattened: [B*H, n_pad, D]
+    flat = lambda x: x.reshape(w.batch * w.heads, w.n_pad, -1)
+    kb = oracle.keep_blocks(w.topk, w.nb)
+    m_ref = oracle.block_map(flat(q), flat(k), w.n_tokens, kb)
+    np.testing.assert_array_equal(bmap.cpu().numpy().reshape(-1, w.nb, kb), m_ref)
     f64 = oracle.widen_bf16
     # an fp32 dout is taken at bf16 precision (the header's contract)
-    do_ref = f64(W.to_bf16_bits(do[0])) if dout_f32 else f64(do[0])
-    ref = OB.backward(f64(q[0]), f64(k[0]), f64(v[0]), wq, wk, m_ref, do_ref, w.n_tokens, w.grid, gate=g)
+    do_ref = f64(W.to_bf16_bits(flat(do))) if dout_f32 else f64(flat(do))
+    ref = OB.backward(f64(flat(q)), f64(flat(k)), f64(flat(v)), wq, wk, m_ref, do_ref, w.n_tokens, w.grid, gate=g)
     n = w.n_tokens
     ratios = {}
     for key, got in (("dq", dq), ("dk", dk), ("dv", dv)):
-        gh = host_f64(got)[0]
+        gh = flat(host_f64(got))
         assert np.all(gh[:, n:] == 0), key
         ratios[key] = _ratio(gh[:, :n], ref[key][:, :n], True)
     ratios["dwq"] = _ratio(host_f64(dwq), ref["dwq"], False)
