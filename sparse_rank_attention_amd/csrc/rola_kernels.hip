@@ -1176,8 +1176,10 @@ static __device__ __forceinline__ void attn_finish(const AttnArgs &args, const b
 //     whose copy would overflow (a |v| >= 2^16, flagged per pass-1 chunk) are
 //     skipped here and computed by the EXACT form launched after it with the
 //     same flags, which then runs those heads only.
-template <int D, int G, int S, bool SPARSE, bool LOWRANK, bool ACCUM, bool OUTF32, bool EXACT = OUTF32>
+template <int D, int G, int S, bool SPARSE, bool LOWRANK, bool ACCUM, bool OUTF32, bool EXACT = OUTF32,
+          bool FALLBACK = false>
 __global__ __launch_bounds__(128 * G, 2) void k_attn(AttnArgs args) {
+  static_assert(!FALLBACK || (SPARSE && EXACT), "the fallback is the EXACT form of the sparse branch");
   constexpr int CH = D / 8;
   constexpr int NS = D / 16;  // k-steps over head_dim
   constexpr int DT = D / 32;  // output d-tiles
@@ -1194,21 +1196,15 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn(AttnArgs args) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, g = lane >> 5;
   const int member = wave >> 1, half = wave & 1;
-  const int64_t L = blockIdx.x;
-  const int64_t sidx = L / 8;
-  const int64_t bh64 = sidx / args.groups_per_xcd;
-  const int64_t group = (L % 8) * args.groups_per_xcd + sidx % args.groups_per_xcd;
-  if (bh64 >= args.bh_count || group >= args.ngroups) return;
-  const int bh = (int)bh64;
-  const int64_t gidx = (int64_t)bh * args.ngroups + group;
-  // any range flag of this head's fp16 V copy set
-  auto v_overflow = [&]() __attribute__((always_inline)) -> bool {
+  // any range flag of head bh's fp16 V copy set
+  auto v_overflow = [&](int bh) __attribute__((always_inline)) -> bool {
     int f = 0;
     for (int i = lane; i < args.nflags; i += 64) f |= args.vovf[(int64_t)bh * args.nflags + i];
     return __builtin_amdgcn_ballot_w64(f != 0) != 0;
   };
-  // the bf16 form as the fallback of the fp16 one: only the flagged heads
-  if (SPARSE && EXACT && args.vovf && !v_overflow()) return;
+  // one group of query blocks of head bh
+  auto run_group = [&](const int bh, const int64_t group) __attribute__((always_inline)) {
+  const int64_t gidx = (int64_t)bh * args.ngroups + group;
   // wave-uniform values through the scalar cache (the schedule is written by
   // earlier kernels and only read here)
   typedef const __attribute__((address_space(4))) int32_t *cint_p;
@@ -1313,7 +1309,7 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn(AttnArgs args) {
       }
       // the fp16 form leaves flagged heads to the bf16 form (checked here,
       // under the prologue's copies, which are complete before the return)
-      const bool skip = !EXACT && args.vovf && v_overflow();
+      const bool skip = !EXACT && args.vovf && v_overflow(bh);
       wait_vmcnt<0>();
       if (skip) return;
 #pragma unroll
@@ -1514,6 +1510,27 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn(AttnArgs args) {
   }
   if (!active) return;
   attn_finish<D, LOWRANK, ACCUM, OUTF32>(args, qreg, oacc, n, base, bh, lane, sfreq);
+  };  // run_group
+  if constexpr (FALLBACK) {
+    // the bf16 form as the fallback of the fp16 one: a grid of
+    // bh_count x per_head workgroups, each taking every per_head-th group of
+    // its head, and only for the flagged heads (so that the common case, no
+    // head flagged, costs one flag read per workgroup)
+    const int per_head = (int)(gridDim.x / args.bh_count);
+    const int bh = (int)(blockIdx.x / per_head);
+    if (!v_overflow(bh)) return;
+    for (int64_t group = blockIdx.x % per_head; group < args.ngroups; group += per_head) {
+      run_group(bh, group);
+      __syncthreads();  // every wave done with the ring, list and table before the next group
+    }
+  } else {
+  const int64_t L = blockIdx.x;
+  const int64_t sidx = L / 8;
+  const int64_t bh64 = sidx / args.groups_per_xcd;
+  const int64_t group = (L % 8) * args.groups_per_xcd + sidx % args.groups_per_xcd;
+  if (bh64 >= args.bh_count || group >= args.ngroups) return;
+  run_group((int)bh64, group);
+  }
 }
 
 // ---------------------------------------------------------------- k_quant8
@@ -2018,6 +2035,7 @@ void launch_schedule(const int32_t *map, int nb, int kb, int G, int ngroups, int
   }
 }
 
+constexpr int64_t kFallbackPerHead = 32;  // workgroups per head of the bf16 fallback launch
 // fp32 output: the EXACT form.  bf16 output with the sparse branch: the fp16
 // form, then the EXACT form for the heads whose fp16 V copy is flagged (an
 // empty pass, each workgroup reading its head's flags, when none is).
@@ -2026,11 +2044,14 @@ static void attn_d3(const AttnArgs &a, bool outf32, hipStream_t st) {
   dim3 grid((unsigned)(8 * a.groups_per_xcd * a.bh_count)), block(128 * G);
   if (outf32) {
     hipLaunchKernelGGL((k_attn<D, G, S, SPARSE, LOWRANK, ACCUM, true, true>), grid, block, 0, st, a);
-  } else if (!SPARSE) {
+  } else if constexpr (!SPARSE) {
     hipLaunchKernelGGL((k_attn<D, G, S, SPARSE, LOWRANK, ACCUM, false, false>), grid, block, 0, st, a);
   } else {
     hipLaunchKernelGGL((k_attn<D, G, S, SPARSE, LOWRANK, ACCUM, false, false>), grid, block, 0, st, a);
-    hipLaunchKernelGGL((k_attn<D, G, S, SPARSE, LOWRANK, ACCUM, false, true>), grid, block, 0, st, a);
+    // the fallback: per_head workgroups per head, each looping over groups
+    const int64_t per_head = std::min<int64_t>(a.ngroups, kFallbackPerHead);
+    hipLaunchKernelGGL((k_attn<D, G, S, SPARSE, LOWRANK, ACCUM, false, true, true>),
+                       dim3((unsigned)(per_head * a.bh_count)), block, 0, st, a);
   }
 }
 
