@@ -104,26 +104,17 @@ void launch_quant_rows(const QuantRowsArgs &a, hipStream_t st) {
 constexpr int kGemmTileT = 256;
 constexpr int kGemmTileC = 256;
 constexpr int kGemmK = 64;
-#ifndef ROLA_GEMM_SLOTS
-#define ROLA_GEMM_SLOTS 4
-#endif
-#ifndef ROLA_GEMM_GROUP
-#define ROLA_GEMM_GROUP 4
-#endif
-constexpr int kGemmSlots = ROLA_GEMM_SLOTS;
+constexpr int kGemmSlots = 4;
 constexpr int kGemmSlotBytes = (kGemmTileT + kGemmTileC) * kGemmK;
-constexpr int kGemmGroupM = ROLA_GEMM_GROUP;  // token tiles per group of the tile order
+constexpr int kGemmGroupM = 4;  // token tiles per group of the tile order
 
 static __device__ __forceinline__ int gemm_swz(int r) { return (((r >> 1) ^ (r >> 3)) & 1) | ((r >> 1) & 2); }
 
-#ifndef ROLA_GEMM_WC
-#define ROLA_GEMM_WC 2
-#endif
-#ifndef ROLA_GEMM_WT
-#define ROLA_GEMM_WT 4
-#endif
+// waves along channels x waves along tokens; each wave owns TI x TJ MFMA
+// tiles of 32 x 32
+constexpr int kGemmWC = 2, kGemmWT = 4;
 // Per-thread copies of a stage: 16 of 1 KB for each part, spread over the waves.
-constexpr int kGemmCopies = 32 / (ROLA_GEMM_WC * ROLA_GEMM_WT);
+constexpr int kGemmCopies = 32 / (kGemmWC * kGemmWT);
 
 template <int N>
 static __device__ __forceinline__ void wait_gemm_stages() {
@@ -145,9 +136,6 @@ static __device__ __forceinline__ i32x8 cat8(u32x4 a, u32x4 b) {
   return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// waves along channels x waves along tokens; each wave owns TI x TJ MFMA
-// tiles of 32 x 32
-constexpr int kGemmWC = ROLA_GEMM_WC, kGemmWT = ROLA_GEMM_WT;
 constexpr int kGemmWaves = kGemmWC * kGemmWT;
 constexpr int kGemmTI = kGemmTileC / 32 / kGemmWC, kGemmTJ = kGemmTileT / 32 / kGemmWT;
 constexpr int kGemmOps = 16 / kGemmWaves;  // 1 KB copies per wave per part per stage
@@ -430,13 +418,10 @@ void k_gemm_w8a8_k128(GemmArgs a) {
 
 // K a multiple of 128 takes the 128-byte stages (4 % faster at 75600 x 5120
 // x 15360 than 64-byte stages), otherwise the 64-byte ring
-#ifndef ROLA_GEMM_K128
-#define ROLA_GEMM_K128 1
-#endif
 
 void launch_gemm_w8a8(const GemmArgs &a, hipStream_t st) {
   const int ntiles = a.tiles_t * a.tiles_c;
-  if (ROLA_GEMM_K128 && a.K % kGemmK2 == 0) {
+  if (a.K % kGemmK2 == 0) {
     if (a.out_f32)
       hipLaunchKernelGGL(k_gemm_w8a8_k128<true>, dim3((unsigned)ntiles), dim3(64 * kGemmWaves), 0, st, a);
     else

@@ -46,12 +46,8 @@ struct Pass1Args {
 
 // Attention workgroup shape: G query blocks per workgroup (2 waves each),
 // S-slot LDS ring of K/V^T tiles.
-#ifndef ROLA_ATTN_G
-#define ROLA_ATTN_G 4
-#endif
-#ifndef ROLA_ATTN_S
-#define ROLA_ATTN_S 4
-#endif
+constexpr int kAttnG = 4;
+constexpr int kAttnS = 4;
 
 
 // fp8 copies of the token tensors (k_quant8): per (batch, head, block)
@@ -74,15 +70,9 @@ struct Quant8Args {
 
 // fp8 attention: ring depth (16 KB tiles at D=128), tiles per barrier and
 // union-list entries staged in LDS
-#ifndef ROLA_ATTN8_S
-#define ROLA_ATTN8_S 8
-#endif
-#ifndef ROLA_ATTN8_P
-#define ROLA_ATTN8_P 4
-#endif
-#ifndef ROLA_ATTN8_LMAX
-#define ROLA_ATTN8_LMAX 1024
-#endif
+constexpr int kAttn8S = 8;
+constexpr int kAttn8P = 4;
+constexpr int kAttn8Lmax = 1024;
 
 struct AttnArgs {
   const uint16_t *q, *k, *v;

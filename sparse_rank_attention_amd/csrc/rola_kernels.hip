@@ -1640,7 +1640,7 @@ __global__ __launch_bounds__(256) void k_quant8(Quant8Args a) {
 // Finally O = O' * sigma * 2^-8 / l.
 template <int D, int G, int S, bool LOWRANK, bool ACCUM, bool OUTF32>
 __global__ __launch_bounds__(128 * G) void k_attn8(AttnArgs args) {
-  constexpr int P = ROLA_ATTN8_P;  // tiles per barrier
+  constexpr int P = kAttn8P;  // tiles per barrier
   constexpr int NS = D / 16;
   constexpr int DT = D / 32;
   constexpr int K8 = D / 64;            // fp8 k-steps over head_dim
@@ -1649,7 +1649,7 @@ __global__ __launch_bounds__(128 * G) void k_attn8(AttnArgs args) {
   constexpr int OPS = TB / 16 / NT;     // DMA ops per thread per tile
   static_assert(OPS >= 1 && (TB / 16) % NT == 0, "tile split");
   static_assert(S >= 2 && S * OPS <= 63, "ring depth");
-  constexpr int LMAX = ROLA_ATTN8_LMAX;
+  constexpr int LMAX = kAttn8Lmax;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[S * TB];
   __shared__ int32_t slist[LMAX];
   __shared__ float sck[LMAX], sku[LMAX], skw[LMAX];
@@ -1988,8 +1988,8 @@ void launch_blk_partial(const uint8_t *blk, int nb, int parts, int D, int bh, fl
 
 void launch_complement(const CompArgs &a, int D, hipStream_t st) {
   const dim3 grid((unsigned)(8 * a.groups_per_xcd * a.bh_count)), block(256);
-  if (D == 64) hipLaunchKernelGGL((k_complement<64, ROLA_ATTN_G>), grid, block, 0, st, a);
-  else hipLaunchKernelGGL((k_complement<128, ROLA_ATTN_G>), grid, block, 0, st, a);
+  if (D == 64) hipLaunchKernelGGL((k_complement<64, kAttnG>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((k_complement<128, kAttnG>), grid, block, 0, st, a);
 }
 
 void launch_scores(const float *qp, const float *kp, float *s, int nb, int D, int bh,
@@ -2069,12 +2069,12 @@ static void attn_d(const AttnArgs &a, bool sparse, bool lowrank, bool accum, boo
   else attn_d2<D, G, S, false, true>(a, accum, outf32, st);
 }
 
-int attn_group_size() { return ROLA_ATTN_G; }
+int attn_group_size() { return kAttnG; }
 
 void launch_attn(const AttnArgs &a, int D, bool sparse, bool lowrank, bool accum, bool outf32,
                  hipStream_t st) {
-  if (D == 64) attn_d<64, ROLA_ATTN_G, ROLA_ATTN_S>(a, sparse, lowrank, accum, outf32, st);
-  else attn_d<128, ROLA_ATTN_G, ROLA_ATTN_S>(a, sparse, lowrank, accum, outf32, st);
+  if (D == 64) attn_d<64, kAttnG, kAttnS>(a, sparse, lowrank, accum, outf32, st);
+  else attn_d<128, kAttnG, kAttnS>(a, sparse, lowrank, accum, outf32, st);
 }
 
 // Pre-quantised input: the caller's e4m3 codes of K and V laid out as the
@@ -2147,11 +2147,11 @@ static void attn8_d2(const AttnArgs &a, bool accum, bool outf32, hipStream_t st)
 
 void launch_attn8(const AttnArgs &a, int D, bool lowrank, bool accum, bool outf32, hipStream_t st) {
   if (D == 64) {
-    if (lowrank) attn8_d2<64, ROLA_ATTN_G, ROLA_ATTN8_S, true>(a, accum, outf32, st);
-    else attn8_d2<64, ROLA_ATTN_G, ROLA_ATTN8_S, false>(a, accum, outf32, st);
+    if (lowrank) attn8_d2<64, kAttnG, kAttn8S, true>(a, accum, outf32, st);
+    else attn8_d2<64, kAttnG, kAttn8S, false>(a, accum, outf32, st);
   } else {
-    if (lowrank) attn8_d2<128, ROLA_ATTN_G, ROLA_ATTN8_S, true>(a, accum, outf32, st);
-    else attn8_d2<128, ROLA_ATTN_G, ROLA_ATTN8_S, false>(a, accum, outf32, st);
+    if (lowrank) attn8_d2<128, kAttnG, kAttn8S, true>(a, accum, outf32, st);
+    else attn8_d2<128, kAttnG, kAttn8S, false>(a, accum, outf32, st);
   }
 }
 
