@@ -68,7 +68,7 @@ def parse():
     ap.add_argument("--complement", action="store_true",
                     help="low-rank state over each query block's unkept blocks instead of all blocks")
     ap.add_argument("--backward", action="store_true",
-                    help="time rola_backward (bf16, global scope) instead of the forward; its own JSON line")
+                    help="time rola_backward (bf16; with --complement, the complement scope) instead of the forward; its own JSON line")
     ap.add_argument("--e4m3-input", action="store_true",
                     help="fp8 workloads: time rola_forward_e4m3 on pre-quantised Q/K/V codes")
     ap.add_argument("--linear", default=None,
@@ -229,7 +229,8 @@ def torch_int16():
 def backward_bench(args, w, rola, torch, np, W, qd, kd, vd, wqd, wkd, gd, stream):
     """rola_backward on the workload: W untimed calls, then K timed ones (HIP events on
     the stream), with the forward's block map and a seeded N(0, 1) dL/dO in bf16."""
-    cfg = rola.Config(topk=w.topk, rank=w.rank)
+    cfg = rola.Config(topk=w.topk, rank=w.rank,
+                      lowrank_scope=rola.ROLA_LR_COMPLEMENT if args.complement else rola.ROLA_LR_GLOBAL)
     B, H = w.batch, w.heads
     kb = rola.plan(rola.problem(qd, w.grid), cfg).kb
     bmap = torch.empty((B, H, w.nb, kb), dtype=torch.int32, device="cuda")
@@ -266,7 +267,8 @@ def backward_bench(args, w, rola, torch, np, W, qd, kd, vd, wqd, wkd, gd, stream
         "data": "synthetic (seeded Wan-shaped smooth field + noise Q/K, N(0,1) V and dL/dO; no weights)",
         "config": {"workload": w.name, "batch": B, "heads": H, "head_dim": w.head_dim, "grid": list(w.grid),
                    "n_tokens": w.n_tokens, "topk": w.topk, "kb": kb, "nb": w.nb, "rank": w.rank,
-                   "output_gate": bool(args.gate), "pass": "backward"},
+                   "output_gate": bool(args.gate), "pass": "backward",
+                   "lowrank_scope": "complement" if args.complement else "global"},
         "bwd_ms": round(ms, 4),
         "kernel_ms": {k_: round(v_, 4) for k_, v_ in sorted(kern_ms.items())},
         "cpu_baseline": None,
@@ -456,8 +458,8 @@ def main():
     cfg = rola.Config(topk=w.topk, rank=w.rank, precision=rola.ROLA_PREC_FP8 if fp8 else rola.ROLA_PREC_BF16,
                       lowrank_scope=rola.ROLA_LR_COMPLEMENT if args.complement else rola.ROLA_LR_GLOBAL)
     if args.backward:
-        if fp8 or args.complement:
-            print("bench.py --backward: the backward is bf16 with the global low-rank scope", file=sys.stderr)
+        if fp8:
+            print("bench.py --backward: the backward is bf16", file=sys.stderr)
             sys.exit(2)
         backward_bench(args, w, rola, torch, np, W, qd, kd, vd, wqd, wkd, gd, torch.cuda.current_stream())
         return

@@ -219,9 +219,12 @@ int32_t rola_forward_noalloc(const rola_problem *prob, const rola_config *cfg, c
  *               exactly when gate is given.
  * The block map is a constant of the backward (the top-k selection has no
  * gradient).  Internally the state S, z, the sparse output and each row's
- * log-sum-exp are recomputed.  Supported: precision ROLA_PREC_BF16 and
- * lowrank_scope ROLA_LR_GLOBAL (ROLA_ERR_UNSUPPORTED otherwise).  The
- * workspace must hold plan.workspace_bytes_backward bytes.
+ * log-sum-exp are recomputed.  Both low-rank scopes are supported: with
+ * ROLA_LR_COMPLEMENT the per-query-block states (the sums over the unkept
+ * blocks, as the forward forms them) are recomputed too, and each key
+ * block's state receives the gradient of the query blocks that do not keep
+ * it.  Supported precision: ROLA_PREC_BF16 (ROLA_ERR_UNSUPPORTED for fp8).
+ * The workspace must hold plan.workspace_bytes_backward bytes.
  */
 int32_t rola_backward(const rola_problem *prob, const rola_config *cfg, const void *q, const void *k,
                       const void *v, const float *wq, const float *wk, const float *gate,

@@ -117,13 +117,22 @@ def backward(q, k, v, wq, wk, bmap, dout, n_valid: int, grid, split=None, theta=
 
 
 def backward_sampled(q_bits, k_bits, v_bits, wq, wk, bmap, dout_bits, n_valid: int, grid, q_rows, k_rows,
-                     split=None, theta=10000.0, scale=None, gate=None):
+                     split=None, theta=10000.0, scale=None, gate=None, complement=False, heads=None):
     """The same gradients at full size, for sampled rows, from the gradient
     formulas written out (no autograd), one head at a time.
 
     q_bits, k_bits, v_bits, dout_bits: bf16 bit patterns [BH, n_pad, D];
-    q_rows, k_rows: {head: row indices} of the dq and of the dk, dv rows wanted.
+    q_rows, k_rows: {head: row indices} of the dq and of the dk, dv rows wanted;
+    heads: the heads to evaluate (default all; dwq, dwk and dgate then sum
+    over those heads only).
     Returns ({head: dq rows}, {head: dk rows}, {head: dv rows}, dwq, dwk, dgate or None).
+
+    With ``complement`` the low-rank sums of query block i run over the key
+    blocks j it does not keep: S_i = sum_j S_j, z_i = sum_j z_j over those j
+    (S_j = b_j^T v_j, z_j = sum b_j over block j's valid tokens), and L = 0 where
+    that set is empty.  The per-token formulas below then use S_i, z_i, and the
+    block states receive dS_j = sum of dS_i over the query blocks i that do not
+    keep j (dS_i = sum over i's tokens of a dnum^T), dz_j likewise.
 
     Per head, with the low-rank sums over all N valid tokens:
       a = phi(R(q) Wq), b = phi(R(k) Wk), S = b^T v, z = sum b, L = a S / (a . z);
@@ -148,30 +157,63 @@ def backward_sampled(q_bits, k_bits, v_bits, wq, wk, bmap, dout_bits, n_valid: i
     dgate = torch.zeros(d + 1, dtype=torch.float64) if gate is not None else None
     dq_out, dk_out, dv_out = {}, {}, {}
     dphi = lambda u: torch.where(u > 0, torch.ones_like(u), torch.exp(u))
-    for h in range(bh_count):
+    for h in (range(bh_count) if heads is None else heads):
         Q, K, V, DO = w16(q_bits[h])[:n], w16(k_bits[h])[:n], w16(v_bits[h])[:n], w16(dout_bits[h])[:n]
         Rq, Rk = _rope(Q, grid, split, theta), _rope(K, grid, split, theta)
         u, wv = Rq @ Wq, Rk @ Wk
         a, b = _phi(u), _phi(wv)
-        S, z = b.T @ V, b.sum(dim=0)
-        den = a @ z
-        L = (a @ S) / den[:, None]
         g = torch.sigmoid(Q @ G[:d] + G[d]) if G is not None else torch.ones(n, dtype=torch.float64)
-        dg = (DO * L).sum(dim=1)
-        dy = dg * g * (1 - g) if G is not None else torch.zeros(n, dtype=torch.float64)
-        dnum = g[:, None] * DO / den[:, None]
-        dden = -g * dg / den
-        du = (dnum @ S.T + dden[:, None] * z[None, :]) * dphi(u)
+        kept = np.asarray(bmap[h])
+        if not complement:
+            S, z = b.T @ V, b.sum(dim=0)
+            den = a @ z
+            L = (a @ S) / den[:, None]
+            dg = (DO * L).sum(dim=1)
+            dy = dg * g * (1 - g) if G is not None else torch.zeros(n, dtype=torch.float64)
+            dnum = g[:, None] * DO / den[:, None]
+            dden = -g * dg / den
+            du = (dnum @ S.T + dden[:, None] * z[None, :]) * dphi(u)
+            dS, dz = a.T @ dnum, (a * dden[:, None]).sum(dim=0)
+            dw_ = (V @ dS.T + dz[None, :]) * dphi(wv)
+            dv_lr = b @ dS
+        else:
+            nbk = (n + BLOCK - 1) // BLOCK
+            blocks = [torch.arange(j * BLOCK, min(j * BLOCK + BLOCK, n)) for j in range(nbk)]
+            Sj = torch.stack([b[r].T @ V[r] for r in blocks])           # [nb, r, D]
+            zj = torch.stack([b[r].sum(dim=0) for r in blocks])         # [nb, r]
+            off = torch.ones(nbk, nbk, dtype=torch.float64)              # off[i, j]: i does not keep j
+            off[torch.arange(nbk)[:, None], torch.as_tensor(kept[:nbk], dtype=torch.long)] = 0.0
+            Si = (off @ Sj.reshape(nbk, -1)).reshape(Sj.shape)
+            zi = off @ zj
+            dy = torch.zeros(n, dtype=torch.float64)
+            du = torch.zeros_like(u)
+            dSi, dzi = torch.zeros_like(Sj), torch.zeros_like(zj)
+            for i, r in enumerate(blocks):
+                den = a[r] @ zi[i]
+                ok = den > 0                                             # empty complement: no term
+                inv = torch.where(ok, 1.0 / torch.where(ok, den, torch.ones_like(den)), torch.zeros_like(den))
+                L = (a[r] @ Si[i]) * inv[:, None]
+                dg_i = (DO[r] * L).sum(dim=1)
+                if G is not None:
+                    dy[r] = dg_i * g[r] * (1 - g[r])
+                dnum = g[r][:, None] * DO[r] * inv[:, None]
+                dden = -g[r] * dg_i * inv
+                du[r] = (dnum @ Si[i].T + dden[:, None] * zi[i][None, :]) * dphi(u[r])
+                dSi[i], dzi[i] = a[r].T @ dnum, (a[r] * dden[:, None]).sum(dim=0)
+            dSj = (off.T @ dSi.reshape(nbk, -1)).reshape(dSi.shape)
+            dzj = off.T @ dzi
+            dw_ = torch.zeros_like(wv)
+            dv_lr = torch.zeros_like(V)
+            for j, r in enumerate(blocks):
+                dw_[r] = (V[r] @ dSj[j].T + dzj[j][None, :]) * dphi(wv[r])
+                dv_lr[r] = b[r] @ dSj[j]
         dq_lr = _rope(du @ Wq.T, grid, split, theta, inverse=True) + dy[:, None] * (G[:d][None, :] if G is not None else 0)
         dwq += Rq.T @ du
-        dS, dz = a.T @ dnum, (a * dden[:, None]).sum(dim=0)
-        dw_ = (V @ dS.T + dz[None, :]) * dphi(wv)
-        dv_lr, dk_lr = b @ dS, _rope(dw_ @ Wk.T, grid, split, theta, inverse=True)
+        dk_lr = _rope(dw_ @ Wk.T, grid, split, theta, inverse=True)
         dwk += Rk.T @ dw_
         if G is not None:
             dgate[:d] += Q.T @ dy
             dgate[d] += dy.sum()
-        kept = np.asarray(bmap[h])
         keys_of = lambda i: torch.cat([torch.arange(j * BLOCK, min(j * BLOCK + BLOCK, n)) for j in sorted(kept[i])])
 
         def block_rows(i):  # P, dS of query block i over its kept keys

@@ -47,6 +47,7 @@ struct Plan {
   // rola_backward: its buffers follow the forward's (offsets from 0)
   int64_t b_os, b_os_elems, b_lse, b_dob, b_dn, b_dqp, b_dkp, b_dvp, b_ahat, b_duq, b_dwk, b_dy, b_dg,
       b_wqP, b_wkP, b_sd, b_dsr, b_dst, b_ds32, b_dz, b_s32, b_part, b_tcount, b_tlist, b_tbits, b_sumtmp, total_bwd;
+  int64_t b_sdc, b_pblk, b_dzblk, b_dsrc, b_dstc, b_dzc;  // complement scope only
 };
 
 int32_t make_plan(const rola_problem *p, const rola_config *c, Plan *pl) {
@@ -187,6 +188,16 @@ int32_t make_plan(const rola_problem *p, const rola_config *c, Plan *pl) {
   P.b_tlist = take(P.BH * nb * (int64_t)nb * 4);
   P.b_tbits = take(P.BH * nb * (int64_t)((nb + 31) / 32) * 4);
   P.b_sumtmp = take(P.BH * D * 32LL * 4);
+  P.b_sdc = P.b_pblk = P.b_dzblk = P.b_dsrc = P.b_dstc = P.b_dzc = 0;
+  if (P.comp) {
+    const int64_t blocks = P.BH * nb;
+    P.b_sdc = take(blocks * 32 * D * 2 * 2);  // hi, then lo
+    P.b_pblk = take(blocks * D * 32 * 2);
+    P.b_dzblk = take(blocks * 32 * 4);
+    P.b_dsrc = take(blocks * 32 * D * 2);
+    P.b_dstc = take(blocks * D * 32 * 2);
+    P.b_dzc = take(blocks * 32 * 4);
+  }
   P.total_bwd = o;
   return ROLA_OK;
 }
@@ -402,6 +413,7 @@ int32_t run_attn(const Plan &P, const rola_problem *p, const rola_config *c, con
     ca.list_stride = P.list_stride;
     ca.stc = (uint16_t *)(ws + P.off_stc);
     ca.zc = (float *)(ws + P.off_zc);
+    ca.sdc = nullptr;
     int32_t s = timed("complement", st, [&] { rola::launch_complement(ca, P.D, st); });
     if (s != ROLA_OK) return s;
     a.st = ca.stc;
@@ -590,7 +602,7 @@ int32_t rola_backward(const rola_problem *prob, const rola_config *cfg, const vo
                       void *stream) {
   Plan P;
   ROLA_TRY(make_plan(prob, cfg, &P));
-  if (P.fp8 || P.comp) return ROLA_ERR_UNSUPPORTED;
+  if (P.fp8) return ROLA_ERR_UNSUPPORTED;
   if (!q || !k || !v || !wq || !wk || !block_idx || !dout || !dq || !dk || !dv || !dwq || !dwk)
     return ROLA_ERR_INVALID_ARG;
   if ((gate != nullptr) != (dgate != nullptr)) return ROLA_ERR_INVALID_ARG;
@@ -604,20 +616,46 @@ int32_t rola_backward(const rola_problem *prob, const rola_config *cfg, const vo
   if (!aligned16(workspace)) return ROLA_ERR_ALIGNMENT;
   hipStream_t st = (hipStream_t)stream;
   uint8_t *ws = (uint8_t *)workspace;
-  // forward state: bf16 projections, S (bf16 permuted and fp32) and z
+  // forward state: bf16 projections, S (bf16 permuted and fp32) and z; in
+  // the complement scope also the per-block states (pass 1 pools Q and K
+  // along, unused) and the global sums of them
   ROLA_TRY(run_setup(P, wq, wk, ws, st));
-  ROLA_TRY(run_pass1(P, prob, nullptr, k, v, ws, false, true, st));
-  ROLA_TRY(timed("state_reduce", st, [&] {
-    rola::launch_state_reduce((const float *)(ws + P.off_part), 2 * P.nchunks, P.D, P.r, (int)P.BH,
-                              (uint16_t *)(ws + P.off_st), (float *)(ws + P.off_z),
-                              (float *)(ws + P.b_s32), st);
-  }));
+  if (P.comp) {
+    ROLA_TRY(run_pass1(P, prob, q, k, v, ws, true, true, st));
+    ROLA_TRY(run_reduce(P, ws, st));
+  } else {
+    ROLA_TRY(run_pass1(P, prob, nullptr, k, v, ws, false, true, st));
+    ROLA_TRY(timed("state_reduce", st, [&] {
+      rola::launch_state_reduce((const float *)(ws + P.off_part), 2 * P.nchunks, P.D, P.r, (int)P.BH,
+                                (uint16_t *)(ws + P.off_st), (float *)(ws + P.off_z),
+                                (float *)(ws + P.b_s32), st);
+    }));
+  }
   // the sparse branch alone again with fp32 weights: O_s (fp32, the
   // problem's strides) and each row's log-sum-exp
   rola_config c32 = *cfg;
   c32.out_dtype = ROLA_OUT_F32;
   ROLA_TRY(run_attn(P, prob, &c32, q, k, v, block_idx, nullptr, ws + P.b_os, ws, true, false, false, st,
                     (float *)(ws + P.b_lse)));
+  if (P.comp) {
+    // per query block: the complement state S_i, z_i (as the forward's) and
+    // S_i as the hi + lo operand of the backward, on the schedule the
+    // recompute left in the workspace
+    rola::CompArgs ca;
+    ca.blk = ws + P.off_blk;
+    ca.s32 = (const float *)(ws + P.off_s32);
+    ca.z = (const float *)(ws + P.off_z);
+    ca.ugroup = (const int32_t *)(ws + P.off_ugroup);
+    ca.ucount = (const int32_t *)(ws + P.off_ucount);
+    ca.ulist = (const int32_t *)(ws + P.off_ulist);
+    ca.nb = P.nb; ca.kb = P.kb;
+    ca.bh_count = P.BH; ca.ngroups = P.ngroups; ca.groups_per_xcd = (P.ngroups + 7) / 8;
+    ca.list_stride = P.list_stride;
+    ca.stc = (uint16_t *)(ws + P.off_stc);
+    ca.zc = (float *)(ws + P.off_zc);
+    ca.sdc = (uint16_t *)(ws + P.b_sdc);
+    ROLA_TRY(timed("complement", st, [&] { rola::launch_complement(ca, P.D, st); }));
+  }
 
   rola::BwdArgs a;
   a.q = (const uint16_t *)q; a.k = (const uint16_t *)k; a.v = (const uint16_t *)v;
@@ -639,7 +677,7 @@ int32_t rola_backward(const rola_problem *prob, const rola_config *cfg, const vo
   a.list_stride = P.list_stride;
   a.wqT = (const uint16_t *)(ws + P.off_wqT); a.wkT = (const uint16_t *)(ws + P.off_wkT);
   a.st = (const uint16_t *)(ws + P.off_st);
-  a.s32 = (const float *)(ws + P.b_s32); a.z = (const float *)(ws + P.off_z);
+  a.s32 = (const float *)(ws + (P.comp ? P.off_s32 : P.b_s32)); a.z = (const float *)(ws + P.off_z);
   a.os = (const float *)(ws + P.b_os); a.lse = (const float *)(ws + P.b_lse);
   a.wqP = (uint16_t *)(ws + P.b_wqP); a.wkP = (uint16_t *)(ws + P.b_wkP);
   a.sd = (uint16_t *)(ws + P.b_sd); a.dsr = (uint16_t *)(ws + P.b_dsr); a.dst = (uint16_t *)(ws + P.b_dst);
@@ -655,17 +693,35 @@ int32_t rola_backward(const rola_problem *prob, const rola_config *cfg, const vo
   a.sumtmp = (float *)(ws + P.b_sumtmp);
   a.dq = (uint16_t *)dq; a.dk = (uint16_t *)dk; a.dv = (uint16_t *)dv;
   a.dwq = dwq; a.dwk = dwk; a.dgate = dgate;
+  a.comp = P.comp ? 1 : 0;
+  a.stc = P.comp ? (const uint16_t *)(ws + P.off_stc) : nullptr;
+  a.zc = P.comp ? (const float *)(ws + P.off_zc) : nullptr;
+  a.sdc = P.comp ? (const uint16_t *)(ws + P.b_sdc) : nullptr;
+  a.pblk = P.comp ? (uint16_t *)(ws + P.b_pblk) : nullptr;
+  a.dzblk = P.comp ? (float *)(ws + P.b_dzblk) : nullptr;
+  a.dsrc = P.comp ? (uint16_t *)(ws + P.b_dsrc) : nullptr;
+  a.dstc = P.comp ? (uint16_t *)(ws + P.b_dstc) : nullptr;
+  a.dzc = P.comp ? (float *)(ws + P.b_dzc) : nullptr;
   const int D = P.D;
   ROLA_TRY(timed("bwd_prep", st, [&] { rola::launch_bwd_prep(a, D, st); }));
   ROLA_TRY(timed("bwd_query", st, [&] { rola::launch_bwd_query(a, D, st); }));
-  ROLA_TRY(timed("bwd_ds", st, [&] { rola::launch_bwd_outer(a, D, rola::kOuterDout, st); }));
-  ROLA_TRY(timed("bwd_dsops", st, [&] { rola::launch_bwd_dsops(a, D, st); }));
+  if (P.comp) {
+    // dS_i, dz_i per query block and dS per head; dz per head (and the gate
+    // bias); the transposed map; then dS_j, dz_j per key block
+    ROLA_TRY(timed("bwd_ds", st, [&] { rola::launch_bwd_comp_parts(a, D, st); }));
+    ROLA_TRY(timed("bwd_dsops", st, [&] { rola::launch_bwd_dsops(a, D, st); }));
+    ROLA_TRY(timed("bwd_tmap", st, [&] { rola::launch_bwd_tmap(a, st); }));
+    ROLA_TRY(timed("bwd_dsc", st, [&] { rola::launch_bwd_comp_keys(a, D, st); }));
+  } else {
+    ROLA_TRY(timed("bwd_ds", st, [&] { rola::launch_bwd_outer(a, D, rola::kOuterDout, st); }));
+    ROLA_TRY(timed("bwd_dsops", st, [&] { rola::launch_bwd_dsops(a, D, st); }));
+  }
   ROLA_TRY(timed("bwd_key", st, [&] { rola::launch_bwd_key(a, D, st); }));
   ROLA_TRY(timed("bwd_dwq", st, [&] { rola::launch_bwd_outer(a, D, rola::kOuterRopeQ, st); }));
   ROLA_TRY(timed("bwd_dwk", st, [&] { rola::launch_bwd_outer(a, D, rola::kOuterRopeK, st); }));
   if (gate) ROLA_TRY(timed("bwd_dgate", st, [&] { rola::launch_bwd_outer(a, D, rola::kOuterGate, st); }));
   ROLA_TRY(timed("bwd_dq", st, [&] { rola::launch_bwd_dq(a, D, st); }));
-  ROLA_TRY(timed("bwd_tmap", st, [&] { rola::launch_bwd_tmap(a, st); }));
+  if (!P.comp) ROLA_TRY(timed("bwd_tmap", st, [&] { rola::launch_bwd_tmap(a, st); }));
   return timed("bwd_dkv", st, [&] { rola::launch_bwd_dkv(a, D, st); });
 }
 

@@ -147,7 +147,10 @@ __global__ __launch_bounds__(256) void k_bwd_query(BwdArgs a) {
     const bf16x8 qr = rope8(qreg[s], 16 * s + 8 * g, pt, ph, pw, freq, a.rope);
     uacc = mfma_bf16(*(const bf16x8 *)(a.wqT + col * D + 16 * s + 8 * g), qr, uacc);
   }
-  const f32x4 *zb = (const f32x4 *)(a.z + (int64_t)bh * 32);
+  // the state this token's low-rank term reads: the head's, or (complement
+  // scope) its query block's
+  const int64_t qi = (int64_t)bh * a.nb + (tile >> 1);
+  const f32x4 *zb = (const f32x4 *)(a.comp ? a.zc + qi * 32 : a.z + (int64_t)bh * 32);
   f32x4 zr[4];
 #pragma unroll
   for (int q4 = 0; q4 < 4; ++q4) zr[q4] = zb[2 * q4 + g];  // z[8 q4 + 4 g .. +4]
@@ -160,12 +163,13 @@ __global__ __launch_bounds__(256) void k_bwd_query(BwdArgs a) {
     den += av[i] * zr[i >> 2][i & 3];
   }
   den += shfl_xor32(den);
-  const float inv_den = 1.0f / den;
+  // den = 0 only for an empty complement (every block kept): no low-rank term
+  const float inv_den = den > 0.0f ? 1.0f / den : 0.0f;
   bf16x8 aop[2];
 #pragma unroll
   for (int i = 0; i < 16; ++i) aop[i >> 3][i & 7] = (__bf16)av[i];
   // num = S^T a (rows d)
-  const uint16_t *stb = a.st + (int64_t)bh * D * 32;
+  const uint16_t *stb = a.comp ? a.stc + qi * D * 32 : a.st + (int64_t)bh * D * 32;
   f32x16 num[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
@@ -210,8 +214,8 @@ __global__ __launch_bounds__(256) void k_bwd_query(BwdArgs a) {
   const float sc = gv * inv_den, dden = -gv * dg * inv_den;
   // da = S dnum + z dden (rows r).  The two terms largely cancel, so S and
   // dnum enter as bf16 pairs hi + lo (three products: hi hi, hi lo, lo hi)
-  const uint16_t *sdb = a.sd + (int64_t)bh * 32 * D;
-  const uint16_t *sdl = sdb + a.bh_count * 32 * D;
+  const uint16_t *sdb = a.comp ? a.sdc + qi * 32 * D : a.sd + (int64_t)bh * 32 * D;
+  const uint16_t *sdl = sdb + (a.comp ? a.bh_count * a.nb : a.bh_count) * 32 * D;
   f32x16 da = f32x16{};
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
@@ -285,8 +289,10 @@ __global__ __launch_bounds__(256) void k_bwd_query(BwdArgs a) {
 //   kOuterDout:  X = dO,   Y = g a / den        -> dS^T per head
 //   kOuterRopeK: X = R(k), Y = dL/dw' (key)     -> dWk (summed over heads)
 //   kOuterGate:  X = q,    Y = (dy, 0, ..., 0)  -> gate weights (column 0)
+//   kOuterDoutBlk: as kOuterDout, one sum per query block (complement scope)
 // Workgroup (p, bh) takes tiles p*4 + wave, p*4 + wave + 4*PP, ... of head bh
-// and writes one fp32 partial [D][32] per wave.
+// and writes one fp32 partial [D][32] per wave; in kOuterDoutBlk it takes
+// query blocks p*4 + wave, ... and writes each block's sum in bf16.
 template <int D, int MODE>
 __global__ __launch_bounds__(256) void k_bwd_outer(BwdArgs a, int PP) {
   constexpr int NS = D / 16, DT = D / 32;
@@ -304,14 +310,14 @@ __global__ __launch_bounds__(256) void k_bwd_outer(BwdArgs a, int PP) {
   f32x16 acc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
-  for (int tile = p * 4 + wave; tile < 2 * a.nb; tile += 4 * PP) {
+  auto do_tile = [&](int tile) __attribute__((always_inline)) {
     const int64_t n = (int64_t)tile * 32 + col;
     const bool valid = n < a.n_tokens;
     const int64_t nc = valid ? n : a.n_tokens - 1;
     const int64_t row = (int64_t)bh * n_pad + n;
     // X row (8 dims per 16-byte chunk 2s + g), zero on padded tokens
     bf16x8 xr[NS];
-    if (MODE == kOuterDout) {
+    if (MODE == kOuterDout || MODE == kOuterDoutBlk) {
 #pragma unroll
       for (int s = 0; s < NS; ++s) xr[s] = *(const bf16x8 *)(a.dob + row * D + 16 * s + 8 * g);
     } else {
@@ -342,7 +348,7 @@ __global__ __launch_bounds__(256) void k_bwd_outer(BwdArgs a, int PP) {
       y0 = u32x4{g == 0 ? (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)dyv) : 0u, 0u, 0u, 0u};
       y1 = u32x4{0u, 0u, 0u, 0u};
     } else {
-      const uint16_t *ysrc = (MODE == kOuterRopeQ ? a.duq : MODE == kOuterDout ? a.ahat : a.dwk_tok) + row * 32;
+      const uint16_t *ysrc = (MODE == kOuterRopeQ ? a.duq : (MODE == kOuterDout || MODE == kOuterDoutBlk) ? a.ahat : a.dwk_tok) + row * 32;
       y0 = *(const u32x4 *)(ysrc + 16 * g);
       y1 = *(const u32x4 *)(ysrc + 16 * g + 8);
     }
@@ -356,7 +362,26 @@ __global__ __launch_bounds__(256) void k_bwd_outer(BwdArgs a, int PP) {
       for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma_bf16(vt_operand<D>(X, s2, dt, lane), yb, acc[dt]);
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next tile's writes
+    };
+  if constexpr (MODE == kOuterDoutBlk) {
+    // one query block (two tiles) at a time: its dS_i^T in bf16
+    for (int qb = p * 4 + wave; qb < a.nb; qb += 4 * PP) {
+      do_tile(2 * qb);
+      do_tile(2 * qb + 1);
+      uint16_t *ob = a.pblk + ((int64_t)bh * a.nb + qb) * (D * 32);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int d = 32 * dt + 8 * (i >> 2) + 4 * g + (i & 3);
+          ob[d * 32 + col] = __builtin_bit_cast(uint16_t, (__bf16)acc[dt][i]);
+        }
+        acc[dt] = f32x16{};
+      }
+    }
+    return;
   }
+  for (int tile = p * 4 + wave; tile < 2 * a.nb; tile += 4 * PP) do_tile(tile);
   float *out = a.part + (((int64_t)bh * PP + p) * 4 + wave) * (D * 32);
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
@@ -465,6 +490,102 @@ __global__ __launch_bounds__(256) void k_bwd_dsops(BwdArgs a) {
   a.dst[bh * D * 32 + d * 32 + perm16_key_of_pos(r)] = __builtin_bit_cast(uint16_t, v);
 }
 
+// ------------------------------------------------------ complement scope
+// Query block i's low-rank term reads S_i = sum of the states S_j of the key
+// blocks i does not keep, so the gradient of a block state is
+//   dS_j = sum over query blocks i that do not keep j of dS_i
+//        = (sum over all i of dS_i) - sum over the i that keep j of dS_i,
+// with dS_i = sum over i's tokens of (g a / den) dO^T, and dz_j likewise
+// from dz_i = -sum over i's tokens of dg (g a / den).  The per-query-block
+// sums are bf16 (dS_i) and fp32 (dz_i); the head totals add the same bf16
+// values in fp32, in block order.
+
+// dz_i: one wave per query block, lane (half, r) summing 32 tokens for rank r
+__global__ __launch_bounds__(256) void k_bwd_dzblk(BwdArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, r = lane & 31, hf = lane >> 5;
+  const int bh = blockIdx.y, qb = blockIdx.x * 4 + wave;
+  if (qb >= a.nb) return;
+  const int64_t n_pad = (int64_t)a.nb * 64;
+  const int64_t row0 = (int64_t)bh * n_pad + (int64_t)qb * 64 + 32 * hf;
+  float acc = 0.0f;
+  for (int t = 0; t < 32; ++t)
+    acc -= a.dg[row0 + t] * __builtin_bit_cast(float, ((uint32_t)a.ahat[(row0 + t) * 32 + r]) << 16);
+  acc += __shfl_xor(acc, 32, 64);
+  if (hf == 0) a.dzblk[((int64_t)bh * a.nb + qb) * 32 + r] = acc;
+}
+
+// head totals of dS_i^T into ds32 [BH][D*32], in block order
+template <int D>
+__global__ __launch_bounds__(256) void k_bwd_sumblk(BwdArgs a) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= D * 32) return;
+  const int bh = blockIdx.y;
+  const uint16_t *p = a.pblk + (int64_t)bh * a.nb * (D * 32) + idx;
+  float acc8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  auto at = [&](int64_t i) { return __builtin_bit_cast(float, ((uint32_t)p[i * (D * 32)]) << 16); };
+  int64_t i = 0;
+  for (; i + 8 <= a.nb; i += 8) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc8[u] += at(i + u);
+  }
+  for (int u = 0; i + u < a.nb; ++u) acc8[u] += at(i + u);
+  a.ds32[(int64_t)bh * D * 32 + idx] =
+      ((acc8[0] + acc8[1]) + (acc8[2] + acc8[3])) + ((acc8[4] + acc8[5]) + (acc8[6] + acc8[7]));
+}
+
+// dS_j, dz_j per key block j: the head total minus the sums of the query
+// blocks that keep j (the transposed map), written as the bf16 operand copies
+// of k_bwd_key (dsrc as dsr, dstc as dst) and dz_j in fp32.  One workgroup per
+// key block; thread t owns elements [t*D/8, (t+1)*D/8) of the [D][32] sum.
+template <int D>
+__global__ __launch_bounds__(256) void k_bwd_dsc(BwdArgs a) {
+  constexpr int EPT = D / 8;
+  typedef const __attribute__((address_space(4))) int32_t *cint_p;
+  const int tid = threadIdx.x, j = blockIdx.x, bh = blockIdx.y;
+  const int64_t kj = (int64_t)bh * a.nb + j;
+  const int cnt = ((cint_p)a.tcount)[kj];
+  const cint_p list = (cint_p)(a.tlist + kj * a.nb);
+  const uint16_t *pb = a.pblk + (int64_t)bh * a.nb * (D * 32) + tid * EPT;
+  const float *zb = a.dzblk + (int64_t)bh * a.nb * 32 + 4 * tid;
+  float acc[EPT], az[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) acc[e] = 0.0f;
+  for (int t = 0; t < cnt; ++t) {
+    const int64_t i = list[t];
+    const u32x4 *src = (const u32x4 *)(pb + i * (D * 32));
+#pragma unroll
+    for (int c = 0; c < EPT / 8; ++c) {
+      const u32x4 w = src[c];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[8 * c + 2 * e] += bflo(w[e]);
+        acc[8 * c + 2 * e + 1] += bfhi(w[e]);
+      }
+    }
+    if (tid < 8) {
+      const f32x4 zz = *(const f32x4 *)(zb + i * 32);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) az[e] += zz[e];
+    }
+  }
+  const float *tot = a.ds32 + (int64_t)bh * D * 32 + tid * EPT;
+  uint16_t *dr = a.dsrc + kj * 32 * D, *dt = a.dstc + kj * D * 32;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int idx = tid * EPT + e, d = idx / 32, r = idx % 32;
+    const uint16_t v = __builtin_bit_cast(uint16_t, (__bf16)(tot[e] - acc[e]));
+    dr[r * D + d] = v;
+    dt[d * 32 + perm16_key_of_pos(r)] = v;
+  }
+  if (tid < 8) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 4 * tid + e;
+      a.dzc[kj * 32 + r] = r < a.rank ? a.dz[(int64_t)bh * 32 + r] - az[e] : 0.0f;
+    }
+  }
+}
+
 // ------------------------------------------------------------- k_bwd_key
 // One wave per 32-token tile of keys: b = phi(Wk^T R(k)), db = dS v + dz,
 // dw' = db phi'(.), the low-rank parts of dk (R^T(Wk dw')) and dv (dS^T b).
@@ -494,7 +615,9 @@ __global__ __launch_bounds__(256) void k_bwd_key(BwdArgs a) {
   int pt, ph, pw;
   token_pos(mc, a.rope, pt, ph, pw);
   f32x16 wacc = f32x16{}, db = f32x16{};
-  const uint16_t *dsb = a.dsr + (int64_t)bh * 32 * D;
+  // dS and dz of the head, or (complement scope) of this key block
+  const int64_t kj = (int64_t)bh * a.nb + (tile >> 1);
+  const uint16_t *dsb = a.comp ? a.dsrc + kj * 32 * D : a.dsr + (int64_t)bh * 32 * D;
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const f32x4 fr = *(const f32x4 *)&sfreq[8 * s + 4 * g];
@@ -503,7 +626,7 @@ __global__ __launch_bounds__(256) void k_bwd_key(BwdArgs a) {
     wacc = mfma_bf16(*(const bf16x8 *)(a.wkT + col * D + 16 * s + 8 * g), kr, wacc);
     db = mfma_bf16(*(const bf16x8 *)(dsb + col * D + 16 * s + 8 * g), vreg[s], db);
   }
-  const f32x4 *dzb = (const f32x4 *)(a.dz + (int64_t)bh * 32);
+  const f32x4 *dzb = (const f32x4 *)(a.comp ? a.dzc + kj * 32 : a.dz + (int64_t)bh * 32);
   float bv[16], dw[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -523,7 +646,7 @@ __global__ __launch_bounds__(256) void k_bwd_key(BwdArgs a) {
   for (int q4 = 0; q4 < 4; ++q4)
     *(uint2 *)(a.dwk_tok + row * 32 + 8 * q4 + 4 * g) =
         pack_bf16x4(dw[4 * q4], dw[4 * q4 + 1], dw[4 * q4 + 2], dw[4 * q4 + 3]);
-  const uint16_t *dstb = a.dst + (int64_t)bh * D * 32;
+  const uint16_t *dstb = a.comp ? a.dstc + kj * D * 32 : a.dst + (int64_t)bh * D * 32;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
     f32x16 dv = f32x16{}, dr = f32x16{};
@@ -1067,9 +1190,27 @@ void launch_bwd_dsops(const BwdArgs &a, int D, hipStream_t st) {
   const int64_t bias_at = a.bh_count * 4LL * PP * (D * 32);
   hipLaunchKernelGGL(k_bwd_dz, dim3(kDzParts, (unsigned)a.bh_count), dim3(256), 0, st, a);
   hipLaunchKernelGGL(k_bwd_dz2, dim3((unsigned)a.bh_count), dim3(64), 0, st, a, bias_at);
+  if (a.comp) return;  // the complement scope's operands are per key block (k_bwd_dsc)
   const dim3 grid(cdiv(a.bh_count * D * 32, 256));
   if (D == 64) hipLaunchKernelGGL(k_bwd_dsops<64>, grid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL(k_bwd_dsops<128>, grid, dim3(256), 0, st, a);
+}
+
+void launch_bwd_comp_parts(const BwdArgs &a, int D, hipStream_t st) {
+  const int PP = cdiv(a.nb, 4);  // one query block per wave
+  const dim3 grid(PP, (unsigned)a.bh_count), block(256);
+  if (D == 64) hipLaunchKernelGGL((k_bwd_outer<64, kOuterDoutBlk>), grid, block, 0, st, a, PP);
+  else hipLaunchKernelGGL((k_bwd_outer<128, kOuterDoutBlk>), grid, block, 0, st, a, PP);
+  hipLaunchKernelGGL(k_bwd_dzblk, grid, block, 0, st, a);
+  const dim3 gsum(cdiv(D * 32, 256), (unsigned)a.bh_count);
+  if (D == 64) hipLaunchKernelGGL(k_bwd_sumblk<64>, gsum, block, 0, st, a);
+  else hipLaunchKernelGGL(k_bwd_sumblk<128>, gsum, block, 0, st, a);
+}
+
+void launch_bwd_comp_keys(const BwdArgs &a, int D, hipStream_t st) {
+  const dim3 grid((unsigned)a.nb, (unsigned)a.bh_count);
+  if (D == 64) hipLaunchKernelGGL(k_bwd_dsc<64>, grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(k_bwd_dsc<128>, grid, dim3(256), 0, st, a);
 }
 
 void launch_bwd_key(const BwdArgs &a, int D, hipStream_t st) {

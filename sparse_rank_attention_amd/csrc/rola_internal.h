@@ -128,6 +128,8 @@ struct CompArgs {
   int64_t bh_count, ngroups, groups_per_xcd, list_stride;
   uint16_t *stc;           // out: bf16 [BH][nb][D][32], rank-permuted like st
   float *zc;               // out: [BH][nb][32]
+  uint16_t *sdc;           // out (backward only, else NULL): bf16 [2][BH][nb][32][D], the
+                           // complement S with d permuted per 16-group, as hi + lo (like sd)
 };
 void launch_complement(const CompArgs &a, int D, hipStream_t st);
 void launch_scores(const float *qp, const float *kp, float *s, int nb, int D, int bh,
@@ -183,19 +185,35 @@ struct BwdArgs {
   float *sumtmp;              // per-head sums of the pooled gradients [BH][D][32]
   int32_t *tcount, *tlist;    // query blocks keeping each key block: [BH][nb], [BH][nb][nb]
   int32_t *tbits;             // the map as bitsets over key blocks [BH][nb][ceil(nb/32)]
+  // complement scope (comp != 0): per query block i the state S_i, z_i over
+  // the key blocks i does not keep (from the forward's complement kernel),
+  // and per key block j the gradient of its block state, dS_j = sum over the
+  // query blocks that do not keep j of their dS_i
+  int comp;
+  const uint16_t *stc;        // bf16 [BH][nb][D][32], rank-permuted (as st)
+  const float *zc;            // [BH][nb][32]
+  const uint16_t *sdc;        // bf16 [2][BH][nb][32][D], d permuted (as sd: hi, lo)
+  uint16_t *pblk;             // bf16 [BH][nb][D][32]: dS_i^T per query block
+  float *dzblk;               // [BH][nb][32]: dz_i per query block
+  uint16_t *dsrc, *dstc;      // bf16 [BH][nb][32][D] (as dsr), [BH][nb][D][32] (as dst): dS_j
+  float *dzc;                 // [BH][nb][32]: dz_j
   // outputs
   uint16_t *dq, *dk, *dv;     // bf16, caller layout
   float *dwq, *dwk, *dgate;   // [D][rank], [D][rank], [D+1]
 };
 
 // X^T Y reductions over tokens (dWq, dWk, dS, gate weights)
-enum BwdOuterMode { kOuterRopeQ = 0, kOuterDout = 1, kOuterRopeK = 2, kOuterGate = 3 };
+enum BwdOuterMode { kOuterRopeQ = 0, kOuterDout = 1, kOuterRopeK = 2, kOuterGate = 3, kOuterDoutBlk = 4 };
 
 void launch_bwd_prep(const BwdArgs &a, int D, hipStream_t st);   // wqP, wkP, sd
 void launch_bwd_query(const BwdArgs &a, int D, hipStream_t st);  // low-rank and gate, per query token
 void launch_bwd_outer(const BwdArgs &a, int D, int mode, hipStream_t st);
 void launch_bwd_dsops(const BwdArgs &a, int D, hipStream_t st);  // dz, then dS operands
 void launch_bwd_key(const BwdArgs &a, int D, hipStream_t st);    // low-rank, per key token
+// complement scope: dS_i, dz_i per query block and their head totals, then
+// (after the transposed map) dS_j, dz_j per key block as operand copies
+void launch_bwd_comp_parts(const BwdArgs &a, int D, hipStream_t st);
+void launch_bwd_comp_keys(const BwdArgs &a, int D, hipStream_t st);
 void launch_bwd_dq(const BwdArgs &a, int D, hipStream_t st);     // sparse dq (+ the low-rank part)
 void launch_bwd_tmap(const BwdArgs &a, hipStream_t st);
 void launch_bwd_dkv(const BwdArgs &a, int D, hipStream_t st);    // sparse dk, dv (+ low-rank parts)

@@ -632,6 +632,18 @@ __global__ __launch_bounds__(256) void k_complement(CompArgs a) {
         uint16_t *so = a.stc + qi * D * 32 + d * 32;
         *(uint2 *)(so + pa) = o[0];
         *(uint2 *)(so + pb) = o[1];
+        if (a.sdc) {
+          // the backward's [32][D] operand of S dnum: d at its permuted
+          // position (the permutation is its own inverse), hi + lo
+          const int pd = perm16_key_of_pos(d);
+          uint16_t *hi = a.sdc + qi * 32 * D + pd, *lo = hi + a.bh_count * a.nb * 32LL * D;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const __bf16 hv = (__bf16)v[e];
+            hi[(r0 + e) * D] = __builtin_bit_cast(uint16_t, hv);
+            lo[(r0 + e) * D] = __builtin_bit_cast(uint16_t, (__bf16)(v[e] - (float)hv));
+          }
+        }
       } else if (c < TC) {
         const int r = 4 * (c - SC);
         const f32x4 zz = *(const f32x4 *)(zg + r);

@@ -149,7 +149,12 @@ def test_backward_validates_before_launch():
     assert call(cfg, args) == 3                               # dout misaligned
     assert call(cfg, ok, big - 1) == 4                        # workspace too small
     assert call(rola.Config(topk=0.25, rank=16, precision=rola.ROLA_PREC_FP8), ok) == 2
-    assert call(rola.Config(topk=0.25, rank=16, lowrank_scope=rola.ROLA_LR_COMPLEMENT), ok) == 2
+    # the complement scope plans per-block states and per-block gradient sums
+    # on top, and checks for them before launching
+    comp = rola.Config(topk=0.25, rank=16, lowrank_scope=rola.ROLA_LR_COMPLEMENT)
+    st, cinfo = _plan(prob, comp)
+    assert st == 0 and cinfo.workspace_bytes_backward > big
+    assert call(comp, ok, cinfo.workspace_bytes_backward - 1) == 4
 
 
 def test_mfma_probe_validates_before_launch():

@@ -34,8 +34,11 @@ def _torch():
 
 
 def _ratio(got, ref, bf16_store):
-    """max over elements of |got - ref| / bound (<= 1 passes)."""
+    """max over elements of |got - ref| / bound (<= 1 passes); a reference that is
+    exactly zero (no low-rank term at all) must be matched exactly."""
     rms = np.sqrt(np.mean(ref ** 2))
+    if rms == 0.0:
+        return 0.0 if np.all(got == 0) else float("inf")
     bound = TOL_BWD * rms
     if bf16_store:
         bound = bound * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(ref)
@@ -46,18 +49,17 @@ CASES = SMALL + [("d128_1280", small_workload((5, 16, 16), D=128, H=2, rank=32, 
                  ("two_batches", W.Workload("b2", 2, 2, 64, (3, 7, 11), 0.25, 16, "iid", seed=3))]
 
 
-@pytest.mark.parametrize("name,w", CASES, ids=[c[0] for c in CASES])
-@pytest.mark.parametrize("gated", [False, True], ids=["nogate", "gate"])
-@pytest.mark.parametrize("dout_f32", [False, True], ids=["dobf16", "dof32"])
-def test_backward_matches_oracle(name, w, gated, dout_f32):
+def _backward_case(name, w, gated, dout_f32, complement=False):
     from sparse_rank_attention_amd import rola
     torch = _torch()
-    say("backward", name, "gate" if gated else "nogate", "f32" if dout_f32 else "bf16")
+    say("backward", name, "complement" if complement else "global", "gate" if gated else "nogate",
+        "f32" if dout_f32 else "bf16")
     q, k, v = W.make_qkv(w)
     wq, wk = W.make_proj(w)
     g = W.make_gate(w) if gated else None
     do = W.make_dout(w, f32=dout_f32)
-    cfg = rola.Config(topk=w.topk, rank=w.rank, out_dtype=rola.ROLA_OUT_F32 if dout_f32 else rola.ROLA_OUT_BF16)
+    cfg = rola.Config(topk=w.topk, rank=w.rank, out_dtype=rola.ROLA_OUT_F32 if dout_f32 else rola.ROLA_OUT_BF16,
+                      lowrank_scope=rola.ROLA_LR_COMPLEMENT if complement else rola.ROLA_LR_GLOBAL)
     qd, kd, vd = dev(q), dev(k), dev(v)
     bmap = rola.rola_select_blocks(qd, kd, w.grid, cfg)
     dod = torch.from_numpy(do).cuda() if dout_f32 else dev(do)
@@ -73,7 +75,8 @@ def test_backward_matches_oracle(name, w, gated, dout_f32):
     f64 = oracle.widen_bf16
     # an fp32 dout is taken at bf16 precision (the header's contract)
     do_ref = f64(W.to_bf16_bits(flat(do))) if dout_f32 else f64(flat(do))
-    ref = OB.backward(f64(flat(q)), f64(flat(k)), f64(flat(v)), wq, wk, m_ref, do_ref, w.n_tokens, w.grid, gate=g)
+    ref = OB.backward(f64(flat(q)), f64(flat(k)), f64(flat(v)), wq, wk, m_ref, do_ref, w.n_tokens, w.grid, gate=g,
+                      complement=complement)
     n = w.n_tokens
     ratios = {}
     for key, got in (("dq", dq), ("dk", dk), ("dv", dv)):
@@ -87,6 +90,21 @@ def test_backward_matches_oracle(name, w, gated, dout_f32):
     say("backward", name, "err/bound", {k_: round(v_, 3) for k_, v_ in ratios.items()})
     for key, r in ratios.items():
         assert r <= 1.0, (key, r)
+
+
+@pytest.mark.parametrize("name,w", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("gated", [False, True], ids=["nogate", "gate"])
+@pytest.mark.parametrize("dout_f32", [False, True], ids=["dobf16", "dof32"])
+def test_backward_matches_oracle(name, w, gated, dout_f32):
+    _backward_case(name, w, gated, dout_f32)
+
+
+# The complement scope: each query block's low-rank sums run over the key
+# blocks it does not keep (single_block keeps its only block: no low-rank term).
+@pytest.mark.parametrize("name,w", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("gated,dout_f32", [(False, False), (True, True)], ids=["nogate-dobf16", "gate-dof32"])
+def test_backward_complement_matches_oracle(name, w, gated, dout_f32):
+    _backward_case(name, w, gated, dout_f32, complement=True)
 
 
 def test_backward_full_size_sampled():
@@ -127,6 +145,48 @@ def test_backward_full_size_sampled():
     ratios["dwq"] = _ratio(host_f64(dwq), dwq_ref, False)
     ratios["dwk"] = _ratio(host_f64(dwk), dwk_ref, False)
     say("backward full size", name, "err/bound", {k_: round(v_, 3) for k_, v_ in ratios.items()})
+    for key, r in ratios.items():
+        assert r <= 1.0, (key, r)
+
+
+def test_backward_complement_full_size_sampled():
+    """The complement-scope backward at the benchmarked size (Wan 14B 720P, bf16
+    dL/dO) against the written-out formulas in that scope
+    (oracle.backward.backward_sampled, pinned to autograd): dq rows of sampled
+    query blocks and dk, dv rows of sampled key blocks in two heads.  The
+    projection gradients sum over all 40 heads; the small cases cover them."""
+    from sparse_rank_attention_amd import rola
+    from tests.test_gpu_parity import _full_inputs
+    torch = _torch()
+    name = "wan14b_720p"
+    say("backward complement full size", name)
+    w, (q, k, v), (wq, wk) = _full_inputs(name)
+    do = W.make_dout(w)
+    cfg = rola.Config(topk=w.topk, rank=w.rank, lowrank_scope=rola.ROLA_LR_COMPLEMENT)
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    bmap = rola.rola_select_blocks(qd, kd, w.grid, cfg)
+    dq, dk, dv, _, _, _ = rola.rola_backward(qd, kd, vd, torch.from_numpy(wq).cuda(), torch.from_numpy(wk).cuda(),
+                                             w.grid, cfg, bmap, dev(do))
+    torch.cuda.synchronize()
+    heads = (1, w.heads - 2)
+    maps = bmap.cpu().numpy()[0]
+    for h in heads:
+        np.testing.assert_array_equal(maps[h], oracle.block_map(q[0][h:h + 1], k[0][h:h + 1], w.n_tokens,
+                                                                oracle.keep_blocks(w.topk, w.nb))[0])
+    rng = np.random.default_rng(19)
+    pick = lambda: sorted({n for b in {0, w.nb // 2, w.nb - 1, *rng.integers(0, w.nb, 3).tolist()}
+                           for n in (b * 64, b * 64 + 33, b * 64 + 63) if n < w.n_tokens})
+    q_rows = {h: pick() for h in heads}
+    k_rows = {h: pick() for h in heads}
+    rq, rk, rv, _, _, _ = OB.backward_sampled(q[0], k[0], v[0], wq, wk, maps, do[0], w.n_tokens, w.grid,
+                                              q_rows, k_rows, complement=True, heads=heads)
+    ratios = {}
+    for h in heads:
+        for key, got, rows, ref in (("dq", dq, q_rows[h], rq[h]), ("dk", dk, k_rows[h], rk[h]),
+                                    ("dv", dv, k_rows[h], rv[h])):
+            g = got[0, h, torch.tensor(rows, device="cuda")].float().cpu().numpy().astype(np.float64)
+            ratios["%s_h%d" % (key, h)] = _ratio(g, ref, True)
+    say("backward complement full size", name, "err/bound", {k_: round(v_, 3) for k_, v_ in ratios.items()})
     for key, r in ratios.items():
         assert r <= 1.0, (key, r)
 

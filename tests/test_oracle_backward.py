@@ -99,18 +99,22 @@ def test_gradients_match_finite_differences(complement, gated):
         assert abs(fd - an) <= 1e-5 * max(1.0, abs(an)), (name, idx, fd, an)
 
 
+@pytest.mark.parametrize("complement", [False, True], ids=["global", "complement"])
 @pytest.mark.parametrize("gated", [False, True], ids=["nogate", "gate"])
-def test_sampled_formulas_equal_autograd(gated):
+def test_sampled_formulas_equal_autograd(gated, complement):
     """The written-out gradient formulas (used at full size on sampled rows)
-    reproduce the autograd gradients on every row of a small case."""
+    reproduce the autograd gradients on every row of a small case, in both
+    low-rank scopes."""
     c = _case(71 + gated, grid=(3, 7, 11), n_pad=256, d=64, r=16, bh=2, kb=2)
     g = c["g"] if gated else None
     dout_bits = to_bf16_bits(c["dout"].astype(np.float32))
     dout = oracle.widen_bf16(dout_bits)
-    ref = B.backward(c["q"], c["k"], c["v"], c["wq"], c["wk"], c["bmap"], dout, c["n_valid"], c["grid"], gate=g)
+    ref = B.backward(c["q"], c["k"], c["v"], c["wq"], c["wk"], c["bmap"], dout, c["n_valid"], c["grid"], gate=g,
+                     complement=complement)
     rows = {h: list(range(c["n_valid"])) for h in range(2)}
     dq, dk, dv, dwq, dwk, dgate = B.backward_sampled(c["qb"], c["kb"], c["vb"], c["wq"], c["wk"], c["bmap"],
-                                                     dout_bits, c["n_valid"], c["grid"], rows, rows, gate=g)
+                                                     dout_bits, c["n_valid"], c["grid"], rows, rows, gate=g,
+                                                     complement=complement)
     for h in range(2):
         np.testing.assert_allclose(dq[h], ref["dq"][h, :c["n_valid"]], rtol=1e-9, atol=1e-12)
         np.testing.assert_allclose(dk[h], ref["dk"][h, :c["n_valid"]], rtol=1e-9, atol=1e-12)
@@ -119,3 +123,24 @@ def test_sampled_formulas_equal_autograd(gated):
     np.testing.assert_allclose(dwk, ref["dwk"], rtol=1e-9, atol=1e-12)
     if gated:
         np.testing.assert_allclose(dgate, ref["dgate"], rtol=1e-9, atol=1e-12)
+
+
+def test_sampled_formulas_empty_complement():
+    """Every block kept (kb = nb): the complement is empty, the low-rank term and
+    its gradients vanish, and the written-out formulas still equal autograd."""
+    c = _case(75, grid=(3, 7, 11), n_pad=256, d=64, r=16, bh=2, kb=4)
+    g = c["g"]
+    dout_bits = to_bf16_bits(c["dout"].astype(np.float32))
+    dout = oracle.widen_bf16(dout_bits)
+    ref = B.backward(c["q"], c["k"], c["v"], c["wq"], c["wk"], c["bmap"], dout, c["n_valid"], c["grid"], gate=g,
+                     complement=True)
+    assert np.all(ref["dwq"] == 0) and np.all(ref["dwk"] == 0)
+    rows = {h: list(range(c["n_valid"])) for h in range(2)}
+    dq, dk, dv, dwq, dwk, dgate = B.backward_sampled(c["qb"], c["kb"], c["vb"], c["wq"], c["wk"], c["bmap"],
+                                                     dout_bits, c["n_valid"], c["grid"], rows, rows, gate=g,
+                                                     complement=True)
+    for h in range(2):
+        np.testing.assert_allclose(dq[h], ref["dq"][h, :c["n_valid"]], rtol=1e-9, atol=1e-12)
+        np.testing.assert_allclose(dk[h], ref["dk"][h, :c["n_valid"]], rtol=1e-9, atol=1e-12)
+        np.testing.assert_allclose(dv[h], ref["dv"][h, :c["n_valid"]], rtol=1e-9, atol=1e-12)
+    assert np.all(dwq == 0) and np.all(dwk == 0) and np.all(dgate == 0)
