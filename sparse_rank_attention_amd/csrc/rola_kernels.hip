@@ -1382,12 +1382,15 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn(AttnArgs args) {
         // fp16 weights below 2^-24 vanish; relative to the row sum (at least
         // 1/2) they are negligible.
         constexpr float W = EXACT ? 64.0f : 15.0f;
-        float mx0 = -INFINITY, mx1 = -INFINITY;
+        float mx0 = -INFINITY, mx1 = -INFINITY, mx2 = -INFINITY, mx3 = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx0 = fmaxf(mx0, sacc0[i]);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx1 = fmaxf(mx1, sacc1[i]);
-        const float mx = pair_max32(fmaxf(mx0, mx1)) * c;
+        for (int i = 0; i < 8; ++i) {
+          mx0 = fmaxf(mx0, sacc0[i]);
+          mx1 = fmaxf(mx1, sacc1[i]);
+          mx2 = fmaxf(mx2, sacc0[8 + i]);
+          mx3 = fmaxf(mx3, sacc1[8 + i]);
+        }
+        const float mx = pair_max32(fmaxf(fmaxf(mx0, mx1), fmaxf(mx2, mx3))) * c;
         const bool grow = mx > m_run + W;  // always true on the first tile (m_run = -inf)
         if (__builtin_amdgcn_ballot_w64(grow)) {
           const float m_new = grow ? ceilf(mx) : m_run;
@@ -1399,7 +1402,9 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn(AttnArgs args) {
         }
         const float negm = -m_run;
         const f16x2 ones = {(__fp16)1.0f, (__fp16)1.0f};
-        float psum = 0.0f;
+        // the row sum in four independent chains, one per step (a single
+        // chain of dependent adds would serialise the step's weights)
+        float psum4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         // ---- weights for 16 keys at a time, each step feeding 4 PV MFMAs
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
@@ -1412,7 +1417,7 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn(AttnArgs args) {
               const float wv = fast_exp2(__builtin_fmaf(src[8 * (s & 1) + e], c, negm));
               pw[e] = (__bf16)wv;
               plo[e] = (__bf16)(wv - (float)pw[e]);
-              psum += wv;
+              psum4[s] += wv;
             }
           } else {
             // fp16 weights rounded toward zero (one packed conversion per
@@ -1425,7 +1430,7 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn(AttnArgs args) {
                                                           fast_exp2(__builtin_fmaf(src[i + 1], c, negm)));
               ph[2 * e] = pr[0];
               ph[2 * e + 1] = pr[1];
-              psum = __builtin_amdgcn_fdot2(pr, ones, psum, false);
+              psum4[s] = __builtin_amdgcn_fdot2(pr, ones, psum4[s], false);
             }
           }
           // the step's V^T operands (2*DT transposing reads) before its MFMAs
@@ -1443,7 +1448,7 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn(AttnArgs args) {
             }
           }
         }
-        l_run += psum;
+        l_run += (psum4[0] + psum4[1]) + (psum4[2] + psum4[3]);
       };
       if constexpr (S == 4) {
       // Two tiles per barrier: iteration k consumes tiles 2k and 2k+1 and,
