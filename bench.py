@@ -75,6 +75,7 @@ def parse():
                     help="time a w8a8 linear layer instead (wan14b_720p_qkv, wan14b_720p_out, ...)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true", help="skip the MFMA-probe and copy measurements")
+    ap.add_argument("--no-graph", action="store_true", help="skip the timing of the forward replayed as a HIP graph")
     ap.add_argument("--cpu-baseline-child", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--sample-stride", type=int, default=32,
                     help="CPU baseline with --complement: every n-th query block of head 0")
@@ -484,12 +485,13 @@ def main():
             del xf
         torch.cuda.synchronize()
 
-    def fwd():
+    def fwd(on=None):
+        st_ = stream if on is None else on
         if e4m3:
-            rola.rola_forward_e4m3(qd, kd, vd, *codes, *scales, wqd, wkd, w.grid, cfg, out=out, stream=stream,
+            rola.rola_forward_e4m3(qd, kd, vd, *codes, *scales, wqd, wkd, w.grid, cfg, out=out, stream=st_,
                                    gate=gd)
         else:
-            rola.rola_forward(qd, kd, vd, wqd, wkd, w.grid, cfg, out=out, stream=stream, gate=gd)
+            rola.rola_forward(qd, kd, vd, wqd, wkd, w.grid, cfg, out=out, stream=st_, gate=gd)
 
     dominant = "attn8_sparse_lowrank" if fp8 else "attn_sparse_lowrank"
     peak = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
@@ -518,6 +520,33 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
+
+    # the same forward captured once as a HIP graph and replayed: one graph launch
+    # per step instead of the binding's per-kernel launches (the call only
+    # launches kernels, so it captures as it is); reported next to the headline
+    graph = None
+    if not args.no_graph:
+        print("[bench] graph capture and %d replays" % args.steps, file=sys.stderr, flush=True)
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            fwd(side)  # the capture stream's workspace, made before the capture
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            fwd(side)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        eg0, eg1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        eg0.record(stream)
+        for _ in range(args.steps):
+            g.replay()
+        eg1.record(stream)
+        torch.cuda.synchronize()
+        graph = {"steps": args.steps, "ms_per_step": round(eg0.elapsed_time(eg1) / args.steps, 4)}
+        del g
 
     # per-kernel breakdown: the same number of forwards again, with the library's
     # HIP events around each kernel on the call's stream (event pool made beforehand)
@@ -582,6 +611,7 @@ def main():
         "dense_equiv_tflops": round(dense / (ms * 1e-3) / 1e12, 1),
         "kept_block_tflops": round(kept / (ms * 1e-3) / 1e12, 1),
         "kernel_ms": {k_: round(v_, 4) for k_, v_ in sorted(kern_ms.items())},
+        "graph_replay": graph,
         "kernel_ms_pass": {"steps": args.steps, "fwd_ms": round(ms_breakdown, 4),
                            "how": "second pass with HIP events around every kernel; the headline ms has none"},
         "roofline": {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 1),
