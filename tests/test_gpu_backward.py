@@ -231,3 +231,36 @@ def test_long_union_lists():
     say("long union lists err/bound", {k_: round(v_, 3) for k_, v_ in ratios.items()})
     for key, r in ratios.items():
         assert r <= 1.0, (key, r)
+
+
+@pytest.mark.parametrize("complement", [False, True], ids=["global", "complement"])
+def test_backward_layouts_and_padding(complement):
+    """The backward on token-major views ([B, N, H, D] storage, the DiT layout)
+    and with NaN in every padded input row (q, k, v and dL/dO rows >= N) gives
+    the gradients of the head-major call bit for bit."""
+    from sparse_rank_attention_amd import rola
+    torch = _torch()
+    say("backward layouts", "complement" if complement else "global")
+    w = small_workload((3, 7, 11), D=128, H=3, rank=32, topk=0.5, kind="field", seed=6)
+    q, k, v = W.make_qkv(w)
+    wq, wk = W.make_proj(w)
+    do = W.make_dout(w)
+    wqd, wkd = torch.from_numpy(wq).cuda(), torch.from_numpy(wk).cuda()
+    cfg = rola.Config(topk=w.topk, rank=w.rank,
+                      lowrank_scope=rola.ROLA_LR_COMPLEMENT if complement else rola.ROLA_LR_GLOBAL)
+    qd, kd, vd, dod = dev(q), dev(k), dev(v), dev(do)
+    bmap = rola.rola_select_blocks(qd, kd, w.grid, cfg)
+    ref = rola.rola_backward(qd, kd, vd, wqd, wkd, w.grid, cfg, bmap, dod)
+    # token-major storage, same values
+    tm = [x.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3) for x in (qd, kd, vd, dod)]
+    got = rola.rola_backward(tm[0], tm[1], tm[2], wqd, wkd, w.grid, cfg, bmap, tm[3])
+    # NaN in the padded rows of every input
+    nan_in = [x.clone() for x in (qd, kd, vd, dod)]
+    for x in nan_in:
+        x[:, :, w.n_tokens:] = float("nan")
+    got_nan = rola.rola_backward(nan_in[0], nan_in[1], nan_in[2], wqd, wkd, w.grid, cfg, bmap, nan_in[3])
+    torch.cuda.synchronize()
+    bits = lambda t: t.contiguous().view(torch.int16) if t.dtype == torch.bfloat16 else t.contiguous().view(torch.int32)
+    for name, a, b, c in zip(("dq", "dk", "dv", "dwq", "dwk"), ref[:5], got[:5], got_nan[:5]):
+        assert torch.equal(bits(a), bits(b)), ("token-major", name)
+        assert torch.equal(bits(a), bits(c)), ("padded NaN", name)
