@@ -134,10 +134,13 @@ int32_t make_plan(const rola_problem *p, const rola_config *c, Plan *pl) {
     P.off_qsc = o; o = align_up(o + P.BH * nb * 8);
     P.off_ksc = o; o = align_up(o + P.BH * nb * 4);
     P.off_vsc = o; o = align_up(o + P.BH * nb * 4);
-    P.off_kv8 = o; o = align_up(o + P.BH * nb * 128LL * D);
+    P.off_kv8 = o; o = align_up(o + P.BH * nb * 64LL * D);
   }
   P.vh = !P.fp8 && c->out_dtype == ROLA_OUT_BF16;
   P.off_vh = P.off_vovf = 0;
+  if (P.fp8) {  // the V codes as fp16 values
+    P.off_vh = o; o = align_up(o + P.BH * P.n_pad * D * 2);
+  }
   if (P.vh) {
     P.off_vh = o; o = align_up(o + P.BH * P.n_pad * D * 2);
     P.off_vovf = o; o = align_up(o + P.BH * 2 * P.nchunks * 4);
@@ -290,7 +293,7 @@ int32_t run_pass1(const Plan &P, const rola_problem *p, const void *q, const voi
   a.ksc = (float *)(ws + P.off_ksc);
   a.vsc = (float *)(ws + P.off_vsc);
   a.kv8 = ws + P.off_kv8;
-  a.vh = vh ? (uint16_t *)(ws + P.off_vh) : nullptr;
+  a.vh = (vh || (quant && P.fp8)) ? (uint16_t *)(ws + P.off_vh) : nullptr;
   a.vovf = vh ? (int32_t *)(ws + P.off_vovf) : nullptr;
   if (!pool && !state)
     return timed("v_fp16", st, [&] { rola::launch_pass1(a, P.D, P.nchunks, (int)P.BH, false, false, false, st); });
@@ -346,6 +349,7 @@ int32_t run_quant8(const Plan &P, const rola_problem *p, const void *q, const vo
   a.ksc = (float *)(ws + P.off_ksc);
   a.vsc = (float *)(ws + P.off_vsc);
   a.kv8 = ws + P.off_kv8;
+  a.vh = (uint16_t *)(ws + P.off_vh);
   return timed(k8 ? "image8" : "quant8", st, [&] { rola::launch_quant8(a, P.D, (int)P.BH, st); });
 }
 
@@ -376,7 +380,7 @@ int32_t run_attn(const Plan &P, const rola_problem *p, const rola_config *c, con
   // pass 1 or the copy pass beforehand), the EXACT form for flagged heads
   const bool f16v = sparse && !P.fp8 && c->out_dtype == ROLA_OUT_BF16;
   if (f16v && !P.vh) return ROLA_ERR_INVALID_ARG;  // (the plan of the same config holds the copy)
-  a.vh = f16v ? (const uint16_t *)(ws + P.off_vh) : nullptr;
+  a.vh = (f16v || (sparse && P.fp8)) ? (const uint16_t *)(ws + P.off_vh) : nullptr;
   a.vovf = f16v ? (const int32_t *)(ws + P.off_vovf) : nullptr;
   a.nflags = 2 * P.nchunks;
   a.lse = (sparse && !lowrank) ? lse : nullptr;

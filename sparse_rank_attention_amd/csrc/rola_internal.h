@@ -65,13 +65,14 @@ struct Quant8Args {
   float *qsc;     // [BH][nb][2]: fl32(absmax/448), fl32(448/absmax) of Q
   float *ksc;     // [BH][nb]: fl32(absmax/448) of K
   float *vsc;     // [BH][nb]: fl32(absmax/448) of V
-  uint8_t *kv8;   // [BH][nb][128*D] tile images (K rows, then V^T rows)
+  uint8_t *kv8;   // [BH][nb][64*D] K tile images (e4m3 codes)
+  uint16_t *vh;   // [BH][n_pad][D] the V codes as fp16 values (exact), rows past N zero
 };
 
-// fp8 attention: ring depth (16 KB tiles at D=128), tiles per barrier and
+// fp8 attention: ring depth (24 KB tiles at D=128), tiles per barrier and
 // union-list entries staged in LDS
-constexpr int kAttn8S = 8;
-constexpr int kAttn8P = 4;
+constexpr int kAttn8S = 4;
+constexpr int kAttn8P = 2;
 constexpr int kAttn8Lmax = 1024;
 
 struct AttnArgs {

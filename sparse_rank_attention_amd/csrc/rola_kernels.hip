@@ -59,17 +59,15 @@ __global__ void k_setup(const float *__restrict__ wq, const float *__restrict__ 
 
 // ---------------------------------------------------------------- fp8 path
 
-// Tile image of one 64-token block (bytes; 128*D per block):
-//  K part, [64 keys][D]: dim d of a key sits at position
-//    p = 64*(d/64) + 32*((d%16)/8) + 8*((d%64)/16) + d%8,
-//  so that each MFMA lane half reads the 32 dims its Q operand holds (the
-//  bf16 Q registers, 16 dims per 16-dim step, 8 per lane half) as two
-//  contiguous 16-byte chunks; chunk c of key row r is stored at
-//  c ^ ((r / (256/D)) & (D/16 - 1)), conflict-free for 16-lane reads.
-//  V^T part, [D][64 keys]: key k sits at position 32*((k%8)/4) + e with
-//    e = 4*((k%32)/8) + k%4 (+16 for k >= 32),
-//  the order in which a lane half holds S^T accumulator rows (keys), so P^T
-//  needs no shuffles; chunk c of row d is stored at c ^ ((d/4) & 3).
+// K tile image of one 64-token block (bytes; 64*D per block), [64 keys][D]:
+// dim d of a key sits at position
+//   p = 64*(d/64) + 32*((d%16)/8) + 8*((d%64)/16) + d%8,
+// so that each MFMA lane half reads the 32 dims its Q operand holds (the
+// bf16 Q registers, 16 dims per 16-dim step, 8 per lane half) as two
+// contiguous 16-byte chunks; chunk c of key row r is stored at
+// c ^ ((r / (256/D)) & (D/16 - 1)), conflict-free for 16-lane reads.
+// The V codes go to their own [BH][n_pad][D] array as fp16 values, the
+// layout of the bf16 path's fp16 copy of V.
 template <int D>
 static __device__ __forceinline__ int img_k_off(int r, int d) {
   const int rem = d & 63;
@@ -77,13 +75,15 @@ static __device__ __forceinline__ int img_k_off(int r, int d) {
   const int f = (r / (256 / D)) & (D / 16 - 1);
   return r * D + ((((p >> 4) ^ f)) << 4) + (p & 15);
 }
-static __device__ __forceinline__ int img_v_pos(int k) {
-  const int g = (k & 7) >> 2;
-  const int e = 4 * ((k & 31) >> 3) + (k & 3) + (k >= 32 ? 16 : 0);
-  return 32 * g + e;
-}
-static __device__ __forceinline__ int img_v_off(int d, int p) {
-  return d * 64 + ((((p >> 4) ^ ((d >> 2) & 3))) << 4) + (p & 15);
+// Eight e4m3 codes (the bytes of w, low byte first) as eight fp16 values:
+// every e4m3 value is an fp16 value, so the conversion is exact.
+static __device__ __forceinline__ u32x4 e4m3x8_f16(uint2 w) {
+  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false), b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);
+  const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false), d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);
+  return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a[0], a[1])),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(b[0], b[1])),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(c[0], c[1])),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(d[0], d[1]))};
 }
 
 // ---------------------------------------------------------------- k_pass1
@@ -129,7 +129,6 @@ __global__ __launch_bounds__(QUANT ? 320 : 256, QUANT ? 1 : 2) void k_pass1(Pass
   constexpr int NSTAGE = 3;
   constexpr int VOPS = (32 * CH) / 64;  // DMA ops per lane per half tile
   __shared__ __attribute__((aligned(1024))) uint16_t vring[STATE ? 2 * NSTAGE * VT : 8];
-  __shared__ __attribute__((aligned(16))) uint8_t vimg8[QUANT ? 64 * D : 16];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
   const int bh = blockIdx.y;
@@ -168,8 +167,10 @@ __global__ __launch_bounds__(QUANT ? 320 : 256, QUANT ? 1 : 2) void k_pass1(Pass
   };
 
   if (QUANT && wave == 4) {
-    // ---- fp8 codes of V: scales, then V^T image part via an LDS transpose
+    // ---- fp8 codes of V: the block's scale, then its rows of codes as fp16
+    // values (rows past N zero)
     const uint16_t *X = args.v + base;
+    uint16_t *Y = args.vh + (int64_t)bh * args.nb * 64 * D;
     for (int i = 0; i < nblk; ++i) {
       const int c = c0 + i;
       const int valid = min(64, (int)(args.n_tokens - (int64_t)c * 64));
@@ -187,20 +188,11 @@ __global__ __launch_bounds__(QUANT ? 320 : 256, QUANT ? 1 : 2) void k_pass1(Pass
       const int64_t sidx = (int64_t)bh * args.nb + c;
       const float inv = m > 0.0f ? __fdiv_rn(448.0f, m) : 1.0f;
       if (lane == 0) args.vsc[sidx] = m > 0.0f ? __fdiv_rn(m, 448.0f) : 1.0f;
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // previous block's image read out
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const int t = TG * r + tg;
-        const uint2 code = e4m3x8(raw[r], inv);
-        const int pos = img_v_pos(t);
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          vimg8[img_v_off(8 * dl + e, pos)] = (uint8_t)(((e < 4 ? code.x : code.y) >> (8 * (e & 3))) & 0xffu);
+        *(u32x4 *)(Y + ((int64_t)c * 64 + t) * D + 8 * dl) = e4m3x8_f16(e4m3x8(raw[r], inv));
       }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // image complete before it is read back
-      u32x4 *dstv = (u32x4 *)(args.kv8 + sidx * (128 * D) + 64 * D);
-#pragma unroll
-      for (int o = 0; o < (64 * D) / (16 * 64); ++o) dstv[o * 64 + lane] = ((const u32x4 *)vimg8)[o * 64 + lane];
     }
     return;
   }
@@ -263,7 +255,7 @@ __global__ __launch_bounds__(QUANT ? 320 : 256, QUANT ? 1 : 2) void k_pass1(Pass
             }
           } else {
             if (lane == 0) args.ksc[sidx] = sc;
-            uint8_t *kimg = args.kv8 + sidx * (128 * D);
+            uint8_t *kimg = args.kv8 + sidx * (64 * D);
 #pragma unroll
             for (int r = 0; r < R; ++r)
               *(uint2 *)(kimg + img_k_off<D>(TG * r + tg, 8 * dl)) = e4m3x8(keep[r], inv);
@@ -1560,7 +1552,7 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn(AttnArgs args) {
 template <int D>
 __global__ __launch_bounds__(256) void k_quant8(Quant8Args a) {
   constexpr int PER = D / 4;
-  __shared__ __attribute__((aligned(16))) uint8_t img[128 * D];
+  __shared__ __attribute__((aligned(16))) uint8_t img[64 * D];
   __shared__ float red[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = blockIdx.x, bh = blockIdx.y;
@@ -1620,41 +1612,45 @@ __global__ __launch_bounds__(256) void k_quant8(Quant8Args a) {
       *(uint2 *)(img + img_k_off<D>(r, part * PER + i)) = make_uint2((uint32_t)w0, (uint32_t)w1);
     }
   }
-  // V: transposed, one byte per code
+  // V: the codes of row r as fp16 values (0 past N)
   load(a.v, x);
   {
     const float m = block_absmax(x);
     const float inv = m > 0.0f ? __fdiv_rn(448.0f, m) : 1.0f;
     if (tid == 0) a.vsc[sidx] = m > 0.0f ? __fdiv_rn(m, 448.0f) : 1.0f;
-    uint8_t *vimg = img + 64 * D;
-    const int p = img_v_pos(r);
+    uint16_t *vrow = a.vh + ((int64_t)bh * a.nb * 64 + (int64_t)c * 64 + r) * D + part * PER;
 #pragma unroll
-    for (int i = 0; i < PER; i += 2) {
-      const int w = cvt_fp8x2<false>(x[i] * inv, x[i + 1] * inv, 0);
-      vimg[img_v_off(part * PER + i, p)] = (uint8_t)(w & 0xff);
-      vimg[img_v_off(part * PER + i + 1, p)] = (uint8_t)((w >> 8) & 0xff);
+    for (int i = 0; i < PER; i += 8) {
+      int w0 = cvt_fp8x2<false>(x[i] * inv, x[i + 1] * inv, 0);
+      w0 = cvt_fp8x2<true>(x[i + 2] * inv, x[i + 3] * inv, w0);
+      int w1 = cvt_fp8x2<false>(x[i + 4] * inv, x[i + 5] * inv, 0);
+      w1 = cvt_fp8x2<true>(x[i + 6] * inv, x[i + 7] * inv, w1);
+      *(u32x4 *)(vrow + i) = e4m3x8_f16(make_uint2((uint32_t)w0, (uint32_t)w1));
     }
   }
   __syncthreads();
-  u32x4 *dst = (u32x4 *)(a.kv8 + sidx * (128 * D));
+  u32x4 *dst = (u32x4 *)(a.kv8 + sidx * (64 * D));
 #pragma unroll
-  for (int i = tid; i < 8 * D; i += 256) dst[i] = *(const u32x4 *)(img + 16 * i);
+  for (int i = tid; i < 4 * D; i += 256) dst[i] = *(const u32x4 *)(img + 16 * i);
 }
 
 // ------------------------------------------------------------------ k_attn8
-// The sparse branch with e4m3 operands on v_mfma_f32_32x32x64_f8f6f4: the
-// workgroup shape, group walk, LDS ring and lazy softmax reference follow
-// k_attn; a tile is the block's 128*D-byte image from k_quant8 (one
-// contiguous copy).  Each wave quantises its Q rows in registers with the
-// query block's inv scale.  Per listed key block j (constants staged in LDS
-// with the list):
+// The sparse branch with e4m3 operands: S^T = K Q^T on
+// v_mfma_f32_32x32x64_f8f6f4 (K codes from the block's K tile image, Q codes
+// quantised in registers with the query block's inv scale), and O^T = V^T P^T
+// on v_mfma_f32_32x32x16_f16 with fp16 weights against the V codes as fp16
+// values (exact).  The workgroup shape, group walk, LDS ring and lazy softmax
+// reference follow k_attn; a tile is the K image (64*D bytes, one contiguous
+// copy) and the 64 V code rows (64*D fp16, the V-style chunk swizzle).  Per
+// listed key block j (constants staged in LDS with the list):
 //   logits (base 2)  t = acc * (sq * sk_j * scale * log2 e) - m_ref,
 //   weights          P' = 2^(t + u_j) with u_j = 8 + log2(sv_j / sigma),
-// sigma the largest V scale on the group's list, so P' <= 2^8 stays inside
-// e4m3 range while P' * code_v carries the V scale (P' enters the PV product
-// as the sum of two e4m3 parts); the row sum adds 2^-u_j * sum(P').  m_ref is the integer ceiling of the running max (moved,
-// with an exact power-of-two rescale, whenever a tile max exceeds it).
-// Finally O = O' * sigma * 2^-8 / l.
+// sigma the largest V scale on the group's list, so P' * code_v carries the
+// V scale; m_ref is an integer that moves (with an exact power-of-two
+// rescale) only when a tile max exceeds it by more than 7, so P' < 2^15
+// stays inside fp16.  Each weight is rounded once to fp16 (toward zero) and
+// the row sum adds 2^-u_j times the same rounded weights.  Finally
+// O = O' * sigma * 2^-8 / l.
 template <int D, int G, int S, bool LOWRANK, bool ACCUM, bool OUTF32>
 __global__ __launch_bounds__(128 * G) void k_attn8(AttnArgs args) {
   constexpr int P = kAttn8P;  // tiles per barrier
@@ -1662,9 +1658,14 @@ __global__ __launch_bounds__(128 * G) void k_attn8(AttnArgs args) {
   constexpr int DT = D / 32;
   constexpr int K8 = D / 64;            // fp8 k-steps over head_dim
   constexpr int NT = 128 * G;
-  constexpr int TB = 128 * D;           // bytes per tile image
-  constexpr int OPS = TB / 16 / NT;     // DMA ops per thread per tile
-  static_assert(OPS >= 1 && (TB / 16) % NT == 0, "tile split");
+  constexpr int CH = D / 8;              // 16-byte chunks per V row
+  constexpr int KB = 64 * D;             // bytes of the K image
+  constexpr int TB = KB + 128 * D;       // bytes per tile: K image, then 64 V rows of fp16
+  constexpr int KC = KB / 16;             // 16-byte chunks of the K image
+  constexpr int VOPS = 64 * CH / NT;      // V row chunks per thread
+  constexpr int OPS = 1 + VOPS;           // DMA ops per thread per tile: one K chunk (thread t takes
+                                          // chunk t % KC, so every wave counts the same ops), VOPS V chunks
+  static_assert(VOPS >= 1 && (64 * CH) % NT == 0 && KC <= NT && NT % KC == 0, "tile split");
   static_assert(S >= 2 && S * OPS <= 63, "ring depth");
   constexpr int LMAX = kAttn8Lmax;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[S * TB];
@@ -1760,8 +1761,11 @@ __global__ __launch_bounds__(128 * G) void k_attn8(AttnArgs args) {
   for (int i = 0; i < DT; ++i) oacc[i] = f32x16{};
   float m_run = -INFINITY, l_run = 0.0f;
 
-  // per-lane LDS byte offsets of the MFMA operands inside a tile image
-  int koff[K8][2], voff[DT][2];
+  // per-lane LDS offsets of the MFMA operands inside a tile: K image bytes;
+  // V^T transposed-read rows 4g + (l%16)/4 (+16 per 16-key step, +8 for the
+  // second half), dims 32dt + 16((l/16)%2) + 4(l%4), in fp16 elements from
+  // the V part
+  int koff[K8][2], voff[DT];
 #pragma unroll
   for (int s8 = 0; s8 < K8; ++s8) {
     const int r = lane & 31;
@@ -1772,15 +1776,26 @@ __global__ __launch_bounds__(128 * G) void k_attn8(AttnArgs args) {
   }
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
-    const int d = 32 * dt + (lane & 31);
-    voff[dt][0] = 64 * D + d * 64 + (((2 * g) ^ ((d >> 2) & 3)) << 4);
-    voff[dt][1] = 64 * D + d * 64 + (((2 * g + 1) ^ ((d >> 2) & 3)) << 4);
+    const int i = lane & 15, dhalf = (lane >> 4) & 1;
+    const int dstart = 32 * dt + 16 * dhalf + 4 * (i & 3);
+    const int r0 = 4 * g + (i >> 2);
+    voff[dt] = r0 * D + (((dstart >> 3) ^ swz_v<D>(r0)) << 3) + (dstart & 7);
+  }
+  // this thread's source byte offsets: its K image chunk, and its V row chunks
+  // (row-major, V-style swizzle) inside a block
+  const uint32_t gk = (uint32_t)((tid % KC) * 16);
+  uint32_t gv[VOPS];
+#pragma unroll
+  for (int o = 0; o < VOPS; ++o) {
+    const int cidx = o * NT + tid, row = cidx / CH, pc = cidx % CH;
+    gv[o] = (uint32_t)((row * D + ((pc ^ swz_v<D>(row)) * 8)) * 2);
   }
   auto ld16 = [](const uint8_t *p) -> u32x4 { return *(const u32x4 *)p; };
   auto cat = [](u32x4 a, u32x4 b) -> i32x8 {
     return i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
   };
-  const uint8_t *img = args.kv8 + (int64_t)bh * args.nb * TB;
+  const uint8_t *img = args.kv8 + (int64_t)bh * args.nb * KB;
+  const uint16_t *vcodes = args.vh + (int64_t)bh * args.nb * 64 * D;
   const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_addr(ring));
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
 
@@ -1791,10 +1806,14 @@ __global__ __launch_bounds__(128 * G) void k_attn8(AttnArgs args) {
       if constexpr (FROM_LDS) j = slist[t] & 0xffff;
       else j = list[t] & 0xffff;
       j = __builtin_amdgcn_readfirstlane(j);
-      const uint8_t *src = img + (int64_t)j * TB;
-      const uint32_t m0 = ring_lds + (uint32_t)((t % S) * TB) + (uint32_t)wave_s * 1024u;
+      const uint32_t m0 = ring_lds + (uint32_t)((t % S) * TB);
+      // K image: chunk t % KC at its own position (waves past KC/64 repeat
+      // the first waves' chunks, the same bytes to the same place)
+      lds_dma16_m0(img + (int64_t)j * KB, gk, m0 + (uint32_t)(((wave_s * 64) % KC) * 16));
+      const uint16_t *vj = vcodes + (int64_t)j * 64 * D;
 #pragma unroll
-      for (int o = 0; o < OPS; ++o) lds_dma16_m0(src, (uint32_t)((o * NT + tid) * 16), m0 + (uint32_t)(o * NT * 16));
+      for (int o = 0; o < VOPS; ++o)
+        lds_dma16_m0(vj, gv[o], m0 + (uint32_t)KB + (uint32_t)((o * NT + wave_s * 64) * 16));
     };
     // P tiles per barrier in an S-slot ring (S/P groups of slots): group k
     // (tiles kP .. kP+P-1) is consumed while the next S/P-1 groups are in
@@ -1855,7 +1874,7 @@ __global__ __launch_bounds__(128 * G) void k_attn8(AttnArgs args) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx1 = fmaxf(mx1, sacc1[i]);
       const float mx = pair_max32(fmaxf(mx0, mx1)) * c;
-      const bool grow = mx > m_run;
+      const bool grow = mx > m_run + 7.0f;  // always true on the first tile (m_run = -inf)
       if (__builtin_amdgcn_ballot_w64(grow)) {
         const float m_new = grow ? ceilf(mx) : m_run;
         const float alpha = fast_exp2(m_run - m_new);
@@ -1864,34 +1883,34 @@ __global__ __launch_bounds__(128 * G) void k_attn8(AttnArgs args) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
       }
-      // P' in two e4m3 parts, hi = e4m3(P') and lo = e4m3(P' - hi): a single
-      // 3-bit-mantissa rounding of the weights would cost far more than the
-      // output tolerance; hi + lo keeps them to about 2^-8 relative.
+      // fp16 weights rounded toward zero (one packed conversion per pair),
+      // 16 keys per step, each step feeding DT PV MFMAs; the row sum, in four
+      // independent chains, adds the same rounded weights
       const float off = ku - m_run;
-      float psum = 0.0f;
-      i32x8 phi8, plo8;
+      const f16x2 ones = {(__fp16)1.0f, (__fp16)1.0f};
+      const uint16_t *sV = (const uint16_t *)(tile + KB);
+      float psum4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        const f32x16 &src = (w < 4) ? sacc0 : sacc1;
-        const int e = 4 * (w & 3);
-        const float p0 = fast_exp2(__builtin_fmaf(src[e], c, off));
-        const float p1 = fast_exp2(__builtin_fmaf(src[e + 1], c, off));
-        const float p2 = fast_exp2(__builtin_fmaf(src[e + 2], c, off));
-        const float p3 = fast_exp2(__builtin_fmaf(src[e + 3], c, off));
-        psum += (p0 + p1) + (p2 + p3);
-        const int hi = cvt_fp8x2<true>(p2, p3, cvt_fp8x2<false>(p0, p1, 0));
-        const f32x2 h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
-        const f32x2 h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
-        phi8[w] = hi;
-        plo8[w] = cvt_fp8x2<true>(p2 - h23[0], p3 - h23[1], cvt_fp8x2<false>(p0 - h01[0], p1 - h01[1], 0));
-      }
-      l_run = __builtin_fmaf(psum, kw, l_run);
+      for (int s = 0; s < 4; ++s) {
+        const f32x16 &src = (s < 2) ? sacc0 : sacc1;
+        f16x8 ph;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const i32x8 va = cat(ld16(tile + voff[dt][0]), ld16(tile + voff[dt][1]));
-        oacc[dt] = mfma_fp8(va, phi8, oacc[dt]);
-        oacc[dt] = mfma_fp8(va, plo8, oacc[dt]);
+        for (int e = 0; e < 4; ++e) {
+          const int i = 8 * (s & 1) + 2 * e;
+          const f16x2 pr = __builtin_amdgcn_cvt_pkrtz(fast_exp2(__builtin_fmaf(src[i], c, off)),
+                                                      fast_exp2(__builtin_fmaf(src[i + 1], c, off)));
+          ph[2 * e] = pr[0];
+          ph[2 * e + 1] = pr[1];
+          psum4[s] = __builtin_amdgcn_fdot2(pr, ones, psum4[s], false);
+        }
+        bf16x8 va[DT];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) va[dt] = vt_operand_at(sV + voff[dt] + s * 16 * D, 8 * D);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[dt] = mfma_f16(__builtin_bit_cast(f16x8, va[dt]), ph, oacc[dt]);
       }
+      l_run = __builtin_fmaf((psum4[0] + psum4[1]) + (psum4[2] + psum4[3]), kw, l_run);
       }
     }
   };
@@ -2101,7 +2120,7 @@ void launch_attn(const AttnArgs &a, int D, bool sparse, bool lowrank, bool accum
 template <int D>
 __global__ __launch_bounds__(256) void k_image8(Quant8Args a) {
   constexpr int PER = D / 4;
-  __shared__ __attribute__((aligned(16))) uint8_t img[128 * D];
+  __shared__ __attribute__((aligned(16))) uint8_t img[64 * D];
   const int tid = threadIdx.x;
   const int c = blockIdx.x, bh = blockIdx.y;
   const int b = bh / a.heads, h = bh % a.heads;
@@ -2123,20 +2142,17 @@ __global__ __launch_bounds__(256) void k_image8(Quant8Args a) {
     const uint2 w = valid ? *(const uint2 *)(a.k8 + roff + i) : make_uint2(0u, 0u);
     *(uint2 *)(img + img_k_off<D>(r, part * PER + i)) = w;
   }
-  // V: transposed, one byte per code
-  uint8_t *vimg = img + 64 * D;
-  const int p = img_v_pos(r);
+  // V: the codes of row r as fp16 values (0 past N)
+  uint16_t *vrow = a.vh + ((int64_t)bh * a.nb * 64 + (int64_t)c * 64 + r) * D + part * PER;
 #pragma unroll
   for (int i = 0; i < PER; i += 8) {
     const uint2 w = valid ? *(const uint2 *)(a.v8 + roff + i) : make_uint2(0u, 0u);
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      vimg[img_v_off(part * PER + i + e, p)] = (uint8_t)(((e < 4 ? w.x : w.y) >> (8 * (e & 3))) & 0xffu);
+    *(u32x4 *)(vrow + i) = e4m3x8_f16(w);
   }
   __syncthreads();
-  u32x4 *dst = (u32x4 *)(a.kv8 + sidx * (128 * D));
+  u32x4 *dst = (u32x4 *)(a.kv8 + sidx * (64 * D));
 #pragma unroll
-  for (int i = tid; i < 8 * D; i += 256) dst[i] = *(const u32x4 *)(img + 16 * i);
+  for (int i = tid; i < 4 * D; i += 256) dst[i] = *(const u32x4 *)(img + 16 * i);
 }
 
 void launch_quant8(const Quant8Args &a, int D, int bh, hipStream_t st) {

@@ -174,21 +174,23 @@ def test_timing_read_without_launches_is_empty():
 
 
 def test_plan_fp8_adds_code_images_to_workspace():
-    """fp8 mode keeps one 128*D-byte e4m3 tile image per (batch, head, block) plus three scales
-    (compared at fp32 output, where neither precision keeps an fp16 copy of V)."""
+    """fp8 mode keeps one 64*D-byte e4m3 K tile image and 64 rows of V codes as fp16 values
+    (128*D bytes) per (batch, head, block), plus three scales (compared at fp32 output, where
+    the bf16 path keeps no fp16 copy of V)."""
     prob = _prob(grid=(21, 45, 80))
     f32 = dict(topk=0.03, out_dtype=rola.ROLA_OUT_F32)
     st, b = _plan(prob, rola.Config(**f32))
     st8, f = _plan(prob, rola.Config(precision=rola.ROLA_PREC_FP8, **f32))
     assert st == st8 == 0
     bh_nb = prob.batch * prob.heads * f.nb
-    assert f.workspace_bytes - b.workspace_bytes >= bh_nb * (128 * prob.head_dim + 16)
-    assert f.workspace_bytes - b.workspace_bytes <= bh_nb * (128 * prob.head_dim + 16) + 4 * 256
+    assert f.workspace_bytes - b.workspace_bytes >= bh_nb * (192 * prob.head_dim + 16)
+    assert f.workspace_bytes - b.workspace_bytes <= bh_nb * (192 * prob.head_dim + 16) + 5 * 256
 
 
 def test_plan_bf16_output_adds_fp16_copy_of_v():
     """bf16 output with bf16 operands keeps an fp16 copy of V ([B*H][nb*64][D]) and two range
-    flags per (batch*head, pass-1 chunk); fp32 output and fp8 mode do not."""
+    flags per (batch*head, pass-1 chunk); fp32 output does not, and fp8 mode keeps its fp16 V
+    codes at either output type."""
     prob = _prob(grid=(21, 45, 80))
     st, a = _plan(prob, rola.Config(topk=0.03))
     st32, b = _plan(prob, rola.Config(topk=0.03, out_dtype=rola.ROLA_OUT_F32))
