@@ -103,10 +103,10 @@ static __device__ __forceinline__ u32x4 e4m3x8_f16(uint2 w) {
 //          blocks ahead), so it only waits for its own copies.  Per-wave
 //          partial sums go to the workspace for a fixed-order reduction.
 //   QUANT: (fp8 mode, with POOL) the pooling waves also take the block
-//          absmax of Q (its scales) and of K (scales and the K part of the
-//          block's e4m3 tile image), and a fifth wave reads V the same way
-//          and writes its scales and the V^T part of the image through an
-//          LDS transpose (see k_quant8 for the image layout and rounding).
+//          absmax of Q (its scales) and of K (scales and the block's e4m3 K
+//          tile image), and wave 0 then reads the block of V the same way
+//          and writes its scales and its codes as fp16 values (see k_quant8
+//          for the image layout and rounding).
 //   VH:    (bf16 output) the two pooling waves also read V, 32 tokens of
 //          each block each, and write its fp16 copy for the attention
 //          kernel's PV product, with a range flag per wave (some valid
@@ -121,7 +121,7 @@ static __device__ __forceinline__ u32x4 e4m3x8_f16(uint2 w) {
 static __host__ __device__ constexpr int blk_state_bytes(int D) { return D * 64 + 128; }
 
 template <int D, bool POOL, bool STATE, bool QUANT, bool BLK, bool VH = false>
-__global__ __launch_bounds__(QUANT ? 320 : 256, QUANT ? 1 : 2) void k_pass1(Pass1Args args) {
+__global__ __launch_bounds__(256, 2) void k_pass1(Pass1Args args) {
   constexpr int CH = D / 8;       // 16-byte chunks per token row
   constexpr int NS = D / 16;      // MFMA k-steps over head_dim
   constexpr int DT = D / 32;      // d-tiles of the state
@@ -166,36 +166,33 @@ __global__ __launch_bounds__(QUANT ? 320 : 256, QUANT ? 1 : 2) void k_pass1(Pass
     return make_uint2((uint32_t)w0, (uint32_t)w1);
   };
 
-  if (QUANT && wave == 4) {
-    // ---- fp8 codes of V: the block's scale, then its rows of codes as fp16
-    // values (rows past N zero)
+  // fp8 codes of V block c (wave 0 in fp8 mode, after the block's Q): the
+  // block's scale, then its rows of codes as fp16 values (rows past N zero)
+  auto quant_v = [&](int c) __attribute__((always_inline)) {
     const uint16_t *X = args.v + base;
     uint16_t *Y = args.vh + (int64_t)bh * args.nb * 64 * D;
-    for (int i = 0; i < nblk; ++i) {
-      const int c = c0 + i;
-      const int valid = min(64, (int)(args.n_tokens - (int64_t)c * 64));
-      u32x4 raw[R];
-      float m = 0.0f;
+    const int valid = min(64, (int)(args.n_tokens - (int64_t)c * 64));
+    u32x4 raw[R];
+    float m = 0.0f;
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int t = TG * r + tg;
-        raw[r] = t < valid ? *(const u32x4 *)(X + ((int64_t)c * 64 + t) * args.stride_n + 8 * dl)
-                           : u32x4{0u, 0u, 0u, 0u};
+    for (int r = 0; r < R; ++r) {
+      const int t = TG * r + tg;
+      raw[r] = t < valid ? *(const u32x4 *)(X + ((int64_t)c * 64 + t) * args.stride_n + 8 * dl)
+                         : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) m = fmaxf(m, fmaxf(fabsf(bflo(raw[r][e])), fabsf(bfhi(raw[r][e]))));
-      }
-      m = wave_absmax(m);
-      const int64_t sidx = (int64_t)bh * args.nb + c;
-      const float inv = m > 0.0f ? __fdiv_rn(448.0f, m) : 1.0f;
-      if (lane == 0) args.vsc[sidx] = m > 0.0f ? __fdiv_rn(m, 448.0f) : 1.0f;
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int t = TG * r + tg;
-        *(u32x4 *)(Y + ((int64_t)c * 64 + t) * D + 8 * dl) = e4m3x8_f16(e4m3x8(raw[r], inv));
-      }
+      for (int e = 0; e < 4; ++e) m = fmaxf(m, fmaxf(fabsf(bflo(raw[r][e])), fabsf(bfhi(raw[r][e]))));
     }
-    return;
-  }
+    m = wave_absmax(m);
+    const int64_t sidx = (int64_t)bh * args.nb + c;
+    const float inv = m > 0.0f ? __fdiv_rn(448.0f, m) : 1.0f;
+    if (lane == 0) args.vsc[sidx] = m > 0.0f ? __fdiv_rn(m, 448.0f) : 1.0f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int t = TG * r + tg;
+      *(u32x4 *)(Y + ((int64_t)c * 64 + t) * D + 8 * dl) = e4m3x8_f16(e4m3x8(raw[r], inv));
+    }
+  };
+
   if (wave < 2) {
     if (!POOL && !VH) return;
     // ---- pooling (wave 0: Q, wave 1: K) and, with VH, the fp16 copy of
@@ -299,6 +296,7 @@ __global__ __launch_bounds__(QUANT ? 320 : 256, QUANT ? 1 : 2) void k_pass1(Pass
           if (t < valid) *(u32x4 *)(YV + ((int64_t)c * 64 + t) * D + 8 * dl) = hv;
         }
       }
+      if (QUANT && wave == 0) quant_v(c);
     }
     // the range flag of this wave's half of the chunk
     if constexpr (VH) {
@@ -1982,12 +1980,12 @@ void launch_setup(const SetupArgs &a, hipStream_t st) {
 template <int D>
 static void pass1_d(const Pass1Args &a, int nchunks, int bh, bool pool, bool state, bool quant,
                     hipStream_t st) {
-  dim3 grid(nchunks, bh), block(256), block5(320);
+  dim3 grid(nchunks, bh), block(256);
   const bool blk = a.blk_state != nullptr;
   const bool vh = a.vh != nullptr && !quant;
   if (pool && state && quant) {
-    if (blk) hipLaunchKernelGGL((k_pass1<D, true, true, true, true>), grid, block5, 0, st, a);
-    else hipLaunchKernelGGL((k_pass1<D, true, true, true, false>), grid, block5, 0, st, a);
+    if (blk) hipLaunchKernelGGL((k_pass1<D, true, true, true, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_pass1<D, true, true, true, false>), grid, block, 0, st, a);
   } else if (pool && state && vh) {
     if (blk) hipLaunchKernelGGL((k_pass1<D, true, true, false, true, true>), grid, block, 0, st, a);
     else hipLaunchKernelGGL((k_pass1<D, true, true, false, false, true>), grid, block, 0, st, a);
