@@ -1667,7 +1667,7 @@ __global__ __launch_bounds__(128 * G) void k_attn8(AttnArgs args) {
   static_assert(S >= 2 && S * OPS <= 63, "ring depth");
   constexpr int LMAX = kAttn8Lmax;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[S * TB];
-  __shared__ int32_t slist[LMAX];
+  __shared__ int32_t slist[LMAX + 8];  // + room for the reads ahead past the end
   __shared__ float sck[LMAX], sku[LMAX], skw[LMAX];
   __shared__ float sred[2 * G];
   __shared__ __attribute__((aligned(16))) float sfreq[D / 2];  // rotary inverse frequency per pair
@@ -1799,10 +1799,11 @@ __global__ __launch_bounds__(128 * G) void k_attn8(AttnArgs args) {
 
   auto main_loop = [&](auto lds_tag) {
     constexpr bool FROM_LDS = decltype(lds_tag)::value;
-    auto issue = [&](int t) {
-      int j;
-      if constexpr (FROM_LDS) j = slist[t] & 0xffff;
-      else j = list[t] & 0xffff;
+    auto entry = [&](int t) __attribute__((always_inline)) -> int {
+      if constexpr (FROM_LDS) return slist[t];
+      else return list[t];
+    };
+    auto issue_j = [&](int t, int j) {
       j = __builtin_amdgcn_readfirstlane(j);
       const uint32_t m0 = ring_lds + (uint32_t)((t % S) * TB);
       // K image: chunk t % KC at its own position (waves past KC/64 repeat
@@ -1813,6 +1814,7 @@ __global__ __launch_bounds__(128 * G) void k_attn8(AttnArgs args) {
       for (int o = 0; o < VOPS; ++o)
         lds_dma16_m0(vj, gv[o], m0 + (uint32_t)KB + (uint32_t)((o * NT + wave_s * 64) * 16));
     };
+    auto issue = [&](int t) { issue_j(t, entry(t) & 0xffff); };
     // P tiles per barrier in an S-slot ring (S/P groups of slots): group k
     // (tiles kP .. kP+P-1) is consumed while the next S/P-1 groups are in
     // flight; group k+S/P-1 is copied into the slots of group k-1 right after
@@ -1821,26 +1823,8 @@ __global__ __launch_bounds__(128 * G) void k_attn8(AttnArgs args) {
     static_assert(S % P == 0 && NGR >= 2, "ring of whole groups");
     for (int t = 0; t < (NGR - 1) * P; ++t)
       if (t < U) issue(t);
-    auto entry = [&](int t) __attribute__((always_inline)) -> int {
-      if constexpr (FROM_LDS) return slist[t];
-      else return list[t];
-    };
-    for (int t2 = 0; t2 < U; t2 += P) {
-      // tiles t2 .. t2+P-1 complete; the tiles copied after them (up to
-      // t2 + (NGR-1)*P - 1) may be in flight
-      wait_tiles<OPS, (NGR - 2) * P>(min((NGR - 2) * P, U - (t2 + P)));
-      barrier_lds();
-      uint32_t mm = 0;  // this wave's membership over the group
-#pragma unroll
-      for (int u = 0; u < P; ++u)
-        if (t2 + u < U && active && ((entry(t2 + u) >> (16 + member)) & 1)) mm |= 1u << u;
-      const int tn = t2 + (NGR - 1) * P;  // first tile of the group to copy now
-      for (int u = 0; u < P; ++u)
-        if (tn + u < U) issue(tn + u);
-      if (!mm) continue;
-      for (int t = t2; t < min(t2 + P, U); ++t) {
-      if (!((mm >> (t - t2)) & 1)) continue;
-      const int ent = entry(t);
+    // one listed tile t (list entry ent) for this wave's 32 query rows
+    auto walk_tile = [&](int t, int ent) __attribute__((always_inline)) {
       float ck, ku, kw;
       if constexpr (FROM_LDS) {
         ck = sck[t]; ku = sku[t]; kw = skw[t];
@@ -1866,12 +1850,16 @@ __global__ __launch_bounds__(128 * G) void k_attn8(AttnArgs args) {
         }
       }
       const float c = sq * ck;
-      float mx0 = -INFINITY, mx1 = -INFINITY;
+      // the tile max in four independent chains
+      float mx0 = -INFINITY, mx1 = -INFINITY, mx2 = -INFINITY, mx3 = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx0 = fmaxf(mx0, sacc0[i]);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx1 = fmaxf(mx1, sacc1[i]);
-      const float mx = pair_max32(fmaxf(mx0, mx1)) * c;
+      for (int i = 0; i < 8; ++i) {
+        mx0 = fmaxf(mx0, sacc0[i]);
+        mx1 = fmaxf(mx1, sacc1[i]);
+        mx2 = fmaxf(mx2, sacc0[8 + i]);
+        mx3 = fmaxf(mx3, sacc1[8 + i]);
+      }
+      const float mx = pair_max32(fmaxf(fmaxf(mx0, mx1), fmaxf(mx2, mx3))) * c;
       const bool grow = mx > m_run + 7.0f;  // always true on the first tile (m_run = -inf)
       if (__builtin_amdgcn_ballot_w64(grow)) {
         const float m_new = grow ? ceilf(mx) : m_run;
@@ -1909,7 +1897,44 @@ __global__ __launch_bounds__(128 * G) void k_attn8(AttnArgs args) {
         for (int dt = 0; dt < DT; ++dt) oacc[dt] = mfma_f16(__builtin_bit_cast(f16x8, va[dt]), ph, oacc[dt]);
       }
       l_run = __builtin_fmaf((psum4[0] + psum4[1]) + (psum4[2] + psum4[3]), kw, l_run);
+    };
+    if constexpr (FROM_LDS && P == 2 && NGR == 2) {
+      // the list entries of tiles t2 .. t2+3, read one iteration ahead so
+      // that no LDS read stands between the barrier and the copies (entries
+      // past U are never used)
+      int ea = slist[0], eb = slist[1], ec = slist[2], ed = slist[3];
+      for (int t2 = 0; t2 < U; t2 += 2) {
+        wait_vmcnt<0>();  // this wave's copies of tiles t2, t2+1
+        barrier_lds();    // both visible to all waves; every wave is done with t2-2, t2-1
+        const int e0 = ea, e1 = eb;
+        if (t2 + 2 < U) issue_j(t2 + 2, ec & 0xffff);
+        if (t2 + 3 < U) issue_j(t2 + 3, ed & 0xffff);
+        ea = ec;
+        eb = ed;
+        ec = slist[t2 + 4];
+        ed = slist[t2 + 5];
+        if (active && ((e0 >> (16 + member)) & 1)) walk_tile(t2, e0);
+        if (active && t2 + 1 < U && ((e1 >> (16 + member)) & 1)) walk_tile(t2 + 1, e1);
       }
+    } else {
+    for (int t2 = 0; t2 < U; t2 += P) {
+      // tiles t2 .. t2+P-1 complete; the tiles copied after them (up to
+      // t2 + (NGR-1)*P - 1) may be in flight
+      wait_tiles<OPS, (NGR - 2) * P>(min((NGR - 2) * P, U - (t2 + P)));
+      barrier_lds();
+      uint32_t mm = 0;  // this wave's membership over the group
+#pragma unroll
+      for (int u = 0; u < P; ++u)
+        if (t2 + u < U && active && ((entry(t2 + u) >> (16 + member)) & 1)) mm |= 1u << u;
+      const int tn = t2 + (NGR - 1) * P;  // first tile of the group to copy now
+      for (int u = 0; u < P; ++u)
+        if (tn + u < U) issue(tn + u);
+      if (!mm) continue;
+      for (int t = t2; t < min(t2 + P, U); ++t) {
+      if (!((mm >> (t - t2)) & 1)) continue;
+      walk_tile(t, entry(t));
+      }
+    }
     }
   };
   if (U <= LMAX) main_loop(std::integral_constant<bool, true>{});
