@@ -2142,16 +2142,13 @@ void launch_attn(const AttnArgs &a, int D, bool sparse, bool lowrank, bool accum
 // Same grid and thread mapping as k_quant8.
 template <int D>
 __global__ __launch_bounds__(256) void k_image8(Quant8Args a) {
-  constexpr int PER = D / 4;
+  constexpr int C8 = D / 8;             // 8-code chunks per row
+  constexpr int IT = 64 * C8 / 256;     // chunks per thread and tensor
   __shared__ __attribute__((aligned(16))) uint8_t img[64 * D];
   const int tid = threadIdx.x;
   const int c = blockIdx.x, bh = blockIdx.y;
   const int b = bh / a.heads, h = bh % a.heads;
   const int64_t base = (int64_t)b * a.stride_b + (int64_t)h * a.stride_h;
-  const int r = tid >> 2, part = tid & 3;
-  const int64_t n = (int64_t)c * 64 + r;
-  const bool valid = n < a.n_tokens;
-  const int64_t roff = base + (valid ? n : 0) * a.stride_n + part * PER;
   const int64_t sidx = (int64_t)bh * a.nb + c;
   if (tid == 0) {
     a.qsc[2 * sidx] = a.qs_in[sidx];
@@ -2159,18 +2156,30 @@ __global__ __launch_bounds__(256) void k_image8(Quant8Args a) {
     a.ksc[sidx] = a.ks_in[sidx];
     a.vsc[sidx] = a.vs_in[sidx];
   }
+  // chunk i = it*256 + tid is codes 8*(i % C8) .. +7 of row i / C8, so that
+  // neighbouring lanes read and write neighbouring 8-code chunks of a row
+  uint2 kw[IT], vw[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int i = it * 256 + tid, r = i / C8, d0 = 8 * (i % C8);
+    const int64_t n = (int64_t)c * 64 + r;
+    const bool valid = n < a.n_tokens;
+    const int64_t off = base + (valid ? n : 0) * a.stride_n + d0;
+    kw[it] = valid ? *(const uint2 *)(a.k8 + off) : make_uint2(0u, 0u);
+    vw[it] = valid ? *(const uint2 *)(a.v8 + off) : make_uint2(0u, 0u);
+  }
   // K: 8 consecutive dims are 8 consecutive image bytes
 #pragma unroll
-  for (int i = 0; i < PER; i += 8) {
-    const uint2 w = valid ? *(const uint2 *)(a.k8 + roff + i) : make_uint2(0u, 0u);
-    *(uint2 *)(img + img_k_off<D>(r, part * PER + i)) = w;
+  for (int it = 0; it < IT; ++it) {
+    const int i = it * 256 + tid;
+    *(uint2 *)(img + img_k_off<D>(i / C8, 8 * (i % C8))) = kw[it];
   }
-  // V: the codes of row r as fp16 values (0 past N)
-  uint16_t *vrow = a.vh + ((int64_t)bh * a.nb * 64 + (int64_t)c * 64 + r) * D + part * PER;
+  // V: the codes of each row as fp16 values (0 past N)
+  uint16_t *vblk = a.vh + ((int64_t)bh * a.nb * 64 + (int64_t)c * 64) * D;
 #pragma unroll
-  for (int i = 0; i < PER; i += 8) {
-    const uint2 w = valid ? *(const uint2 *)(a.v8 + roff + i) : make_uint2(0u, 0u);
-    *(u32x4 *)(vrow + i) = e4m3x8_f16(w);
+  for (int it = 0; it < IT; ++it) {
+    const int i = it * 256 + tid;
+    *(u32x4 *)(vblk + (i / C8) * D + 8 * (i % C8)) = e4m3x8_f16(vw[it]);
   }
   __syncthreads();
   u32x4 *dst = (u32x4 *)(a.kv8 + sidx * (64 * D));
