@@ -238,24 +238,46 @@ def backward_bench(args, w, rola, torch, np, W, qd, kd, vd, wqd, wkd, gd, stream
     rola.rola_forward(qd, kd, vd, wqd, wkd, w.grid, cfg, block_idx_out=bmap, stream=stream, gate=gd)
     print("[bench] generating dL/dO", file=sys.stderr, flush=True)
     dod = torch.from_numpy(W.make_dout(w).view(np.int16)).view(torch.bfloat16).cuda()
-    rola.timing_enable(True)
+    def timed_steps(fn, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    bwd = lambda: rola.rola_backward(qd, kd, vd, wqd, wkd, w.grid, cfg, bmap, dod, gate=gd, stream=stream)
     for _ in range(args.warmup):
-        rola.rola_backward(qd, kd, vd, wqd, wkd, w.grid, cfg, bmap, dod, gate=gd, stream=stream)
+        bwd()
     torch.cuda.synchronize()
-    rola.timing_enable(False)
-    rola.timing_read()
     print("[bench] timing %d backward steps" % args.steps, file=sys.stderr, flush=True)
+    ms = timed_steps(bwd, args.steps)  # no per-kernel events inside the headline
+    # per-kernel times from a second pass with events around every kernel
+    rola.timing_read()
     rola.timing_enable(True)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(args.steps):
-        rola.rola_backward(qd, kd, vd, wqd, wkd, w.grid, cfg, bmap, dod, gate=gd, stream=stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
+    ms_events = timed_steps(bwd, args.steps)
     rola.timing_enable(False)
-    ms = e0.elapsed_time(e1) / args.steps
     kern_ms = {name: tot / n for name, (n, tot) in rola.timing_read().items()}
+    # the training pair: the forward that keeps O_s and the log-sum-exp, and
+    # the backward that takes them, against rola_forward + rola_backward
+    print("[bench] timing the training pair", file=sys.stderr, flush=True)
+    fwd = lambda: rola.rola_forward(qd, kd, vd, wqd, wkd, w.grid, cfg, block_idx_out=bmap, stream=stream, gate=gd)
+    saved = {}
+    ftrain = lambda: saved.__setitem__("t", rola.rola_forward_train(qd, kd, vd, wqd, wkd, w.grid, cfg,
+                                                                    block_idx_out=bmap, stream=stream, gate=gd))
+    ftrain()
+    _, os_, lse = saved["t"]
+    bsaved = lambda: rola.rola_backward(qd, kd, vd, wqd, wkd, w.grid, cfg, bmap, dod, gate=gd, stream=stream,
+                                        saved=(os_, lse))
+    for _ in range(max(1, args.warmup)):
+        fwd(); ftrain(); bsaved()
+    pair = {"fwd_ms": timed_steps(fwd, args.steps), "fwd_train_ms": timed_steps(ftrain, args.steps),
+            "bwd_ms": ms, "bwd_saved_ms": timed_steps(bsaved, args.steps)}
+    pair = {k_: round(v_, 4) for k_, v_ in pair.items()}
+    pair["step_ms_recompute"] = round(pair["fwd_ms"] + pair["bwd_ms"], 4)
+    pair["step_ms_saved"] = round(pair["fwd_train_ms"] + pair["bwd_saved_ms"], 4)
     pairs = w.nb * kb * B * H
     unit = 2.0 * 64 * 64 * w.head_dim  # one 64x64xD product
     total = 5 * unit * pairs            # S, dP, dV, dQ, dK per kept block pair
@@ -272,6 +294,9 @@ def backward_bench(args, w, rola, torch, np, W, qd, kd, vd, wqd, wkd, gd, stream
                    "lowrank_scope": "complement" if args.complement else "global"},
         "bwd_ms": round(ms, 4),
         "kernel_ms": {k_: round(v_, 4) for k_, v_ in sorted(kern_ms.items())},
+        "kernel_ms_pass": {"steps": args.steps, "bwd_ms": round(ms_events, 4),
+                           "how": "second pass with HIP events around every kernel; the headline ms has none"},
+        "training_pair": pair,
         "cpu_baseline": None,
     }
     # the two sparse kernels against the bf16 MFMA peak, on their algorithmic

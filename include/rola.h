@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define ROLA_ABI_VERSION 7
+#define ROLA_ABI_VERSION 8
 #define ROLA_BLOCK 64
 #define ROLA_MAX_BLOCKS 4096 /* nb limit: N <= 262144 tokens */
 
@@ -231,6 +231,38 @@ int32_t rola_backward(const rola_problem *prob, const rola_config *cfg, const vo
                       const int32_t *block_idx, const void *dout, void *dq, void *dk, void *dv,
                       float *dwq, float *dwk, float *dgate, void *workspace, size_t workspace_bytes,
                       void *stream);
+
+/*
+ * Training pair (same passages as rola_backward): a forward that keeps what
+ * the backward would otherwise recompute, and the backward that takes it.
+ *
+ * rola_forward_train: rola_forward (bf16 precision only; ROLA_ERR_UNSUPPORTED
+ * for fp8), and also writes, from the same attention launch,
+ *   os:  fp32, the sparse branch's output O_s before the low-rank term is
+ *        added, with the element strides of prob (rows >= N written as 0),
+ *        16-byte aligned, caller-owned;
+ *   lse: fp32 [B*H][n_pad], each valid row's base-2 log-sum-exp of its scaled
+ *        logits (s * scale * log2 e), 4-byte aligned, caller-owned; rows >= N
+ *        are not written.
+ * With bf16 output both come from the fp16-weight form of the forward (its
+ * rounding, not the backward's fp32 recompute); with fp32 output they equal
+ * what rola_backward recomputes, bit for bit.  Workspace as for rola_forward.
+ *
+ * rola_backward_saved: rola_backward with os and lse from rola_forward_train
+ * on the same inputs, block map and config (both required: NULL is
+ * ROLA_ERR_INVALID_ARG); it skips the recompute of the sparse branch and
+ * forms only the group schedule of the map.  Workspace as for rola_backward.
+ */
+int32_t rola_forward_train(const rola_problem *prob, const rola_config *cfg, const void *q,
+                           const void *k, const void *v, const float *wq, const float *wk,
+                           const float *gate, int32_t *block_idx_out, void *out, float *os, float *lse,
+                           void *workspace, size_t workspace_bytes, void *stream);
+int32_t rola_backward_saved(const rola_problem *prob, const rola_config *cfg, const void *q,
+                            const void *k, const void *v, const float *wq, const float *wk,
+                            const float *gate, const int32_t *block_idx, const void *dout,
+                            const float *os, const float *lse, void *dq, void *dk, void *dv, float *dwq,
+                            float *dwk, float *dgate, void *workspace, size_t workspace_bytes,
+                            void *stream);
 
 /*
  * Optional kernel timing for measurement.  While enabled, each call records a

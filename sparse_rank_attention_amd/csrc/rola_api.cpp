@@ -353,10 +353,19 @@ int32_t run_quant8(const Plan &P, const rola_problem *p, const void *q, const vo
   return timed(k8 ? "image8" : "quant8", st, [&] { rola::launch_quant8(a, P.D, (int)P.BH, st); });
 }
 
+// the group schedule of a block map alone (what run_attn forms first)
+int32_t run_schedule(const Plan &P, const int32_t *map, uint8_t *ws, hipStream_t st) {
+  return timed("schedule", st, [&] {
+    rola::launch_schedule(map, P.nb, P.kb, P.G, (int)P.ngroups, (int)P.list_stride, (int)P.BH,
+                          (int32_t *)(ws + P.off_ugroup), (int32_t *)(ws + P.off_ucount),
+                          (int32_t *)(ws + P.off_ulist), st);
+  });
+}
+
 int32_t run_attn(const Plan &P, const rola_problem *p, const rola_config *c, const void *q,
                  const void *k, const void *v, const int32_t *map, const float *gate, void *out,
                  uint8_t *ws, bool sparse, bool lowrank, bool accum, hipStream_t st,
-                 float *lse = nullptr, const uint8_t *q8 = nullptr) {
+                 float *lse = nullptr, const uint8_t *q8 = nullptr, float *os_save = nullptr) {
   rola::AttnArgs a;
   a.q8 = q8;
   a.q = (const uint16_t *)q; a.k = (const uint16_t *)k; a.v = (const uint16_t *)v;
@@ -383,7 +392,10 @@ int32_t run_attn(const Plan &P, const rola_problem *p, const rola_config *c, con
   a.vh = (f16v || (sparse && P.fp8)) ? (const uint16_t *)(ws + P.off_vh) : nullptr;
   a.vovf = f16v ? (const int32_t *)(ws + P.off_vovf) : nullptr;
   a.nflags = 2 * P.nchunks;
-  a.lse = (sparse && !lowrank) ? lse : nullptr;
+  // the log-sum-exp: the backward's recompute (sparse alone) or a training
+  // forward (fused, which also keeps O_s)
+  a.lse = sparse ? lse : nullptr;
+  a.os_save = (sparse && lowrank) ? os_save : nullptr;
   a.rope = rope_args(P, ws);
   a.kv8 = ws + P.off_kv8;
   a.qsc = (const float *)(ws + P.off_qsc);
@@ -567,6 +579,31 @@ int32_t rola_forward(const rola_problem *prob, const rola_config *cfg, const voi
   return run_attn(P, prob, cfg, q, k, v, map, gate, out, ws, true, true, false, st);
 }
 
+int32_t rola_forward_train(const rola_problem *prob, const rola_config *cfg, const void *q,
+                           const void *k, const void *v, const float *wq, const float *wk,
+                           const float *gate, int32_t *block_idx_out, void *out, float *os, float *lse,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+  Plan P;
+  ROLA_TRY(make_plan(prob, cfg, &P));
+  if (P.fp8) return ROLA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !wq || !wk || !out || !os || !lse) return ROLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(os) ||
+      (block_idx_out && !aligned16(block_idx_out)))
+    return ROLA_ERR_ALIGNMENT;
+  if (((uintptr_t)wq & 3u) || ((uintptr_t)wk & 3u) || ((uintptr_t)lse & 3u)) return ROLA_ERR_ALIGNMENT;
+  if (gate && !aligned16(gate)) return ROLA_ERR_ALIGNMENT;
+  if (!workspace || (int64_t)workspace_bytes < P.total) return ROLA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return ROLA_ERR_ALIGNMENT;
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t *ws = (uint8_t *)workspace;
+  int32_t *map = block_idx_out ? block_idx_out : (int32_t *)(ws + P.off_map);
+  ROLA_TRY(run_setup(P, wq, wk, ws, st));
+  ROLA_TRY(run_pass1(P, prob, q, k, v, ws, true, true, st, false, P.vh));
+  ROLA_TRY(run_reduce(P, ws, st));
+  ROLA_TRY(run_select(P, ws, (float *)(ws + P.off_scores), map, st));
+  return run_attn(P, prob, cfg, q, k, v, map, gate, out, ws, true, true, false, st, lse, nullptr, os);
+}
+
 int32_t rola_forward_e4m3(const rola_problem *prob, const rola_config *cfg, const void *q,
                           const void *k, const void *v, const uint8_t *q8, const uint8_t *k8,
                           const uint8_t *v8, const float *qs, const float *ks, const float *vs,
@@ -599,16 +636,21 @@ int32_t rola_forward_e4m3(const rola_problem *prob, const rola_config *cfg, cons
   return run_attn(P, prob, cfg, q, k, v, map, gate, out, ws, true, true, false, st, nullptr, q8);
 }
 
-int32_t rola_backward(const rola_problem *prob, const rola_config *cfg, const void *q, const void *k,
-                      const void *v, const float *wq, const float *wk, const float *gate,
-                      const int32_t *block_idx, const void *dout, void *dq, void *dk, void *dv,
-                      float *dwq, float *dwk, float *dgate, void *workspace, size_t workspace_bytes,
-                      void *stream) {
+// os, lse: the training forward's O_s and log-sum-exp (both set), or NULL:
+// recompute them here
+static int32_t backward_impl(const rola_problem *prob, const rola_config *cfg, const void *q,
+                             const void *k, const void *v, const float *wq, const float *wk,
+                             const float *gate, const int32_t *block_idx, const void *dout,
+                             const float *os, const float *lse, void *dq, void *dk, void *dv, float *dwq,
+                             float *dwk, float *dgate, void *workspace, size_t workspace_bytes,
+                             void *stream) {
   Plan P;
   ROLA_TRY(make_plan(prob, cfg, &P));
   if (P.fp8) return ROLA_ERR_UNSUPPORTED;
   if (!q || !k || !v || !wq || !wk || !block_idx || !dout || !dq || !dk || !dv || !dwq || !dwk)
     return ROLA_ERR_INVALID_ARG;
+  if ((os != nullptr) != (lse != nullptr)) return ROLA_ERR_INVALID_ARG;
+  if ((os && !aligned16(os)) || ((uintptr_t)lse & 3u)) return ROLA_ERR_ALIGNMENT;
   if ((gate != nullptr) != (dgate != nullptr)) return ROLA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(dq) ||
       !aligned16(dk) || !aligned16(dv) || !aligned16(block_idx) || (gate && !aligned16(gate)))
@@ -635,12 +677,18 @@ int32_t rola_backward(const rola_problem *prob, const rola_config *cfg, const vo
                                 (float *)(ws + P.b_s32), st);
     }));
   }
-  // the sparse branch alone again with fp32 weights: O_s (fp32, the
-  // problem's strides) and each row's log-sum-exp
-  rola_config c32 = *cfg;
-  c32.out_dtype = ROLA_OUT_F32;
-  ROLA_TRY(run_attn(P, prob, &c32, q, k, v, block_idx, nullptr, ws + P.b_os, ws, true, false, false, st,
-                    (float *)(ws + P.b_lse)));
+  if (os) {
+    // O_s and the log-sum-exp from the training forward: only the group
+    // schedule of the map is formed again
+    ROLA_TRY(run_schedule(P, block_idx, ws, st));
+  } else {
+    // the sparse branch alone again with fp32 weights: O_s (fp32, the
+    // problem's strides) and each row's log-sum-exp
+    rola_config c32 = *cfg;
+    c32.out_dtype = ROLA_OUT_F32;
+    ROLA_TRY(run_attn(P, prob, &c32, q, k, v, block_idx, nullptr, ws + P.b_os, ws, true, false, false, st,
+                      (float *)(ws + P.b_lse)));
+  }
   if (P.comp) {
     // per query block: the complement state S_i, z_i (as the forward's) and
     // S_i as the hi + lo operand of the backward, on the schedule the
@@ -682,7 +730,7 @@ int32_t rola_backward(const rola_problem *prob, const rola_config *cfg, const vo
   a.wqT = (const uint16_t *)(ws + P.off_wqT); a.wkT = (const uint16_t *)(ws + P.off_wkT);
   a.st = (const uint16_t *)(ws + P.off_st);
   a.s32 = (const float *)(ws + (P.comp ? P.off_s32 : P.b_s32)); a.z = (const float *)(ws + P.off_z);
-  a.os = (const float *)(ws + P.b_os); a.lse = (const float *)(ws + P.b_lse);
+  a.os = os ? os : (const float *)(ws + P.b_os); a.lse = lse ? lse : (const float *)(ws + P.b_lse);
   a.wqP = (uint16_t *)(ws + P.b_wqP); a.wkP = (uint16_t *)(ws + P.b_wkP);
   a.sd = (uint16_t *)(ws + P.b_sd); a.dsr = (uint16_t *)(ws + P.b_dsr); a.dst = (uint16_t *)(ws + P.b_dst);
   a.ds32 = (float *)(ws + P.b_ds32); a.dz = (float *)(ws + P.b_dz);
@@ -727,6 +775,26 @@ int32_t rola_backward(const rola_problem *prob, const rola_config *cfg, const vo
   ROLA_TRY(timed("bwd_dq", st, [&] { rola::launch_bwd_dq(a, D, st); }));
   if (!P.comp) ROLA_TRY(timed("bwd_tmap", st, [&] { rola::launch_bwd_tmap(a, st); }));
   return timed("bwd_dkv", st, [&] { rola::launch_bwd_dkv(a, D, st); });
+}
+
+int32_t rola_backward(const rola_problem *prob, const rola_config *cfg, const void *q, const void *k,
+                      const void *v, const float *wq, const float *wk, const float *gate,
+                      const int32_t *block_idx, const void *dout, void *dq, void *dk, void *dv,
+                      float *dwq, float *dwk, float *dgate, void *workspace, size_t workspace_bytes,
+                      void *stream) {
+  return backward_impl(prob, cfg, q, k, v, wq, wk, gate, block_idx, dout, nullptr, nullptr, dq, dk, dv, dwq,
+                       dwk, dgate, workspace, workspace_bytes, stream);
+}
+
+int32_t rola_backward_saved(const rola_problem *prob, const rola_config *cfg, const void *q,
+                            const void *k, const void *v, const float *wq, const float *wk,
+                            const float *gate, const int32_t *block_idx, const void *dout,
+                            const float *os, const float *lse, void *dq, void *dk, void *dv, float *dwq,
+                            float *dwk, float *dgate, void *workspace, size_t workspace_bytes,
+                            void *stream) {
+  if (!os || !lse) return ROLA_ERR_INVALID_ARG;
+  return backward_impl(prob, cfg, q, k, v, wq, wk, gate, block_idx, dout, os, lse, dq, dk, dv, dwq, dwk,
+                       dgate, workspace, workspace_bytes, stream);
 }
 
 int32_t rola_quant_rows(const void *x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t *codes,

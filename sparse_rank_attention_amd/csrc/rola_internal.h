@@ -97,9 +97,11 @@ struct AttnArgs {
   int nflags;
   const float *gate;    // fp32 [D+1] output gate (w, then b) on the low-rank term; NULL: none
   int complement;       // st and z hold one state per query block ([BH][nb][D][32], [BH][nb][32])
-  float *lse;           // sparse branch alone with fp32 output: if set, the backward's
-                        // recompute -- fp32 weights, and the base-2 log-sum-exp of each
-                        // row's scaled logits (s * scale * log2 e), [BH][n_pad]
+  float *lse;           // if set, the base-2 log-sum-exp of each row's scaled logits
+                        // (s * scale * log2 e), [BH][n_pad]: the backward's recompute (the
+                        // sparse branch alone, fp32 weights) or the training forward
+  float *os_save;       // training forward (fused, bf16 operands): if set, the sparse
+                        // branch's output O_s, fp32 with the problem's strides (rows >= N 0)
   RopeArgsHost rope;
   // fp8 sparse branch only
   const uint8_t *kv8;   // tile images, see Quant8Args

@@ -1511,9 +1511,25 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn(AttnArgs args) {
     const float inv_l = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) oacc[dt] *= inv_l;
-    // the sparse branch alone can leave each row's log-sum-exp for the backward
-    if (!LOWRANK && args.lse && active && lane < 32 && n < args.n_tokens)
+    // each row's log-sum-exp for the backward: from its recompute (the sparse
+    // branch alone) or from a training forward
+    if (args.lse && active && lane < 32 && n < args.n_tokens)
       args.lse[(int64_t)bh * args.nb * 64 + n] = m_run + log2f(l_tot);
+    // a training forward also keeps O_s (fp32, the problem's strides; lane
+    // holds dims 32*dt + 8*q4 + 4*g + 0..3 of row n), before the merge
+    if (LOWRANK && args.os_save && active) {
+      float *orow = args.os_save + base + n * args.stride_n;
+      const bool valid = n < args.n_tokens;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          f32x4 v = {oacc[dt][4 * q4], oacc[dt][4 * q4 + 1], oacc[dt][4 * q4 + 2], oacc[dt][4 * q4 + 3]};
+          if (!valid) v = f32x4{0.f, 0.f, 0.f, 0.f};
+          *(f32x4 *)(orow + 32 * dt + 8 * q4 + 4 * g) = v;
+        }
+      }
+    }
   }
   if (!active) return;
   attn_finish<D, LOWRANK, ACCUM, OUTF32>(args, qreg, oacc, n, base, bh, lane, sfreq);

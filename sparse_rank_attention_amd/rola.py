@@ -47,13 +47,13 @@ class RolaKernelTime(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_int32), ("total_ms", ctypes.c_double)]
 
 
-ABI_VERSION = 7  # ROLA_ABI_VERSION of include/rola.h
+ABI_VERSION = 8  # ROLA_ABI_VERSION of include/rola.h
 NOALLOC_SCRATCH_BYTES = 128 << 20  # ROLA_NOALLOC_SCRATCH_BYTES
 
 EXPORTS = ["rola_abi_version", "rola_status_str", "rola_plan", "rola_select_blocks",
            "rola_sparse_attn", "rola_lowrank_attn", "rola_forward", "rola_backward", "rola_timing_enable",
            "rola_timing_read", "rola_mfma_probe", "rola_quant_rows", "rola_gemm_w8a8",
-           "rola_forward_e4m3", "rola_forward_noalloc"]
+           "rola_forward_e4m3", "rola_forward_noalloc", "rola_forward_train", "rola_backward_saved"]
 
 _lib = None
 
@@ -87,6 +87,10 @@ def lib():
         L.rola_forward.argtypes = [P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.rola_backward.restype = I32
         L.rola_backward.argtypes = [P] * 17 + [ctypes.c_size_t, P]
+        L.rola_forward_train.restype = I32
+        L.rola_forward_train.argtypes = [P] * 13 + [ctypes.c_size_t, P]
+        L.rola_backward_saved.restype = I32
+        L.rola_backward_saved.argtypes = [P] * 19 + [ctypes.c_size_t, P]
         L.rola_timing_enable.restype = I32
         L.rola_timing_enable.argtypes = [I32]
         L.rola_timing_read.restype = I32
@@ -327,6 +331,32 @@ def rola_forward(q, k, v, wq, wk, grid, cfg: Config, out=None, block_idx_out=Non
     return out
 
 
+def rola_forward_train(q, k, v, wq, wk, grid, cfg: Config, out=None, block_idx_out=None, stream=None,
+                       gate=None):
+    """rola_forward that also keeps, for rola_backward_saved, the sparse branch's
+    output O_s (fp32, the layout of q) and each row's base-2 log-sum-exp
+    (fp32 [B*H, n_pad]).  Returns (out, os, lse)."""
+    _check_tokens(q, k, v)
+    _check_gate(gate, q)
+    prob = problem(q, grid)
+    info = plan(prob, cfg)
+    _check_planned(q, info)
+    _check_proj(q, cfg, wq, wk)
+    if block_idx_out is not None:
+        _check_map(block_idx_out, q, info, "block_idx_out")
+    out = _new_out(q, cfg) if out is None else out
+    _check_out(out, q, cfg)
+    _require_gpu(q)
+    os_ = torch.empty_strided(q.shape, q.stride(), dtype=torch.float32, device=q.device)
+    lse = torch.empty((q.shape[0] * q.shape[1], info.n_pad), dtype=torch.float32, device=q.device)
+    ws = workspace(q.device, info.workspace_bytes, stream)
+    c = cfg.c()
+    _check(lib().rola_forward_train(ctypes.byref(prob), ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(wq),
+                                    _ptr(wk), _ptr(gate), _ptr(block_idx_out), _ptr(out), _ptr(os_), _ptr(lse),
+                                    _ptr(ws), ws.numel(), _stream(stream)), "rola_forward_train")
+    return out, os_, lse
+
+
 def rola_forward_noalloc(q, k, v, wq, wk, grid, cfg: Config, out, block_idx_out=None, stream=None, gate=None):
     """rola_forward on the library's own per-GPU scratch (no workspace): ``out``
     is required, so the call itself allocates nothing.  Problems whose
@@ -386,11 +416,14 @@ def rola_forward_e4m3(q, k, v, q8, k8, v8, qs, ks, vs, wq, wk, grid, cfg: Config
     return out
 
 
-def rola_backward(q, k, v, wq, wk, grid, cfg: Config, block_idx, dout, gate=None, stream=None):
+def rola_backward(q, k, v, wq, wk, grid, cfg: Config, block_idx, dout, gate=None, stream=None, saved=None):
     """Gradients of the forward for dL/dO = dout (the block map held constant).
 
-    Returns (dq, dk, dv, dwq, dwk, dgate): bf16 tensors like q, fp32 [D, rank]
-    tensors, and the fp32 [D+1] gate gradient (None without a gate)."""
+    ``saved``: the (os, lse) pair of rola_forward_train on the same inputs,
+    map and config (rola_backward_saved), else None (the sparse branch is
+    recomputed).  Returns (dq, dk, dv, dwq, dwk, dgate): bf16 tensors like q,
+    fp32 [D, rank] tensors, and the fp32 [D+1] gate gradient (None without a
+    gate)."""
     _check_tokens(q, k, v)
     _check_gate(gate, q)
     want = torch.float32 if cfg.out_dtype == ROLA_OUT_F32 else torch.bfloat16
@@ -407,13 +440,28 @@ def rola_backward(q, k, v, wq, wk, grid, cfg: Config, block_idx, dout, gate=None
     dwq = torch.empty((D, cfg.rank), dtype=torch.float32, device=q.device)
     dwk = torch.empty((D, cfg.rank), dtype=torch.float32, device=q.device)
     dgate = torch.empty(D + 1, dtype=torch.float32, device=q.device) if gate is not None else None
+    if saved is not None:
+        os_, lse = saved
+        if (os_.dtype != torch.float32 or os_.shape != q.shape or os_.stride() != q.stride()
+                or os_.device != q.device):
+            raise RolaError("saved O_s must be fp32 with the layout of q")
+        if (lse.dtype != torch.float32 or tuple(lse.shape) != (B * H, info.n_pad) or not lse.is_contiguous()
+                or lse.device != q.device):
+            raise RolaError("saved lse must be contiguous fp32 [B*H, n_pad]")
     _require_gpu(q)
     ws = workspace(q.device, info.workspace_bytes_backward, stream)
     c = cfg.c()
-    _check(lib().rola_backward(ctypes.byref(prob), ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(wq),
-                               _ptr(wk), _ptr(gate), _ptr(block_idx), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
-                               _ptr(dwq), _ptr(dwk), _ptr(dgate), _ptr(ws), ws.numel(), _stream(stream)),
-           "rola_backward")
+    if saved is None:
+        _check(lib().rola_backward(ctypes.byref(prob), ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(wq),
+                                   _ptr(wk), _ptr(gate), _ptr(block_idx), _ptr(dout), _ptr(dq), _ptr(dk),
+                                   _ptr(dv), _ptr(dwq), _ptr(dwk), _ptr(dgate), _ptr(ws), ws.numel(),
+                                   _stream(stream)), "rola_backward")
+    else:
+        _check(lib().rola_backward_saved(ctypes.byref(prob), ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v),
+                                         _ptr(wq), _ptr(wk), _ptr(gate), _ptr(block_idx), _ptr(dout),
+                                         _ptr(os_), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dwq),
+                                         _ptr(dwk), _ptr(dgate), _ptr(ws), ws.numel(), _stream(stream)),
+               "rola_backward_saved")
     return dq, dk, dv, dwq, dwk, dgate
 
 

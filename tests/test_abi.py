@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     for name in _declared_functions():
         assert hasattr(L, name), name
     assert set(rola.EXPORTS) == set(_declared_functions())
-    assert L.rola_abi_version() == rola.ABI_VERSION == 7
+    assert L.rola_abi_version() == rola.ABI_VERSION == 8
 
 
 def _prob(B=1, H=40, D=128, grid=(21, 45, 80), sn=None):
@@ -155,6 +155,57 @@ def test_backward_validates_before_launch():
     st, cinfo = _plan(prob, comp)
     assert st == 0 and cinfo.workspace_bytes_backward > big
     assert call(comp, ok, cinfo.workspace_bytes_backward - 1) == 4
+
+
+def test_training_pair_validates_before_launch():
+    """rola_forward_train needs both saved outputs and bf16 precision; rola_backward_saved
+    needs both saved inputs (aligned) and otherwise checks as rola_backward does."""
+    L = rola.lib()
+    prob = _prob(grid=(4, 16, 16), D=64, H=2)
+    cfg = rola.Config(topk=0.25, rank=16)
+    fp8 = rola.Config(topk=0.25, rank=16, precision=rola.ROLA_PREC_FP8)
+    st, info = _plan(prob, cfg)
+    assert st == 0
+    fake = ctypes.c_void_p(0x10000)
+    odd = ctypes.c_void_p(0x10008)
+    odd4 = ctypes.c_void_p(0x10002)
+    null = ctypes.c_void_p(0)
+    # forward_train: q, k, v, wq, wk, gate, block_idx_out, out, os, lse
+    fwd = [fake] * 5 + [null, null, fake, fake, fake]
+
+    def ftrain(c, args, ws_bytes=info.workspace_bytes):
+        return L.rola_forward_train(P(prob), P(c.c()), *args, fake, ws_bytes, null)
+
+    for i in (8, 9):
+        args = list(fwd)
+        args[i] = null
+        assert ftrain(cfg, args) == 1                          # os or lse missing
+    args = list(fwd)
+    args[8] = odd
+    assert ftrain(cfg, args) == 3                              # os misaligned
+    args = list(fwd)
+    args[9] = odd4
+    assert ftrain(cfg, args) == 3                              # lse misaligned
+    assert ftrain(cfg, fwd, info.workspace_bytes - 1) == 4     # workspace too small
+    assert ftrain(fp8, fwd) == 2                               # fp8: no training pair
+    # backward_saved: q, k, v, wq, wk, gate, block_idx, dout, os, lse, dq, dk, dv, dwq, dwk, dgate
+    bwd = [fake] * 5 + [null] + [fake] * 9 + [null]
+
+    def bsaved(c, args, ws_bytes=info.workspace_bytes_backward):
+        return L.rola_backward_saved(P(prob), P(c.c()), *args, fake, ws_bytes, null)
+
+    for i in (8, 9):
+        args = list(bwd)
+        args[i] = null
+        assert bsaved(cfg, args) == 1                          # os or lse missing
+    args = list(bwd)
+    args[8] = odd
+    assert bsaved(cfg, args) == 3                              # os misaligned
+    args = list(bwd)
+    args[0] = null
+    assert bsaved(cfg, args) == 1                              # q missing
+    assert bsaved(cfg, bwd, info.workspace_bytes_backward - 1) == 4
+    assert bsaved(fp8, bwd) == 2
 
 
 def test_mfma_probe_validates_before_launch():
