@@ -107,24 +107,34 @@ def test_backward_complement_matches_oracle(name, w, gated, dout_f32):
     _backward_case(name, w, gated, dout_f32, complement=True)
 
 
-def test_backward_full_size_sampled():
+@pytest.mark.parametrize("saved", [False, True], ids=["recompute", "saved"])
+def test_backward_full_size_sampled(saved):
     """The benchmarked backward launch (Wan 14B 720P: 40 heads, N = 75600, 35
     kept blocks of 1182, bf16 dL/dO) against the written-out gradient formulas
     (oracle.backward.backward_sampled, pinned to autograd): dq rows of sampled
     query blocks and dk, dv rows of sampled key blocks in two heads, and the
-    projection gradients, which sum over all heads and tokens."""
+    projection gradients, which sum over all heads and tokens.  ``saved``: the
+    backward takes O_s and the log-sum-exp of rola_forward_train (bf16 output)
+    instead of recomputing them."""
     from sparse_rank_attention_amd import rola
     from tests.test_gpu_parity import _full_inputs
     torch = _torch()
     name = "wan14b_720p"
-    say("backward full size", name)
+    say("backward full size", name, "saved" if saved else "recompute")
     w, (q, k, v), (wq, wk) = _full_inputs(name)
     do = W.make_dout(w)
     cfg = rola.Config(topk=w.topk, rank=w.rank)
     qd, kd, vd = dev(q), dev(k), dev(v)
-    bmap = rola.rola_select_blocks(qd, kd, w.grid, cfg)
-    dq, dk, dv, dwq, dwk, _ = rola.rola_backward(qd, kd, vd, torch.from_numpy(wq).cuda(), torch.from_numpy(wk).cuda(),
-                                                 w.grid, cfg, bmap, dev(do))
+    wqd, wkd = torch.from_numpy(wq).cuda(), torch.from_numpy(wk).cuda()
+    if saved:
+        info = rola.plan(rola.problem(qd, w.grid), cfg)
+        bmap = torch.empty((w.batch, w.heads, info.nb, info.kb), dtype=torch.int32, device="cuda")
+        _, os_, lse = rola.rola_forward_train(qd, kd, vd, wqd, wkd, w.grid, cfg, block_idx_out=bmap)
+        pair = (os_, lse)
+    else:
+        bmap = rola.rola_select_blocks(qd, kd, w.grid, cfg)
+        pair = None
+    dq, dk, dv, dwq, dwk, _ = rola.rola_backward(qd, kd, vd, wqd, wkd, w.grid, cfg, bmap, dev(do), saved=pair)
     torch.cuda.synchronize()
     m_ref = oracle.block_map(q[0], k[0], w.n_tokens, oracle.keep_blocks(w.topk, w.nb))
     np.testing.assert_array_equal(bmap.cpu().numpy()[0], m_ref)
