@@ -106,3 +106,32 @@ def test_saved_pair_matches_oracle_with_bf16_output(name, w, complement):
     say("training pair bf16", name, "err/bound", {k_: round(v_, 3) for k_, v_ in ratios.items()})
     for key, r in ratios.items():
         assert r <= 1.0, (key, r)
+
+
+def test_saved_pair_for_heads_beyond_fp16():
+    """Heads whose V leaves the fp16 range take the bf16 form (fp32 weights) in the
+    forward, also in the training forward: for those heads the saved pair is the
+    backward's own recompute, so their dq, dk, dv equal rola_backward's bit for bit
+    (the projection gradients sum over all heads and are not compared)."""
+    import torch
+    from sparse_rank_attention_amd import rola
+    from tests.test_gpu_parity import small_workload
+    say("training pair, V beyond fp16")
+    w = small_workload((5, 9, 13), D=128, H=3, rank=32, topk=0.3, kind="field")
+    q, k, v = W.make_qkv(w)
+    v = v.copy()
+    big = np.array([1.0e5, -7.0e4], dtype=np.float32).view(np.uint32) >> 16  # bf16 99840, -70144
+    v[0, 1, 100, 3] = big[0]
+    v[0, 2, w.n_tokens - 1, 77] = big[1]
+    wq, wk = W.make_proj(w)
+    cfg = rola.Config(topk=w.topk, rank=w.rank)
+    t = dict(q=dev(q), k=dev(k), v=dev(v), wq=torch.from_numpy(wq).cuda(), wk=torch.from_numpy(wk).cuda(),
+             gate=None, dout=dev(W.make_dout(w)))
+    bmap, os_, lse = _forward_pair(w, cfg, t)
+    args = (t["q"], t["k"], t["v"], t["wq"], t["wk"], w.grid, cfg, bmap, t["dout"])
+    ref = rola.rola_backward(*args)
+    got = rola.rola_backward(*args, saved=(os_, lse))
+    torch.cuda.synchronize()
+    for key, a, b in zip(("dq", "dk", "dv"), got[:3], ref[:3]):
+        for h in (1, 2):
+            assert torch.equal(a[0, h].view(torch.int16), b[0, h].view(torch.int16)), (key, h)
