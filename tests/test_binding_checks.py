@@ -90,3 +90,28 @@ def test_token_tensors_must_agree():
         rola.rola_forward(q.float(), k, v, wq, wk, GRID, _cfg())
     with pytest.raises(rola.RolaError, match="share shape"):
         rola.rola_forward(q, k[:, :1], v, wq, wk, GRID, _cfg())
+
+
+def test_training_pair_arguments():
+    """rola_forward_train checks as rola_forward does; the saved pair handed to
+    rola_backward must be fp32 O_s with the layout of q and contiguous fp32
+    [B*H, n_pad] log-sum-exps."""
+    q, k, v = _qkv()
+    wq, wk = _proj()
+    with pytest.raises(rola.RolaError, match="GPU"):
+        rola.rola_forward_train(q, k, v, wq, wk, GRID, _cfg())
+    with pytest.raises(rola.RolaError, match="n_pad"):
+        rola.rola_forward_train(*_qkv(rows=90), wq, wk, GRID, _cfg())
+    bmap = torch.zeros((B, H, NB, 1), dtype=torch.int32)
+    dout = torch.zeros_like(q)
+    good_os = torch.zeros((B, H, NPAD, D), dtype=torch.float32)
+    good_lse = torch.zeros((B * H, NPAD), dtype=torch.float32)
+    with pytest.raises(rola.RolaError, match="GPU"):
+        rola.rola_backward(q, k, v, wq, wk, GRID, _cfg(), bmap, dout, saved=(good_os, good_lse))
+    for os_, lse, msg in ((good_os.to(torch.bfloat16), good_lse, "O_s"),
+                          (good_os[:, :, :90], good_lse, "O_s"),
+                          (good_os, good_lse[:, :90], "lse"),
+                          (good_os, good_lse.t().contiguous().t(), "lse"),
+                          (good_os, good_lse.to(torch.float64), "lse")):
+        with pytest.raises(rola.RolaError, match=msg):
+            rola.rola_backward(q, k, v, wq, wk, GRID, _cfg(), bmap, dout, saved=(os_, lse))
