@@ -159,24 +159,33 @@ def test_backward_full_size_sampled(saved):
         assert r <= 1.0, (key, r)
 
 
-def test_backward_complement_full_size_sampled():
+@pytest.mark.parametrize("saved", [False, True], ids=["recompute", "saved"])
+def test_backward_complement_full_size_sampled(saved):
     """The complement-scope backward at the benchmarked size (Wan 14B 720P, bf16
     dL/dO) against the written-out formulas in that scope
     (oracle.backward.backward_sampled, pinned to autograd): dq rows of sampled
     query blocks and dk, dv rows of sampled key blocks in two heads.  The
-    projection gradients sum over all 40 heads; the small cases cover them."""
+    projection gradients sum over all 40 heads; the small cases cover them.
+    ``saved``: with O_s and the log-sum-exp of rola_forward_train."""
     from sparse_rank_attention_amd import rola
     from tests.test_gpu_parity import _full_inputs
     torch = _torch()
     name = "wan14b_720p"
-    say("backward complement full size", name)
+    say("backward complement full size", name, "saved" if saved else "recompute")
     w, (q, k, v), (wq, wk) = _full_inputs(name)
     do = W.make_dout(w)
     cfg = rola.Config(topk=w.topk, rank=w.rank, lowrank_scope=rola.ROLA_LR_COMPLEMENT)
     qd, kd, vd = dev(q), dev(k), dev(v)
-    bmap = rola.rola_select_blocks(qd, kd, w.grid, cfg)
-    dq, dk, dv, _, _, _ = rola.rola_backward(qd, kd, vd, torch.from_numpy(wq).cuda(), torch.from_numpy(wk).cuda(),
-                                             w.grid, cfg, bmap, dev(do))
+    wqd, wkd = torch.from_numpy(wq).cuda(), torch.from_numpy(wk).cuda()
+    if saved:
+        info = rola.plan(rola.problem(qd, w.grid), cfg)
+        bmap = torch.empty((w.batch, w.heads, info.nb, info.kb), dtype=torch.int32, device="cuda")
+        _, os_, lse = rola.rola_forward_train(qd, kd, vd, wqd, wkd, w.grid, cfg, block_idx_out=bmap)
+        pair = (os_, lse)
+    else:
+        bmap = rola.rola_select_blocks(qd, kd, w.grid, cfg)
+        pair = None
+    dq, dk, dv, _, _, _ = rola.rola_backward(qd, kd, vd, wqd, wkd, w.grid, cfg, bmap, dev(do), saved=pair)
     torch.cuda.synchronize()
     heads = (1, w.heads - 2)
     maps = bmap.cpu().numpy()[0]
